@@ -1,0 +1,18 @@
+"""Plain CPU oracle (fp64) for indexer-selected block-sparse attention.
+
+Test infrastructure only: imported by ``tests/``, by the package smoke check and by
+the CPU-baseline leg of ``bench.py``.  Nothing in the library imports it.
+"""
+from .sparse_attn_oracle import (  # noqa: F401
+    SequencePools,
+    attend,
+    block_scores,
+    pool_blocks,
+    round_to_storage,
+    run_case,
+    run_query,
+    select_blocks,
+    select_positions,
+    select_positions_token_expanded,
+    visible_tokens,
+)
