@@ -1,0 +1,362 @@
+"""Benchmark of the indexer-selected sparse-attention decode step on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+
+A step is one pass of the whole path -- pool the newest block, score every block,
+select, attend -- for one decode token of a DeepSeek-V4-shaped layer at 128K context
+(16 query heads on one 576-wide latent KV head with V = its first 512 dims; indexer of
+64 heads x 128, compress_ratio 4, top_k 2048; bf16 caches).  Steps cycle through
+`--layers` independent copies of the layer's caches (like a model's layers), so that
+every step reads its ~10.7 MB from HBM rather than from the 256 MB last-level cache.
+The timed steps are replayed as one HIP graph (the same kernel launches, without the
+host-side launch overhead of the Python binding).
+
+Prints one JSON line.  `value` is algorithmic HBM bytes per step (pooled indexer keys
+of the visible blocks + gathered K rows) divided by the step time, in GB/s.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from indexer_top_block_amd import datagen  # noqa: E402
+from indexer_top_block_amd import sparse_attn as sa  # noqa: E402
+
+METRIC = "sparse-attn decode µs/step + HBM GB/s @128K ctx; prefill TFLOP/s (% roofline)"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+# --------------------------------------------------------------------------- layers
+
+class RotatingLayers:
+    """`n` copies of one layer's caches in HBM, and the calls of one decode step on copy r."""
+
+    def __init__(self, case: datagen.Case, n: int, device="cuda"):
+        d = case.dims
+        self.case, self.n, self.device = case, n, torch.device(device)
+        self.dims = sa.make_dims(d.h_q, d.h_kv, d.d_kq, d.d_v, d.h_idx, d.d_idx, d.compress_ratio, d.top_k, d.dtype)
+        dt = sa.TORCH_DTYPE[d.dtype]
+        c = d.compress_ratio
+        rows = case.rows
+        self.alias = case.v is None
+        k1 = torch.from_numpy(case.k).to(dt).to(device)
+        kidx1 = torch.from_numpy(case.kidx).to(dt).to(device)
+        self.k = torch.empty((n, rows, d.h_kv, d.d_kq), dtype=dt, device=device)
+        self.kidx = torch.empty((n, rows, d.d_idx), dtype=dt, device=device)
+        self.kpool = torch.zeros((n, rows // c, d.d_idx), dtype=dt, device=device)
+        for r in range(n):
+            self.k[r].copy_(k1)
+            self.kidx[r].copy_(kidx1)
+        del k1, kidx1
+        if not self.alias:
+            v1 = torch.from_numpy(case.v).to(dt).to(device)
+            self.v = torch.empty((n, rows, d.h_kv, d.d_v), dtype=dt, device=device)
+            for r in range(n):
+                self.v[r].copy_(v1)
+            del v1
+        else:
+            self.v = self.k
+        self.seq_row0 = torch.from_numpy(case.row0.astype(np.int64)).to(device)
+        self.seq_blk0 = torch.from_numpy(case.blk0.astype(np.int64)).to(device)
+        self.seq_len = torch.from_numpy(case.seq_len.astype(np.int32)).to(device)
+        self.q = torch.from_numpy(case.q).to(dt).to(device)
+        self.qidx = torch.from_numpy(case.qidx).to(dt).to(device)
+        self.q_seq = torch.from_numpy(case.q_seq.astype(np.int32)).to(device)
+        self.q_pos = torch.from_numpy(case.q_pos.astype(np.int32)).to(device)
+        self.n_q = case.n_q
+        self.max_len = int(case.seq_cap.max())
+        self.scores_ld = self.max_len // c
+        self.sel_ld = d.top_k + c - 1
+        self.scores = torch.zeros((self.n_q, self.scores_ld), dtype=torch.float32, device=device)
+        self.sel = torch.zeros((self.n_q, self.sel_ld), dtype=torch.int32, device=device)
+        self.n_sel = torch.zeros((self.n_q,), dtype=torch.int32, device=device)
+        self.out = torch.zeros((self.n_q, d.h_q, d.d_v), dtype=torch.float32, device=device)
+        self.ws_bytes = sa.sparse_attn_workspace_bytes(self.dims, self.n_q)
+        self.ws = torch.empty((max(self.ws_bytes, 16),), dtype=torch.uint8, device=device)
+        nb_full = (case.seq_len.astype(np.int64) // c).astype(np.int32)
+        # each step re-pools the newest complete block (what a decode step adds every c tokens)
+        self.n_pooled_prev = torch.from_numpy(np.maximum(nb_full - 1, 0)).to(device)
+        self.n_pooled_out = torch.zeros_like(self.n_pooled_prev)
+        self.caches = []
+        for r in range(n):
+            self.caches.append(sa.Cache(
+                seq_row0=self.seq_row0, seq_blk0=self.seq_blk0, seq_len=self.seq_len, max_len=self.max_len,
+                k=self.k[r], k_ld=d.h_kv * d.d_kq, k_head_stride=d.d_kq,
+                v=(self.k[r] if self.alias else self.v[r]),
+                v_ld=(d.h_kv * d.d_kq if self.alias else d.h_kv * d.d_v),
+                v_head_stride=(d.d_kq if self.alias else d.d_v),
+                kidx=self.kidx[r], kidx_ld=d.d_idx, kpool=self.kpool[r], kpool_ld=d.d_idx))
+
+    def fill_pools(self) -> None:
+        zeros = torch.zeros_like(self.n_pooled_prev)
+        for r in range(self.n):
+            sa.sparse_attn_pool(self.dims, self.caches[r], zeros, self.n_pooled_out, 2 ** 31 - 1)
+
+    # the four calls of a step, on copy r
+    def pool(self, r):
+        sa.sparse_attn_pool(self.dims, self.caches[r], self.n_pooled_prev, self.n_pooled_out, 1)
+
+    def score(self, r):
+        sa.sparse_attn_score(self.dims, self.caches[r], self.qidx, self.q_seq, self.q_pos, self.n_q, self.scores,
+                             self.scores_ld)
+
+    def select(self, r):
+        sa.sparse_attn_select(self.dims, self.caches[r], self.scores, self.scores_ld, self.q_seq, self.q_pos,
+                              self.n_q, self.sel, self.sel_ld, self.n_sel, self.ws, self.ws_bytes)
+
+    def fwd(self, r):
+        sa.sparse_attn_fwd(self.dims, self.caches[r], self.q, self.q_seq, self.sel, self.sel_ld, self.n_sel,
+                           self.n_q, self.case.scale, self.out, self.ws, self.ws_bytes)
+
+    def step(self, r):
+        self.pool(r)
+        self.score(r)
+        self.select(r)
+        self.fwd(r)
+
+
+def algorithmic_bytes(case: datagen.Case) -> dict:
+    """Bytes a step must read from HBM: pooled keys of every visible complete block of
+    every query, and the selected K rows (plus V rows when V is stored separately)."""
+    d = case.dims
+    es = 4 if d.dtype == "f32" else 2
+    c = d.compress_ratio
+    pooled = 0
+    gathered = 0
+    for i in range(case.n_q):
+        s = int(case.q_seq[i])
+        n_vis = max(0, min(int(case.seq_len[s]), int(case.q_pos[i]) + 1))
+        nb = n_vis // c
+        n_sel = min(nb, d.top_k // c) * c + (n_vis - nb * c)
+        pooled += nb * d.d_idx * es
+        gathered += n_sel * (d.h_kv * d.d_kq + (0 if case.v is None else d.h_kv * d.d_v)) * es
+    return {"pooled": pooled, "gathered": gathered, "total": pooled + gathered}
+
+
+# ----------------------------------------------------------------------- timing
+
+def time_graph(fn_per_step, n_steps: int, warmup: int) -> float:
+    """Capture n_steps calls of fn_per_step(k) in one graph; return ms per step of a replay."""
+    for k in range(max(warmup, 1)):
+        fn_per_step(k)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for k in range(n_steps):
+            fn_per_step(k)
+    torch.cuda.synchronize()
+    g.replay()                       # one untimed replay
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    g.replay()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / n_steps
+
+
+def time_eager(fn_per_step, n_steps: int, warmup: int) -> float:
+    for k in range(warmup):
+        fn_per_step(k)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for k in range(n_steps):
+        fn_per_step(k)
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / n_steps
+
+
+# -------------------------------------------------------------------- CPU oracle
+
+def cpu_baseline(case: datagen.Case, seconds: float, bytes_per_step: int) -> dict:
+    """The oracle's decode step on the host: re-pool the newest block, score every
+    block against the resident pooled keys, select, attend -- repeated for about
+    `seconds` of wall time."""
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([int(x.get("num_threads", 1)) for x in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    d = case.dims
+    c = d.compress_ratio
+    L = int(case.seq_len[0])
+    n_vis = min(L, int(case.q_pos[0]) + 1)
+    nb = n_vis // c
+    pooled = oracle.pool_blocks(case.kidx[:L], c, d.dtype)           # resident state, untimed
+    k_rows = case.k
+    v_rows = case.v_rows()
+
+    def one_step():
+        newest = oracle.pool_blocks(case.kidx[(nb - 1) * c: nb * c], c, d.dtype)
+        pooled[nb - 1] = newest[0]
+        scores = oracle.block_scores(case.qidx[0], pooled[:nb])
+        pos = oracle.select_positions(scores.astype(np.float32), n_vis, c, d.top_k)
+        return oracle.attend(case.q[0], k_rows[pos], v_rows[pos], case.scale)
+
+    one_step()
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        one_step()
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or n >= 1000:
+            break
+    per = el / n
+    return {"value": round(bytes_per_step / per / 1e9, 4), "unit": "GB/s", "cores": blas_threads,
+            "kind": "oracle", "sample": f"{n} full decode steps of the same workload (1 query), "
+                                        f"{per * 1e3:.1f} ms/step, numpy fp64",
+            "ms_per_step": round(per * 1e3, 3)}
+
+
+# ------------------------------------------------------------------------ prefill
+
+def prefill_report(steps: int) -> dict:
+    """Workload 4: 2048 query tokens at depth 32768 -- TFLOP/s of the score and the
+    attention stages and of the whole path, against the dense bf16 MFMA peak."""
+    from indexer_top_block_amd.device import DeviceLayer
+
+    case = datagen.make_workload(4)
+    lay = DeviceLayer(case)
+    lay.pool()
+    torch.cuda.synchronize()
+    d = case.dims
+    c = d.compress_ratio
+    nb = np.array([min(int(case.seq_len[0]), int(p) + 1) // c for p in case.q_pos], dtype=np.int64)
+    idx_flop = 2.0 * d.h_idx * d.d_idx * float(nb.sum())
+    lay.score(); lay.select(); torch.cuda.synchronize()
+    n_sel = lay.n_sel.cpu().numpy().astype(np.int64)
+    att_flop = 2.0 * d.h_q * float(n_sel.sum()) * (d.d_kq + d.d_v)
+    t_score = time_eager(lambda k: lay.score(), steps, 2)
+    t_select = time_eager(lambda k: lay.select(), steps, 2)
+    t_fwd = time_eager(lambda k: lay.fwd(), steps, 2)
+    t_all = time_eager(lambda k: (lay.score(), lay.select(), lay.fwd()), steps, 2)
+    tf = lambda flop, ms: flop / (ms * 1e-3) / 1e12
+    return {
+        "workload": datagen.WORKLOADS[4],
+        "ms_per_step": round(t_all, 4),
+        "tflops": round(tf(idx_flop + att_flop, t_all), 2),
+        "frac_of_mfma_peak": round(tf(idx_flop + att_flop, t_all) / MFMA_BF16_PEAK_TFLOPS, 4),
+        "gflop": {"indexer": round(idx_flop / 1e9, 2), "attention": round(att_flop / 1e9, 2)},
+        "stage_ms": {"score": round(t_score, 4), "select": round(t_select, 4), "fwd": round(t_fwd, 4)},
+        "stage_tflops": {"score": round(tf(idx_flop, t_score), 2), "fwd": round(tf(att_flop, t_fwd), 2)},
+    }
+
+
+# --------------------------------------------------------------------------- main
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--layers", type=int, default=64, help="copies of the layer's caches the steps cycle through")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--eager", action="store_true", help="launch every step from the host (no graph)")
+    ap.add_argument("--only", choices=["pool", "score", "select", "fwd"], default=None,
+                    help="run just this kernel for --steps launches (for counter collection)")
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark measures one GPU; the path runs on one MI355X and has no "
+                                   "multi-GPU mode (a sequence- or query-sharded layout is described in the design "
+                                   "notes)", "n_gpus": args.gpus}))
+        return 2
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        return 2
+    torch.cuda.set_device(0)
+    sa.load()
+
+    log("[bench] generating workload 2")
+    case = datagen.make_workload(2)
+    ab = algorithmic_bytes(case)
+    lay = RotatingLayers(case, args.layers)
+    lay.fill_pools()
+    torch.cuda.synchronize()
+    log(f"[bench] {args.layers} layer copies resident; algorithmic bytes/step {ab}")
+
+    if args.copy_probe_mb:
+        n = args.copy_probe_mb * 1024 * 1024 // 4
+        src = torch.randn(n, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy probe: {args.copy_probe_mb} MiB read + written")
+        del src, dst
+
+    R = args.layers
+    if args.only:
+        fn = getattr(lay, args.only)
+        ms = time_eager(lambda k: fn(k % R), args.steps, args.warmup)
+        print(json.dumps({"only": args.only, "launches": args.steps, "ms_per_launch": ms}))
+        return 0
+
+    # whole steps
+    run = time_eager if args.eager else time_graph
+    log("[bench] timing steps")
+    ms = run(lambda k: lay.step(k % R), args.steps, args.warmup)
+    # each kernel alone, back to back over the same rotation (average launch duration)
+    kernels = {}
+    for name in ("pool", "score", "select", "fwd"):
+        fn = getattr(lay, name)
+        kernels[name] = run(lambda k, fn=fn: fn(k % R), args.steps, args.warmup) * 1e3
+    log(f"[bench] step {ms * 1e3:.2f} us; per-call us {kernels}")
+    value = ab["total"] / (ms * 1e-3) / 1e9
+
+    # the dominant kernel and its roofline
+    per_call_bytes = {"score": ab["pooled"], "fwd": ab["gathered"]}
+    dom = max(("score", "fwd"), key=lambda n: kernels[n])
+    achieved = per_call_bytes[dom] / (kernels[dom] * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "bytes_per_launch": per_call_bytes[dom], "avg_launch_us": round(kernels[dom], 3)}
+
+    rec = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 6), "us_per_step": round(ms * 1e3, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "dsv4_decode_128k_bf16: 1 decode token, ctx 131072, 16 q heads on 1 latent KV "
+                               "head (DKQ 576 / DV 512, V = K[:512]), indexer 64x128, compress_ratio 4, "
+                               "top_k 2048",
+                   "layers_rotated": R, "graph": not args.eager,
+                   "bytes_per_step": ab},
+        "kernel_avg_us": {k: round(v, 3) for k, v in kernels.items()},
+        "roofline": roofline,
+    }
+    if not args.no_prefill:
+        log("[bench] prefill workload")
+        rec["prefill"] = prefill_report(max(5, min(args.steps, 20)))
+    if not args.no_cpu_baseline:
+        log("[bench] CPU oracle baseline")
+        rec["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds, ab["total"])
+    print(json.dumps(rec))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,182 @@
+/*
+ * sparse_attn.h -- C ABI of the indexer-selected block-sparse attention library
+ * for AMD Instinct MI355X (gfx950).  Library: libsparse_attn.so.
+ *
+ * The method (llama.cpp commit "llama: QSA sparse attention for qwen4exp", in the
+ * Qwen3.8-Flash-Next / qwen4exp series #27742): an indexer keeps one raw key per
+ * cached token; every block of compress_ratio consecutive positions gets one
+ * mean-pooled key; each query token scores every complete block as the sum over
+ * indexer heads of ReLU(q_h . kbar_b); it keeps the best blocks up to a budget of
+ * indexer_top_k tokens plus the tail of tokens not yet forming a complete block
+ * (exactly dense below indexer_top_k + compress_ratio - 1 visible tokens); and
+ * attention softmax(scale * Q K^T) V runs over the kept rows only (llama.cpp PR
+ * #27970 "CUDA + ggml: add sparse-fa for DSV4/GLM": gather through an ascending
+ * int32 index list, many query heads per KV head, V optionally a view of K).
+ *
+ * Four calls, one per step, all asynchronous on the caller's HIP stream:
+ *   sparse_attn_pool   -- incremental block mean-pool of the raw indexer keys
+ *   sparse_attn_score  -- indexer block scores per query token
+ *   sparse_attn_select -- kept blocks + tail -> ascending position list per query
+ *   sparse_attn_fwd    -- gather-fused attention over the position lists
+ *
+ * Conventions shared by every call
+ *  - Ownership: the caller allocates every buffer; the library never allocates,
+ *    frees or synchronises.  Every pointer in sa_cache and every array argument
+ *    is DEVICE memory unless stated otherwise; sa_dims / sa_cache themselves are
+ *    host structs read during the call only.
+ *  - Stream: `stream` is a hipStream_t (NULL = the default stream).  Calls return
+ *    after enqueueing; results are ready when the stream reaches them.
+ *  - Errors: 0 on success or a negative SA_ERR_* code.  Every argument error is
+ *    detected on the host before any HIP call, so nothing is enqueued on error.
+ *    SA_ERR_HIP reports a failed launch (hipGetLastError after the launch).
+ *  - Positions: row seq_row0[s] + t of a cache holds position t of sequence s.
+ *    A query token i (sequence q_seq[i], position q_pos[i]) sees position t iff
+ *    t <= q_pos[i] and t < seq_len[q_seq[i]]; n_vis = number of such positions.
+ *    Block b of sequence s covers positions [b*c, (b+1)*c); it is complete for a
+ *    query when (b+1)*c <= n_vis.  NB = n_vis / c; tail = n_vis - NB*c.
+ *  - Element types: every cache and query tensor has the one dtype of sa_dims;
+ *    scores, outputs and workspaces are float32; lists are int32.
+ *  - Calls that overlap on one stream are ordered; calls on different streams that
+ *    write the same buffers race (as with any kernel).
+ */
+#ifndef SPARSE_ATTN_H
+#define SPARSE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of the caches and query tensors. */
+typedef enum { SA_F32 = 0, SA_F16 = 1, SA_BF16 = 2 } sa_dtype;
+
+/* Error codes. */
+enum {
+  SA_OK = 0,
+  SA_ERR_NULL = -1,      /* a required pointer is NULL                                   */
+  SA_ERR_DIMS = -2,      /* dimensions unsupported or inconsistent (see sparse_attn_check_dims) */
+  SA_ERR_ARG = -3,       /* another argument out of range (count, leading dimension, size) */
+  SA_ERR_WORKSPACE = -4, /* workspace NULL or smaller than sparse_attn_workspace_bytes     */
+  SA_ERR_HIP = -5        /* a kernel launch failed                                        */
+};
+
+/* Shape of one attention layer and its indexer. */
+typedef struct {
+  int32_t h_q;            /* query heads                                                   */
+  int32_t h_kv;           /* KV heads; h_q % h_kv == 0; query head h reads KV head h/(h_q/h_kv) */
+  int32_t d_kq;           /* K and Q head size                                             */
+  int32_t d_v;            /* V head size                                                   */
+  int32_t h_idx;          /* indexer heads                                                 */
+  int32_t d_idx;          /* indexer head size (one indexer key head)                      */
+  int32_t compress_ratio; /* c: tokens per pooled block, >= 1                              */
+  int32_t top_k;          /* indexer_top_k: token budget of kept blocks, a multiple of c    */
+  int32_t dtype;          /* sa_dtype of K, V, raw/pooled indexer keys, q, indexer queries  */
+} sa_dims;
+
+/* One layer's caches for n_seq sequences (all pointers device memory, caller-owned).
+ * Element (row r, KV head g, dim d) of K is k[r*k_ld + g*k_head_stride + d]; V
+ * likewise.  V may alias K (v == k, v_ld == k_ld, v_head_stride == k_head_stride):
+ * V is then the first d_v elements of each K head, as in MLA's latent cache
+ * (llama.cpp "Create V as a view of K" in the llm_graph_input_attn_k_iswa fix).   */
+typedef struct {
+  int32_t n_seq;            /* sequences                                                     */
+  int32_t max_len;          /* host-side upper bound on every seq_len[s] (sizes the grids)   */
+  const int64_t* seq_row0;  /* [n_seq] first cache row of sequence s                          */
+  const int64_t* seq_blk0;  /* [n_seq] first pooled-key row of sequence s                     */
+  const int32_t* seq_len;   /* [n_seq] cached tokens L_s (positions 0..L_s-1)                 */
+  const void* k;            /* K cache, d_kq per head                                        */
+  int64_t k_ld;             /* row stride of K in elements (>= h_kv*d_kq when unaliased)      */
+  int64_t k_head_stride;    /* KV-head stride of K in elements                               */
+  const void* v;            /* V cache, d_v per head (may alias k)                           */
+  int64_t v_ld;
+  int64_t v_head_stride;
+  const void* kidx;         /* raw indexer keys, one head of d_idx per row                   */
+  int64_t kidx_ld;
+  void* kpool;              /* pooled indexer keys, d_idx per pooled row (written by pool)   */
+  int64_t kpool_ld;
+} sa_cache;
+
+/* Host-only validation of the dimensions: 0 or SA_ERR_NULL / SA_ERR_DIMS.
+ * Supported: dtype in {F32, F16, BF16}; h_q, h_kv >= 1 with h_q % h_kv == 0 and
+ * h_q / h_kv <= 16; 1 <= d_kq <= 1024; 1 <= d_v <= 1024; 1 <= h_idx <= 128;
+ * d_idx in [8, 512] and a multiple of 8; 1 <= compress_ratio <= 64; top_k >= c and
+ * top_k % c == 0; top_k + c - 1 <= 65536.  Makes no HIP call.                        */
+int sparse_attn_check_dims(const sa_dims* dims);
+
+/* Bytes of workspace that sparse_attn_select and sparse_attn_fwd need for n_q query
+ * tokens of this layer (the two calls may share one buffer).  0 on bad dims.       */
+size_t sparse_attn_workspace_bytes(const sa_dims* dims, int32_t n_q);
+
+/* Incremental block mean-pool (pages: the indexer cache holds raw keys because
+ * pooling happens before the norm and the rotation; one pooled key per block of
+ * compress_ratio tokens).  For each sequence s, pools blocks
+ * [n_pooled_in[s], n_new) where n_new = min(seq_len[s] / c, n_pooled_in[s] + max_new_blocks):
+ *     kpool[seq_blk0[s] + b] = (sum_{i<c} kidx[seq_row0[s] + b*c + i]) / c,
+ * summed in float32 in position order and rounded to the cache dtype (RNE), and
+ * writes n_pooled_out[s] = n_new (device arrays of n_seq int32; they may alias --
+ * the update is ordered after every read).  Resuming from raw keys = n_pooled_in 0.
+ * A sequence whose seq_len shrank below n_pooled_in*c gets n_pooled_out = seq_len/c.
+ * Errors: SA_ERR_NULL, SA_ERR_DIMS, SA_ERR_ARG (n_seq < 1, max_new_blocks < 0,
+ * kidx_ld / kpool_ld < d_idx, max_len < 0), SA_ERR_HIP.                            */
+int sparse_attn_pool(const sa_dims* dims, const sa_cache* cache, const int32_t* n_pooled_in,
+                     int32_t* n_pooled_out, int32_t max_new_blocks, void* stream);
+
+/* Indexer block scores (pages: each head's dot product is rectified before the sum
+ * over heads; scoring is batched per sequence so a sequence's queries meet only its
+ * own blocks).  For query token i and every complete block b < NB(i):
+ *     scores[i*scores_ld + b] = sum_{h<h_idx} max(0, sum_d qidx[i][h][d] * kpool[seq_blk0[s]+b][d])
+ * accumulated in float32, written as +0.0 when no head is positive.  Entries
+ * b >= NB(i) are not written.  qidx is [n_q][h_idx][d_idx] contiguous, in the
+ * cache dtype.  The pooled keys of blocks < NB(i) must be current (sparse_attn_pool).
+ * Requires scores_ld >= max_len / c.  Errors: SA_ERR_NULL, SA_ERR_DIMS, SA_ERR_ARG
+ * (n_q < 0, scores_ld too small), SA_ERR_HIP.  n_q == 0 is a no-op.                  */
+int sparse_attn_score(const sa_dims* dims, const sa_cache* cache, const void* qidx,
+                      const int32_t* q_seq, const int32_t* q_pos, int32_t n_q,
+                      float* scores, int64_t scores_ld, void* stream);
+
+/* Block selection (pages: keep a budget of the best blocks plus the tail; exactly
+ * dense below top_k + c - 1 tokens; block scores are expanded to tokens and the cut
+ * lands on a block boundary).  For query token i with K_blk = top_k / c:
+ *   kept = all NB blocks if NB <= K_blk, else the first K_blk blocks in the order
+ *          (score descending, block index ascending) -- ties go to the lower index,
+ *          and +0.0 / -0.0 compare equal;
+ *   sel[i*sel_ld + j], j < n_sel[i] = the positions of the kept blocks (c each) in
+ *          ascending order, followed by the tail positions [NB*c, n_vis);
+ *   sel[i*sel_ld + j], n_sel[i] <= j < sel_ld = -1.
+ * n_sel[i] = min(NB, K_blk)*c + tail <= top_k + c - 1 (the list cannot overflow).
+ * Requires sel_ld >= top_k + c - 1 and scores_ld >= max_len / c.  Scores must not be
+ * NaN.  ws: workspace of sparse_attn_workspace_bytes(dims, n_q) bytes (may be NULL
+ * when that is 0).  Errors: SA_ERR_NULL, SA_ERR_DIMS, SA_ERR_ARG, SA_ERR_WORKSPACE,
+ * SA_ERR_HIP.                                                                        */
+int sparse_attn_select(const sa_dims* dims, const sa_cache* cache, const float* scores,
+                       int64_t scores_ld, const int32_t* q_seq, const int32_t* q_pos, int32_t n_q,
+                       int32_t* sel, int64_t sel_ld, int32_t* n_sel, void* ws, size_t ws_bytes,
+                       void* stream);
+
+/* Gather-fused attention over the selected rows (pages: the sparse flash-attention
+ * kernel loads K/V rows through the index list; rows -1 contribute nothing).  For
+ * query token i, query head h (KV head g = h / (h_q/h_kv)):
+ *     out[i][h][:] = sum_t softmax_t(scale * q[i][h] . K[t][g]) V[t][g][:]
+ * over t in { seq_row0[s] + sel[i*sel_ld + j] : j < min(n_sel[i], sel_ld),
+ *             0 <= sel[...] < seq_len[s] } (other entries are skipped), accumulated
+ * in float32; out = 0 when the set is empty.  q is [n_q][h_q][d_kq] contiguous in
+ * the cache dtype; out is [n_q][h_q][d_v] float32 contiguous.  ws: workspace of
+ * sparse_attn_workspace_bytes(dims, n_q) bytes (split-KV partial results).
+ * Errors: SA_ERR_NULL, SA_ERR_DIMS, SA_ERR_ARG, SA_ERR_WORKSPACE, SA_ERR_HIP.        */
+int sparse_attn_fwd(const sa_dims* dims, const sa_cache* cache, const void* q,
+                    const int32_t* q_seq, const int32_t* sel, int64_t sel_ld, const int32_t* n_sel,
+                    int32_t n_q, float scale, float* out, void* ws, size_t ws_bytes, void* stream);
+
+/* Static description of an error code (never NULL). */
+const char* sparse_attn_strerror(int code);
+
+/* Library version string, e.g. "sparse_attn 0.1 gfx950". */
+const char* sparse_attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSE_ATTN_H */

@@ -1,0 +1,157 @@
+// C ABI of libsparse_attn: argument validation on the host, then the launchers.
+// Every argument error is reported before any HIP call is made.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "sa_launch.hpp"
+#include "sparse_attn.h"
+
+namespace {
+
+using sa::CacheArgs;
+
+bool dtype_ok(int32_t t) { return t == SA_F32 || t == SA_F16 || t == SA_BF16; }
+
+int check_dims(const sa_dims* d) {
+  if (!d) return SA_ERR_NULL;
+  if (!dtype_ok(d->dtype)) return SA_ERR_DIMS;
+  if (d->h_q < 1 || d->h_kv < 1 || d->h_q % d->h_kv != 0 || d->h_q / d->h_kv > 16) return SA_ERR_DIMS;
+  if (d->d_kq < 1 || d->d_kq > 1024 || d->d_v < 1 || d->d_v > 1024) return SA_ERR_DIMS;
+  if (d->h_idx < 1 || d->h_idx > 128) return SA_ERR_DIMS;
+  if (d->d_idx < 8 || d->d_idx > 512 || d->d_idx % 8 != 0) return SA_ERR_DIMS;
+  if (d->compress_ratio < 1 || d->compress_ratio > 64) return SA_ERR_DIMS;
+  if (d->top_k < d->compress_ratio || d->top_k % d->compress_ratio != 0) return SA_ERR_DIMS;
+  if ((int64_t)d->top_k + d->compress_ratio - 1 > 65536) return SA_ERR_DIMS;
+  return SA_OK;
+}
+
+// Checks shared by every call that reads the cache struct.
+int check_cache_common(const sa_dims* d, const sa_cache* c) {
+  if (!c) return SA_ERR_NULL;
+  if (!c->seq_row0 || !c->seq_len) return SA_ERR_NULL;
+  if (c->n_seq < 1 || c->max_len < 0) return SA_ERR_ARG;
+  (void)d;
+  return SA_OK;
+}
+
+CacheArgs to_args(const sa_cache* c) {
+  CacheArgs a;
+  a.n_seq = c->n_seq;
+  a.max_len = c->max_len;
+  a.seq_row0 = c->seq_row0;
+  a.seq_blk0 = c->seq_blk0;
+  a.seq_len = c->seq_len;
+  a.k = c->k;
+  a.k_ld = c->k_ld;
+  a.k_hs = c->k_head_stride;
+  a.v = c->v;
+  a.v_ld = c->v_ld;
+  a.v_hs = c->v_head_stride;
+  a.kidx = c->kidx;
+  a.kidx_ld = c->kidx_ld;
+  a.kpool = c->kpool;
+  a.kpool_ld = c->kpool_ld;
+  return a;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? SA_OK : SA_ERR_HIP; }
+
+constexpr int kMaxGridY = 65535;
+
+}  // namespace
+
+extern "C" {
+
+int sparse_attn_check_dims(const sa_dims* dims) { return check_dims(dims); }
+
+size_t sparse_attn_workspace_bytes(const sa_dims* dims, int32_t n_q) {
+  if (check_dims(dims) != SA_OK || n_q < 0) return 0;
+  return sa::plan_fwd(*dims, n_q).ws_bytes;
+}
+
+int sparse_attn_pool(const sa_dims* dims, const sa_cache* cache, const int32_t* n_pooled_in, int32_t* n_pooled_out,
+                     int32_t max_new_blocks, void* stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if ((rc = check_cache_common(dims, cache))) return rc;
+  if (!cache->seq_blk0 || !cache->kidx || !cache->kpool || !n_pooled_in || !n_pooled_out) return SA_ERR_NULL;
+  if (max_new_blocks < 0 || cache->kidx_ld < dims->d_idx || cache->kpool_ld < dims->d_idx) return SA_ERR_ARG;
+  if (cache->n_seq > kMaxGridY) return SA_ERR_ARG;
+  (void)hipGetLastError();  // clear a stale error so that a failure below is this call's own
+  return hip_status(sa::launch_pool(*dims, to_args(cache), n_pooled_in, n_pooled_out, max_new_blocks,
+                                    (hipStream_t)stream));
+}
+
+int sparse_attn_score(const sa_dims* dims, const sa_cache* cache, const void* qidx, const int32_t* q_seq,
+                      const int32_t* q_pos, int32_t n_q, float* scores, int64_t scores_ld, void* stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if ((rc = check_cache_common(dims, cache))) return rc;
+  if (n_q < 0 || n_q > kMaxGridY) return SA_ERR_ARG;
+  if (n_q == 0) return SA_OK;
+  if (!cache->seq_blk0 || !cache->kpool || !qidx || !q_seq || !q_pos || !scores) return SA_ERR_NULL;
+  if (cache->kpool_ld < dims->d_idx) return SA_ERR_ARG;
+  if (scores_ld < (int64_t)(cache->max_len / dims->compress_ratio) || scores_ld < 0) return SA_ERR_ARG;
+  (void)hipGetLastError();
+  return hip_status(
+      sa::launch_score(*dims, to_args(cache), qidx, q_seq, q_pos, n_q, scores, scores_ld, (hipStream_t)stream));
+}
+
+int sparse_attn_select(const sa_dims* dims, const sa_cache* cache, const float* scores, int64_t scores_ld,
+                       const int32_t* q_seq, const int32_t* q_pos, int32_t n_q, int32_t* sel, int64_t sel_ld,
+                       int32_t* n_sel, void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;  // the selection needs no workspace at present
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if ((rc = check_cache_common(dims, cache))) return rc;
+  if (n_q < 0) return SA_ERR_ARG;
+  if (n_q == 0) return SA_OK;
+  if (!scores || !q_seq || !q_pos || !sel || !n_sel) return SA_ERR_NULL;
+  if (sel_ld < (int64_t)dims->top_k + dims->compress_ratio - 1) return SA_ERR_ARG;
+  if (scores_ld < (int64_t)(cache->max_len / dims->compress_ratio) || scores_ld < 0) return SA_ERR_ARG;
+  (void)hipGetLastError();
+  return hip_status(sa::launch_select(*dims, to_args(cache), scores, scores_ld, q_seq, q_pos, n_q, sel, sel_ld,
+                                      n_sel, (hipStream_t)stream));
+}
+
+int sparse_attn_fwd(const sa_dims* dims, const sa_cache* cache, const void* q, const int32_t* q_seq,
+                    const int32_t* sel, int64_t sel_ld, const int32_t* n_sel, int32_t n_q, float scale, float* out,
+                    void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if ((rc = check_cache_common(dims, cache))) return rc;
+  if (n_q < 0 || (int64_t)n_q * dims->h_kv > kMaxGridY) return SA_ERR_ARG;
+  if (n_q == 0) return SA_OK;
+  if (!cache->k || !cache->v || !q || !q_seq || !sel || !n_sel || !out) return SA_ERR_NULL;
+  if (sel_ld < 1) return SA_ERR_ARG;
+  if (cache->k_ld < 1 || cache->v_ld < 1 || cache->k_head_stride < 0 || cache->v_head_stride < 0) return SA_ERR_ARG;
+  if (dims->h_kv > 1 && (cache->k_head_stride < dims->d_kq || cache->v_head_stride < dims->d_v)) return SA_ERR_ARG;
+  if (cache->k_ld < (int64_t)(dims->h_kv - 1) * cache->k_head_stride + dims->d_kq) return SA_ERR_ARG;
+  const bool alias = cache->v == cache->k;
+  if (alias && dims->d_v > dims->d_kq) return SA_ERR_ARG;
+  if (cache->v_ld < (int64_t)(dims->h_kv - 1) * cache->v_head_stride + dims->d_v) return SA_ERR_ARG;
+  if (!(scale == scale)) return SA_ERR_ARG;  // NaN
+  const sa::FwdPlan plan = sa::plan_fwd(*dims, n_q);
+  if (plan.ws_bytes > 0 && (!ws || ws_bytes < plan.ws_bytes)) return SA_ERR_WORKSPACE;
+  (void)hipGetLastError();
+  return hip_status(sa::launch_fwd(*dims, to_args(cache), q, q_seq, sel, sel_ld, n_sel, n_q, scale, out, ws, plan,
+                                   (hipStream_t)stream));
+}
+
+const char* sparse_attn_strerror(int code) {
+  switch (code) {
+    case SA_OK: return "success";
+    case SA_ERR_NULL: return "a required pointer is NULL";
+    case SA_ERR_DIMS: return "unsupported or inconsistent dimensions";
+    case SA_ERR_ARG: return "argument out of range";
+    case SA_ERR_WORKSPACE: return "workspace missing or too small";
+    case SA_ERR_HIP: return "HIP kernel launch failed";
+    default: return "unknown error code";
+  }
+}
+
+const char* sparse_attn_version(void) { return "sparse_attn 0.1 gfx950"; }
+
+}  // extern "C"

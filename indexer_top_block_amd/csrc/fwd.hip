@@ -1,0 +1,463 @@
+// Gather-fused attention over each query token's selected rows, with split-KV
+// partial results and an online-softmax combine.
+//
+// The pages' sparse flash attention loads K/V rows through an ascending int32 index
+// list inside the attention kernel instead of materialising a dense copy (llama.cpp
+// PR #27970 "CUDA + ggml: add sparse-fa for DSV4/GLM": the gather-vs-get_rows review
+// exchange, and the index-guarded row loads); V may be the first DV elements of each
+// K row (MLA latent cache).  Shapes of note: DKQ/DV = 576/512 with 16 query heads per
+// KV head, 512/512 with 8.
+//
+// MFMA path (f16 / bf16, up to 16 query heads per KV head, DKQ % 32 == 0, DV % 64 == 0):
+//   one workgroup = 4 waves = one (query token, KV head, split).  Per 32-row tile the
+//   workgroup gathers K rows (and V rows when separate) into LDS with 16-byte loads;
+//   every wave computes S^T = K Q^T for the tile with v_mfma_f32_16x16x32 (rows as
+//   M, the up-to-16 heads as N, Q^T kept in registers), so the softmax statistics of
+//   a head sit in one lane column; each wave then accumulates its quarter of DV as
+//   O^T = V^T P^T with v_mfma_f32_16x16x16, where P^T is the S^T accumulator itself
+//   (same lane layout) converted to 16-bit and V^T is read from LDS column-wise.
+// VALU path (any dtype): the same tiles with plain float dot products.
+//
+// Partial results: o (unnormalised, float32), m (running max, log2 units) and l
+// (sum of weights) per (query, head, split); the combine kernel merges the splits.
+#include "sa_common.hpp"
+#include "sa_launch.hpp"
+
+namespace sa {
+
+constexpr int kRowTile = 32;
+
+// ------------------------------------------------------------------- shared helpers
+
+__device__ __forceinline__ int64_t tile_row(const int32_t* list, int j, int r_end, int seq_len, int64_t row0) {
+  if (j >= r_end) return -1;
+  const int pos = list[j];
+  return (pos >= 0 && pos < seq_len) ? row0 + pos : -1;
+}
+
+template <typename T>
+__device__ __forceinline__ f32x4 mfma16x16x32(const typename vec8<T>::type& a, const typename vec8<T>::type& b,
+                                              const f32x4& c);
+template <>
+__device__ __forceinline__ f32x4 mfma16x16x32<bf16>(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+template <>
+__device__ __forceinline__ f32x4 mfma16x16x32<f16>(const f16x8& a, const f16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// 16x16x16 product with four 16-bit A and B elements per lane.
+template <typename T> struct pv_mfma;
+template <> struct pv_mfma<bf16> {
+  static __device__ __forceinline__ f32x4 run(const bf16 (&a)[4], const bf16 (&b)[4], const f32x4& c) {
+    bf16x4 av = {a[0], a[1], a[2], a[3]};
+    bf16x4 bv = {b[0], b[1], b[2], b[3]};
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, av), __builtin_bit_cast(i16x4, bv),
+                                                     c, 0, 0, 0);
+  }
+};
+template <> struct pv_mfma<f16> {
+  static __device__ __forceinline__ f32x4 run(const f16 (&a)[4], const f16 (&b)[4], const f32x4& c) {
+    f16x4 av = {a[0], a[1], a[2], a[3]};
+    f16x4 bv = {b[0], b[1], b[2], b[3]};
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(av, bv, c, 0, 0, 0);
+  }
+};
+
+// ---------------------------------------------------------------------------- MFMA
+
+template <typename T, int DKQ, int DV, bool ALIAS>
+__global__ void __launch_bounds__(256)
+fwd_mfma_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, int64_t k_hs,
+                const T* __restrict__ v, int64_t v_ld, int64_t v_hs, const int64_t* __restrict__ seq_row0,
+                const int32_t* __restrict__ seq_len, const int32_t* __restrict__ q_seq,
+                const int32_t* __restrict__ sel, int64_t sel_ld, const int32_t* __restrict__ n_sel, int h_q,
+                int h_kv, float scale_log2, int n_split, int rows_per_split, float* __restrict__ out,
+                float* __restrict__ ws_o, float* __restrict__ ws_ml) {
+  typedef typename vec8<T>::type V8;
+  constexpr int KST = DKQ / 32;       // QK^T MFMA steps
+  constexpr int KP = DKQ + 8;         // LDS row pitch of the K tile (elements)
+  constexpr int VP = ALIAS ? KP : DV + 8;
+  constexpr int DVW = DV / 4;         // DV columns per wave
+  constexpr int NT = DVW / 16;        // 16-column output tiles per wave
+  constexpr int KCH = DKQ / 8;        // 16-byte chunks per K row
+  constexpr int VCH = DV / 8;
+  __shared__ __attribute__((aligned(16))) T ks[kRowTile * KP];
+  __shared__ __attribute__((aligned(16))) T vs_sep[ALIAS ? 8 : kRowTile * VP];
+  __shared__ int64_t rows[kRowTile];
+  const T* vs = ALIAS ? ks : vs_sep;
+
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave, wave = tid / kWave;
+  const int col = lane & 15, grp = lane >> 4;
+  const int split = blockIdx.x;
+  const int i = blockIdx.y / h_kv, g = blockIdx.y % h_kv;
+  const int G = h_q / h_kv;
+  const int s = q_seq[i];
+  const int L = seq_len[s];
+  const int64_t row0 = seq_row0[s];
+  const int cnt = max(0, (int)min((int64_t)n_sel[i], sel_ld));
+  const int r_begin = split * rows_per_split;
+  const int r_end = min(cnt, r_begin + rows_per_split);
+  const int32_t* list = sel + (int64_t)i * sel_ld;
+
+  // Q^T as the B operand: lane (col = head, grp) holds dims ks*32 + grp*8 .. +8.
+  V8 qf[KST];
+  {
+    const T* qh = q + ((int64_t)i * h_q + (int64_t)g * G + col) * DKQ + grp * 8;
+#pragma unroll
+    for (int st = 0; st < KST; ++st) qf[st] = (col < G) ? *reinterpret_cast<const V8*>(qh + st * 32) : V8{};
+  }
+  float m = -INFINITY, lsum = 0.f;
+  f32x4 o[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int r0 = r_begin; r0 < r_end; r0 += kRowTile) {
+    if (tid < kRowTile) rows[tid] = tile_row(list, r0 + tid, r_end, L, row0);
+    __syncthreads();
+    for (int e = tid; e < kRowTile * KCH; e += 256) {
+      const int r = e / KCH, cc = e % KCH;
+      const int64_t row = rows[r];
+      V8 val = V8{};
+      if (row >= 0) val = *reinterpret_cast<const V8*>(k + row * k_ld + (int64_t)g * k_hs + cc * 8);
+      *reinterpret_cast<V8*>(ks + r * KP + cc * 8) = val;
+    }
+    if (!ALIAS) {
+      for (int e = tid; e < kRowTile * VCH; e += 256) {
+        const int r = e / VCH, cc = e % VCH;
+        const int64_t row = rows[r];
+        V8 val = V8{};
+        if (row >= 0) val = *reinterpret_cast<const V8*>(v + row * v_ld + (int64_t)g * v_hs + cc * 8);
+        *reinterpret_cast<V8*>(vs_sep + r * VP + cc * 8) = val;
+      }
+    }
+    __syncthreads();
+
+    // S^T[row][head] for the tile's two 16-row halves.
+    f32x4 sacc[2];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      sacc[h2] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const T* arow = ks + (h2 * 16 + col) * KP + grp * 8;
+#pragma unroll
+      for (int st = 0; st < KST; ++st)
+        sacc[h2] = mfma16x16x32<T>(*reinterpret_cast<const V8*>(arow + st * 32), qf[st], sacc[h2]);
+    }
+    // Online softmax for head `col`; this lane holds rows h2*16 + 4*grp + j.
+    float x[2][4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bool ok = rows[h2 * 16 + 4 * grp + j] >= 0;
+        x[h2][j] = ok ? sacc[h2][j] * scale_log2 : -INFINITY;
+        mx = fmaxf(mx, x[h2][j]);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m, mx);
+    const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m - m_new);
+    T pb[2][4];
+    float psum = 0.f;
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float p = (x[h2][j] == -INFINITY) ? 0.f : fast_exp2(x[h2][j] - m_new);
+        psum += p;
+        pb[h2][j] = (T)p;
+      }
+    lsum = lsum * alpha + psum;
+    m = m_new;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) o[nt] *= alpha;
+
+    // O^T[dv][head] += V^T[dv][row] P^T[row][head], 16 rows per product.
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int dv = wave * DVW + nt * 16 + col;
+        T a[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) a[j] = vs[(h2 * 16 + 4 * grp + j) * VP + dv];
+        o[nt] = pv_mfma<T>::run(a, pb[h2], o[nt]);
+      }
+    }
+    __syncthreads();
+  }
+
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
+  if (col < G) {
+    const int hq = g * G + col;
+    const int64_t qh = (int64_t)i * h_q + hq;
+    if (n_split == 1) {
+      const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int dv = wave * DVW + nt * 16 + 4 * grp;
+        *reinterpret_cast<f32x4*>(out + qh * DV + dv) = o[nt] * inv;
+      }
+    } else {
+      float* dst = ws_o + (qh * n_split + split) * DV;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int dv = wave * DVW + nt * 16 + 4 * grp;
+        *reinterpret_cast<f32x4*>(dst + dv) = o[nt];
+      }
+      if (wave == 0 && grp == 0) {
+        ws_ml[(qh * n_split + split) * 2 + 0] = m;
+        ws_ml[(qh * n_split + split) * 2 + 1] = lsum;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------- VALU
+
+template <typename T, int ACC>
+__global__ void __launch_bounds__(256)
+fwd_valu_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, int64_t k_hs,
+                const T* __restrict__ v, int64_t v_ld, int64_t v_hs, const int64_t* __restrict__ seq_row0,
+                const int32_t* __restrict__ seq_len, const int32_t* __restrict__ q_seq,
+                const int32_t* __restrict__ sel, int64_t sel_ld, const int32_t* __restrict__ n_sel, int h_q,
+                int h_kv, int d_kq, int d_v, float scale_log2, int n_split, int rows_per_split,
+                float* __restrict__ out, float* __restrict__ ws_o, float* __restrict__ ws_ml) {
+  __shared__ int64_t rows[kRowTile];
+  __shared__ float p[16][kRowTile];
+  __shared__ float m_s[16], l_s[16], a_s[16];
+  const int tid = threadIdx.x;
+  const int split = blockIdx.x;
+  const int i = blockIdx.y / h_kv, g = blockIdx.y % h_kv;
+  const int G = h_q / h_kv;
+  const int s = q_seq[i];
+  const int L = seq_len[s];
+  const int64_t row0 = seq_row0[s];
+  const int cnt = max(0, (int)min((int64_t)n_sel[i], sel_ld));
+  const int r_begin = split * rows_per_split;
+  const int r_end = min(cnt, r_begin + rows_per_split);
+  const int32_t* list = sel + (int64_t)i * sel_ld;
+  const T* qg = q + ((int64_t)i * h_q + (int64_t)g * G) * d_kq;
+  if (tid < 16) {
+    m_s[tid] = -INFINITY;
+    l_s[tid] = 0.f;
+  }
+  float acc[ACC];
+#pragma unroll
+  for (int a = 0; a < ACC; ++a) acc[a] = 0.f;
+
+  for (int r0 = r_begin; r0 < r_end; r0 += kRowTile) {
+    __syncthreads();
+    if (tid < kRowTile) rows[tid] = tile_row(list, r0 + tid, r_end, L, row0);
+    __syncthreads();
+    for (int e = tid; e < G * kRowTile; e += 256) {
+      const int h = e / kRowTile, r = e % kRowTile;
+      const int64_t row = rows[r];
+      float xv = -INFINITY;
+      if (row >= 0) {
+        const T* kr = k + row * k_ld + (int64_t)g * k_hs;
+        const T* qr = qg + (int64_t)h * d_kq;
+        float dot = 0.f;
+        for (int d = 0; d < d_kq; ++d) dot += (float)qr[d] * (float)kr[d];
+        xv = dot * scale_log2;
+      }
+      p[h][r] = xv;
+    }
+    __syncthreads();
+    if (tid < G) {
+      const int h = tid;
+      float mx = -INFINITY;
+      for (int r = 0; r < kRowTile; ++r) mx = fmaxf(mx, p[h][r]);
+      const float m_new = fmaxf(m_s[h], mx);
+      const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_s[h] - m_new);
+      float sum = 0.f;
+      for (int r = 0; r < kRowTile; ++r) {
+        const float pr = (p[h][r] == -INFINITY) ? 0.f : fast_exp2(p[h][r] - m_new);
+        p[h][r] = pr;
+        sum += pr;
+      }
+      l_s[h] = l_s[h] * alpha + sum;
+      m_s[h] = m_new;
+      a_s[h] = alpha;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int a = 0; a < ACC; ++a) {
+      const int e = tid + 256 * a;
+      if (e < G * d_v) {
+        const int h = e / d_v, dv = e % d_v;
+        float o = acc[a] * a_s[h];
+        for (int r = 0; r < kRowTile; ++r) {
+          const int64_t row = rows[r];
+          if (row >= 0) o += p[h][r] * (float)v[row * v_ld + (int64_t)g * v_hs + dv];
+        }
+        acc[a] = o;
+      }
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int a = 0; a < ACC; ++a) {
+    const int e = tid + 256 * a;
+    if (e < G * d_v) {
+      const int h = e / d_v, dv = e % d_v;
+      const int64_t qh = (int64_t)i * h_q + (int64_t)g * G + h;
+      if (n_split == 1) {
+        out[qh * d_v + dv] = l_s[h] > 0.f ? acc[a] / l_s[h] : 0.f;
+      } else {
+        ws_o[(qh * n_split + split) * d_v + dv] = acc[a];
+      }
+    }
+  }
+  if (n_split > 1 && tid < G) {
+    const int64_t qh = (int64_t)i * h_q + (int64_t)g * G + tid;
+    ws_ml[(qh * n_split + split) * 2 + 0] = m_s[tid];
+    ws_ml[(qh * n_split + split) * 2 + 1] = l_s[tid];
+  }
+}
+
+// ------------------------------------------------------------------------- combine
+
+// out[qh][dv] = sum_s 2^(m_s - M) o_s[dv] / sum_s 2^(m_s - M) l_s, M = max_s m_s.
+__global__ void __launch_bounds__(256)
+fwd_combine_kernel(const float* __restrict__ ws_o, const float* __restrict__ ws_ml, int n_split, int d_v,
+                   float* __restrict__ out) {
+  extern __shared__ float wsh[];                     // n_split weights
+  const int64_t qh = blockIdx.x;
+  const float* ml = ws_ml + qh * n_split * 2;
+  __shared__ float inv_l;
+  if (threadIdx.x == 0) {
+    float M = -INFINITY;
+    for (int s = 0; s < n_split; ++s) M = fmaxf(M, ml[2 * s]);
+    float L = 0.f;
+    for (int s = 0; s < n_split; ++s) {
+      const float w = (ml[2 * s] == -INFINITY) ? 0.f : fast_exp2(ml[2 * s] - M);
+      wsh[s] = w;
+      L += w * ml[2 * s + 1];
+    }
+    inv_l = L > 0.f ? 1.f / L : 0.f;
+  }
+  __syncthreads();
+  for (int dv = threadIdx.x; dv < d_v; dv += blockDim.x) {
+    float acc = 0.f;
+    for (int s = 0; s < n_split; ++s) acc += wsh[s] * ws_o[(qh * n_split + s) * d_v + dv];
+    out[qh * d_v + dv] = acc * inv_l;
+  }
+}
+
+// ---------------------------------------------------------------------------- host
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+static int fwd_cap(const sa_dims& d) { return d.top_k + d.compress_ratio - 1; }
+
+FwdPlan plan_fwd(const sa_dims& d, int n_q) {
+  FwdPlan p{};
+  const int cap = fwd_cap(d);
+  const long long units = (long long)n_q * d.h_kv;
+  // Aim at about 512 workgroups; never split below 64 rows.
+  long long want = units > 0 ? (512 + units - 1) / units : 1;
+  const long long max_split = (cap + 63) / 64;
+  if (want > max_split) want = max_split;
+  if (want < 1) want = 1;
+  int rps = (int)((cap + want - 1) / want);
+  rps = (rps + kRowTile - 1) / kRowTile * kRowTile;
+  p.rows_per_split = rps;
+  p.n_split = (cap + rps - 1) / rps;
+  p.ws_bytes = p.n_split > 1 ? (size_t)n_q * d.h_q * p.n_split * ((size_t)d.d_v + 2) * sizeof(float) : 0;
+  return p;
+}
+
+bool fwd_uses_mfma(const sa_dims& d, const CacheArgs& c, const void* q) {
+  if (d.dtype != SA_F16 && d.dtype != SA_BF16) return false;
+  const int G = d.h_q / d.h_kv;
+  if (G > 16) return false;
+  const bool shape = (d.d_kq == 576 && d.d_v == 512) || (d.d_kq == 512 && d.d_v == 512) ||
+                     (d.d_kq == 256 && d.d_v == 256) || (d.d_kq == 128 && d.d_v == 128);
+  if (!shape) return false;
+  const bool alias = c.v == c.k && c.v_ld == c.k_ld && c.v_hs == c.k_hs;
+  if (c.k_ld % 8 || c.k_hs % 8 || !aligned16(c.k) || !aligned16(q)) return false;
+  if (!alias && (c.v_ld % 8 || c.v_hs % 8 || !aligned16(c.v))) return false;
+  return true;
+}
+
+template <typename T, int DKQ, int DV, bool ALIAS>
+static void launch_mfma_t(const sa_dims& d, const CacheArgs& c, const void* q, const int32_t* q_seq,
+                          const int32_t* sel, int64_t sel_ld, const int32_t* n_sel, int n_q, float scale_log2,
+                          float* out, float* ws_o, float* ws_ml, const FwdPlan& plan, hipStream_t stream) {
+  dim3 grid(plan.n_split, n_q * d.h_kv);
+  hipLaunchKernelGGL((fwd_mfma_kernel<T, DKQ, DV, ALIAS>), grid, dim3(256), 0, stream, (const T*)q, (const T*)c.k,
+                     c.k_ld, c.k_hs, (const T*)c.v, c.v_ld, c.v_hs, c.seq_row0, c.seq_len, q_seq, sel, sel_ld, n_sel,
+                     d.h_q, d.h_kv, scale_log2, plan.n_split, plan.rows_per_split, out, ws_o, ws_ml);
+}
+
+template <typename T>
+static void dispatch_mfma(const sa_dims& d, const CacheArgs& c, const void* q, const int32_t* q_seq,
+                          const int32_t* sel, int64_t sel_ld, const int32_t* n_sel, int n_q, float scale_log2,
+                          float* out, float* ws_o, float* ws_ml, const FwdPlan& plan, hipStream_t stream) {
+  const bool alias = c.v == c.k && c.v_ld == c.k_ld && c.v_hs == c.k_hs;
+#define SA_FWD_CASE(DKQ_, DV_)                                                                                  \
+  if (d.d_kq == DKQ_ && d.d_v == DV_) {                                                                          \
+    if (alias) launch_mfma_t<T, DKQ_, DV_, true>(d, c, q, q_seq, sel, sel_ld, n_sel, n_q, scale_log2, out, ws_o, \
+                                                 ws_ml, plan, stream);                                           \
+    else launch_mfma_t<T, DKQ_, DV_, false>(d, c, q, q_seq, sel, sel_ld, n_sel, n_q, scale_log2, out, ws_o,      \
+                                            ws_ml, plan, stream);                                                \
+    return;                                                                                                      \
+  }
+  SA_FWD_CASE(576, 512)
+  SA_FWD_CASE(512, 512)
+  SA_FWD_CASE(256, 256)
+  SA_FWD_CASE(128, 128)
+#undef SA_FWD_CASE
+}
+
+template <typename T>
+static void dispatch_valu(const sa_dims& d, const CacheArgs& c, const void* q, const int32_t* q_seq,
+                          const int32_t* sel, int64_t sel_ld, const int32_t* n_sel, int n_q, float scale_log2,
+                          float* out, float* ws_o, float* ws_ml, const FwdPlan& plan, hipStream_t stream) {
+  dim3 grid(plan.n_split, n_q * d.h_kv);
+  const int per = (d.h_q / d.h_kv) * d.d_v;
+#define SA_VALU_CASE(ACC_)                                                                                        \
+  if (per <= 256 * ACC_) {                                                                                        \
+    hipLaunchKernelGGL((fwd_valu_kernel<T, ACC_>), grid, dim3(256), 0, stream, (const T*)q, (const T*)c.k, c.k_ld, \
+                       c.k_hs, (const T*)c.v, c.v_ld, c.v_hs, c.seq_row0, c.seq_len, q_seq, sel, sel_ld, n_sel,    \
+                       d.h_q, d.h_kv, d.d_kq, d.d_v, scale_log2, plan.n_split, plan.rows_per_split, out, ws_o,     \
+                       ws_ml);                                                                                    \
+    return;                                                                                                       \
+  }
+  SA_VALU_CASE(4)
+  SA_VALU_CASE(16)
+  SA_VALU_CASE(64)
+#undef SA_VALU_CASE
+}
+
+hipError_t launch_fwd(const sa_dims& d, const CacheArgs& c, const void* q, const int32_t* q_seq, const int32_t* sel,
+                      int64_t sel_ld, const int32_t* n_sel, int n_q, float scale, float* out, void* ws,
+                      const FwdPlan& plan, hipStream_t stream) {
+  if (n_q == 0) return hipSuccess;
+  const float scale_log2 = scale * kLog2e;
+  float* ws_o = (float*)ws;
+  float* ws_ml = plan.n_split > 1 ? ws_o + (size_t)n_q * d.h_q * plan.n_split * d.d_v : nullptr;
+  if (fwd_uses_mfma(d, c, q)) {
+    if (d.dtype == SA_BF16) dispatch_mfma<bf16>(d, c, q, q_seq, sel, sel_ld, n_sel, n_q, scale_log2, out, ws_o, ws_ml, plan, stream);
+    else dispatch_mfma<f16>(d, c, q, q_seq, sel, sel_ld, n_sel, n_q, scale_log2, out, ws_o, ws_ml, plan, stream);
+  } else {
+    switch (d.dtype) {
+      case SA_F32: dispatch_valu<float>(d, c, q, q_seq, sel, sel_ld, n_sel, n_q, scale_log2, out, ws_o, ws_ml, plan, stream); break;
+      case SA_F16: dispatch_valu<f16>(d, c, q, q_seq, sel, sel_ld, n_sel, n_q, scale_log2, out, ws_o, ws_ml, plan, stream); break;
+      default: dispatch_valu<bf16>(d, c, q, q_seq, sel, sel_ld, n_sel, n_q, scale_log2, out, ws_o, ws_ml, plan, stream); break;
+    }
+  }
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || plan.n_split == 1) return err;
+  const size_t shm = (size_t)plan.n_split * sizeof(float);
+  hipLaunchKernelGGL(fwd_combine_kernel, dim3((unsigned)((size_t)n_q * d.h_q)), dim3(256), shm, stream, ws_o, ws_ml,
+                     plan.n_split, d.d_v, out);
+  return hipGetLastError();
+}
+
+}  // namespace sa

@@ -1,0 +1,209 @@
+// Indexer block scores: s[i][b] = sum_h max(0, qidx[i][h] . kpool[b]).
+//
+// The rectification is applied per head before the head sum (llama.cpp commit
+// "llama: QSA sparse attention for qwen4exp", the paragraph on the direct index
+// comparison against the reference implementation), and each query meets only its
+// own sequence's blocks ("qwen4exp: support a non-unified KV cache in QSA").
+//
+// MFMA path (f16 / bf16, h_idx a multiple of 32, d_idx in {64, 128, 256}): a wave
+// holds one query's indexer heads as the M operand of v_mfma_f32_32x32x16 in
+// registers (loaded once) and streams 32 pooled keys per tile as the N operand
+// straight from HBM -- each lane loads one key's contiguous half row, so no LDS is
+// needed.  The contraction index is permuted identically in both operands (lane half
+// hf, step s, slot j <-> dim hf*D/2 + s*8 + j), which leaves the dot products
+// unchanged.  The epilogue rectifies the 32x32 fp32 tile, sums the 16 rows a lane
+// holds, and adds the partner lane (lane ^ 32) that holds the other 16 rows of the
+// same block column.
+//
+// VALU path (any dtype or shape): the query's heads are staged in LDS as float and
+// each thread computes the rectified dot products of one block for a quarter of
+// the heads.
+#include "sa_common.hpp"
+#include "sa_launch.hpp"
+
+namespace sa {
+
+// ----------------------------------------------------------------------------- MFMA
+
+template <typename T>
+__device__ __forceinline__ f32x16 mfma32x32x16(const typename vec8<T>::type& a, const typename vec8<T>::type& b,
+                                               const f32x16& c);
+template <>
+__device__ __forceinline__ f32x16 mfma32x32x16<bf16>(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+template <>
+__device__ __forceinline__ f32x16 mfma32x32x16<f16>(const f16x8& a, const f16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+constexpr int kScoreWaves = 4;        // waves per workgroup
+constexpr int kScoreTile = 32;        // blocks per wave tile (MFMA N)
+
+// grid = (ceil(max_blocks / (4 * 32)), n_q); wave w of workgroup x scores blocks
+// [(x*4 + w) * 32, +32) of query blockIdx.y.
+template <typename T, int MT, int D>
+__global__ void __launch_bounds__(256)
+score_mfma_kernel(const T* __restrict__ qidx, const T* __restrict__ kpool, int64_t kpool_ld,
+                  const int64_t* __restrict__ seq_blk0, const int32_t* __restrict__ seq_len,
+                  const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos, int c,
+                  float* __restrict__ scores, int64_t scores_ld) {
+  typedef typename vec8<T>::type V8;
+  constexpr int KS = D / 16;          // MFMA steps over the indexer dim (8 per lane half)
+  const int i = blockIdx.y;
+  const int s = q_seq[i];
+  const int nb = visible_tokens(seq_len[s], q_pos[i]) / c;
+  const int wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  const int b_base = (blockIdx.x * kScoreWaves + wave) * kScoreTile;
+  if (b_base >= nb) return;
+  const int n = lane & 31;
+  const int hf = lane >> 5;
+
+  // Issue the key loads first: one 16-byte slice per step of this lane's half row.
+  const int b = b_base + n;
+  const bool valid = b < nb;
+  V8 kb[KS];
+  const T* krow = kpool + (seq_blk0[s] + (valid ? b : 0)) * kpool_ld + hf * (D / 2);
+#pragma unroll
+  for (int st = 0; st < KS; ++st) {
+    kb[st] = valid ? *reinterpret_cast<const V8*>(krow + st * 8) : V8{};
+  }
+  // Indexer query heads mt*32 + n, same dim slices.
+  const T* qrow = qidx + (int64_t)i * (MT * 32) * D + (int64_t)n * D + hf * (D / 2);
+  V8 qa[MT][KS];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int st = 0; st < KS; ++st) qa[mt][st] = *reinterpret_cast<const V8*>(qrow + (int64_t)mt * 32 * D + st * 8);
+
+  float sum = 0.f;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    f32x16 acc = {};
+#pragma unroll
+    for (int st = 0; st < KS; ++st) acc = mfma32x32x16<T>(qa[mt][st], kb[st], acc);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sum += fmaxf(acc[r], 0.f);
+  }
+  sum += __shfl_xor(sum, 32);
+  if (hf == 0 && valid) scores[(int64_t)i * scores_ld + b] = sum + 0.0f;  // +0.0 turns -0.0 into +0.0
+}
+
+// ----------------------------------------------------------------------------- VALU
+
+constexpr int kValuBlocks = 64;       // blocks per workgroup
+constexpr int kValuQFloats = 8192;    // query floats staged in LDS per pass
+
+template <typename T>
+__global__ void __launch_bounds__(256)
+score_valu_kernel(const T* __restrict__ qidx, const T* __restrict__ kpool, int64_t kpool_ld,
+                  const int64_t* __restrict__ seq_blk0, const int32_t* __restrict__ seq_len,
+                  const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos, int c, int h_idx, int d_idx,
+                  float* __restrict__ scores, int64_t scores_ld) {
+  __shared__ float sq[kValuQFloats];
+  __shared__ float part[4][kValuBlocks];
+  const int i = blockIdx.y;
+  const int s = q_seq[i];
+  const int nb = visible_tokens(seq_len[s], q_pos[i]) / c;
+  const int b0 = blockIdx.x * kValuBlocks;
+  if (b0 >= nb) return;
+  const int lb = threadIdx.x % kValuBlocks;
+  const int hg = threadIdx.x / kValuBlocks;
+  const int b = b0 + lb;
+  const T* krow = kpool + (seq_blk0[s] + (b < nb ? b : 0)) * kpool_ld;
+  const T* q = qidx + (int64_t)i * h_idx * d_idx;
+  const int heads_per_pass = kValuQFloats / d_idx;
+  float sum = 0.f;
+  for (int h0 = 0; h0 < h_idx; h0 += heads_per_pass) {
+    const int hn = min(heads_per_pass, h_idx - h0);
+    __syncthreads();
+    for (int e = threadIdx.x; e < hn * d_idx; e += blockDim.x) sq[e] = (float)q[(int64_t)h0 * d_idx + e];
+    __syncthreads();
+    if (b < nb) {
+      for (int h = hg; h < hn; h += 4) {
+        float dot = 0.f;
+        for (int d = 0; d < d_idx; ++d) dot += sq[h * d_idx + d] * (float)krow[d];
+        sum += fmaxf(dot, 0.f);
+      }
+    }
+  }
+  part[hg][lb] = sum;
+  __syncthreads();
+  if (hg == 0 && b < nb) {
+    scores[(int64_t)i * scores_ld + b] = part[0][lb] + part[1][lb] + part[2][lb] + part[3][lb] + 0.0f;
+  }
+}
+
+// ----------------------------------------------------------------------------- host
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool score_uses_mfma(const sa_dims& d, const CacheArgs& c, const void* qidx) {
+  if (d.dtype != SA_F16 && d.dtype != SA_BF16) return false;
+  if (d.h_idx % 32 != 0 || d.h_idx > 128) return false;
+  if (d.d_idx != 64 && d.d_idx != 128 && d.d_idx != 256) return false;
+  return c.kpool_ld % 8 == 0 && aligned16(c.kpool) && aligned16(qidx);
+}
+
+template <typename T, int MT, int D>
+static void launch_mfma(const sa_dims& d, const CacheArgs& c, const void* qidx, const int32_t* q_seq,
+                        const int32_t* q_pos, int n_q, float* scores, int64_t scores_ld, hipStream_t stream) {
+  const long long max_blocks = (long long)c.max_len / d.compress_ratio;
+  const long long per_wg = kScoreWaves * kScoreTile;
+  dim3 grid((unsigned)((max_blocks + per_wg - 1) / per_wg), (unsigned)n_q);
+  if (grid.x == 0) return;
+  hipLaunchKernelGGL((score_mfma_kernel<T, MT, D>), grid, dim3(256), 0, stream, (const T*)qidx,
+                     (const T*)c.kpool, c.kpool_ld, c.seq_blk0, c.seq_len, q_seq, q_pos, d.compress_ratio, scores,
+                     scores_ld);
+}
+
+template <typename T, int MT>
+static void dispatch_mfma_d(const sa_dims& d, const CacheArgs& c, const void* qidx, const int32_t* q_seq,
+                            const int32_t* q_pos, int n_q, float* scores, int64_t scores_ld, hipStream_t stream) {
+  switch (d.d_idx) {
+    case 64: launch_mfma<T, MT, 64>(d, c, qidx, q_seq, q_pos, n_q, scores, scores_ld, stream); break;
+    case 128: launch_mfma<T, MT, 128>(d, c, qidx, q_seq, q_pos, n_q, scores, scores_ld, stream); break;
+    default: launch_mfma<T, MT, 256>(d, c, qidx, q_seq, q_pos, n_q, scores, scores_ld, stream); break;
+  }
+}
+
+template <typename T>
+static void dispatch_mfma(const sa_dims& d, const CacheArgs& c, const void* qidx, const int32_t* q_seq,
+                          const int32_t* q_pos, int n_q, float* scores, int64_t scores_ld, hipStream_t stream) {
+  switch (d.h_idx / 32) {
+    case 1: dispatch_mfma_d<T, 1>(d, c, qidx, q_seq, q_pos, n_q, scores, scores_ld, stream); break;
+    case 2: dispatch_mfma_d<T, 2>(d, c, qidx, q_seq, q_pos, n_q, scores, scores_ld, stream); break;
+    case 3: dispatch_mfma_d<T, 3>(d, c, qidx, q_seq, q_pos, n_q, scores, scores_ld, stream); break;
+    default: dispatch_mfma_d<T, 4>(d, c, qidx, q_seq, q_pos, n_q, scores, scores_ld, stream); break;
+  }
+}
+
+template <typename T>
+static void launch_valu(const sa_dims& d, const CacheArgs& c, const void* qidx, const int32_t* q_seq,
+                        const int32_t* q_pos, int n_q, float* scores, int64_t scores_ld, hipStream_t stream) {
+  const long long max_blocks = (long long)c.max_len / d.compress_ratio;
+  dim3 grid((unsigned)((max_blocks + kValuBlocks - 1) / kValuBlocks), (unsigned)n_q);
+  if (grid.x == 0) return;
+  hipLaunchKernelGGL(score_valu_kernel<T>, grid, dim3(256), 0, stream, (const T*)qidx, (const T*)c.kpool,
+                     c.kpool_ld, c.seq_blk0, c.seq_len, q_seq, q_pos, d.compress_ratio, d.h_idx, d.d_idx, scores,
+                     scores_ld);
+}
+
+hipError_t launch_score(const sa_dims& d, const CacheArgs& c, const void* qidx, const int32_t* q_seq,
+                        const int32_t* q_pos, int n_q, float* scores, int64_t scores_ld, hipStream_t stream) {
+  if (n_q == 0) return hipSuccess;
+  if (score_uses_mfma(d, c, qidx)) {
+    if (d.dtype == SA_BF16) dispatch_mfma<bf16>(d, c, qidx, q_seq, q_pos, n_q, scores, scores_ld, stream);
+    else dispatch_mfma<f16>(d, c, qidx, q_seq, q_pos, n_q, scores, scores_ld, stream);
+  } else {
+    switch (d.dtype) {
+      case SA_F32: launch_valu<float>(d, c, qidx, q_seq, q_pos, n_q, scores, scores_ld, stream); break;
+      case SA_F16: launch_valu<f16>(d, c, qidx, q_seq, q_pos, n_q, scores, scores_ld, stream); break;
+      default: launch_valu<bf16>(d, c, qidx, q_seq, q_pos, n_q, scores, scores_ld, stream); break;
+    }
+  }
+  return hipGetLastError();
+}
+
+}  // namespace sa

@@ -1,0 +1,98 @@
+"""Device-side buffers for one layer, and the four calls on them.
+
+Plumbing for tests, the smoke check and the benchmark: torch allocates the device
+memory and supplies the stream; every step runs in libsparse_attn through the
+ctypes binding.  Nothing here computes any part of the method.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import sparse_attn as sa
+from .datagen import Case
+
+
+def _dev(x: np.ndarray, dtype: torch.dtype, device) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(x)).to(dtype).to(device)
+
+
+class DeviceLayer:
+    """One layer's caches and a batch of query tokens on the GPU."""
+
+    def __init__(self, case: Case, device="cuda", max_len: Optional[int] = None):
+        d = case.dims
+        self.case = case
+        self.device = torch.device(device)
+        self.dims = sa.make_dims(d.h_q, d.h_kv, d.d_kq, d.d_v, d.h_idx, d.d_idx, d.compress_ratio, d.top_k, d.dtype)
+        dt = sa.TORCH_DTYPE[d.dtype]
+        c = d.compress_ratio
+        self.k = _dev(case.k, dt, device)                                     # [rows, h_kv, d_kq]
+        self.alias = case.v is None
+        self.v = self.k if self.alias else _dev(case.v, dt, device)          # [rows, h_kv, d_v]
+        self.kidx = _dev(case.kidx, dt, device)                               # [rows, d_idx]
+        self.kpool = torch.zeros((case.rows // c, d.d_idx), dtype=dt, device=device)
+        self.seq_row0 = torch.from_numpy(case.row0.astype(np.int64)).to(device)
+        self.seq_blk0 = torch.from_numpy(case.blk0.astype(np.int64)).to(device)
+        self.seq_len = torch.from_numpy(case.seq_len.astype(np.int32)).to(device)
+        self.q = _dev(case.q, dt, device)
+        self.qidx = _dev(case.qidx, dt, device)
+        self.q_seq = torch.from_numpy(case.q_seq.astype(np.int32)).to(device)
+        self.q_pos = torch.from_numpy(case.q_pos.astype(np.int32)).to(device)
+        self.n_q = case.n_q
+        self.max_len = int(max_len if max_len is not None else max(int(case.seq_cap.max()), 1))
+        self.scores_ld = max(1, self.max_len // c)
+        self.sel_ld = d.top_k + c - 1
+        self.scores = torch.zeros((self.n_q, self.scores_ld), dtype=torch.float32, device=device)
+        self.sel = torch.full((self.n_q, self.sel_ld), -7, dtype=torch.int32, device=device)
+        self.n_sel = torch.zeros((self.n_q,), dtype=torch.int32, device=device)
+        self.out = torch.zeros((self.n_q, d.h_q, d.d_v), dtype=torch.float32, device=device)
+        self.ws_bytes = sa.sparse_attn_workspace_bytes(self.dims, self.n_q)
+        self.ws = torch.empty((max(self.ws_bytes, 16),), dtype=torch.uint8, device=device)
+        self.n_pooled = torch.zeros((case.n_seq,), dtype=torch.int32, device=device)
+        self.scale = case.scale
+        self.cache = self._make_cache(self.k, self.v, self.kidx, self.kpool)
+
+    def _make_cache(self, k, v, kidx, kpool) -> sa.Cache:
+        d = self.case.dims
+        return sa.Cache(seq_row0=self.seq_row0, seq_blk0=self.seq_blk0, seq_len=self.seq_len, max_len=self.max_len,
+                        k=k, k_ld=d.h_kv * d.d_kq, k_head_stride=d.d_kq,
+                        v=v, v_ld=(d.h_kv * d.d_kq if self.alias else d.h_kv * d.d_v),
+                        v_head_stride=(d.d_kq if self.alias else d.d_v),
+                        kidx=kidx, kidx_ld=d.d_idx, kpool=kpool, kpool_ld=d.d_idx)
+
+    # ------------------------------------------------------------------ the calls
+    def pool(self, max_new_blocks: int = 2 ** 31 - 1, n_in=None, n_out=None, stream=None) -> None:
+        n_in = self.n_pooled if n_in is None else n_in
+        n_out = self.n_pooled if n_out is None else n_out
+        sa.sparse_attn_pool(self.dims, self.cache, n_in, n_out, max_new_blocks, stream)
+
+    def score(self, stream=None) -> None:
+        sa.sparse_attn_score(self.dims, self.cache, self.qidx, self.q_seq, self.q_pos, self.n_q, self.scores,
+                             self.scores_ld, stream)
+
+    def select(self, scores: Optional[torch.Tensor] = None, stream=None) -> None:
+        scores = self.scores if scores is None else scores
+        sa.sparse_attn_select(self.dims, self.cache, scores, scores.shape[1], self.q_seq, self.q_pos, self.n_q,
+                              self.sel, self.sel_ld, self.n_sel, self.ws, self.ws_bytes, stream)
+
+    def fwd(self, sel: Optional[torch.Tensor] = None, n_sel: Optional[torch.Tensor] = None, stream=None) -> None:
+        sel = self.sel if sel is None else sel
+        n_sel = self.n_sel if n_sel is None else n_sel
+        sa.sparse_attn_fwd(self.dims, self.cache, self.q, self.q_seq, sel, sel.shape[1], n_sel, self.n_q,
+                           self.scale, self.out, self.ws, self.ws_bytes, stream)
+
+    def step(self, stream=None) -> None:
+        """One pass of the whole path: pool what is new, score, select, attend."""
+        self.pool(stream=stream)
+        self.score(stream)
+        self.select(stream=stream)
+        self.fwd(stream=stream)
+
+    # ------------------------------------------------------------------ readback
+    def selections(self) -> list[np.ndarray]:
+        sel = self.sel.cpu().numpy()
+        n = self.n_sel.cpu().numpy()
+        return [sel[i, : n[i]].astype(np.int64) for i in range(self.n_q)]

@@ -1,0 +1,249 @@
+"""GPU parity: every step of the HIP library against the CPU oracle (needs an MI355X).
+
+Each case is run end to end (pool -> score -> select -> fwd) through the C ABI and
+checked step by step; the select and fwd kernels are also fed the oracle's own
+scores / selection, where the comparison must be exact (selection) or within the
+output tolerance (attention).  See tests/parity.py for the tolerances.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import parity
+from indexer_top_block_amd import datagen
+from indexer_top_block_amd.device import DeviceLayer
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def run_and_check(case, queries=None, components=True, gpu_lib=None):
+    """Run the whole path on the GPU and compare with the oracle on `queries`."""
+    say(f"[parity] {case.name}: n_q={case.n_q} seqs={case.n_seq} dims={case.dims}")
+    layer = DeviceLayer(case)
+    layer.pool()
+    layer.score()
+    layer.select()
+    layer.fwd()
+    torch.cuda.synchronize()
+    pools = oracle.SequencePools(case)
+    n_off = parity.check_pool(layer, case, pools)
+    queries = list(range(case.n_q)) if queries is None else list(queries)
+    gpu_scores = layer.scores.cpu().numpy()
+    gpu_sel = layer.selections()
+    gpu_out = layer.out.cpu().numpy()
+    dt = case.dims.dtype
+    results = {}
+    kinds = {"exact": 0, "near-tie": 0}
+    worst = 0.0
+    for qi in queries:
+        res = oracle.run_query(case, qi, pools)
+        results[qi] = res
+        parity.check_scores(gpu_scores[qi], case, qi, res, pools)
+        kind = parity.compare_selection(gpu_sel[qi], res, case)
+        kinds[kind] += 1
+        want = res["out"] if kind == "exact" else oracle.run_query(case, qi, pools, positions=gpu_sel[qi])["out"]
+        worst = max(worst, parity.check_out(gpu_out[qi], want, dt, f"{case.name} q{qi} end-to-end"))
+    if components:
+        # The select kernel on the oracle's float32 scores: exactly the oracle's list.
+        sc = parity.upload_scores(layer, [results[qi]["scores32"] if qi in results else np.zeros(0, np.float32)
+                                          for qi in range(case.n_q)])
+        layer.select(scores=sc)
+        torch.cuda.synchronize()
+        sel2 = layer.selections()
+        for qi in queries:
+            assert np.array_equal(sel2[qi], results[qi]["positions"]), f"q{qi}: select on oracle scores differs"
+        # The attention kernel on the oracle's selection.
+        sel, n_sel = parity.upload_selection(layer, [results[qi]["positions"] if qi in results
+                                                     else np.zeros(0, np.int64) for qi in range(case.n_q)])
+        layer.fwd(sel, n_sel)
+        torch.cuda.synchronize()
+        out2 = layer.out.cpu().numpy()
+        for qi in queries:
+            worst = max(worst, parity.check_out(out2[qi], results[qi]["out"], dt, f"{case.name} q{qi} fwd"))
+    say(f"[parity] {case.name}: ok  pooled-ulp-diffs={n_off} selections={kinds} max-abs={worst:.3g}")
+    return layer, results
+
+
+def dims(**kw):
+    base = dict(h_q=16, h_kv=1, d_kq=576, d_v=512, h_idx=64, d_idx=128, compress_ratio=4, top_k=256, dtype="bf16")
+    base.update(kw)
+    return datagen.Dims(**base)
+
+
+# ------------------------------------------------------------------ small cases
+
+def test_tiny_decode_fp32(gpu_lib):
+    run_and_check(datagen.make_workload(1))
+
+
+def test_mla_bf16_decode_and_prefill_positions(gpu_lib):
+    # positions chosen around the edges: tail only, one block, dense through
+    # top_k + c - 1 = 259 visible tokens, first sparse at 260, and a decode token
+    L = 3001
+    pos = [L, 0, 2, 3, 258, 259, 1500, 2998, 2999, 3000]
+    case = datagen.make_case("mla_bf16_small", dims(), [L], [0] * len(pos), pos, seed=0, case_id=201,
+                             std="inv_sqrt_dim", v_separate=False)
+    run_and_check(case)
+
+
+def test_gqa_f16_ragged_sequences(gpu_lib):
+    lens = [4093, 1, 700, 2051, 2052, 513, 9000]
+    d = dims(h_q=8, d_kq=512, d_v=512, h_idx=32, top_k=512, dtype="f16")
+    case = datagen.make_case("gqa_f16_ragged", d, lens, list(range(len(lens))), lens, seed=0, case_id=202, std=0.5,
+                             v_separate=True)
+    run_and_check(case)
+
+
+def test_pages_sparse_fa_shapes(gpu_lib):
+    # the (DKQ, DV, heads per KV head, n_kv_max) cases of the pages' op tests, at
+    # their K length of 4096, with token-level selection (c = 1, top_k = n_kv_max)
+    shapes = json.load(open(os.path.join(GOLDEN, "qsa_page_facts.json")))["sparse_fa_test_shapes"]["cases"]
+    for j, sh in enumerate(shapes):
+        d = dims(h_q=sh["heads_per_kv"], d_kq=sh["d_kq"], d_v=sh["d_v"], h_idx=32, compress_ratio=1,
+                 top_k=sh["n_kv_max"], dtype="f16")
+        alias = sh["d_kq"] == 576
+        case = datagen.make_case(f"pages_shape_{j}", d, [4096], [0, 0, 0], [4096, 100, 3000], seed=0,
+                                 case_id=210 + j, std="inv_sqrt_dim", v_separate=not alias)
+        run_and_check(case)
+
+
+def test_two_kv_heads_and_generic_paths(gpu_lib):
+    # h_kv = 2 (4 query heads per KV head), an indexer too narrow for MFMA (d_idx 48,
+    # 20 heads) and a head size the MFMA attention does not cover (192 / 128)
+    d = dims(h_q=8, h_kv=2, d_kq=192, d_v=128, h_idx=20, d_idx=48, compress_ratio=3, top_k=96, dtype="bf16")
+    case = datagen.make_case("generic_bf16", d, [1000, 333], [0, 1, 0], [1000, 333, 500], seed=0, case_id=220,
+                             std=1.0, v_separate=True)
+    run_and_check(case)
+    d = dims(h_q=8, h_kv=2, d_kq=128, d_v=128, h_idx=32, d_idx=64, compress_ratio=4, top_k=64, dtype="f16")
+    case = datagen.make_case("two_kv_heads_f16", d, [777], [0, 0], [777, 401], seed=0, case_id=221, std=1.0,
+                             v_separate=True)
+    run_and_check(case)
+
+
+def test_ties_at_the_cut(gpu_lib):
+    # one indexer head: about half of the blocks score exactly +0 and the budget
+    # reaches into them, so the cut is decided by the lower-index rule
+    d = dims(h_q=16, d_kq=128, d_v=128, h_idx=1, d_idx=64, compress_ratio=4, top_k=2400, dtype="bf16")
+    case = datagen.make_case("ties_zero_scores", d, [4000], [0], [4000], seed=0, case_id=230, std=1.0,
+                             v_separate=True)
+    _, res = run_and_check(case)
+    s = res[0]["scores32"]
+    k_blk = d.top_k // d.compress_ratio
+    assert np.sort(s)[::-1][k_blk - 1] == 0.0 and np.count_nonzero(s == 0.0) > 100
+    # identical pooled keys in runs of blocks: exact ties at positive scores (MFMA path)
+    d = dims(h_q=16, d_kq=576, d_v=512, h_idx=32, d_idx=128, compress_ratio=4, top_k=256, dtype="bf16")
+    case = datagen.make_case("ties_repeated_keys", d, [4096], [0], [4096], seed=0, case_id=231, std="inv_sqrt_dim",
+                             v_separate=False)
+    c = d.compress_ratio
+    # every block of 8 consecutive blocks gets the raw keys of the first block of its run
+    blocks = case.kidx[: 4096].reshape(-1, c, d.d_idx)
+    blocks[:] = np.repeat(blocks[::8], 8, axis=0)[: blocks.shape[0]]
+    _, res = run_and_check(case)
+    s = res[0]["scores32"]
+    assert len(np.unique(s)) * 8 == len(s)
+
+
+def test_select_streams_long_score_rows(gpu_lib):
+    # more blocks per query than one workgroup holds in registers: chunked passes
+    d = dims(h_q=16, d_kq=128, d_v=128, h_idx=32, d_idx=64, compress_ratio=1, top_k=2048, dtype="bf16")
+    case = datagen.make_case("select_stream_wide", d, [40000], [0], [40000], seed=0, case_id=240, std=1.0,
+                             v_separate=True)
+    run_and_check(case)
+    pos = [20000 - 1 - 97 * j for j in range(80)]                 # 80 queries -> narrow workgroups
+    case = datagen.make_case("select_stream_narrow", d, [20000], [0] * 80, pos, seed=0, case_id=241, std=1.0,
+                             v_separate=True)
+    run_and_check(case, queries=[0, 1, 40, 79])
+
+
+def test_max_list_capacity(gpu_lib):
+    # the largest list the library accepts: top_k + c - 1 = 65536
+    d = dims(h_q=16, d_kq=128, d_v=128, h_idx=32, d_idx=64, compress_ratio=1, top_k=65536, dtype="bf16")
+    case = datagen.make_case("max_capacity", d, [70000], [0, 0], [70000, 50000], seed=0, case_id=250, std=1.0,
+                             v_separate=False)
+    run_and_check(case)
+
+
+def test_empty_and_degenerate_queries(gpu_lib):
+    d = dims(h_q=16, d_kq=576, d_v=512, h_idx=64, d_idx=128, compress_ratio=4, top_k=256, dtype="bf16")
+    # q_pos -1 (nothing visible), a zero-length sequence, a query before the cache end
+    case = datagen.make_case("degenerate", d, [600, 0], [0, 1, 0, 0], [-1, 0, 0, 599], seed=0, case_id=260,
+                             std="inv_sqrt_dim", v_separate=False)
+    layer, res = run_and_check(case)
+    out = layer.out.cpu().numpy()
+    assert np.all(out[0] == 0) and np.all(out[1] == 0)
+    assert layer.n_sel.cpu().numpy().tolist()[:2] == [0, 0]
+    assert np.all(layer.sel.cpu().numpy()[:2] == -1)
+
+
+# --------------------------------------------------------------- incremental pool
+
+def test_incremental_pool_matches_one_shot(gpu_lib):
+    d = dims(h_q=16, d_kq=576, d_v=512, h_idx=64, d_idx=128, compress_ratio=4, top_k=256, dtype="bf16")
+    lens = [1000, 37, 4096]
+    case = datagen.make_case("pool_incremental", d, lens, [0, 1, 2], lens, seed=0, case_id=270, std="inv_sqrt_dim",
+                             v_separate=False)
+    say("[parity] pool_incremental")
+    one = DeviceLayer(case)
+    one.pool()
+    inc = DeviceLayer(case)
+    # grow the sequences token by token in a few strides, pooling at most 3 new blocks per call
+    full = inc.seq_len.clone()
+    for L in list(range(0, 200, 7)) + [1000, 4096]:
+        inc.seq_len.copy_(torch.minimum(full, torch.full_like(full, L)))
+        for _ in range(200):
+            before = inc.n_pooled.clone()
+            inc.pool(max_new_blocks=3)
+            if torch.equal(before, inc.n_pooled):
+                break
+    inc.seq_len.copy_(full)
+    inc.pool(max_new_blocks=5)
+    # separate in / out arrays: the in-array is not touched
+    n_in = torch.zeros_like(inc.n_pooled)
+    n_out = torch.full_like(inc.n_pooled, -5)
+    inc.pool(max_new_blocks=0, n_in=n_in, n_out=n_out)
+    torch.cuda.synchronize()
+    assert n_in.cpu().tolist() == [0, 0, 0] and n_out.cpu().tolist() == [0, 0, 0]
+    want = [L // 4 for L in lens]
+    assert one.n_pooled.cpu().tolist() == want
+    for _ in range(4):
+        inc.pool(max_new_blocks=1000)
+    torch.cuda.synchronize()
+    assert inc.n_pooled.cpu().tolist() == want
+    for s in range(3):
+        b0 = int(case.blk0[s])
+        a = one.kpool[b0:b0 + want[s]]
+        b = inc.kpool[b0:b0 + want[s]]
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"sequence {s}: incremental != one-shot"
+    # a shrunken sequence reports its new block count
+    inc.seq_len.copy_(torch.tensor([10, 37, 4096], dtype=torch.int32, device=inc.device))
+    inc.pool(max_new_blocks=1)
+    torch.cuda.synchronize()
+    assert inc.n_pooled.cpu().tolist() == [2, 9, 1024]
+
+
+# ----------------------------------------------------------- full-size workloads
+
+@pytest.mark.parametrize("cfg,queries", [
+    (2, None),
+    (5, None),
+    (3, None),
+    (4, [0, 1, 2, 3, 511, 1024, 1500, 2046, 2047]),
+])
+def test_full_size_workload(gpu_lib, cfg, queries):
+    say(f"[parity] generating workload {cfg}: {datagen.WORKLOADS[cfg]}")
+    case = datagen.make_workload(cfg)
+    layer, res = run_and_check(case, queries=queries)
+    if cfg == 5:
+        kept = set((res[0]["positions"] // 4).tolist())
+        assert len(kept & set(case.planted_blocks.tolist())) >= 500   # planted blocks dominate the selection

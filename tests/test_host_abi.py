@@ -1,0 +1,130 @@
+"""The C ABI on the host (CPU only): the library loads, exports every function the
+header declares, and rejects bad arguments before making any HIP call."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from indexer_top_block_amd import sparse_attn as sa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sparse_attn.h")
+
+# Any non-zero value: validation never dereferences device pointers on the host.
+FAKE = 0x10000
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sparse_attn_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = sa.load()
+    declared = _declared_functions()
+    assert set(declared) == set(sa.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+    nm = subprocess.run(["nm", "-D", "--defined-only", sa.LIB_PATH], capture_output=True, text=True, check=True)
+    exported = set(re.findall(r"\bT (sparse_attn_\w+)$", nm.stdout, flags=re.M))
+    assert set(declared) <= exported
+
+
+def test_version_and_strerror():
+    assert "gfx950" in sa.sparse_attn_version()
+    for code in (0, -1, -2, -3, -4, -5, 7):
+        assert isinstance(sa.sparse_attn_strerror(code), str) and sa.sparse_attn_strerror(code)
+
+
+def _dims(**kw):
+    base = dict(h_q=16, h_kv=1, d_kq=576, d_v=512, h_idx=64, d_idx=128, compress_ratio=4, top_k=2048, dtype="bf16")
+    base.update(kw)
+    return sa.make_dims(**base)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(), dict(dtype="f32", h_q=8, d_kq=128, d_v=128, h_idx=4, d_idx=64, top_k=256),
+    dict(dtype="f16", h_q=8, d_kq=512, h_idx=32), dict(compress_ratio=1, top_k=1),
+    dict(h_q=32, h_kv=2), dict(compress_ratio=64, top_k=64 * 1024 - 64),
+])
+def test_check_dims_accepts(kw):
+    assert sa.sparse_attn_check_dims(_dims(**kw)) == sa.SA_OK
+
+
+@pytest.mark.parametrize("kw", [
+    dict(top_k=2050), dict(compress_ratio=0), dict(compress_ratio=-4), dict(top_k=0), dict(h_q=17),
+    dict(h_q=32, h_kv=1), dict(h_kv=0), dict(d_idx=100), dict(d_idx=0), dict(dtype=7), dict(h_idx=0),
+    dict(h_idx=129), dict(d_kq=1025), dict(d_v=0), dict(compress_ratio=65, top_k=65),
+    dict(compress_ratio=1, top_k=65537),
+])
+def test_check_dims_rejects(kw):
+    assert sa.sparse_attn_check_dims(_dims(**kw)) == sa.SA_ERR_DIMS
+
+
+def test_check_dims_null():
+    lib = sa.load()
+    assert lib.sparse_attn_check_dims(None) == sa.SA_ERR_NULL
+
+
+def test_workspace_bytes():
+    d = _dims()
+    # one decode token: split-KV partials (o, m, l) for 16 heads
+    ws = sa.sparse_attn_workspace_bytes(d, 1)
+    assert ws > 0 and ws % (16 * (512 + 2) * 4) == 0
+    # a prefill chunk runs unsplit and needs none
+    assert sa.sparse_attn_workspace_bytes(d, 2048) == 0
+    assert sa.sparse_attn_workspace_bytes(_dims(top_k=2050), 1) == 0
+
+
+def _cache(**kw):
+    base = dict(n_seq=1, max_len=4096, seq_row0=FAKE, seq_blk0=FAKE, seq_len=FAKE, k=FAKE, k_ld=576,
+                k_head_stride=576, v=FAKE, v_ld=576, v_head_stride=576, kidx=FAKE, kidx_ld=128, kpool=FAKE,
+                kpool_ld=128)
+    base.update(kw)
+    return sa.SaCache(**base)
+
+
+def _call(name, *args):
+    lib = sa.load()
+    return getattr(lib, name)(*args)
+
+
+def test_entry_points_reject_bad_arguments_before_any_launch():
+    d = ctypes.byref(_dims())
+    c = ctypes.byref(_cache())
+    # pool
+    assert _call("sparse_attn_pool", d, None, FAKE, FAKE, 1, None) == sa.SA_ERR_NULL
+    assert _call("sparse_attn_pool", d, c, None, FAKE, 1, None) == sa.SA_ERR_NULL
+    assert _call("sparse_attn_pool", d, c, FAKE, FAKE, -1, None) == sa.SA_ERR_ARG
+    assert _call("sparse_attn_pool", d, ctypes.byref(_cache(kidx_ld=64)), FAKE, FAKE, 1, None) == sa.SA_ERR_ARG
+    assert _call("sparse_attn_pool", d, ctypes.byref(_cache(n_seq=0)), FAKE, FAKE, 1, None) == sa.SA_ERR_ARG
+    assert _call("sparse_attn_pool", ctypes.byref(_dims(top_k=3)), c, FAKE, FAKE, 1, None) == sa.SA_ERR_DIMS
+    # score
+    assert _call("sparse_attn_score", d, c, None, FAKE, FAKE, 1, FAKE, 1024, None) == sa.SA_ERR_NULL
+    assert _call("sparse_attn_score", d, c, FAKE, FAKE, FAKE, -1, FAKE, 1024, None) == sa.SA_ERR_ARG
+    assert _call("sparse_attn_score", d, c, FAKE, FAKE, FAKE, 1, FAKE, 1023, None) == sa.SA_ERR_ARG
+    assert _call("sparse_attn_score", d, c, FAKE, FAKE, FAKE, 0, FAKE, 1024, None) == sa.SA_OK  # no-op
+    # select
+    assert _call("sparse_attn_select", d, c, FAKE, 1024, FAKE, FAKE, 1, FAKE, 2050, FAKE, None, 0, None) == sa.SA_ERR_ARG
+    assert _call("sparse_attn_select", d, c, FAKE, 1023, FAKE, FAKE, 1, FAKE, 2051, FAKE, None, 0, None) == sa.SA_ERR_ARG
+    assert _call("sparse_attn_select", d, c, FAKE, 1024, FAKE, FAKE, 1, FAKE, 2051, None, None, 0, None) == sa.SA_ERR_NULL
+    assert _call("sparse_attn_select", d, ctypes.byref(_cache(seq_len=None)), FAKE, 1024, FAKE, FAKE, 1, FAKE,
+                 2051, FAKE, None, 0, None) == sa.SA_ERR_NULL
+    # fwd
+    ws = sa.sparse_attn_workspace_bytes(_dims(), 1)
+    args = [d, c, FAKE, FAKE, FAKE, 2051, FAKE, 1, ctypes.c_float(0.04), FAKE]
+    assert _call("sparse_attn_fwd", *args, None, 0, None) == sa.SA_ERR_WORKSPACE
+    assert _call("sparse_attn_fwd", *args, FAKE, ws - 1, None) == sa.SA_ERR_WORKSPACE
+    assert _call("sparse_attn_fwd", d, c, None, FAKE, FAKE, 2051, FAKE, 1, ctypes.c_float(0.04), FAKE, FAKE, ws,
+                 None) == sa.SA_ERR_NULL
+    assert _call("sparse_attn_fwd", d, c, FAKE, FAKE, FAKE, 2051, FAKE, 1, ctypes.c_float(float("nan")), FAKE, FAKE,
+                 ws, None) == sa.SA_ERR_ARG
+    # V aliasing K may not be wider than K
+    bad = ctypes.byref(_dims(d_kq=512, d_v=576))
+    assert _call("sparse_attn_fwd", bad, ctypes.byref(_cache(k_ld=512, v_ld=512)), FAKE, FAKE, FAKE, 2051, FAKE, 1,
+                 ctypes.c_float(0.04), FAKE, FAKE, 1 << 30, None) == sa.SA_ERR_ARG
+    assert _call("sparse_attn_fwd", d, c, FAKE, FAKE, FAKE, 2051, FAKE, 0, ctypes.c_float(0.04), FAKE, None, 0,
+                 None) == sa.SA_OK  # no queries: nothing to do
