@@ -105,9 +105,12 @@ typedef struct {
  * top_k % c == 0; top_k + c - 1 <= 65536.  Makes no HIP call.                        */
 int sparse_attn_check_dims(const sa_dims* dims);
 
-/* Bytes of workspace that sparse_attn_select and sparse_attn_fwd need for n_q query
- * tokens of this layer (the two calls may share one buffer).  0 on bad dims.       */
-size_t sparse_attn_workspace_bytes(const sa_dims* dims, int32_t n_q);
+/* Bytes of device workspace that sparse_attn_select and sparse_attn_fwd need for n_q
+ * query tokens over caches whose sa_cache.max_len is max_len.  One buffer of this
+ * size serves both calls (each overwrites it; its contents need no initialisation
+ * and carry nothing between calls).  Returns 0 on bad arguments or when no
+ * workspace is needed.  Host only, no HIP call.                                    */
+size_t sparse_attn_workspace_bytes(const sa_dims* dims, int32_t n_q, int32_t max_len);
 
 /* Incremental block mean-pool (pages: the indexer cache holds raw keys because
  * pooling happens before the norm and the rotation; one pooled key per block of
@@ -147,9 +150,9 @@ int sparse_attn_score(const sa_dims* dims, const sa_cache* cache, const void* qi
  *   sel[i*sel_ld + j], n_sel[i] <= j < sel_ld = -1.
  * n_sel[i] = min(NB, K_blk)*c + tail <= top_k + c - 1 (the list cannot overflow).
  * Requires sel_ld >= top_k + c - 1 and scores_ld >= max_len / c.  Scores must not be
- * NaN.  ws: workspace of sparse_attn_workspace_bytes(dims, n_q) bytes (may be NULL
- * when that is 0).  Errors: SA_ERR_NULL, SA_ERR_DIMS, SA_ERR_ARG, SA_ERR_WORKSPACE,
- * SA_ERR_HIP.                                                                        */
+ * NaN.  ws: workspace of sparse_attn_workspace_bytes(dims, n_q, max_len) bytes (may
+ * be NULL when that is 0).  Errors: SA_ERR_NULL, SA_ERR_DIMS, SA_ERR_ARG,
+ * SA_ERR_WORKSPACE, SA_ERR_HIP.                                                      */
 int sparse_attn_select(const sa_dims* dims, const sa_cache* cache, const float* scores,
                        int64_t scores_ld, const int32_t* q_seq, const int32_t* q_pos, int32_t n_q,
                        int32_t* sel, int64_t sel_ld, int32_t* n_sel, void* ws, size_t ws_bytes,
@@ -163,7 +166,7 @@ int sparse_attn_select(const sa_dims* dims, const sa_cache* cache, const float* 
  *             0 <= sel[...] < seq_len[s] } (other entries are skipped), accumulated
  * in float32; out = 0 when the set is empty.  q is [n_q][h_q][d_kq] contiguous in
  * the cache dtype; out is [n_q][h_q][d_v] float32 contiguous.  ws: workspace of
- * sparse_attn_workspace_bytes(dims, n_q) bytes (split-KV partial results).
+ * sparse_attn_workspace_bytes(dims, n_q, cache->max_len) bytes (split-KV partials).
  * Errors: SA_ERR_NULL, SA_ERR_DIMS, SA_ERR_ARG, SA_ERR_WORKSPACE, SA_ERR_HIP.        */
 int sparse_attn_fwd(const sa_dims* dims, const sa_cache* cache, const void* q,
                     const int32_t* q_seq, const int32_t* sel, int64_t sel_ld, const int32_t* n_sel,

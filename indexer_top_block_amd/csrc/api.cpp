@@ -65,9 +65,11 @@ extern "C" {
 
 int sparse_attn_check_dims(const sa_dims* dims) { return check_dims(dims); }
 
-size_t sparse_attn_workspace_bytes(const sa_dims* dims, int32_t n_q) {
-  if (check_dims(dims) != SA_OK || n_q < 0) return 0;
-  return sa::plan_fwd(*dims, n_q).ws_bytes;
+size_t sparse_attn_workspace_bytes(const sa_dims* dims, int32_t n_q, int32_t max_len) {
+  if (check_dims(dims) != SA_OK || n_q < 0 || max_len < 0) return 0;
+  const size_t f = sa::plan_fwd(*dims, n_q).ws_bytes;
+  const size_t s = sa::select_ws_bytes(*dims, n_q, max_len);
+  return f > s ? f : s;
 }
 
 int sparse_attn_pool(const sa_dims* dims, const sa_cache* cache, const int32_t* n_pooled_in, int32_t* n_pooled_out,
@@ -101,8 +103,6 @@ int sparse_attn_score(const sa_dims* dims, const sa_cache* cache, const void* qi
 int sparse_attn_select(const sa_dims* dims, const sa_cache* cache, const float* scores, int64_t scores_ld,
                        const int32_t* q_seq, const int32_t* q_pos, int32_t n_q, int32_t* sel, int64_t sel_ld,
                        int32_t* n_sel, void* ws, size_t ws_bytes, void* stream) {
-  (void)ws;
-  (void)ws_bytes;  // the selection needs no workspace at present
   int rc = check_dims(dims);
   if (rc) return rc;
   if ((rc = check_cache_common(dims, cache))) return rc;
@@ -111,9 +111,11 @@ int sparse_attn_select(const sa_dims* dims, const sa_cache* cache, const float* 
   if (!scores || !q_seq || !q_pos || !sel || !n_sel) return SA_ERR_NULL;
   if (sel_ld < (int64_t)dims->top_k + dims->compress_ratio - 1) return SA_ERR_ARG;
   if (scores_ld < (int64_t)(cache->max_len / dims->compress_ratio) || scores_ld < 0) return SA_ERR_ARG;
+  const size_t need = sa::select_ws_bytes(*dims, n_q, cache->max_len);
+  if (need > 0 && (!ws || ws_bytes < need)) return SA_ERR_WORKSPACE;
   (void)hipGetLastError();
   return hip_status(sa::launch_select(*dims, to_args(cache), scores, scores_ld, q_seq, q_pos, n_q, sel, sel_ld,
-                                      n_sel, (hipStream_t)stream));
+                                      n_sel, ws, (hipStream_t)stream));
 }
 
 int sparse_attn_fwd(const sa_dims* dims, const sa_cache* cache, const void* q, const int32_t* q_seq,

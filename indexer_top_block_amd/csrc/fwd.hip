@@ -83,9 +83,12 @@ fwd_mfma_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, 
   constexpr int NT = DVW / 16;        // 16-column output tiles per wave
   constexpr int KCH = DKQ / 8;        // 16-byte chunks per K row
   constexpr int VCH = DV / 8;
+  constexpr int KLD = kRowTile * KCH / 256;               // K chunks per thread per tile
+  constexpr int VLD = ALIAS ? 1 : kRowTile * VCH / 256;   // V chunks per thread per tile
+  static_assert(kRowTile * KCH % 256 == 0 && (ALIAS || kRowTile * VCH % 256 == 0), "tile must split evenly");
   __shared__ __attribute__((aligned(16))) T ks[kRowTile * KP];
   __shared__ __attribute__((aligned(16))) T vs_sep[ALIAS ? 8 : kRowTile * VP];
-  __shared__ int64_t rows[kRowTile];
+  __shared__ int64_t rows[2][kRowTile];              // cache rows of tiles t (t % 2) and t + 1
   const T* vs = ALIAS ? ks : vs_sep;
 
   const int tid = threadIdx.x;
@@ -94,15 +97,25 @@ fwd_mfma_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, 
   const int split = blockIdx.x;
   const int i = blockIdx.y / h_kv, g = blockIdx.y % h_kv;
   const int G = h_q / h_kv;
+  const int32_t* list = sel + (int64_t)i * sel_ld;
+  const int r_begin = split * rows_per_split;
+  // The first two tiles' list entries are read alongside the query's metadata
+  // (entries below sel_ld are valid memory; validity is decided once n_sel is known).
+  int pre0 = -1, pre1 = -1;
+  if (tid < kRowTile) {
+    if (r_begin + tid < sel_ld) pre0 = list[r_begin + tid];
+    if (r_begin + kRowTile + tid < sel_ld) pre1 = list[r_begin + kRowTile + tid];
+  }
   const int s = q_seq[i];
   const int L = seq_len[s];
   const int64_t row0 = seq_row0[s];
   const int cnt = max(0, (int)min((int64_t)n_sel[i], sel_ld));
-  const int r_begin = split * rows_per_split;
   const int r_end = min(cnt, r_begin + rows_per_split);
-  const int32_t* list = sel + (int64_t)i * sel_ld;
+  const int n_tiles = r_end > r_begin ? (r_end - r_begin + kRowTile - 1) / kRowTile : 0;
+  const T* kg = k + (int64_t)g * k_hs;
+  const T* vg = v + (int64_t)g * v_hs;
 
-  // Q^T as the B operand: lane (col = head, grp) holds dims ks*32 + grp*8 .. +8.
+  // Q^T as the B operand: lane (col = head, grp) holds dims st*32 + grp*8 .. +8.
   V8 qf[KST];
   {
     const T* qh = q + ((int64_t)i * h_q + (int64_t)g * G + col) * DKQ + grp * 8;
@@ -114,26 +127,59 @@ fwd_mfma_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, 
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int r0 = r_begin; r0 < r_end; r0 += kRowTile) {
-    if (tid < kRowTile) rows[tid] = tile_row(list, r0 + tid, r_end, L, row0);
-    __syncthreads();
-    for (int e = tid; e < kRowTile * KCH; e += 256) {
-      const int r = e / KCH, cc = e % KCH;
-      const int64_t row = rows[r];
-      V8 val = V8{};
-      if (row >= 0) val = *reinterpret_cast<const V8*>(k + row * k_ld + (int64_t)g * k_hs + cc * 8);
-      *reinterpret_cast<V8*>(ks + r * KP + cc * 8) = val;
+  // Gathered rows of the next tile are held in registers while the current tile is
+  // computed from LDS; the row list runs one tile further ahead.
+  V8 kreg[KLD], vreg[VLD];
+  auto issue_loads = [&](const int64_t* trow) {
+#pragma unroll
+    for (int j = 0; j < KLD; ++j) {
+      const int e = tid + 256 * j, r = e / KCH, cc = e % KCH;
+      const int64_t row = trow[r];
+      kreg[j] = row >= 0 ? *reinterpret_cast<const V8*>(kg + row * k_ld + cc * 8) : V8{};
     }
     if (!ALIAS) {
-      for (int e = tid; e < kRowTile * VCH; e += 256) {
-        const int r = e / VCH, cc = e % VCH;
-        const int64_t row = rows[r];
-        V8 val = V8{};
-        if (row >= 0) val = *reinterpret_cast<const V8*>(v + row * v_ld + (int64_t)g * v_hs + cc * 8);
-        *reinterpret_cast<V8*>(vs_sep + r * VP + cc * 8) = val;
+#pragma unroll
+      for (int j = 0; j < VLD; ++j) {
+        const int e = tid + 256 * j, r = e / VCH, cc = e % VCH;
+        const int64_t row = trow[r];
+        vreg[j] = row >= 0 ? *reinterpret_cast<const V8*>(vg + row * v_ld + cc * 8) : V8{};
       }
     }
+  };
+  int64_t lnext = -1;
+  if (n_tiles > 0) {
+    if (tid < kRowTile) {
+      const int j0 = r_begin + tid, j1 = j0 + kRowTile;
+      const int p0 = pre0, p1 = pre1;
+      rows[0][tid] = (j0 < r_end && p0 >= 0 && p0 < L) ? row0 + p0 : -1;
+      lnext = (j1 < r_end && p1 >= 0 && p1 < L) ? row0 + p1 : -1;
+    }
     __syncthreads();
+    issue_loads(rows[0]);
+  }
+
+  for (int t = 0; t < n_tiles; ++t) {
+    const int64_t* trow = rows[t & 1];
+    // land tile t in LDS
+#pragma unroll
+    for (int j = 0; j < KLD; ++j) {
+      const int e = tid + 256 * j, r = e / KCH, cc = e % KCH;
+      *reinterpret_cast<V8*>(ks + r * KP + cc * 8) = kreg[j];
+    }
+    if (!ALIAS) {
+#pragma unroll
+      for (int j = 0; j < VLD; ++j) {
+        const int e = tid + 256 * j, r = e / VCH, cc = e % VCH;
+        *reinterpret_cast<V8*>(vs_sep + r * VP + cc * 8) = vreg[j];
+      }
+    }
+    // publish the rows of tile t+1 and fetch those of tile t+2
+    if (tid < kRowTile) {
+      rows[(t + 1) & 1][tid] = lnext;
+      lnext = (t + 2 < n_tiles) ? tile_row(list, r_begin + (t + 2) * kRowTile + tid, r_end, L, row0) : -1;
+    }
+    __syncthreads();
+    if (t + 1 < n_tiles) issue_loads(rows[(t + 1) & 1]);
 
     // S^T[row][head] for the tile's two 16-row halves.
     f32x4 sacc[2];
@@ -152,7 +198,7 @@ fwd_mfma_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, 
     for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const bool ok = rows[h2 * 16 + 4 * grp + j] >= 0;
+        const bool ok = trow[h2 * 16 + 4 * grp + j] >= 0;
         x[h2][j] = ok ? sacc[h2][j] * scale_log2 : -INFINITY;
         mx = fmaxf(mx, x[h2][j]);
       }
@@ -323,28 +369,46 @@ fwd_valu_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, 
 // ------------------------------------------------------------------------- combine
 
 // out[qh][dv] = sum_s 2^(m_s - M) o_s[dv] / sum_s 2^(m_s - M) l_s, M = max_s m_s.
+// One workgroup per (query, head); the split statistics are read in parallel.
 __global__ void __launch_bounds__(256)
 fwd_combine_kernel(const float* __restrict__ ws_o, const float* __restrict__ ws_ml, int n_split, int d_v,
                    float* __restrict__ out) {
   extern __shared__ float wsh[];                     // n_split weights
+  __shared__ float red[256 / kWave];
+  __shared__ float sh_m, sh_inv_l;
   const int64_t qh = blockIdx.x;
   const float* ml = ws_ml + qh * n_split * 2;
-  __shared__ float inv_l;
-  if (threadIdx.x == 0) {
-    float M = -INFINITY;
-    for (int s = 0; s < n_split; ++s) M = fmaxf(M, ml[2 * s]);
-    float L = 0.f;
-    for (int s = 0; s < n_split; ++s) {
-      const float w = (ml[2 * s] == -INFINITY) ? 0.f : fast_exp2(ml[2 * s] - M);
-      wsh[s] = w;
-      L += w * ml[2 * s + 1];
-    }
-    inv_l = L > 0.f ? 1.f / L : 0.f;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  float M = -INFINITY;
+  for (int s = tid; s < n_split; s += 256) M = fmaxf(M, ml[2 * s]);
+  M = wave_max(M);
+  if (lane == 0) red[wave] = M;
+  __syncthreads();
+  if (tid == 0) sh_m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  M = sh_m;
+  float lpart = 0.f;
+  for (int s = tid; s < n_split; s += 256) {
+    const float ms = ml[2 * s];
+    const float w = (ms == -INFINITY) ? 0.f : fast_exp2(ms - M);
+    wsh[s] = w;
+    lpart += w * ml[2 * s + 1];
+  }
+  lpart = wave_sum(lpart);
+  __syncthreads();
+  if (lane == 0) red[wave] = lpart;
+  __syncthreads();
+  if (tid == 0) {
+    const float L = red[0] + red[1] + red[2] + red[3];
+    sh_inv_l = L > 0.f ? 1.f / L : 0.f;
   }
   __syncthreads();
-  for (int dv = threadIdx.x; dv < d_v; dv += blockDim.x) {
+  const float inv_l = sh_inv_l;
+  for (int dv = tid; dv < d_v; dv += 256) {
+    const float* src = ws_o + qh * n_split * d_v + dv;
     float acc = 0.f;
-    for (int s = 0; s < n_split; ++s) acc += wsh[s] * ws_o[(qh * n_split + s) * d_v + dv];
+#pragma unroll 16
+    for (int s = 0; s < n_split; ++s) acc += wsh[s] * src[(int64_t)s * d_v];
     out[qh * d_v + dv] = acc * inv_l;
   }
 }

@@ -32,9 +32,12 @@ hipError_t launch_pool(const sa_dims& d, const CacheArgs& c, const int32_t* n_po
 hipError_t launch_score(const sa_dims& d, const CacheArgs& c, const void* qidx, const int32_t* q_seq,
                         const int32_t* q_pos, int n_q, float* scores, int64_t scores_ld, hipStream_t stream);
 
+// Workspace bytes of the selection (0 when one workgroup per query token is used).
+size_t select_ws_bytes(const sa_dims& d, int n_q, int max_len);
+
 hipError_t launch_select(const sa_dims& d, const CacheArgs& c, const float* scores, int64_t scores_ld,
                          const int32_t* q_seq, const int32_t* q_pos, int n_q, int32_t* sel, int64_t sel_ld,
-                         int32_t* n_sel, hipStream_t stream);
+                         int32_t* n_sel, void* ws, hipStream_t stream);
 
 // Split-KV partition of the attention for n_q query tokens: rows of each query's
 // list handled per split (a multiple of 32) and the number of splits.

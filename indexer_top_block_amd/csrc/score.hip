@@ -51,16 +51,24 @@ score_mfma_kernel(const T* __restrict__ qidx, const T* __restrict__ kpool, int64
   typedef typename vec8<T>::type V8;
   constexpr int KS = D / 16;          // MFMA steps over the indexer dim (8 per lane half)
   const int i = blockIdx.y;
-  const int s = q_seq[i];
-  const int nb = visible_tokens(seq_len[s], q_pos[i]) / c;
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
-  const int b_base = (blockIdx.x * kScoreWaves + wave) * kScoreTile;
-  if (b_base >= nb) return;
   const int n = lane & 31;
   const int hf = lane >> 5;
+  // Indexer query heads mt*32 + n, dim slices of this lane's half; read alongside the
+  // query's metadata, which the key addresses depend on.
+  const T* qrow = qidx + (int64_t)i * (MT * 32) * D + (int64_t)n * D + hf * (D / 2);
+  V8 qa[MT][KS];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int st = 0; st < KS; ++st) qa[mt][st] = *reinterpret_cast<const V8*>(qrow + (int64_t)mt * 32 * D + st * 8);
+  const int s = q_seq[i];
+  const int nb = visible_tokens(seq_len[s], q_pos[i]) / c;
+  const int b_base = (blockIdx.x * kScoreWaves + wave) * kScoreTile;
+  if (b_base >= nb) return;
 
-  // Issue the key loads first: one 16-byte slice per step of this lane's half row.
+  // Pooled keys: one 16-byte slice per step of this lane's half row.
   const int b = b_base + n;
   const bool valid = b < nb;
   V8 kb[KS];
@@ -69,13 +77,6 @@ score_mfma_kernel(const T* __restrict__ qidx, const T* __restrict__ kpool, int64
   for (int st = 0; st < KS; ++st) {
     kb[st] = valid ? *reinterpret_cast<const V8*>(krow + st * 8) : V8{};
   }
-  // Indexer query heads mt*32 + n, same dim slices.
-  const T* qrow = qidx + (int64_t)i * (MT * 32) * D + (int64_t)n * D + hf * (D / 2);
-  V8 qa[MT][KS];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int st = 0; st < KS; ++st) qa[mt][st] = *reinterpret_cast<const V8*>(qrow + (int64_t)mt * 32 * D + st * 8);
 
   float sum = 0.f;
 #pragma unroll

@@ -49,7 +49,7 @@ class DeviceLayer:
         self.sel = torch.full((self.n_q, self.sel_ld), -7, dtype=torch.int32, device=device)
         self.n_sel = torch.zeros((self.n_q,), dtype=torch.int32, device=device)
         self.out = torch.zeros((self.n_q, d.h_q, d.d_v), dtype=torch.float32, device=device)
-        self.ws_bytes = sa.sparse_attn_workspace_bytes(self.dims, self.n_q)
+        self.ws_bytes = sa.sparse_attn_workspace_bytes(self.dims, self.n_q, self.max_len)
         self.ws = torch.empty((max(self.ws_bytes, 16),), dtype=torch.uint8, device=device)
         self.n_pooled = torch.zeros((case.n_seq,), dtype=torch.int32, device=device)
         self.scale = case.scale

@@ -71,7 +71,7 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     dp, cp = ctypes.POINTER(SaDims), ctypes.POINTER(SaCache)
     lib.sparse_attn_check_dims.argtypes = [dp]
     lib.sparse_attn_check_dims.restype = ctypes.c_int
-    lib.sparse_attn_workspace_bytes.argtypes = [dp, I32]
+    lib.sparse_attn_workspace_bytes.argtypes = [dp, I32, I32]
     lib.sparse_attn_workspace_bytes.restype = SZ
     lib.sparse_attn_pool.argtypes = [dp, cp, P, P, I32, P]
     lib.sparse_attn_pool.restype = ctypes.c_int
@@ -132,8 +132,8 @@ def sparse_attn_check_dims(dims: SaDims) -> int:
     return load().sparse_attn_check_dims(ctypes.byref(dims))
 
 
-def sparse_attn_workspace_bytes(dims: SaDims, n_q: int) -> int:
-    return int(load().sparse_attn_workspace_bytes(ctypes.byref(dims), int(n_q)))
+def sparse_attn_workspace_bytes(dims: SaDims, n_q: int, max_len: int) -> int:
+    return int(load().sparse_attn_workspace_bytes(ctypes.byref(dims), int(n_q), int(max_len)))
 
 
 def sparse_attn_pool(dims: SaDims, cache: Cache, n_pooled_in, n_pooled_out, max_new_blocks: int,

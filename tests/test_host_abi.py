@@ -71,12 +71,18 @@ def test_check_dims_null():
 
 def test_workspace_bytes():
     d = _dims()
-    # one decode token: split-KV partials (o, m, l) for 16 heads
-    ws = sa.sparse_attn_workspace_bytes(d, 1)
+    # one decode token over short rows: split-KV partials (o, m, l) for 16 heads only
+    ws = sa.sparse_attn_workspace_bytes(d, 1, 4096)
     assert ws > 0 and ws % (16 * (512 + 2) * 4) == 0
-    # a prefill chunk runs unsplit and needs none
-    assert sa.sparse_attn_workspace_bytes(d, 2048) == 0
-    assert sa.sparse_attn_workspace_bytes(_dims(top_k=2050), 1) == 0
+    # a prefill chunk: unsplit attention and one selection workgroup per query
+    assert sa.sparse_attn_workspace_bytes(d, 2048, 34816) == 0
+    # one decode token at 128K: also room for the chunked selection's histogram and candidates
+    big = sa.sparse_attn_workspace_bytes(d, 1, 131072)
+    assert big >= 4096 * 4 + 16384 * 8 and big >= ws
+    # many short-row decode tokens: the selection needs nothing, the partials grow with n_q
+    assert sa.sparse_attn_workspace_bytes(d, 8, 4096) > ws
+    assert sa.sparse_attn_workspace_bytes(_dims(top_k=2050), 1, 4096) == 0
+    assert sa.sparse_attn_workspace_bytes(d, 1, -1) == 0
 
 
 def _cache(**kw):
@@ -113,8 +119,16 @@ def test_entry_points_reject_bad_arguments_before_any_launch():
     assert _call("sparse_attn_select", d, c, FAKE, 1024, FAKE, FAKE, 1, FAKE, 2051, None, None, 0, None) == sa.SA_ERR_NULL
     assert _call("sparse_attn_select", d, ctypes.byref(_cache(seq_len=None)), FAKE, 1024, FAKE, FAKE, 1, FAKE,
                  2051, FAKE, None, 0, None) == sa.SA_ERR_NULL
+    # a 128K row needs the chunked selection's workspace
+    long_c = ctypes.byref(_cache(max_len=131072))
+    need = sa.sparse_attn_workspace_bytes(_dims(), 1, 131072)
+    assert _call("sparse_attn_select", d, long_c, FAKE, 32768, FAKE, FAKE, 1, FAKE, 2051, FAKE, None, 0,
+                 None) == sa.SA_ERR_WORKSPACE
+    assert need > 1000
+    assert _call("sparse_attn_select", d, long_c, FAKE, 32768, FAKE, FAKE, 1, FAKE, 2051, FAKE, FAKE, 1000,
+                 None) == sa.SA_ERR_WORKSPACE
     # fwd
-    ws = sa.sparse_attn_workspace_bytes(_dims(), 1)
+    ws = sa.sparse_attn_workspace_bytes(_dims(), 1, 4096)
     args = [d, c, FAKE, FAKE, FAKE, 2051, FAKE, 1, ctypes.c_float(0.04), FAKE]
     assert _call("sparse_attn_fwd", *args, None, 0, None) == sa.SA_ERR_WORKSPACE
     assert _call("sparse_attn_fwd", *args, FAKE, ws - 1, None) == sa.SA_ERR_WORKSPACE
