@@ -87,7 +87,8 @@ class RotatingLayers:
         self.n_sel = torch.zeros((self.n_q,), dtype=torch.int32, device=device)
         self.out = torch.zeros((self.n_q, d.h_q, d.d_v), dtype=torch.float32, device=device)
         self.ws_bytes = sa.sparse_attn_workspace_bytes(self.dims, self.n_q, self.max_len)
-        self.ws = torch.empty((max(self.ws_bytes, 16),), dtype=torch.uint8, device=device)
+        # zero-filled once: the leading state region must start at zero (the library keeps it so)
+        self.ws = torch.zeros((max(self.ws_bytes, 16),), dtype=torch.uint8, device=device)
         nb_full = (case.seq_len.astype(np.int64) // c).astype(np.int32)
         # each step re-pools the newest complete block (what a decode step adds every c tokens)
         self.n_pooled_prev = torch.from_numpy(np.maximum(nb_full - 1, 0)).to(device)

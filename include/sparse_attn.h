@@ -105,11 +105,18 @@ typedef struct {
  * top_k % c == 0; top_k + c - 1 <= 65536.  Makes no HIP call.                        */
 int sparse_attn_check_dims(const sa_dims* dims);
 
+/* Bytes at the start of a workspace that hold state between calls. */
+#define SA_WS_STATE_BYTES ((size_t)1056768)
+
 /* Bytes of device workspace that sparse_attn_select and sparse_attn_fwd need for n_q
- * query tokens over caches whose sa_cache.max_len is max_len.  One buffer of this
- * size serves both calls (each overwrites it; its contents need no initialisation
- * and carry nothing between calls).  Returns 0 on bad arguments or when no
- * workspace is needed.  Host only, no HIP call.                                    */
+ * query tokens over caches whose sa_cache.max_len is max_len; one buffer of this
+ * size serves both calls.  Returns 0 on bad arguments or when no workspace is needed.
+ * Host only, no HIP call.
+ * Contract: zero-fill the buffer once before its first use (e.g. hipMemset when it is
+ * allocated).  Its first SA_WS_STATE_BYTES bytes hold histograms and arrival counters
+ * that every call returns to zero, so later calls need no re-initialisation; the rest
+ * is scratch that each call overwrites.  Calls that share a workspace must not run
+ * concurrently (use one workspace per stream).                                     */
 size_t sparse_attn_workspace_bytes(const sa_dims* dims, int32_t n_q, int32_t max_len);
 
 /* Incremental block mean-pool (pages: the indexer cache holds raw keys because

@@ -67,9 +67,7 @@ int sparse_attn_check_dims(const sa_dims* dims) { return check_dims(dims); }
 
 size_t sparse_attn_workspace_bytes(const sa_dims* dims, int32_t n_q, int32_t max_len) {
   if (check_dims(dims) != SA_OK || n_q < 0 || max_len < 0) return 0;
-  const size_t f = sa::plan_fwd(*dims, n_q).ws_bytes;
-  const size_t s = sa::select_ws_bytes(*dims, n_q, max_len);
-  return f > s ? f : s;
+  return sa::workspace_bytes(*dims, n_q, max_len);
 }
 
 int sparse_attn_pool(const sa_dims* dims, const sa_cache* cache, const int32_t* n_pooled_in, int32_t* n_pooled_out,
@@ -111,8 +109,10 @@ int sparse_attn_select(const sa_dims* dims, const sa_cache* cache, const float* 
   if (!scores || !q_seq || !q_pos || !sel || !n_sel) return SA_ERR_NULL;
   if (sel_ld < (int64_t)dims->top_k + dims->compress_ratio - 1) return SA_ERR_ARG;
   if (scores_ld < (int64_t)(cache->max_len / dims->compress_ratio) || scores_ld < 0) return SA_ERR_ARG;
-  const size_t need = sa::select_ws_bytes(*dims, n_q, cache->max_len);
-  if (need > 0 && (!ws || ws_bytes < need)) return SA_ERR_WORKSPACE;
+  if (sa::select_scratch_bytes(*dims, n_q, cache->max_len) > 0) {
+    const size_t need = sa::workspace_bytes(*dims, n_q, cache->max_len);
+    if (!ws || ws_bytes < need) return SA_ERR_WORKSPACE;
+  }
   (void)hipGetLastError();
   return hip_status(sa::launch_select(*dims, to_args(cache), scores, scores_ld, q_seq, q_pos, n_q, sel, sel_ld,
                                       n_sel, ws, (hipStream_t)stream));
@@ -136,10 +136,14 @@ int sparse_attn_fwd(const sa_dims* dims, const sa_cache* cache, const void* q, c
   if (cache->v_ld < (int64_t)(dims->h_kv - 1) * cache->v_head_stride + dims->d_v) return SA_ERR_ARG;
   if (!(scale == scale)) return SA_ERR_ARG;  // NaN
   const sa::FwdPlan plan = sa::plan_fwd(*dims, n_q);
-  if (plan.ws_bytes > 0 && (!ws || ws_bytes < plan.ws_bytes)) return SA_ERR_WORKSPACE;
+  void* scratch = nullptr;
+  if (plan.ws_bytes > 0) {
+    if (!ws || ws_bytes < SA_WS_STATE_BYTES + plan.ws_bytes) return SA_ERR_WORKSPACE;
+    scratch = (char*)ws + SA_WS_STATE_BYTES;
+  }
   (void)hipGetLastError();
-  return hip_status(sa::launch_fwd(*dims, to_args(cache), q, q_seq, sel, sel_ld, n_sel, n_q, scale, out, ws, plan,
-                                   (hipStream_t)stream));
+  return hip_status(sa::launch_fwd(*dims, to_args(cache), q, q_seq, sel, sel_ld, n_sel, n_q, scale, out, scratch,
+                                   plan, (hipStream_t)stream));
 }
 
 const char* sparse_attn_strerror(int code) {

@@ -29,10 +29,10 @@ constexpr int kRowTile = 32;
 
 // ------------------------------------------------------------------- shared helpers
 
-__device__ __forceinline__ int64_t tile_row(const int32_t* list, int j, int r_end, int seq_len, int64_t row0) {
-  if (j >= r_end) return -1;
-  const int pos = list[j];
-  return (pos >= 0 && pos < seq_len) ? row0 + pos : -1;
+// Cache row of list entry j holding position `pos`, or -1 when j is past the
+// query's count or pos is padding / not a cached position.
+__device__ __forceinline__ int64_t tile_row(int pos, int j, int r_end, int seq_len, int64_t row0) {
+  return (j < r_end && pos >= 0 && pos < seq_len) ? row0 + pos : -1;
 }
 
 template <typename T>
@@ -67,8 +67,10 @@ template <> struct pv_mfma<f16> {
 
 // ---------------------------------------------------------------------------- MFMA
 
+constexpr int kMfmaTile = 64;        // rows per workgroup tile: 16 per wave
+
 template <typename T, int DKQ, int DV, bool ALIAS>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(256, 1)
 fwd_mfma_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, int64_t k_hs,
                 const T* __restrict__ v, int64_t v_ld, int64_t v_hs, const int64_t* __restrict__ seq_row0,
                 const int32_t* __restrict__ seq_len, const int32_t* __restrict__ q_seq,
@@ -76,19 +78,21 @@ fwd_mfma_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, 
                 int h_kv, float scale_log2, int n_split, int rows_per_split, float* __restrict__ out,
                 float* __restrict__ ws_o, float* __restrict__ ws_ml) {
   typedef typename vec8<T>::type V8;
+  constexpr int RT = kMfmaTile;
   constexpr int KST = DKQ / 32;       // QK^T MFMA steps
   constexpr int KP = DKQ + 8;         // LDS row pitch of the K tile (elements)
   constexpr int VP = ALIAS ? KP : DV + 8;
-  constexpr int DVW = DV / 4;         // DV columns per wave
-  constexpr int NT = DVW / 16;        // 16-column output tiles per wave
+  constexpr int NT = DV / 16;         // 16-column output tiles (every wave holds all of DV)
   constexpr int KCH = DKQ / 8;        // 16-byte chunks per K row
   constexpr int VCH = DV / 8;
-  constexpr int KLD = kRowTile * KCH / 256;               // K chunks per thread per tile
-  constexpr int VLD = ALIAS ? 1 : kRowTile * VCH / 256;   // V chunks per thread per tile
-  static_assert(kRowTile * KCH % 256 == 0 && (ALIAS || kRowTile * VCH % 256 == 0), "tile must split evenly");
-  __shared__ __attribute__((aligned(16))) T ks[kRowTile * KP];
-  __shared__ __attribute__((aligned(16))) T vs_sep[ALIAS ? 8 : kRowTile * VP];
-  __shared__ int64_t rows[2][kRowTile];              // cache rows of tiles t (t % 2) and t + 1
+  constexpr int KLD = RT * KCH / 256;                 // K chunks per thread per tile
+  constexpr int VLD = ALIAS ? 1 : RT * VCH / 256;     // V chunks per thread per tile
+  static_assert(RT * KCH % 256 == 0 && (ALIAS || RT * VCH % 256 == 0), "tile must split evenly");
+  static_assert(2 * 16 * DV * 4 <= RT * KP * (int)sizeof(T), "wave merge must fit in the K tile");
+  __shared__ __attribute__((aligned(16))) T ks[RT * KP];
+  __shared__ __attribute__((aligned(16))) T vs_sep[ALIAS ? 8 : RT * VP];
+  __shared__ int64_t rows[2][RT];                    // cache rows of tiles t (t % 2) and t + 1
+  __shared__ float wm[4][16], wl[4][16];             // per-wave statistics for the final merge
   const T* vs = ALIAS ? ks : vs_sep;
 
   const int tid = threadIdx.x;
@@ -99,28 +103,37 @@ fwd_mfma_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, 
   const int G = h_q / h_kv;
   const int32_t* list = sel + (int64_t)i * sel_ld;
   const int r_begin = split * rows_per_split;
-  // The first two tiles' list entries are read alongside the query's metadata
-  // (entries below sel_ld are valid memory; validity is decided once n_sel is known).
-  int pre0 = -1, pre1 = -1;
-  if (tid < kRowTile) {
-    if (r_begin + tid < sel_ld) pre0 = list[r_begin + tid];
-    if (r_begin + kRowTile + tid < sel_ld) pre1 = list[r_begin + kRowTile + tid];
+  // The first three tiles' list entries are read alongside the query's metadata.
+  // List indices are clamped into the row rather than guarded, so the loads issue
+  // back to back; entries at or past the query's count are discarded once it is known.
+  const int lim = (int)sel_ld - 1;
+  int pre0 = -1, pre1 = -1, pre2 = -1;
+  if (tid < RT) {
+    pre0 = list[min(r_begin + tid, lim)];
+    pre1 = list[min(r_begin + RT + tid, lim)];
+    pre2 = list[min(r_begin + 2 * RT + tid, lim)];
   }
-  const int s = q_seq[i];
-  const int L = seq_len[s];
-  const int64_t row0 = seq_row0[s];
+  const SeqMeta sm = seq_meta(q_seq, seq_len, seq_row0, nullptr, i);
+  const int L = sm.len;
+  const int64_t row0 = sm.row0;
   const int cnt = max(0, (int)min((int64_t)n_sel[i], sel_ld));
   const int r_end = min(cnt, r_begin + rows_per_split);
-  const int n_tiles = r_end > r_begin ? (r_end - r_begin + kRowTile - 1) / kRowTile : 0;
+  const int n_tiles = r_end > r_begin ? (r_end - r_begin + RT - 1) / RT : 0;
   const T* kg = k + (int64_t)g * k_hs;
   const T* vg = v + (int64_t)g * v_hs;
 
   // Q^T as the B operand: lane (col = head, grp) holds dims st*32 + grp*8 .. +8.
+  // Lanes past the group's heads read head 0 and zero the values.
+  const T* qbase = q + ((int64_t)i * h_q + (int64_t)g * G) * DKQ;
   V8 qf[KST];
   {
-    const T* qh = q + ((int64_t)i * h_q + (int64_t)g * G + col) * DKQ + grp * 8;
+    const T* qh = qbase + (col < G ? col : 0) * DKQ + grp * 8;
 #pragma unroll
-    for (int st = 0; st < KST; ++st) qf[st] = (col < G) ? *reinterpret_cast<const V8*>(qh + st * 32) : V8{};
+    for (int st = 0; st < KST; ++st) qf[st] = *reinterpret_cast<const V8*>(qh + st * 32);
+    if (col >= G) {
+#pragma unroll
+      for (int st = 0; st < KST; ++st) qf[st] = V8{};
+    }
   }
   float m = -INFINITY, lsum = 0.f;
   f32x4 o[NT];
@@ -128,36 +141,42 @@ fwd_mfma_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, 
   for (int nt = 0; nt < NT; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // Gathered rows of the next tile are held in registers while the current tile is
-  // computed from LDS; the row list runs one tile further ahead.
+  // computed from LDS; the row list runs two tiles further ahead.  Rows that are not
+  // selected are read from this query's own Q row instead (finite values, and their
+  // scores are masked to -inf, so they add exactly zero); every gather is an
+  // unconditional load, so all of a tile's loads are in flight together.
   V8 kreg[KLD], vreg[VLD];
   auto issue_loads = [&](const int64_t* trow) {
 #pragma unroll
     for (int j = 0; j < KLD; ++j) {
       const int e = tid + 256 * j, r = e / KCH, cc = e % KCH;
       const int64_t row = trow[r];
-      kreg[j] = row >= 0 ? *reinterpret_cast<const V8*>(kg + row * k_ld + cc * 8) : V8{};
+      const T* p = row >= 0 ? kg + row * k_ld + cc * 8 : qbase;
+      kreg[j] = *reinterpret_cast<const V8*>(p);
     }
     if (!ALIAS) {
 #pragma unroll
       for (int j = 0; j < VLD; ++j) {
         const int e = tid + 256 * j, r = e / VCH, cc = e % VCH;
         const int64_t row = trow[r];
-        vreg[j] = row >= 0 ? *reinterpret_cast<const V8*>(vg + row * v_ld + cc * 8) : V8{};
+        const T* p = row >= 0 ? vg + row * v_ld + cc * 8 : qbase;
+        vreg[j] = *reinterpret_cast<const V8*>(p);
       }
     }
   };
-  int64_t lnext = -1;
+  int64_t lnext = -1;                                // checked row of tile t + 1 (threads < RT)
+  int lraw = -1;                                     // list entry of tile t + 2
   if (n_tiles > 0) {
-    if (tid < kRowTile) {
-      const int j0 = r_begin + tid, j1 = j0 + kRowTile;
-      const int p0 = pre0, p1 = pre1;
-      rows[0][tid] = (j0 < r_end && p0 >= 0 && p0 < L) ? row0 + p0 : -1;
-      lnext = (j1 < r_end && p1 >= 0 && p1 < L) ? row0 + p1 : -1;
+    if (tid < RT) {
+      rows[0][tid] = tile_row(pre0, r_begin + tid, r_end, L, row0);
+      lnext = tile_row(pre1, r_begin + RT + tid, r_end, L, row0);
+      lraw = pre2;
     }
     __syncthreads();
     issue_loads(rows[0]);
   }
 
+  const int wr = wave * 16;                          // this wave's 16 rows of the tile
   for (int t = 0; t < n_tiles; ++t) {
     const int64_t* trow = rows[t & 1];
     // land tile t in LDS
@@ -173,91 +192,109 @@ fwd_mfma_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, 
         *reinterpret_cast<V8*>(vs_sep + r * VP + cc * 8) = vreg[j];
       }
     }
-    // publish the rows of tile t+1 and fetch those of tile t+2
-    if (tid < kRowTile) {
+    // publish the rows of tile t+1, check those of tile t+2, fetch the list of t+3
+    if (tid < RT) {
       rows[(t + 1) & 1][tid] = lnext;
-      lnext = (t + 2 < n_tiles) ? tile_row(list, r_begin + (t + 2) * kRowTile + tid, r_end, L, row0) : -1;
+      lnext = tile_row(lraw, r_begin + (t + 2) * RT + tid, r_end, L, row0);
     }
     __syncthreads();
     if (t + 1 < n_tiles) issue_loads(rows[(t + 1) & 1]);
+    if (tid < RT) lraw = list[min(r_begin + (t + 3) * RT + tid, lim)];
 
-    // S^T[row][head] for the tile's two 16-row halves.
-    f32x4 sacc[2];
+    // S^T[row][head] for this wave's 16 rows, as two independent accumulation chains.
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+    const T* arow = ks + (wr + col) * KP + grp * 8;
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-      sacc[h2] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const T* arow = ks + (h2 * 16 + col) * KP + grp * 8;
-#pragma unroll
-      for (int st = 0; st < KST; ++st)
-        sacc[h2] = mfma16x16x32<T>(*reinterpret_cast<const V8*>(arow + st * 32), qf[st], sacc[h2]);
+    for (int st = 0; st + 1 < KST; st += 2) {
+      s0 = mfma16x16x32<T>(*reinterpret_cast<const V8*>(arow + st * 32), qf[st], s0);
+      s1 = mfma16x16x32<T>(*reinterpret_cast<const V8*>(arow + (st + 1) * 32), qf[st + 1], s1);
     }
-    // Online softmax for head `col`; this lane holds rows h2*16 + 4*grp + j.
-    float x[2][4];
+    if (KST & 1) s0 = mfma16x16x32<T>(*reinterpret_cast<const V8*>(arow + (KST - 1) * 32), qf[KST - 1], s0);
+    const f32x4 sacc = s0 + s1;
+    // Online softmax for head `col`; this lane holds rows wr + 4*grp + j.
+    float x[4];
     float mx = -INFINITY;
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const bool ok = trow[h2 * 16 + 4 * grp + j] >= 0;
-        x[h2][j] = ok ? sacc[h2][j] * scale_log2 : -INFINITY;
-        mx = fmaxf(mx, x[h2][j]);
-      }
+    for (int j = 0; j < 4; ++j) {
+      const bool ok = trow[wr + 4 * grp + j] >= 0;
+      x[j] = ok ? sacc[j] * scale_log2 : -INFINITY;
+      mx = fmaxf(mx, x[j]);
+    }
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float m_new = fmaxf(m, mx);
     const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m - m_new);
-    T pb[2][4];
+    T pb[4];
     float psum = 0.f;
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float p = (x[h2][j] == -INFINITY) ? 0.f : fast_exp2(x[h2][j] - m_new);
-        psum += p;
-        pb[h2][j] = (T)p;
-      }
+    for (int j = 0; j < 4; ++j) {
+      const float p = (x[j] == -INFINITY) ? 0.f : fast_exp2(x[j] - m_new);
+      psum += p;
+      pb[j] = (T)p;
+    }
     lsum = lsum * alpha + psum;
     m = m_new;
+    // O^T[dv][head] = alpha * O^T + V^T[dv][row] P^T[row][head] over this wave's 16 rows.
+    const T* vrow = vs + (wr + 4 * grp) * VP + col;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) o[nt] *= alpha;
-
-    // O^T[dv][head] += V^T[dv][row] P^T[row][head], 16 rows per product.
+    for (int nt = 0; nt < NT; ++nt) {
+      T a[4];
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const int dv = wave * DVW + nt * 16 + col;
-        T a[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) a[j] = vs[(h2 * 16 + 4 * grp + j) * VP + dv];
-        o[nt] = pv_mfma<T>::run(a, pb[h2], o[nt]);
-      }
+      for (int j = 0; j < 4; ++j) a[j] = vrow[j * VP + nt * 16];
+      o[nt] = pv_mfma<T>::run(a, pb, o[nt] * alpha);
     }
     __syncthreads();
   }
 
+  // ---- merge the four waves' (m, l, O) -------------------------------------------
   lsum += __shfl_xor(lsum, 16);
   lsum += __shfl_xor(lsum, 32);
-  if (col < G) {
+  if (grp == 0) {
+    wm[wave][col] = m;
+    wl[wave][col] = lsum;
+  }
+  __syncthreads();
+  float M = fmaxf(fmaxf(wm[0][col], wm[1][col]), fmaxf(wm[2][col], wm[3][col]));
+  float Lt = 0.f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) Lt += (wm[w][col] == -INFINITY) ? 0.f : fast_exp2(wm[w][col] - M) * wl[w][col];
+  const float sc = (m == -INFINITY) ? 0.f : fast_exp2(m - M);
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) o[nt] *= sc;
+  f32x4* xo = reinterpret_cast<f32x4*>(ks);          // 2 slots of [NT][64 lanes] f32x4
+  if (wave >= 2) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) xo[((wave - 2) * NT + nt) * kWave + lane] = o[nt];
+  }
+  __syncthreads();
+  if (wave < 2) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) o[nt] += xo[(wave * NT + nt) * kWave + lane];
+  }
+  __syncthreads();
+  if (wave == 1) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) xo[nt * kWave + lane] = o[nt];
+  }
+  __syncthreads();
+  if (wave == 0 && col < G) {
     const int hq = g * G + col;
     const int64_t qh = (int64_t)i * h_q + hq;
     if (n_split == 1) {
-      const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+      const float inv = Lt > 0.f ? 1.f / Lt : 0.f;
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        const int dv = wave * DVW + nt * 16 + 4 * grp;
-        *reinterpret_cast<f32x4*>(out + qh * DV + dv) = o[nt] * inv;
+        const f32x4 r = (o[nt] + xo[nt * kWave + lane]) * inv;
+        *reinterpret_cast<f32x4*>(out + qh * DV + nt * 16 + 4 * grp) = r;
       }
     } else {
       float* dst = ws_o + (qh * n_split + split) * DV;
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const int dv = wave * DVW + nt * 16 + 4 * grp;
-        *reinterpret_cast<f32x4*>(dst + dv) = o[nt];
-      }
-      if (wave == 0 && grp == 0) {
-        ws_ml[(qh * n_split + split) * 2 + 0] = m;
-        ws_ml[(qh * n_split + split) * 2 + 1] = lsum;
+      for (int nt = 0; nt < NT; ++nt)
+        *reinterpret_cast<f32x4*>(dst + nt * 16 + 4 * grp) = o[nt] + xo[nt * kWave + lane];
+      if (grp == 0) {
+        ws_ml[(qh * n_split + split) * 2 + 0] = M;
+        ws_ml[(qh * n_split + split) * 2 + 1] = Lt;
       }
     }
   }
@@ -280,9 +317,9 @@ fwd_valu_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, 
   const int split = blockIdx.x;
   const int i = blockIdx.y / h_kv, g = blockIdx.y % h_kv;
   const int G = h_q / h_kv;
-  const int s = q_seq[i];
-  const int L = seq_len[s];
-  const int64_t row0 = seq_row0[s];
+  const SeqMeta sm = seq_meta(q_seq, seq_len, seq_row0, nullptr, i);
+  const int L = sm.len;
+  const int64_t row0 = sm.row0;
   const int cnt = max(0, (int)min((int64_t)n_sel[i], sel_ld));
   const int r_begin = split * rows_per_split;
   const int r_end = min(cnt, r_begin + rows_per_split);
@@ -298,7 +335,7 @@ fwd_valu_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, 
 
   for (int r0 = r_begin; r0 < r_end; r0 += kRowTile) {
     __syncthreads();
-    if (tid < kRowTile) rows[tid] = tile_row(list, r0 + tid, r_end, L, row0);
+    if (tid < kRowTile) rows[tid] = tile_row(r0 + tid < r_end ? list[r0 + tid] : -1, r0 + tid, r_end, L, row0);
     __syncthreads();
     for (int e = tid; e < G * kRowTile; e += 256) {
       const int h = e / kRowTile, r = e % kRowTile;
@@ -423,17 +460,24 @@ FwdPlan plan_fwd(const sa_dims& d, int n_q) {
   FwdPlan p{};
   const int cap = fwd_cap(d);
   const long long units = (long long)n_q * d.h_kv;
-  // Aim at about 512 workgroups; never split below 64 rows.
+  // Aim at about 512 workgroups; never split below one 64-row tile.
   long long want = units > 0 ? (512 + units - 1) / units : 1;
-  const long long max_split = (cap + 63) / 64;
+  const long long max_split = (cap + kMfmaTile - 1) / kMfmaTile;
   if (want > max_split) want = max_split;
   if (want < 1) want = 1;
   int rps = (int)((cap + want - 1) / want);
-  rps = (rps + kRowTile - 1) / kRowTile * kRowTile;
+  rps = (rps + kMfmaTile - 1) / kMfmaTile * kMfmaTile;
   p.rows_per_split = rps;
   p.n_split = (cap + rps - 1) / rps;
   p.ws_bytes = p.n_split > 1 ? (size_t)n_q * d.h_q * p.n_split * ((size_t)d.d_v + 2) * sizeof(float) : 0;
   return p;
+}
+
+size_t workspace_bytes(const sa_dims& d, int n_q, int max_len) {
+  const size_t f = plan_fwd(d, n_q).ws_bytes;
+  const size_t s = select_scratch_bytes(d, n_q, max_len);
+  if (f == 0 && s == 0) return 0;
+  return SA_WS_STATE_BYTES + (f > s ? f : s);
 }
 
 bool fwd_uses_mfma(const sa_dims& d, const CacheArgs& c, const void* q) {

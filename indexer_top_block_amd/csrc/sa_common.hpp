@@ -57,6 +57,31 @@ __device__ __forceinline__ int wave_inclusive_scan(int x, int lane) {
 // 2^x with the hardware exponential (v_exp_f32); exp2(-inf) = 0.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Sequence metadata of query token i.  Sequence 0's entries are read together with
+// q_seq[i] (one memory round trip instead of two when, as in single-sequence decode,
+// the token belongs to sequence 0); other sequences take a second read.
+struct SeqMeta {
+  int s;
+  int len;
+  int64_t row0;
+  int64_t blk0;
+};
+__device__ __forceinline__ SeqMeta seq_meta(const int32_t* __restrict__ q_seq, const int32_t* __restrict__ seq_len,
+                                            const int64_t* __restrict__ seq_row0,
+                                            const int64_t* __restrict__ seq_blk0, int i) {
+  SeqMeta m;
+  m.s = q_seq[i];
+  m.len = seq_len[0];
+  m.row0 = seq_row0 ? seq_row0[0] : 0;
+  m.blk0 = seq_blk0 ? seq_blk0[0] : 0;
+  if (m.s != 0) {
+    m.len = seq_len[m.s];
+    m.row0 = seq_row0 ? seq_row0[m.s] : 0;
+    m.blk0 = seq_blk0 ? seq_blk0[m.s] : 0;
+  }
+  return m;
+}
+
 // Visible cached positions for a query: t <= q_pos and t < seq_len.
 __device__ __forceinline__ int visible_tokens(int seq_len, int q_pos) {
   long long v = (long long)q_pos + 1;

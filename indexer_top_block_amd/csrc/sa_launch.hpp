@@ -32,9 +32,22 @@ hipError_t launch_pool(const sa_dims& d, const CacheArgs& c, const int32_t* n_po
 hipError_t launch_score(const sa_dims& d, const CacheArgs& c, const void* qidx, const int32_t* q_seq,
                         const int32_t* q_pos, int n_q, float* scores, int64_t scores_ld, hipStream_t stream);
 
-// Workspace bytes of the selection (0 when one workgroup per query token is used).
-size_t select_ws_bytes(const sa_dims& d, int n_q, int max_len);
+// Workspace layout shared by sparse_attn_select and sparse_attn_fwd:
+//   [0, SA_WS_STATE_BYTES)   state -- zero before the first call, left zero by every call
+//                            (histograms and arrival counters of the chunked selection);
+//   [SA_WS_STATE_BYTES, ...) scratch -- overwritten by each call.
+constexpr int kStateQueries = 64;          // query tokens the chunked selection keeps state for
+struct WsState {
+  uint32_t ghist[kStateQueries][4096];     // per-query histogram of the top 12 key bits
+  uint32_t hist_done[kStateQueries];       // chunks of the histogram pass that have arrived
+  uint32_t sel_done[kStateQueries];        // chunks of the selection pass that have arrived
+};
+static_assert(sizeof(WsState) <= SA_WS_STATE_BYTES, "state region too small");
 
+// Scratch bytes of the chunked selection (0 when one workgroup per query token is used).
+size_t select_scratch_bytes(const sa_dims& d, int n_q, int max_len);
+
+// ws: the whole workspace (state at offset 0).
 hipError_t launch_select(const sa_dims& d, const CacheArgs& c, const float* scores, int64_t scores_ld,
                          const int32_t* q_seq, const int32_t* q_pos, int n_q, int32_t* sel, int64_t sel_ld,
                          int32_t* n_sel, void* ws, hipStream_t stream);
@@ -44,13 +57,17 @@ hipError_t launch_select(const sa_dims& d, const CacheArgs& c, const float* scor
 struct FwdPlan {
   int n_split;
   int rows_per_split;
-  size_t ws_bytes;
+  size_t ws_bytes;                         // scratch bytes (partial results), 0 when unsplit
 };
 FwdPlan plan_fwd(const sa_dims& d, int n_q);
 
+// ws: the scratch part of the workspace.
 hipError_t launch_fwd(const sa_dims& d, const CacheArgs& c, const void* q, const int32_t* q_seq,
                       const int32_t* sel, int64_t sel_ld, const int32_t* n_sel, int n_q, float scale, float* out,
                       void* ws, const FwdPlan& plan, hipStream_t stream);
+
+// Total workspace bytes for n_q query tokens (state + the larger scratch), 0 if none.
+size_t workspace_bytes(const sa_dims& d, int n_q, int max_len);
 
 // Which implementation a call takes (exposed for tests and reports).
 bool score_uses_mfma(const sa_dims& d, const CacheArgs& c, const void* qidx);

@@ -63,8 +63,8 @@ score_mfma_kernel(const T* __restrict__ qidx, const T* __restrict__ kpool, int64
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int st = 0; st < KS; ++st) qa[mt][st] = *reinterpret_cast<const V8*>(qrow + (int64_t)mt * 32 * D + st * 8);
-  const int s = q_seq[i];
-  const int nb = visible_tokens(seq_len[s], q_pos[i]) / c;
+  const SeqMeta sm = seq_meta(q_seq, seq_len, nullptr, seq_blk0, i);
+  const int nb = visible_tokens(sm.len, q_pos[i]) / c;
   const int b_base = (blockIdx.x * kScoreWaves + wave) * kScoreTile;
   if (b_base >= nb) return;
 
@@ -72,7 +72,7 @@ score_mfma_kernel(const T* __restrict__ qidx, const T* __restrict__ kpool, int64
   const int b = b_base + n;
   const bool valid = b < nb;
   V8 kb[KS];
-  const T* krow = kpool + (seq_blk0[s] + (valid ? b : 0)) * kpool_ld + hf * (D / 2);
+  const T* krow = kpool + (sm.blk0 + (valid ? b : 0)) * kpool_ld + hf * (D / 2);
 #pragma unroll
   for (int st = 0; st < KS; ++st) {
     kb[st] = valid ? *reinterpret_cast<const V8*>(krow + st * 8) : V8{};
@@ -105,14 +105,14 @@ score_valu_kernel(const T* __restrict__ qidx, const T* __restrict__ kpool, int64
   __shared__ float sq[kValuQFloats];
   __shared__ float part[4][kValuBlocks];
   const int i = blockIdx.y;
-  const int s = q_seq[i];
-  const int nb = visible_tokens(seq_len[s], q_pos[i]) / c;
+  const SeqMeta sm = seq_meta(q_seq, seq_len, nullptr, seq_blk0, i);
+  const int nb = visible_tokens(sm.len, q_pos[i]) / c;
   const int b0 = blockIdx.x * kValuBlocks;
   if (b0 >= nb) return;
   const int lb = threadIdx.x % kValuBlocks;
   const int hg = threadIdx.x / kValuBlocks;
   const int b = b0 + lb;
-  const T* krow = kpool + (seq_blk0[s] + (b < nb ? b : 0)) * kpool_ld;
+  const T* krow = kpool + (sm.blk0 + (b < nb ? b : 0)) * kpool_ld;
   const T* q = qidx + (int64_t)i * h_idx * d_idx;
   const int heads_per_pass = kValuQFloats / d_idx;
   float sum = 0.f;

@@ -53,6 +53,13 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Key of row[min(idx, last)]: the index is clamped rather than the load guarded, so
+// consecutive loads issue back to back instead of each waiting behind a branch.
+// Callers mask keys past the row's end themselves.
+__device__ __forceinline__ uint32_t key_clamped(const float* __restrict__ row, int idx, int last) {
+  return order_key(row[idx < last ? idx : last]);
+}
+
 // Exclusive prefix sum of one int per thread over the workgroup; returns the
 // exclusive value and writes the total to *total.  `scratch` holds >= BLOCK/64 ints.
 template <int BLOCK>
@@ -113,7 +120,7 @@ __device__ void select_one_query(const float* __restrict__ row, int nb, int n_vi
   auto load_chunk = [&](int ch) {
     const int base = ch * CH + tid * KPT;
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) key[j] = (base + j < nb) ? order_key(row[base + j]) : 0u;
+    for (int j = 0; j < KPT; ++j) key[j] = key_clamped(row, base + j, nb - 1);
   };
   if (resident) load_chunk(0);
 
@@ -225,7 +232,7 @@ select_kernel(const float* __restrict__ scores, int64_t scores_ld, const int32_t
               int32_t* __restrict__ sel, int64_t sel_ld, int32_t* __restrict__ n_sel) {
   __shared__ WgSmem sm;
   const int i = blockIdx.x;
-  const int n_vis = visible_tokens(seq_len[q_seq[i]], q_pos[i]);
+  const int n_vis = visible_tokens(seq_meta(q_seq, seq_len, nullptr, nullptr, i).len, q_pos[i]);
   const int nb = n_vis / c;
   int32_t* out = sel + (int64_t)i * sel_ld;
   if (nb <= k_blk) {
@@ -238,104 +245,47 @@ select_kernel(const float* __restrict__ scores, int64_t scores_ld, const int32_t
 // ------------------------------------------------------------------ chunked select
 
 constexpr int kChunk = 2048;                         // blocks per chunk workgroup
-constexpr int kChunkThreads = 256;
-constexpr int kChunkKpt = kChunk / kChunkThreads;   // 8
+constexpr int kHistThreads = 256;
+constexpr int kHistKpt = kChunk / kHistThreads;      // 8
+constexpr int kSelThreads = 1024;
+constexpr int kSelKpt = kChunk / kSelThreads;        // 2
 constexpr int kTopBits = 12;
 constexpr int kBins1 = 1 << kTopBits;                // 4096 bins of the top 12 bits
 constexpr int kHistCopies = 4;
-constexpr int kCandCap = 16384;                      // candidates the final step holds in LDS
-constexpr int kMaxChunks = 2048;                     // chunks per query the final step tallies
-constexpr int kFinalThreads = 1024;
+constexpr int kEntCap = 16384;                       // entries the last workgroup holds in LDS
+constexpr int kMaxChunks = 2048;                     // chunks per query it tallies
 
-// Per-query control words in the workspace.
-enum { CT_FALLBACK = 0, CT_T = 1, CT_CUT = 2, CT_WORDS = 16 };
+struct QueryRowInfo {
+  int nb, n_vis;                                     // visible complete blocks, visible positions
+};
 
-struct ChunkWs {
-  // per query: ghist[kBins1] | ctrl[CT_WORDS] | n_above[g] | n_cand[g] | offsets[g] | cand[g][kChunk] (u64)
+// Scratch of one query: bin and remaining count from the histogram pass, the
+// number of entries each chunk kept, and each chunk's entries (index order).
+struct ChunkScratch {
   char* base;
   size_t q_stride;
   int g;
-  __device__ __host__ uint32_t* ghist(int q) const { return (uint32_t*)(base + q * q_stride); }
-  __device__ __host__ uint32_t* ctrl(int q) const { return ghist(q) + kBins1; }
-  __device__ __host__ uint32_t* n_above(int q) const { return ctrl(q) + CT_WORDS; }
-  __device__ __host__ uint32_t* n_cand(int q) const { return n_above(q) + g; }
-  __device__ __host__ uint32_t* offsets(int q) const { return n_cand(q) + g; }
-  static __device__ __host__ size_t head_bytes(int g) {
-    return ((size_t)(kBins1 + CT_WORDS + 3 * (size_t)g) * 4 + 255) / 256 * 256;
-  }
-  __device__ __host__ uint64_t* cand(int q, int w) const {
+  static __device__ __host__ size_t head_bytes(int g) { return ((size_t)(16 + g) * 4 + 255) / 256 * 256; }
+  __device__ uint32_t* ctrl(int q) const { return (uint32_t*)(base + q * q_stride); }
+  __device__ uint32_t* n_ent(int q) const { return ctrl(q) + 16; }
+  __device__ uint64_t* ent(int q, int w) const {
     return (uint64_t*)(base + q * q_stride + head_bytes(g)) + (size_t)w * kChunk;
   }
   static __host__ size_t query_bytes(int g) { return head_bytes(g) + (size_t)g * kChunk * 8; }
 };
 
-struct QueryRow {
-  int nb, n_vis;
-};
-__device__ __forceinline__ QueryRow query_row(const int32_t* seq_len, const int32_t* q_seq, const int32_t* q_pos,
-                                              int q, int c) {
-  const int n_vis = visible_tokens(seq_len[q_seq[q]], q_pos[q]);
-  return QueryRow{n_vis / c, n_vis};
-}
-
-// Keys of this chunk, read before the query's length is known (indices up to the
-// row's capacity are valid memory; those past nb are masked by the caller).
-// `contiguous`: thread t holds blocks [t*8, t*8+8) (index order); otherwise
-// j*256 + t (coalesced).
-template <bool contiguous>
-__device__ __forceinline__ void load_chunk_keys(const float* __restrict__ row, int64_t row_cap, int base,
-                                                uint32_t (&key)[kChunkKpt], int (&idx)[kChunkKpt]) {
-#pragma unroll
-  for (int j = 0; j < kChunkKpt; ++j) {
-    idx[j] = contiguous ? base + (int)threadIdx.x * kChunkKpt + j : base + j * kChunkThreads + (int)threadIdx.x;
-    key[j] = idx[j] < row_cap ? order_key(row[idx[j]]) : 0u;
-  }
-}
-
-__global__ void __launch_bounds__(256) chunk_zero_kernel(ChunkWs ws) {
-  uint32_t* h = ws.ghist(blockIdx.x);
-  for (int e = threadIdx.x; e < kBins1 + CT_WORDS; e += blockDim.x) h[e] = 0u;  // ghist and ctrl are adjacent
-}
-
-__global__ void __launch_bounds__(kChunkThreads)
-chunk_hist_kernel(const float* __restrict__ scores, int64_t scores_ld, const int32_t* __restrict__ seq_len,
-                  const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos, int c, int k_blk, ChunkWs ws) {
-  constexpr int kStride = kBins1 + 1;
-  __shared__ uint32_t h[kHistCopies * kStride];
-  const int q = blockIdx.y, tid = threadIdx.x;
-  const int base = blockIdx.x * kChunk;
-  uint32_t key[kChunkKpt];
-  int idx[kChunkKpt];
-  load_chunk_keys<false>(scores + (int64_t)q * scores_ld, scores_ld, base, key, idx);
-  for (int e = tid; e < kHistCopies * kStride; e += kChunkThreads) h[e] = 0u;
-  const QueryRow qr = query_row(seq_len, q_seq, q_pos, q, c);
-  if (qr.nb <= k_blk || base >= qr.nb) return;      // uniform over the workgroup
-  __syncthreads();
-  uint32_t* mine = h + (tid & (kHistCopies - 1)) * kStride;
-#pragma unroll
-  for (int j = 0; j < kChunkKpt; ++j)
-    if (idx[j] < qr.nb) atomicAdd(&mine[key[j] >> (32 - kTopBits)], 1u);
-  __syncthreads();
-  uint32_t* g = ws.ghist(q);
-  for (int b = tid; b < kBins1; b += kChunkThreads) {
-    uint32_t n = 0;
-#pragma unroll
-    for (int cp = 0; cp < kHistCopies; ++cp) n += h[cp * kStride + b];
-    if (n) atomicAdd(&g[b], n);
-  }
-}
-
-// Bin holding the k-th largest key of the query histogram (`cnt` = this thread's 16
-// bins [t*16, t*16+16)), and the number of keys in higher bins, to all threads.
-__device__ __forceinline__ void find_top_bin(const uint32_t (&cnt)[kBins1 / kChunkThreads], int k, int* lds_scan,
-                                             int* out_bin, int* out_above) {
-  constexpr int PER = kBins1 / kChunkThreads;
+// Bin holding the k-th largest key of a histogram split as 16 bins per thread
+// (thread t holds bins [t*16, t*16+16)), and the number of keys in higher bins,
+// to all threads of the 256-thread workgroup.
+__device__ __forceinline__ void find_top_bin(const uint32_t (&cnt)[16], int k, int* lds_scan, int* out_bin,
+                                             int* out_above) {
+  constexpr int PER = 16;
   const int tid = threadIdx.x;
   int sum = 0;
 #pragma unroll
   for (int j = 0; j < PER; ++j) sum += (int)cnt[j];
   int total;
-  const int below_incl = block_exclusive_scan<kChunkThreads>(sum, lds_scan, &total) + sum;
+  const int below_incl = block_exclusive_scan<256>(sum, lds_scan, &total) + sum;
   int above = total - below_incl;                    // keys in bins >= (t+1)*16
 #pragma unroll
   for (int j = PER - 1; j >= 0; --j) {
@@ -349,164 +299,208 @@ __device__ __forceinline__ void find_top_bin(const uint32_t (&cnt)[kBins1 / kChu
   __syncthreads();
 }
 
-__global__ void __launch_bounds__(kChunkThreads)
-chunk_cand_kernel(const float* __restrict__ scores, int64_t scores_ld, const int32_t* __restrict__ seq_len,
-                  const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos, int c, int k_blk, ChunkWs ws) {
-  constexpr int PER = kBins1 / kChunkThreads;
-  constexpr int W = kChunkThreads / kWave;
-  __shared__ int scan[W + 1];
-  __shared__ int sh_bin, sh_above;
-  __shared__ int wave_cand[W], wave_gt[W];
-  const int q = blockIdx.y, tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-  const int base = blockIdx.x * kChunk;
-  uint32_t key[kChunkKpt];
-  int idx[kChunkKpt];
-  load_chunk_keys<false>(scores + (int64_t)q * scores_ld, scores_ld, base, key, idx);
-  uint32_t hc[PER];
-  const uint32_t* gh = ws.ghist(q);
-#pragma unroll
-  for (int j = 0; j < PER; ++j) hc[j] = gh[tid * PER + j];
-  const QueryRow qr = query_row(seq_len, q_seq, q_pos, q, c);
-  if (qr.nb <= k_blk || base >= qr.nb) return;
-  find_top_bin(hc, k_blk, scan, &sh_bin, &sh_above);
-  const uint32_t bin = (uint32_t)sh_bin;
-  // this thread's candidates (top bits == bin) and keys above the bin
-  uint64_t masks[kChunkKpt];
-  int n_gt = 0, n_c = 0;
-#pragma unroll
-  for (int j = 0; j < kChunkKpt; ++j) {
-    const bool ok = idx[j] < qr.nb;
-    const uint32_t kb = key[j] >> (32 - kTopBits);
-    n_gt += (ok && kb > bin) ? 1 : 0;
-    masks[j] = __ballot(ok && kb == bin);
-    n_c += __popcll(masks[j]);                       // the wave's candidates (same in every lane)
-  }
-  n_gt = wave_sum_int(n_gt);
-  if (lane == 0) {
-    wave_cand[wave] = n_c;
-    wave_gt[wave] = n_gt;
+__device__ __forceinline__ uint32_t coherent_load(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Visible complete blocks of query q.
+__device__ __forceinline__ QueryRowInfo query_blocks(const int32_t* seq_len, const int32_t* q_seq,
+                                                     const int32_t* q_pos, int q, int c) {
+  const SeqMeta m = seq_meta(q_seq, seq_len, nullptr, nullptr, q);
+  const int n_vis = visible_tokens(m.len, q_pos[q]);
+  return QueryRowInfo{n_vis / c, n_vis};
+}
+
+// True in every thread of the workgroup that arrives last at `counter` out of `n`
+// (the counter is returned to zero by that workgroup).  Releases this workgroup's
+// writes before arriving and acquires the others' in the last one.
+__device__ __forceinline__ bool arrive_last(uint32_t* counter, int n, int* lds_flag) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __threadfence();
+    const uint32_t prev = atomicAdd(counter, 1u);
+    *lds_flag = (prev == (uint32_t)(n - 1));
   }
   __syncthreads();
-  int slot = 0, tot_c = 0, tot_gt = 0;
-#pragma unroll
-  for (int w = 0; w < W; ++w) {
-    slot += w < wave ? wave_cand[w] : 0;
-    tot_c += wave_cand[w];
-    tot_gt += wave_gt[w];
+  const bool last = *lds_flag != 0;
+  if (last) {
+    __threadfence();
+    if (threadIdx.x == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  uint64_t* seg = ws.cand(q, blockIdx.x);
-  const uint64_t below = (1ull << lane) - 1ull;
+  return last;
+}
+
+// Pass 1 (one workgroup per chunk): the chunk's histogram of the top 12 key bits is
+// added to the query's histogram; the last chunk to arrive finds the bin holding the
+// K_blk-th largest key, records it with the number still to take inside it, and
+// clears the histogram for the next call.
+__global__ void __launch_bounds__(kHistThreads)
+chunk_hist_kernel(const float* __restrict__ scores, int64_t scores_ld, const int32_t* __restrict__ seq_len,
+                  const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos, int c, int k_blk,
+                  WsState* __restrict__ st, ChunkScratch sc) {
+  constexpr int kStride = kBins1 + 1;
+  constexpr int PER = kBins1 / kHistThreads;         // 16 bins per thread in the last workgroup
+  __shared__ uint32_t h[kHistCopies * kStride];
+  __shared__ int scan[kHistThreads / kWave + 1];
+  __shared__ int sh_last, sh_bin, sh_above;
+  const int q = blockIdx.y, tid = threadIdx.x;
+  const int base = blockIdx.x * kChunk;
+  const float* row = scores + (int64_t)q * scores_ld;
+  // keys read before the query's length is known (indices below scores_ld are valid)
+  uint32_t key[kHistKpt];
+  int idx[kHistKpt];
 #pragma unroll
-  for (int j = 0; j < kChunkKpt; ++j) {
-    if ((masks[j] >> lane) & 1ull)
-      seg[slot + __popcll(masks[j] & below)] = ((uint64_t)key[j] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)idx[j]);
-    slot += __popcll(masks[j]);
+  for (int j = 0; j < kHistKpt; ++j) {
+    idx[j] = base + j * kHistThreads + tid;
+    key[j] = key_clamped(row, idx[j], (int)scores_ld - 1);
   }
+  for (int e = tid; e < kHistCopies * kStride; e += kHistThreads) h[e] = 0u;
+  const QueryRowInfo qr = query_blocks(seq_len, q_seq, q_pos, q, c);
+  if (qr.nb <= k_blk || base >= qr.nb) return;      // uniform over the workgroup
+  const int n_chunks = (qr.nb + kChunk - 1) / kChunk;
+  __syncthreads();
+  uint32_t* mine = h + (tid & (kHistCopies - 1)) * kStride;
+#pragma unroll
+  for (int j = 0; j < kHistKpt; ++j)
+    if (idx[j] < qr.nb) atomicAdd(&mine[key[j] >> (32 - kTopBits)], 1u);
+  __syncthreads();
+  uint32_t* g = st->ghist[q];
+  for (int b = tid; b < kBins1; b += kHistThreads) {
+    uint32_t n = 0;
+#pragma unroll
+    for (int cp = 0; cp < kHistCopies; ++cp) n += h[cp * kStride + b];
+    if (n) atomicAdd(&g[b], n);
+  }
+  if (!arrive_last(&st->hist_done[q], n_chunks, &sh_last)) return;
+  uint32_t hc[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) hc[j] = coherent_load(&g[tid * PER + j]);
+  find_top_bin(hc, k_blk, scan, &sh_bin, &sh_above);
+#pragma unroll
+  for (int j = 0; j < PER; ++j) g[tid * PER + j] = 0u;
   if (tid == 0) {
-    ws.n_above(q)[blockIdx.x] = (uint32_t)tot_gt;
-    ws.n_cand(q)[blockIdx.x] = (uint32_t)tot_c;
+    uint32_t* ctrl = sc.ctrl(q);
+    ctrl[0] = (uint32_t)sh_bin;
+    ctrl[1] = (uint32_t)(k_blk - sh_above);
   }
 }
 
-struct FinalSmem {
-  uint64_t cand[kCandCap];                           // 128 KiB
+struct SelSmem {
+  uint64_t ent[kEntCap];                             // 128 KiB
   uint32_t hist[8 * kCopyStride];
-  uint32_t tally[kMaxChunks];                        // kept blocks per chunk
-  uint32_t cpre[kMaxChunks + 1];                     // exclusive prefix of candidates per chunk
-  int scan[kFinalThreads / kWave + 1];
+  uint32_t cpre[kMaxChunks + 1];                     // exclusive prefix of entries per chunk
+  int scan[kSelThreads / kWave + 1];
   int pick[3];
+  int last;
   uint64_t cut;
 };
 
-__global__ void __launch_bounds__(kFinalThreads)
-chunk_final_kernel(const float* __restrict__ scores, int64_t scores_ld, const int32_t* __restrict__ seq_len,
-                   const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos, int c, int k_blk,
-                   int32_t* __restrict__ sel, int64_t sel_ld, int32_t* __restrict__ n_sel, ChunkWs ws) {
+// Pass 2 (one workgroup per chunk): the chunk keeps, in index order, every block
+// whose key lies in the recorded bin or above as (key << 32 | ~index) -- unique
+// values ordered exactly as (score desc, index asc).  The last chunk to arrive
+// gathers all entries, radix-selects the cut among those inside the bin (8-bit
+// digits below the shared 12 bits, stopping once the chosen bin holds one value),
+// and writes the list: every entry at or above the cut in index order, then the
+// tail and the padding.
+__global__ void __launch_bounds__(kSelThreads)
+chunk_select_kernel(const float* __restrict__ scores, int64_t scores_ld, const int32_t* __restrict__ seq_len,
+                    const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos, int c, int k_blk,
+                    int32_t* __restrict__ sel, int64_t sel_ld, int32_t* __restrict__ n_sel, WsState* __restrict__ st,
+                    ChunkScratch sc) {
   __shared__ union {
-    FinalSmem f;
+    SelSmem f;
     WgSmem w;
   } sm;
-  constexpr int PER = kMaxChunks / kFinalThreads;    // chunks per thread, contiguous
-  const int q = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid % kWave;
-  // per-chunk counts, read before the query's length is known (entries past the
-  // query's chunks are ignored)
-  uint32_t na[PER], nc[PER];
-  const int gcap = ws.g < kMaxChunks ? ws.g : kMaxChunks;
+  const int q = blockIdx.y, tid = threadIdx.x, lane = tid % kWave;
+  const int base = blockIdx.x * kChunk;
+  const float* row = scores + (int64_t)q * scores_ld;
+  uint32_t key[kSelKpt];
+  int idx[kSelKpt];
 #pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const int w = tid * PER + j;
-    na[j] = w < gcap ? ws.n_above(q)[w] : 0u;
-    nc[j] = w < gcap ? ws.n_cand(q)[w] : 0u;
+  for (int j = 0; j < kSelKpt; ++j) {
+    idx[j] = base + tid * kSelKpt + j;               // contiguous: index order across threads
+    key[j] = key_clamped(row, idx[j], (int)scores_ld - 1);
   }
-  const QueryRow qr = query_row(seq_len, q_seq, q_pos, q, c);
+  const uint32_t* ctrl = sc.ctrl(q);
+  const uint32_t bin = ctrl[0];
+  int k_rem = (int)ctrl[1];
+  const QueryRowInfo qr = query_blocks(seq_len, q_seq, q_pos, q, c);
   int32_t* out = sel + (int64_t)q * sel_ld;
-  if (qr.nb <= k_blk) {
-    write_dense<kFinalThreads>(out, sel_ld, qr.n_vis, n_sel + q);
+  if (qr.nb <= k_blk) {                              // every block fits: dense
+    if (blockIdx.x == 0) write_dense<kSelThreads>(out, sel_ld, qr.n_vis, n_sel + q);
     return;
   }
-  uint32_t* ctrl = ws.ctrl(q);
+  if (base >= qr.nb) return;
   const int n_chunks = (qr.nb + kChunk - 1) / kChunk;
-  int la = 0, lc = 0;
+  // this chunk's entries, in index order
+  bool keep[kSelKpt];
+  int n = 0;
+#pragma unroll
+  for (int j = 0; j < kSelKpt; ++j) {
+    keep[j] = idx[j] < qr.nb && (key[j] >> (32 - kTopBits)) >= bin;
+    n += keep[j] ? 1 : 0;
+  }
+  int tot;
+  int slot = block_exclusive_scan<kSelThreads>(n, sm.f.scan, &tot);
+  uint64_t* seg = sc.ent(q, blockIdx.x);
+#pragma unroll
+  for (int j = 0; j < kSelKpt; ++j)
+    if (keep[j]) seg[slot++] = ((uint64_t)key[j] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)idx[j]);
+  if (tid == 0) sc.n_ent(q)[blockIdx.x] = (uint32_t)tot;
+  if (!arrive_last(&st->sel_done[q], n_chunks, &sm.f.last)) return;
+
+  // ---- the last chunk: gather, cut, write ---------------------------------------
+  constexpr int PER = kMaxChunks / kSelThreads;      // 2 chunk counts per thread
+  const int gcap = n_chunks < kMaxChunks ? n_chunks : kMaxChunks;
+  uint32_t ne[PER];
+  int loc = 0;
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
     const int w = tid * PER + j;
-    if (w >= n_chunks) na[j] = nc[j] = 0u;
-    la += (int)na[j];
-    lc += (int)nc[j];
+    ne[j] = w < gcap ? coherent_load(&sc.n_ent(q)[w]) : 0u;
+    loc += (int)ne[j];
   }
-  int tot_above, n_cand;
-  (void)block_exclusive_scan<kFinalThreads>(la, sm.f.scan, &tot_above);
-  int cp = block_exclusive_scan<kFinalThreads>(lc, sm.f.scan, &n_cand);
-  if (n_cand > kCandCap || n_chunks > kMaxChunks) {
-    if (tid == 0) ctrl[CT_FALLBACK] = 1u;
-    select_one_query<kFinalThreads, 8>(scores + (int64_t)q * scores_ld, qr.nb, qr.n_vis, c, k_blk, out, sel_ld,
-                                       n_sel + q, sm.w);
+  int n_ent;
+  int cp = block_exclusive_scan<kSelThreads>(loc, sm.f.scan, &n_ent);
+  if (n_ent > kEntCap || n_chunks > kMaxChunks) {   // massive exact ties: per-query select over the row
+    select_one_query<kSelThreads, 8>(row, qr.nb, qr.n_vis, c, k_blk, out, sel_ld, n_sel + q, sm.w);
     return;
   }
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
-    const int w = tid * PER + j;
-    sm.f.cpre[w] = (uint32_t)cp;
-    sm.f.tally[w] = na[j];
-    cp += (int)nc[j];
+    sm.f.cpre[tid * PER + j] = (uint32_t)cp;
+    cp += (int)ne[j];
   }
-  if (tid == 0) sm.f.cpre[kMaxChunks] = (uint32_t)n_cand;
   __syncthreads();
-  // gather the candidates: entry e lives in the chunk whose prefix range holds it
-  for (int e = tid; e < n_cand; e += kFinalThreads) {
+  for (int e = tid; e < n_ent; e += kSelThreads) {
     int lo = 0, hi = n_chunks - 1;                   // largest w with cpre[w] <= e
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
       if ((int)sm.f.cpre[mid] <= e) lo = mid;
       else hi = mid - 1;
     }
-    sm.f.cand[e] = ws.cand(q, lo)[e - (int)sm.f.cpre[lo]];
+    sm.f.ent[e] = sc.ent(q, lo)[e - (int)sm.f.cpre[lo]];
   }
-  int k_rem = k_blk - tot_above;                     // >= 1 by the choice of the bin
-  if (tid == 0) sm.f.pick[2] = 0;
   __syncthreads();
-  // Radix select of the k_rem-th largest candidate over the 52 bits below the
-  // shared top 12, 8 bits at a time (the last digit has 4), stopping once the
-  // chosen bin holds a single value -- values are unique, so it always ends.
-  uint64_t prefix = sm.f.cand[0] >> (64 - kTopBits);
+  // k_rem-th largest value among the entries inside the bin (top 12 bits == bin)
+  uint64_t prefix = bin;
   for (int shift = 64 - kTopBits; shift > 0;) {
     const int width = shift >= 8 ? 8 : shift;
     shift -= width;
     const uint32_t dmask = (1u << width) - 1u;
-    for (int e = tid; e < 8 * kCopyStride; e += kFinalThreads) sm.f.hist[e] = 0u;
+    for (int e = tid; e < 8 * kCopyStride; e += kSelThreads) sm.f.hist[e] = 0u;
     __syncthreads();
     uint32_t* mine = sm.f.hist + (lane & 7) * kCopyStride;
-    for (int e = tid; e < n_cand; e += kFinalThreads) {
-      const uint64_t v = sm.f.cand[e];
+    for (int e = tid; e < n_ent; e += kSelThreads) {
+      const uint64_t v = sm.f.ent[e];
       if ((v >> (shift + width)) == prefix) atomicAdd(&mine[(uint32_t)(v >> shift) & dmask], 1u);
     }
     __syncthreads();
     if (tid < kBins) {                               // 4 whole waves
-      uint32_t n = 0;
+      uint32_t cnt = 0;
 #pragma unroll
-      for (int cpy = 0; cpy < 8; ++cpy) n += sm.f.hist[cpy * kCopyStride + tid];
-      sm.f.hist[tid] = n;                            // copy 0 now holds the totals
+      for (int cpy = 0; cpy < 8; ++cpy) cnt += sm.f.hist[cpy * kCopyStride + tid];
+      sm.f.hist[tid] = cnt;                          // copy 0 now holds the totals
     }
     __syncthreads();
     int ge_in_wave = 0;
@@ -532,8 +526,8 @@ chunk_final_kernel(const float* __restrict__ scores, int64_t scores_ld, const in
     const int cnt = sm.f.pick[2];
     __syncthreads();
     if (cnt == 1 || shift == 0) {                    // the cut is the single value left in the bin
-      for (int e = tid; e < n_cand; e += kFinalThreads) {
-        const uint64_t v = sm.f.cand[e];
+      for (int e = tid; e < n_ent; e += kSelThreads) {
+        const uint64_t v = sm.f.ent[e];
         if ((v >> shift) == prefix) sm.f.cut = v;
       }
       __syncthreads();
@@ -541,72 +535,205 @@ chunk_final_kernel(const float* __restrict__ scores, int64_t scores_ld, const in
     }
   }
   const uint64_t cut = sm.f.cut;
-  // kept blocks per chunk: those above the bin plus the kept candidates
-  for (int e = tid; e < n_cand; e += kFinalThreads) {
-    const uint64_t v = sm.f.cand[e];
-    if (v >= cut) atomicAdd(&sm.f.tally[(0xFFFFFFFFu - (uint32_t)v) / kChunk], 1u);
-  }
-  __syncthreads();
-  int loc = 0;
-#pragma unroll
-  for (int j = 0; j < PER; ++j) loc += (int)sm.f.tally[tid * PER + j];   // entries past n_chunks are 0
-  int tot;
-  int run = block_exclusive_scan<kFinalThreads>(loc, sm.f.scan, &tot);
-  uint32_t* offs = ws.offsets(q);
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const int w = tid * PER + j;
-    if (w < n_chunks) offs[w] = (uint32_t)run;
-    run += (int)sm.f.tally[w];
-  }
-  if (tid == 0) {
-    ctrl[CT_T] = (uint32_t)(cut >> 32);
-    ctrl[CT_CUT] = 0xFFFFFFFFu - (uint32_t)cut;
-  }
-  write_tail<kFinalThreads>(out, sel_ld, qr.nb, qr.n_vis, c, k_blk, n_sel + q);
-}
-
-__global__ void __launch_bounds__(kChunkThreads)
-chunk_emit_kernel(const float* __restrict__ scores, int64_t scores_ld, const int32_t* __restrict__ seq_len,
-                  const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos, int c, int k_blk,
-                  int32_t* __restrict__ sel, int64_t sel_ld, ChunkWs ws) {
-  __shared__ int scan[kChunkThreads / kWave + 1];
-  const int q = blockIdx.y;
-  const int base = blockIdx.x * kChunk;
-  uint32_t key[kChunkKpt];
-  int idx[kChunkKpt];
-  load_chunk_keys<true>(scores + (int64_t)q * scores_ld, scores_ld, base, key, idx);
-  const uint32_t* ctrl = ws.ctrl(q);
-  const uint32_t fallback = ctrl[CT_FALLBACK], T = ctrl[CT_T], cut = ctrl[CT_CUT];
-  const int off = (int)ws.offsets(q)[blockIdx.x];
-  const QueryRow qr = query_row(seq_len, q_seq, q_pos, q, c);
-  if (qr.nb <= k_blk || base >= qr.nb || fallback) return;
-  bool take[kChunkKpt];
-  int n = 0;
-#pragma unroll
-  for (int j = 0; j < kChunkKpt; ++j) {
-    take[j] = idx[j] < qr.nb && (key[j] > T || (key[j] == T && (uint32_t)idx[j] <= cut));
-    n += take[j] ? 1 : 0;
-  }
-  int tot;
-  int o = off + block_exclusive_scan<kChunkThreads>(n, scan, &tot);
-  int32_t* out = sel + (int64_t)q * sel_ld;
-#pragma unroll
-  for (int j = 0; j < kChunkKpt; ++j) {
-    if (take[j] && o < k_blk) {                      // o < k_blk always; the bound only guards memory
-      const int32_t p0 = (int32_t)idx[j] * c;
+  // kept entries (value >= cut) in index order -> positions
+  const int per = (n_ent + kSelThreads - 1) / kSelThreads;
+  const int e0 = tid * per, e1 = min(n_ent, e0 + per);
+  int nk = 0;
+  for (int e = e0; e < e1; ++e) nk += sm.f.ent[e] >= cut ? 1 : 0;
+  int ktot;
+  int o = block_exclusive_scan<kSelThreads>(nk, sm.f.scan, &ktot);
+  for (int e = e0; e < e1; ++e) {
+    const uint64_t v = sm.f.ent[e];
+    if (v >= cut && o < k_blk) {                     // o < k_blk always; the bound only guards memory
+      const int32_t p0 = (int32_t)(0xFFFFFFFFu - (uint32_t)v) * c;
       int32_t* dst = out + (int64_t)o * c;
       for (int t = 0; t < c; ++t) dst[t] = p0 + t;
       ++o;
     }
   }
+  write_tail<kSelThreads>(out, sel_ld, qr.nb, qr.n_vis, c, k_blk, n_sel + q);
+}
+
+// ------------------------------------------------------ one wide workgroup per row
+
+// Decode rows of up to 32768 blocks: one 1024-thread workgroup holds the whole row in
+// registers and needs no workspace.  Thread t owns blocks j*1024 + t (j < KPT), so
+// every load is coalesced.  The K_blk-th largest key T is found by radix select
+// over the registers, most significant digit first (11, 11, then 10 bits), each
+// pass histogramming the keys that match the digits fixed so far; a pass whose
+// chosen bin is taken whole (its count equals the number still to take) ends the
+// search early, and the remaining digits do not matter.  Kept blocks (above the
+// fixed prefix, or equal to it) are marked in an LDS bitmap of the row; when the
+// search ran to the full 32 bits, the keys equal to T are marked in a second bitmap
+// and only the first ones in index order are taken.  One prefix sum over the words'
+// popcounts then places every kept block in index order.
+constexpr int kWideThreads = 1024;
+constexpr int kWideMaxKpt = 32;
+constexpr int kWideCopies = 8;                       // lane-privatised copies in the first pass
+constexpr int kWideBins = 2048;
+constexpr int kWideStride = kWideBins + 1;
+constexpr int kWideWords = kWideThreads * kWideMaxKpt / 32;   // bitmap words, one per thread
+
+struct WideSmem {
+  uint32_t h1[kWideCopies * kWideStride];            // pass 1, then pass 3 in copy 0
+  uint32_t h2[kWideBins];                            // pass 2
+  uint32_t keep[kWideWords];                         // blocks above the prefix (or in its bin)
+  uint32_t tie[kWideWords];                          // blocks equal to T (full-width search)
+  int scan[kWideThreads / kWave + 1];
+  int pick[3];
+};
+
+// The bin holding the k-th largest of the counted keys, for a histogram held as PER
+// consecutive bins per thread (thread t: bins [t*PER, t*PER + PER)).  Writes bin,
+// keys in higher bins and keys in the bin to pick[0..2] and synchronises.
+template <int PER>
+__device__ __forceinline__ void wide_pick(const uint32_t (&cnt)[PER], int k, WideSmem& sm) {
+  int sum = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) sum += (int)cnt[j];
+  int total;
+  const int below_incl = block_exclusive_scan<kWideThreads>(sum, sm.scan, &total) + sum;
+  int above = total - below_incl;                    // keys in bins >= (t+1)*PER
+#pragma unroll
+  for (int j = PER - 1; j >= 0; --j) {
+    const int gt = above, ge = above + (int)cnt[j];
+    if (gt < k && ge >= k) {
+      sm.pick[0] = (int)threadIdx.x * PER + j;
+      sm.pick[1] = gt;
+      sm.pick[2] = (int)cnt[j];
+    }
+    above = ge;
+  }
+  __syncthreads();
+}
+
+template <int KPT>
+__global__ void __launch_bounds__(kWideThreads)
+select_wide_kernel(const float* __restrict__ scores, int64_t scores_ld, const int32_t* __restrict__ seq_len,
+                   const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos, int c, int k_blk,
+                   int32_t* __restrict__ sel, int64_t sel_ld, int32_t* __restrict__ n_sel) {
+  __shared__ WideSmem sm;
+  const int q = blockIdx.x, tid = threadIdx.x, lane = tid % kWave;
+  const float* row = scores + (int64_t)q * scores_ld;
+  // The whole row is loaded up front and kept in registers for every pass; the
+  // query's length arrives with it (indices below scores_ld are valid memory).
+  const int last = (int)min(scores_ld, (int64_t)KPT * kWideThreads) - 1;
+  uint32_t key[KPT];
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) key[j] = key_clamped(row, j * kWideThreads + tid, last);
+  const QueryRowInfo qr = query_blocks(seq_len, q_seq, q_pos, q, c);
+  for (int e = tid; e < kWideCopies * kWideStride; e += kWideThreads) sm.h1[e] = 0u;
+  for (int e = tid; e < kWideBins; e += kWideThreads) sm.h2[e] = 0u;
+  sm.keep[tid] = 0u;
+  sm.tie[tid] = 0u;
+  int32_t* out = sel + (int64_t)q * sel_ld;
+  if (qr.nb <= k_blk) {
+    write_dense<kWideThreads>(out, sel_ld, qr.n_vis, n_sel + q);
+    return;
+  }
+  const int nb = min(qr.nb, KPT * kWideThreads);     // the launch guarantees qr.nb fits; the bitmap relies on it
+  __syncthreads();
+
+  // ---- pass 1: top 11 bits, 8 privatised copies -----------------------------------
+  {
+    uint32_t* mine = sm.h1 + (lane & (kWideCopies - 1)) * kWideStride;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j)
+      if (j * kWideThreads + tid < nb) atomicAdd(&mine[key[j] >> 21], 1u);
+  }
+  __syncthreads();
+  {
+    uint32_t cnt[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      uint32_t n = 0;
+#pragma unroll
+      for (int cp = 0; cp < kWideCopies; ++cp) n += sm.h1[cp * kWideStride + tid * 2 + j];
+      cnt[j] = n;
+    }
+    wide_pick<2>(cnt, k_blk, sm);
+  }
+  uint32_t prefix = (uint32_t)sm.pick[0];
+  int k_rem = k_blk - sm.pick[1];
+  int width = 11;                                    // bits of the key the prefix fixes
+  bool whole = sm.pick[2] == k_rem;
+  __syncthreads();                                   // pick[] is rewritten below
+  // ---- pass 2: next 11 bits among keys in the bin ---------------------------------
+  if (!whole) {
+    sm.h1[tid] = 0u;                                 // copy 0 serves pass 3
+#pragma unroll
+    for (int j = 0; j < KPT; ++j)
+      if (j * kWideThreads + tid < nb && (key[j] >> 21) == prefix) atomicAdd(&sm.h2[(key[j] >> 10) & 2047u], 1u);
+    __syncthreads();
+    uint32_t cnt[2] = {sm.h2[tid * 2], sm.h2[tid * 2 + 1]};
+    wide_pick<2>(cnt, k_rem, sm);
+    prefix = (prefix << 11) | (uint32_t)sm.pick[0];
+    k_rem -= sm.pick[1];
+    width = 22;
+    whole = sm.pick[2] == k_rem;
+    __syncthreads();
+    // ---- pass 3: last 10 bits ------------------------------------------------------
+    if (!whole) {
+#pragma unroll
+      for (int j = 0; j < KPT; ++j)
+        if (j * kWideThreads + tid < nb && (key[j] >> 10) == prefix) atomicAdd(&sm.h1[key[j] & 1023u], 1u);
+      __syncthreads();
+      uint32_t cnt1[1] = {tid < 1024 ? sm.h1[tid] : 0u};
+      wide_pick<1>(cnt1, k_rem, sm);
+      prefix = (prefix << 10) | (uint32_t)sm.pick[0];
+      k_rem -= sm.pick[1];
+      width = 32;
+      whole = sm.pick[2] == k_rem;
+      __syncthreads();
+    }
+  }
+  // ---- kept blocks -> bitmap -----------------------------------------------------------
+  // Above the prefix, or inside its bin when the bin is taken whole, always kept; at
+  // full width with the bin not whole, the keys equal to T go to the tie bitmap.
+  const int shift = 32 - width;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const int idx = j * kWideThreads + tid;
+    if (idx < nb) {
+      const uint32_t hi = (uint32_t)((uint64_t)key[j] >> shift);
+      if (hi > prefix || (whole && hi == prefix)) atomicOr(&sm.keep[idx >> 5], 1u << (idx & 31));
+      else if (hi == prefix) atomicOr(&sm.tie[idx >> 5], 1u << (idx & 31));
+    }
+  }
+  __syncthreads();
+  uint32_t word = sm.keep[tid];
+  if (!whole) {                                      // the first k_rem tied blocks in index order
+    uint32_t t = sm.tie[tid];
+    int n_tie;
+    const int before = block_exclusive_scan<kWideThreads>(__popc(t), sm.scan, &n_tie);
+    int take = k_rem - before;
+    while (t != 0u && take > 0) {
+      const uint32_t low = t & (0u - t);
+      word |= low;
+      t ^= low;
+      --take;
+    }
+  }
+  int ktot;
+  int o = block_exclusive_scan<kWideThreads>(__popc(word), sm.scan, &ktot);
+  while (word != 0u && o < k_blk) {                  // o < k_blk always; the bound only guards memory
+    const int b = __ffs(word) - 1;
+    word &= word - 1u;
+    const int32_t p0 = (tid * 32 + b) * c;
+    int32_t* dst = out + (int64_t)o * c;
+    for (int t = 0; t < c; ++t) dst[t] = p0 + t;
+    ++o;
+  }
+  write_tail<kWideThreads>(out, sel_ld, nb, qr.n_vis, c, k_blk, n_sel + q);
 }
 
 // ---------------------------------------------------------------------------- host
 
+constexpr long long kWideMax = (long long)kWideThreads * kWideMaxKpt;   // blocks one wide workgroup holds
+
 static bool use_chunked(const sa_dims& d, int n_q, int max_len) {
   const long long max_blocks = (long long)max_len / d.compress_ratio;
-  return n_q <= 64 && max_blocks > 4096 && max_blocks > d.top_k / d.compress_ratio;
+  return n_q <= kStateQueries && max_blocks > kWideMax && max_blocks > d.top_k / d.compress_ratio;
 }
 
 static int chunks_for(const sa_dims& d, int max_len) {
@@ -614,9 +741,9 @@ static int chunks_for(const sa_dims& d, int max_len) {
   return (int)((max_blocks + kChunk - 1) / kChunk);
 }
 
-size_t select_ws_bytes(const sa_dims& d, int n_q, int max_len) {
+size_t select_scratch_bytes(const sa_dims& d, int n_q, int max_len) {
   if (!use_chunked(d, n_q, max_len)) return 0;
-  return (size_t)n_q * ChunkWs::query_bytes(chunks_for(d, max_len));
+  return (size_t)n_q * ChunkScratch::query_bytes(chunks_for(d, max_len));
 }
 
 template <int BLOCK, int KPT>
@@ -635,22 +762,24 @@ hipError_t launch_select(const sa_dims& d, const CacheArgs& c, const float* scor
   const long long max_blocks = (long long)c.max_len / cr;
   if (use_chunked(d, n_q, c.max_len)) {
     const int g = chunks_for(d, c.max_len);
-    ChunkWs cw{(char*)ws, ChunkWs::query_bytes(g), g};
-    hipLaunchKernelGGL(chunk_zero_kernel, dim3(n_q), dim3(256), 0, stream, cw);
+    WsState* st = (WsState*)ws;
+    ChunkScratch sc{(char*)ws + SA_WS_STATE_BYTES, ChunkScratch::query_bytes(g), g};
     dim3 grid(g, n_q);
-    hipLaunchKernelGGL(chunk_hist_kernel, grid, dim3(kChunkThreads), 0, stream, scores, scores_ld, c.seq_len, q_seq,
-                       q_pos, cr, k_blk, cw);
-    hipLaunchKernelGGL(chunk_cand_kernel, grid, dim3(kChunkThreads), 0, stream, scores, scores_ld, c.seq_len, q_seq,
-                       q_pos, cr, k_blk, cw);
-    hipLaunchKernelGGL(chunk_final_kernel, dim3(n_q), dim3(kFinalThreads), 0, stream, scores, scores_ld, c.seq_len,
-                       q_seq, q_pos, cr, k_blk, sel, sel_ld, n_sel, cw);
-    hipLaunchKernelGGL(chunk_emit_kernel, grid, dim3(kChunkThreads), 0, stream, scores, scores_ld, c.seq_len, q_seq,
-                       q_pos, cr, k_blk, sel, sel_ld, cw);
+    hipLaunchKernelGGL(chunk_hist_kernel, grid, dim3(kHistThreads), 0, stream, scores, scores_ld, c.seq_len, q_seq,
+                       q_pos, cr, k_blk, st, sc);
+    hipLaunchKernelGGL(chunk_select_kernel, grid, dim3(kSelThreads), 0, stream, scores, scores_ld, c.seq_len, q_seq,
+                       q_pos, cr, k_blk, sel, sel_ld, n_sel, st, sc);
     return hipGetLastError();
   }
-  if (n_q <= 64) {                                   // few queries, short rows: wide workgroups
-    if (max_blocks <= 1024 * 4) launch_select_t<1024, 4>(d, scores, scores_ld, c, q_seq, q_pos, n_q, sel, sel_ld, n_sel, stream);
-    else launch_select_t<1024, 8>(d, scores, scores_ld, c, q_seq, q_pos, n_q, sel, sel_ld, n_sel, stream);
+  if (n_q <= kStateQueries) {                        // few query tokens: one wide workgroup per row
+#define SA_WIDE(KPT_)                                                                                         \
+  hipLaunchKernelGGL(select_wide_kernel<KPT_>, dim3(n_q), dim3(kWideThreads), 0, stream, scores, scores_ld,  \
+                     c.seq_len, q_seq, q_pos, cr, k_blk, sel, sel_ld, n_sel)
+    if (max_blocks <= 1024 * 4) SA_WIDE(4);
+    else if (max_blocks <= 1024 * 8) SA_WIDE(8);
+    else if (max_blocks <= 1024 * 16) SA_WIDE(16);
+    else SA_WIDE(32);
+#undef SA_WIDE
   } else {
     if (max_blocks <= 256 * 8) launch_select_t<256, 8>(d, scores, scores_ld, c, q_seq, q_pos, n_q, sel, sel_ld, n_sel, stream);
     else if (max_blocks <= 256 * 16) launch_select_t<256, 16>(d, scores, scores_ld, c, q_seq, q_pos, n_q, sel, sel_ld, n_sel, stream);

@@ -50,7 +50,8 @@ class DeviceLayer:
         self.n_sel = torch.zeros((self.n_q,), dtype=torch.int32, device=device)
         self.out = torch.zeros((self.n_q, d.h_q, d.d_v), dtype=torch.float32, device=device)
         self.ws_bytes = sa.sparse_attn_workspace_bytes(self.dims, self.n_q, self.max_len)
-        self.ws = torch.empty((max(self.ws_bytes, 16),), dtype=torch.uint8, device=device)
+        # zero-filled once: the leading state region must start at zero (the library keeps it so)
+        self.ws = torch.zeros((max(self.ws_bytes, 16),), dtype=torch.uint8, device=device)
         self.n_pooled = torch.zeros((case.n_seq,), dtype=torch.int32, device=device)
         self.scale = case.scale
         self.cache = self._make_cache(self.k, self.v, self.kidx, self.kpool)

@@ -21,6 +21,10 @@ TORCH_DTYPE = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat1
 
 SA_OK, SA_ERR_NULL, SA_ERR_DIMS, SA_ERR_ARG, SA_ERR_WORKSPACE, SA_ERR_HIP = 0, -1, -2, -3, -4, -5
 
+# Leading bytes of a workspace that hold state between calls (zero-filled once by the
+# caller, kept at zero by the library); SA_WS_STATE_BYTES in the header.
+WS_STATE_BYTES = 1056768
+
 EXPORTS = (
     "sparse_attn_check_dims",
     "sparse_attn_workspace_bytes",

@@ -16,6 +16,7 @@ import torch
 import oracle
 import parity
 from indexer_top_block_amd import datagen
+from indexer_top_block_amd import sparse_attn as sa
 from indexer_top_block_amd.device import DeviceLayer
 
 pytestmark = pytest.mark.gpu
@@ -154,6 +155,23 @@ def test_ties_at_the_cut(gpu_lib):
     assert len(np.unique(s)) * 8 == len(s)
 
 
+def test_massive_ties(gpu_lib):
+    # one indexer head and a budget beyond the positive scores: the cut falls among
+    # ~10^4 exact zeros.  The one-workgroup selection resolves them with its tie
+    # bitmap; the chunked selection overflows its candidate buffer and hands the row
+    # to the per-query algorithm
+    d = dims(h_q=16, d_kq=128, d_v=128, h_idx=1, d_idx=64, compress_ratio=4, top_k=48000, dtype="bf16")
+    case = datagen.make_case("ties_wide_fallback", d, [80000], [0], [80000], seed=0, case_id=232, std=1.0,
+                             v_separate=False)
+    _, res = run_and_check(case)
+    assert np.count_nonzero(res[0]["scores32"] == 0.0) > 8192
+    d = dims(h_q=16, d_kq=128, d_v=128, h_idx=1, d_idx=64, compress_ratio=1, top_k=40000, dtype="bf16")
+    case = datagen.make_case("ties_chunked_fallback", d, [60000], [0], [60000], seed=0, case_id=233, std=1.0,
+                             v_separate=False)
+    _, res = run_and_check(case)
+    assert np.count_nonzero(res[0]["scores32"] == 0.0) > 16384
+
+
 def test_select_streams_long_score_rows(gpu_lib):
     # more blocks per query than one workgroup holds in registers: chunked passes
     d = dims(h_q=16, d_kq=128, d_v=128, h_idx=32, d_idx=64, compress_ratio=1, top_k=2048, dtype="bf16")
@@ -230,6 +248,36 @@ def test_incremental_pool_matches_one_shot(gpu_lib):
     inc.pool(max_new_blocks=1)
     torch.cuda.synchronize()
     assert inc.n_pooled.cpu().tolist() == [2, 9, 1024]
+
+
+def test_workspace_state_returns_to_zero(gpu_lib):
+    # chunked selection on long rows: repeated calls on one workspace give the same
+    # lists and leave the state region (histograms, arrival counters) at zero
+    # token-level rows of more than 32768 blocks take the chunked path
+    d = dims(h_q=16, d_kq=576, d_v=512, h_idx=64, d_idx=128, compress_ratio=1, top_k=512, dtype="bf16")
+    lens = [40000, 1000, 35000]
+    case = datagen.make_case("ws_state", d, lens, [0, 1, 2], lens, seed=0, case_id=280, std="inv_sqrt_dim",
+                             v_separate=False)
+    layer, res = run_and_check(case)
+    first = layer.selections()
+    for _ in range(3):
+        layer.step()
+    torch.cuda.synchronize()
+    again = layer.selections()
+    for a, b in zip(first, again):
+        assert np.array_equal(a, b)
+    state = layer.ws[: sa.WS_STATE_BYTES].cpu().numpy()
+    assert not state.any(), "workspace state not returned to zero"
+    # the same workspace serves a call with fewer query tokens
+    one = datagen.make_case("ws_state_one", d, [40000], [0], [40000], seed=0, case_id=280, std="inv_sqrt_dim",
+                            v_separate=False)
+    lay1 = DeviceLayer(one)
+    assert lay1.ws_bytes <= layer.ws_bytes
+    lay1.ws, lay1.ws_bytes = layer.ws, layer.ws_bytes
+    lay1.step()
+    torch.cuda.synchronize()
+    assert np.array_equal(lay1.selections()[0], first[0])
+    assert not layer.ws[: sa.WS_STATE_BYTES].cpu().numpy().any()
 
 
 # ----------------------------------------------------------- full-size workloads

@@ -71,16 +71,17 @@ def test_check_dims_null():
 
 def test_workspace_bytes():
     d = _dims()
-    # one decode token over short rows: split-KV partials (o, m, l) for 16 heads only
-    ws = sa.sparse_attn_workspace_bytes(d, 1, 4096)
-    assert ws > 0 and ws % (16 * (512 + 2) * 4) == 0
-    # a prefill chunk: unsplit attention and one selection workgroup per query
+    hdr = open(HEADER).read()
+    assert f"#define SA_WS_STATE_BYTES ((size_t){sa.WS_STATE_BYTES})" in hdr
+    partials_1 = 33 * 16 * (512 + 2) * 4            # one decode token: 33 splits of (o, m, l) for 16 heads
+    # short rows: state region + split-KV partials
+    assert sa.sparse_attn_workspace_bytes(d, 1, 4096) == sa.WS_STATE_BYTES + partials_1
+    # a prefill chunk: unsplit attention and one selection workgroup per query token
     assert sa.sparse_attn_workspace_bytes(d, 2048, 34816) == 0
-    # one decode token at 128K: also room for the chunked selection's histogram and candidates
-    big = sa.sparse_attn_workspace_bytes(d, 1, 131072)
-    assert big >= 4096 * 4 + 16384 * 8 and big >= ws
-    # many short-row decode tokens: the selection needs nothing, the partials grow with n_q
-    assert sa.sparse_attn_workspace_bytes(d, 8, 4096) > ws
+    # 128K rows: one workgroup holds a row of 32768 blocks, so selection adds nothing
+    assert sa.sparse_attn_workspace_bytes(d, 1, 131072) == sa.WS_STATE_BYTES + partials_1
+    # 1M rows: 128 chunks of 2048 8-byte entries outgrow the partials
+    assert sa.sparse_attn_workspace_bytes(d, 1, 1048576) >= sa.WS_STATE_BYTES + 128 * 2048 * 8
     assert sa.sparse_attn_workspace_bytes(_dims(top_k=2050), 1, 4096) == 0
     assert sa.sparse_attn_workspace_bytes(d, 1, -1) == 0
 
@@ -119,13 +120,15 @@ def test_entry_points_reject_bad_arguments_before_any_launch():
     assert _call("sparse_attn_select", d, c, FAKE, 1024, FAKE, FAKE, 1, FAKE, 2051, None, None, 0, None) == sa.SA_ERR_NULL
     assert _call("sparse_attn_select", d, ctypes.byref(_cache(seq_len=None)), FAKE, 1024, FAKE, FAKE, 1, FAKE,
                  2051, FAKE, None, 0, None) == sa.SA_ERR_NULL
-    # a 128K row needs the chunked selection's workspace
-    long_c = ctypes.byref(_cache(max_len=131072))
-    need = sa.sparse_attn_workspace_bytes(_dims(), 1, 131072)
-    assert _call("sparse_attn_select", d, long_c, FAKE, 32768, FAKE, FAKE, 1, FAKE, 2051, FAKE, None, 0,
+    # a 1M row needs the chunked selection's workspace
+    long_c = ctypes.byref(_cache(max_len=1048576))
+    need = sa.sparse_attn_workspace_bytes(_dims(), 1, 1048576)
+    assert _call("sparse_attn_select", d, long_c, FAKE, 262144, FAKE, FAKE, 1, FAKE, 2051, FAKE, None, 0,
                  None) == sa.SA_ERR_WORKSPACE
     assert need > 1000
-    assert _call("sparse_attn_select", d, long_c, FAKE, 32768, FAKE, FAKE, 1, FAKE, 2051, FAKE, FAKE, 1000,
+    assert _call("sparse_attn_select", d, long_c, FAKE, 262144, FAKE, FAKE, 1, FAKE, 2051, FAKE, FAKE, 1000,
+                 None) == sa.SA_ERR_WORKSPACE
+    assert _call("sparse_attn_select", d, long_c, FAKE, 262144, FAKE, FAKE, 1, FAKE, 2051, FAKE, FAKE, need - 1,
                  None) == sa.SA_ERR_WORKSPACE
     # fwd
     ws = sa.sparse_attn_workspace_bytes(_dims(), 1, 4096)
