@@ -91,6 +91,139 @@ score_mfma_kernel(const T* __restrict__ qidx, const T* __restrict__ kpool, int64
   if (hf == 0 && valid) scores[(int64_t)i * scores_ld + b] = sum + 0.0f;  // +0.0 turns -0.0 into +0.0
 }
 
+// ------------------------------------------------------------- MFMA, many queries
+
+// Prefill chunks (many query tokens of one sequence): a workgroup of kGemmQ waves
+// takes kGemmQ consecutive query tokens -- wave w holds token w's indexer heads as
+// the M operand in registers for the whole launch -- and walks a range of blocks in
+// tiles of kGemmBN pooled keys that all its waves share.  Each tile is loaded once
+// into LDS (rows padded by 16 bytes so the lanes' 16-byte reads spread over the
+// banks) while the previous one is being multiplied, so the pooled keys are read
+// from L2 once per kGemmQ queries instead of once per query, and each query's
+// heads once per block range.  Scores above a token's own visible blocks are not
+// written.  When the group's tokens belong to different sequences every wave reads
+// its own sequence's keys straight from memory instead.
+constexpr int kGemmQ = 8;             // query tokens (waves) per workgroup
+constexpr int kGemmBN = 128;          // pooled keys per LDS tile
+
+template <typename T, int MT, int D>
+__global__ void __launch_bounds__(kGemmQ * 64)
+score_gemm_kernel(const T* __restrict__ qidx, const T* __restrict__ kpool, int64_t kpool_ld,
+                  const int64_t* __restrict__ seq_blk0, const int32_t* __restrict__ seq_len,
+                  const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos, int c, int n_q,
+                  int tiles_per_range, float* __restrict__ scores, int64_t scores_ld) {
+  typedef typename vec8<T>::type V8;
+  constexpr int KS = D / 16;
+  constexpr int KP = D + 8;                          // LDS row pitch (elements)
+  constexpr int CH = D / 8;                          // 16-byte chunks per key row
+  constexpr int NLD = kGemmBN * CH / (kGemmQ * 64);  // chunks per thread per tile
+  static_assert(kGemmBN * CH % (kGemmQ * 64) == 0, "tile must split evenly");
+  __shared__ __attribute__((aligned(16))) T ks[2][kGemmBN * KP];
+  __shared__ int g_seq[kGemmQ], g_nb[kGemmQ];
+  __shared__ int64_t g_blk0[kGemmQ];
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int n = lane & 31, hf = lane >> 5;
+  const int i = blockIdx.y * kGemmQ + wave;
+  const bool has_q = i < n_q;
+  const int ic = has_q ? i : n_q - 1;
+  const T* qrow = qidx + (int64_t)ic * (MT * 32) * D + (int64_t)n * D + hf * (D / 2);
+  V8 qa[MT][KS];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int st = 0; st < KS; ++st) qa[mt][st] = *reinterpret_cast<const V8*>(qrow + (int64_t)mt * 32 * D + st * 8);
+  const SeqMeta sm = seq_meta(q_seq, seq_len, nullptr, seq_blk0, ic);
+  const int nb = has_q ? visible_tokens(sm.len, q_pos[ic]) / c : 0;
+  if (lane == 0) {
+    g_seq[wave] = has_q ? sm.s : -1;
+    g_nb[wave] = nb;
+    g_blk0[wave] = sm.blk0;
+  }
+  __syncthreads();
+  int nb_max = 0;
+  bool shared = true;
+  const int s0 = g_seq[0];
+#pragma unroll
+  for (int w = 0; w < kGemmQ; ++w) {
+    nb_max = max(nb_max, g_nb[w]);
+    shared = shared && (g_seq[w] == s0 || g_seq[w] < 0);
+  }
+  const int t_begin = blockIdx.x * tiles_per_range;
+  const int t_end = min(t_begin + tiles_per_range, (nb_max + kGemmBN - 1) / kGemmBN);
+  if (t_begin >= t_end) return;                      // uniform over the workgroup
+  float* srow = scores + (int64_t)ic * scores_ld;
+
+  // one 32-block product of this wave's query: ReLU, head sum, write
+  auto finish = [&](const V8 (&kb)[KS], int b) {
+    float sum = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      f32x16 acc = {};
+#pragma unroll
+      for (int st = 0; st < KS; ++st) acc = mfma32x32x16<T>(qa[mt][st], kb[st], acc);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sum += fmaxf(acc[r], 0.f);
+    }
+    sum += __shfl_xor(sum, 32);
+    if (hf == 0 && b < nb) srow[b] = sum + 0.0f;     // +0.0 turns -0.0 into +0.0
+  };
+
+  if (!shared) {                                     // tokens of different sequences
+    const T* kseq = kpool + sm.blk0 * kpool_ld + hf * (D / 2);
+    for (int t = t_begin; t < t_end; ++t) {
+      for (int nt = 0; nt < kGemmBN / 32; ++nt) {
+        const int b0 = t * kGemmBN + nt * 32;
+        if (b0 >= nb) break;
+        const int b = b0 + n;
+        const T* krow = kseq + (int64_t)(b < nb ? b : nb - 1) * kpool_ld;
+        V8 kb[KS];
+#pragma unroll
+        for (int st = 0; st < KS; ++st) kb[st] = *reinterpret_cast<const V8*>(krow + st * 8);
+        finish(kb, b);
+      }
+    }
+    return;
+  }
+
+  // shared tiles: thread e-chunks of rows [t*BN, t*BN + BN), clamped into the sequence
+  const T* kseq = kpool + g_blk0[0] * kpool_ld;
+  const int last = nb_max - 1;
+  V8 kreg[NLD];
+  auto load_tile = [&](int t) {
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) {
+      const int e = tid + j * kGemmQ * 64, r = e / CH, cc = e % CH;
+      const int b = min(t * kGemmBN + r, last);
+      kreg[j] = *reinterpret_cast<const V8*>(kseq + (int64_t)b * kpool_ld + cc * 8);
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) {
+      const int e = tid + j * kGemmQ * 64, r = e / CH, cc = e % CH;
+      *reinterpret_cast<V8*>(&ks[buf][r * KP + cc * 8]) = kreg[j];
+    }
+  };
+  load_tile(t_begin);
+  store_tile(0);
+  __syncthreads();
+  for (int t = t_begin; t < t_end; ++t) {
+    const int buf = (t - t_begin) & 1;
+    if (t + 1 < t_end) load_tile(t + 1);             // in flight while this tile is multiplied
+    for (int nt = 0; nt < kGemmBN / 32; ++nt) {
+      const int b0 = t * kGemmBN + nt * 32;
+      if (b0 >= nb) break;                           // uniform per wave
+      const T* krow = &ks[buf][(nt * 32 + n) * KP + hf * (D / 2)];
+      V8 kb[KS];
+#pragma unroll
+      for (int st = 0; st < KS; ++st) kb[st] = *reinterpret_cast<const V8*>(krow + st * 8);
+      finish(kb, b0 + n);
+    }
+    if (t + 1 < t_end) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+}
+
 // ----------------------------------------------------------------------------- VALU
 
 constexpr int kValuBlocks = 64;       // blocks per workgroup
@@ -147,10 +280,29 @@ bool score_uses_mfma(const sa_dims& d, const CacheArgs& c, const void* qidx) {
   return c.kpool_ld % 8 == 0 && aligned16(c.kpool) && aligned16(qidx);
 }
 
+// Query tokens from which the shared-tile kernel is used (a prefill chunk).
+constexpr int kGemmMinQueries = 64;
+
 template <typename T, int MT, int D>
 static void launch_mfma(const sa_dims& d, const CacheArgs& c, const void* qidx, const int32_t* q_seq,
                         const int32_t* q_pos, int n_q, float* scores, int64_t scores_ld, hipStream_t stream) {
   const long long max_blocks = (long long)c.max_len / d.compress_ratio;
+  // (the 256-wide indexer with more than 32 heads would spill the held heads)
+  if (n_q >= kGemmMinQueries && (D <= 128 || MT == 1)) {
+    // block ranges per query group: enough workgroups for ~4 per CU, each range
+    // long enough that the query heads are loaded once per many tiles
+    const long long tiles = (max_blocks + kGemmBN - 1) / kGemmBN;
+    const long long groups = (n_q + kGemmQ - 1) / kGemmQ;
+    long long ranges = (1024 + groups - 1) / groups;
+    ranges = ranges < 1 ? 1 : (ranges > tiles ? tiles : ranges);
+    const int per_range = (int)((tiles + ranges - 1) / ranges);
+    ranges = (tiles + per_range - 1) / per_range;
+    if (tiles == 0) return;
+    hipLaunchKernelGGL((score_gemm_kernel<T, MT, D>), dim3((unsigned)ranges, (unsigned)groups), dim3(kGemmQ * 64), 0,
+                       stream, (const T*)qidx, (const T*)c.kpool, c.kpool_ld, c.seq_blk0, c.seq_len, q_seq, q_pos,
+                       d.compress_ratio, n_q, per_range, scores, scores_ld);
+    return;
+  }
   const long long per_wg = kScoreWaves * kScoreTile;
   dim3 grid((unsigned)((max_blocks + per_wg - 1) / per_wg), (unsigned)n_q);
   if (grid.x == 0) return;
