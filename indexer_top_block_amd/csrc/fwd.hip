@@ -9,13 +9,17 @@
 // KV head, 512/512 with 8.
 //
 // MFMA path (f16 / bf16, up to 16 query heads per KV head, DKQ % 32 == 0, DV % 64 == 0):
-//   one workgroup = 4 waves = one (query token, KV head, split).  Per 32-row tile the
-//   workgroup gathers K rows (and V rows when separate) into LDS with 16-byte loads;
-//   every wave computes S^T = K Q^T for the tile with v_mfma_f32_16x16x32 (rows as
-//   M, the up-to-16 heads as N, Q^T kept in registers), so the softmax statistics of
-//   a head sit in one lane column; each wave then accumulates its quarter of DV as
-//   O^T = V^T P^T with v_mfma_f32_16x16x16, where P^T is the S^T accumulator itself
-//   (same lane layout) converted to 16-bit and V^T is read from LDS column-wise.
+//   one workgroup = 4 waves = one (query token, KV head, split).  Per 64-row tile the
+//   workgroup gathers K rows (and V rows when separate) into LDS with 16-byte loads,
+//   holding the next tile's rows in registers meanwhile.  Wave w computes S^T = K Q^T
+//   for rows [16w, 16w+16) with v_mfma_f32_16x16x32 (rows as M, the up-to-16 heads as
+//   N, Q^T kept in registers) and writes it, scaled, to a small transposed LDS tile;
+//   every wave then reads the whole tile back in the B-operand layout of
+//   v_mfma_f32_16x16x16 (a head's rows in one lane column), runs the same online
+//   softmax, and accumulates its own quarter of DV as O^T = V^T P^T, with V^T read
+//   from LDS column-wise.  Splitting DV rather than rows keeps one accumulator per
+//   output element (32 registers per lane), so two workgroups share a CU and their
+//   gathers overlap.
 // VALU path (any dtype): the same tiles with plain float dot products.
 //
 // Partial results: o (unnormalised, float32), m (running max, log2 units) and l
@@ -67,7 +71,14 @@ template <> struct pv_mfma<f16> {
 
 // ---------------------------------------------------------------------------- MFMA
 
-constexpr int kMfmaTile = 64;        // rows per workgroup tile: 16 per wave
+constexpr int kMfmaTile = 64;        // rows per workgroup tile: S for 16 per wave
+
+// Lane `src` (wave-uniform) of a 64-bit per-lane value.
+__device__ __forceinline__ int64_t readlane64(int64_t x, int src) {
+  const int lo = __builtin_amdgcn_readlane((int)(uint32_t)x, src);
+  const int hi = __builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)x >> 32), src);
+  return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
 
 template <typename T, int DKQ, int DV, bool ALIAS>
 __global__ void __launch_bounds__(256, 1)
@@ -78,41 +89,41 @@ fwd_mfma_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, 
                 int h_kv, float scale_log2, int n_split, int rows_per_split, float* __restrict__ out,
                 float* __restrict__ ws_o, float* __restrict__ ws_ml) {
   typedef typename vec8<T>::type V8;
-  constexpr int RT = kMfmaTile;
+  constexpr int RT = kMfmaTile;       // = 64: one list entry per lane
   constexpr int KST = DKQ / 32;       // QK^T MFMA steps
   constexpr int KP = DKQ + 8;         // LDS row pitch of the K tile (elements)
   constexpr int VP = ALIAS ? KP : DV + 8;
-  constexpr int NT = DV / 16;         // 16-column output tiles (every wave holds all of DV)
+  constexpr int DVW = DV / 4;         // output dims owned by one wave
+  constexpr int NTW = DVW / 16;       // its 16-dim MFMA tiles
   constexpr int KCH = DKQ / 8;        // 16-byte chunks per K row
   constexpr int VCH = DV / 8;
   constexpr int KLD = RT * KCH / 256;                 // K chunks per thread per tile
   constexpr int VLD = ALIAS ? 1 : RT * VCH / 256;     // V chunks per thread per tile
+  constexpr int SP = RT + 4;                          // pitch of the transposed score tile (floats)
+  static_assert(RT == kWave, "one list entry per lane");
   static_assert(RT * KCH % 256 == 0 && (ALIAS || RT * VCH % 256 == 0), "tile must split evenly");
-  static_assert(2 * 16 * DV * 4 <= RT * KP * (int)sizeof(T), "wave merge must fit in the K tile");
+  static_assert(DV % 64 == 0, "four waves split DV in 16-dim tiles");
   __shared__ __attribute__((aligned(16))) T ks[RT * KP];
   __shared__ __attribute__((aligned(16))) T vs_sep[ALIAS ? 8 : RT * VP];
-  __shared__ int64_t rows[2][RT];                    // cache rows of tiles t (t % 2) and t + 1
-  __shared__ float wm[4][16], wl[4][16];             // per-wave statistics for the final merge
+  __shared__ __attribute__((aligned(16))) float st[16 * SP];   // scaled scores, [head][row]
   const T* vs = ALIAS ? ks : vs_sep;
 
   const int tid = threadIdx.x;
-  const int lane = tid % kWave, wave = tid / kWave;
+  const int lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int col = lane & 15, grp = lane >> 4;
   const int split = blockIdx.x;
   const int i = blockIdx.y / h_kv, g = blockIdx.y % h_kv;
   const int G = h_q / h_kv;
   const int32_t* list = sel + (int64_t)i * sel_ld;
   const int r_begin = split * rows_per_split;
-  // The first three tiles' list entries are read alongside the query's metadata.
-  // List indices are clamped into the row rather than guarded, so the loads issue
-  // back to back; entries at or past the query's count are discarded once it is known.
+  // Every wave reads the list itself, lane l taking entry l of a tile.  Indices are
+  // clamped into the row rather than guarded, so the loads issue back to back;
+  // entries at or past the query's count are discarded once it is known.  The
+  // first four tiles' entries are read alongside the query's metadata.
   const int lim = (int)sel_ld - 1;
-  int pre0 = -1, pre1 = -1, pre2 = -1;
-  if (tid < RT) {
-    pre0 = list[min(r_begin + tid, lim)];
-    pre1 = list[min(r_begin + RT + tid, lim)];
-    pre2 = list[min(r_begin + 2 * RT + tid, lim)];
-  }
+  auto list_at = [&](int t) { return list[min(r_begin + t * RT + lane, lim)]; };
+  const int pre0 = list_at(0), pre1 = list_at(1), pre2 = list_at(2), pre3 = list_at(3);
   const SeqMeta sm = seq_meta(q_seq, seq_len, seq_row0, nullptr, i);
   const int L = sm.len;
   const int64_t row0 = sm.row0;
@@ -129,172 +140,208 @@ fwd_mfma_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, 
   {
     const T* qh = qbase + (col < G ? col : 0) * DKQ + grp * 8;
 #pragma unroll
-    for (int st = 0; st < KST; ++st) qf[st] = *reinterpret_cast<const V8*>(qh + st * 32);
+    for (int st_ = 0; st_ < KST; ++st_) qf[st_] = *reinterpret_cast<const V8*>(qh + st_ * 32);
     if (col >= G) {
 #pragma unroll
-      for (int st = 0; st < KST; ++st) qf[st] = V8{};
+      for (int st_ = 0; st_ < KST; ++st_) qf[st_] = V8{};
     }
   }
+  // Running max (log2 units) and weight sum of head `col` over all rows so far: every
+  // wave sees the whole score tile, so every wave holds the same values.
   float m = -INFINITY, lsum = 0.f;
-  f32x4 o[NT];
+  f32x4 o[NTW];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int nt = 0; nt < NTW; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Gathered rows of the next tile are held in registers while the current tile is
-  // computed from LDS; the row list runs two tiles further ahead.  Rows that are not
-  // selected are read from this query's own Q row instead (finite values, and their
-  // scores are masked to -inf, so they add exactly zero); every gather is an
-  // unconditional load, so all of a tile's loads are in flight together.
-  V8 kreg[KLD], vreg[VLD];
-  auto issue_loads = [&](const int64_t* trow) {
+  // A tile's rows as held by every wave: lane l has row l's gather offsets (element
+  // offsets from kg / vg), and a 64-bit mask marks the selected rows.  Rows that are
+  // not selected gather this query's own Q row instead (finite values, and their
+  // scores are masked to -inf, so they add exactly zero), so every gather is an
+  // unconditional load.
+  struct TileRows {
+    int64_t ko, vo;
+    uint64_t valid;
+  };
+  const int64_t safe_k = qbase - kg, safe_v = qbase - vg;
+  auto tile_rows = [&](int pos, int t) {
+    const int64_t row = tile_row(pos, r_begin + t * RT + lane, r_end, L, row0);
+    TileRows tr;
+    tr.ko = row >= 0 ? row * k_ld : safe_k;
+    tr.vo = ALIAS ? 0 : (row >= 0 ? row * v_ld : safe_v);
+    tr.valid = __ballot(row >= 0);
+    return tr;
+  };
+  // Offset of chunk e's row: the chunks of one wave instruction span at most NR rows
+  // starting at the wave-uniform row R, whose offsets are read from their lanes.
+  auto chunk_off = [&](int64_t per_lane, int e0, int e, int CH) -> int64_t {
+    const int R = e0 / CH;
+    const int r = e / CH;
+    int64_t off = readlane64(per_lane, R);
+    const int nr = (kWave + CH - 1) / CH + 1;
+    for (int u = 1; u < nr; ++u) {
+      const int64_t o2 = readlane64(per_lane, min(R + u, RT - 1));
+      off = (r == R + u) ? o2 : off;
+    }
+    return off;
+  };
+
+  // Gathered rows of the next PD tiles are held in registers (PD buffers, used in
+  // turn) while the current tile is computed from LDS, so PD tiles' gathers are in
+  // flight at a time; the row list runs two tiles further ahead still.  With V
+  // aliasing K a tile is 18 registers of 16 bytes per thread and two fit; with a
+  // separate V tile only one does.
+  constexpr int PD = ALIAS ? 2 : 1;
+  V8 kbuf[PD][KLD], vbuf[PD][VLD];
+  auto issue = [&](V8 (&kr)[KLD], V8 (&vr)[VLD], const TileRows& tr) {
 #pragma unroll
     for (int j = 0; j < KLD; ++j) {
-      const int e = tid + 256 * j, r = e / KCH, cc = e % KCH;
-      const int64_t row = trow[r];
-      const T* p = row >= 0 ? kg + row * k_ld + cc * 8 : qbase;
-      kreg[j] = *reinterpret_cast<const V8*>(p);
+      const int e0 = wave * kWave + 256 * j, e = e0 + lane;
+      const int cc = e % KCH;
+      kr[j] = *reinterpret_cast<const V8*>(kg + chunk_off(tr.ko, e0, e, KCH) + cc * 8);
     }
     if (!ALIAS) {
 #pragma unroll
       for (int j = 0; j < VLD; ++j) {
-        const int e = tid + 256 * j, r = e / VCH, cc = e % VCH;
-        const int64_t row = trow[r];
-        const T* p = row >= 0 ? vg + row * v_ld + cc * 8 : qbase;
-        vreg[j] = *reinterpret_cast<const V8*>(p);
+        const int e0 = wave * kWave + 256 * j, e = e0 + lane;
+        const int cc = e % VCH;
+        vr[j] = *reinterpret_cast<const V8*>(vg + chunk_off(tr.vo, e0, e, VCH) + cc * 8);
       }
     }
   };
-  int64_t lnext = -1;                                // checked row of tile t + 1 (threads < RT)
-  int lraw = -1;                                     // list entry of tile t + 2
-  if (n_tiles > 0) {
-    if (tid < RT) {
-      rows[0][tid] = tile_row(pre0, r_begin + tid, r_end, L, row0);
-      lnext = tile_row(pre1, r_begin + RT + tid, r_end, L, row0);
-      lraw = pre2;
-    }
-    __syncthreads();
-    issue_loads(rows[0]);
-  }
-
-  const int wr = wave * 16;                          // this wave's 16 rows of the tile
-  for (int t = 0; t < n_tiles; ++t) {
-    const int64_t* trow = rows[t & 1];
-    // land tile t in LDS
+  auto land = [&](const V8 (&kr)[KLD], const V8 (&vr)[VLD]) {
 #pragma unroll
     for (int j = 0; j < KLD; ++j) {
       const int e = tid + 256 * j, r = e / KCH, cc = e % KCH;
-      *reinterpret_cast<V8*>(ks + r * KP + cc * 8) = kreg[j];
+      *reinterpret_cast<V8*>(ks + r * KP + cc * 8) = kr[j];
     }
     if (!ALIAS) {
 #pragma unroll
       for (int j = 0; j < VLD; ++j) {
         const int e = tid + 256 * j, r = e / VCH, cc = e % VCH;
-        *reinterpret_cast<V8*>(vs_sep + r * VP + cc * 8) = vreg[j];
+        *reinterpret_cast<V8*>(vs_sep + r * VP + cc * 8) = vr[j];
       }
     }
-    // publish the rows of tile t+1, check those of tile t+2, fetch the list of t+3
-    if (tid < RT) {
-      rows[(t + 1) & 1][tid] = lnext;
-      lnext = tile_row(lraw, r_begin + (t + 2) * RT + tid, r_end, L, row0);
+  };
+
+  const int wr = wave * 16;                          // this wave's 16 rows of S
+  const int dvb = wave * DVW;                        // this wave's output dims
+  auto compute = [&](uint64_t valid) {
+    // S^T[row][head] for this wave's 16 rows, as two independent accumulation chains,
+    // scaled to log2 units (-inf for rows not selected) and shared through LDS.
+    {
+      f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+      const T* arow = ks + (wr + col) * KP + grp * 8;
+#pragma unroll
+      for (int st_ = 0; st_ + 1 < KST; st_ += 2) {
+        s0 = mfma16x16x32<T>(*reinterpret_cast<const V8*>(arow + st_ * 32), qf[st_], s0);
+        s1 = mfma16x16x32<T>(*reinterpret_cast<const V8*>(arow + (st_ + 1) * 32), qf[st_ + 1], s1);
+      }
+      if (KST & 1) s0 = mfma16x16x32<T>(*reinterpret_cast<const V8*>(arow + (KST - 1) * 32), qf[KST - 1], s0);
+      const f32x4 sacc = s0 + s1;
+      f32x4 x;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) x[j] = ((valid >> (wr + 4 * grp + j)) & 1ull) ? sacc[j] * scale_log2 : -INFINITY;
+      *reinterpret_cast<f32x4*>(st + col * SP + wr + 4 * grp) = x;
     }
     __syncthreads();
-    if (t + 1 < n_tiles) issue_loads(rows[(t + 1) & 1]);
-    if (tid < RT) lraw = list[min(r_begin + (t + 3) * RT + tid, lim)];
-
-    // S^T[row][head] for this wave's 16 rows, as two independent accumulation chains.
-    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-    const T* arow = ks + (wr + col) * KP + grp * 8;
+    // Online softmax of head `col` over the whole tile; this lane takes rows
+    // 16*kk + 4*grp + j, which is the B-operand layout of the P^T MFMA steps below.
+    f32x4 xs[4];
 #pragma unroll
-    for (int st = 0; st + 1 < KST; st += 2) {
-      s0 = mfma16x16x32<T>(*reinterpret_cast<const V8*>(arow + st * 32), qf[st], s0);
-      s1 = mfma16x16x32<T>(*reinterpret_cast<const V8*>(arow + (st + 1) * 32), qf[st + 1], s1);
-    }
-    if (KST & 1) s0 = mfma16x16x32<T>(*reinterpret_cast<const V8*>(arow + (KST - 1) * 32), qf[KST - 1], s0);
-    const f32x4 sacc = s0 + s1;
-    // Online softmax for head `col`; this lane holds rows wr + 4*grp + j.
-    float x[4];
+    for (int kk = 0; kk < 4; ++kk) xs[kk] = *reinterpret_cast<const f32x4*>(st + col * SP + 16 * kk + 4 * grp);
     float mx = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const bool ok = trow[wr + 4 * grp + j] >= 0;
-      x[j] = ok ? sacc[j] * scale_log2 : -INFINITY;
-      mx = fmaxf(mx, x[j]);
-    }
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) mx = fmaxf(mx, xs[kk][j]);
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float m_new = fmaxf(m, mx);
     const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m - m_new);
-    T pb[4];
+    T pb[4][4];
     float psum = 0.f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float p = (x[j] == -INFINITY) ? 0.f : fast_exp2(x[j] - m_new);
-      psum += p;
-      pb[j] = (T)p;
-    }
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float p = (xs[kk][j] == -INFINITY) ? 0.f : fast_exp2(xs[kk][j] - m_new);
+        psum += p;
+        pb[kk][j] = (T)p;
+      }
+    psum += __shfl_xor(psum, 16);
+    psum += __shfl_xor(psum, 32);
     lsum = lsum * alpha + psum;
     m = m_new;
-    // O^T[dv][head] = alpha * O^T + V^T[dv][row] P^T[row][head] over this wave's 16 rows.
-    const T* vrow = vs + (wr + 4 * grp) * VP + col;
+    // O^T[dv][head] = alpha * O^T + V^T[dv][row] P^T[row][head] for this wave's dims.
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      T a[4];
+    for (int nt = 0; nt < NTW; ++nt) o[nt] *= alpha;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) a[j] = vrow[j * VP + nt * 16];
-      o[nt] = pv_mfma<T>::run(a, pb, o[nt] * alpha);
+    for (int kk = 0; kk < 4; ++kk) {
+      const T* vrow = vs + (16 * kk + 4 * grp) * VP + dvb + col;
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) {
+        T a[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) a[j] = vrow[j * VP + nt * 16];
+        o[nt] = pv_mfma<T>::run(a, pb[kk], o[nt]);
+      }
     }
-    __syncthreads();
+  };
+
+  // Pipeline: while tile t is computed, tiles t+1 .. t+PD are in flight and the list
+  // entries of tiles t+PD+1 and t+PD+2 are in registers.
+  uint64_t vq[PD];                                   // selected-row masks of tiles t .. t+PD-1
+#pragma unroll
+  for (int b = 0; b < PD; ++b) vq[b] = 0;
+  int rawA = PD == 2 ? pre2 : pre1;                  // list entries of tile t+PD
+  int rawB = PD == 2 ? pre3 : pre2;                  // and of tile t+PD+1
+  if (n_tiles > 0) {
+    const TileRows r0 = tile_rows(pre0, 0);
+    vq[0] = r0.valid;
+    issue(kbuf[0], vbuf[0], r0);
+    if (PD == 2 && n_tiles > 1) {
+      const TileRows r1 = tile_rows(pre1, 1);
+      vq[PD - 1] = r1.valid;
+      issue(kbuf[PD - 1], vbuf[PD - 1], r1);
+    }
+  }
+  for (int t0 = 0; t0 < n_tiles; t0 += PD) {
+#pragma unroll
+    for (int b = 0; b < PD; ++b) {
+      const int t = t0 + b;
+      if (t < n_tiles) {
+        land(kbuf[b], vbuf[b]);
+        __syncthreads();
+        const int raw_new = list_at(t + PD + 2);     // before the gathers: waiting for it must not wait for them
+        const TileRows rn = tile_rows(rawA, t + PD);
+        if (t + PD < n_tiles) issue(kbuf[b], vbuf[b], rn);
+        compute(vq[0]);
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u + 1 < PD; ++u) vq[u] = vq[u + 1];
+        vq[PD - 1] = rn.valid;
+        rawA = rawB;
+        rawB = raw_new;
+      }
+    }
   }
 
-  // ---- merge the four waves' (m, l, O) -------------------------------------------
-  lsum += __shfl_xor(lsum, 16);
-  lsum += __shfl_xor(lsum, 32);
-  if (grp == 0) {
-    wm[wave][col] = m;
-    wl[wave][col] = lsum;
-  }
-  __syncthreads();
-  float M = fmaxf(fmaxf(wm[0][col], wm[1][col]), fmaxf(wm[2][col], wm[3][col]));
-  float Lt = 0.f;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) Lt += (wm[w][col] == -INFINITY) ? 0.f : fast_exp2(wm[w][col] - M) * wl[w][col];
-  const float sc = (m == -INFINITY) ? 0.f : fast_exp2(m - M);
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) o[nt] *= sc;
-  f32x4* xo = reinterpret_cast<f32x4*>(ks);          // 2 slots of [NT][64 lanes] f32x4
-  if (wave >= 2) {
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) xo[((wave - 2) * NT + nt) * kWave + lane] = o[nt];
-  }
-  __syncthreads();
-  if (wave < 2) {
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) o[nt] += xo[(wave * NT + nt) * kWave + lane];
-  }
-  __syncthreads();
-  if (wave == 1) {
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) xo[nt * kWave + lane] = o[nt];
-  }
-  __syncthreads();
-  if (wave == 0 && col < G) {
+  // ---- this wave's dims of the result (or of the split's partial) ------------------
+  if (col < G) {
     const int hq = g * G + col;
     const int64_t qh = (int64_t)i * h_q + hq;
     if (n_split == 1) {
-      const float inv = Lt > 0.f ? 1.f / Lt : 0.f;
+      const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const f32x4 r = (o[nt] + xo[nt * kWave + lane]) * inv;
-        *reinterpret_cast<f32x4*>(out + qh * DV + nt * 16 + 4 * grp) = r;
-      }
+      for (int nt = 0; nt < NTW; ++nt)
+        *reinterpret_cast<f32x4*>(out + qh * DV + dvb + nt * 16 + 4 * grp) = o[nt] * inv;
     } else {
-      float* dst = ws_o + (qh * n_split + split) * DV;
+      float* dst = ws_o + (qh * n_split + split) * DV + dvb;
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        *reinterpret_cast<f32x4*>(dst + nt * 16 + 4 * grp) = o[nt] + xo[nt * kWave + lane];
-      if (grp == 0) {
-        ws_ml[(qh * n_split + split) * 2 + 0] = M;
-        ws_ml[(qh * n_split + split) * 2 + 1] = Lt;
+      for (int nt = 0; nt < NTW; ++nt) *reinterpret_cast<f32x4*>(dst + nt * 16 + 4 * grp) = o[nt];
+      if (wave == 0 && grp == 0) {
+        ws_ml[(qh * n_split + split) * 2 + 0] = m;
+        ws_ml[(qh * n_split + split) * 2 + 1] = lsum;
       }
     }
   }

@@ -10,34 +10,39 @@
 // block index, which is where the pages' token-level top-k over expanded block
 // scores cuts as well (members of a block tie, the budget is whole blocks).
 //
-// Scores are mapped to order-preserving 32-bit keys (+0/-0 identical).  Two designs:
+// Scores are mapped to order-preserving 32-bit keys (+0/-0 identical).  Three designs,
+// by row length and number of query tokens:
 //
-// Per-query workgroup (many query tokens, e.g. a prefill chunk): one workgroup per
-// query finds the K_blk-th largest key T exactly by a 4-pass radix select over 8-bit
-// digits, most significant first; each pass histograms the digit among the keys
-// that match the digits fixed so far.  The histogram is privatised per lane (32
-// copies, padded by one word) so that keys sharing a digit -- scores crowd into a
-// few binades -- hit different LDS banks instead of serialising on one address.
-// The kept blocks (key > T, or key == T among the first r such in index order) are
-// then compacted in index order with two workgroup prefix sums.  Thread t owns
-// blocks [t*KPT, (t+1)*KPT) of a chunk; longer rows stream chunk by chunk.
+// Rows of up to 32768 blocks (any number of query tokens): one 1024-thread workgroup
+// per query holds the whole row in registers and radix-selects over them (see the
+// wide kernel below); no workspace.
 //
-// Chunked (few query tokens over long rows, i.e. decode): the row is cut into
-// chunks of 2048 blocks, one workgroup each, so the whole GPU takes part.
-//   zero   clear the per-query histogram and counters in the workspace;
-//   hist   each chunk histograms the top 12 bits of its keys in LDS and adds the
-//          non-empty bins to the query's histogram (device-scope atomics);
-//   cand   every chunk finds the bin b holding the K_blk-th largest key, counts its
-//          keys above b and appends its keys inside b to a candidate list as
-//          (key << 32 | ~index) -- unique 64-bit values whose order is exactly
-//          (score desc, index asc), so ties need no special case;
-//   final  one workgroup radix-selects the cut among the candidates (8-bit digits
-//          below the 12 shared bits, stopping as soon as the cut's bin holds one
-//          value), tallies the kept blocks per chunk and turns the tallies into
-//          output offsets; it also writes the tail, the padding and n_sel;
-//   emit   each chunk writes its kept blocks' positions at its offset.
-// If the candidates overflow their buffer (massive exact ties), `final` runs the
-// per-query algorithm above over the whole row instead and `emit` does nothing.
+// Longer rows, many query tokens: one workgroup per query finds the K_blk-th largest
+// key T exactly by a 4-pass radix select over 8-bit digits, most significant first;
+// each pass histograms the digit among the keys that match the digits fixed so far.
+// The histogram is privatised per lane (32 copies, padded by one word) so that keys
+// sharing a digit -- scores crowd into a few binades -- hit different LDS banks
+// instead of serialising on one address.  The kept blocks (key > T, or key == T among
+// the first r such in index order) are then compacted in index order with two
+// workgroup prefix sums.  Thread t owns blocks [t*KPT, (t+1)*KPT) of a chunk; longer
+// rows stream chunk by chunk.
+//
+// Longer rows, few query tokens (long-context decode), chunked: the row is cut into
+// chunks of 2048 blocks, one workgroup each, so the whole GPU takes part; two kernels.
+//   hist    each chunk histograms the top 12 bits of its keys in LDS and adds the
+//           non-empty bins to the query's histogram in the workspace (device-scope
+//           atomics); the last chunk to arrive finds the bin b holding the K_blk-th
+//           largest key and the number of keys above it, records both and clears
+//           the histogram for the next call;
+//   select  each chunk writes its keys in b or above, in index order, to its own
+//           segment as (key << 32 | ~index) -- unique 64-bit values whose order is
+//           exactly (score desc, index asc), so ties need no special case; the last
+//           chunk to arrive gathers the segments, radix-selects the cut among the
+//           values inside b (8-bit digits below the 12 shared bits, stopping once
+//           the chosen bin holds one value) and writes every value at or above the
+//           cut as positions in index order, then the tail, the padding and n_sel.
+// If the values in b and above overflow what the last workgroup holds (massive exact
+// ties), it runs the 4-pass algorithm above over the whole row instead.
 #include "sa_common.hpp"
 #include "sa_launch.hpp"
 
@@ -771,7 +776,7 @@ hipError_t launch_select(const sa_dims& d, const CacheArgs& c, const float* scor
                        q_pos, cr, k_blk, sel, sel_ld, n_sel, st, sc);
     return hipGetLastError();
   }
-  if (n_q <= kStateQueries) {                        // few query tokens: one wide workgroup per row
+  if (max_blocks <= kWideMax) {                      // rows that fit one workgroup's registers
 #define SA_WIDE(KPT_)                                                                                         \
   hipLaunchKernelGGL(select_wide_kernel<KPT_>, dim3(n_q), dim3(kWideThreads), 0, stream, scores, scores_ld,  \
                      c.seq_len, q_seq, q_pos, cr, k_blk, sel, sel_ld, n_sel)
