@@ -453,48 +453,53 @@ fwd_valu_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, 
 // ------------------------------------------------------------------------- combine
 
 // out[qh][dv] = sum_s 2^(m_s - M) o_s[dv] / sum_s 2^(m_s - M) l_s, M = max_s m_s.
-// One workgroup per (query, head); the split statistics are read in parallel.
-__global__ void __launch_bounds__(256)
+// One thread per output element, kCombineThreads per workgroup (all of one (query,
+// head), so the split statistics are wave-uniform), no LDS and no barriers.  Up to
+// MAXS splits every partial value and statistic is loaded into registers before any
+// is used (indices clamped, not guarded), so the combine costs one round trip;
+// beyond that the splits stream in chunks.
+constexpr int kCombineThreads = 128;
+
+template <int MAXS>
+__global__ void __launch_bounds__(kCombineThreads)
 fwd_combine_kernel(const float* __restrict__ ws_o, const float* __restrict__ ws_ml, int n_split, int d_v,
-                   float* __restrict__ out) {
-  extern __shared__ float wsh[];                     // n_split weights
-  __shared__ float red[256 / kWave];
-  __shared__ float sh_m, sh_inv_l;
-  const int64_t qh = blockIdx.x;
+                   int64_t n_out, float* __restrict__ out) {
+  const int64_t e = (int64_t)blockIdx.x * kCombineThreads + threadIdx.x;
+  if (e >= n_out) return;
+  const int64_t qh = e / d_v;
+  const int dv = (int)(e - qh * d_v);
   const float* ml = ws_ml + qh * n_split * 2;
-  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-  float M = -INFINITY;
-  for (int s = tid; s < n_split; s += 256) M = fmaxf(M, ml[2 * s]);
-  M = wave_max(M);
-  if (lane == 0) red[wave] = M;
-  __syncthreads();
-  if (tid == 0) sh_m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  __syncthreads();
-  M = sh_m;
-  float lpart = 0.f;
-  for (int s = tid; s < n_split; s += 256) {
-    const float ms = ml[2 * s];
-    const float w = (ms == -INFINITY) ? 0.f : fast_exp2(ms - M);
-    wsh[s] = w;
-    lpart += w * ml[2 * s + 1];
+  const float* src = ws_o + qh * n_split * d_v + dv;
+  float acc = 0.f, L = 0.f;
+  if (n_split <= MAXS) {
+    float o[MAXS], m[MAXS], l[MAXS];
+#pragma unroll
+    for (int s = 0; s < MAXS; ++s) {
+      const int sc = min(s, n_split - 1);
+      o[s] = src[(int64_t)sc * d_v];
+      m[s] = s < n_split ? ml[2 * sc] : -INFINITY;
+      l[s] = ml[2 * sc + 1];
+    }
+    float M = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < MAXS; ++s) M = fmaxf(M, m[s]);
+#pragma unroll
+    for (int s = 0; s < MAXS; ++s) {
+      const float w = m[s] == -INFINITY ? 0.f : fast_exp2(m[s] - M);
+      acc += w * o[s];
+      L += w * l[s];
+    }
+  } else {
+    float M = -INFINITY;
+    for (int s = 0; s < n_split; ++s) M = fmaxf(M, ml[2 * s]);
+    for (int s = 0; s < n_split; ++s) {
+      const float ms = ml[2 * s];
+      const float w = ms == -INFINITY ? 0.f : fast_exp2(ms - M);
+      acc += w * src[(int64_t)s * d_v];
+      L += w * ml[2 * s + 1];
+    }
   }
-  lpart = wave_sum(lpart);
-  __syncthreads();
-  if (lane == 0) red[wave] = lpart;
-  __syncthreads();
-  if (tid == 0) {
-    const float L = red[0] + red[1] + red[2] + red[3];
-    sh_inv_l = L > 0.f ? 1.f / L : 0.f;
-  }
-  __syncthreads();
-  const float inv_l = sh_inv_l;
-  for (int dv = tid; dv < d_v; dv += 256) {
-    const float* src = ws_o + qh * n_split * d_v + dv;
-    float acc = 0.f;
-#pragma unroll 16
-    for (int s = 0; s < n_split; ++s) acc += wsh[s] * src[(int64_t)s * d_v];
-    out[qh * d_v + dv] = acc * inv_l;
-  }
+  out[e] = L > 0.f ? acc / L : 0.f;
 }
 
 // ---------------------------------------------------------------------------- host
@@ -507,7 +512,9 @@ FwdPlan plan_fwd(const sa_dims& d, int n_q) {
   FwdPlan p{};
   const int cap = fwd_cap(d);
   const long long units = (long long)n_q * d.h_kv;
-  // Aim at about 512 workgroups; never split below one 64-row tile.
+  // Aim at about 512 workgroups; never split below one 64-row tile.  (Decode is bound
+  // by what one CU can pull: a second tile per workgroup costs more than the smaller
+  // combine it buys.)
   long long want = units > 0 ? (512 + units - 1) / units : 1;
   const long long max_split = (cap + kMfmaTile - 1) / kMfmaTile;
   if (want > max_split) want = max_split;
@@ -609,9 +616,14 @@ hipError_t launch_fwd(const sa_dims& d, const CacheArgs& c, const void* q, const
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || plan.n_split == 1) return err;
-  const size_t shm = (size_t)plan.n_split * sizeof(float);
-  hipLaunchKernelGGL(fwd_combine_kernel, dim3((unsigned)((size_t)n_q * d.h_q)), dim3(256), shm, stream, ws_o, ws_ml,
-                     plan.n_split, d.d_v, out);
+  const int64_t n_out = (int64_t)n_q * d.h_q * d.d_v;
+  const dim3 grid((unsigned)((n_out + kCombineThreads - 1) / kCombineThreads));
+  if (plan.n_split <= 40)
+    hipLaunchKernelGGL(fwd_combine_kernel<40>, grid, dim3(kCombineThreads), 0, stream, ws_o, ws_ml, plan.n_split,
+                       d.d_v, n_out, out);
+  else
+    hipLaunchKernelGGL(fwd_combine_kernel<8>, grid, dim3(kCombineThreads), 0, stream, ws_o, ws_ml, plan.n_split,
+                       d.d_v, n_out, out);
   return hipGetLastError();
 }
 

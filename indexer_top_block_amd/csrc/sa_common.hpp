@@ -44,13 +44,17 @@ __device__ __forceinline__ int wave_sum_int(int x) {
   return x;
 }
 
-// Inclusive prefix sum over the 64 lanes of a wave.
-__device__ __forceinline__ int wave_inclusive_scan(int x, int lane) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    int y = __shfl_up(x, off);
-    if (lane >= off) x += y;
-  }
+// Inclusive prefix sum over the 64 lanes of a wave, with DPP: shifts by 1, 2, 4, 8
+// within each row of 16 lanes, then the last lane of rows 0 and 2 is added to rows 1
+// and 3 (row_bcast:15) and lane 31 to rows 2 and 3 (row_bcast:31).  `lane` is unused
+// and kept for the call sites' readability.
+__device__ __forceinline__ int wave_inclusive_scan(int x, int /*lane*/) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15 into rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31 into rows 2, 3
   return x;
 }
 

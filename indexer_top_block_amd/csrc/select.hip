@@ -637,14 +637,20 @@ select_wide_kernel(const float* __restrict__ scores, int64_t scores_ld, const in
     return;
   }
   const int nb = min(qr.nb, KPT * kWideThreads);     // the launch guarantees qr.nb fits; the bitmap relies on it
+  // Keys past the row's end become 0 -- below every key a score can have except
+  // negative NaNs -- so the passes need no bounds checks: the picks take the n_pad
+  // padding keys back out of bin 0, and a prefix of 0 (the only one they can match)
+  // never takes its bin whole, so they are never kept.
+  const int n_pad = KPT * kWideThreads - nb;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) key[j] = (j * kWideThreads + tid < nb) ? key[j] : 0u;
   __syncthreads();
 
   // ---- pass 1: top 11 bits, 8 privatised copies -----------------------------------
   {
     uint32_t* mine = sm.h1 + (lane & (kWideCopies - 1)) * kWideStride;
 #pragma unroll
-    for (int j = 0; j < KPT; ++j)
-      if (j * kWideThreads + tid < nb) atomicAdd(&mine[key[j] >> 21], 1u);
+    for (int j = 0; j < KPT; ++j) atomicAdd(&mine[key[j] >> 21], 1u);
   }
   __syncthreads();
   {
@@ -656,54 +662,56 @@ select_wide_kernel(const float* __restrict__ scores, int64_t scores_ld, const in
       for (int cp = 0; cp < kWideCopies; ++cp) n += sm.h1[cp * kWideStride + tid * 2 + j];
       cnt[j] = n;
     }
+    if (tid == 0) cnt[0] -= (uint32_t)n_pad;
     wide_pick<2>(cnt, k_blk, sm);
   }
   uint32_t prefix = (uint32_t)sm.pick[0];
   int k_rem = k_blk - sm.pick[1];
   int width = 11;                                    // bits of the key the prefix fixes
-  bool whole = sm.pick[2] == k_rem;
+  bool whole = sm.pick[2] == k_rem && prefix != 0u;
   __syncthreads();                                   // pick[] is rewritten below
   // ---- pass 2: next 11 bits among keys in the bin ---------------------------------
   if (!whole) {
     sm.h1[tid] = 0u;                                 // copy 0 serves pass 3
 #pragma unroll
     for (int j = 0; j < KPT; ++j)
-      if (j * kWideThreads + tid < nb && (key[j] >> 21) == prefix) atomicAdd(&sm.h2[(key[j] >> 10) & 2047u], 1u);
+      if ((key[j] >> 21) == prefix) atomicAdd(&sm.h2[(key[j] >> 10) & 2047u], 1u);
     __syncthreads();
     uint32_t cnt[2] = {sm.h2[tid * 2], sm.h2[tid * 2 + 1]};
+    if (tid == 0 && prefix == 0u) cnt[0] -= (uint32_t)n_pad;
     wide_pick<2>(cnt, k_rem, sm);
     prefix = (prefix << 11) | (uint32_t)sm.pick[0];
     k_rem -= sm.pick[1];
     width = 22;
-    whole = sm.pick[2] == k_rem;
+    whole = sm.pick[2] == k_rem && prefix != 0u;
     __syncthreads();
     // ---- pass 3: last 10 bits ------------------------------------------------------
     if (!whole) {
 #pragma unroll
       for (int j = 0; j < KPT; ++j)
-        if (j * kWideThreads + tid < nb && (key[j] >> 10) == prefix) atomicAdd(&sm.h1[key[j] & 1023u], 1u);
+        if ((key[j] >> 10) == prefix) atomicAdd(&sm.h1[key[j] & 1023u], 1u);
       __syncthreads();
-      uint32_t cnt1[1] = {tid < 1024 ? sm.h1[tid] : 0u};
+      uint32_t cnt1[1] = {sm.h1[tid]};
+      if (tid == 0 && prefix == 0u) cnt1[0] -= (uint32_t)n_pad;
       wide_pick<1>(cnt1, k_rem, sm);
       prefix = (prefix << 10) | (uint32_t)sm.pick[0];
       k_rem -= sm.pick[1];
       width = 32;
-      whole = sm.pick[2] == k_rem;
+      whole = sm.pick[2] == k_rem && prefix != 0u;
       __syncthreads();
     }
   }
   // ---- kept blocks -> bitmap -----------------------------------------------------------
-  // Above the prefix, or inside its bin when the bin is taken whole, always kept; at
-  // full width with the bin not whole, the keys equal to T go to the tie bitmap.
+  // Above the prefix, or inside its bin when the bin is taken whole, always kept;
+  // otherwise the keys equal to the prefix go to the tie bitmap.  Padding keys are 0:
+  // never above a prefix, and equal only to a prefix of 0, which is never whole.
   const int shift = 32 - width;
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
     const int idx = j * kWideThreads + tid;
-    if (idx < nb) {
-      const uint32_t hi = (uint32_t)((uint64_t)key[j] >> shift);
-      if (hi > prefix || (whole && hi == prefix)) atomicOr(&sm.keep[idx >> 5], 1u << (idx & 31));
-      else if (hi == prefix) atomicOr(&sm.tie[idx >> 5], 1u << (idx & 31));
-    }
+    const uint32_t hi = (uint32_t)((uint64_t)key[j] >> shift);
+    if (hi > prefix || (whole && hi == prefix)) atomicOr(&sm.keep[idx >> 5], 1u << (idx & 31));
+    else if (hi == prefix) atomicOr(&sm.tie[idx >> 5], 1u << (idx & 31));
   }
   __syncthreads();
   uint32_t word = sm.keep[tid];
