@@ -24,6 +24,8 @@
 //
 // Partial results: o (unnormalised, float32), m (running max, log2 units) and l
 // (sum of weights) per (query, head, split); the combine kernel merges the splits.
+#include <type_traits>
+
 #include "sa_common.hpp"
 #include "sa_launch.hpp"
 
@@ -72,6 +74,11 @@ template <> struct pv_mfma<f16> {
 // ---------------------------------------------------------------------------- MFMA
 
 constexpr int kMfmaTile = 64;        // rows per workgroup tile: S for 16 per wave
+
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS operations but
+// not for its global loads (a __syncthreads fence waits for those too).  The memory
+// clobber keeps the compiler from moving memory operations across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Lane `src` (wave-uniform) of a 64-bit per-lane value.
 __device__ __forceinline__ int64_t readlane64(int64_t x, int src) {
@@ -289,44 +296,296 @@ fwd_mfma_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, 
   };
 
   // Pipeline: while tile t is computed, tiles t+1 .. t+PD are in flight and the list
-  // entries of tiles t+PD+1 and t+PD+2 are in registers.
+  // entries of tiles t+PD+1 and t+PD+2 are in registers.  Inside the loop every step
+  // issues its next tile unconditionally (past the end a tile has no selected rows
+  // and gathers the Q row), so the number of loads in flight behind each tile is
+  // the same on every path and the wait before landing a tile leaves the next
+  // tile's loads outstanding; the last tile is landed by a step that issues nothing.
   uint64_t vq[PD];                                   // selected-row masks of tiles t .. t+PD-1
 #pragma unroll
-  for (int b = 0; b < PD; ++b) vq[b] = 0;
+  for (int u = 0; u < PD; ++u) vq[u] = 0;
   int rawA = PD == 2 ? pre2 : pre1;                  // list entries of tile t+PD
   int rawB = PD == 2 ? pre3 : pre2;                  // and of tile t+PD+1
-  if (n_tiles > 0) {
-    const TileRows r0 = tile_rows(pre0, 0);
-    vq[0] = r0.valid;
-    issue(kbuf[0], vbuf[0], r0);
-    if (PD == 2 && n_tiles > 1) {
-      const TileRows r1 = tile_rows(pre1, 1);
-      vq[PD - 1] = r1.valid;
-      issue(kbuf[PD - 1], vbuf[PD - 1], r1);
+  auto step = [&](int t, V8 (&kr)[KLD], V8 (&vr)[VLD], auto issue_next) {
+    land(kr, vr);
+    __syncthreads();
+    if constexpr (decltype(issue_next)::value) {
+      const int raw_new = list_at(t + PD + 2);       // before the gathers: waiting for it must not wait for them
+      const TileRows rn = tile_rows(rawA, t + PD);
+      issue(kr, vr, rn);
+      compute(vq[0]);
+#pragma unroll
+      for (int u = 0; u + 1 < PD; ++u) vq[u] = vq[u + 1];
+      vq[PD - 1] = rn.valid;
+      rawA = rawB;
+      rawB = raw_new;
+    } else {
+      compute(vq[0]);
+#pragma unroll
+      for (int u = 0; u + 1 < PD; ++u) vq[u] = vq[u + 1];
     }
-  }
-  for (int t0 = 0; t0 < n_tiles; t0 += PD) {
-#pragma unroll
-    for (int b = 0; b < PD; ++b) {
-      const int t = t0 + b;
-      if (t < n_tiles) {
-        land(kbuf[b], vbuf[b]);
-        __syncthreads();
-        const int raw_new = list_at(t + PD + 2);     // before the gathers: waiting for it must not wait for them
-        const TileRows rn = tile_rows(rawA, t + PD);
-        if (t + PD < n_tiles) issue(kbuf[b], vbuf[b], rn);
-        compute(vq[0]);
-        __syncthreads();
-#pragma unroll
-        for (int u = 0; u + 1 < PD; ++u) vq[u] = vq[u + 1];
-        vq[PD - 1] = rn.valid;
-        rawA = rawB;
-        rawB = raw_new;
+    __syncthreads();
+  };
+  using issue_t = std::integral_constant<bool, true>;
+  using final_t = std::integral_constant<bool, false>;
+  if constexpr (PD == 2) {
+    if (n_tiles >= 2) {
+      const TileRows r0 = tile_rows(pre0, 0), r1 = tile_rows(pre1, 1);
+      vq[0] = r0.valid;
+      vq[1] = r1.valid;
+      issue(kbuf[0], vbuf[0], r0);
+      issue(kbuf[1], vbuf[1], r1);
+      int t = 0;
+      for (; t + 1 < n_tiles; t += 2) {
+        step(t, kbuf[0], vbuf[0], issue_t{});
+        step(t + 1, kbuf[1], vbuf[1], issue_t{});
       }
+      if (t < n_tiles) step(t, kbuf[0], vbuf[0], final_t{});
+    } else if (n_tiles == 1) {
+      const TileRows r0 = tile_rows(pre0, 0);
+      vq[0] = r0.valid;
+      issue(kbuf[0], vbuf[0], r0);
+      step(0, kbuf[0], vbuf[0], final_t{});
+    }
+  } else {
+    if (n_tiles >= 1) {
+      const TileRows r0 = tile_rows(pre0, 0);
+      vq[0] = r0.valid;
+      issue(kbuf[0], vbuf[0], r0);
+      int t = 0;
+      for (; t + 1 < n_tiles; ++t) step(t, kbuf[0], vbuf[0], issue_t{});
+      step(t, kbuf[0], vbuf[0], final_t{});
     }
   }
 
   // ---- this wave's dims of the result (or of the split's partial) ------------------
+  if (col < G) {
+    const int hq = g * G + col;
+    const int64_t qh = (int64_t)i * h_q + hq;
+    if (n_split == 1) {
+      const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt)
+        *reinterpret_cast<f32x4*>(out + qh * DV + dvb + nt * 16 + 4 * grp) = o[nt] * inv;
+    } else {
+      float* dst = ws_o + (qh * n_split + split) * DV + dvb;
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) *reinterpret_cast<f32x4*>(dst + nt * 16 + 4 * grp) = o[nt];
+      if (wave == 0 && grp == 0) {
+        ws_ml[(qh * n_split + split) * 2 + 0] = m;
+        ws_ml[(qh * n_split + split) * 2 + 1] = lsum;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------- MFMA, direct-to-LDS gathers (MLA)
+
+// For V aliasing K with DV = 512 (DKQ 512 or 576, the MLA shapes) the rows go from
+// memory straight into LDS (global_load_lds_dwordx4: each lane names its own 16
+// source bytes, and a wave instruction fills 1 KiB of LDS contiguously).  One wave
+// instruction therefore carries the first 512 dims of one row, with a wave-uniform
+// row offset read from the lane that holds it; the 64 dims past 512 (DKQ 576) go 8
+// rows to an instruction into a dense region whose 16-byte chunks are XOR-swizzled
+// by row so that the MFMA operand reads spread over the LDS banks.  Tiles are
+// double-buffered in LDS: tile t+1 is in flight while tile t is computed.  There are
+// no register buffers and no landing stores; the compute is that of the kernel above.
+template <typename T, int DKQ>
+__global__ void __launch_bounds__(256, 1)
+fwd_lds_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, int64_t k_hs,
+               const int64_t* __restrict__ seq_row0, const int32_t* __restrict__ seq_len,
+               const int32_t* __restrict__ q_seq, const int32_t* __restrict__ sel, int64_t sel_ld,
+               const int32_t* __restrict__ n_sel, int h_q, int h_kv, float scale_log2, int n_split,
+               int rows_per_split, float* __restrict__ out, float* __restrict__ ws_o, float* __restrict__ ws_ml) {
+  typedef typename vec8<T>::type V8;
+  typedef __attribute__((address_space(3))) void lds_void;
+  constexpr int DV = 512;
+  constexpr int RT = kMfmaTile;       // = 64: one list entry per lane
+  constexpr int KST = DKQ / 32;       // QK^T MFMA steps
+  constexpr int MP = 512 + 8;         // pitch of the main region (elements)
+  constexpr int REM = (DKQ - 512) / 8;                // 16-byte chunks per row past 512 dims (0 or 8)
+  constexpr int REMP = REM > 0 ? REM : 1;
+  constexpr int DVW = DV / 4;         // output dims owned by one wave
+  constexpr int NTW = DVW / 16;       // its 16-dim MFMA tiles
+  constexpr int SP = RT + 4;          // pitch of the transposed score tile (floats)
+  static_assert(DKQ == 512 || DKQ == 576, "MLA shapes only");
+  // Two tile buffers as separate LDS objects, so that reads of one need not wait for
+  // the gathers landing in the other.
+  __shared__ __attribute__((aligned(16))) T kmain0[RT * MP];
+  __shared__ __attribute__((aligned(16))) T kmain1[RT * MP];
+  __shared__ __attribute__((aligned(16))) T krem0[RT * REMP * 8];
+  __shared__ __attribute__((aligned(16))) T krem1[RT * REMP * 8];
+  __shared__ __attribute__((aligned(16))) float st[16 * SP];   // scaled scores, [head][row]
+
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int col = lane & 15, grp = lane >> 4;
+  const int split = blockIdx.x;
+  const int i = blockIdx.y / h_kv, g = blockIdx.y % h_kv;
+  const int G = h_q / h_kv;
+  const int32_t* list = sel + (int64_t)i * sel_ld;
+  const int r_begin = split * rows_per_split;
+  const int lim = (int)sel_ld - 1;
+  auto list_at = [&](int t) { return list[min(r_begin + t * RT + lane, lim)]; };
+  const int pre0 = list_at(0), pre1 = list_at(1), pre2 = list_at(2);
+  const SeqMeta sm = seq_meta(q_seq, seq_len, seq_row0, nullptr, i);
+  const int L = sm.len;
+  const int64_t row0 = sm.row0;
+  const int cnt = max(0, (int)min((int64_t)n_sel[i], sel_ld));
+  const int r_end = min(cnt, r_begin + rows_per_split);
+  const int n_tiles = r_end > r_begin ? (r_end - r_begin + RT - 1) / RT : 0;
+  const T* kg = k + (int64_t)g * k_hs;
+
+  const T* qbase = q + ((int64_t)i * h_q + (int64_t)g * G) * DKQ;
+  V8 qf[KST];
+  {
+    const T* qh = qbase + (col < G ? col : 0) * DKQ + grp * 8;
+#pragma unroll
+    for (int st_ = 0; st_ < KST; ++st_) qf[st_] = *reinterpret_cast<const V8*>(qh + st_ * 32);
+    if (col >= G) {
+#pragma unroll
+      for (int st_ = 0; st_ < KST; ++st_) qf[st_] = V8{};
+    }
+  }
+  float m = -INFINITY, lsum = 0.f;
+  f32x4 o[NTW];
+#pragma unroll
+  for (int nt = 0; nt < NTW; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // A tile's rows: lane l has row l's element offset from kg (rows not selected
+  // point at this query's own Q row: finite values, masked to -inf), and a mask
+  // marks the selected rows.
+  const int64_t safe_k = qbase - kg;
+  auto row_off = [&](int pos, int t, uint64_t* valid) {
+    const int64_t row = tile_row(pos, r_begin + t * RT + lane, r_end, L, row0);
+    *valid = __ballot(row >= 0);
+    return row >= 0 ? row * k_ld : safe_k;
+  };
+  // Issue tile t's gathers into LDS buffer b: wave w carries rows w*16 .. w*16+15
+  // (one instruction each) and, for DKQ 576, rows w*16 .. w*16+15 of the dims past
+  // 512 (two instructions of 8 rows).
+  auto issue = [&](T* kmain, T* krem, int64_t ko) {
+    const T* lanep = kg + lane * 8;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int r = wave * 16 + u;
+      const int64_t off = readlane64(ko, r);
+      __builtin_amdgcn_global_load_lds((const void*)(lanep + off), (lds_void*)&kmain[r * MP], 16, 0, 0);
+    }
+    if constexpr (REM > 0) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int r = wave * 16 + u * 8 + lane / REM;   // this lane's row
+        const int p = lane % REM;                       // its LDS chunk within the row
+        const int c = p ^ (r & 7);                      // the source chunk stored there
+        const int lo = __shfl((int)(uint32_t)ko, r), hi = __shfl((int)(uint32_t)((uint64_t)ko >> 32), r);
+        const int64_t off = (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+        __builtin_amdgcn_global_load_lds((const void*)(kg + off + 512 + c * 8),
+                                         (lds_void*)&krem[(wave * 16 + u * 8) * REM * 8], 16, 0, 0);
+      }
+    }
+  };
+
+  const int wr = wave * 16;                          // this wave's 16 rows of S
+  const int dvb = wave * DVW;                        // this wave's output dims
+  // `between` runs after the score tile has been read back: it issues the next
+  // tile's gathers, which then overlap the softmax and the PV products (LDS reads
+  // issued after an LDS-bound load are made to wait for it, so the exchange's reads
+  // come first).
+  auto compute = [&](const T* kmain, const T* krem, uint64_t valid, auto&& between) {
+    {
+      f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+      const int r = wr + col;
+      const T* arow = &kmain[r * MP + grp * 8];
+#pragma unroll
+      for (int st_ = 0; st_ < KST; ++st_) {
+        V8 a;
+        if (st_ < 16) {
+          a = *reinterpret_cast<const V8*>(arow + st_ * 32);
+        } else {
+          const int c = (st_ - 16) * 4 + grp;           // chunk past 512 dims
+          a = *reinterpret_cast<const V8*>(&krem[(r * REMP + (c ^ (r & 7))) * 8]);
+        }
+        if (st_ & 1) s1 = mfma16x16x32<T>(a, qf[st_], s1);
+        else s0 = mfma16x16x32<T>(a, qf[st_], s0);
+      }
+      const f32x4 sacc = s0 + s1;
+      f32x4 x;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) x[j] = ((valid >> (wr + 4 * grp + j)) & 1ull) ? sacc[j] * scale_log2 : -INFINITY;
+      *reinterpret_cast<f32x4*>(st + col * SP + wr + 4 * grp) = x;
+    }
+    lds_barrier();
+    f32x4 xs[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) xs[kk] = *reinterpret_cast<const f32x4*>(st + col * SP + 16 * kk + 4 * grp);
+    between();
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) mx = fmaxf(mx, xs[kk][j]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m, mx);
+    const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m - m_new);
+    T pb[4][4];
+    float psum = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float p = (xs[kk][j] == -INFINITY) ? 0.f : fast_exp2(xs[kk][j] - m_new);
+        psum += p;
+        pb[kk][j] = (T)p;
+      }
+    psum += __shfl_xor(psum, 16);
+    psum += __shfl_xor(psum, 32);
+    lsum = lsum * alpha + psum;
+    m = m_new;
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) o[nt] *= alpha;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const T* vrow = &kmain[(16 * kk + 4 * grp) * MP + dvb + col];
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) {
+        T a[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) a[j] = vrow[j * MP + nt * 16];
+        o[nt] = pv_mfma<T>::run(a, pb[kk], o[nt]);
+      }
+    }
+  };
+
+  // Pipeline: tile t+1's gathers are in flight while tile t's softmax and PV run; the
+  // list runs two tiles ahead of the gathers.  Unrolled by two so that each step names its
+  // buffers statically.
+  if (n_tiles > 0) {
+    uint64_t v0, v1, v2;
+    const int64_t ko0 = row_off(pre0, 0, &v0);
+    issue(kmain0, krem0, ko0);
+    int64_t ko_next = row_off(pre1, 1, &v1);         // tile t+1
+    int raw_next = pre2;                             // tile t+2
+    auto step = [&](int t, const T* km, const T* kr, T* km_next, T* kr_next) {
+      __builtin_amdgcn_s_waitcnt(0);                 // this wave's gathers of tile t (nothing newer is in flight)
+      __syncthreads();                               // everyone's gathers of tile t; tile t-1's buffer is free
+      const int raw_new = list_at(t + 3);
+      compute(km, kr, v0, [&] {
+        if (t + 1 < n_tiles) issue(km_next, kr_next, ko_next);
+      });
+      ko_next = row_off(raw_next, t + 2, &v2);
+      raw_next = raw_new;
+      v0 = v1;
+      v1 = v2;
+    };
+    for (int t = 0; t < n_tiles; t += 2) {
+      step(t, kmain0, krem0, kmain1, krem1);
+      if (t + 1 < n_tiles) step(t + 1, kmain1, krem1, kmain0, krem0);
+    }
+  }
+
   if (col < G) {
     const int hq = g * G + col;
     const int64_t qh = (int64_t)i * h_q + hq;
@@ -557,11 +816,26 @@ static void launch_mfma_t(const sa_dims& d, const CacheArgs& c, const void* q, c
                      d.h_q, d.h_kv, scale_log2, plan.n_split, plan.rows_per_split, out, ws_o, ws_ml);
 }
 
+template <typename T, int DKQ>
+static void launch_lds_t(const sa_dims& d, const CacheArgs& c, const void* q, const int32_t* q_seq,
+                         const int32_t* sel, int64_t sel_ld, const int32_t* n_sel, int n_q, float scale_log2,
+                         float* out, float* ws_o, float* ws_ml, const FwdPlan& plan, hipStream_t stream) {
+  dim3 grid(plan.n_split, n_q * d.h_kv);
+  hipLaunchKernelGGL((fwd_lds_kernel<T, DKQ>), grid, dim3(256), 0, stream, (const T*)q, (const T*)c.k, c.k_ld,
+                     c.k_hs, c.seq_row0, c.seq_len, q_seq, sel, sel_ld, n_sel, d.h_q, d.h_kv, scale_log2,
+                     plan.n_split, plan.rows_per_split, out, ws_o, ws_ml);
+}
+
 template <typename T>
 static void dispatch_mfma(const sa_dims& d, const CacheArgs& c, const void* q, const int32_t* q_seq,
                           const int32_t* sel, int64_t sel_ld, const int32_t* n_sel, int n_q, float scale_log2,
                           float* out, float* ws_o, float* ws_ml, const FwdPlan& plan, hipStream_t stream) {
   const bool alias = c.v == c.k && c.v_ld == c.k_ld && c.v_hs == c.k_hs;
+  if (alias && d.d_v == 512 && (d.d_kq == 576 || d.d_kq == 512)) {   // MLA: gathers straight into LDS
+    if (d.d_kq == 576) launch_lds_t<T, 576>(d, c, q, q_seq, sel, sel_ld, n_sel, n_q, scale_log2, out, ws_o, ws_ml, plan, stream);
+    else launch_lds_t<T, 512>(d, c, q, q_seq, sel, sel_ld, n_sel, n_q, scale_log2, out, ws_o, ws_ml, plan, stream);
+    return;
+  }
 #define SA_FWD_CASE(DKQ_, DV_)                                                                                  \
   if (d.d_kq == DKQ_ && d.d_v == DV_) {                                                                          \
     if (alias) launch_mfma_t<T, DKQ_, DV_, true>(d, c, q, q_seq, sel, sel_ld, n_sel, n_q, scale_log2, out, ws_o, \
