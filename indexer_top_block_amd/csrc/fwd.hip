@@ -56,6 +56,10 @@ __device__ __forceinline__ f32x4 mfma16x16x32<f16>(const f16x8& a, const f16x8& 
 // 16x16x16 product with four 16-bit A and B elements per lane.
 template <typename T> struct pv_mfma;
 template <> struct pv_mfma<bf16> {
+  static __device__ __forceinline__ f32x4 run_v(const i16x4& a, const bf16 (&b)[4], const f32x4& c) {
+    bf16x4 bv = {b[0], b[1], b[2], b[3]};
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, __builtin_bit_cast(i16x4, bv), c, 0, 0, 0);
+  }
   static __device__ __forceinline__ f32x4 run(const bf16 (&a)[4], const bf16 (&b)[4], const f32x4& c) {
     bf16x4 av = {a[0], a[1], a[2], a[3]};
     bf16x4 bv = {b[0], b[1], b[2], b[3]};
@@ -64,6 +68,10 @@ template <> struct pv_mfma<bf16> {
   }
 };
 template <> struct pv_mfma<f16> {
+  static __device__ __forceinline__ f32x4 run_v(const i16x4& a, const f16 (&b)[4], const f32x4& c) {
+    f16x4 bv = {b[0], b[1], b[2], b[3]};
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a), bv, c, 0, 0, 0);
+  }
   static __device__ __forceinline__ f32x4 run(const f16 (&a)[4], const f16 (&b)[4], const f32x4& c) {
     f16x4 av = {a[0], a[1], a[2], a[3]};
     f16x4 bv = {b[0], b[1], b[2], b[3]};
@@ -402,7 +410,7 @@ fwd_lds_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, i
   constexpr int DV = 512;
   constexpr int RT = kMfmaTile;       // = 64: one list entry per lane
   constexpr int KST = DKQ / 32;       // QK^T MFMA steps
-  constexpr int MP = 512 + 8;         // pitch of the main region (elements)
+  constexpr int MP = 512 + 16;        // pitch of the main region (elements): 8 dwords mod 64 banks
   constexpr int REM = (DKQ - 512) / 8;                // 16-byte chunks per row past 512 dims (0 or 8)
   constexpr int REMP = REM > 0 ? REM : 1;
   constexpr int DVW = DV / 4;         // output dims owned by one wave
@@ -546,15 +554,17 @@ fwd_lds_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, i
     m = m_new;
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt) o[nt] *= alpha;
+    // V^T operand by transposing LDS reads: in each 16-lane group, lane r reads 4
+    // dims at row 4*grp + r/4, dims 4*(r%4) .. +4 of the 16-dim tile, and lane i then
+    // holds dim i of rows 4*grp .. 4*grp+3 -- the A-operand layout.
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      const T* vrow = &kmain[(16 * kk + 4 * grp) * MP + dvb + col];
+      const T* vrow = &kmain[(16 * kk + 4 * grp + (col >> 2)) * MP + dvb + 4 * (col & 3)];
 #pragma unroll
       for (int nt = 0; nt < NTW; ++nt) {
-        T a[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) a[j] = vrow[j * MP + nt * 16];
-        o[nt] = pv_mfma<T>::run(a, pb[kk], o[nt]);
+        const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(vrow + nt * 16));
+        o[nt] = pv_mfma<T>::run_v(a, pb[kk], o[nt]);
       }
     }
   };
