@@ -106,8 +106,8 @@ fwd_mfma_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, 
   typedef typename vec8<T>::type V8;
   constexpr int RT = kMfmaTile;       // = 64: one list entry per lane
   constexpr int KST = DKQ / 32;       // QK^T MFMA steps
-  constexpr int KP = DKQ + 8;         // LDS row pitch of the K tile (elements)
-  constexpr int VP = ALIAS ? KP : DV + 8;
+  constexpr int KP = DKQ + 16;        // LDS row pitches (elements): 8 dwords mod 64 banks (40 for DKQ 576)
+  constexpr int VP = ALIAS ? KP : DV + 16;
   constexpr int DVW = DV / 4;         // output dims owned by one wave
   constexpr int NTW = DVW / 16;       // its 16-dim MFMA tiles
   constexpr int KCH = DKQ / 8;        // 16-byte chunks per K row
@@ -290,15 +290,17 @@ fwd_mfma_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, 
     // O^T[dv][head] = alpha * O^T + V^T[dv][row] P^T[row][head] for this wave's dims.
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt) o[nt] *= alpha;
+    // V^T operand by transposing LDS reads: in each 16-lane group, lane r reads 4
+    // dims at row 4*grp + r/4, dims 4*(r%4) .. +4 of the 16-dim tile, and lane i then
+    // holds dim i of rows 4*grp .. 4*grp+3 -- the A-operand layout.
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      const T* vrow = vs + (16 * kk + 4 * grp) * VP + dvb + col;
+      const T* vrow = vs + (16 * kk + 4 * grp + (col >> 2)) * VP + dvb + 4 * (col & 3);
 #pragma unroll
       for (int nt = 0; nt < NTW; ++nt) {
-        T a[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) a[j] = vrow[j * VP + nt * 16];
-        o[nt] = pv_mfma<T>::run(a, pb[kk], o[nt]);
+        const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(vrow + nt * 16));
+        o[nt] = pv_mfma<T>::run_v(a, pb[kk], o[nt]);
       }
     }
   };
@@ -356,13 +358,24 @@ fwd_mfma_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, 
       step(0, kbuf[0], vbuf[0], final_t{});
     }
   } else {
+    // One buffer: only one tile is ever in flight, so the plain loop (conditional
+    // issue, conservative waits) loses nothing.
     if (n_tiles >= 1) {
       const TileRows r0 = tile_rows(pre0, 0);
       vq[0] = r0.valid;
       issue(kbuf[0], vbuf[0], r0);
-      int t = 0;
-      for (; t + 1 < n_tiles; ++t) step(t, kbuf[0], vbuf[0], issue_t{});
-      step(t, kbuf[0], vbuf[0], final_t{});
+      for (int t = 0; t < n_tiles; ++t) {
+        land(kbuf[0], vbuf[0]);
+        __syncthreads();
+        const int raw_new = list_at(t + 3);
+        const TileRows rn = tile_rows(rawA, t + 1);
+        if (t + 1 < n_tiles) issue(kbuf[0], vbuf[0], rn);
+        compute(vq[0]);
+        __syncthreads();
+        vq[0] = rn.valid;
+        rawA = rawB;
+        rawB = raw_new;
+      }
     }
   }
 
@@ -854,8 +867,15 @@ static void dispatch_mfma(const sa_dims& d, const CacheArgs& c, const void* q, c
                                             ws_ml, plan, stream);                                                \
     return;                                                                                                      \
   }
-  SA_FWD_CASE(576, 512)
-  SA_FWD_CASE(512, 512)
+  // (V aliasing K at DV 512 went to the LDS kernel above)
+  if (d.d_kq == 576 && d.d_v == 512) {
+    launch_mfma_t<T, 576, 512, false>(d, c, q, q_seq, sel, sel_ld, n_sel, n_q, scale_log2, out, ws_o, ws_ml, plan, stream);
+    return;
+  }
+  if (d.d_kq == 512 && d.d_v == 512) {
+    launch_mfma_t<T, 512, 512, false>(d, c, q, q_seq, sel, sel_ld, n_sel, n_q, scale_log2, out, ws_o, ws_ml, plan, stream);
+    return;
+  }
   SA_FWD_CASE(256, 256)
   SA_FWD_CASE(128, 128)
 #undef SA_FWD_CASE
