@@ -408,11 +408,12 @@ fwd_mfma_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, 
 // instruction therefore carries the first 512 dims of one row, with a wave-uniform
 // row offset read from the lane that holds it; the 64 dims past 512 (DKQ 576) go 8
 // rows to an instruction into a dense region whose 16-byte chunks are XOR-swizzled
-// by row so that the MFMA operand reads spread over the LDS banks.  Tiles are
-// double-buffered in LDS: tile t+1 is in flight while tile t is computed.  There are
-// no register buffers and no landing stores; the compute is that of the kernel above.
+// by row so that the MFMA operand reads spread over the LDS banks.  One tile buffer
+// per workgroup keeps LDS at 78 KiB, so two workgroups share a CU and one's gathers
+// overlap the other's compute.  There are no register buffers and no landing
+// stores; the compute is that of the kernel above.
 template <typename T, int DKQ>
-__global__ void __launch_bounds__(256, 1)
+__global__ void __launch_bounds__(256, 2)
 fwd_lds_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, int64_t k_hs,
                const int64_t* __restrict__ seq_row0, const int32_t* __restrict__ seq_len,
                const int32_t* __restrict__ q_seq, const int32_t* __restrict__ sel, int64_t sel_ld,
@@ -430,12 +431,10 @@ fwd_lds_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, i
   constexpr int NTW = DVW / 16;       // its 16-dim MFMA tiles
   constexpr int SP = RT + 4;          // pitch of the transposed score tile (floats)
   static_assert(DKQ == 512 || DKQ == 576, "MLA shapes only");
-  // Two tile buffers as separate LDS objects, so that reads of one need not wait for
-  // the gathers landing in the other.
+  // One tile buffer (78 KiB with the score tile), so that two workgroups share a CU:
+  // one computes while the other's gathers land.
   __shared__ __attribute__((aligned(16))) T kmain0[RT * MP];
-  __shared__ __attribute__((aligned(16))) T kmain1[RT * MP];
   __shared__ __attribute__((aligned(16))) T krem0[RT * REMP * 8];
-  __shared__ __attribute__((aligned(16))) T krem1[RT * REMP * 8];
   __shared__ __attribute__((aligned(16))) float st[16 * SP];   // scaled scores, [head][row]
 
   const int tid = threadIdx.x;
@@ -510,11 +509,7 @@ fwd_lds_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, i
 
   const int wr = wave * 16;                          // this wave's 16 rows of S
   const int dvb = wave * DVW;                        // this wave's output dims
-  // `between` runs after the score tile has been read back: it issues the next
-  // tile's gathers, which then overlap the softmax and the PV products (LDS reads
-  // issued after an LDS-bound load are made to wait for it, so the exchange's reads
-  // come first).
-  auto compute = [&](const T* kmain, const T* krem, uint64_t valid, auto&& between) {
+  auto compute = [&](const T* kmain, const T* krem, uint64_t valid) {
     {
       f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
       const int r = wr + col;
@@ -541,7 +536,6 @@ fwd_lds_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, i
     f32x4 xs[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) xs[kk] = *reinterpret_cast<const f32x4*>(st + col * SP + 16 * kk + 4 * grp);
-    between();
     float mx = -INFINITY;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
@@ -582,30 +576,24 @@ fwd_lds_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, i
     }
   };
 
-  // Pipeline: tile t+1's gathers are in flight while tile t's softmax and PV run; the
-  // list runs two tiles ahead of the gathers.  Unrolled by two so that each step names its
-  // buffers statically.
+  // Per tile: wait for its gathers, compute it, then gather the next one into the
+  // same buffer (the other workgroup on the CU runs meanwhile); the list runs two
+  // tiles ahead of the gathers.
   if (n_tiles > 0) {
-    uint64_t v0, v1, v2;
-    const int64_t ko0 = row_off(pre0, 0, &v0);
-    issue(kmain0, krem0, ko0);
-    int64_t ko_next = row_off(pre1, 1, &v1);         // tile t+1
-    int raw_next = pre2;                             // tile t+2
-    auto step = [&](int t, const T* km, const T* kr, T* km_next, T* kr_next) {
-      __builtin_amdgcn_s_waitcnt(0);                 // this wave's gathers of tile t (nothing newer is in flight)
-      __syncthreads();                               // everyone's gathers of tile t; tile t-1's buffer is free
+    uint64_t v0, v1;
+    issue(kmain0, krem0, row_off(pre0, 0, &v0));
+    int raw1 = pre1, raw2 = pre2;                    // list entries of tiles t+1 and t+2
+    for (int t = 0; t < n_tiles; ++t) {
+      __builtin_amdgcn_s_waitcnt(0);                 // this wave's gathers of tile t
+      __syncthreads();                               // everyone's
       const int raw_new = list_at(t + 3);
-      compute(km, kr, v0, [&] {
-        if (t + 1 < n_tiles) issue(km_next, kr_next, ko_next);
-      });
-      ko_next = row_off(raw_next, t + 2, &v2);
-      raw_next = raw_new;
+      const int64_t ko1 = row_off(raw1, t + 1, &v1);
+      compute(kmain0, krem0, v0);
+      __syncthreads();                               // the buffer is free
+      if (t + 1 < n_tiles) issue(kmain0, krem0, ko1);
       v0 = v1;
-      v1 = v2;
-    };
-    for (int t = 0; t < n_tiles; t += 2) {
-      step(t, kmain0, krem0, kmain1, krem1);
-      if (t + 1 < n_tiles) step(t + 1, kmain1, krem1, kmain0, krem0);
+      raw1 = raw2;
+      raw2 = raw_new;
     }
   }
 
