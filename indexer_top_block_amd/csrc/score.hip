@@ -7,9 +7,9 @@
 //
 // MFMA path (f16 / bf16, h_idx a multiple of 32, d_idx in {64, 128, 256}): a wave
 // holds one query's indexer heads as the M operand of v_mfma_f32_32x32x16 in
-// registers (loaded once) and streams 32 pooled keys per tile as the N operand
-// straight from HBM -- each lane loads one key's contiguous half row, so no LDS is
-// needed.  The contraction index is permuted identically in both operands (lane half
+// registers (staged once per workgroup through LDS) and streams 32 pooled keys per
+// tile as the N operand straight from HBM -- each lane loads one key's contiguous
+// half row.  The contraction index is permuted identically in both operands (lane half
 // hf, step s, slot j <-> dim hf*D/2 + s*8 + j), which leaves the dot products
 // unchanged.  The epilogue rectifies the 32x32 fp32 tile, sums the 16 rows a lane
 // holds, and adds the partner lane (lane ^ 32) that holds the other 16 rows of the
@@ -50,33 +50,57 @@ score_mfma_kernel(const T* __restrict__ qidx, const T* __restrict__ kpool, int64
                   float* __restrict__ scores, int64_t scores_ld) {
   typedef typename vec8<T>::type V8;
   constexpr int KS = D / 16;          // MFMA steps over the indexer dim (8 per lane half)
+  constexpr int QP = D + 8;           // LDS pitch of a staged head row (elements)
+  constexpr int QCH = MT * 32 * D / 8;                // 16-byte chunks of the query's heads
+  constexpr int QLD = (QCH + 255) / 256;              // per thread
+  __shared__ __attribute__((aligned(16))) T qs[MT * 32 * QP];
   const int i = blockIdx.y;
+  const int tid = threadIdx.x;
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
   const int n = lane & 31;
   const int hf = lane >> 5;
-  // Indexer query heads mt*32 + n, dim slices of this lane's half; read alongside the
-  // query's metadata, which the key addresses depend on.
-  const T* qrow = qidx + (int64_t)i * (MT * 32) * D + (int64_t)n * D + hf * (D / 2);
+  // The query's indexer heads are staged once per workgroup in LDS (the four waves
+  // share them); they are read alongside the query's metadata, which the key
+  // addresses depend on.
+  const T* qrow = qidx + (int64_t)i * (MT * 32) * D;
+  V8 qreg[QLD];
+#pragma unroll
+  for (int j = 0; j < QLD; ++j) {
+    const int e = min(tid + 256 * j, QCH - 1);
+    qreg[j] = *reinterpret_cast<const V8*>(qrow + (int64_t)e * 8);
+  }
+  const SeqMeta sm = seq_meta(q_seq, seq_len, nullptr, seq_blk0, i);
+  const int nb = visible_tokens(sm.len, q_pos[i]) / c;
+  const int b_base = (blockIdx.x * kScoreWaves + wave) * kScoreTile;
+
+  // Pooled keys: one 16-byte slice per step of this lane's half row (clamped into
+  // the visible blocks; scores past them are not written).
+  const int b = b_base + n;
+  const bool valid = b < nb;
+  V8 kb[KS];
+  const T* krow = kpool + (sm.blk0 + (valid ? b : max(nb - 1, 0))) * kpool_ld + hf * (D / 2);
+  if (b_base < nb) {
+#pragma unroll
+    for (int st = 0; st < KS; ++st) kb[st] = *reinterpret_cast<const V8*>(krow + st * 8);
+  }
+#pragma unroll
+  for (int j = 0; j < QLD; ++j) {
+    const int e = tid + 256 * j;
+    if (e < QCH) {
+      const int r = e / (D / 8), cc = e % (D / 8);
+      *reinterpret_cast<V8*>(qs + r * QP + cc * 8) = qreg[j];
+    }
+  }
+  __syncthreads();
+  if (b_base >= nb) return;
+  // A operand: lane (n, hf) takes head mt*32 + n, dims hf*D/2 + st*8 .. +8.
   V8 qa[MT][KS];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int st = 0; st < KS; ++st) qa[mt][st] = *reinterpret_cast<const V8*>(qrow + (int64_t)mt * 32 * D + st * 8);
-  const SeqMeta sm = seq_meta(q_seq, seq_len, nullptr, seq_blk0, i);
-  const int nb = visible_tokens(sm.len, q_pos[i]) / c;
-  const int b_base = (blockIdx.x * kScoreWaves + wave) * kScoreTile;
-  if (b_base >= nb) return;
-
-  // Pooled keys: one 16-byte slice per step of this lane's half row.
-  const int b = b_base + n;
-  const bool valid = b < nb;
-  V8 kb[KS];
-  const T* krow = kpool + (sm.blk0 + (valid ? b : 0)) * kpool_ld + hf * (D / 2);
-#pragma unroll
-  for (int st = 0; st < KS; ++st) {
-    kb[st] = valid ? *reinterpret_cast<const V8*>(krow + st * 8) : V8{};
-  }
+    for (int st = 0; st < KS; ++st)
+      qa[mt][st] = *reinterpret_cast<const V8*>(qs + (mt * 32 + n) * QP + hf * (D / 2) + st * 8);
 
   float sum = 0.f;
 #pragma unroll
