@@ -8,8 +8,8 @@
 // MFMA path (f16 / bf16, h_idx a multiple of 32, d_idx in {64, 128, 256}): a wave
 // holds one query's indexer heads as the M operand of v_mfma_f32_32x32x16 in
 // registers (staged once per workgroup through LDS) and streams 32 pooled keys per
-// tile as the N operand straight from HBM -- each lane loads one key's contiguous
-// half row.  The contraction index is permuted identically in both operands (lane half
+// tile as the N operand from HBM straight into LDS (global_load_lds, four whole keys
+// per wave instruction).  The contraction index is permuted identically in both operands (lane half
 // hf, step s, slot j <-> dim hf*D/2 + s*8 + j), which leaves the dot products
 // unchanged.  The epilogue rectifies the 32x32 fp32 tile, sums the 16 rows a lane
 // holds, and adds the partner lane (lane ^ 32) that holds the other 16 rows of the
@@ -54,6 +54,7 @@ score_mfma_kernel(const T* __restrict__ qidx, const T* __restrict__ kpool, int64
   constexpr int QCH = MT * 32 * D / 8;                // 16-byte chunks of the query's heads
   constexpr int QLD = (QCH + 255) / 256;              // per thread
   __shared__ __attribute__((aligned(16))) T qs[MT * 32 * QP];
+  __shared__ __attribute__((aligned(16))) T ks[kScoreWaves * kScoreTile * D];
   const int i = blockIdx.y;
   const int tid = threadIdx.x;
   const int wave = threadIdx.x / kWave;
@@ -74,15 +75,25 @@ score_mfma_kernel(const T* __restrict__ qidx, const T* __restrict__ kpool, int64
   const int nb = visible_tokens(sm.len, q_pos[i]) / c;
   const int b_base = (blockIdx.x * kScoreWaves + wave) * kScoreTile;
 
-  // Pooled keys: one 16-byte slice per step of this lane's half row (clamped into
-  // the visible blocks; scores past them are not written).
+  // Pooled keys: each wave gathers its 32 keys straight into its own LDS region,
+  // four whole keys per instruction (fully coalesced), clamped into the visible
+  // blocks (scores past them are not written).  Chunk c of key k sits at position
+  // c ^ (k % CH) of the key's row, so that the operand reads below, 32 keys at one
+  // chunk, spread over the LDS banks.
+  typedef __attribute__((address_space(3))) void lds_void;
+  constexpr int CH = D / 8;                          // 16-byte chunks per key
+  constexpr int KPI = kWave / CH;                    // keys per instruction
   const int b = b_base + n;
   const bool valid = b < nb;
-  V8 kb[KS];
-  const T* krow = kpool + (sm.blk0 + (valid ? b : max(nb - 1, 0))) * kpool_ld + hf * (D / 2);
+  T* kw = ks + wave * kScoreTile * D;
   if (b_base < nb) {
+    const int last = nb - 1;
 #pragma unroll
-    for (int st = 0; st < KS; ++st) kb[st] = *reinterpret_cast<const V8*>(krow + st * 8);
+    for (int j = 0; j < kScoreTile / KPI; ++j) {
+      const int kk = j * KPI + lane / CH, p = lane % CH, c = p ^ (kk & (CH - 1));
+      const T* src = kpool + (sm.blk0 + min(b_base + kk, last)) * kpool_ld + c * 8;
+      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(kw + j * kWave * 8), 16, 0, 0);
+    }
   }
 #pragma unroll
   for (int j = 0; j < QLD; ++j) {
@@ -101,6 +112,13 @@ score_mfma_kernel(const T* __restrict__ qidx, const T* __restrict__ kpool, int64
 #pragma unroll
     for (int st = 0; st < KS; ++st)
       qa[mt][st] = *reinterpret_cast<const V8*>(qs + (mt * 32 + n) * QP + hf * (D / 2) + st * 8);
+
+  // B operand: lane (n, hf) takes key n, dims hf*D/2 + st*8 .. +8 (chunk hf*CH/2 + st).
+  __builtin_amdgcn_s_waitcnt(0);                     // this wave's keys are in LDS
+  V8 kb[KS];
+#pragma unroll
+  for (int st = 0; st < KS; ++st)
+    kb[st] = *reinterpret_cast<const V8*>(kw + n * D + (((hf * (CH / 2) + st) ^ (n & (CH - 1))) * 8));
 
   float sum = 0.f;
 #pragma unroll
