@@ -105,13 +105,6 @@ score_mfma_kernel(const T* __restrict__ qidx, const T* __restrict__ kpool, int64
   }
   __syncthreads();
   if (b_base >= nb) return;
-  // A operand: lane (n, hf) takes head mt*32 + n, dims hf*D/2 + st*8 .. +8.
-  V8 qa[MT][KS];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int st = 0; st < KS; ++st)
-      qa[mt][st] = *reinterpret_cast<const V8*>(qs + (mt * 32 + n) * QP + hf * (D / 2) + st * 8);
 
   // B operand: lane (n, hf) takes key n, dims hf*D/2 + st*8 .. +8 (chunk hf*CH/2 + st).
   __builtin_amdgcn_s_waitcnt(0);                     // this wave's keys are in LDS
@@ -120,12 +113,15 @@ score_mfma_kernel(const T* __restrict__ qidx, const T* __restrict__ kpool, int64
   for (int st = 0; st < KS; ++st)
     kb[st] = *reinterpret_cast<const V8*>(kw + n * D + (((hf * (CH / 2) + st) ^ (n & (CH - 1))) * 8));
 
+  // A operand, read from LDS per step: lane (n, hf) takes head mt*32 + n, dims
+  // hf*D/2 + st*8 .. +8.
   float sum = 0.f;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
+    const T* qa = qs + (mt * 32 + n) * QP + hf * (D / 2);
     f32x16 acc = {};
 #pragma unroll
-    for (int st = 0; st < KS; ++st) acc = mfma32x32x16<T>(qa[mt][st], kb[st], acc);
+    for (int st = 0; st < KS; ++st) acc = mfma32x32x16<T>(*reinterpret_cast<const V8*>(qa + st * 8), kb[st], acc);
 #pragma unroll
     for (int r = 0; r < 16; ++r) sum += fmaxf(acc[r], 0.f);
   }
