@@ -290,6 +290,26 @@ def prefill_report(steps: int) -> dict:
     }
 
 
+# ------------------------------------------------------------------ token-level
+
+def token_level_report(steps: int, warmup: int, layers: int) -> dict:
+    """Workload 6: the decode step of workload 2 with token-level selection
+    (compress_ratio 1: 131072 candidates per query, so selection runs on the whole GPU)."""
+    case = datagen.make_workload(6)
+    ab = algorithmic_bytes(case)
+    lay = RotatingLayers(case, layers)
+    lay.fill_pools()
+    torch.cuda.synchronize()
+    ms = time_graph(lambda k: lay.step(k % layers), steps, warmup)
+    kernels = {name: round(time_graph(lambda k, fn=getattr(lay, name): fn(k % layers), steps, warmup) * 1e3, 3)
+               for name in ("pool", "score", "select", "fwd")}
+    del lay
+    torch.cuda.empty_cache()
+    return {"workload": datagen.WORKLOADS[6], "layers_rotated": layers, "us_per_step": round(ms * 1e3, 3),
+            "value": round(ab["total"] / (ms * 1e-3) / 1e9, 2), "unit": "GB/s", "bytes_per_step": ab,
+            "kernel_avg_us": kernels}
+
+
 # --------------------------------------------------------------------------- main
 
 def main() -> int:
@@ -301,6 +321,7 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-token-level", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch every step from the host (no graph)")
     ap.add_argument("--only", choices=["pool", "score", "select", "fwd"], default=None,
                     help="run just this kernel for --steps launches (for counter collection)")
@@ -386,6 +407,11 @@ def main() -> int:
     if not args.no_prefill:
         log("[bench] prefill workload")
         rec["prefill"] = prefill_report(max(5, min(args.steps, 20)))
+    if not args.no_token_level:
+        del lay
+        torch.cuda.empty_cache()
+        log("[bench] token-level decode workload")
+        rec["token_level"] = token_level_report(args.steps, args.warmup, min(args.layers, 32))
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline")
         rec["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds, ab["total"])

@@ -201,7 +201,8 @@ def make_case(name: str, dims: Dims, seq_lens, q_seq, q_pos, *, seed: int, case_
 
 
 # ---------------------------------------------------------------------------
-# The five workloads.  Sizes follow the configurations the library is measured on.
+# The workloads.  Sizes follow the configurations the library is measured on;
+# workload 6 is workload 2 with token-level selection (every token its own block).
 # ---------------------------------------------------------------------------
 
 WORKLOADS = {
@@ -210,6 +211,7 @@ WORKLOADS = {
     3: "batched decode f16: 32 seqs, L~U[4096,65536], 8:1 heads, 512/512, idx 32x128, c=4, top_k=2048",
     4: "prefill chunk bf16: 2048 queries at 32768..34815, 16 heads, 576/512, idx 64x128, c=4, top_k=2048",
     5: "long decode bf16: 1 seq x 1048576 cached, 16 heads, 576/512, idx 64x128, c=4, top_k=2048, 1% planted blocks",
+    6: "token-level decode bf16: 1 seq x 131072 cached, 16 heads on 1 latent KV head, 576/512, idx 64x128, c=1, top_k=2048",
 }
 
 
@@ -222,11 +224,14 @@ def workload_dims(cfg: int) -> Dims:
     if cfg == 3:
         return Dims(h_q=8, h_kv=1, d_kq=512, d_v=512, h_idx=32, d_idx=128, compress_ratio=4, top_k=2048,
                     dtype="f16")
+    if cfg == 6:
+        return Dims(h_q=16, h_kv=1, d_kq=576, d_v=512, h_idx=64, d_idx=128, compress_ratio=1, top_k=2048,
+                    dtype="bf16")
     raise ValueError(f"unknown workload {cfg}")
 
 
 def make_workload(cfg: int, seed: int = 0, ctx: Optional[int] = None) -> Case:
-    """Build workload ``cfg`` (1..5).  ``ctx`` overrides the cached length of the
+    """Build workload ``cfg`` (1..6).  ``ctx`` overrides the cached length of the
     single-sequence decode workloads (used for reduced-size test variants)."""
     dims = workload_dims(cfg)
     if cfg == 1:
@@ -251,4 +256,8 @@ def make_workload(cfg: int, seed: int = 0, ctx: Optional[int] = None) -> Case:
         L = ctx or 1048576
         return make_case("long_decode_1m_bf16", dims, [L], [0], [L], seed=seed, case_id=cfg, std="inv_sqrt_dim",
                          v_separate=False, scale=1.0 / math.sqrt(576), plant_fraction=0.01, plant_sigmas=3.0)
+    if cfg == 6:
+        L = ctx or 131072
+        return make_case("token_level_decode_128k_bf16", dims, [L], [0], [L], seed=seed, case_id=cfg,
+                         std="inv_sqrt_dim", v_separate=False, scale=1.0 / math.sqrt(576))
     raise ValueError(f"unknown workload {cfg}")

@@ -287,6 +287,7 @@ def test_workspace_state_returns_to_zero(gpu_lib):
     (5, None),
     (3, None),
     (4, [0, 1, 2, 3, 511, 1024, 1500, 2046, 2047]),
+    (6, None),
 ])
 def test_full_size_workload(gpu_lib, cfg, queries):
     say(f"[parity] generating workload {cfg}: {datagen.WORKLOADS[cfg]}")
