@@ -261,3 +261,27 @@ def make_workload(cfg: int, seed: int = 0, ctx: Optional[int] = None) -> Case:
         return make_case("token_level_decode_128k_bf16", dims, [L], [0], [L], seed=seed, case_id=cfg,
                          std="inv_sqrt_dim", v_separate=False, scale=1.0 / math.sqrt(576))
     raise ValueError(f"unknown workload {cfg}")
+
+
+# ---------------------------------------------------------------------------
+# Additive masks in the form of the pages' sparse flash-attention tests.
+# ---------------------------------------------------------------------------
+
+def sparse_mask(n_rows: int, n_kv: int, n_kv_max: int, *, seed: int, case_id: int,
+                count_spread: int = 17, single_entry_stride: int = 32, dtype: str = "f16") -> np.ndarray:
+    """[n_rows, n_kv] float32 mask holding exactly the storage values of ``dtype``.
+
+    Row r keeps 1 entry when r is a multiple of ``single_entry_stride`` and otherwise
+    n_kv_max - r mod min(n_kv_max, count_spread) entries, at positions drawn without
+    replacement from the seed; the i-th kept position (ascending) carries the value
+    -(1 + (i + r) mod 7) / 32 and every other entry is -inf ("CUDA + ggml: add
+    sparse-fa for DSV4/GLM", the test-backend-ops mask initialisation).
+    """
+    rng = np.random.default_rng([seed, case_id, 5])
+    m = np.full((n_rows, n_kv), -np.inf, dtype=np.float32)
+    for r in range(n_rows):
+        cnt = 1 if r % single_entry_stride == 0 else n_kv_max - r % min(n_kv_max, count_spread)
+        cnt = min(cnt, n_kv)
+        pos = np.sort(rng.choice(n_kv, size=cnt, replace=False))
+        m[r, pos] = -(1.0 + (np.arange(cnt) + r) % 7) / 32.0
+    return round_to_dtype(m, dtype)

@@ -7,6 +7,7 @@ from .sparse_attn_oracle import (  # noqa: F401
     SequencePools,
     attend,
     block_scores,
+    mask_positions,
     pool_blocks,
     round_to_storage,
     run_case,

@@ -146,11 +146,15 @@ def select_positions_token_expanded(scores: np.ndarray, n_vis: int, c: int, top_
 
 # ------------------------------------------------------------------------- attend
 
-def attend(q: np.ndarray, k_rows: np.ndarray, v_rows: np.ndarray, scale: float) -> np.ndarray:
-    """softmax(scale * q K^T) V over the given rows, per query head.
+def attend(q: np.ndarray, k_rows: np.ndarray, v_rows: np.ndarray, scale: float,
+           bias: np.ndarray | None = None) -> np.ndarray:
+    """softmax(scale * q K^T + bias) V over the given rows, per query head.
 
     ``q`` is [H_q, DKQ]; ``k_rows`` [n, H_kv, DKQ]; ``v_rows`` [n, H_kv, DV].  Query
-    head h reads KV head h // (H_q / H_kv).  With no rows the output is zero
+    head h reads KV head h // (H_q / H_kv).  ``bias`` (optional, [n]) is added to
+    every head's logit of a row: the additive-mask form of the pages' sparse flash
+    attention, where a row's mask value is its bias ("CUDA + ggml: add sparse-fa for
+    DSV4/GLM", the mask-driven sparse mode).  With no rows the output is zero
     (reading: the pages define no value for an empty set).
     """
     q = np.asarray(q, dtype=np.float64)
@@ -163,12 +167,26 @@ def attend(q: np.ndarray, k_rows: np.ndarray, v_rows: np.ndarray, scale: float) 
     out = np.zeros((h_q, d_v), dtype=np.float64)
     if n == 0:
         return out
+    b = np.zeros(n) if bias is None else np.asarray(bias, dtype=np.float64)
     for h in range(h_q):
         g = h // group
-        logits = scale * (k_rows[:, g, :] @ q[h])
+        logits = scale * (k_rows[:, g, :] @ q[h]) + b
         w = np.exp(logits - logits.max())
         out[h] = (w / w.sum()) @ v_rows[:, g, :]
     return out
+
+
+# ------------------------------------------------------------ additive-mask form
+
+def mask_positions(mask_row: np.ndarray) -> np.ndarray:
+    """The positions of a mask row that form the K/V set: its finite entries, in
+    ascending order.  In the pages' sparse flash attention the finite entries of each
+    mask row are the keys attended (their values added to the logits) and the rest
+    (-inf) are skipped; a bound on the finite count per row sizes the index list
+    ("CUDA + ggml: add sparse-fa for DSV4/GLM", ggml_flash_attn_ext_set_sparse and
+    the mask-to-indices kernel).  NaN entries are not finite and are skipped."""
+    m = np.asarray(mask_row, dtype=np.float64)
+    return np.flatnonzero(np.isfinite(m)).astype(np.int64)
 
 
 # ----------------------------------------------------------------------- pipeline

@@ -282,6 +282,54 @@ def test_attend_closed_forms():
     assert np.allclose(oracle.attend(q, k[:1], v[:1], 1.0), np.tile(v[0, 0], (4, 1)))
 
 
+# ------------------------------------------------------------ additive-mask form
+
+def test_mask_positions_follow_the_pages_mask_pattern():
+    """The pages' test masks: 1 finite entry on every 32nd row, otherwise
+    n_kv_max - row mod min(n_kv_max, 17); mask_positions lists exactly the finite
+    entries, ascending, and skips -inf, +inf and NaN."""
+    facts = json.load(open(os.path.join(GOLDEN, "qsa_page_facts.json")))["sparse_mask_pattern"]
+    spread, stride = facts["count_spread"], facts["single_entry_stride"]
+    n_kv, n_kv_max = 4096, 512
+    mask = datagen.sparse_mask(70, n_kv, n_kv_max, seed=0, case_id=900, count_spread=spread,
+                               single_entry_stride=stride)
+    for r in range(70):
+        pos = oracle.mask_positions(mask[r])
+        want = 1 if r % stride == 0 else n_kv_max - r % min(n_kv_max, spread)
+        assert len(pos) == want and np.all(np.diff(pos) > 0)
+        assert np.isfinite(mask[r, pos]).all() and np.isneginf(np.delete(mask[r], pos)).all()
+    row = np.array([0.0, -np.inf, 1.5, np.nan, np.inf, -2.0])
+    assert list(oracle.mask_positions(row)) == [0, 2, 5]
+
+
+def test_attend_bias_matches_library_attention_with_a_float_mask():
+    rng = np.random.default_rng(21)
+    n, h_q, dkq, dv = 50, 8, 32, 24
+    q = rng.standard_normal((h_q, dkq))
+    k = rng.standard_normal((n, 2, dkq))
+    v = rng.standard_normal((n, 2, dv))
+    mask = np.full(n, -np.inf)
+    sel = np.sort(rng.choice(n, 17, replace=False))
+    mask[sel] = rng.uniform(-1.0, 0.5, size=17)
+    got = oracle.attend(q, k[sel], v[sel], 0.2, bias=mask[sel])
+    assert np.allclose(got, _sdpa(q, k, v, 0.2, mask), rtol=1e-12, atol=1e-12)
+
+
+def test_attend_bias_closed_forms():
+    rng = np.random.default_rng(22)
+    q, k, v = rng.standard_normal((4, 8)), rng.standard_normal((10, 1, 8)), rng.standard_normal((10, 1, 6))
+    b = rng.standard_normal(10)
+    # a constant added to every bias leaves the softmax unchanged
+    assert np.allclose(oracle.attend(q, k, v, 0.5, bias=b + 3.25), oracle.attend(q, k, v, 0.5, bias=b),
+                       rtol=1e-13, atol=1e-13)
+    # zero bias is no bias
+    assert np.array_equal(oracle.attend(q, k, v, 0.5, bias=np.zeros(10)), oracle.attend(q, k, v, 0.5))
+    # one row far above the rest takes all the weight
+    dom = np.full(10, -1e4)
+    dom[6] = 0.0
+    assert np.allclose(oracle.attend(q, k, v, 0.5, bias=dom), np.tile(v[6, 0], (4, 1)), rtol=1e-13)
+
+
 # ------------------------------------------------------------------ pipeline
 
 def _small_dims(**kw):
@@ -378,3 +426,9 @@ def test_mutants_are_caught():
     rng = np.random.default_rng(14)
     q, k, v = rng.standard_normal((2, 8)), rng.standard_normal((6, 1, 8)), rng.standard_normal((6, 1, 3))
     assert not np.allclose(oracle.attend(q, k, v, 1.0), _sdpa(q, k, v, 0.25))
+
+    # 7. the mask bias scaled with the logits, or subtracted
+    b = rng.uniform(-1.0, 0.0, size=6)
+    want = _sdpa(q, k, v, 0.25, b)
+    assert not np.allclose(oracle.attend(q, k, v, 0.25, bias=0.25 * b), want)
+    assert not np.allclose(oracle.attend(q, k, v, 0.25, bias=-b), want)
