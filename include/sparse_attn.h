@@ -179,6 +179,39 @@ int sparse_attn_fwd(const sa_dims* dims, const sa_cache* cache, const void* q,
                     const int32_t* q_seq, const int32_t* sel, int64_t sel_ld, const int32_t* n_sel,
                     int32_t n_q, float scale, float* out, void* ws, size_t ws_bytes, void* stream);
 
+/* The additive-mask form of the attention (pages: PR #27970, the sparse mode of the
+ * flash-attention op: the finite entries of each query's mask row are its K/V set
+ * and their values are added to the logits; the caller bounds the finite entries per
+ * row, which sizes the index list).  This call turns masks into the index lists the
+ * attention consumes -- the same form the block selection writes.
+ *   mask:     device, [n_q][mask_ld] of mask_dtype (SA_F16 or SA_F32); column p of row
+ *             i is position p of query token i's sequence.  Entries that are not
+ *             finite (-inf, +inf, NaN) are excluded.  May be NULL when n_kv == 0.
+ *   sel:      device, [n_q][sel_ld] int32 out: row i's finite columns in ascending
+ *             order, then -1 up to sel_ld.
+ *   n_sel:    device, [n_q] int32 out: the number of finite entries of row i; a count
+ *             above sel_ld means the row was cut to its first sel_ld positions.
+ *   sel_bias: device, [n_q][sel_ld] float out, optional (NULL): the mask value at each
+ *             listed position, 0 for the padding -- the bias input of
+ *             sparse_attn_fwd_bias.
+ * Errors: SA_ERR_ARG (bad dtype, negative sizes, sel_ld < 1, mask_ld < n_kv),
+ *         SA_ERR_NULL, SA_ERR_HIP.                                                     */
+int sparse_attn_mask_to_indices(const void* mask, int32_t mask_dtype, int64_t mask_ld, int32_t n_q,
+                                int32_t n_kv, int32_t* sel, int64_t sel_ld, int32_t* n_sel, float* sel_bias,
+                                void* stream);
+
+/* sparse_attn_fwd with an additive logit bias per list entry (pages: PR #27970, the
+ * mask value added to the logit in the mask-driven sparse mode): the logit of list
+ * entry j of query token i, for every head, is
+ *     scale * q[i][h] . K[row][g] + sel_bias[i*sel_ld + j].
+ * sel_bias: device, [n_q][sel_ld] float, or NULL for no bias (then identical to
+ * sparse_attn_fwd).  Entries must be finite or -inf (-inf drops the row).  All other
+ * arguments, the workspace and the errors are those of sparse_attn_fwd.             */
+int sparse_attn_fwd_bias(const sa_dims* dims, const sa_cache* cache, const void* q,
+                         const int32_t* q_seq, const int32_t* sel, int64_t sel_ld, const int32_t* n_sel,
+                         const float* sel_bias, int32_t n_q, float scale, float* out, void* ws,
+                         size_t ws_bytes, void* stream);
+
 /* Static description of an error code (never NULL). */
 const char* sparse_attn_strerror(int code);
 

@@ -118,9 +118,9 @@ int sparse_attn_select(const sa_dims* dims, const sa_cache* cache, const float* 
                                       n_sel, ws, (hipStream_t)stream));
 }
 
-int sparse_attn_fwd(const sa_dims* dims, const sa_cache* cache, const void* q, const int32_t* q_seq,
-                    const int32_t* sel, int64_t sel_ld, const int32_t* n_sel, int32_t n_q, float scale, float* out,
-                    void* ws, size_t ws_bytes, void* stream) {
+static int fwd_common(const sa_dims* dims, const sa_cache* cache, const void* q, const int32_t* q_seq,
+                      const int32_t* sel, int64_t sel_ld, const int32_t* n_sel, const float* sel_bias, int32_t n_q,
+                      float scale, float* out, void* ws, size_t ws_bytes, void* stream) {
   int rc = check_dims(dims);
   if (rc) return rc;
   if ((rc = check_cache_common(dims, cache))) return rc;
@@ -142,8 +142,31 @@ int sparse_attn_fwd(const sa_dims* dims, const sa_cache* cache, const void* q, c
     scratch = (char*)ws + SA_WS_STATE_BYTES;
   }
   (void)hipGetLastError();
-  return hip_status(sa::launch_fwd(*dims, to_args(cache), q, q_seq, sel, sel_ld, n_sel, n_q, scale, out, scratch,
-                                   plan, (hipStream_t)stream));
+  return hip_status(sa::launch_fwd(*dims, to_args(cache), q, q_seq, sel, sel_ld, n_sel, sel_bias, n_q, scale, out,
+                                   scratch, plan, (hipStream_t)stream));
+}
+
+int sparse_attn_fwd(const sa_dims* dims, const sa_cache* cache, const void* q, const int32_t* q_seq,
+                    const int32_t* sel, int64_t sel_ld, const int32_t* n_sel, int32_t n_q, float scale, float* out,
+                    void* ws, size_t ws_bytes, void* stream) {
+  return fwd_common(dims, cache, q, q_seq, sel, sel_ld, n_sel, nullptr, n_q, scale, out, ws, ws_bytes, stream);
+}
+
+int sparse_attn_fwd_bias(const sa_dims* dims, const sa_cache* cache, const void* q, const int32_t* q_seq,
+                         const int32_t* sel, int64_t sel_ld, const int32_t* n_sel, const float* sel_bias,
+                         int32_t n_q, float scale, float* out, void* ws, size_t ws_bytes, void* stream) {
+  return fwd_common(dims, cache, q, q_seq, sel, sel_ld, n_sel, sel_bias, n_q, scale, out, ws, ws_bytes, stream);
+}
+
+int sparse_attn_mask_to_indices(const void* mask, int32_t mask_dtype, int64_t mask_ld, int32_t n_q, int32_t n_kv,
+                                int32_t* sel, int64_t sel_ld, int32_t* n_sel, float* sel_bias, void* stream) {
+  if (mask_dtype != SA_F16 && mask_dtype != SA_F32) return SA_ERR_ARG;
+  if (n_q < 0 || n_kv < 0 || sel_ld < 1 || mask_ld < n_kv) return SA_ERR_ARG;
+  if (n_q == 0) return SA_OK;
+  if ((n_kv > 0 && !mask) || !sel || !n_sel) return SA_ERR_NULL;
+  (void)hipGetLastError();
+  return hip_status(sa::launch_mask_to_indices(mask, mask_dtype, mask_ld, n_q, n_kv, sel, sel_ld, n_sel, sel_bias,
+                                               (hipStream_t)stream));
 }
 
 const char* sparse_attn_strerror(int code) {

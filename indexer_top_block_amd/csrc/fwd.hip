@@ -100,9 +100,9 @@ __global__ void __launch_bounds__(256, 1)
 fwd_mfma_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, int64_t k_hs,
                 const T* __restrict__ v, int64_t v_ld, int64_t v_hs, const int64_t* __restrict__ seq_row0,
                 const int32_t* __restrict__ seq_len, const int32_t* __restrict__ q_seq,
-                const int32_t* __restrict__ sel, int64_t sel_ld, const int32_t* __restrict__ n_sel, int h_q,
-                int h_kv, float scale_log2, int n_split, int rows_per_split, float* __restrict__ out,
-                float* __restrict__ ws_o, float* __restrict__ ws_ml) {
+                const int32_t* __restrict__ sel, int64_t sel_ld, const int32_t* __restrict__ n_sel,
+                const float* __restrict__ sel_bias, int h_q, int h_kv, float scale_log2, int n_split,
+                int rows_per_split, float* __restrict__ out, float* __restrict__ ws_o, float* __restrict__ ws_ml) {
   typedef typename vec8<T>::type V8;
   constexpr int RT = kMfmaTile;       // = 64: one list entry per lane
   constexpr int KST = DKQ / 32;       // QK^T MFMA steps
@@ -131,6 +131,7 @@ fwd_mfma_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, 
   const int i = blockIdx.y / h_kv, g = blockIdx.y % h_kv;
   const int G = h_q / h_kv;
   const int32_t* list = sel + (int64_t)i * sel_ld;
+  const float* blist = sel_bias ? sel_bias + (int64_t)i * sel_ld : nullptr;   // additive logit bias per entry
   const int r_begin = split * rows_per_split;
   // Every wave reads the list itself, lane l taking entry l of a tile.  Indices are
   // clamped into the row rather than guarded, so the loads issue back to back;
@@ -176,6 +177,7 @@ fwd_mfma_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, 
   struct TileRows {
     int64_t ko, vo;
     uint64_t valid;
+    float bias;                                      // lane l: the bias of entry l (0 without one)
   };
   const int64_t safe_k = qbase - kg, safe_v = qbase - vg;
   auto tile_rows = [&](int pos, int t) {
@@ -184,6 +186,7 @@ fwd_mfma_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, 
     tr.ko = row >= 0 ? row * k_ld : safe_k;
     tr.vo = ALIAS ? 0 : (row >= 0 ? row * v_ld : safe_v);
     tr.valid = __ballot(row >= 0);
+    tr.bias = blist ? blist[min(r_begin + t * RT + lane, lim)] : 0.f;
     return tr;
   };
   // Offset of chunk e's row: the chunks of one wave instruction span at most NR rows
@@ -240,7 +243,7 @@ fwd_mfma_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, 
 
   const int wr = wave * 16;                          // this wave's 16 rows of S
   const int dvb = wave * DVW;                        // this wave's output dims
-  auto compute = [&](uint64_t valid) {
+  auto compute = [&](uint64_t valid, float bias) {
     // S^T[row][head] for this wave's 16 rows, as two independent accumulation chains,
     // scaled to log2 units (-inf for rows not selected) and shared through LDS.
     {
@@ -255,7 +258,10 @@ fwd_mfma_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, 
       const f32x4 sacc = s0 + s1;
       f32x4 x;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) x[j] = ((valid >> (wr + 4 * grp + j)) & 1ull) ? sacc[j] * scale_log2 : -INFINITY;
+      for (int j = 0; j < 4; ++j) {
+        const float b = blist ? __shfl(bias, wr + 4 * grp + j) * kLog2e : 0.f;
+        x[j] = ((valid >> (wr + 4 * grp + j)) & 1ull) ? sacc[j] * scale_log2 + b : -INFINITY;
+      }
       *reinterpret_cast<f32x4*>(st + col * SP + wr + 4 * grp) = x;
     }
     __syncthreads();
@@ -312,8 +318,12 @@ fwd_mfma_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, 
   // the same on every path and the wait before landing a tile leaves the next
   // tile's loads outstanding; the last tile is landed by a step that issues nothing.
   uint64_t vq[PD];                                   // selected-row masks of tiles t .. t+PD-1
+  float bq[PD];                                      // and the lanes' entry biases
 #pragma unroll
-  for (int u = 0; u < PD; ++u) vq[u] = 0;
+  for (int u = 0; u < PD; ++u) {
+    vq[u] = 0;
+    bq[u] = 0.f;
+  }
   int rawA = PD == 2 ? pre2 : pre1;                  // list entries of tile t+PD
   int rawB = PD == 2 ? pre3 : pre2;                  // and of tile t+PD+1
   auto step = [&](int t, V8 (&kr)[KLD], V8 (&vr)[VLD], auto issue_next) {
@@ -323,16 +333,23 @@ fwd_mfma_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, 
       const int raw_new = list_at(t + PD + 2);       // before the gathers: waiting for it must not wait for them
       const TileRows rn = tile_rows(rawA, t + PD);
       issue(kr, vr, rn);
-      compute(vq[0]);
+      compute(vq[0], bq[0]);
 #pragma unroll
-      for (int u = 0; u + 1 < PD; ++u) vq[u] = vq[u + 1];
+      for (int u = 0; u + 1 < PD; ++u) {
+        vq[u] = vq[u + 1];
+        bq[u] = bq[u + 1];
+      }
       vq[PD - 1] = rn.valid;
+      bq[PD - 1] = rn.bias;
       rawA = rawB;
       rawB = raw_new;
     } else {
-      compute(vq[0]);
+      compute(vq[0], bq[0]);
 #pragma unroll
-      for (int u = 0; u + 1 < PD; ++u) vq[u] = vq[u + 1];
+      for (int u = 0; u + 1 < PD; ++u) {
+        vq[u] = vq[u + 1];
+        bq[u] = bq[u + 1];
+      }
     }
     __syncthreads();
   };
@@ -343,6 +360,8 @@ fwd_mfma_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, 
       const TileRows r0 = tile_rows(pre0, 0), r1 = tile_rows(pre1, 1);
       vq[0] = r0.valid;
       vq[1] = r1.valid;
+      bq[0] = r0.bias;
+      bq[1] = r1.bias;
       issue(kbuf[0], vbuf[0], r0);
       issue(kbuf[1], vbuf[1], r1);
       int t = 0;
@@ -354,6 +373,7 @@ fwd_mfma_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, 
     } else if (n_tiles == 1) {
       const TileRows r0 = tile_rows(pre0, 0);
       vq[0] = r0.valid;
+      bq[0] = r0.bias;
       issue(kbuf[0], vbuf[0], r0);
       step(0, kbuf[0], vbuf[0], final_t{});
     }
@@ -363,6 +383,7 @@ fwd_mfma_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, 
     if (n_tiles >= 1) {
       const TileRows r0 = tile_rows(pre0, 0);
       vq[0] = r0.valid;
+      bq[0] = r0.bias;
       issue(kbuf[0], vbuf[0], r0);
       for (int t = 0; t < n_tiles; ++t) {
         land(kbuf[0], vbuf[0]);
@@ -370,9 +391,10 @@ fwd_mfma_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, 
         const int raw_new = list_at(t + 3);
         const TileRows rn = tile_rows(rawA, t + 1);
         if (t + 1 < n_tiles) issue(kbuf[0], vbuf[0], rn);
-        compute(vq[0]);
+        compute(vq[0], bq[0]);
         __syncthreads();
         vq[0] = rn.valid;
+        bq[0] = rn.bias;
         rawA = rawB;
         rawB = raw_new;
       }
@@ -417,8 +439,9 @@ __global__ void __launch_bounds__(256, 2)
 fwd_lds_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, int64_t k_hs,
                const int64_t* __restrict__ seq_row0, const int32_t* __restrict__ seq_len,
                const int32_t* __restrict__ q_seq, const int32_t* __restrict__ sel, int64_t sel_ld,
-               const int32_t* __restrict__ n_sel, int h_q, int h_kv, float scale_log2, int n_split,
-               int rows_per_split, float* __restrict__ out, float* __restrict__ ws_o, float* __restrict__ ws_ml) {
+               const int32_t* __restrict__ n_sel, const float* __restrict__ sel_bias, int h_q, int h_kv,
+               float scale_log2, int n_split, int rows_per_split, float* __restrict__ out,
+               float* __restrict__ ws_o, float* __restrict__ ws_ml) {
   typedef typename vec8<T>::type V8;
   typedef __attribute__((address_space(3))) void lds_void;
   constexpr int DV = 512;
@@ -445,9 +468,11 @@ fwd_lds_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, i
   const int i = blockIdx.y / h_kv, g = blockIdx.y % h_kv;
   const int G = h_q / h_kv;
   const int32_t* list = sel + (int64_t)i * sel_ld;
+  const float* blist = sel_bias ? sel_bias + (int64_t)i * sel_ld : nullptr;   // additive logit bias per entry
   const int r_begin = split * rows_per_split;
   const int lim = (int)sel_ld - 1;
   auto list_at = [&](int t) { return list[min(r_begin + t * RT + lane, lim)]; };
+  auto bias_at = [&](int t) { return blist ? blist[min(r_begin + t * RT + lane, lim)] : 0.f; };
   const int pre0 = list_at(0), pre1 = list_at(1), pre2 = list_at(2);
   const SeqMeta sm = seq_meta(q_seq, seq_len, seq_row0, nullptr, i);
   const int L = sm.len;
@@ -509,7 +534,7 @@ fwd_lds_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, i
 
   const int wr = wave * 16;                          // this wave's 16 rows of S
   const int dvb = wave * DVW;                        // this wave's output dims
-  auto compute = [&](const T* kmain, const T* krem, uint64_t valid) {
+  auto compute = [&](const T* kmain, const T* krem, uint64_t valid, float bias) {
     {
       f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
       const int r = wr + col;
@@ -529,7 +554,10 @@ fwd_lds_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, i
       const f32x4 sacc = s0 + s1;
       f32x4 x;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) x[j] = ((valid >> (wr + 4 * grp + j)) & 1ull) ? sacc[j] * scale_log2 : -INFINITY;
+      for (int j = 0; j < 4; ++j) {
+        const float b = blist ? __shfl(bias, wr + 4 * grp + j) * kLog2e : 0.f;
+        x[j] = ((valid >> (wr + 4 * grp + j)) & 1ull) ? sacc[j] * scale_log2 + b : -INFINITY;
+      }
       *reinterpret_cast<f32x4*>(st + col * SP + wr + 4 * grp) = x;
     }
     lds_barrier();
@@ -581,6 +609,7 @@ fwd_lds_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, i
   // tiles ahead of the gathers.
   if (n_tiles > 0) {
     uint64_t v0, v1;
+    float b0 = bias_at(0);
     issue(kmain0, krem0, row_off(pre0, 0, &v0));
     int raw1 = pre1, raw2 = pre2;                    // list entries of tiles t+1 and t+2
     for (int t = 0; t < n_tiles; ++t) {
@@ -588,10 +617,12 @@ fwd_lds_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, i
       __syncthreads();                               // everyone's
       const int raw_new = list_at(t + 3);
       const int64_t ko1 = row_off(raw1, t + 1, &v1);
-      compute(kmain0, krem0, v0);
+      const float b1 = bias_at(t + 1);
+      compute(kmain0, krem0, v0, b0);
       __syncthreads();                               // the buffer is free
       if (t + 1 < n_tiles) issue(kmain0, krem0, ko1);
       v0 = v1;
+      b0 = b1;
       raw1 = raw2;
       raw2 = raw_new;
     }
@@ -624,10 +655,12 @@ __global__ void __launch_bounds__(256)
 fwd_valu_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, int64_t k_hs,
                 const T* __restrict__ v, int64_t v_ld, int64_t v_hs, const int64_t* __restrict__ seq_row0,
                 const int32_t* __restrict__ seq_len, const int32_t* __restrict__ q_seq,
-                const int32_t* __restrict__ sel, int64_t sel_ld, const int32_t* __restrict__ n_sel, int h_q,
-                int h_kv, int d_kq, int d_v, float scale_log2, int n_split, int rows_per_split,
-                float* __restrict__ out, float* __restrict__ ws_o, float* __restrict__ ws_ml) {
+                const int32_t* __restrict__ sel, int64_t sel_ld, const int32_t* __restrict__ n_sel,
+                const float* __restrict__ sel_bias, int h_q, int h_kv, int d_kq, int d_v, float scale_log2,
+                int n_split, int rows_per_split, float* __restrict__ out, float* __restrict__ ws_o,
+                float* __restrict__ ws_ml) {
   __shared__ int64_t rows[kRowTile];
+  __shared__ float rbias[kRowTile];                  // additive logit bias of each row (log2 units)
   __shared__ float p[16][kRowTile];
   __shared__ float m_s[16], l_s[16], a_s[16];
   const int tid = threadIdx.x;
@@ -641,6 +674,7 @@ fwd_valu_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, 
   const int r_begin = split * rows_per_split;
   const int r_end = min(cnt, r_begin + rows_per_split);
   const int32_t* list = sel + (int64_t)i * sel_ld;
+  const float* blist = sel_bias ? sel_bias + (int64_t)i * sel_ld : nullptr;
   const T* qg = q + ((int64_t)i * h_q + (int64_t)g * G) * d_kq;
   if (tid < 16) {
     m_s[tid] = -INFINITY;
@@ -652,7 +686,10 @@ fwd_valu_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, 
 
   for (int r0 = r_begin; r0 < r_end; r0 += kRowTile) {
     __syncthreads();
-    if (tid < kRowTile) rows[tid] = tile_row(r0 + tid < r_end ? list[r0 + tid] : -1, r0 + tid, r_end, L, row0);
+    if (tid < kRowTile) {
+      rows[tid] = tile_row(r0 + tid < r_end ? list[r0 + tid] : -1, r0 + tid, r_end, L, row0);
+      rbias[tid] = (blist && r0 + tid < r_end) ? blist[r0 + tid] * kLog2e : 0.f;
+    }
     __syncthreads();
     for (int e = tid; e < G * kRowTile; e += 256) {
       const int h = e / kRowTile, r = e % kRowTile;
@@ -663,7 +700,7 @@ fwd_valu_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, 
         const T* qr = qg + (int64_t)h * d_kq;
         float dot = 0.f;
         for (int d = 0; d < d_kq; ++d) dot += (float)qr[d] * (float)kr[d];
-        xv = dot * scale_log2;
+        xv = dot * scale_log2 + rbias[r];
       }
       p[h][r] = xv;
     }
@@ -819,49 +856,49 @@ bool fwd_uses_mfma(const sa_dims& d, const CacheArgs& c, const void* q) {
 
 template <typename T, int DKQ, int DV, bool ALIAS>
 static void launch_mfma_t(const sa_dims& d, const CacheArgs& c, const void* q, const int32_t* q_seq,
-                          const int32_t* sel, int64_t sel_ld, const int32_t* n_sel, int n_q, float scale_log2,
+                          const int32_t* sel, int64_t sel_ld, const int32_t* n_sel, const float* sel_bias, int n_q, float scale_log2,
                           float* out, float* ws_o, float* ws_ml, const FwdPlan& plan, hipStream_t stream) {
   dim3 grid(plan.n_split, n_q * d.h_kv);
   hipLaunchKernelGGL((fwd_mfma_kernel<T, DKQ, DV, ALIAS>), grid, dim3(256), 0, stream, (const T*)q, (const T*)c.k,
                      c.k_ld, c.k_hs, (const T*)c.v, c.v_ld, c.v_hs, c.seq_row0, c.seq_len, q_seq, sel, sel_ld, n_sel,
-                     d.h_q, d.h_kv, scale_log2, plan.n_split, plan.rows_per_split, out, ws_o, ws_ml);
+                     sel_bias, d.h_q, d.h_kv, scale_log2, plan.n_split, plan.rows_per_split, out, ws_o, ws_ml);
 }
 
 template <typename T, int DKQ>
 static void launch_lds_t(const sa_dims& d, const CacheArgs& c, const void* q, const int32_t* q_seq,
-                         const int32_t* sel, int64_t sel_ld, const int32_t* n_sel, int n_q, float scale_log2,
+                         const int32_t* sel, int64_t sel_ld, const int32_t* n_sel, const float* sel_bias, int n_q, float scale_log2,
                          float* out, float* ws_o, float* ws_ml, const FwdPlan& plan, hipStream_t stream) {
   dim3 grid(plan.n_split, n_q * d.h_kv);
   hipLaunchKernelGGL((fwd_lds_kernel<T, DKQ>), grid, dim3(256), 0, stream, (const T*)q, (const T*)c.k, c.k_ld,
-                     c.k_hs, c.seq_row0, c.seq_len, q_seq, sel, sel_ld, n_sel, d.h_q, d.h_kv, scale_log2,
+                     c.k_hs, c.seq_row0, c.seq_len, q_seq, sel, sel_ld, n_sel, sel_bias, d.h_q, d.h_kv, scale_log2,
                      plan.n_split, plan.rows_per_split, out, ws_o, ws_ml);
 }
 
 template <typename T>
 static void dispatch_mfma(const sa_dims& d, const CacheArgs& c, const void* q, const int32_t* q_seq,
-                          const int32_t* sel, int64_t sel_ld, const int32_t* n_sel, int n_q, float scale_log2,
+                          const int32_t* sel, int64_t sel_ld, const int32_t* n_sel, const float* sel_bias, int n_q, float scale_log2,
                           float* out, float* ws_o, float* ws_ml, const FwdPlan& plan, hipStream_t stream) {
   const bool alias = c.v == c.k && c.v_ld == c.k_ld && c.v_hs == c.k_hs;
   if (alias && d.d_v == 512 && (d.d_kq == 576 || d.d_kq == 512)) {   // MLA: gathers straight into LDS
-    if (d.d_kq == 576) launch_lds_t<T, 576>(d, c, q, q_seq, sel, sel_ld, n_sel, n_q, scale_log2, out, ws_o, ws_ml, plan, stream);
-    else launch_lds_t<T, 512>(d, c, q, q_seq, sel, sel_ld, n_sel, n_q, scale_log2, out, ws_o, ws_ml, plan, stream);
+    if (d.d_kq == 576) launch_lds_t<T, 576>(d, c, q, q_seq, sel, sel_ld, n_sel, sel_bias, n_q, scale_log2, out, ws_o, ws_ml, plan, stream);
+    else launch_lds_t<T, 512>(d, c, q, q_seq, sel, sel_ld, n_sel, sel_bias, n_q, scale_log2, out, ws_o, ws_ml, plan, stream);
     return;
   }
 #define SA_FWD_CASE(DKQ_, DV_)                                                                                  \
   if (d.d_kq == DKQ_ && d.d_v == DV_) {                                                                          \
-    if (alias) launch_mfma_t<T, DKQ_, DV_, true>(d, c, q, q_seq, sel, sel_ld, n_sel, n_q, scale_log2, out, ws_o, \
+    if (alias) launch_mfma_t<T, DKQ_, DV_, true>(d, c, q, q_seq, sel, sel_ld, n_sel, sel_bias, n_q, scale_log2, out, ws_o, \
                                                  ws_ml, plan, stream);                                           \
-    else launch_mfma_t<T, DKQ_, DV_, false>(d, c, q, q_seq, sel, sel_ld, n_sel, n_q, scale_log2, out, ws_o,      \
+    else launch_mfma_t<T, DKQ_, DV_, false>(d, c, q, q_seq, sel, sel_ld, n_sel, sel_bias, n_q, scale_log2, out, ws_o,      \
                                             ws_ml, plan, stream);                                                \
     return;                                                                                                      \
   }
   // (V aliasing K at DV 512 went to the LDS kernel above)
   if (d.d_kq == 576 && d.d_v == 512) {
-    launch_mfma_t<T, 576, 512, false>(d, c, q, q_seq, sel, sel_ld, n_sel, n_q, scale_log2, out, ws_o, ws_ml, plan, stream);
+    launch_mfma_t<T, 576, 512, false>(d, c, q, q_seq, sel, sel_ld, n_sel, sel_bias, n_q, scale_log2, out, ws_o, ws_ml, plan, stream);
     return;
   }
   if (d.d_kq == 512 && d.d_v == 512) {
-    launch_mfma_t<T, 512, 512, false>(d, c, q, q_seq, sel, sel_ld, n_sel, n_q, scale_log2, out, ws_o, ws_ml, plan, stream);
+    launch_mfma_t<T, 512, 512, false>(d, c, q, q_seq, sel, sel_ld, n_sel, sel_bias, n_q, scale_log2, out, ws_o, ws_ml, plan, stream);
     return;
   }
   SA_FWD_CASE(256, 256)
@@ -871,7 +908,7 @@ static void dispatch_mfma(const sa_dims& d, const CacheArgs& c, const void* q, c
 
 template <typename T>
 static void dispatch_valu(const sa_dims& d, const CacheArgs& c, const void* q, const int32_t* q_seq,
-                          const int32_t* sel, int64_t sel_ld, const int32_t* n_sel, int n_q, float scale_log2,
+                          const int32_t* sel, int64_t sel_ld, const int32_t* n_sel, const float* sel_bias, int n_q, float scale_log2,
                           float* out, float* ws_o, float* ws_ml, const FwdPlan& plan, hipStream_t stream) {
   dim3 grid(plan.n_split, n_q * d.h_kv);
   const int per = (d.h_q / d.h_kv) * d.d_v;
@@ -879,7 +916,7 @@ static void dispatch_valu(const sa_dims& d, const CacheArgs& c, const void* q, c
   if (per <= 256 * ACC_) {                                                                                        \
     hipLaunchKernelGGL((fwd_valu_kernel<T, ACC_>), grid, dim3(256), 0, stream, (const T*)q, (const T*)c.k, c.k_ld, \
                        c.k_hs, (const T*)c.v, c.v_ld, c.v_hs, c.seq_row0, c.seq_len, q_seq, sel, sel_ld, n_sel,    \
-                       d.h_q, d.h_kv, d.d_kq, d.d_v, scale_log2, plan.n_split, plan.rows_per_split, out, ws_o,     \
+                       sel_bias, d.h_q, d.h_kv, d.d_kq, d.d_v, scale_log2, plan.n_split, plan.rows_per_split, out, ws_o,     \
                        ws_ml);                                                                                    \
     return;                                                                                                       \
   }
@@ -890,20 +927,20 @@ static void dispatch_valu(const sa_dims& d, const CacheArgs& c, const void* q, c
 }
 
 hipError_t launch_fwd(const sa_dims& d, const CacheArgs& c, const void* q, const int32_t* q_seq, const int32_t* sel,
-                      int64_t sel_ld, const int32_t* n_sel, int n_q, float scale, float* out, void* ws,
-                      const FwdPlan& plan, hipStream_t stream) {
+                      int64_t sel_ld, const int32_t* n_sel, const float* sel_bias, int n_q, float scale, float* out,
+                      void* ws, const FwdPlan& plan, hipStream_t stream) {
   if (n_q == 0) return hipSuccess;
   const float scale_log2 = scale * kLog2e;
   float* ws_o = (float*)ws;
   float* ws_ml = plan.n_split > 1 ? ws_o + (size_t)n_q * d.h_q * plan.n_split * d.d_v : nullptr;
   if (fwd_uses_mfma(d, c, q)) {
-    if (d.dtype == SA_BF16) dispatch_mfma<bf16>(d, c, q, q_seq, sel, sel_ld, n_sel, n_q, scale_log2, out, ws_o, ws_ml, plan, stream);
-    else dispatch_mfma<f16>(d, c, q, q_seq, sel, sel_ld, n_sel, n_q, scale_log2, out, ws_o, ws_ml, plan, stream);
+    if (d.dtype == SA_BF16) dispatch_mfma<bf16>(d, c, q, q_seq, sel, sel_ld, n_sel, sel_bias, n_q, scale_log2, out, ws_o, ws_ml, plan, stream);
+    else dispatch_mfma<f16>(d, c, q, q_seq, sel, sel_ld, n_sel, sel_bias, n_q, scale_log2, out, ws_o, ws_ml, plan, stream);
   } else {
     switch (d.dtype) {
-      case SA_F32: dispatch_valu<float>(d, c, q, q_seq, sel, sel_ld, n_sel, n_q, scale_log2, out, ws_o, ws_ml, plan, stream); break;
-      case SA_F16: dispatch_valu<f16>(d, c, q, q_seq, sel, sel_ld, n_sel, n_q, scale_log2, out, ws_o, ws_ml, plan, stream); break;
-      default: dispatch_valu<bf16>(d, c, q, q_seq, sel, sel_ld, n_sel, n_q, scale_log2, out, ws_o, ws_ml, plan, stream); break;
+      case SA_F32: dispatch_valu<float>(d, c, q, q_seq, sel, sel_ld, n_sel, sel_bias, n_q, scale_log2, out, ws_o, ws_ml, plan, stream); break;
+      case SA_F16: dispatch_valu<f16>(d, c, q, q_seq, sel, sel_ld, n_sel, sel_bias, n_q, scale_log2, out, ws_o, ws_ml, plan, stream); break;
+      default: dispatch_valu<bf16>(d, c, q, q_seq, sel, sel_ld, n_sel, sel_bias, n_q, scale_log2, out, ws_o, ws_ml, plan, stream); break;
     }
   }
   hipError_t err = hipGetLastError();

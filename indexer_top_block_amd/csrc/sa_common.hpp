@@ -58,6 +58,27 @@ __device__ __forceinline__ int wave_inclusive_scan(int x, int /*lane*/) {
   return x;
 }
 
+// Exclusive prefix sum of one int per thread over the workgroup; returns the
+// exclusive value and writes the total to *total.  `scratch` holds >= BLOCK/64 ints.
+template <int BLOCK>
+__device__ __forceinline__ int block_exclusive_scan(int x, int* scratch, int* total) {
+  constexpr int W = BLOCK / kWave;
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int inc = wave_inclusive_scan(x, lane);
+  __syncthreads();
+  if (lane == kWave - 1) scratch[wave] = inc;
+  __syncthreads();
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < W; ++w) {
+    const int v = scratch[w];
+    base += (w < wave) ? v : 0;
+    tot += v;
+  }
+  *total = tot;
+  return base + inc - x;
+}
+
 // 2^x with the hardware exponential (v_exp_f32); exp2(-inf) = 0.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

@@ -65,27 +65,6 @@ __device__ __forceinline__ uint32_t key_clamped(const float* __restrict__ row, i
   return order_key(row[idx < last ? idx : last]);
 }
 
-// Exclusive prefix sum of one int per thread over the workgroup; returns the
-// exclusive value and writes the total to *total.  `scratch` holds >= BLOCK/64 ints.
-template <int BLOCK>
-__device__ __forceinline__ int block_exclusive_scan(int x, int* scratch, int* total) {
-  constexpr int W = BLOCK / kWave;
-  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  const int inc = wave_inclusive_scan(x, lane);
-  __syncthreads();
-  if (lane == kWave - 1) scratch[wave] = inc;
-  __syncthreads();
-  int base = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < W; ++w) {
-    const int v = scratch[w];
-    base += (w < wave) ? v : 0;
-    tot += v;
-  }
-  *total = tot;
-  return base + inc - x;
-}
-
 // Positions of the dense case (every block fits): 0 .. n_vis-1, then -1.
 template <int BLOCK>
 __device__ __forceinline__ void write_dense(int32_t* out, int64_t sel_ld, int n_vis, int32_t* n_sel_out) {

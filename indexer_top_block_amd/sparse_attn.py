@@ -32,6 +32,8 @@ EXPORTS = (
     "sparse_attn_score",
     "sparse_attn_select",
     "sparse_attn_fwd",
+    "sparse_attn_mask_to_indices",
+    "sparse_attn_fwd_bias",
     "sparse_attn_strerror",
     "sparse_attn_version",
 )
@@ -85,6 +87,10 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.sparse_attn_select.restype = ctypes.c_int
     lib.sparse_attn_fwd.argtypes = [dp, cp, P, P, P, I64, P, I32, ctypes.c_float, P, P, SZ, P]
     lib.sparse_attn_fwd.restype = ctypes.c_int
+    lib.sparse_attn_mask_to_indices.argtypes = [P, I32, I64, I32, I32, P, I64, P, P, P]
+    lib.sparse_attn_mask_to_indices.restype = ctypes.c_int
+    lib.sparse_attn_fwd_bias.argtypes = [dp, cp, P, P, P, I64, P, P, I32, ctypes.c_float, P, P, SZ, P]
+    lib.sparse_attn_fwd_bias.restype = ctypes.c_int
     lib.sparse_attn_strerror.argtypes = [ctypes.c_int]
     lib.sparse_attn_strerror.restype = ctypes.c_char_p
     lib.sparse_attn_version.argtypes = []
@@ -168,6 +174,22 @@ def sparse_attn_fwd(dims: SaDims, cache: Cache, q, q_seq, sel, sel_ld: int, n_se
                                                      _ptr(q_seq), _ptr(sel), int(sel_ld), _ptr(n_sel), int(n_q),
                                                      float(scale), _ptr(out), _ptr(ws), int(ws_bytes),
                                                      _stream(stream)))
+
+
+def sparse_attn_mask_to_indices(mask, mask_dtype, mask_ld: int, n_q: int, n_kv: int, sel, sel_ld: int, n_sel,
+                                sel_bias=None, stream=None) -> None:
+    code = DTYPE_CODE[mask_dtype] if isinstance(mask_dtype, str) else int(mask_dtype)
+    _check("sparse_attn_mask_to_indices",
+           load().sparse_attn_mask_to_indices(_ptr(mask), code, int(mask_ld), int(n_q), int(n_kv), _ptr(sel),
+                                              int(sel_ld), _ptr(n_sel), _ptr(sel_bias), _stream(stream)))
+
+
+def sparse_attn_fwd_bias(dims: SaDims, cache: Cache, q, q_seq, sel, sel_ld: int, n_sel, sel_bias, n_q: int,
+                         scale: float, out, ws=None, ws_bytes: int = 0, stream=None) -> None:
+    _check("sparse_attn_fwd_bias",
+           load().sparse_attn_fwd_bias(ctypes.byref(dims), ctypes.byref(cache.struct), _ptr(q), _ptr(q_seq),
+                                       _ptr(sel), int(sel_ld), _ptr(n_sel), _ptr(sel_bias), int(n_q), float(scale),
+                                       _ptr(out), _ptr(ws), int(ws_bytes), _stream(stream)))
 
 
 def sparse_attn_strerror(code: int) -> str:

@@ -280,6 +280,77 @@ def test_workspace_state_returns_to_zero(gpu_lib):
     assert not layer.ws[: sa.WS_STATE_BYTES].cpu().numpy().any()
 
 
+# ------------------------------------------------------------ additive-mask form
+
+def run_mask_form(case, mask, mask_dtype="f16"):
+    """mask -> index lists -> biased attention on the GPU, against the oracle's
+    finite positions (exact) and its attention with the mask values as bias."""
+    layer = DeviceLayer(case)
+    n_q, n_kv = mask.shape
+    dev_mask = torch.from_numpy(mask).to(sa.TORCH_DTYPE[mask_dtype]).cuda()
+    sel_bias = torch.full((n_q, layer.sel_ld), 7.0, dtype=torch.float32, device="cuda")
+    sa.sparse_attn_mask_to_indices(dev_mask, mask_dtype, n_kv, n_q, n_kv, layer.sel, layer.sel_ld, layer.n_sel,
+                                   sel_bias)
+    sa.sparse_attn_fwd_bias(layer.dims, layer.cache, layer.q, layer.q_seq, layer.sel, layer.sel_ld, layer.n_sel,
+                            sel_bias, n_q, case.scale, layer.out, layer.ws, layer.ws_bytes)
+    torch.cuda.synchronize()
+    sel = layer.sel.cpu().numpy()
+    n_sel = layer.n_sel.cpu().numpy()
+    bias = sel_bias.cpu().numpy()
+    out = layer.out.cpu().numpy()
+    worst = 0.0
+    for qi in range(n_q):
+        pos = oracle.mask_positions(mask[qi])
+        assert n_sel[qi] == len(pos), f"row {qi}: count {n_sel[qi]} != {len(pos)}"
+        m = min(len(pos), layer.sel_ld)
+        assert np.array_equal(sel[qi, :m], pos[:m]) and (sel[qi, m:] == -1).all(), f"row {qi}: list differs"
+        assert np.array_equal(bias[qi, :m], mask[qi, pos[:m]].astype(np.float32)) and (bias[qi, m:] == 0).all()
+        rows = int(case.row0[case.q_seq[qi]]) + pos[:m]
+        want = oracle.attend(case.q[qi], case.k[rows], case.v_rows()[rows], case.scale, bias=mask[qi, pos[:m]])
+        worst = max(worst, parity.check_out(out[qi], want, case.dims.dtype, f"{case.name} row {qi}"))
+    say(f"[parity] {case.name}: mask form ok  max-abs={worst:.3g}")
+    return layer
+
+
+def test_mask_form_pages_shapes(gpu_lib):
+    # the pages' sparse-FA test shapes and mask pattern: each row's finite entries
+    # (1 on every 32nd row, otherwise n_kv_max - row mod 17) with values -k/32
+    facts = json.load(open(os.path.join(GOLDEN, "qsa_page_facts.json")))
+    pat = facts["sparse_mask_pattern"]
+    n_kv, n_q = 4096, 40
+    for j, sh in enumerate(facts["sparse_fa_test_shapes"]["cases"]):
+        d = dims(h_q=sh["heads_per_kv"], d_kq=sh["d_kq"], d_v=sh["d_v"], h_idx=32, compress_ratio=1,
+                 top_k=sh["n_kv_max"], dtype="f16")
+        case = datagen.make_case(f"mask_form_{j}", d, [n_kv], [0] * n_q, [n_kv - 1] * n_q, seed=0, case_id=300 + j,
+                                 std="inv_sqrt_dim", v_separate=sh["d_kq"] != 576)
+        mask = datagen.sparse_mask(n_q, n_kv, sh["n_kv_max"], seed=0, case_id=300 + j,
+                                   count_spread=pat["count_spread"], single_entry_stride=pat["single_entry_stride"])
+        run_mask_form(case, mask)
+
+
+def test_mask_form_edges(gpu_lib):
+    # fp32 masks; a row with more finite entries than the list holds (cut to its first
+    # positions, the true count reported); +inf and NaN excluded; an empty row; a
+    # long row streamed in several chunks; fp32 caches on the generic kernel
+    for dt, d in (("bf16", dims(h_q=16, d_kq=576, d_v=512, h_idx=32, compress_ratio=1, top_k=300)),
+                  ("f32", dims(h_q=8, d_kq=64, d_v=48, h_idx=4, d_idx=64, compress_ratio=1, top_k=300, dtype="f32"))):
+        n_kv, n_q = 9000, 5
+        case = datagen.make_case(f"mask_edges_{dt}", d, [n_kv], [0] * n_q, [n_kv - 1] * n_q, seed=0, case_id=310,
+                                 std="inv_sqrt_dim", v_separate=dt == "f32")
+        rng = np.random.default_rng(311)
+        mask = np.full((n_q, n_kv), -np.inf, dtype=np.float32)
+        mask[0, rng.choice(n_kv, 1000, replace=False)] = rng.uniform(-2, 1, 1000)     # more than the list holds
+        pos = rng.choice(n_kv, 200, replace=False)
+        mask[1, pos] = rng.uniform(-1, 0, 200)
+        mask[1, pos[:7]] = np.inf
+        mask[1, pos[7:11]] = np.nan
+        # row 2 empty
+        mask[3, -3:] = 0.25                                                            # the last columns only
+        mask[4, ::37] = -0.5
+        layer = run_mask_form(case, mask, "f32")
+        assert layer.n_sel.cpu().numpy()[0] == 1000 and not layer.out[2].abs().max().item()
+
+
 # ----------------------------------------------------------- full-size workloads
 
 @pytest.mark.parametrize("cfg,queries", [

@@ -145,3 +145,28 @@ def test_entry_points_reject_bad_arguments_before_any_launch():
                  ctypes.c_float(0.04), FAKE, FAKE, 1 << 30, None) == sa.SA_ERR_ARG
     assert _call("sparse_attn_fwd", d, c, FAKE, FAKE, FAKE, 2051, FAKE, 0, ctypes.c_float(0.04), FAKE, None, 0,
                  None) == sa.SA_OK  # no queries: nothing to do
+
+
+def test_mask_form_entry_points_reject_bad_arguments():
+    F16 = sa.SA_F16
+    # bad dtype, negative sizes, too-short rows or lists
+    assert _call("sparse_attn_mask_to_indices", FAKE, 7, 4096, 1, 4096, FAKE, 512, FAKE, None, None) == sa.SA_ERR_ARG
+    assert _call("sparse_attn_mask_to_indices", FAKE, F16, 4096, -1, 4096, FAKE, 512, FAKE, None, None) == sa.SA_ERR_ARG
+    assert _call("sparse_attn_mask_to_indices", FAKE, F16, 4095, 1, 4096, FAKE, 512, FAKE, None, None) == sa.SA_ERR_ARG
+    assert _call("sparse_attn_mask_to_indices", FAKE, F16, 4096, 1, 4096, FAKE, 0, FAKE, None, None) == sa.SA_ERR_ARG
+    # required pointers
+    assert _call("sparse_attn_mask_to_indices", None, F16, 4096, 1, 4096, FAKE, 512, FAKE, None, None) == sa.SA_ERR_NULL
+    assert _call("sparse_attn_mask_to_indices", FAKE, F16, 4096, 1, 4096, None, 512, FAKE, None, None) == sa.SA_ERR_NULL
+    assert _call("sparse_attn_mask_to_indices", FAKE, F16, 4096, 1, 4096, FAKE, 512, None, None, None) == sa.SA_ERR_NULL
+    # nothing to do
+    assert _call("sparse_attn_mask_to_indices", None, F16, 4096, 0, 4096, None, 512, None, None, None) == sa.SA_OK
+    # the biased attention validates like the plain one
+    d = ctypes.byref(_dims())
+    c = ctypes.byref(_cache())
+    ws = sa.sparse_attn_workspace_bytes(_dims(), 1, 4096)
+    assert _call("sparse_attn_fwd_bias", d, c, FAKE, FAKE, FAKE, 2051, FAKE, FAKE, 1, ctypes.c_float(0.04), FAKE, None,
+                 0, None) == sa.SA_ERR_WORKSPACE
+    assert _call("sparse_attn_fwd_bias", d, c, None, FAKE, FAKE, 2051, FAKE, FAKE, 1, ctypes.c_float(0.04), FAKE,
+                 FAKE, ws, None) == sa.SA_ERR_NULL
+    assert _call("sparse_attn_fwd_bias", d, c, FAKE, FAKE, FAKE, 2051, FAKE, None, 0, ctypes.c_float(0.04), FAKE,
+                 None, 0, None) == sa.SA_OK
