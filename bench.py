@@ -290,6 +290,38 @@ def prefill_report(steps: int) -> dict:
     }
 
 
+# ------------------------------------------------------------------ mask form
+
+def mask_form_report(lay: "RotatingLayers", steps: int, warmup: int) -> dict:
+    """The additive-mask form on the 128K decode layer: one f16 mask row of 131072
+    columns whose finite entries are the step's 2051 selected positions (values -k/32)
+    -> index list -> attention with the mask values as bias, per step."""
+    R = lay.n
+    lay.step(0)
+    torch.cuda.synchronize()
+    n_kv = lay.max_len
+    pos = lay.sel[0, : int(lay.n_sel[0].item())].cpu().numpy()
+    mask = np.full((1, n_kv), -np.inf, dtype=np.float32)
+    mask[0, pos] = -(1.0 + np.arange(len(pos)) % 7) / 32.0
+    dev_mask = torch.from_numpy(mask).to(torch.float16).cuda()
+    sel_bias = torch.zeros((1, lay.sel_ld), dtype=torch.float32, device="cuda")
+
+    def m2i(k):
+        sa.sparse_attn_mask_to_indices(dev_mask, "f16", n_kv, 1, n_kv, lay.sel, lay.sel_ld, lay.n_sel, sel_bias)
+
+    def fwd_b(k):
+        sa.sparse_attn_fwd_bias(lay.dims, lay.caches[k % R], lay.q, lay.q_seq, lay.sel, lay.sel_ld, lay.n_sel,
+                                sel_bias, 1, lay.case.scale, lay.out, lay.ws, lay.ws_bytes)
+
+    both = time_graph(lambda k: (m2i(k), fwd_b(k)), steps, warmup)
+    t_m2i = time_graph(m2i, steps, warmup)
+    t_fwd = time_graph(fwd_b, steps, warmup)
+    return {"workload": "one 131072-column f16 mask row over the 128K decode layer, 2051 finite entries",
+            "us_per_step": round(both * 1e3, 3),
+            "kernel_avg_us": {"mask_to_indices": round(t_m2i * 1e3, 3), "fwd_bias": round(t_fwd * 1e3, 3)},
+            "mask_bytes": n_kv * 2}
+
+
 # ------------------------------------------------------------------ token-level
 
 def token_level_report(steps: int, warmup: int, layers: int) -> dict:
@@ -407,6 +439,8 @@ def main() -> int:
     if not args.no_prefill:
         log("[bench] prefill workload")
         rec["prefill"] = prefill_report(max(5, min(args.steps, 20)))
+    log("[bench] mask form")
+    rec["mask_form"] = mask_form_report(lay, args.steps, args.warmup)
     if not args.no_token_level:
         del lay
         torch.cuda.empty_cache()
