@@ -8,6 +8,7 @@ from .sparse_attn_oracle import (  # noqa: F401
     attend,
     block_scores,
     mask_positions,
+    merge_partials,
     pool_blocks,
     round_to_storage,
     run_case,
@@ -16,4 +17,5 @@ from .sparse_attn_oracle import (  # noqa: F401
     select_positions,
     select_positions_token_expanded,
     visible_tokens,
+    window_union,
 )

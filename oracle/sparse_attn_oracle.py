@@ -189,6 +189,29 @@ def mask_positions(mask_row: np.ndarray) -> np.ndarray:
     return np.flatnonzero(np.isfinite(m)).astype(np.int64)
 
 
+# ------------------------------------------------------------- dense window form
+
+def window_union(selected: np.ndarray, n_vis: int, window: int) -> np.ndarray:
+    """The selected positions together with the ``window`` most recent visible ones,
+    ascending and each once.  A dense attention over the contiguous block of recent
+    keys, a sparse one over the selected keys, and a merge of the two is the
+    optimisation the pages report from a Vulkan fork ("CUDA + ggml: add sparse-fa for
+    DSV4/GLM", review thread); reading: the contiguous block is the most recent
+    ``window`` visible positions, and the result is attention over the union."""
+    w0 = max(0, n_vis - max(window, 0))
+    return np.union1d(np.asarray(selected, dtype=np.int64), np.arange(w0, n_vis, dtype=np.int64))
+
+
+def merge_partials(parts) -> np.ndarray:
+    """Exact merge of attention results over disjoint row sets: ``parts`` holds
+    (out, m, l) per set, out the normalised [H, DV] result, m and l the per-head max
+    logit and the sum of exp(logit - m)."""
+    M = np.max([p[1] for p in parts], axis=0)
+    num = sum(p[0] * (p[2] * np.exp(p[1] - M))[:, None] for p in parts)
+    den = sum(p[2] * np.exp(p[1] - M) for p in parts)
+    return num / den[:, None]
+
+
 # ----------------------------------------------------------------------- pipeline
 
 class SequencePools:

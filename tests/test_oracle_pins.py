@@ -330,6 +330,43 @@ def test_attend_bias_closed_forms():
     assert np.allclose(oracle.attend(q, k, v, 0.5, bias=dom), np.tile(v[6, 0], (4, 1)), rtol=1e-13)
 
 
+# ------------------------------------------------------------- dense window form
+
+def _stats(q, k, v, scale):
+    """(out, m, l) of one row set: the normalised output, per-head max logit and sum."""
+    logits = scale * np.einsum("nd,hd->hn", k[:, 0], q)
+    m = logits.max(axis=1)
+    l = np.exp(logits - m[:, None]).sum(axis=1)
+    return oracle.attend(q, k, v, scale), m, l
+
+
+def test_window_union_definition_and_limits():
+    sel = np.array([0, 1, 2, 3, 40, 41, 42, 43, 96, 97, 98, 99])
+    assert np.array_equal(oracle.window_union(sel, 100, 0), sel)                 # no window: the selection
+    assert np.array_equal(oracle.window_union(sel, 100, 10),
+                          np.concatenate([sel[:8], np.arange(90, 100)]))          # overlap counted once
+    assert np.array_equal(oracle.window_union(sel, 100, 500), np.arange(100))    # window past the start: dense
+    assert np.array_equal(oracle.window_union(np.array([], np.int64), 5, 3), np.arange(2, 5))
+
+
+def test_window_union_attention_is_the_merge_of_window_and_sparse_parts():
+    # the dense-window + sparse + combine form computes attention over the union
+    rng = np.random.default_rng(23)
+    n, h_q, d = 300, 8, 32
+    q = rng.standard_normal((h_q, d))
+    k = rng.standard_normal((n, 1, d))
+    v = rng.standard_normal((n, 1, 24))
+    sel = np.sort(rng.choice(n, 60, replace=False))
+    u = oracle.window_union(sel, n, 50)
+    win = np.arange(n - 50, n)
+    rest = np.setdiff1d(sel, win)
+    parts = [_stats(q, k[win], v[win], 0.2), _stats(q, k[rest], v[rest], 0.2)]
+    assert np.allclose(oracle.merge_partials(parts), oracle.attend(q, k[u], v[u], 0.2), rtol=1e-12, atol=1e-12)
+    # counting the overlap twice is a different (wrong) answer
+    dup = np.concatenate([sel, win])
+    assert not np.allclose(oracle.attend(q, k[dup], v[dup], 0.2), oracle.attend(q, k[u], v[u], 0.2))
+
+
 # ------------------------------------------------------------------ pipeline
 
 def _small_dims(**kw):
