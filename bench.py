@@ -322,6 +322,30 @@ def mask_form_report(lay: "RotatingLayers", steps: int, warmup: int) -> dict:
             "mask_bytes": n_kv * 2}
 
 
+# ------------------------------------------------------------------ dense window
+
+def window_report(lay: "RotatingLayers", steps: int, warmup: int, window: int = 128) -> dict:
+    """The decode step with the attention taken over the selected rows together with
+    the `window` most recent positions (dense window + selection, merged in one pass;
+    the window size is not fixed by the method's description, 128 is an example)."""
+    R = lay.n
+
+    def fwd_w(k):
+        sa.sparse_attn_fwd_window(lay.dims, lay.caches[k % R], lay.q, lay.q_seq, lay.q_pos, lay.sel, lay.sel_ld,
+                                  lay.n_sel, window, lay.n_q, lay.case.scale, lay.out, lay.ws, lay.ws_bytes)
+
+    def step_w(k):
+        lay.pool(k % R)
+        lay.score(k % R)
+        lay.select(k % R)
+        fwd_w(k)
+
+    ms = time_graph(step_w, steps, warmup)
+    t_fwd = time_graph(fwd_w, steps, warmup)
+    return {"workload": f"the 128K decode step with a dense window of the {window} most recent positions",
+            "window": window, "us_per_step": round(ms * 1e3, 3), "kernel_avg_us": {"fwd_window": round(t_fwd * 1e3, 3)}}
+
+
 # ------------------------------------------------------------------ token-level
 
 def token_level_report(steps: int, warmup: int, layers: int) -> dict:
@@ -441,6 +465,8 @@ def main() -> int:
         rec["prefill"] = prefill_report(max(5, min(args.steps, 20)))
     log("[bench] mask form")
     rec["mask_form"] = mask_form_report(lay, args.steps, args.warmup)
+    log("[bench] dense window + selection")
+    rec["window"] = window_report(lay, args.steps, args.warmup)
     if not args.no_token_level:
         del lay
         torch.cuda.empty_cache()

@@ -212,6 +212,21 @@ int sparse_attn_fwd_bias(const sa_dims* dims, const sa_cache* cache, const void*
                          const float* sel_bias, int32_t n_q, float scale, float* out, void* ws,
                          size_t ws_bytes, void* stream);
 
+/* sparse_attn_fwd over the selected rows together with a dense window: the
+ * `window` most recent visible positions of each query token (t in [n_vis - window,
+ * n_vis), n_vis = min(seq_len[s], q_pos[i] + 1)), each position once -- list
+ * entries inside the window are covered by it (pages: PR #27970 review thread, the
+ * dense attention over the contiguous recent keys plus sparse attention over the
+ * selected keys, merged; reading: the contiguous block is the most recent window).
+ * The window rows are contiguous and need no list.  q_pos: device [n_q] int32,
+ * required when window > 0.  window = 0 gives sparse_attn_fwd.  The workspace is
+ * that of sparse_attn_fwd (sparse_attn_workspace_bytes).
+ * Errors: those of sparse_attn_fwd; SA_ERR_ARG for window < 0 or > 2^24.            */
+int sparse_attn_fwd_window(const sa_dims* dims, const sa_cache* cache, const void* q,
+                           const int32_t* q_seq, const int32_t* q_pos, const int32_t* sel, int64_t sel_ld,
+                           const int32_t* n_sel, int32_t window, int32_t n_q, float scale, float* out,
+                           void* ws, size_t ws_bytes, void* stream);
+
 /* Static description of an error code (never NULL). */
 const char* sparse_attn_strerror(int code);
 

@@ -119,8 +119,9 @@ int sparse_attn_select(const sa_dims* dims, const sa_cache* cache, const float* 
 }
 
 static int fwd_common(const sa_dims* dims, const sa_cache* cache, const void* q, const int32_t* q_seq,
-                      const int32_t* sel, int64_t sel_ld, const int32_t* n_sel, const float* sel_bias, int32_t n_q,
-                      float scale, float* out, void* ws, size_t ws_bytes, void* stream) {
+                      const int32_t* sel, int64_t sel_ld, const int32_t* n_sel, const float* sel_bias,
+                      const int32_t* q_pos, int32_t window, int32_t n_q, float scale, float* out, void* ws,
+                      size_t ws_bytes, void* stream) {
   int rc = check_dims(dims);
   if (rc) return rc;
   if ((rc = check_cache_common(dims, cache))) return rc;
@@ -135,27 +136,39 @@ static int fwd_common(const sa_dims* dims, const sa_cache* cache, const void* q,
   if (alias && dims->d_v > dims->d_kq) return SA_ERR_ARG;
   if (cache->v_ld < (int64_t)(dims->h_kv - 1) * cache->v_head_stride + dims->d_v) return SA_ERR_ARG;
   if (!(scale == scale)) return SA_ERR_ARG;  // NaN
-  const sa::FwdPlan plan = sa::plan_fwd(*dims, n_q);
+  if (window < 0 || window > (1 << 24)) return SA_ERR_ARG;
+  if (window > 0 && !q_pos) return SA_ERR_NULL;
+  const sa::FwdPlan plan = sa::plan_fwd_window(*dims, n_q, window);
   void* scratch = nullptr;
   if (plan.ws_bytes > 0) {
     if (!ws || ws_bytes < SA_WS_STATE_BYTES + plan.ws_bytes) return SA_ERR_WORKSPACE;
     scratch = (char*)ws + SA_WS_STATE_BYTES;
   }
   (void)hipGetLastError();
-  return hip_status(sa::launch_fwd(*dims, to_args(cache), q, q_seq, sel, sel_ld, n_sel, sel_bias, n_q, scale, out,
-                                   scratch, plan, (hipStream_t)stream));
+  return hip_status(sa::launch_fwd(*dims, to_args(cache), q, q_seq, sel, sel_ld, n_sel, sel_bias, q_pos, window,
+                                   n_q, scale, out, scratch, plan, (hipStream_t)stream));
 }
 
 int sparse_attn_fwd(const sa_dims* dims, const sa_cache* cache, const void* q, const int32_t* q_seq,
                     const int32_t* sel, int64_t sel_ld, const int32_t* n_sel, int32_t n_q, float scale, float* out,
                     void* ws, size_t ws_bytes, void* stream) {
-  return fwd_common(dims, cache, q, q_seq, sel, sel_ld, n_sel, nullptr, n_q, scale, out, ws, ws_bytes, stream);
+  return fwd_common(dims, cache, q, q_seq, sel, sel_ld, n_sel, nullptr, nullptr, 0, n_q, scale, out, ws, ws_bytes,
+                    stream);
+}
+
+int sparse_attn_fwd_window(const sa_dims* dims, const sa_cache* cache, const void* q, const int32_t* q_seq,
+                           const int32_t* q_pos, const int32_t* sel, int64_t sel_ld, const int32_t* n_sel,
+                           int32_t window, int32_t n_q, float scale, float* out, void* ws, size_t ws_bytes,
+                           void* stream) {
+  return fwd_common(dims, cache, q, q_seq, sel, sel_ld, n_sel, nullptr, q_pos, window, n_q, scale, out, ws,
+                    ws_bytes, stream);
 }
 
 int sparse_attn_fwd_bias(const sa_dims* dims, const sa_cache* cache, const void* q, const int32_t* q_seq,
                          const int32_t* sel, int64_t sel_ld, const int32_t* n_sel, const float* sel_bias,
                          int32_t n_q, float scale, float* out, void* ws, size_t ws_bytes, void* stream) {
-  return fwd_common(dims, cache, q, q_seq, sel, sel_ld, n_sel, sel_bias, n_q, scale, out, ws, ws_bytes, stream);
+  return fwd_common(dims, cache, q, q_seq, sel, sel_ld, n_sel, sel_bias, nullptr, 0, n_q, scale, out, ws, ws_bytes,
+                    stream);
 }
 
 int sparse_attn_mask_to_indices(const void* mask, int32_t mask_dtype, int64_t mask_ld, int32_t n_q, int32_t n_kv,

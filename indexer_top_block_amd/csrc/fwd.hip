@@ -41,6 +41,14 @@ __device__ __forceinline__ int64_t tile_row(int pos, int j, int r_end, int seq_l
   return (j < r_end && pos >= 0 && pos < seq_len) ? row0 + pos : -1;
 }
 
+// Position of row j of a query's attended rows: the list entries first (an entry
+// inside the dense window is dropped there, the window covers it), then the window's
+// wlen positions w0 .. w0 + wlen - 1.  Without a window (wlen 0) it is the entry.
+__device__ __forceinline__ int row_pos(int entry, int j, int cnt, int w0, int wlen) {
+  if (j < cnt) return (wlen > 0 && entry >= w0) ? -1 : entry;
+  return w0 + (j - cnt);
+}
+
 template <typename T>
 __device__ __forceinline__ f32x4 mfma16x16x32(const typename vec8<T>::type& a, const typename vec8<T>::type& b,
                                               const f32x4& c);
@@ -101,8 +109,9 @@ fwd_mfma_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, 
                 const T* __restrict__ v, int64_t v_ld, int64_t v_hs, const int64_t* __restrict__ seq_row0,
                 const int32_t* __restrict__ seq_len, const int32_t* __restrict__ q_seq,
                 const int32_t* __restrict__ sel, int64_t sel_ld, const int32_t* __restrict__ n_sel,
-                const float* __restrict__ sel_bias, int h_q, int h_kv, float scale_log2, int n_split,
-                int rows_per_split, float* __restrict__ out, float* __restrict__ ws_o, float* __restrict__ ws_ml) {
+                const float* __restrict__ sel_bias, const int32_t* __restrict__ q_pos, int window, int h_q,
+                int h_kv, float scale_log2, int n_split, int rows_per_split, float* __restrict__ out,
+                float* __restrict__ ws_o, float* __restrict__ ws_ml) {
   typedef typename vec8<T>::type V8;
   constexpr int RT = kMfmaTile;       // = 64: one list entry per lane
   constexpr int KST = DKQ / 32;       // QK^T MFMA steps
@@ -144,7 +153,13 @@ fwd_mfma_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, 
   const int L = sm.len;
   const int64_t row0 = sm.row0;
   const int cnt = max(0, (int)min((int64_t)n_sel[i], sel_ld));
-  const int r_end = min(cnt, r_begin + rows_per_split);
+  int w0 = 0, wlen = 0;                              // dense window of the most recent positions
+  if (window > 0) {
+    const int n_vis = visible_tokens(L, q_pos[i]);
+    wlen = min(window, n_vis);
+    w0 = n_vis - wlen;
+  }
+  const int r_end = min(cnt + wlen, r_begin + rows_per_split);
   const int n_tiles = r_end > r_begin ? (r_end - r_begin + RT - 1) / RT : 0;
   const T* kg = k + (int64_t)g * k_hs;
   const T* vg = v + (int64_t)g * v_hs;
@@ -181,7 +196,8 @@ fwd_mfma_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, 
   };
   const int64_t safe_k = qbase - kg, safe_v = qbase - vg;
   auto tile_rows = [&](int pos, int t) {
-    const int64_t row = tile_row(pos, r_begin + t * RT + lane, r_end, L, row0);
+    const int j = r_begin + t * RT + lane;
+    const int64_t row = tile_row(row_pos(pos, j, cnt, w0, wlen), j, r_end, L, row0);
     TileRows tr;
     tr.ko = row >= 0 ? row * k_ld : safe_k;
     tr.vo = ALIAS ? 0 : (row >= 0 ? row * v_ld : safe_v);
@@ -439,9 +455,9 @@ __global__ void __launch_bounds__(256, 2)
 fwd_lds_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, int64_t k_hs,
                const int64_t* __restrict__ seq_row0, const int32_t* __restrict__ seq_len,
                const int32_t* __restrict__ q_seq, const int32_t* __restrict__ sel, int64_t sel_ld,
-               const int32_t* __restrict__ n_sel, const float* __restrict__ sel_bias, int h_q, int h_kv,
-               float scale_log2, int n_split, int rows_per_split, float* __restrict__ out,
-               float* __restrict__ ws_o, float* __restrict__ ws_ml) {
+               const int32_t* __restrict__ n_sel, const float* __restrict__ sel_bias,
+               const int32_t* __restrict__ q_pos, int window, int h_q, int h_kv, float scale_log2, int n_split,
+               int rows_per_split, float* __restrict__ out, float* __restrict__ ws_o, float* __restrict__ ws_ml) {
   typedef typename vec8<T>::type V8;
   typedef __attribute__((address_space(3))) void lds_void;
   constexpr int DV = 512;
@@ -478,7 +494,13 @@ fwd_lds_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, i
   const int L = sm.len;
   const int64_t row0 = sm.row0;
   const int cnt = max(0, (int)min((int64_t)n_sel[i], sel_ld));
-  const int r_end = min(cnt, r_begin + rows_per_split);
+  int w0 = 0, wlen = 0;                              // dense window of the most recent positions
+  if (window > 0) {
+    const int n_vis = visible_tokens(L, q_pos[i]);
+    wlen = min(window, n_vis);
+    w0 = n_vis - wlen;
+  }
+  const int r_end = min(cnt + wlen, r_begin + rows_per_split);
   const int n_tiles = r_end > r_begin ? (r_end - r_begin + RT - 1) / RT : 0;
   const T* kg = k + (int64_t)g * k_hs;
 
@@ -503,7 +525,8 @@ fwd_lds_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, i
   // marks the selected rows.
   const int64_t safe_k = qbase - kg;
   auto row_off = [&](int pos, int t, uint64_t* valid) {
-    const int64_t row = tile_row(pos, r_begin + t * RT + lane, r_end, L, row0);
+    const int j = r_begin + t * RT + lane;
+    const int64_t row = tile_row(row_pos(pos, j, cnt, w0, wlen), j, r_end, L, row0);
     *valid = __ballot(row >= 0);
     return row >= 0 ? row * k_ld : safe_k;
   };
@@ -656,9 +679,9 @@ fwd_valu_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, 
                 const T* __restrict__ v, int64_t v_ld, int64_t v_hs, const int64_t* __restrict__ seq_row0,
                 const int32_t* __restrict__ seq_len, const int32_t* __restrict__ q_seq,
                 const int32_t* __restrict__ sel, int64_t sel_ld, const int32_t* __restrict__ n_sel,
-                const float* __restrict__ sel_bias, int h_q, int h_kv, int d_kq, int d_v, float scale_log2,
-                int n_split, int rows_per_split, float* __restrict__ out, float* __restrict__ ws_o,
-                float* __restrict__ ws_ml) {
+                const float* __restrict__ sel_bias, const int32_t* __restrict__ q_pos, int window, int h_q,
+                int h_kv, int d_kq, int d_v, float scale_log2, int n_split, int rows_per_split,
+                float* __restrict__ out, float* __restrict__ ws_o, float* __restrict__ ws_ml) {
   __shared__ int64_t rows[kRowTile];
   __shared__ float rbias[kRowTile];                  // additive logit bias of each row (log2 units)
   __shared__ float p[16][kRowTile];
@@ -672,7 +695,13 @@ fwd_valu_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, 
   const int64_t row0 = sm.row0;
   const int cnt = max(0, (int)min((int64_t)n_sel[i], sel_ld));
   const int r_begin = split * rows_per_split;
-  const int r_end = min(cnt, r_begin + rows_per_split);
+  int w0 = 0, wlen = 0;                              // dense window of the most recent positions
+  if (window > 0) {
+    const int n_vis = visible_tokens(L, q_pos[i]);
+    wlen = min(window, n_vis);
+    w0 = n_vis - wlen;
+  }
+  const int r_end = min(cnt + wlen, r_begin + rows_per_split);
   const int32_t* list = sel + (int64_t)i * sel_ld;
   const float* blist = sel_bias ? sel_bias + (int64_t)i * sel_ld : nullptr;
   const T* qg = q + ((int64_t)i * h_q + (int64_t)g * G) * d_kq;
@@ -687,8 +716,10 @@ fwd_valu_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, 
   for (int r0 = r_begin; r0 < r_end; r0 += kRowTile) {
     __syncthreads();
     if (tid < kRowTile) {
-      rows[tid] = tile_row(r0 + tid < r_end ? list[r0 + tid] : -1, r0 + tid, r_end, L, row0);
-      rbias[tid] = (blist && r0 + tid < r_end) ? blist[r0 + tid] * kLog2e : 0.f;
+      const int j = r0 + tid;
+      const int entry = list[min(j, (int)sel_ld - 1)];
+      rows[tid] = tile_row(row_pos(entry, j, cnt, w0, wlen), j, r_end, L, row0);
+      rbias[tid] = (blist && j < min(r_end, cnt)) ? blist[j] * kLog2e : 0.f;
     }
     __syncthreads();
     for (int e = tid; e < G * kRowTile; e += 256) {
@@ -834,6 +865,18 @@ FwdPlan plan_fwd(const sa_dims& d, int n_q) {
   return p;
 }
 
+// With a dense window of `window` positions the rows per query grow by up to
+// `window`; the split count (and so the workspace) stays that of the plain plan and
+// each split takes more rows.
+FwdPlan plan_fwd_window(const sa_dims& d, int n_q, int window) {
+  FwdPlan p = plan_fwd(d, n_q);
+  const long long total = (long long)fwd_cap(d) + (window > 0 ? window : 0);
+  long long rps = (total + p.n_split - 1) / p.n_split;
+  rps = (rps + kMfmaTile - 1) / kMfmaTile * kMfmaTile;
+  if (rps > p.rows_per_split) p.rows_per_split = (int)rps;
+  return p;
+}
+
 size_t workspace_bytes(const sa_dims& d, int n_q, int max_len) {
   const size_t f = plan_fwd(d, n_q).ws_bytes;
   const size_t s = select_scratch_bytes(d, n_q, max_len);
@@ -856,49 +899,52 @@ bool fwd_uses_mfma(const sa_dims& d, const CacheArgs& c, const void* q) {
 
 template <typename T, int DKQ, int DV, bool ALIAS>
 static void launch_mfma_t(const sa_dims& d, const CacheArgs& c, const void* q, const int32_t* q_seq,
-                          const int32_t* sel, int64_t sel_ld, const int32_t* n_sel, const float* sel_bias, int n_q, float scale_log2,
+                          const int32_t* sel, int64_t sel_ld, const int32_t* n_sel, const float* sel_bias, const int32_t* q_pos, int window, int n_q,
+                          float scale_log2,
                           float* out, float* ws_o, float* ws_ml, const FwdPlan& plan, hipStream_t stream) {
   dim3 grid(plan.n_split, n_q * d.h_kv);
   hipLaunchKernelGGL((fwd_mfma_kernel<T, DKQ, DV, ALIAS>), grid, dim3(256), 0, stream, (const T*)q, (const T*)c.k,
                      c.k_ld, c.k_hs, (const T*)c.v, c.v_ld, c.v_hs, c.seq_row0, c.seq_len, q_seq, sel, sel_ld, n_sel,
-                     sel_bias, d.h_q, d.h_kv, scale_log2, plan.n_split, plan.rows_per_split, out, ws_o, ws_ml);
+                     sel_bias, q_pos, window, d.h_q, d.h_kv, scale_log2, plan.n_split, plan.rows_per_split, out, ws_o, ws_ml);
 }
 
 template <typename T, int DKQ>
 static void launch_lds_t(const sa_dims& d, const CacheArgs& c, const void* q, const int32_t* q_seq,
-                         const int32_t* sel, int64_t sel_ld, const int32_t* n_sel, const float* sel_bias, int n_q, float scale_log2,
+                         const int32_t* sel, int64_t sel_ld, const int32_t* n_sel, const float* sel_bias, const int32_t* q_pos, int window, int n_q,
+                          float scale_log2,
                          float* out, float* ws_o, float* ws_ml, const FwdPlan& plan, hipStream_t stream) {
   dim3 grid(plan.n_split, n_q * d.h_kv);
   hipLaunchKernelGGL((fwd_lds_kernel<T, DKQ>), grid, dim3(256), 0, stream, (const T*)q, (const T*)c.k, c.k_ld,
-                     c.k_hs, c.seq_row0, c.seq_len, q_seq, sel, sel_ld, n_sel, sel_bias, d.h_q, d.h_kv, scale_log2,
+                     c.k_hs, c.seq_row0, c.seq_len, q_seq, sel, sel_ld, n_sel, sel_bias, q_pos, window, d.h_q, d.h_kv, scale_log2,
                      plan.n_split, plan.rows_per_split, out, ws_o, ws_ml);
 }
 
 template <typename T>
 static void dispatch_mfma(const sa_dims& d, const CacheArgs& c, const void* q, const int32_t* q_seq,
-                          const int32_t* sel, int64_t sel_ld, const int32_t* n_sel, const float* sel_bias, int n_q, float scale_log2,
+                          const int32_t* sel, int64_t sel_ld, const int32_t* n_sel, const float* sel_bias, const int32_t* q_pos, int window, int n_q,
+                          float scale_log2,
                           float* out, float* ws_o, float* ws_ml, const FwdPlan& plan, hipStream_t stream) {
   const bool alias = c.v == c.k && c.v_ld == c.k_ld && c.v_hs == c.k_hs;
   if (alias && d.d_v == 512 && (d.d_kq == 576 || d.d_kq == 512)) {   // MLA: gathers straight into LDS
-    if (d.d_kq == 576) launch_lds_t<T, 576>(d, c, q, q_seq, sel, sel_ld, n_sel, sel_bias, n_q, scale_log2, out, ws_o, ws_ml, plan, stream);
-    else launch_lds_t<T, 512>(d, c, q, q_seq, sel, sel_ld, n_sel, sel_bias, n_q, scale_log2, out, ws_o, ws_ml, plan, stream);
+    if (d.d_kq == 576) launch_lds_t<T, 576>(d, c, q, q_seq, sel, sel_ld, n_sel, sel_bias, q_pos, window, n_q, scale_log2, out, ws_o, ws_ml, plan, stream);
+    else launch_lds_t<T, 512>(d, c, q, q_seq, sel, sel_ld, n_sel, sel_bias, q_pos, window, n_q, scale_log2, out, ws_o, ws_ml, plan, stream);
     return;
   }
 #define SA_FWD_CASE(DKQ_, DV_)                                                                                  \
   if (d.d_kq == DKQ_ && d.d_v == DV_) {                                                                          \
-    if (alias) launch_mfma_t<T, DKQ_, DV_, true>(d, c, q, q_seq, sel, sel_ld, n_sel, sel_bias, n_q, scale_log2, out, ws_o, \
+    if (alias) launch_mfma_t<T, DKQ_, DV_, true>(d, c, q, q_seq, sel, sel_ld, n_sel, sel_bias, q_pos, window, n_q, scale_log2, out, ws_o, \
                                                  ws_ml, plan, stream);                                           \
-    else launch_mfma_t<T, DKQ_, DV_, false>(d, c, q, q_seq, sel, sel_ld, n_sel, sel_bias, n_q, scale_log2, out, ws_o,      \
+    else launch_mfma_t<T, DKQ_, DV_, false>(d, c, q, q_seq, sel, sel_ld, n_sel, sel_bias, q_pos, window, n_q, scale_log2, out, ws_o,      \
                                             ws_ml, plan, stream);                                                \
     return;                                                                                                      \
   }
   // (V aliasing K at DV 512 went to the LDS kernel above)
   if (d.d_kq == 576 && d.d_v == 512) {
-    launch_mfma_t<T, 576, 512, false>(d, c, q, q_seq, sel, sel_ld, n_sel, sel_bias, n_q, scale_log2, out, ws_o, ws_ml, plan, stream);
+    launch_mfma_t<T, 576, 512, false>(d, c, q, q_seq, sel, sel_ld, n_sel, sel_bias, q_pos, window, n_q, scale_log2, out, ws_o, ws_ml, plan, stream);
     return;
   }
   if (d.d_kq == 512 && d.d_v == 512) {
-    launch_mfma_t<T, 512, 512, false>(d, c, q, q_seq, sel, sel_ld, n_sel, sel_bias, n_q, scale_log2, out, ws_o, ws_ml, plan, stream);
+    launch_mfma_t<T, 512, 512, false>(d, c, q, q_seq, sel, sel_ld, n_sel, sel_bias, q_pos, window, n_q, scale_log2, out, ws_o, ws_ml, plan, stream);
     return;
   }
   SA_FWD_CASE(256, 256)
@@ -908,7 +954,8 @@ static void dispatch_mfma(const sa_dims& d, const CacheArgs& c, const void* q, c
 
 template <typename T>
 static void dispatch_valu(const sa_dims& d, const CacheArgs& c, const void* q, const int32_t* q_seq,
-                          const int32_t* sel, int64_t sel_ld, const int32_t* n_sel, const float* sel_bias, int n_q, float scale_log2,
+                          const int32_t* sel, int64_t sel_ld, const int32_t* n_sel, const float* sel_bias, const int32_t* q_pos, int window, int n_q,
+                          float scale_log2,
                           float* out, float* ws_o, float* ws_ml, const FwdPlan& plan, hipStream_t stream) {
   dim3 grid(plan.n_split, n_q * d.h_kv);
   const int per = (d.h_q / d.h_kv) * d.d_v;
@@ -916,7 +963,7 @@ static void dispatch_valu(const sa_dims& d, const CacheArgs& c, const void* q, c
   if (per <= 256 * ACC_) {                                                                                        \
     hipLaunchKernelGGL((fwd_valu_kernel<T, ACC_>), grid, dim3(256), 0, stream, (const T*)q, (const T*)c.k, c.k_ld, \
                        c.k_hs, (const T*)c.v, c.v_ld, c.v_hs, c.seq_row0, c.seq_len, q_seq, sel, sel_ld, n_sel,    \
-                       sel_bias, d.h_q, d.h_kv, d.d_kq, d.d_v, scale_log2, plan.n_split, plan.rows_per_split, out, ws_o,     \
+                       sel_bias, q_pos, window, d.h_q, d.h_kv, d.d_kq, d.d_v, scale_log2, plan.n_split, plan.rows_per_split, out, ws_o,     \
                        ws_ml);                                                                                    \
     return;                                                                                                       \
   }
@@ -927,20 +974,20 @@ static void dispatch_valu(const sa_dims& d, const CacheArgs& c, const void* q, c
 }
 
 hipError_t launch_fwd(const sa_dims& d, const CacheArgs& c, const void* q, const int32_t* q_seq, const int32_t* sel,
-                      int64_t sel_ld, const int32_t* n_sel, const float* sel_bias, int n_q, float scale, float* out,
-                      void* ws, const FwdPlan& plan, hipStream_t stream) {
+                      int64_t sel_ld, const int32_t* n_sel, const float* sel_bias, const int32_t* q_pos, int window,
+                      int n_q, float scale, float* out, void* ws, const FwdPlan& plan, hipStream_t stream) {
   if (n_q == 0) return hipSuccess;
   const float scale_log2 = scale * kLog2e;
   float* ws_o = (float*)ws;
   float* ws_ml = plan.n_split > 1 ? ws_o + (size_t)n_q * d.h_q * plan.n_split * d.d_v : nullptr;
   if (fwd_uses_mfma(d, c, q)) {
-    if (d.dtype == SA_BF16) dispatch_mfma<bf16>(d, c, q, q_seq, sel, sel_ld, n_sel, sel_bias, n_q, scale_log2, out, ws_o, ws_ml, plan, stream);
-    else dispatch_mfma<f16>(d, c, q, q_seq, sel, sel_ld, n_sel, sel_bias, n_q, scale_log2, out, ws_o, ws_ml, plan, stream);
+    if (d.dtype == SA_BF16) dispatch_mfma<bf16>(d, c, q, q_seq, sel, sel_ld, n_sel, sel_bias, q_pos, window, n_q, scale_log2, out, ws_o, ws_ml, plan, stream);
+    else dispatch_mfma<f16>(d, c, q, q_seq, sel, sel_ld, n_sel, sel_bias, q_pos, window, n_q, scale_log2, out, ws_o, ws_ml, plan, stream);
   } else {
     switch (d.dtype) {
-      case SA_F32: dispatch_valu<float>(d, c, q, q_seq, sel, sel_ld, n_sel, sel_bias, n_q, scale_log2, out, ws_o, ws_ml, plan, stream); break;
-      case SA_F16: dispatch_valu<f16>(d, c, q, q_seq, sel, sel_ld, n_sel, sel_bias, n_q, scale_log2, out, ws_o, ws_ml, plan, stream); break;
-      default: dispatch_valu<bf16>(d, c, q, q_seq, sel, sel_ld, n_sel, sel_bias, n_q, scale_log2, out, ws_o, ws_ml, plan, stream); break;
+      case SA_F32: dispatch_valu<float>(d, c, q, q_seq, sel, sel_ld, n_sel, sel_bias, q_pos, window, n_q, scale_log2, out, ws_o, ws_ml, plan, stream); break;
+      case SA_F16: dispatch_valu<f16>(d, c, q, q_seq, sel, sel_ld, n_sel, sel_bias, q_pos, window, n_q, scale_log2, out, ws_o, ws_ml, plan, stream); break;
+      default: dispatch_valu<bf16>(d, c, q, q_seq, sel, sel_ld, n_sel, sel_bias, q_pos, window, n_q, scale_log2, out, ws_o, ws_ml, plan, stream); break;
     }
   }
   hipError_t err = hipGetLastError();

@@ -60,14 +60,16 @@ struct FwdPlan {
   size_t ws_bytes;                         // scratch bytes (partial results), 0 when unsplit
 };
 FwdPlan plan_fwd(const sa_dims& d, int n_q);
+FwdPlan plan_fwd_window(const sa_dims& d, int n_q, int window);
 
 // ws: the scratch part of the workspace.
 hipError_t launch_mask_to_indices(const void* mask, int mask_dtype, int64_t mask_ld, int n_q, int n_kv,
                                   int32_t* sel, int64_t sel_ld, int32_t* n_sel, float* sel_bias, hipStream_t stream);
 
 hipError_t launch_fwd(const sa_dims& d, const CacheArgs& c, const void* q, const int32_t* q_seq,
-                      const int32_t* sel, int64_t sel_ld, const int32_t* n_sel, const float* sel_bias, int n_q,
-                      float scale, float* out, void* ws, const FwdPlan& plan, hipStream_t stream);
+                      const int32_t* sel, int64_t sel_ld, const int32_t* n_sel, const float* sel_bias,
+                      const int32_t* q_pos, int window, int n_q, float scale, float* out, void* ws,
+                      const FwdPlan& plan, hipStream_t stream);
 
 // Total workspace bytes for n_q query tokens (state + the larger scratch), 0 if none.
 size_t workspace_bytes(const sa_dims& d, int n_q, int max_len);

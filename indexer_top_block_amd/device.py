@@ -85,6 +85,13 @@ class DeviceLayer:
         sa.sparse_attn_fwd(self.dims, self.cache, self.q, self.q_seq, sel, sel.shape[1], n_sel, self.n_q,
                            self.scale, self.out, self.ws, self.ws_bytes, stream)
 
+    def fwd_window(self, window: int, sel: Optional[torch.Tensor] = None, n_sel: Optional[torch.Tensor] = None,
+                   stream=None) -> None:
+        sel = self.sel if sel is None else sel
+        n_sel = self.n_sel if n_sel is None else n_sel
+        sa.sparse_attn_fwd_window(self.dims, self.cache, self.q, self.q_seq, self.q_pos, sel, sel.shape[1], n_sel,
+                                  window, self.n_q, self.scale, self.out, self.ws, self.ws_bytes, stream)
+
     def step(self, stream=None) -> None:
         """One pass of the whole path: pool what is new, score, select, attend."""
         self.pool(stream=stream)

@@ -34,6 +34,7 @@ EXPORTS = (
     "sparse_attn_fwd",
     "sparse_attn_mask_to_indices",
     "sparse_attn_fwd_bias",
+    "sparse_attn_fwd_window",
     "sparse_attn_strerror",
     "sparse_attn_version",
 )
@@ -91,6 +92,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.sparse_attn_mask_to_indices.restype = ctypes.c_int
     lib.sparse_attn_fwd_bias.argtypes = [dp, cp, P, P, P, I64, P, P, I32, ctypes.c_float, P, P, SZ, P]
     lib.sparse_attn_fwd_bias.restype = ctypes.c_int
+    lib.sparse_attn_fwd_window.argtypes = [dp, cp, P, P, P, P, I64, P, I32, I32, ctypes.c_float, P, P, SZ, P]
+    lib.sparse_attn_fwd_window.restype = ctypes.c_int
     lib.sparse_attn_strerror.argtypes = [ctypes.c_int]
     lib.sparse_attn_strerror.restype = ctypes.c_char_p
     lib.sparse_attn_version.argtypes = []
@@ -190,6 +193,14 @@ def sparse_attn_fwd_bias(dims: SaDims, cache: Cache, q, q_seq, sel, sel_ld: int,
            load().sparse_attn_fwd_bias(ctypes.byref(dims), ctypes.byref(cache.struct), _ptr(q), _ptr(q_seq),
                                        _ptr(sel), int(sel_ld), _ptr(n_sel), _ptr(sel_bias), int(n_q), float(scale),
                                        _ptr(out), _ptr(ws), int(ws_bytes), _stream(stream)))
+
+
+def sparse_attn_fwd_window(dims: SaDims, cache: Cache, q, q_seq, q_pos, sel, sel_ld: int, n_sel, window: int,
+                           n_q: int, scale: float, out, ws=None, ws_bytes: int = 0, stream=None) -> None:
+    _check("sparse_attn_fwd_window",
+           load().sparse_attn_fwd_window(ctypes.byref(dims), ctypes.byref(cache.struct), _ptr(q), _ptr(q_seq),
+                                         _ptr(q_pos), _ptr(sel), int(sel_ld), _ptr(n_sel), int(window), int(n_q),
+                                         float(scale), _ptr(out), _ptr(ws), int(ws_bytes), _stream(stream)))
 
 
 def sparse_attn_strerror(code: int) -> str:

@@ -351,6 +351,78 @@ def test_mask_form_edges(gpu_lib):
         assert layer.n_sel.cpu().numpy()[0] == 1000 and not layer.out[2].abs().max().item()
 
 
+# ------------------------------------------------------ dense window + selection
+
+def run_window(case, windows, queries=None):
+    """Selection on the GPU, then attention over the selected rows together with
+    the dense window of recent positions, against the oracle's attention over the
+    union of the two (each position once).  The kernel is also fed the oracle's
+    selection, and window 0 must reproduce the plain attention bit for bit."""
+    layer = DeviceLayer(case)
+    layer.pool()
+    layer.score()
+    layer.select()
+    layer.fwd()
+    torch.cuda.synchronize()
+    plain = layer.out.cpu().numpy()
+    gpu_sel = layer.selections()
+    pools = oracle.SequencePools(case)
+    queries = list(range(case.n_q)) if queries is None else list(queries)
+    res = {qi: oracle.run_query(case, qi, pools) for qi in queries}
+    for qi in queries:
+        parity.compare_selection(gpu_sel[qi], res[qi], case)
+    want_sel = [res[qi]["positions"] if qi in res else np.zeros(0, np.int64) for qi in range(case.n_q)]
+    o_sel, o_n = parity.upload_selection(layer, want_sel)
+    v_rows = case.v_rows()
+    for w in windows:
+        layer.out.fill_(-3.0)
+        layer.fwd_window(w)
+        torch.cuda.synchronize()
+        out = layer.out.cpu().numpy()
+        if w == 0:
+            assert np.array_equal(out, plain), "window 0 differs from the plain attention"
+        layer.fwd_window(w, o_sel, o_n)
+        torch.cuda.synchronize()
+        out2 = layer.out.cpu().numpy()
+        worst = 0.0
+        for qi in queries:
+            s = int(case.q_seq[qi])
+            n_vis = oracle.visible_tokens(case.seq_len[s], case.q_pos[qi])
+            r0 = int(case.row0[s])
+            for got, sel_q, tag in ((out[qi], gpu_sel[qi], "end-to-end"), (out2[qi], want_sel[qi], "fwd")):
+                pos = oracle.window_union(sel_q, n_vis, w)
+                want = oracle.attend(case.q[qi], case.k[r0 + pos], v_rows[r0 + pos], case.scale)
+                worst = max(worst, parity.check_out(got, want, case.dims.dtype, f"{case.name} q{qi} w{w} {tag}"))
+        say(f"[parity] {case.name}: window {w} ok  max-abs={worst:.3g}")
+    return layer
+
+
+def test_window_mla_lds_kernel(gpu_lib):
+    # MLA 576/512 with V inside K: windows none, small, a tile's worth, larger than
+    # the selection (the plan widens each split), and past the sequence start
+    d = dims(top_k=256, compress_ratio=4)
+    lens = [5000, 777, 3001]
+    q_seq = [0, 0, 0, 1, 1, 2, 2, 2]
+    q_pos = [4999, 2500, 3, 776, 0, 3000, 1029, 64]
+    case = datagen.make_case("window_mla", d, lens, q_seq, q_pos, seed=0, case_id=400, std="inv_sqrt_dim",
+                             v_separate=False)
+    run_window(case, [0, 1, 64, 200, 1500, 6000])
+
+
+def test_window_register_and_generic_kernels(gpu_lib):
+    # non-aliased 512/512 and GQA 128/128 on the register kernel; fp32 on the generic one
+    for j, d in enumerate((dims(d_kq=512, d_v=512, h_q=8, top_k=128, compress_ratio=4),
+                           dims(h_q=8, h_kv=2, d_kq=128, d_v=128, h_idx=8, top_k=96, compress_ratio=8, dtype="f16"),
+                           dims(h_q=4, h_kv=1, d_kq=64, d_v=48, h_idx=4, d_idx=64, top_k=40, compress_ratio=2,
+                                dtype="f32"))):
+        lens = [2100, 333]
+        q_seq = [0, 0, 1, 1]
+        q_pos = [2099, 700, 332, 5]
+        case = datagen.make_case(f"window_{j}", d, lens, q_seq, q_pos, seed=0, case_id=410 + j, std="inv_sqrt_dim",
+                                 v_separate=True)
+        run_window(case, [0, 17, 300, 2500])
+
+
 # ----------------------------------------------------------- full-size workloads
 
 @pytest.mark.parametrize("cfg,queries", [
@@ -367,3 +439,11 @@ def test_full_size_workload(gpu_lib, cfg, queries):
     if cfg == 5:
         kept = set((res[0]["positions"] // 4).tolist())
         assert len(kept & set(case.planted_blocks.tolist())) >= 500   # planted blocks dominate the selection
+
+
+def test_window_full_size_decode(gpu_lib):
+    # the 128K MLA decode step, attention over the selection plus the 128 most
+    # recent positions, in the launch configuration the benchmark times
+    say(f"[parity] generating workload 2: {datagen.WORKLOADS[2]}")
+    case = datagen.make_workload(2)
+    run_window(case, [128])

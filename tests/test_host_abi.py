@@ -170,3 +170,23 @@ def test_mask_form_entry_points_reject_bad_arguments():
                  FAKE, ws, None) == sa.SA_ERR_NULL
     assert _call("sparse_attn_fwd_bias", d, c, FAKE, FAKE, FAKE, 2051, FAKE, None, 0, ctypes.c_float(0.04), FAKE,
                  None, 0, None) == sa.SA_OK
+
+
+def test_window_entry_point_rejects_bad_arguments():
+    d = ctypes.byref(_dims())
+    c = ctypes.byref(_cache())
+    ws = sa.sparse_attn_workspace_bytes(_dims(), 1, 4096)
+    f = ctypes.c_float(0.04)
+    # negative or oversized window
+    assert _call("sparse_attn_fwd_window", d, c, FAKE, FAKE, FAKE, FAKE, 2051, FAKE, -1, 1, f, FAKE, FAKE, ws,
+                 None) == sa.SA_ERR_ARG
+    assert _call("sparse_attn_fwd_window", d, c, FAKE, FAKE, FAKE, FAKE, 2051, FAKE, (1 << 24) + 1, 1, f, FAKE, FAKE,
+                 ws, None) == sa.SA_ERR_ARG
+    # q_pos is required only with a window
+    assert _call("sparse_attn_fwd_window", d, c, FAKE, FAKE, None, FAKE, 2051, FAKE, 128, 1, f, FAKE, FAKE, ws,
+                 None) == sa.SA_ERR_NULL
+    # same workspace as the plain attention, whatever the window
+    assert _call("sparse_attn_fwd_window", d, c, FAKE, FAKE, FAKE, FAKE, 2051, FAKE, 4096, 1, f, FAKE, None, 0,
+                 None) == sa.SA_ERR_WORKSPACE
+    assert _call("sparse_attn_fwd_window", d, c, FAKE, FAKE, None, FAKE, 2051, FAKE, 0, 0, f, FAKE, None, 0,
+                 None) == sa.SA_OK
