@@ -329,15 +329,21 @@ def window_report(lay: "RotatingLayers", steps: int, warmup: int, window: int = 
     the `window` most recent positions (dense window + selection, merged in one pass;
     the window size is not fixed by the method's description, 128 is an example)."""
     R = lay.n
+    ws_bytes = sa.sparse_attn_workspace_bytes_window(lay.dims, lay.n_q, lay.max_len, window)
+    ws = torch.zeros((max(ws_bytes, 16),), dtype=torch.uint8, device=lay.device)
 
     def fwd_w(k):
         sa.sparse_attn_fwd_window(lay.dims, lay.caches[k % R], lay.q, lay.q_seq, lay.q_pos, lay.sel, lay.sel_ld,
-                                  lay.n_sel, window, lay.n_q, lay.case.scale, lay.out, lay.ws, lay.ws_bytes)
+                                  lay.n_sel, window, lay.n_q, lay.case.scale, lay.out, ws, ws_bytes)
+
+    def select_w(k):
+        sa.sparse_attn_select(lay.dims, lay.caches[k % R], lay.scores, lay.scores_ld, lay.q_seq, lay.q_pos,
+                              lay.n_q, lay.sel, lay.sel_ld, lay.n_sel, ws, ws_bytes)
 
     def step_w(k):
         lay.pool(k % R)
         lay.score(k % R)
-        lay.select(k % R)
+        select_w(k)
         fwd_w(k)
 
     ms = time_graph(step_w, steps, warmup)

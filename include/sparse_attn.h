@@ -169,7 +169,7 @@ int sparse_attn_select(const sa_dims* dims, const sa_cache* cache, const float* 
  * kernel loads K/V rows through the index list; rows -1 contribute nothing).  For
  * query token i, query head h (KV head g = h / (h_q/h_kv)):
  *     out[i][h][:] = sum_t softmax_t(scale * q[i][h] . K[t][g]) V[t][g][:]
- * over t in { seq_row0[s] + sel[i*sel_ld + j] : j < min(n_sel[i], sel_ld),
+ * over t in { seq_row0[s] + sel[i*sel_ld + j] : j < min(n_sel[i], sel_ld, top_k + c - 1),
  *             0 <= sel[...] < seq_len[s] } (other entries are skipped), accumulated
  * in float32; out = 0 when the set is empty.  q is [n_q][h_q][d_kq] contiguous in
  * the cache dtype; out is [n_q][h_q][d_v] float32 contiguous.  ws: workspace of
@@ -219,9 +219,15 @@ int sparse_attn_fwd_bias(const sa_dims* dims, const sa_cache* cache, const void*
  * dense attention over the contiguous recent keys plus sparse attention over the
  * selected keys, merged; reading: the contiguous block is the most recent window).
  * The window rows are contiguous and need no list.  q_pos: device [n_q] int32,
- * required when window > 0.  window = 0 gives sparse_attn_fwd.  The workspace is
- * that of sparse_attn_fwd (sparse_attn_workspace_bytes).
+ * required when window > 0.  window = 0 gives sparse_attn_fwd.  The workspace of
+ * sparse_attn_workspace_bytes suffices; one of sparse_attn_workspace_bytes_window
+ * bytes lets the window rows take workgroups of their own instead of lengthening
+ * every split (same results up to rounding order).
  * Errors: those of sparse_attn_fwd; SA_ERR_ARG for window < 0 or > 2^24.            */
+/* Workspace for sparse_attn_fwd_window with this window (>= that of
+ * sparse_attn_workspace_bytes; same contract).  0 on invalid arguments.             */
+size_t sparse_attn_workspace_bytes_window(const sa_dims* dims, int32_t n_q, int32_t max_len, int32_t window);
+
 int sparse_attn_fwd_window(const sa_dims* dims, const sa_cache* cache, const void* q,
                            const int32_t* q_seq, const int32_t* q_pos, const int32_t* sel, int64_t sel_ld,
                            const int32_t* n_sel, int32_t window, int32_t n_q, float scale, float* out,

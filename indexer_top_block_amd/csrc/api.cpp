@@ -70,6 +70,11 @@ size_t sparse_attn_workspace_bytes(const sa_dims* dims, int32_t n_q, int32_t max
   return sa::workspace_bytes(*dims, n_q, max_len);
 }
 
+size_t sparse_attn_workspace_bytes_window(const sa_dims* dims, int32_t n_q, int32_t max_len, int32_t window) {
+  if (check_dims(dims) != SA_OK || n_q < 0 || max_len < 0 || window < 0 || window > (1 << 24)) return 0;
+  return sa::workspace_bytes_window(*dims, n_q, max_len, window);
+}
+
 int sparse_attn_pool(const sa_dims* dims, const sa_cache* cache, const int32_t* n_pooled_in, int32_t* n_pooled_out,
                      int32_t max_new_blocks, void* stream) {
   int rc = check_dims(dims);
@@ -138,7 +143,8 @@ static int fwd_common(const sa_dims* dims, const sa_cache* cache, const void* q,
   if (!(scale == scale)) return SA_ERR_ARG;  // NaN
   if (window < 0 || window > (1 << 24)) return SA_ERR_ARG;
   if (window > 0 && !q_pos) return SA_ERR_NULL;
-  const sa::FwdPlan plan = sa::plan_fwd_window(*dims, n_q, window);
+  const size_t ws_avail = (ws && ws_bytes > SA_WS_STATE_BYTES) ? ws_bytes - SA_WS_STATE_BYTES : 0;
+  const sa::FwdPlan plan = sa::plan_fwd_window(*dims, n_q, window, ws_avail);
   void* scratch = nullptr;
   if (plan.ws_bytes > 0) {
     if (!ws || ws_bytes < SA_WS_STATE_BYTES + plan.ws_bytes) return SA_ERR_WORKSPACE;

@@ -109,7 +109,7 @@ fwd_mfma_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, 
                 const T* __restrict__ v, int64_t v_ld, int64_t v_hs, const int64_t* __restrict__ seq_row0,
                 const int32_t* __restrict__ seq_len, const int32_t* __restrict__ q_seq,
                 const int32_t* __restrict__ sel, int64_t sel_ld, const int32_t* __restrict__ n_sel,
-                const float* __restrict__ sel_bias, const int32_t* __restrict__ q_pos, int window, int h_q,
+                const float* __restrict__ sel_bias, const int32_t* __restrict__ q_pos, int window, int list_max, int h_q,
                 int h_kv, float scale_log2, int n_split, int rows_per_split, float* __restrict__ out,
                 float* __restrict__ ws_o, float* __restrict__ ws_ml) {
   typedef typename vec8<T>::type V8;
@@ -146,13 +146,13 @@ fwd_mfma_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, 
   // clamped into the row rather than guarded, so the loads issue back to back;
   // entries at or past the query's count are discarded once it is known.  The
   // first four tiles' entries are read alongside the query's metadata.
-  const int lim = (int)sel_ld - 1;
+  const int lim = (int)min(sel_ld, (int64_t)list_max) - 1;
   auto list_at = [&](int t) { return list[min(r_begin + t * RT + lane, lim)]; };
   const int pre0 = list_at(0), pre1 = list_at(1), pre2 = list_at(2), pre3 = list_at(3);
   const SeqMeta sm = seq_meta(q_seq, seq_len, seq_row0, nullptr, i);
   const int L = sm.len;
   const int64_t row0 = sm.row0;
-  const int cnt = max(0, (int)min((int64_t)n_sel[i], sel_ld));
+  const int cnt = max(0, (int)min((int64_t)n_sel[i], min(sel_ld, (int64_t)list_max)));
   int w0 = 0, wlen = 0;                              // dense window of the most recent positions
   if (window > 0) {
     const int n_vis = visible_tokens(L, q_pos[i]);
@@ -456,7 +456,7 @@ fwd_lds_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, i
                const int64_t* __restrict__ seq_row0, const int32_t* __restrict__ seq_len,
                const int32_t* __restrict__ q_seq, const int32_t* __restrict__ sel, int64_t sel_ld,
                const int32_t* __restrict__ n_sel, const float* __restrict__ sel_bias,
-               const int32_t* __restrict__ q_pos, int window, int h_q, int h_kv, float scale_log2, int n_split,
+               const int32_t* __restrict__ q_pos, int window, int list_max, int h_q, int h_kv, float scale_log2, int n_split,
                int rows_per_split, float* __restrict__ out, float* __restrict__ ws_o, float* __restrict__ ws_ml) {
   typedef typename vec8<T>::type V8;
   typedef __attribute__((address_space(3))) void lds_void;
@@ -486,14 +486,14 @@ fwd_lds_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, i
   const int32_t* list = sel + (int64_t)i * sel_ld;
   const float* blist = sel_bias ? sel_bias + (int64_t)i * sel_ld : nullptr;   // additive logit bias per entry
   const int r_begin = split * rows_per_split;
-  const int lim = (int)sel_ld - 1;
+  const int lim = (int)min(sel_ld, (int64_t)list_max) - 1;
   auto list_at = [&](int t) { return list[min(r_begin + t * RT + lane, lim)]; };
   auto bias_at = [&](int t) { return blist ? blist[min(r_begin + t * RT + lane, lim)] : 0.f; };
   const int pre0 = list_at(0), pre1 = list_at(1), pre2 = list_at(2);
   const SeqMeta sm = seq_meta(q_seq, seq_len, seq_row0, nullptr, i);
   const int L = sm.len;
   const int64_t row0 = sm.row0;
-  const int cnt = max(0, (int)min((int64_t)n_sel[i], sel_ld));
+  const int cnt = max(0, (int)min((int64_t)n_sel[i], min(sel_ld, (int64_t)list_max)));
   int w0 = 0, wlen = 0;                              // dense window of the most recent positions
   if (window > 0) {
     const int n_vis = visible_tokens(L, q_pos[i]);
@@ -679,7 +679,7 @@ fwd_valu_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, 
                 const T* __restrict__ v, int64_t v_ld, int64_t v_hs, const int64_t* __restrict__ seq_row0,
                 const int32_t* __restrict__ seq_len, const int32_t* __restrict__ q_seq,
                 const int32_t* __restrict__ sel, int64_t sel_ld, const int32_t* __restrict__ n_sel,
-                const float* __restrict__ sel_bias, const int32_t* __restrict__ q_pos, int window, int h_q,
+                const float* __restrict__ sel_bias, const int32_t* __restrict__ q_pos, int window, int list_max, int h_q,
                 int h_kv, int d_kq, int d_v, float scale_log2, int n_split, int rows_per_split,
                 float* __restrict__ out, float* __restrict__ ws_o, float* __restrict__ ws_ml) {
   __shared__ int64_t rows[kRowTile];
@@ -693,7 +693,7 @@ fwd_valu_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, 
   const SeqMeta sm = seq_meta(q_seq, seq_len, seq_row0, nullptr, i);
   const int L = sm.len;
   const int64_t row0 = sm.row0;
-  const int cnt = max(0, (int)min((int64_t)n_sel[i], sel_ld));
+  const int cnt = max(0, (int)min((int64_t)n_sel[i], min(sel_ld, (int64_t)list_max)));
   const int r_begin = split * rows_per_split;
   int w0 = 0, wlen = 0;                              // dense window of the most recent positions
   if (window > 0) {
@@ -717,7 +717,7 @@ fwd_valu_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, 
     __syncthreads();
     if (tid < kRowTile) {
       const int j = r0 + tid;
-      const int entry = list[min(j, (int)sel_ld - 1)];
+      const int entry = list[min(j, (int)min(sel_ld, (int64_t)list_max) - 1)];
       rows[tid] = tile_row(row_pos(entry, j, cnt, w0, wlen), j, r_end, L, row0);
       rbias[tid] = (blist && j < min(r_end, cnt)) ? blist[j] * kLog2e : 0.f;
     }
@@ -846,31 +846,41 @@ static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 static int fwd_cap(const sa_dims& d) { return d.top_k + d.compress_ratio - 1; }
 
-FwdPlan plan_fwd(const sa_dims& d, int n_q) {
+// Split plan for up to `rows` attended rows per query.
+static FwdPlan plan_rows(const sa_dims& d, int n_q, long long rows) {
   FwdPlan p{};
-  const int cap = fwd_cap(d);
   const long long units = (long long)n_q * d.h_kv;
   // Aim at about 512 workgroups; never split below one 64-row tile.  (Decode is bound
   // by what one CU can pull: a second tile per workgroup costs more than the smaller
   // combine it buys.)
   long long want = units > 0 ? (512 + units - 1) / units : 1;
-  const long long max_split = (cap + kMfmaTile - 1) / kMfmaTile;
+  const long long max_split = (rows + kMfmaTile - 1) / kMfmaTile;
   if (want > max_split) want = max_split;
   if (want < 1) want = 1;
-  int rps = (int)((cap + want - 1) / want);
+  long long rps = (rows + want - 1) / want;
   rps = (rps + kMfmaTile - 1) / kMfmaTile * kMfmaTile;
-  p.rows_per_split = rps;
-  p.n_split = (cap + rps - 1) / rps;
+  if (rps < kMfmaTile) rps = kMfmaTile;
+  p.rows_per_split = (int)rps;
+  p.list_max = fwd_cap(d);
+  p.n_split = (int)((rows + rps - 1) / rps);
+  if (p.n_split < 1) p.n_split = 1;
   p.ws_bytes = p.n_split > 1 ? (size_t)n_q * d.h_q * p.n_split * ((size_t)d.d_v + 2) * sizeof(float) : 0;
   return p;
 }
 
+FwdPlan plan_fwd(const sa_dims& d, int n_q) { return plan_rows(d, n_q, fwd_cap(d)); }
+
+static long long window_rows(const sa_dims& d, int window) { return (long long)fwd_cap(d) + (window > 0 ? window : 0); }
+
 // With a dense window of `window` positions the rows per query grow by up to
-// `window`; the split count (and so the workspace) stays that of the plain plan and
-// each split takes more rows.
-FwdPlan plan_fwd_window(const sa_dims& d, int n_q, int window) {
+// `window`.  When the workspace holds the partials of the plan for all those rows
+// (workspace_bytes_window), that plan is used; otherwise the split count of the
+// plain plan is kept -- its workspace always suffices -- and each split takes more rows.
+FwdPlan plan_fwd_window(const sa_dims& d, int n_q, int window, size_t ws_avail) {
+  const long long total = window_rows(d, window);
+  FwdPlan full = plan_rows(d, n_q, total);
+  if (full.ws_bytes <= ws_avail) return full;
   FwdPlan p = plan_fwd(d, n_q);
-  const long long total = (long long)fwd_cap(d) + (window > 0 ? window : 0);
   long long rps = (total + p.n_split - 1) / p.n_split;
   rps = (rps + kMfmaTile - 1) / kMfmaTile * kMfmaTile;
   if (rps > p.rows_per_split) p.rows_per_split = (int)rps;
@@ -882,6 +892,13 @@ size_t workspace_bytes(const sa_dims& d, int n_q, int max_len) {
   const size_t s = select_scratch_bytes(d, n_q, max_len);
   if (f == 0 && s == 0) return 0;
   return SA_WS_STATE_BYTES + (f > s ? f : s);
+}
+
+size_t workspace_bytes_window(const sa_dims& d, int n_q, int max_len, int window) {
+  const size_t base = workspace_bytes(d, n_q, max_len);
+  const size_t f = plan_rows(d, n_q, window_rows(d, window)).ws_bytes;
+  const size_t w = f > 0 ? SA_WS_STATE_BYTES + f : 0;
+  return w > base ? w : base;
 }
 
 bool fwd_uses_mfma(const sa_dims& d, const CacheArgs& c, const void* q) {
@@ -905,7 +922,7 @@ static void launch_mfma_t(const sa_dims& d, const CacheArgs& c, const void* q, c
   dim3 grid(plan.n_split, n_q * d.h_kv);
   hipLaunchKernelGGL((fwd_mfma_kernel<T, DKQ, DV, ALIAS>), grid, dim3(256), 0, stream, (const T*)q, (const T*)c.k,
                      c.k_ld, c.k_hs, (const T*)c.v, c.v_ld, c.v_hs, c.seq_row0, c.seq_len, q_seq, sel, sel_ld, n_sel,
-                     sel_bias, q_pos, window, d.h_q, d.h_kv, scale_log2, plan.n_split, plan.rows_per_split, out, ws_o, ws_ml);
+                     sel_bias, q_pos, window, plan.list_max, d.h_q, d.h_kv, scale_log2, plan.n_split, plan.rows_per_split, out, ws_o, ws_ml);
 }
 
 template <typename T, int DKQ>
@@ -915,7 +932,7 @@ static void launch_lds_t(const sa_dims& d, const CacheArgs& c, const void* q, co
                          float* out, float* ws_o, float* ws_ml, const FwdPlan& plan, hipStream_t stream) {
   dim3 grid(plan.n_split, n_q * d.h_kv);
   hipLaunchKernelGGL((fwd_lds_kernel<T, DKQ>), grid, dim3(256), 0, stream, (const T*)q, (const T*)c.k, c.k_ld,
-                     c.k_hs, c.seq_row0, c.seq_len, q_seq, sel, sel_ld, n_sel, sel_bias, q_pos, window, d.h_q, d.h_kv, scale_log2,
+                     c.k_hs, c.seq_row0, c.seq_len, q_seq, sel, sel_ld, n_sel, sel_bias, q_pos, window, plan.list_max, d.h_q, d.h_kv, scale_log2,
                      plan.n_split, plan.rows_per_split, out, ws_o, ws_ml);
 }
 
@@ -963,7 +980,7 @@ static void dispatch_valu(const sa_dims& d, const CacheArgs& c, const void* q, c
   if (per <= 256 * ACC_) {                                                                                        \
     hipLaunchKernelGGL((fwd_valu_kernel<T, ACC_>), grid, dim3(256), 0, stream, (const T*)q, (const T*)c.k, c.k_ld, \
                        c.k_hs, (const T*)c.v, c.v_ld, c.v_hs, c.seq_row0, c.seq_len, q_seq, sel, sel_ld, n_sel,    \
-                       sel_bias, q_pos, window, d.h_q, d.h_kv, d.d_kq, d.d_v, scale_log2, plan.n_split, plan.rows_per_split, out, ws_o,     \
+                       sel_bias, q_pos, window, plan.list_max, d.h_q, d.h_kv, d.d_kq, d.d_v, scale_log2, plan.n_split, plan.rows_per_split, out, ws_o,     \
                        ws_ml);                                                                                    \
     return;                                                                                                       \
   }

@@ -57,10 +57,11 @@ hipError_t launch_select(const sa_dims& d, const CacheArgs& c, const float* scor
 struct FwdPlan {
   int n_split;
   int rows_per_split;
+  int list_max;                            // list entries attended at most (top_k + c - 1)
   size_t ws_bytes;                         // scratch bytes (partial results), 0 when unsplit
 };
 FwdPlan plan_fwd(const sa_dims& d, int n_q);
-FwdPlan plan_fwd_window(const sa_dims& d, int n_q, int window);
+FwdPlan plan_fwd_window(const sa_dims& d, int n_q, int window, size_t ws_avail);
 
 // ws: the scratch part of the workspace.
 hipError_t launch_mask_to_indices(const void* mask, int mask_dtype, int64_t mask_ld, int n_q, int n_kv,
@@ -73,6 +74,7 @@ hipError_t launch_fwd(const sa_dims& d, const CacheArgs& c, const void* q, const
 
 // Total workspace bytes for n_q query tokens (state + the larger scratch), 0 if none.
 size_t workspace_bytes(const sa_dims& d, int n_q, int max_len);
+size_t workspace_bytes_window(const sa_dims& d, int n_q, int max_len, int window);
 
 // Which implementation a call takes (exposed for tests and reports).
 bool score_uses_mfma(const sa_dims& d, const CacheArgs& c, const void* qidx);

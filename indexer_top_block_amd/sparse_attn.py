@@ -34,6 +34,7 @@ EXPORTS = (
     "sparse_attn_fwd",
     "sparse_attn_mask_to_indices",
     "sparse_attn_fwd_bias",
+    "sparse_attn_workspace_bytes_window",
     "sparse_attn_fwd_window",
     "sparse_attn_strerror",
     "sparse_attn_version",
@@ -92,6 +93,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.sparse_attn_mask_to_indices.restype = ctypes.c_int
     lib.sparse_attn_fwd_bias.argtypes = [dp, cp, P, P, P, I64, P, P, I32, ctypes.c_float, P, P, SZ, P]
     lib.sparse_attn_fwd_bias.restype = ctypes.c_int
+    lib.sparse_attn_workspace_bytes_window.argtypes = [dp, I32, I32, I32]
+    lib.sparse_attn_workspace_bytes_window.restype = SZ
     lib.sparse_attn_fwd_window.argtypes = [dp, cp, P, P, P, P, I64, P, I32, I32, ctypes.c_float, P, P, SZ, P]
     lib.sparse_attn_fwd_window.restype = ctypes.c_int
     lib.sparse_attn_strerror.argtypes = [ctypes.c_int]
@@ -147,6 +150,10 @@ def sparse_attn_check_dims(dims: SaDims) -> int:
 
 def sparse_attn_workspace_bytes(dims: SaDims, n_q: int, max_len: int) -> int:
     return int(load().sparse_attn_workspace_bytes(ctypes.byref(dims), int(n_q), int(max_len)))
+
+
+def sparse_attn_workspace_bytes_window(dims: SaDims, n_q: int, max_len: int, window: int) -> int:
+    return int(load().sparse_attn_workspace_bytes_window(ctypes.byref(dims), int(n_q), int(max_len), int(window)))
 
 
 def sparse_attn_pool(dims: SaDims, cache: Cache, n_pooled_in, n_pooled_out, max_new_blocks: int,

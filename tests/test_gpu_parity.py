@@ -374,26 +374,36 @@ def run_window(case, windows, queries=None):
     want_sel = [res[qi]["positions"] if qi in res else np.zeros(0, np.int64) for qi in range(case.n_q)]
     o_sel, o_n = parity.upload_selection(layer, want_sel)
     v_rows = case.v_rows()
+    plain_ws = (layer.ws, layer.ws_bytes)
     for w in windows:
-        layer.out.fill_(-3.0)
-        layer.fwd_window(w)
-        torch.cuda.synchronize()
-        out = layer.out.cpu().numpy()
-        if w == 0:
-            assert np.array_equal(out, plain), "window 0 differs from the plain attention"
-        layer.fwd_window(w, o_sel, o_n)
-        torch.cuda.synchronize()
-        out2 = layer.out.cpu().numpy()
-        worst = 0.0
-        for qi in queries:
-            s = int(case.q_seq[qi])
-            n_vis = oracle.visible_tokens(case.seq_len[s], case.q_pos[qi])
-            r0 = int(case.row0[s])
-            for got, sel_q, tag in ((out[qi], gpu_sel[qi], "end-to-end"), (out2[qi], want_sel[qi], "fwd")):
-                pos = oracle.window_union(sel_q, n_vis, w)
-                want = oracle.attend(case.q[qi], case.k[r0 + pos], v_rows[r0 + pos], case.scale)
-                worst = max(worst, parity.check_out(got, want, case.dims.dtype, f"{case.name} q{qi} w{w} {tag}"))
-        say(f"[parity] {case.name}: window {w} ok  max-abs={worst:.3g}")
+        # the plain workspace (window rows lengthen the splits), then the window's own
+        # (window rows get splits of their own)
+        wide_bytes = sa.sparse_attn_workspace_bytes_window(layer.dims, layer.n_q, layer.max_len, w)
+        assert wide_bytes >= layer.ws_bytes
+        wide_ws = torch.zeros((max(wide_bytes, 16),), dtype=torch.uint8, device=layer.device)
+        for ws, ws_bytes, ws_tag in (plain_ws + ("plain-ws",), (wide_ws, wide_bytes, "window-ws")):
+            layer.ws, layer.ws_bytes = ws, ws_bytes
+            layer.out.fill_(-3.0)
+            layer.fwd_window(w)
+            torch.cuda.synchronize()
+            out = layer.out.cpu().numpy()
+            if w == 0:
+                assert np.array_equal(out, plain), "window 0 differs from the plain attention"
+            layer.fwd_window(w, o_sel, o_n)
+            torch.cuda.synchronize()
+            out2 = layer.out.cpu().numpy()
+            worst = 0.0
+            for qi in queries:
+                s = int(case.q_seq[qi])
+                n_vis = oracle.visible_tokens(case.seq_len[s], case.q_pos[qi])
+                r0 = int(case.row0[s])
+                for got, sel_q, tag in ((out[qi], gpu_sel[qi], "end-to-end"), (out2[qi], want_sel[qi], "fwd")):
+                    pos = oracle.window_union(sel_q, n_vis, w)
+                    want = oracle.attend(case.q[qi], case.k[r0 + pos], v_rows[r0 + pos], case.scale)
+                    worst = max(worst, parity.check_out(got, want, case.dims.dtype,
+                                                        f"{case.name} q{qi} w{w} {tag} {ws_tag}"))
+            say(f"[parity] {case.name}: window {w} {ws_tag} ok  max-abs={worst:.3g}")
+        layer.ws, layer.ws_bytes = plain_ws
     return layer
 
 
@@ -447,3 +457,28 @@ def test_window_full_size_decode(gpu_lib):
     say(f"[parity] generating workload 2: {datagen.WORKLOADS[2]}")
     case = datagen.make_workload(2)
     run_window(case, [128])
+
+
+def test_list_longer_than_capacity(gpu_lib):
+    # a list pitch and count above top_k + c - 1: only the first top_k + c - 1
+    # entries are attended, with and without a window (the window rows come after them)
+    d = dims(top_k=128, compress_ratio=4, h_q=16)
+    case = datagen.make_case("over_capacity", d, [4000], [0, 0], [3999, 1500], seed=0, case_id=420,
+                             std="inv_sqrt_dim", v_separate=False)
+    layer = DeviceLayer(case)
+    cap = d.top_k + d.compress_ratio - 1
+    rng = np.random.default_rng(421)
+    lists = [np.sort(rng.choice(1400, cap + 90, replace=False)) for _ in range(case.n_q)]
+    sel = torch.from_numpy(np.stack(lists).astype(np.int32)).cuda()
+    n_sel = torch.full((case.n_q,), cap + 90, dtype=torch.int32, device="cuda")
+    v_rows = case.v_rows()
+    for w in (0, 50):
+        layer.fwd_window(w, sel, n_sel)
+        torch.cuda.synchronize()
+        out = layer.out.cpu().numpy()
+        for qi in range(case.n_q):
+            n_vis = oracle.visible_tokens(case.seq_len[0], case.q_pos[qi])
+            pos = oracle.window_union(lists[qi][:cap], n_vis, w)
+            want = oracle.attend(case.q[qi], case.k[pos], v_rows[pos], case.scale)
+            parity.check_out(out[qi], want, d.dtype, f"over-capacity q{qi} w{w}")
+    say("[parity] list longer than capacity: ok")

@@ -190,3 +190,13 @@ def test_window_entry_point_rejects_bad_arguments():
                  None) == sa.SA_ERR_WORKSPACE
     assert _call("sparse_attn_fwd_window", d, c, FAKE, FAKE, None, FAKE, 2051, FAKE, 0, 0, f, FAKE, None, 0,
                  None) == sa.SA_OK
+
+
+def test_window_workspace_size():
+    d = _dims()
+    base = sa.sparse_attn_workspace_bytes(d, 1, 4096)
+    assert sa.sparse_attn_workspace_bytes_window(d, 1, 4096, 0) == base
+    assert sa.sparse_attn_workspace_bytes_window(d, 1, 4096, 128) >= base
+    assert sa.sparse_attn_workspace_bytes_window(d, 1, 4096, 100000) > base
+    assert sa.sparse_attn_workspace_bytes_window(d, 1, 4096, -1) == 0
+    assert sa.sparse_attn_workspace_bytes_window(d, -1, 4096, 8) == 0
