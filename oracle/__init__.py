@@ -7,9 +7,11 @@ from .sparse_attn_oracle import (  # noqa: F401
     SequencePools,
     attend,
     block_scores,
+    dequantize_q8_0,
     mask_positions,
     merge_partials,
     pool_blocks,
+    quantize_q8_0,
     round_to_storage,
     run_case,
     run_query,

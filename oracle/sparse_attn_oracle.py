@@ -212,6 +212,50 @@ def merge_partials(parts) -> np.ndarray:
     return num / den[:, None]
 
 
+# ------------------------------------------------------------ quantized KV cache
+
+Q8_0_BLOCK = 32
+
+
+def quantize_q8_0(x) -> tuple[np.ndarray, np.ndarray]:
+    """Quantize rows to the q8_0 KV-cache type: per block of 32 consecutive values one
+    scale d and 32 signed 8-bit codes, value ~ d * code.
+
+    The pages put a quantized KV cache on the QSA attention path ("qwen4exp: support
+    a quantized KV cache in the QSA attention path", in the qwen4exp commit series)
+    and run the sparse graph with K and V cache types q8_0 (the commit there on
+    reserving the sparse graph).  Reading: q8_0 is ggml's published block format --
+    d = max|x| / 127 over the block, codes = x / d rounded half away from zero (0 for
+    an all-zero block), d stored as float16.  The codes are integers decided by
+    floating point, so that decision is taken in float32, the precision of the format's
+    reference quantizer and of the GPU kernel: max|x| exact, one correctly rounded
+    division for d and one for 1/d, one float32 product per value, then the rounding.
+
+    ``x``: float values [..., n], n % 32 == 0.  Returns (codes int8 [..., n],
+    scales float64 [..., n / 32] holding float16 values).
+    """
+    x = np.asarray(x, dtype=np.float32)
+    n = x.shape[-1]
+    assert n % Q8_0_BLOCK == 0, "row length must be a multiple of 32"
+    blocks = x.reshape(x.shape[:-1] + (n // Q8_0_BLOCK, Q8_0_BLOCK))
+    amax = np.abs(blocks).max(axis=-1)
+    d = (amax / np.float32(127.0)).astype(np.float32)
+    inv = np.zeros_like(d)
+    nz = d != 0
+    inv[nz] = np.float32(1.0) / d[nz]
+    y = (blocks * inv[..., None]).astype(np.float32).astype(np.float64)
+    codes = np.sign(y) * np.floor(np.abs(y) + 0.5)          # exact in float64: half away from zero
+    return codes.astype(np.int8).reshape(x.shape), round_to_storage(d.astype(np.float64), "f16")
+
+
+def dequantize_q8_0(codes, scales) -> np.ndarray:
+    """The values a q8_0 cache holds: scale of the block times the code, in float64
+    (exact: an 8-bit code times an 11-bit scale)."""
+    codes = np.asarray(codes, dtype=np.float64)
+    scales = np.asarray(scales, dtype=np.float64)
+    return codes * np.repeat(scales, Q8_0_BLOCK, axis=-1)
+
+
 # ----------------------------------------------------------------------- pipeline
 
 class SequencePools:

@@ -367,6 +367,110 @@ def test_window_union_attention_is_the_merge_of_window_and_sparse_parts():
     assert not np.allclose(oracle.attend(q, k[dup], v[dup], 0.2), oracle.attend(q, k[u], v[u], 0.2))
 
 
+# ------------------------------------------------------------ quantized KV cache
+
+def _f16(v: float) -> float:
+    """float16 rounding by Python's own half-precision packing (ties to even)."""
+    import struct
+    return struct.unpack("<e", struct.pack("<e", v))[0]
+
+
+def _round_half_away(fr):
+    """Round a Fraction half away from zero."""
+    from fractions import Fraction
+    a = abs(fr)
+    r = math.floor(a + Fraction(1, 2))
+    return r if fr >= 0 else -r
+
+
+def test_q8_0_hand_block():
+    # codes = round(x * 127 / max|x|) in exact rational arithmetic (the block has no
+    # value near a rounding tie, so float32 cannot change a code); scale = the float16
+    # of max|x| / 127
+    from fractions import Fraction
+    x = (np.arange(32) - 16) * 3 + 1                              # -47 .. 46 step 3
+    amax = int(np.abs(x).max())
+    exact = [Fraction(int(v) * 127, amax) for v in x]
+    assert all(abs(abs(e - math.floor(e)) - Fraction(1, 2)) > Fraction(1, 1000) for e in exact)
+    want = [_round_half_away(e) for e in exact]
+    codes, scales = oracle.quantize_q8_0(x.astype(np.float32))
+    assert codes.tolist() == want
+    assert codes[0] == -127
+    assert scales.shape == (1,) and scales[0] == _f16(float(np.float32(amax) / np.float32(127)))
+
+
+def test_q8_0_ties_round_half_away_from_zero():
+    # max|x| = 127 makes d = 1 and 1/d = 1 exactly, so x * (1/d) = x: halves are ties
+    x = np.zeros(32, np.float32)
+    x[:8] = [127, 2.5, -2.5, 0.5, -0.5, 1.5, -1.5, 126.5]
+    codes, scales = oracle.quantize_q8_0(x)
+    assert codes[:8].tolist() == [127, 3, -3, 1, -1, 2, -2, 127]
+    assert scales[0] == 1.0
+
+
+def test_q8_0_invariants():
+    rng = np.random.default_rng(31)
+    x = (rng.standard_normal((40, 96)) * np.exp(rng.uniform(-6, 3, (40, 1)))).astype(np.float32)
+    x[3, 32:64] = 0.0                                            # an all-zero block
+    codes, scales = oracle.quantize_q8_0(x)
+    assert codes.shape == x.shape and scales.shape == (40, 3)
+    assert np.abs(codes.astype(int)).max() <= 127
+    blk = x.reshape(40, 3, 32)
+    cb = codes.reshape(40, 3, 32).astype(int)
+    arg = np.abs(blk).argmax(axis=-1)
+    top = np.take_along_axis(cb, arg[..., None], axis=-1)[..., 0]
+    top_x = np.take_along_axis(blk, arg[..., None], axis=-1)[..., 0]
+    nz = np.abs(top_x) > 0
+    assert (np.abs(top[nz]) == 127).all() and (np.sign(top[nz]) == np.sign(top_x[nz])).all()
+    assert (cb[3, 1] == 0).all() and scales[3, 1] == 0.0
+    assert (np.sign(cb) * np.sign(blk) >= 0).all()                # signs kept (or zero)
+    # reconstruction error: half a step, plus the scale's float16 rounding
+    d32 = np.abs(blk).max(axis=-1).astype(np.float64) / 127.0
+    err = np.abs(oracle.dequantize_q8_0(codes, scales) - x.astype(np.float64)).reshape(40, 3, 32).max(axis=-1)
+    assert (err <= d32 / 2 * (1 + 1e-6) + 127 * np.abs(scales - d32) + 1e-30).all()
+    # a power-of-two scaling of a block scales d and leaves the codes
+    c2, s2 = oracle.quantize_q8_0(x[:, :32] * np.float32(4.0))
+    ok = (scales[:, 0] * 4 < 65504) & (scales[:, 0] >= 2.0 ** -14)      # normal float16 both ways
+    assert np.array_equal(c2[ok], codes[ok, :32]) and np.array_equal(s2[ok, 0], scales[ok, 0] * 4)
+
+
+def test_q8_0_blocks_are_independent_and_round_trip_exactly():
+    rng = np.random.default_rng(32)
+    x = rng.standard_normal((5, 64)).astype(np.float32)
+    c0, s0 = oracle.quantize_q8_0(x)
+    y = x.copy()
+    y[:, 40] *= 50.0                                             # only the second block changes
+    c1, s1 = oracle.quantize_q8_0(y)
+    assert np.array_equal(c0[:, :32], c1[:, :32]) and np.array_equal(s0[:, 0], s1[:, 0])
+    assert not np.array_equal(s0[:, 1], s1[:, 1])
+    # values already of the form d * code (d a float16 power of two, one code of +-127)
+    # quantize and dequantize back exactly
+    codes = rng.integers(-127, 128, size=(6, 64))
+    codes[:, ::32] = 127
+    d = np.float64(2.0) ** rng.integers(-12, 2, size=(6, 2))
+    vals = (codes * np.repeat(d, 32, axis=1)).astype(np.float32)
+    c2, s2 = oracle.quantize_q8_0(vals)
+    assert np.array_equal(c2, codes) and np.array_equal(s2, d)
+    assert np.array_equal(oracle.dequantize_q8_0(c2, s2), vals.astype(np.float64))
+
+
+def test_attention_on_a_q8_0_cache_is_attention_on_its_values():
+    # rows exactly representable in q8_0 round-trip unchanged, so the attention over
+    # the quantized cache equals torch's attention over the original values
+    rng = np.random.default_rng(33)
+    n, h_q, dkq, dv = 40, 8, 64, 64
+    codes = rng.integers(-127, 128, size=(n, dkq))
+    codes[:, ::32] = -127
+    d = np.float64(2.0) ** rng.integers(-9, -5, size=(n, dkq // 32))
+    k = codes * np.repeat(d, 32, axis=1)
+    kc, ks = oracle.quantize_q8_0(k.astype(np.float32))
+    kq = oracle.dequantize_q8_0(kc, ks)
+    assert np.array_equal(kq, k)
+    q = rng.standard_normal((h_q, dkq))
+    got = oracle.attend(q, kq[:, None, :], kq[:, None, :dv], 0.125)
+    assert np.allclose(got, _sdpa(q, k[:, None, :], k[:, None, :dv], 0.125), rtol=1e-12, atol=1e-12)
+
+
 # ------------------------------------------------------------------ pipeline
 
 def _small_dims(**kw):
@@ -469,3 +573,18 @@ def test_mutants_are_caught():
     want = _sdpa(q, k, v, 0.25, b)
     assert not np.allclose(oracle.attend(q, k, v, 0.25, bias=0.25 * b), want)
     assert not np.allclose(oracle.attend(q, k, v, 0.25, bias=-b), want)
+
+    # 8. q8_0 with 128 levels, with ties to even, or with one scale per row
+    x = np.zeros(32, np.float32)
+    x[:8] = [127, 2.5, -2.5, 0.5, -0.5, 1.5, -1.5, 126.5]
+    def q8_levels128(x):
+        d = np.abs(x).max() / np.float32(128.0)
+        return np.rint(x / d).astype(int)
+    assert q8_levels128(x)[:8].tolist() != [127, 3, -3, 1, -1, 2, -2, 127]
+    assert np.rint(x[:8]).astype(int).tolist() != [127, 3, -3, 1, -1, 2, -2, 127]
+    r = np.random.default_rng(15).standard_normal(64).astype(np.float32)
+    r[40] *= 50.0
+    def q8_per_row(x):
+        d = np.abs(x).max() / np.float32(127.0)
+        return np.sign(x / d) * np.floor(np.abs(x / d) + 0.5)
+    assert not np.array_equal(q8_per_row(r)[:32], oracle.quantize_q8_0(r)[0][:32])
