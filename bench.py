@@ -131,11 +131,14 @@ class RotatingLayers:
         self.fwd(r)
 
 
-def algorithmic_bytes(case: datagen.Case) -> dict:
+def algorithmic_bytes(case: datagen.Case, kv: str = "cache") -> dict:
     """Bytes a step must read from HBM: pooled keys of every visible complete block of
-    every query, and the selected K rows (plus V rows when V is stored separately)."""
+    every query, and the selected K rows (plus V rows when V is stored separately).
+    kv="q8_0": the rows are q8_0 codes (1 byte per element) plus a 2-byte scale per
+    32 elements."""
     d = case.dims
     es = 4 if d.dtype == "f32" else 2
+    row_bytes = (lambda n: n * es) if kv == "cache" else (lambda n: n + n // 32 * 2)
     c = d.compress_ratio
     pooled = 0
     gathered = 0
@@ -145,7 +148,7 @@ def algorithmic_bytes(case: datagen.Case) -> dict:
         nb = n_vis // c
         n_sel = min(nb, d.top_k // c) * c + (n_vis - nb * c)
         pooled += nb * d.d_idx * es
-        gathered += n_sel * (d.h_kv * d.d_kq + (0 if case.v is None else d.h_kv * d.d_v)) * es
+        gathered += n_sel * row_bytes(d.h_kv * d.d_kq + (0 if case.v is None else d.h_kv * d.d_v))
     return {"pooled": pooled, "gathered": gathered, "total": pooled + gathered}
 
 
@@ -352,6 +355,51 @@ def window_report(lay: "RotatingLayers", steps: int, warmup: int, window: int = 
             "window": window, "us_per_step": round(ms * 1e3, 3), "kernel_avg_us": {"fwd_window": round(t_fwd * 1e3, 3)}}
 
 
+# ------------------------------------------------------------------ q8_0 cache
+
+def q8_report(lay: "RotatingLayers", steps: int, warmup: int) -> dict:
+    """The 128K decode step over q8_0 copies of the layer's K/V cache (quantized once on
+    the GPU from the bf16 copies): pool, score, select, attention over the q8_0 rows."""
+    d = lay.case.dims
+    R = lay.n
+    rows = lay.case.rows
+    nb = d.d_kq // 32
+    codes = torch.empty((R, rows, d.d_kq), dtype=torch.int8, device=lay.device)
+    scales = torch.empty((R, rows, nb), dtype=torch.float16, device=lay.device)
+    for r in range(R):
+        sa.sparse_attn_quantize_q8_0(lay.k[r], d.dtype, rows, d.d_kq, d.d_kq, codes[r], d.d_kq, scales[r], nb)
+    kvs = [sa.KvQ8(k=codes[r], k_ld=d.d_kq, k_head_stride=d.d_kq, k_scale=scales[r], k_scale_ld=nb,
+                   k_scale_head_stride=nb, v=codes[r], v_ld=d.d_kq, v_head_stride=d.d_kq, v_scale=scales[r],
+                   v_scale_ld=nb, v_scale_head_stride=nb) for r in range(R)]
+    torch.cuda.synchronize()
+
+    def fwd_q(k):
+        sa.sparse_attn_fwd_q8_0(lay.dims, lay.caches[k % R], kvs[k % R], lay.q, lay.q_seq, lay.sel, lay.sel_ld,
+                                lay.n_sel, lay.n_q, lay.case.scale, lay.out, lay.ws, lay.ws_bytes)
+
+    def step_q(k):
+        lay.pool(k % R)
+        lay.score(k % R)
+        lay.select(k % R)
+        fwd_q(k)
+
+    new_row = lay.k[0, rows - 1:rows]
+
+    def write_row(k):                            # the cache write of one new token (18 blocks)
+        sa.sparse_attn_quantize_q8_0(new_row, d.dtype, 1, d.d_kq, d.d_kq, codes[k % R, rows - 1:rows], d.d_kq,
+                                     scales[k % R, rows - 1:rows], nb)
+
+    ms = time_graph(step_q, steps, warmup)
+    t_fwd = time_graph(fwd_q, steps, warmup)
+    t_w = time_graph(write_row, steps, warmup)
+    ab = algorithmic_bytes(lay.case, kv="q8_0")
+    del kvs, codes, scales
+    torch.cuda.empty_cache()
+    return {"workload": "the 128K decode step over a q8_0 K/V cache (V = K[:512])", "us_per_step": round(ms * 1e3, 3),
+            "value": round(ab["total"] / (ms * 1e-3) / 1e9, 2), "unit": "GB/s", "bytes_per_step": ab,
+            "kernel_avg_us": {"fwd_q8_0": round(t_fwd * 1e3, 3), "quantize_one_row": round(t_w * 1e3, 3)}}
+
+
 # ------------------------------------------------------------------ token-level
 
 def token_level_report(steps: int, warmup: int, layers: int) -> dict:
@@ -473,6 +521,8 @@ def main() -> int:
     rec["mask_form"] = mask_form_report(lay, args.steps, args.warmup)
     log("[bench] dense window + selection")
     rec["window"] = window_report(lay, args.steps, args.warmup)
+    log("[bench] q8_0 cache")
+    rec["q8_0"] = q8_report(lay, args.steps, args.warmup)
     if not args.no_token_level:
         del lay
         torch.cuda.empty_cache()

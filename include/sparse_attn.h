@@ -233,6 +233,57 @@ int sparse_attn_fwd_window(const sa_dims* dims, const sa_cache* cache, const voi
                            const int32_t* n_sel, int32_t window, int32_t n_q, float scale, float* out,
                            void* ws, size_t ws_bytes, void* stream);
 
+/* ---- q8_0 K/V cache (pages: the qwen4exp commit series, a quantized KV cache on the
+ * QSA attention path, served with K and V caches of type q8_0).  q8_0 is ggml's
+ * block format: per 32 consecutive elements of a row one float16 scale d and 32
+ * signed 8-bit codes c; element = d * c.  Here codes and scales are separate planes
+ * (codes [rows][h_kv][d] int8, scales [rows][h_kv][d / 32] float16 bits), so a row's
+ * codes are one contiguous run.  Strides are in elements of each plane.  V may be the
+ * same planes as K (v == k, v_scale == k_scale, equal strides): V is then the first
+ * d_v elements of each K head, as in MLA.  d_kq and d_v must be multiples of 32.    */
+typedef struct sa_kv_q8_0 {
+  const int8_t*   k;        /* K codes                                                     */
+  int64_t         k_ld;     /* codes per cache row (>= (h_kv-1)*k_head_stride + d_kq)      */
+  int64_t         k_head_stride;
+  const uint16_t* k_scale;  /* K scales (float16)                                          */
+  int64_t         k_scale_ld;     /* scales per cache row (>= (h_kv-1)*stride + d_kq/32)   */
+  int64_t         k_scale_head_stride;
+  const int8_t*   v;        /* V codes                                                     */
+  int64_t         v_ld;
+  int64_t         v_head_stride;
+  const uint16_t* v_scale;  /* V scales (float16)                                          */
+  int64_t         v_scale_ld;
+  int64_t         v_scale_head_stride;
+} sa_kv_q8_0;
+
+/* Quantize rows to q8_0: for row r < n_rows and block b < n_cols / 32, with
+ * x_b = x[r*x_ld + 32b .. 32b + 31]:
+ *     d = max|x_b| / 127,  codes[r*codes_ld + 32b + e] = round(x_b[e] / d)
+ * (round half away from zero; all codes 0 when d = 0), scales[r*scales_ld + b] =
+ * float16(d).  The codes are decided in float32 (the division by 127, then 1/d, then
+ * x * (1/d), each correctly rounded).  x: device [n_rows][x_ld] of x_dtype (SA_F32,
+ * SA_F16 or SA_BF16); codes: device int8 [n_rows][codes_ld], 4-byte aligned rows;
+ * scales: device float16 [n_rows][scales_ld].  This is the cache write: a step's new
+ * K/V rows are quantized into the cache planes (for h_kv heads, view each cache row
+ * as h_kv rows when the heads are contiguous).
+ * Errors: SA_ERR_ARG (bad dtype, n_cols % 32, negative sizes, lds too small,
+ *         codes pointer or codes_ld not 4-byte aligned), SA_ERR_NULL, SA_ERR_HIP.    */
+int sparse_attn_quantize_q8_0(const void* x, int32_t x_dtype, int64_t n_rows, int32_t n_cols, int64_t x_ld,
+                              int8_t* codes, int64_t codes_ld, uint16_t* scales, int64_t scales_ld,
+                              void* stream);
+
+/* sparse_attn_fwd over a q8_0 K/V cache: K[t][g][e] = k_scale[...][e / 32] *
+ * k[...][e] (likewise V), otherwise as sparse_attn_fwd.  cache supplies the sequence
+ * layout (seq_row0, seq_len, max_len); its k and v are not read.  q is in
+ * dims->dtype.  The MLA shapes (V = K prefix, d_v 512, d_kq 512 or 576, f16/bf16
+ * queries, 16-byte aligned code rows, 4-byte aligned scale rows) run the LDS-gather
+ * MFMA kernel; everything else the generic kernel.  Workspace: that of
+ * sparse_attn_fwd.  Errors: those of sparse_attn_fwd; SA_ERR_ARG when d_kq or d_v is
+ * not a multiple of 32 or a stride is too small.                                     */
+int sparse_attn_fwd_q8_0(const sa_dims* dims, const sa_cache* cache, const sa_kv_q8_0* kv, const void* q,
+                         const int32_t* q_seq, const int32_t* sel, int64_t sel_ld, const int32_t* n_sel,
+                         int32_t n_q, float scale, float* out, void* ws, size_t ws_bytes, void* stream);
+
 /* Static description of an error code (never NULL). */
 const char* sparse_attn_strerror(int code);
 

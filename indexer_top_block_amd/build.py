@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsparse_attn.so")
-SOURCES = ["api.cpp", "pool.hip", "score.hip", "select.hip", "fwd.hip", "mask.hip"]
+SOURCES = ["api.cpp", "pool.hip", "score.hip", "select.hip", "fwd.hip", "fwd_q8.hip", "mask.hip", "quant.hip"]
 ARCH = "gfx950"
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"

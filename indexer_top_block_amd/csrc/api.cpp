@@ -188,6 +188,68 @@ int sparse_attn_mask_to_indices(const void* mask, int32_t mask_dtype, int64_t ma
                                                (hipStream_t)stream));
 }
 
+int sparse_attn_quantize_q8_0(const void* x, int32_t x_dtype, int64_t n_rows, int32_t n_cols, int64_t x_ld,
+                              int8_t* codes, int64_t codes_ld, uint16_t* scales, int64_t scales_ld, void* stream) {
+  if (!dtype_ok(x_dtype)) return SA_ERR_ARG;
+  if (n_rows < 0 || n_cols < 0 || n_cols % 32 != 0) return SA_ERR_ARG;
+  if (n_rows == 0 || n_cols == 0) return SA_OK;
+  if (!x || !codes || !scales) return SA_ERR_NULL;
+  if (x_ld < n_cols || codes_ld < n_cols || scales_ld < n_cols / 32) return SA_ERR_ARG;
+  if ((uintptr_t)codes % 4 != 0 || codes_ld % 4 != 0) return SA_ERR_ARG;
+  if (n_rows > ((int64_t)1 << 40) / (n_cols / 32)) return SA_ERR_ARG;
+  (void)hipGetLastError();
+  return hip_status(sa::launch_quantize_q8_0(x, x_dtype, n_rows, n_cols, x_ld, codes, codes_ld, scales, scales_ld,
+                                             (hipStream_t)stream));
+}
+
+int sparse_attn_fwd_q8_0(const sa_dims* dims, const sa_cache* cache, const sa_kv_q8_0* kv, const void* q,
+                         const int32_t* q_seq, const int32_t* sel, int64_t sel_ld, const int32_t* n_sel,
+                         int32_t n_q, float scale, float* out, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if ((rc = check_cache_common(dims, cache))) return rc;
+  if (!kv) return SA_ERR_NULL;
+  if (dims->d_kq % 32 != 0 || dims->d_v % 32 != 0) return SA_ERR_ARG;
+  if (n_q < 0 || (int64_t)n_q * dims->h_kv > kMaxGridY) return SA_ERR_ARG;
+  if (n_q == 0) return SA_OK;
+  if (!kv->k || !kv->k_scale || !kv->v || !kv->v_scale || !q || !q_seq || !sel || !n_sel || !out) return SA_ERR_NULL;
+  if (sel_ld < 1) return SA_ERR_ARG;
+  if (kv->k_head_stride < 0 || kv->v_head_stride < 0 || kv->k_scale_head_stride < 0 || kv->v_scale_head_stride < 0)
+    return SA_ERR_ARG;
+  const int64_t hk = dims->h_kv - 1;
+  if (dims->h_kv > 1 && (kv->k_head_stride < dims->d_kq || kv->v_head_stride < dims->d_v ||
+                         kv->k_scale_head_stride < dims->d_kq / 32 || kv->v_scale_head_stride < dims->d_v / 32))
+    return SA_ERR_ARG;
+  if (kv->k_ld < hk * kv->k_head_stride + dims->d_kq || kv->v_ld < hk * kv->v_head_stride + dims->d_v) return SA_ERR_ARG;
+  if (kv->k_scale_ld < hk * kv->k_scale_head_stride + dims->d_kq / 32 ||
+      kv->v_scale_ld < hk * kv->v_scale_head_stride + dims->d_v / 32)
+    return SA_ERR_ARG;
+  if (kv->v == kv->k && dims->d_v > dims->d_kq) return SA_ERR_ARG;
+  if (!(scale == scale)) return SA_ERR_ARG;  // NaN
+  const sa::FwdPlan plan = sa::plan_fwd(*dims, n_q);
+  void* scratch = nullptr;
+  if (plan.ws_bytes > 0) {
+    if (!ws || ws_bytes < SA_WS_STATE_BYTES + plan.ws_bytes) return SA_ERR_WORKSPACE;
+    scratch = (char*)ws + SA_WS_STATE_BYTES;
+  }
+  sa::Q8Args a;
+  a.k = kv->k;
+  a.k_ld = kv->k_ld;
+  a.k_hs = kv->k_head_stride;
+  a.ks = kv->k_scale;
+  a.ks_ld = kv->k_scale_ld;
+  a.ks_hs = kv->k_scale_head_stride;
+  a.v = kv->v;
+  a.v_ld = kv->v_ld;
+  a.v_hs = kv->v_head_stride;
+  a.vs = kv->v_scale;
+  a.vs_ld = kv->v_scale_ld;
+  a.vs_hs = kv->v_scale_head_stride;
+  (void)hipGetLastError();
+  return hip_status(sa::launch_fwd_q8(*dims, to_args(cache), a, q, q_seq, sel, sel_ld, n_sel, n_q, scale, out,
+                                      scratch, plan, (hipStream_t)stream));
+}
+
 const char* sparse_attn_strerror(int code) {
   switch (code) {
     case SA_OK: return "success";

@@ -61,6 +61,27 @@ struct FwdPlan {
   size_t ws_bytes;                         // scratch bytes (partial results), 0 when unsplit
 };
 FwdPlan plan_fwd(const sa_dims& d, int n_q);
+// A q8_0 K/V cache: int8 code planes and float16 scale planes (one scale per 32
+// codes), strides in elements.
+struct Q8Args {
+  const void* k;
+  int64_t k_ld, k_hs;
+  const void* ks;
+  int64_t ks_ld, ks_hs;
+  const void* v;
+  int64_t v_ld, v_hs;
+  const void* vs;
+  int64_t vs_ld, vs_hs;
+};
+bool fwd_q8_uses_lds(const sa_dims& d, const Q8Args& kv, const void* q);
+hipError_t launch_fwd_q8(const sa_dims& d, const CacheArgs& c, const Q8Args& kv, const void* q, const int32_t* q_seq,
+                         const int32_t* sel, int64_t sel_ld, const int32_t* n_sel, int n_q, float scale, float* out,
+                         void* ws, const FwdPlan& plan, hipStream_t stream);
+hipError_t launch_quantize_q8_0(const void* x, int x_dtype, int64_t n_rows, int n_cols, int64_t x_ld, int8_t* codes,
+                                int64_t codes_ld, void* scales, int64_t scales_ld, hipStream_t stream);
+// Merges the split partials (ws_o, ws_ml) into out; nothing when unsplit.
+hipError_t launch_combine(const sa_dims& d, int n_q, float* out, const float* ws_o, const float* ws_ml,
+                          const FwdPlan& plan, hipStream_t stream);
 FwdPlan plan_fwd_window(const sa_dims& d, int n_q, int window, size_t ws_avail);
 
 // ws: the scratch part of the workspace.

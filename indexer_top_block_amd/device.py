@@ -92,6 +92,36 @@ class DeviceLayer:
         sa.sparse_attn_fwd_window(self.dims, self.cache, self.q, self.q_seq, self.q_pos, sel, sel.shape[1], n_sel,
                                   window, self.n_q, self.scale, self.out, self.ws, self.ws_bytes, stream)
 
+    # ------------------------------------------------------------ q8_0 K/V cache
+    def quantize_kv(self, stream=None) -> None:
+        """Quantize the layer's K (and a separate V) into q8_0 planes on the GPU:
+        codes [rows][h_kv][d] int8, scales [rows][h_kv][d / 32] float16."""
+        d = self.case.dims
+        rows = self.case.rows
+        self.kq = torch.zeros((rows, d.h_kv, d.d_kq), dtype=torch.int8, device=self.device)
+        self.kqs = torch.zeros((rows, d.h_kv, d.d_kq // 32), dtype=torch.float16, device=self.device)
+        sa.sparse_attn_quantize_q8_0(self.k, d.dtype, rows * d.h_kv, d.d_kq, d.d_kq, self.kq, d.d_kq, self.kqs,
+                                     d.d_kq // 32, stream)
+        if self.alias:
+            self.vq, self.vqs = self.kq, self.kqs
+            vd = d.d_kq
+        else:
+            self.vq = torch.zeros((rows, d.h_kv, d.d_v), dtype=torch.int8, device=self.device)
+            self.vqs = torch.zeros((rows, d.h_kv, d.d_v // 32), dtype=torch.float16, device=self.device)
+            sa.sparse_attn_quantize_q8_0(self.v, d.dtype, rows * d.h_kv, d.d_v, d.d_v, self.vq, d.d_v, self.vqs,
+                                         d.d_v // 32, stream)
+            vd = d.d_v
+        self.kv_q8 = sa.KvQ8(k=self.kq, k_ld=d.h_kv * d.d_kq, k_head_stride=d.d_kq, k_scale=self.kqs,
+                             k_scale_ld=d.h_kv * d.d_kq // 32, k_scale_head_stride=d.d_kq // 32,
+                             v=self.vq, v_ld=d.h_kv * vd, v_head_stride=vd, v_scale=self.vqs,
+                             v_scale_ld=d.h_kv * vd // 32, v_scale_head_stride=vd // 32)
+
+    def fwd_q8(self, sel: Optional[torch.Tensor] = None, n_sel: Optional[torch.Tensor] = None, stream=None) -> None:
+        sel = self.sel if sel is None else sel
+        n_sel = self.n_sel if n_sel is None else n_sel
+        sa.sparse_attn_fwd_q8_0(self.dims, self.cache, self.kv_q8, self.q, self.q_seq, sel, sel.shape[1], n_sel,
+                                self.n_q, self.scale, self.out, self.ws, self.ws_bytes, stream)
+
     def step(self, stream=None) -> None:
         """One pass of the whole path: pool what is new, score, select, attend."""
         self.pool(stream=stream)

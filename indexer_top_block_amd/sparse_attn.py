@@ -36,6 +36,8 @@ EXPORTS = (
     "sparse_attn_fwd_bias",
     "sparse_attn_workspace_bytes_window",
     "sparse_attn_fwd_window",
+    "sparse_attn_quantize_q8_0",
+    "sparse_attn_fwd_q8_0",
     "sparse_attn_strerror",
     "sparse_attn_version",
 )
@@ -54,6 +56,13 @@ class SaCache(ctypes.Structure):
                 ("v", ctypes.c_void_p), ("v_ld", ctypes.c_int64), ("v_head_stride", ctypes.c_int64),
                 ("kidx", ctypes.c_void_p), ("kidx_ld", ctypes.c_int64),
                 ("kpool", ctypes.c_void_p), ("kpool_ld", ctypes.c_int64)]
+
+
+class SaKvQ8(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("k_ld", ctypes.c_int64), ("k_head_stride", ctypes.c_int64),
+                ("k_scale", ctypes.c_void_p), ("k_scale_ld", ctypes.c_int64), ("k_scale_head_stride", ctypes.c_int64),
+                ("v", ctypes.c_void_p), ("v_ld", ctypes.c_int64), ("v_head_stride", ctypes.c_int64),
+                ("v_scale", ctypes.c_void_p), ("v_scale_ld", ctypes.c_int64), ("v_scale_head_stride", ctypes.c_int64)]
 
 
 class SparseAttnError(RuntimeError):
@@ -97,6 +106,11 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.sparse_attn_workspace_bytes_window.restype = SZ
     lib.sparse_attn_fwd_window.argtypes = [dp, cp, P, P, P, P, I64, P, I32, I32, ctypes.c_float, P, P, SZ, P]
     lib.sparse_attn_fwd_window.restype = ctypes.c_int
+    kp = ctypes.POINTER(SaKvQ8)
+    lib.sparse_attn_quantize_q8_0.argtypes = [P, I32, I64, I32, I64, P, I64, P, I64, P]
+    lib.sparse_attn_quantize_q8_0.restype = ctypes.c_int
+    lib.sparse_attn_fwd_q8_0.argtypes = [dp, cp, kp, P, P, P, I64, P, I32, ctypes.c_float, P, P, SZ, P]
+    lib.sparse_attn_fwd_q8_0.restype = ctypes.c_int
     lib.sparse_attn_strerror.argtypes = [ctypes.c_int]
     lib.sparse_attn_strerror.restype = ctypes.c_char_p
     lib.sparse_attn_version.argtypes = []
@@ -137,6 +151,18 @@ class Cache:
         self.struct = SaCache(int(seq_len.numel()), int(max_len), _ptr(seq_row0), _ptr(seq_blk0), _ptr(seq_len),
                               _ptr(k), int(k_ld), int(k_head_stride), _ptr(v), int(v_ld), int(v_head_stride),
                               _ptr(kidx), int(kidx_ld), _ptr(kpool), int(kpool_ld))
+
+
+class KvQ8:
+    """Owns the ctypes sa_kv_q8_0 struct and references to the planes it points at
+    (codes int8, scales float16 -- passed as int16/float16 tensors)."""
+
+    def __init__(self, *, k, k_ld, k_head_stride, k_scale, k_scale_ld, k_scale_head_stride, v, v_ld, v_head_stride,
+                 v_scale, v_scale_ld, v_scale_head_stride):
+        self._keep = (k, k_scale, v, v_scale)
+        self.struct = SaKvQ8(_ptr(k), int(k_ld), int(k_head_stride), _ptr(k_scale), int(k_scale_ld),
+                             int(k_scale_head_stride), _ptr(v), int(v_ld), int(v_head_stride), _ptr(v_scale),
+                             int(v_scale_ld), int(v_scale_head_stride))
 
 
 def _check(fn: str, rc: int) -> None:
@@ -216,3 +242,19 @@ def sparse_attn_strerror(code: int) -> str:
 
 def sparse_attn_version() -> str:
     return load().sparse_attn_version().decode()
+
+
+def sparse_attn_quantize_q8_0(x, x_dtype, n_rows: int, n_cols: int, x_ld: int, codes, codes_ld: int, scales,
+                              scales_ld: int, stream=None) -> None:
+    code = DTYPE_CODE[x_dtype] if isinstance(x_dtype, str) else int(x_dtype)
+    _check("sparse_attn_quantize_q8_0",
+           load().sparse_attn_quantize_q8_0(_ptr(x), code, int(n_rows), int(n_cols), int(x_ld), _ptr(codes),
+                                            int(codes_ld), _ptr(scales), int(scales_ld), _stream(stream)))
+
+
+def sparse_attn_fwd_q8_0(dims: SaDims, cache: Cache, kv: KvQ8, q, q_seq, sel, sel_ld: int, n_sel, n_q: int,
+                         scale: float, out, ws=None, ws_bytes: int = 0, stream=None) -> None:
+    _check("sparse_attn_fwd_q8_0",
+           load().sparse_attn_fwd_q8_0(ctypes.byref(dims), ctypes.byref(cache.struct), ctypes.byref(kv.struct),
+                                       _ptr(q), _ptr(q_seq), _ptr(sel), int(sel_ld), _ptr(n_sel), int(n_q),
+                                       float(scale), _ptr(out), _ptr(ws), int(ws_bytes), _stream(stream)))

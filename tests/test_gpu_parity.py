@@ -482,3 +482,113 @@ def test_list_longer_than_capacity(gpu_lib):
             want = oracle.attend(case.q[qi], case.k[pos], v_rows[pos], case.scale)
             parity.check_out(out[qi], want, d.dtype, f"over-capacity q{qi} w{w}")
     say("[parity] list longer than capacity: ok")
+
+
+# --------------------------------------------------------------- q8_0 K/V cache
+
+def test_quantize_q8_0_matches_oracle(gpu_lib):
+    # codes and scales bit-exact against the oracle (both decide in float32), for
+    # every input dtype, an all-zero block, exact ties and a wide range of magnitudes
+    rng = np.random.default_rng(500)
+    for dt in ("bf16", "f16", "f32"):
+        x = rng.standard_normal((300, 96)) * np.exp(rng.uniform(-5, 4, (300, 1)))
+        x[7, 32:64] = 0.0
+        x[8, :32] = 0.0
+        x[8, :8] = [127, 2.5, -2.5, 0.5, -0.5, 1.5, -1.5, 126.5]
+        x = oracle.round_to_storage(x, dt)
+        xt = torch.from_numpy(x).to(sa.TORCH_DTYPE[dt]).cuda()
+        codes = torch.full((300, 100), 99, dtype=torch.int8, device="cuda")      # codes_ld 100: padding untouched
+        scales = torch.full((300, 4), 7.0, dtype=torch.float16, device="cuda")
+        sa.sparse_attn_quantize_q8_0(xt, dt, 300, 96, 96, codes, 100, scales, 4)
+        torch.cuda.synchronize()
+        want_c, want_s = oracle.quantize_q8_0(x)
+        got_c = codes.cpu().numpy()
+        got_s = scales.cpu().numpy().astype(np.float64)
+        assert np.array_equal(got_c[:, :96], want_c), f"{dt}: codes differ"
+        assert np.array_equal(got_s[:, :3], want_s), f"{dt}: scales differ"
+        assert (got_c[:, 96:] == 99).all() and (got_s[:, 3] == 7.0).all()
+        say(f"[parity] quantize q8_0 {dt}: bit-exact")
+
+
+def _q8_planes(case):
+    """The oracle's q8_0 planes of a case's K (and separate V), as device tensors."""
+    d = case.dims
+    kc, ks = oracle.quantize_q8_0(case.k)
+    planes = {"k": torch.from_numpy(kc).cuda(), "ks": torch.from_numpy(ks).to(torch.float16).cuda()}
+    if case.v is None:
+        planes["v"], planes["vs"], vd = planes["k"], planes["ks"], d.d_kq
+        deq_v = None
+    else:
+        vc, vs = oracle.quantize_q8_0(case.v)
+        planes["v"], planes["vs"], vd = torch.from_numpy(vc).cuda(), torch.from_numpy(vs).to(torch.float16).cuda(), d.d_v
+        deq_v = oracle.dequantize_q8_0(vc, vs)
+    deq_k = oracle.dequantize_q8_0(kc, ks)
+    kv = sa.KvQ8(k=planes["k"], k_ld=d.h_kv * d.d_kq, k_head_stride=d.d_kq, k_scale=planes["ks"],
+                 k_scale_ld=d.h_kv * d.d_kq // 32, k_scale_head_stride=d.d_kq // 32, v=planes["v"],
+                 v_ld=d.h_kv * vd, v_head_stride=vd, v_scale=planes["vs"], v_scale_ld=d.h_kv * vd // 32,
+                 v_scale_head_stride=vd // 32)
+    deq_v = deq_k[:, :, : d.d_v] if deq_v is None else deq_v
+    return kv, deq_k, deq_v
+
+
+def run_q8(case, queries=None, expect_lds=None):
+    """Selection on the GPU, then attention over the oracle's q8_0 planes, against the
+    oracle's attention over the dequantized rows (the GPU's selection and the
+    oracle's)."""
+    layer = DeviceLayer(case)
+    layer.pool()
+    layer.score()
+    layer.select()
+    torch.cuda.synchronize()
+    gpu_sel = layer.selections()
+    kv, deq_k, deq_v = _q8_planes(case)
+    layer.kv_q8 = kv
+    pools = oracle.SequencePools(case)
+    queries = list(range(case.n_q)) if queries is None else list(queries)
+    res = {qi: oracle.run_query(case, qi, pools) for qi in queries}
+    for qi in queries:
+        parity.compare_selection(gpu_sel[qi], res[qi], case)
+    want_sel = [res[qi]["positions"] if qi in res else np.zeros(0, np.int64) for qi in range(case.n_q)]
+    o_sel, o_n = parity.upload_selection(layer, want_sel)
+    worst = 0.0
+    for sel, n_sel, sel_q, tag in ((None, None, gpu_sel, "end-to-end"), (o_sel, o_n, want_sel, "fwd")):
+        layer.out.fill_(-3.0)
+        layer.fwd_q8(sel, n_sel)
+        torch.cuda.synchronize()
+        out = layer.out.cpu().numpy()
+        for qi in queries:
+            rows = int(case.row0[case.q_seq[qi]]) + np.asarray(sel_q[qi], dtype=np.int64)
+            want = oracle.attend(case.q[qi], deq_k[rows], deq_v[rows], case.scale)
+            worst = max(worst, parity.check_out(out[qi], want, case.dims.dtype, f"{case.name} q{qi} q8 {tag}"))
+    say(f"[parity] {case.name}: q8_0 attention ok  max-abs={worst:.3g}")
+    return layer
+
+
+def test_q8_mla_lds_kernel(gpu_lib):
+    # MLA with V inside K on the LDS-gather kernel: 576/512 bf16 and 512/512 f16,
+    # decode and prefill positions, multi-tile splits, a list shorter than one tile
+    for j, d in enumerate((dims(top_k=256, compress_ratio=4),
+                           dims(d_kq=512, d_v=512, top_k=512, compress_ratio=4, dtype="f16"))):
+        lens = [5000, 777, 40]
+        q_seq = [0, 0, 0, 1, 1, 2]
+        q_pos = [4999, 2500, 3, 776, 0, 39]
+        case = datagen.make_case(f"q8_mla_{j}", d, lens, q_seq, q_pos, seed=0, case_id=510 + j, std="inv_sqrt_dim",
+                                 v_separate=False)
+        run_q8(case)
+
+
+def test_q8_generic_kernel(gpu_lib):
+    # separate V, GQA, fp32 queries: the generic kernel with the q8_0 reader
+    for j, d in enumerate((dims(h_q=8, h_kv=2, d_kq=128, d_v=128, h_idx=8, top_k=96, compress_ratio=8, dtype="f16"),
+                           dims(h_q=4, h_kv=1, d_kq=64, d_v=96, h_idx=4, d_idx=64, top_k=40, compress_ratio=2,
+                                dtype="f32"))):
+        case = datagen.make_case(f"q8_generic_{j}", d, [2100, 333], [0, 0, 1], [2099, 700, 332], seed=0,
+                                 case_id=520 + j, std=0.5, v_separate=True)
+        run_q8(case)
+
+
+def test_q8_full_size_decode(gpu_lib):
+    # the 128K MLA decode step over a q8_0 cache, in the benchmark's launch configuration
+    say(f"[parity] generating workload 2: {datagen.WORKLOADS[2]}")
+    case = datagen.make_workload(2)
+    run_q8(case)

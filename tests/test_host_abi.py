@@ -200,3 +200,37 @@ def test_window_workspace_size():
     assert sa.sparse_attn_workspace_bytes_window(d, 1, 4096, 100000) > base
     assert sa.sparse_attn_workspace_bytes_window(d, 1, 4096, -1) == 0
     assert sa.sparse_attn_workspace_bytes_window(d, -1, 4096, 8) == 0
+
+
+def test_q8_entry_points_reject_bad_arguments():
+    F16 = sa.SA_F16
+    q = "sparse_attn_quantize_q8_0"
+    assert _call(q, FAKE, 9, 4, 64, 64, FAKE, 64, FAKE, 2, None) == sa.SA_ERR_ARG        # dtype
+    assert _call(q, FAKE, F16, 4, 48, 48, FAKE, 48, FAKE, 2, None) == sa.SA_ERR_ARG      # n_cols % 32
+    assert _call(q, FAKE, F16, -1, 64, 64, FAKE, 64, FAKE, 2, None) == sa.SA_ERR_ARG
+    assert _call(q, FAKE, F16, 4, 64, 63, FAKE, 64, FAKE, 2, None) == sa.SA_ERR_ARG      # x_ld
+    assert _call(q, FAKE, F16, 4, 64, 64, FAKE, 62, FAKE, 2, None) == sa.SA_ERR_ARG      # codes_ld
+    assert _call(q, FAKE, F16, 4, 64, 64, FAKE, 64, FAKE, 1, None) == sa.SA_ERR_ARG      # scales_ld
+    assert _call(q, FAKE, F16, 4, 64, 64, FAKE + 2, 64, FAKE, 2, None) == sa.SA_ERR_ARG  # codes alignment
+    assert _call(q, FAKE, F16, 4, 64, 64, FAKE, 66, FAKE, 2, None) == sa.SA_ERR_ARG      # codes_ld alignment
+    assert _call(q, None, F16, 4, 64, 64, FAKE, 64, FAKE, 2, None) == sa.SA_ERR_NULL
+    assert _call(q, None, F16, 0, 64, 64, None, 64, None, 2, None) == sa.SA_OK
+    d = _dims()
+    kv = sa.SaKvQ8(FAKE, 576, 576, FAKE, 18, 18, FAKE, 576, 576, FAKE, 18, 18)
+    f = ctypes.c_float(0.04)
+    ws = sa.sparse_attn_workspace_bytes(d, 1, 4096)
+    fq = "sparse_attn_fwd_q8_0"
+    c = ctypes.byref(_cache())
+    args = lambda kv_, dd=d, ws_=FAKE, wsb=ws: (ctypes.byref(dd), c, ctypes.byref(kv_) if kv_ is not None else None,
+                                               FAKE, FAKE, FAKE, 2051, FAKE, 1, f, FAKE, ws_, wsb, None)
+    assert _call(fq, *args(None)) == sa.SA_ERR_NULL
+    assert _call(fq, *args(kv, ws_=None, wsb=0)) == sa.SA_ERR_WORKSPACE
+    bad = sa.SaKvQ8(FAKE, 575, 576, FAKE, 18, 18, FAKE, 576, 576, FAKE, 18, 18)         # k_ld too small
+    assert _call(fq, *args(bad)) == sa.SA_ERR_ARG
+    bad = sa.SaKvQ8(FAKE, 576, 576, FAKE, 17, 18, FAKE, 576, 576, FAKE, 18, 18)         # scale ld too small
+    assert _call(fq, *args(bad)) == sa.SA_ERR_ARG
+    bad = sa.SaKvQ8(FAKE, 576, 576, None, 18, 18, FAKE, 576, 576, FAKE, 18, 18)
+    assert _call(fq, *args(bad)) == sa.SA_ERR_NULL
+    odd = _dims()
+    odd.d_kq = 520
+    assert _call(fq, *args(kv, dd=odd)) == sa.SA_ERR_ARG                                # d_kq % 32
