@@ -9,9 +9,9 @@
 // that gathers straight into LDS.
 //
 // MLA shapes (V = the first 512 elements of each K row, DKQ 512 or 576, up to 16
-// query heads, f16/bf16 queries): `fwd_q8_lds_kernel`.  Per 64-row tile each wave
-// gathers 16 rows of codes into LDS (one instruction per row, 16 bytes per lane) and
-// its rows' scales (4 bytes per lane).  The scale never enters an MFMA operand
+// query heads, f16/bf16 queries): `fwd_q8_lds_kernel`, 8 waves per workgroup.  Per
+// 64-row tile each wave gathers 8 rows of codes into LDS (one instruction per row, 16
+// bytes per lane) and those rows' scales (4 bytes per lane).  The scale never enters an MFMA operand
 // rounded: S^T = K Q^T is taken one 32-element block at a time (one
 // v_mfma_f32_16x16x32 per block, codes converted exactly to the query type) and
 // each block's product is multiplied by that row's block scale in float32.  For
@@ -52,8 +52,12 @@ __device__ __forceinline__ uint64_t shfl64(uint64_t x, int src) {
   return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
 }
 
-template <typename T, int DKQ>
-__global__ void __launch_bounds__(256, 2)
+// NW waves per workgroup (4 or 8).  With 8, two waves share each 16-row group of S
+// (one takes the first half of the q8_0 blocks, the other the second, and the
+// softmax sums the two partial tiles) and each wave owns 64 output dims, so a tile's
+// conversion work -- the bulk of its VALU time -- is spread over twice the waves.
+template <typename T, int DKQ, int NW>
+__global__ void __launch_bounds__(64 * NW, 8 / NW)
 fwd_q8_lds_kernel(const T* __restrict__ q, const int8_t* __restrict__ kq, int64_t k_ld, int64_t k_hs,
                   const f16* __restrict__ ks, int64_t ks_ld, int64_t ks_hs, const int64_t* __restrict__ seq_row0,
                   const int32_t* __restrict__ seq_len, const int32_t* __restrict__ q_seq,
@@ -66,18 +70,24 @@ fwd_q8_lds_kernel(const T* __restrict__ q, const int8_t* __restrict__ kq, int64_
   constexpr int DV = 512;
   constexpr int RT = kMfmaTile;                   // = 64: one list entry per lane
   constexpr int NBLK = DKQ / 32;                  // q8_0 blocks per K row = QK^T MFMA steps
+  constexpr int KSPLIT = NW / 4;                  // waves sharing a 16-row group of S
+  constexpr int KB = (NBLK / KSPLIT + 1) & ~1;    // blocks per such wave at most (even, so that
+                                                  // every wave's first block starts a scale dword)
   constexpr int PITCH = DKQ + 16;                 // bytes per LDS code row: 4 or 20 dwords mod 64 banks
   constexpr int NCH = DKQ / 16;                   // 16-byte chunks per code row
   constexpr int SRCW = NBLK / 2;                  // scale dwords per cache row
   constexpr int SCW = (SRCW + 1) & ~1;            // scale dwords per LDS row (even: 8-byte aligned rows)
-  constexpr int NSW = 16 * SCW;                   // scale dwords of one wave's 16 rows
-  constexpr int DVW = DV / 4;                     // output dims owned by one wave (4 q8_0 blocks)
+  constexpr int RPW = RT / NW;                    // rows gathered per wave
+  constexpr int NSW = RPW * SCW;                  // scale dwords gathered per wave
+  constexpr int DVW = DV / NW;                    // output dims owned by one wave
   constexpr int NTW = DVW / 16;                   // its 16-dim MFMA tiles
-  constexpr int SP = RT + 4;                      // pitch of the transposed score tile (floats)
+  constexpr int BPW = DVW / 32;                   // its q8_0 blocks of V
+  constexpr int SP = RT + 4;                      // pitch of the transposed score tiles (floats)
   static_assert(DKQ == 512 || DKQ == 576, "MLA shapes only");
+  static_assert(NW == 4 || NW == 8, "4 or 8 waves");
   __shared__ __attribute__((aligned(16))) int8_t kt[RT * PITCH];
   __shared__ __attribute__((aligned(16))) uint32_t sct[RT * SCW];
-  __shared__ __attribute__((aligned(16))) float st[16 * SP];     // scaled scores, [head][row]
+  __shared__ __attribute__((aligned(16))) float st[KSPLIT * 16 * SP];   // scaled partial scores, [part][head][row]
 
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
@@ -100,15 +110,19 @@ fwd_q8_lds_kernel(const T* __restrict__ q, const int8_t* __restrict__ kq, int64_
   const int8_t* kqg = kq + (int64_t)g * k_hs;
   const f16* ksg = ks + (int64_t)g * ks_hs;
 
+  const int wr = (wave % 4) * 16;                 // this wave's 16 rows of S
+  const int kb0 = (wave / 4) * KB;                // and its first q8_0 block
+  const int nkb = min(KB, NBLK - kb0);            // and its block count (wave-uniform)
+  const int dvb = wave * DVW;                     // its output dims
   const T* qbase = q + ((int64_t)i * h_q + (int64_t)g * G) * DKQ;
-  V8 qf[NBLK];
+  V8 qf[KB];
   {
-    const T* qh = qbase + (col < G ? col : 0) * DKQ + grp * 8;
+    const T* qh = qbase + (col < G ? col : 0) * DKQ + grp * 8 + kb0 * 32;
 #pragma unroll
-    for (int b = 0; b < NBLK; ++b) qf[b] = *reinterpret_cast<const V8*>(qh + b * 32);
+    for (int b = 0; b < KB; ++b) qf[b] = b < nkb ? *reinterpret_cast<const V8*>(qh + b * 32) : V8{};
     if (col >= G) {
 #pragma unroll
-      for (int b = 0; b < NBLK; ++b) qf[b] = V8{};
+      for (int b = 0; b < KB; ++b) qf[b] = V8{};
     }
   }
   float m = -INFINITY, lsum = 0.f;
@@ -124,13 +138,13 @@ fwd_q8_lds_kernel(const T* __restrict__ q, const int8_t* __restrict__ kq, int64_
     *sp = row >= 0 ? (uint64_t)(ksg + row * ks_ld) : (uint64_t)kQ8ZeroRow;
     return row >= 0 ? (uint64_t)(kqg + row * k_ld) : (uint64_t)kQ8ZeroRow;
   };
-  // Wave w gathers the codes of rows 16w .. 16w+15 (one instruction per row, NCH
-  // lanes of 16 bytes) and their scales (SRCW dwords per row; the padding dword of an
-  // LDS row repeats the last one).
+  // Wave w gathers the codes of rows RPW w .. RPW w + RPW - 1 (one instruction per
+  // row, NCH lanes of 16 bytes) and their scales (SRCW dwords per row; the padding
+  // dword of an LDS row repeats the last one).
   auto issue = [&](uint64_t kp, uint64_t sp) {
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int r = wave * 16 + u;
+    for (int u = 0; u < RPW; ++u) {
+      const int r = wave * RPW + u;
       const uint64_t base = (uint64_t)readlane64((int64_t)kp, r);
       if (lane < NCH)
         __builtin_amdgcn_global_load_lds((const void*)(base + lane * 16), (lds_void*)&kt[r * PITCH], 16, 0, 0);
@@ -138,46 +152,45 @@ fwd_q8_lds_kernel(const T* __restrict__ q, const int8_t* __restrict__ kq, int64_
 #pragma unroll
     for (int u = 0; u < (NSW + 63) / 64; ++u) {
       const int f = u * 64 + lane;
-      const int rl = min(f / SCW, 15);
+      const int rl = min(f / SCW, RPW - 1);
       const int dw = min(f % SCW, SRCW - 1);
-      const uint64_t sbase = shfl64(sp, wave * 16 + rl);
+      const uint64_t sbase = shfl64(sp, wave * RPW + rl);
       if (f < NSW)
-        __builtin_amdgcn_global_load_lds((const void*)(sbase + dw * 4), (lds_void*)&sct[wave * 16 * SCW + u * 64], 4,
-                                         0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(sbase + dw * 4), (lds_void*)&sct[wave * NSW + u * 64], 4, 0,
+                                         0);
     }
   };
 
-  const int wr = wave * 16;                       // this wave's 16 rows of S
-  const int dvb = wave * DVW;                     // this wave's output dims
   auto compute = [&](uint64_t valid) {
     {
-      // S^T rows wr .. wr+15: lane (col, grp) gets rows wr + 4 grp + j of head col
+      // partial S^T over this wave's blocks: lane (col, grp) gets rows wr + 4 grp + j
+      // every LDS read of the tile's part first (codes of the wave's blocks, scale
+      // dwords of its 4 rows per lane), then the products
       f32x4 s = {0.f, 0.f, 0.f, 0.f};
-      const int8_t* arow = &kt[(wr + col) * PITCH + grp * 8];
-      const uint32_t* srow = &sct[(wr + 4 * grp) * SCW];
+      const int8_t* arow = &kt[(wr + col) * PITCH + grp * 8 + kb0 * 32];
+      const uint32_t* srow = &sct[(wr + 4 * grp) * SCW + kb0 / 2];
+      uint2 cw[KB];
+      uint32_t sw[4][KB / 2];
 #pragma unroll
-      for (int b2 = 0; b2 < NBLK / 2; ++b2) {
-        float d0[4], d1[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t w = srow[j * SCW + b2];
-          d0[j] = half_lo(w);
-          d1[j] = half_hi(w);
-        }
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int b = 2 * b2 + h;
-          const uint2 cw = *reinterpret_cast<const uint2*>(arow + b * 32);
-          const f32x4 part = mfma16x16x32<T>(codes_to<T>(cw.x, cw.y), qf[b], f32x4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-          for (int j = 0; j < 4; ++j) s[j] += (h ? d1[j] : d0[j]) * part[j];
-        }
-      }
-      f32x4 x;
+      for (int b = 0; b < KB; ++b)
+        if (b < nkb) cw[b] = *reinterpret_cast<const uint2*>(arow + b * 32);
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        x[j] = ((valid >> (wr + 4 * grp + j)) & 1ull) ? s[j] * scale_log2 : -INFINITY;
-      *reinterpret_cast<f32x4*>(st + col * SP + wr + 4 * grp) = x;
+#pragma unroll
+        for (int u = 0; u < KB / 2; ++u)
+          if (2 * u < nkb) sw[j][u] = srow[j * SCW + u];
+#pragma unroll
+      for (int b = 0; b < KB; ++b) {
+        if (b < nkb) {
+          const f32x4 part = mfma16x16x32<T>(codes_to<T>(cw[b].x, cw[b].y), qf[b], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const uint32_t w = sw[j][b / 2];
+            s[j] += ((b & 1) ? half_hi(w) : half_lo(w)) * part[j];
+          }
+        }
+      }
+      *reinterpret_cast<f32x4*>(st + ((wave / 4) * 16 + col) * SP + wr + 4 * grp) = s * scale_log2;
     }
     lds_barrier();
     // Lane (col, grp) takes head col's rows 32 kk + 8 grp + j, j < 8: the B layout of
@@ -185,13 +198,22 @@ fwd_q8_lds_kernel(const T* __restrict__ q, const int8_t* __restrict__ kq, int64_
     float xs[2][8];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      const f32x4 a = *reinterpret_cast<const f32x4*>(st + col * SP + 32 * kk + 8 * grp);
-      const f32x4 b = *reinterpret_cast<const f32x4*>(st + col * SP + 32 * kk + 8 * grp + 4);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        xs[kk][j] = a[j];
-        xs[kk][4 + j] = b[j];
+      for (int j = 0; j < 8; ++j) xs[kk][j] = 0.f;
+#pragma unroll
+      for (int part = 0; part < KSPLIT; ++part) {
+        const float* src = st + (part * 16 + col) * SP + 32 * kk + 8 * grp;
+        const f32x4 a = *reinterpret_cast<const f32x4*>(src);
+        const f32x4 b = *reinterpret_cast<const f32x4*>(src + 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          xs[kk][j] += a[j];
+          xs[kk][4 + j] += b[j];
+        }
       }
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (!((valid >> (32 * kk + 8 * grp + j)) & 1ull)) xs[kk][j] = -INFINITY;
     }
     float mx = -INFINITY;
 #pragma unroll
@@ -219,28 +241,31 @@ fwd_q8_lds_kernel(const T* __restrict__ q, const int8_t* __restrict__ kq, int64_
     for (int nt = 0; nt < NTW; ++nt) o[nt] *= alpha;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      // the scales of this lane's 8 rows for the wave's 4 blocks of V
-      uint2 sw[8];
+      // the scales of this lane's 8 rows for the wave's BPW blocks of V
+      uint32_t sw[8][BPW / 2];
 #pragma unroll
       for (int j = 0; j < 8; ++j)
-        sw[j] = *reinterpret_cast<const uint2*>(&sct[(32 * kk + 8 * grp + j) * SCW + 2 * wave]);
+#pragma unroll
+        for (int u = 0; u < BPW / 2; ++u) sw[j][u] = sct[(32 * kk + 8 * grp + j) * SCW + dvb / 64 + u];
       // V^T codes: in each 16-lane group lane c reads row 32 kk + 8 grp + c / 2,
       // bytes 8 (c % 2) .. of the 16-dim tile; lane i then holds dim i of the 8 rows
       const int8_t* vrow = &kt[(32 * kk + 8 * grp + (col >> 1)) * PITCH + dvb + 8 * (col & 1)];
+      i32x2 vc[NTW];
 #pragma unroll
-      for (int bb = 0; bb < 4; ++bb) {
+      for (int nt = 0; nt < NTW; ++nt) vc[nt] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(vrow + nt * 16));
+#pragma unroll
+      for (int bb = 0; bb < BPW; ++bb) {
         bf16x8 pb;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const uint32_t w = (bb < 2) ? sw[j].x : sw[j].y;
+          const uint32_t w = sw[j][bb / 2];
           const float d = (bb & 1) ? half_hi(w) : half_lo(w);
           pb[j] = (bf16)(p[kk][j] * d);
         }
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int nt = 2 * bb + h;
-          const i32x2 cw = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(vrow + nt * 16));
-          o[nt] = mfma16x16x32<bf16>(codes_to<bf16>((uint32_t)cw.x, (uint32_t)cw.y), pb, o[nt]);
+          o[nt] = mfma16x16x32<bf16>(codes_to<bf16>((uint32_t)vc[nt].x, (uint32_t)vc[nt].y), pb, o[nt]);
         }
       }
     }
@@ -289,6 +314,11 @@ fwd_q8_lds_kernel(const T* __restrict__ q, const int8_t* __restrict__ kq, int64_
 
 // ---------------------------------------------------------------------------- host
 
+#ifndef SA_Q8_WAVES
+#define SA_Q8_WAVES 8
+#endif
+constexpr int kQ8Waves = SA_Q8_WAVES;
+
 static bool aligned_to(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
 bool fwd_q8_uses_lds(const sa_dims& d, const Q8Args& kv, const void* q) {
@@ -308,10 +338,10 @@ static void launch_q8_lds_t(const sa_dims& d, const CacheArgs& c, const Q8Args& 
                             float scale_log2, float* out, float* ws_o, float* ws_ml, const FwdPlan& plan,
                             hipStream_t stream) {
   dim3 grid(plan.n_split, n_q * d.h_kv);
-  hipLaunchKernelGGL((fwd_q8_lds_kernel<T, DKQ>), grid, dim3(256), 0, stream, (const T*)q, (const int8_t*)kv.k,
-                     kv.k_ld, kv.k_hs, (const f16*)kv.ks, kv.ks_ld, kv.ks_hs, c.seq_row0, c.seq_len, q_seq, sel,
-                     sel_ld, n_sel, plan.list_max, d.h_q, d.h_kv, scale_log2, plan.n_split, plan.rows_per_split, out,
-                     ws_o, ws_ml);
+  hipLaunchKernelGGL((fwd_q8_lds_kernel<T, DKQ, kQ8Waves>), grid, dim3(64 * kQ8Waves), 0, stream, (const T*)q,
+                     (const int8_t*)kv.k, kv.k_ld, kv.k_hs, (const f16*)kv.ks, kv.ks_ld, kv.ks_hs, c.seq_row0,
+                     c.seq_len, q_seq, sel, sel_ld, n_sel, plan.list_max, d.h_q, d.h_kv, scale_log2, plan.n_split,
+                     plan.rows_per_split, out, ws_o, ws_ml);
 }
 
 template <typename T>
