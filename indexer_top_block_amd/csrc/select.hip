@@ -621,15 +621,24 @@ select_wide_kernel(const float* __restrict__ scores, int64_t scores_ld, const in
   // padding keys back out of bin 0, and a prefix of 0 (the only one they can match)
   // never takes its bin whole, so they are never kept.
   const int n_pad = KPT * kWideThreads - nb;
+  uint32_t all = 0xffffffffu;
 #pragma unroll
-  for (int j = 0; j < KPT; ++j) key[j] = (j * kWideThreads + tid < nb) ? key[j] : 0u;
-  __syncthreads();
+  for (int j = 0; j < KPT; ++j) {
+    const bool ok = j * kWideThreads + tid < nb;
+    all &= ok ? key[j] : 0xffffffffu;
+    key[j] = ok ? key[j] : 0u;
+  }
+  // When every key of the row has its top bit set (no negative scores: the usual
+  // case, as block scores are sums of rectified products), that bit tells nothing
+  // and the digits start one bit lower, over twice the bins the keys fall into.
+  const int top = __syncthreads_and((int)(all >> 31));
+  const int s1 = 21 - top, s2 = 10 - top;            // digits: [s1, s1+11), [s2, s1), [0, s2)
 
-  // ---- pass 1: top 11 bits, 8 privatised copies -----------------------------------
+  // ---- pass 1: the top digit, 8 privatised copies ----------------------------------
   {
     uint32_t* mine = sm.h1 + (lane & (kWideCopies - 1)) * kWideStride;
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) atomicAdd(&mine[key[j] >> 21], 1u);
+    for (int j = 0; j < KPT; ++j) atomicAdd(&mine[(key[j] >> s1) & 2047u], 1u);
   }
   __syncthreads();
   {
@@ -644,9 +653,11 @@ select_wide_kernel(const float* __restrict__ scores, int64_t scores_ld, const in
     if (tid == 0) cnt[0] -= (uint32_t)n_pad;
     wide_pick<2>(cnt, k_blk, sm);
   }
-  uint32_t prefix = (uint32_t)sm.pick[0];
+  // prefix = key >> shift of the keys still in the running (the padding's 0 is below
+  // every such prefix when top is set)
+  uint32_t prefix = ((uint32_t)top << 11) | (uint32_t)sm.pick[0];
   int k_rem = k_blk - sm.pick[1];
-  int width = 11;                                    // bits of the key the prefix fixes
+  int shift = s1;
   bool whole = sm.pick[2] == k_rem && prefix != 0u;
   __syncthreads();                                   // pick[] is rewritten below
   // ---- pass 2: next 11 bits among keys in the bin ---------------------------------
@@ -654,28 +665,28 @@ select_wide_kernel(const float* __restrict__ scores, int64_t scores_ld, const in
     sm.h1[tid] = 0u;                                 // copy 0 serves pass 3
 #pragma unroll
     for (int j = 0; j < KPT; ++j)
-      if ((key[j] >> 21) == prefix) atomicAdd(&sm.h2[(key[j] >> 10) & 2047u], 1u);
+      if ((key[j] >> s1) == prefix) atomicAdd(&sm.h2[(key[j] >> s2) & 2047u], 1u);
     __syncthreads();
     uint32_t cnt[2] = {sm.h2[tid * 2], sm.h2[tid * 2 + 1]};
     if (tid == 0 && prefix == 0u) cnt[0] -= (uint32_t)n_pad;
     wide_pick<2>(cnt, k_rem, sm);
     prefix = (prefix << 11) | (uint32_t)sm.pick[0];
     k_rem -= sm.pick[1];
-    width = 22;
+    shift = s2;
     whole = sm.pick[2] == k_rem && prefix != 0u;
     __syncthreads();
     // ---- pass 3: last 10 bits ------------------------------------------------------
     if (!whole) {
 #pragma unroll
       for (int j = 0; j < KPT; ++j)
-        if ((key[j] >> 10) == prefix) atomicAdd(&sm.h1[key[j] & 1023u], 1u);
+        if ((key[j] >> s2) == prefix) atomicAdd(&sm.h1[key[j] & ((1u << s2) - 1u)], 1u);
       __syncthreads();
       uint32_t cnt1[1] = {sm.h1[tid]};
       if (tid == 0 && prefix == 0u) cnt1[0] -= (uint32_t)n_pad;
       wide_pick<1>(cnt1, k_rem, sm);
-      prefix = (prefix << 10) | (uint32_t)sm.pick[0];
+      prefix = (prefix << s2) | (uint32_t)sm.pick[0];
       k_rem -= sm.pick[1];
-      width = 32;
+      shift = 0;
       whole = sm.pick[2] == k_rem && prefix != 0u;
       __syncthreads();
     }
@@ -684,7 +695,6 @@ select_wide_kernel(const float* __restrict__ scores, int64_t scores_ld, const in
   // Above the prefix, or inside its bin when the bin is taken whole, always kept;
   // otherwise the keys equal to the prefix go to the tie bitmap.  Padding keys are 0:
   // never above a prefix, and equal only to a prefix of 0, which is never whole.
-  const int shift = 32 - width;
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
     const int idx = j * kWideThreads + tid;
