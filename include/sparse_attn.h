@@ -146,6 +146,18 @@ int sparse_attn_score(const sa_dims* dims, const sa_cache* cache, const void* qi
                       const int32_t* q_seq, const int32_t* q_pos, int32_t n_q,
                       float* scores, int64_t scores_ld, void* stream);
 
+/* sparse_attn_pool followed by sparse_attn_score, with the same arguments and the
+ * same results (kpool, n_pooled_out and scores bit for bit), in one launch where
+ * the decode scoring kernel applies (f16/bf16, h_idx a multiple of 32 up to 128,
+ * d_idx 64/128/256, fewer than 64 query tokens, aligned rows, n_pooled_in and
+ * n_pooled_out distinct): the workgroups that score a new block pool it from the raw
+ * keys themselves, while others write the cache.  Otherwise it makes the two calls.
+ * Errors: those of sparse_attn_pool and sparse_attn_score.                           */
+int sparse_attn_pool_score(const sa_dims* dims, const sa_cache* cache, const int32_t* n_pooled_in,
+                           int32_t* n_pooled_out, int32_t max_new_blocks, const void* qidx,
+                           const int32_t* q_seq, const int32_t* q_pos, int32_t n_q, float* scores,
+                           int64_t scores_ld, void* stream);
+
 /* Block selection (pages: keep a budget of the best blocks plus the tail; exactly
  * dense below top_k + c - 1 tokens; block scores are expanded to tokens and the cut
  * lands on a block boundary).  For query token i with K_blk = top_k / c:

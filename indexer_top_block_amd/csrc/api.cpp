@@ -103,6 +103,28 @@ int sparse_attn_score(const sa_dims* dims, const sa_cache* cache, const void* qi
       sa::launch_score(*dims, to_args(cache), qidx, q_seq, q_pos, n_q, scores, scores_ld, (hipStream_t)stream));
 }
 
+int sparse_attn_pool_score(const sa_dims* dims, const sa_cache* cache, const int32_t* n_pooled_in,
+                           int32_t* n_pooled_out, int32_t max_new_blocks, const void* qidx, const int32_t* q_seq,
+                           const int32_t* q_pos, int32_t n_q, float* scores, int64_t scores_ld, void* stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if ((rc = check_cache_common(dims, cache))) return rc;
+  if (!cache->seq_blk0 || !cache->kidx || !cache->kpool || !n_pooled_in || !n_pooled_out) return SA_ERR_NULL;
+  if (max_new_blocks < 0 || cache->kidx_ld < dims->d_idx || cache->kpool_ld < dims->d_idx) return SA_ERR_ARG;
+  if (cache->n_seq > kMaxGridY) return SA_ERR_ARG;
+  if (n_q < 0 || n_q > kMaxGridY) return SA_ERR_ARG;
+  if (n_q > 0) {
+    if (!qidx || !q_seq || !q_pos || !scores) return SA_ERR_NULL;
+    if (scores_ld < (int64_t)(cache->max_len / dims->compress_ratio) || scores_ld < 0) return SA_ERR_ARG;
+  }
+  (void)hipGetLastError();
+  const sa::CacheArgs a = to_args(cache);
+  if (n_q == 0)
+    return hip_status(sa::launch_pool(*dims, a, n_pooled_in, n_pooled_out, max_new_blocks, (hipStream_t)stream));
+  return hip_status(sa::launch_pool_score(*dims, a, n_pooled_in, n_pooled_out, max_new_blocks, qidx, q_seq, q_pos,
+                                          n_q, scores, scores_ld, (hipStream_t)stream));
+}
+
 int sparse_attn_select(const sa_dims* dims, const sa_cache* cache, const float* scores, int64_t scores_ld,
                        const int32_t* q_seq, const int32_t* q_pos, int32_t n_q, int32_t* sel, int64_t sel_ld,
                        int32_t* n_sel, void* ws, size_t ws_bytes, void* stream) {

@@ -31,9 +31,7 @@ pool_kernel(const T* __restrict__ kidx, int64_t kidx_ld, T* __restrict__ kpool, 
     const int64_t b = start + e / d_idx;
     const int d = (int)(e % d_idx);
     const T* src = kidx + (row0 + b * c) * kidx_ld + d;
-    float acc = 0.f;
-    for (int i = 0; i < c; ++i) acc += (float)src[(int64_t)i * kidx_ld];
-    kpool[(blk0 + b) * kpool_ld + d] = (T)(acc / den);
+    kpool[(blk0 + b) * kpool_ld + d] = (T)(pool_sum(src, kidx_ld, c) / den);
   }
   if (update_here) {  // one workgroup per sequence: every thread has read `start`
     __syncthreads();

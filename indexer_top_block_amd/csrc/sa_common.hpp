@@ -79,6 +79,42 @@ __device__ __forceinline__ int block_exclusive_scan(int x, int* scratch, int* to
   return base + inc - x;
 }
 
+// The pooling sum of one element over a block's c raw rows (row stride ld): float
+// adds in row order.  Rows are loaded 8 at a time (clamped, not guarded), so a block
+// of up to 8 rows costs one memory round trip.
+template <typename T>
+__device__ __forceinline__ float pool_sum(const T* src, int64_t ld, int c) {
+  float acc = 0.f;
+  for (int r0 = 0; r0 < c; r0 += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = (float)src[(int64_t)min(r0 + u, c - 1) * ld];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (r0 + u < c) acc += v[u];
+  }
+  return acc;
+}
+
+// The same for 8 consecutive elements (one 16-byte load per row; src 16-byte aligned).
+template <typename T>
+__device__ __forceinline__ void pool_sum8(const T* src, int64_t ld, int c, float (&acc)[8]) {
+  typedef typename vec8<T>::type V8;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  for (int r0 = 0; r0 < c; r0 += 8) {
+    V8 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const V8*>(src + (int64_t)min(r0 + u, c - 1) * ld);
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (r0 + u < c) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += (float)v[u][e];
+      }
+  }
+}
+
 // 2^x with the hardware exponential (v_exp_f32); exp2(-inf) = 0.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

@@ -31,6 +31,13 @@ hipError_t launch_pool(const sa_dims& d, const CacheArgs& c, const int32_t* n_po
 
 hipError_t launch_score(const sa_dims& d, const CacheArgs& c, const void* qidx, const int32_t* q_seq,
                         const int32_t* q_pos, int n_q, float* scores, int64_t scores_ld, hipStream_t stream);
+// sparse_attn_pool then sparse_attn_score, in one launch when the decode scoring
+// kernel applies (else the two launches).
+hipError_t launch_pool_score(const sa_dims& d, const CacheArgs& c, const int32_t* n_in, int32_t* n_out, int max_new,
+                             const void* qidx, const int32_t* q_seq, const int32_t* q_pos, int n_q, float* scores,
+                             int64_t scores_ld, hipStream_t stream);
+bool pool_score_fused(const sa_dims& d, const CacheArgs& c, const void* qidx, int n_q, const int32_t* n_in,
+                      const int32_t* n_out);
 
 // Workspace layout shared by sparse_attn_select and sparse_attn_fwd:
 //   [0, SA_WS_STATE_BYTES)   state -- zero before the first call, left zero by every call

@@ -41,13 +41,56 @@ constexpr int kScoreWaves = 4;        // waves per workgroup
 constexpr int kScoreTile = 32;        // blocks per wave tile (MFMA N)
 
 // grid = (ceil(max_blocks / (4 * 32)), n_q); wave w of workgroup x scores blocks
-// [(x*4 + w) * 32, +32) of query blockIdx.y.
-template <typename T, int MT, int D>
+// [(x*4 + w) * 32, +32) of query blockIdx.y (with pooling, the grid is one-dimensional
+// and x, y come from the workgroup index).
+// With pooling (POOL), the launch also does sparse_attn_pool's work: rows y >= n_q
+// of the grid pool sequence y - n_q's new blocks into the cache exactly as the pool
+// kernel does, and a scoring wave takes the pooled keys of new blocks in its range
+// -- blocks [n_pooled_in[s], end_s), which the cache does not hold yet -- from the
+// raw keys itself, with the same arithmetic (float sum in index order, divided by c,
+// rounded to the cache type), instead of from the cache.  The two kinds of
+// workgroups share nothing, so the result is that of pool followed by score.
+template <typename T>
+struct PoolArgs {
+  const T* kidx;
+  int64_t kidx_ld;
+  T* kpool;                           // written by the pooling workgroups only
+  const int64_t* seq_row0;
+  const int32_t* n_in;
+  int32_t* n_out;                     // not n_in (the host checks)
+  int max_new;
+  int pool_wgs, n_seq;                // pooling workgroups per sequence; sequences
+  int gx;                             // scoring workgroups per query
+};
+
+template <typename T, int MT, int D, bool POOL>
 __global__ void __launch_bounds__(256)
 score_mfma_kernel(const T* __restrict__ qidx, const T* __restrict__ kpool, int64_t kpool_ld,
                   const int64_t* __restrict__ seq_blk0, const int32_t* __restrict__ seq_len,
                   const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos, int c,
-                  float* __restrict__ scores, int64_t scores_ld) {
+                  float* __restrict__ scores, int64_t scores_ld, PoolArgs<T> pa) {
+  int wx = blockIdx.x, wy = blockIdx.y;             // this workgroup's block range and query
+  if constexpr (POOL) {
+    // one-dimensional grid, the pooling workgroups first (so that they start first)
+    const int id = blockIdx.x, n_pool = pa.pool_wgs * pa.n_seq;
+    if (id < n_pool) {                               // a pooling workgroup
+      const int s = id / pa.pool_wgs, px = id % pa.pool_wgs;
+      const int start = max(pa.n_in[s], 0);
+      const int end = (int)min((long long)(max(seq_len[s], 0) / c), (long long)start + pa.max_new);
+      const long long total = (long long)max(end - start, 0) * D;
+      const int64_t row0 = pa.seq_row0[s], blk0 = seq_blk0[s];
+      for (long long e = (long long)px * 256 + threadIdx.x; e < total; e += (long long)pa.pool_wgs * 256) {
+        const int64_t b = start + e / D;
+        const int d = (int)(e % D);
+        const T* src = pa.kidx + (row0 + b * c) * pa.kidx_ld + d;
+        pa.kpool[(blk0 + b) * kpool_ld + d] = (T)(pool_sum(src, pa.kidx_ld, c) / (float)c);
+      }
+      if (px == 0 && threadIdx.x == 0) pa.n_out[s] = end;
+      return;
+    }
+    wx = (id - n_pool) % pa.gx;
+    wy = (id - n_pool) / pa.gx;
+  }
   typedef typename vec8<T>::type V8;
   constexpr int KS = D / 16;          // MFMA steps over the indexer dim (8 per lane half)
   constexpr int QP = D + 8;           // LDS pitch of a staged head row (elements)
@@ -55,7 +98,7 @@ score_mfma_kernel(const T* __restrict__ qidx, const T* __restrict__ kpool, int64
   constexpr int QLD = (QCH + 255) / 256;              // per thread
   __shared__ __attribute__((aligned(16))) T qs[MT * 32 * QP];
   __shared__ __attribute__((aligned(16))) T ks[kScoreWaves * kScoreTile * D];
-  const int i = blockIdx.y;
+  const int i = wy;
   const int tid = threadIdx.x;
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
@@ -71,9 +114,13 @@ score_mfma_kernel(const T* __restrict__ qidx, const T* __restrict__ kpool, int64
     const int e = min(tid + 256 * j, QCH - 1);
     qreg[j] = *reinterpret_cast<const V8*>(qrow + (int64_t)e * 8);
   }
-  const SeqMeta sm = seq_meta(q_seq, seq_len, nullptr, seq_blk0, i);
+  const SeqMeta sm = seq_meta(q_seq, seq_len, POOL ? pa.seq_row0 : nullptr, seq_blk0, i);
   const int nb = visible_tokens(sm.len, q_pos[i]) / c;
-  const int b_base = (blockIdx.x * kScoreWaves + wave) * kScoreTile;
+  const int b_base = (wx * kScoreWaves + wave) * kScoreTile;
+  // POOL: the sequence's pooled count, read with its metadata (sequence 0's at once,
+  // like the rest of the metadata); used only after the gathers are issued
+  int n_in_s = 0;
+  if constexpr (POOL) n_in_s = sm.s == 0 ? pa.n_in[0] : pa.n_in[sm.s];
 
   // Pooled keys: each wave gathers its 32 keys straight into its own LDS region,
   // four whole keys per instruction (fully coalesced), clamped into the visible
@@ -95,6 +142,24 @@ score_mfma_kernel(const T* __restrict__ qidx, const T* __restrict__ kpool, int64
       __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(kw + j * kWave * 8), 16, 0, 0);
     }
   }
+  // POOL: the first KPI new blocks' raw rows, chunk lane % CH of block p_lo + lane / CH
+  // (more new blocks in the range are pooled in further rounds below)
+  // (issued now, summed after the barrier, so that the workgroup does not wait for
+  // them before it stages the query)
+  int p_lo = 0, p_hi = 0;                            // new blocks of this wave's range
+  V8 raw[8];
+  if constexpr (POOL) {
+    const int start = max(n_in_s, 0);
+    const int end = (int)min((long long)(max(sm.len, 0) / c), (long long)start + pa.max_new);
+    p_lo = max(b_base, start);
+    p_hi = min(min(b_base + kScoreTile, end), nb);
+    if (p_lo < p_hi) {
+      const int pb = min(p_lo + lane / CH, p_hi - 1);
+      const T* src = pa.kidx + (sm.row0 + (int64_t)pb * c) * pa.kidx_ld + (lane % CH) * 8;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) raw[u] = *reinterpret_cast<const V8*>(src + (int64_t)min(u, c - 1) * pa.kidx_ld);
+    }
+  }
 #pragma unroll
   for (int j = 0; j < QLD; ++j) {
     const int e = tid + 256 * j;
@@ -108,6 +173,33 @@ score_mfma_kernel(const T* __restrict__ qidx, const T* __restrict__ kpool, int64
 
   // B operand: lane (n, hf) takes key n, dims hf*D/2 + st*8 .. +8 (chunk hf*CH/2 + st).
   __builtin_amdgcn_s_waitcnt(0);                     // this wave's keys are in LDS
+  if constexpr (POOL) {
+    // new blocks: their pooled keys replace the cache rows just gathered, KPI per round
+    for (int g0 = p_lo; g0 < p_hi; g0 += KPI) {
+      const int pb = g0 + lane / CH;
+      float pacc[8];
+      if (g0 > p_lo || c > 8) {
+        pool_sum8<T>(pa.kidx + (sm.row0 + (int64_t)min(pb, p_hi - 1) * c) * pa.kidx_ld + (lane % CH) * 8,
+                     pa.kidx_ld, c, pacc);
+      } else {                                       // the first round's rows, loaded above
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pacc[e] = 0.f;
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (u < c) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pacc[e] += (float)raw[u][e];
+          }
+      }
+      if (pb < p_hi) {
+        V8 pv;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pv[e] = (T)(pacc[e] / (float)c);
+        const int kk = pb - b_base, q = lane % CH;
+        *reinterpret_cast<V8*>(kw + kk * D + ((q ^ (kk & (CH - 1))) * 8)) = pv;
+      }
+    }
+  }
   V8 kb[KS];
 #pragma unroll
   for (int st = 0; st < KS; ++st)
@@ -344,9 +436,27 @@ static void launch_mfma(const sa_dims& d, const CacheArgs& c, const void* qidx, 
   const long long per_wg = kScoreWaves * kScoreTile;
   dim3 grid((unsigned)((max_blocks + per_wg - 1) / per_wg), (unsigned)n_q);
   if (grid.x == 0) return;
-  hipLaunchKernelGGL((score_mfma_kernel<T, MT, D>), grid, dim3(256), 0, stream, (const T*)qidx,
+  hipLaunchKernelGGL((score_mfma_kernel<T, MT, D, false>), grid, dim3(256), 0, stream, (const T*)qidx,
                      (const T*)c.kpool, c.kpool_ld, c.seq_blk0, c.seq_len, q_seq, q_pos, d.compress_ratio, scores,
-                     scores_ld);
+                     scores_ld, PoolArgs<T>{});
+}
+
+template <typename T, int MT, int D>
+static void launch_pool_score_t(const sa_dims& d, const CacheArgs& c, const int32_t* n_in, int32_t* n_out,
+                                int max_new, const void* qidx, const int32_t* q_seq, const int32_t* q_pos, int n_q,
+                                float* scores, int64_t scores_ld, hipStream_t stream) {
+  const long long max_blocks = (long long)c.max_len / d.compress_ratio;
+  const long long per_wg = kScoreWaves * kScoreTile;
+  const long long gx = (max_blocks + per_wg - 1) / per_wg;
+  const long long blocks = max_new < max_blocks ? max_new : max_blocks;
+  long long pool_wgs = (blocks * d.d_idx + 255) / 256;
+  pool_wgs = pool_wgs < 1 ? 1 : (pool_wgs > 2048 ? 2048 : pool_wgs);
+  const dim3 grid((unsigned)(pool_wgs * c.n_seq + gx * n_q));
+  const PoolArgs<T> pa{(const T*)c.kidx, c.kidx_ld, (T*)c.kpool, c.seq_row0, n_in, n_out, max_new,
+                       (int)pool_wgs, c.n_seq, (int)gx};
+  hipLaunchKernelGGL((score_mfma_kernel<T, MT, D, true>), grid, dim3(256), 0, stream, (const T*)qidx,
+                     (const T*)c.kpool, c.kpool_ld, c.seq_blk0, c.seq_len, q_seq, q_pos, d.compress_ratio, scores,
+                     scores_ld, pa);
 }
 
 template <typename T, int MT>
@@ -379,6 +489,45 @@ static void launch_valu(const sa_dims& d, const CacheArgs& c, const void* qidx, 
   hipLaunchKernelGGL(score_valu_kernel<T>, grid, dim3(256), 0, stream, (const T*)qidx, (const T*)c.kpool,
                      c.kpool_ld, c.seq_blk0, c.seq_len, q_seq, q_pos, d.compress_ratio, d.h_idx, d.d_idx, scores,
                      scores_ld);
+}
+
+bool pool_score_fused(const sa_dims& d, const CacheArgs& c, const void* qidx, int n_q, const int32_t* n_in,
+                      const int32_t* n_out) {
+  if (!score_uses_mfma(d, c, qidx) || n_q <= 0 || n_q >= kGemmMinQueries) return false;
+  if ((const void*)n_in == (const void*)n_out) return false;   // in-place counts: pool first
+  const long long gx = ((long long)c.max_len / d.compress_ratio + kScoreWaves * kScoreTile - 1) / (kScoreWaves * kScoreTile);
+  if ((long long)c.n_seq * 2048 + gx * n_q >= (1LL << 31)) return false;   // one-dimensional grid
+  return c.kidx_ld % 8 == 0 && aligned16(c.kidx);
+}
+
+template <typename T>
+static void dispatch_pool_score(const sa_dims& d, const CacheArgs& c, const int32_t* n_in, int32_t* n_out,
+                                int max_new, const void* qidx, const int32_t* q_seq, const int32_t* q_pos, int n_q,
+                                float* scores, int64_t scores_ld, hipStream_t stream) {
+#define SA_PS_CASE(MT_, D_)                                                                                        \
+  if (d.h_idx / 32 == MT_ && d.d_idx == D_) {                                                                      \
+    launch_pool_score_t<T, MT_, D_>(d, c, n_in, n_out, max_new, qidx, q_seq, q_pos, n_q, scores, scores_ld,       \
+                                    stream);                                                                       \
+    return;                                                                                                        \
+  }
+  SA_PS_CASE(1, 64) SA_PS_CASE(1, 128) SA_PS_CASE(1, 256)
+  SA_PS_CASE(2, 64) SA_PS_CASE(2, 128) SA_PS_CASE(2, 256)
+  SA_PS_CASE(3, 64) SA_PS_CASE(3, 128) SA_PS_CASE(3, 256)
+  SA_PS_CASE(4, 64) SA_PS_CASE(4, 128) SA_PS_CASE(4, 256)
+#undef SA_PS_CASE
+}
+
+hipError_t launch_pool_score(const sa_dims& d, const CacheArgs& c, const int32_t* n_in, int32_t* n_out, int max_new,
+                             const void* qidx, const int32_t* q_seq, const int32_t* q_pos, int n_q, float* scores,
+                             int64_t scores_ld, hipStream_t stream) {
+  if (!pool_score_fused(d, c, qidx, n_q, n_in, n_out)) {
+    hipError_t err = launch_pool(d, c, n_in, n_out, max_new, stream);
+    if (err != hipSuccess) return err;
+    return launch_score(d, c, qidx, q_seq, q_pos, n_q, scores, scores_ld, stream);
+  }
+  if (d.dtype == SA_BF16) dispatch_pool_score<bf16>(d, c, n_in, n_out, max_new, qidx, q_seq, q_pos, n_q, scores, scores_ld, stream);
+  else dispatch_pool_score<f16>(d, c, n_in, n_out, max_new, qidx, q_seq, q_pos, n_q, scores, scores_ld, stream);
+  return hipGetLastError();
 }
 
 hipError_t launch_score(const sa_dims& d, const CacheArgs& c, const void* qidx, const int32_t* q_seq,

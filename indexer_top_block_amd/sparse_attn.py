@@ -30,6 +30,7 @@ EXPORTS = (
     "sparse_attn_workspace_bytes",
     "sparse_attn_pool",
     "sparse_attn_score",
+    "sparse_attn_pool_score",
     "sparse_attn_select",
     "sparse_attn_fwd",
     "sparse_attn_mask_to_indices",
@@ -94,6 +95,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.sparse_attn_pool.restype = ctypes.c_int
     lib.sparse_attn_score.argtypes = [dp, cp, P, P, P, I32, P, I64, P]
     lib.sparse_attn_score.restype = ctypes.c_int
+    lib.sparse_attn_pool_score.argtypes = [dp, cp, P, P, I32, P, P, P, I32, P, I64, P]
+    lib.sparse_attn_pool_score.restype = ctypes.c_int
     lib.sparse_attn_select.argtypes = [dp, cp, P, I64, P, P, I32, P, I64, P, P, SZ, P]
     lib.sparse_attn_select.restype = ctypes.c_int
     lib.sparse_attn_fwd.argtypes = [dp, cp, P, P, P, I64, P, I32, ctypes.c_float, P, P, SZ, P]
@@ -194,6 +197,14 @@ def sparse_attn_score(dims: SaDims, cache: Cache, qidx, q_seq, q_pos, n_q: int, 
     _check("sparse_attn_score", load().sparse_attn_score(ctypes.byref(dims), ctypes.byref(cache.struct), _ptr(qidx),
                                                          _ptr(q_seq), _ptr(q_pos), int(n_q), _ptr(scores),
                                                          int(scores_ld), _stream(stream)))
+
+
+def sparse_attn_pool_score(dims: SaDims, cache: Cache, n_pooled_in, n_pooled_out, max_new_blocks: int, qidx, q_seq,
+                           q_pos, n_q: int, scores, scores_ld: int, stream=None) -> None:
+    _check("sparse_attn_pool_score",
+           load().sparse_attn_pool_score(ctypes.byref(dims), ctypes.byref(cache.struct), _ptr(n_pooled_in),
+                                         _ptr(n_pooled_out), int(max_new_blocks), _ptr(qidx), _ptr(q_seq),
+                                         _ptr(q_pos), int(n_q), _ptr(scores), int(scores_ld), _stream(stream)))
 
 
 def sparse_attn_select(dims: SaDims, cache: Cache, scores, scores_ld: int, q_seq, q_pos, n_q: int, sel, sel_ld: int,

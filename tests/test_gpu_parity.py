@@ -592,3 +592,55 @@ def test_q8_full_size_decode(gpu_lib):
     say(f"[parity] generating workload 2: {datagen.WORKLOADS[2]}")
     case = datagen.make_workload(2)
     run_q8(case)
+
+
+# ------------------------------------------------------- fused pooling + scoring
+
+def _pool_then_score(case, prepool, max_new, alias=False):
+    """(kpool, n_pooled_out, scores) from pool then score, and from the fused call,
+    on two copies of the same layer whose caches first pooled `prepool` blocks per
+    sequence (None: nothing)."""
+    outs = []
+    for fused in (False, True):
+        layer = DeviceLayer(case)
+        n_in = torch.zeros_like(layer.n_pooled)
+        if prepool is not None:
+            sa.sparse_attn_pool(layer.dims, layer.cache, n_in, n_in, prepool)
+        n_out = n_in if alias else torch.full_like(n_in, -5)
+        layer.scores.fill_(-7.0)
+        if fused:
+            sa.sparse_attn_pool_score(layer.dims, layer.cache, n_in, n_out, max_new, layer.qidx, layer.q_seq,
+                                      layer.q_pos, layer.n_q, layer.scores, layer.scores_ld)
+        else:
+            sa.sparse_attn_pool(layer.dims, layer.cache, n_in, n_out, max_new)
+            layer.score()
+        torch.cuda.synchronize()
+        outs.append((layer.kpool.cpu(), n_out.cpu(), layer.scores.cpu()))
+    return outs
+
+
+def test_pool_score_matches_pool_then_score(gpu_lib):
+    # bit for bit: the newest block only (a decode step), a fresh cache (every block
+    # new, pooled in rounds inside each wave), a capped count, in-place counts (the
+    # two-launch path), several sequences (one without a query), other indexer shapes
+    cases = []
+    d = dims(top_k=256, compress_ratio=4)
+    lens = [5001, 777, 40]
+    case = datagen.make_case("ps_mla", d, lens, [0, 0, 1, 0], [5000, 2500, 776, 3], seed=0, case_id=600,
+                             std="inv_sqrt_dim", v_separate=False)
+    cases += [(case, max(lens) // 4 - 1, 2 ** 30, False, "newest block"), (case, None, 2 ** 30, False, "fresh"),
+              (case, None, 7, False, "capped"), (case, max(lens) // 4 - 1, 2 ** 30, True, "in place")]
+    d2 = dims(h_q=8, h_kv=2, d_kq=128, d_v=128, h_idx=32, d_idx=64, top_k=96, compress_ratio=8, dtype="f16")
+    case2 = datagen.make_case("ps_f16", d2, [2100, 333, 900], [0, 2, 2], [2099, 100, 899], seed=0, case_id=601,
+                              std=0.5)
+    cases += [(case2, 100, 2 ** 30, False, "three sequences"), (case2, None, 5, False, "capped, f16")]
+    d3 = dims(h_idx=128, d_idx=256, top_k=64, compress_ratio=2)
+    case3 = datagen.make_case("ps_256", d3, [3000], [0], [2999], seed=0, case_id=602, std="inv_sqrt_dim",
+                              v_separate=False)
+    cases += [(case3, 1498, 2 ** 30, False, "h_idx 128, d_idx 256")]
+    for case, prepool, max_new, alias, tag in cases:
+        (kp0, n0, s0), (kp1, n1, s1) = _pool_then_score(case, prepool, max_new, alias)
+        assert torch.equal(n0, n1), f"{tag}: counts differ"
+        assert torch.equal(kp0.view(torch.int16), kp1.view(torch.int16)), f"{tag}: pooled cache differs"
+        assert torch.equal(s0.view(torch.int32), s1.view(torch.int32)), f"{tag}: scores differ"
+        say(f"[parity] pool+score fused = pool then score: {tag}")

@@ -234,3 +234,16 @@ def test_q8_entry_points_reject_bad_arguments():
     odd = _dims()
     odd.d_kq = 520
     assert _call(fq, *args(kv, dd=odd)) == sa.SA_ERR_ARG                                # d_kq % 32
+
+
+def test_pool_score_rejects_bad_arguments():
+    d = ctypes.byref(_dims())
+    c = ctypes.byref(_cache())
+    f = "sparse_attn_pool_score"
+    assert _call(f, d, c, None, FAKE, 1, FAKE, FAKE, FAKE, 1, FAKE, 32768, None) == sa.SA_ERR_NULL
+    assert _call(f, d, c, FAKE, FAKE, -1, FAKE, FAKE, FAKE, 1, FAKE, 32768, None) == sa.SA_ERR_ARG
+    assert _call(f, d, c, FAKE, FAKE, 1, FAKE, FAKE, FAKE, -1, FAKE, 32768, None) == sa.SA_ERR_ARG
+    assert _call(f, d, c, FAKE, FAKE, 1, None, FAKE, FAKE, 1, FAKE, 32768, None) == sa.SA_ERR_NULL
+    assert _call(f, d, c, FAKE, FAKE, 1, FAKE, FAKE, FAKE, 1, FAKE, 1000, None) == sa.SA_ERR_ARG   # scores_ld
+    bad = _cache(kidx_ld=64)
+    assert _call(f, d, ctypes.byref(bad), FAKE, FAKE, 1, FAKE, FAKE, FAKE, 1, FAKE, 32768, None) == sa.SA_ERR_ARG
