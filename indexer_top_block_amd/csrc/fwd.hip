@@ -537,8 +537,10 @@ fwd_lds_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, i
     psum += __shfl_xor(psum, 32);
     lsum = lsum * alpha + psum;
     m = m_new;
+    if (__ballot(alpha != 1.f) != 0ull) {            // the running max moved (else nothing to rescale)
 #pragma unroll
-    for (int nt = 0; nt < NTW; ++nt) o[nt] *= alpha;
+      for (int nt = 0; nt < NTW; ++nt) o[nt] *= alpha;
+    }
     // V^T operand by transposing LDS reads: in each 16-lane group, lane r reads 4
     // dims at row 4*grp + r/4, dims 4*(r%4) .. +4 of the 16-dim tile, and lane i then
     // holds dim i of rows 4*grp .. 4*grp+3 -- the A-operand layout.

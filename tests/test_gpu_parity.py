@@ -644,3 +644,22 @@ def test_pool_score_matches_pool_then_score(gpu_lib):
         assert torch.equal(kp0.view(torch.int16), kp1.view(torch.int16)), f"{tag}: pooled cache differs"
         assert torch.equal(s0.view(torch.int32), s1.view(torch.int32)), f"{tag}: scores differ"
         say(f"[parity] pool+score fused = pool then score: {tag}")
+
+
+def test_pool_score_full_size_decode(gpu_lib):
+    # the 128K decode step as the benchmark launches it: the newest block pooled inside
+    # the scoring launch, bit for bit equal to pool then score; and a prefill-sized
+    # batch of 70 query tokens (the two-launch path)
+    say(f"[parity] generating workload 2: {datagen.WORKLOADS[2]}")
+    case = datagen.make_workload(2)
+    nb = int(case.seq_len[0]) // case.dims.compress_ratio
+    (kp0, n0, s0), (kp1, n1, s1) = _pool_then_score(case, nb - 1, 1)
+    assert torch.equal(n0, n1) and torch.equal(kp0.view(torch.int16), kp1.view(torch.int16))
+    assert torch.equal(s0.view(torch.int32), s1.view(torch.int32))
+    d = dims(top_k=256, compress_ratio=4)
+    many = datagen.make_case("ps_many", d, [3000], [0] * 70, list(range(2930, 3000)), seed=0, case_id=603,
+                             std="inv_sqrt_dim", v_separate=False)
+    (kp0, n0, s0), (kp1, n1, s1) = _pool_then_score(many, 700, 2 ** 30)
+    assert torch.equal(n0, n1) and torch.equal(kp0.view(torch.int16), kp1.view(torch.int16))
+    assert torch.equal(s0.view(torch.int32), s1.view(torch.int32))
+    say("[parity] pool+score fused at 128K and the 70-token fallback: bit for bit")
