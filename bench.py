@@ -255,7 +255,7 @@ def cpu_baseline(case: datagen.Case, seconds: float, bytes_per_step: int) -> dic
         one_step()
         n += 1
         el = time.perf_counter() - t0
-        if el >= seconds or n >= 1000:
+        if el >= seconds or n >= 10000:
             break
     per = el / n
     return {"value": round(bytes_per_step / per / 1e9, 4), "unit": "GB/s", "cores": blas_threads,
