@@ -226,29 +226,33 @@ score_mfma_kernel(const T* __restrict__ qidx, const T* __restrict__ kpool, int64
 // Prefill chunks (many query tokens of one sequence): a workgroup of kGemmQ waves
 // takes kGemmQ consecutive query tokens -- wave w holds token w's indexer heads as
 // the M operand in registers for the whole launch -- and walks a range of blocks in
-// tiles of kGemmBN pooled keys that all its waves share.  Each tile is loaded once
-// into LDS (rows padded by 16 bytes so the lanes' 16-byte reads spread over the
-// banks) while the previous one is being multiplied, so the pooled keys are read
-// from L2 once per kGemmQ queries instead of once per query, and each query's
-// heads once per block range.  Scores above a token's own visible blocks are not
+// tiles of kGemmBN pooled keys that all its waves share.  Each tile is gathered once
+// straight into LDS (global_load_lds, chunks XOR-swizzled by key so that the lanes'
+// 16-byte reads spread over the banks) while the previous one is being multiplied, so
+// the pooled keys are read from L2 once per kGemmQ queries instead of once per query,
+// and each query's heads once per block range.  Scores above a token's own visible blocks are not
 // written.  When the group's tokens belong to different sequences every wave reads
 // its own sequence's keys straight from memory instead.
 constexpr int kGemmQ = 8;             // query tokens (waves) per workgroup
 constexpr int kGemmBN = 128;          // pooled keys per LDS tile
 
 template <typename T, int MT, int D>
-__global__ void __launch_bounds__(kGemmQ * 64)
+__global__ void __launch_bounds__(kGemmQ * 64, 2)
 score_gemm_kernel(const T* __restrict__ qidx, const T* __restrict__ kpool, int64_t kpool_ld,
                   const int64_t* __restrict__ seq_blk0, const int32_t* __restrict__ seq_len,
                   const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos, int c, int n_q,
                   int tiles_per_range, float* __restrict__ scores, int64_t scores_ld) {
   typedef typename vec8<T>::type V8;
+  typedef __attribute__((address_space(3))) void lds_void;
   constexpr int KS = D / 16;
-  constexpr int KP = D + 8;                          // LDS row pitch (elements)
   constexpr int CH = D / 8;                          // 16-byte chunks per key row
-  constexpr int NLD = kGemmBN * CH / (kGemmQ * 64);  // chunks per thread per tile
-  static_assert(kGemmBN * CH % (kGemmQ * 64) == 0, "tile must split evenly");
-  __shared__ __attribute__((aligned(16))) T ks[2][kGemmBN * KP];
+  constexpr int KPI = kWave / CH;                    // keys per wave instruction
+  constexpr int NI = kGemmBN / (KPI * kGemmQ);       // instructions per wave per tile
+  static_assert(NI * KPI * kGemmQ == kGemmBN, "tile must split evenly");
+  // two tile buffers as separate objects, so that reading one never waits on the
+  // gathers into the other
+  __shared__ __attribute__((aligned(16))) T ks0[kGemmBN * D];
+  __shared__ __attribute__((aligned(16))) T ks1[kGemmBN * D];
   __shared__ int g_seq[kGemmQ], g_nb[kGemmQ];
   __shared__ int64_t g_blk0[kGemmQ];
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
@@ -315,41 +319,62 @@ score_gemm_kernel(const T* __restrict__ qidx, const T* __restrict__ kpool, int64
     return;
   }
 
-  // shared tiles: thread e-chunks of rows [t*BN, t*BN + BN), clamped into the sequence
+  // Shared tiles: rows [t*BN, t*BN + BN), clamped into the sequence, gathered straight
+  // into LDS (each wave NI instructions of KPI whole keys).  Chunk c of key k sits at
+  // position c ^ (k % CH) of its row, so that the B reads below (32 keys at one chunk)
+  // spread over the banks.  Tile t+1 is gathered into the other buffer while tile t is
+  // multiplied.
   const T* kseq = kpool + g_blk0[0] * kpool_ld;
   const int last = nb_max - 1;
-  V8 kreg[NLD];
-  auto load_tile = [&](int t) {
+  auto issue = [&](int t, T* buf) {
 #pragma unroll
-    for (int j = 0; j < NLD; ++j) {
-      const int e = tid + j * kGemmQ * 64, r = e / CH, cc = e % CH;
-      const int b = min(t * kGemmBN + r, last);
-      kreg[j] = *reinterpret_cast<const V8*>(kseq + (int64_t)b * kpool_ld + cc * 8);
+    for (int j = 0; j < NI; ++j) {
+      const int k0 = (wave * NI + j) * KPI;          // first key of the instruction
+      const int kk = k0 + lane / CH, p = lane % CH, cc = p ^ (kk & (CH - 1));
+      const int b = min(t * kGemmBN + kk, last);
+      __builtin_amdgcn_global_load_lds((const void*)(kseq + (int64_t)b * kpool_ld + cc * 8),
+                                       (lds_void*)(buf + k0 * D), 16, 0, 0);
     }
   };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < NLD; ++j) {
-      const int e = tid + j * kGemmQ * 64, r = e / CH, cc = e % CH;
-      *reinterpret_cast<V8*>(&ks[buf][r * KP + cc * 8]) = kreg[j];
-    }
-  };
-  load_tile(t_begin);
-  store_tile(0);
-  __syncthreads();
-  for (int t = t_begin; t < t_end; ++t) {
-    const int buf = (t - t_begin) & 1;
-    if (t + 1 < t_end) load_tile(t + 1);             // in flight while this tile is multiplied
+  auto multiply = [&](int t, const T* buf) {
     for (int nt = 0; nt < kGemmBN / 32; ++nt) {
       const int b0 = t * kGemmBN + nt * 32;
       if (b0 >= nb) break;                           // uniform per wave
-      const T* krow = &ks[buf][(nt * 32 + n) * KP + hf * (D / 2)];
-      V8 kb[KS];
+      const int key = nt * 32 + n;
+      const T* krow = buf + key * D;
+      // one B step at a time, shared by the M tiles (a register budget of 128 lets two
+      // workgroups share a CU)
+      f32x16 acc[MT];
 #pragma unroll
-      for (int st = 0; st < KS; ++st) kb[st] = *reinterpret_cast<const V8*>(krow + st * 8);
-      finish(kb, b0 + n);
+      for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x16{};
+#pragma unroll
+      for (int st = 0; st < KS; ++st) {
+        const V8 kb = *reinterpret_cast<const V8*>(krow + (((hf * (CH / 2) + st) ^ (key & (CH - 1))) * 8));
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma32x32x16<T>(qa[mt][st], kb, acc[mt]);
+      }
+      float sum = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sum += fmaxf(acc[mt][r], 0.f);
+      sum += __shfl_xor(sum, 32);
+      const int b = b0 + n;
+      if (hf == 0 && b < nb) srow[b] = sum + 0.0f;   // +0.0 turns -0.0 into +0.0
     }
-    if (t + 1 < t_end) store_tile(buf ^ 1);
+  };
+  issue(t_begin, ks0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int t = t_begin; t < t_end; t += 2) {
+    if (t + 1 < t_end) issue(t + 1, ks1);
+    multiply(t, ks0);
+    __builtin_amdgcn_s_waitcnt(0);                   // this wave's gathers into ks1
+    __syncthreads();                                 // everyone's; ks0 is free
+    if (t + 1 >= t_end) break;
+    if (t + 2 < t_end) issue(t + 2, ks0);
+    multiply(t + 1, ks1);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 }
