@@ -577,6 +577,15 @@ def test_q8_mla_lds_kernel(gpu_lib):
         run_q8(case)
 
 
+def test_q8_two_kv_heads_and_long_lists(gpu_lib):
+    # the LDS-gather q8_0 kernel with two latent KV heads (head strides in both planes)
+    # and lists several tiles long per split
+    d = dims(h_q=32, h_kv=2, top_k=512, compress_ratio=4)
+    case = datagen.make_case("q8_two_heads", d, [6000, 1200], [0, 1, 0], [5999, 1199, 4000], seed=0, case_id=530,
+                             std="inv_sqrt_dim", v_separate=False)
+    run_q8(case)
+
+
 def test_q8_generic_kernel(gpu_lib):
     # separate V, GQA, fp32 queries: the generic kernel with the q8_0 reader
     for j, d in enumerate((dims(h_q=8, h_kv=2, d_kq=128, d_v=128, h_idx=8, top_k=96, compress_ratio=8, dtype="f16"),
