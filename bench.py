@@ -108,7 +108,7 @@ class RotatingLayers:
         for r in range(self.n):
             sa.sparse_attn_pool(self.dims, self.caches[r], zeros, self.n_pooled_out, 2 ** 31 - 1)
 
-    # the four calls of a step, on copy r
+    # the calls of a step, on copy r
     def pool(self, r):
         sa.sparse_attn_pool(self.dims, self.caches[r], self.n_pooled_prev, self.n_pooled_out, 1)
 

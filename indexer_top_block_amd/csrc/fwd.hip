@@ -20,7 +20,11 @@
 //   from LDS column-wise.  Splitting DV rather than rows keeps one accumulator per
 //   output element (32 registers per lane), so two workgroups share a CU and their
 //   gathers overlap.
-// VALU path (any dtype): the same tiles with plain float dot products.
+// MLA shapes with V inside K (DV 512, DKQ 512 or 576): fwd_lds_kernel, rows gathered
+// straight into LDS (described at the kernel).
+// VALU path (any dtype; fwd_common.hpp): the same tiles with plain float dot products.
+// Entry forms: plain, with a bias per list entry, and with a dense window of recent
+// positions appended to the list (row_pos in fwd_common.hpp).
 //
 // Partial results: o (unnormalised, float32), m (running max, log2 units) and l
 // (sum of weights) per (query, head, split); the combine kernel merges the splits.

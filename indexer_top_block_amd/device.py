@@ -1,4 +1,4 @@
-"""Device-side buffers for one layer, and the four calls on them.
+"""Device-side buffers for one layer, and the library's calls on them.
 
 Plumbing for tests, the smoke check and the benchmark: torch allocates the device
 memory and supplies the stream; every step runs in libsparse_attn through the
