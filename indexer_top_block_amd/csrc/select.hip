@@ -546,49 +546,114 @@ chunk_select_kernel(const float* __restrict__ scores, int64_t scores_ld, const i
 // over the registers, most significant digit first (11, 11, then 10 bits), each
 // pass histogramming the keys that match the digits fixed so far; a pass whose
 // chosen bin is taken whole (its count equals the number still to take) ends the
-// search early, and the remaining digits do not matter.  Kept blocks (above the
-// fixed prefix, or equal to it) are marked in an LDS bitmap of the row; when the
-// search ran to the full 32 bits, the keys equal to T are marked in a second bitmap
-// and only the first ones in index order are taken.  One prefix sum over the words'
-// popcounts then places every kept block in index order.
+// search early, and the remaining digits do not matter.
+//
+// One compute unit runs the whole row, so the cost is the vector instructions spent
+// per key in each pass (about 0.2 us per instruction per key at 32768 keys), and the
+// passes are written for few of them:
+//   - keys are formed with two integer operations after an add that folds -0 into +0;
+//   - the first pass, which counts every key, adds into 16 copies of its histogram
+//     laid out [bin][copy] (the address is the digit shifted onto the lane's copy, no
+//     other arithmetic), so keys sharing a digit -- scores crowd into a few binades --
+//     hit different copies;
+//   - later passes test membership in the running bin with one subtract and compare;
+//   - kept blocks (key at or above a threshold) and, when the search ran to the full
+//     32 bits, the keys equal to T go to bitmaps of the row with one compare and one
+//     wave ballot per register (64 consecutive blocks); every wave then places its 64
+//     bitmap words itself, counting the bits of the words before its own, so the
+//     output needs no workgroup-wide prefix sum.  Only the first keys equal to T in
+//     index order are taken.
 constexpr int kWideThreads = 1024;
 constexpr int kWideMaxKpt = 32;
-constexpr int kWideCopies = 8;                       // lane-privatised copies in the first pass
 constexpr int kWideBins = 2048;
-constexpr int kWideStride = kWideBins + 1;
-constexpr int kWideWords = kWideThreads * kWideMaxKpt / 32;   // bitmap words, one per thread
+constexpr int kWideCopies = 16;                      // pass-1 copies: lanes l, l+16, l+32, l+48 share one
+constexpr int kWideWords = kWideThreads * kWideMaxKpt / 32;   // bitmap words, 64 per wave
 
-struct WideSmem {
-  uint32_t h1[kWideCopies * kWideStride];            // pass 1, then pass 3 in copy 0
+struct alignas(16) WideSmem {
+  uint32_t h1[kWideBins * kWideCopies];              // pass 1 [bin][copy]; pass 3 uses words 0..1023
   uint32_t h2[kWideBins];                            // pass 2
-  uint32_t keep[kWideWords];                         // blocks above the prefix (or in its bin)
+  uint32_t keep[kWideWords];                         // blocks at or above the threshold
   uint32_t tie[kWideWords];                          // blocks equal to T (full-width search)
-  int scan[kWideThreads / kWave + 1];
-  int pick[3];
+  int scan[2][kWideThreads / kWave];                 // per-wave sums, alternating between picks
+  int pick[4];
 };
 
+// Order-preserving 32-bit key of a score: +0 and -0 give the same key, negative
+// scores map below positive ones.
+__device__ __forceinline__ uint32_t score_key(float f) {
+  const uint32_t u = __float_as_uint(f + 0.0f);      // -0 + +0 = +0
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
+}
+
 // The bin holding the k-th largest of the counted keys, for a histogram held as PER
-// consecutive bins per thread (thread t: bins [t*PER, t*PER + PER)).  Writes bin,
-// keys in higher bins and keys in the bin to pick[0..2] and synchronises.
+// consecutive bins per thread (thread t: bins [t*PER, t*PER + PER)), with `pad` keys
+// taken back out of bin 0.  Writes bin, keys in higher bins and keys in the bin to
+// pick[0..2] and synchronises.  `scan` must not be in use by the previous pick.
 template <int PER>
-__device__ __forceinline__ void wide_pick(const uint32_t (&cnt)[PER], int k, WideSmem& sm) {
+__device__ __forceinline__ void wide_pick(uint32_t (&cnt)[PER], int k, int pad, int* scan, int* pick) {
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  if (tid == 0) cnt[0] -= (uint32_t)pad;
   int sum = 0;
 #pragma unroll
   for (int j = 0; j < PER; ++j) sum += (int)cnt[j];
-  int total;
-  const int below_incl = block_exclusive_scan<kWideThreads>(sum, sm.scan, &total) + sum;
-  int above = total - below_incl;                    // keys in bins >= (t+1)*PER
+  const int incl = wave_inclusive_scan(sum, lane);
+  if (lane == kWave - 1) scan[wave] = incl;
+  __syncthreads();
+  int after = 0;                                     // keys counted by later waves
+#pragma unroll
+  for (int w = 0; w < kWideThreads / kWave; ++w) after += w > wave ? scan[w] : 0;
+  int above = after + __builtin_amdgcn_readlane(incl, kWave - 1) - incl;   // keys in bins >= (t+1)*PER
 #pragma unroll
   for (int j = PER - 1; j >= 0; --j) {
     const int gt = above, ge = above + (int)cnt[j];
     if (gt < k && ge >= k) {
-      sm.pick[0] = (int)threadIdx.x * PER + j;
-      sm.pick[1] = gt;
-      sm.pick[2] = (int)cnt[j];
+      pick[0] = tid * PER + j;
+      pick[1] = gt;
+      pick[2] = (int)cnt[j];
     }
     above = ge;
   }
   __syncthreads();
+}
+
+// Set bits in the bitmap words before word 64 * wave (lane l reads words [16 l, 16 l + 16)).
+__device__ __forceinline__ int bits_before(const uint32_t* bm, int wave, int lane) {
+  int n = 0;
+  if (lane < 4 * wave) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 v = *(const uint4*)&bm[lane * 16 + i * 4];
+      n += __popc(v.x) + __popc(v.y) + __popc(v.z) + __popc(v.w);
+    }
+  }
+  return __builtin_amdgcn_readlane(wave_inclusive_scan(n, lane), kWave - 1);
+}
+
+// The compiler's lane write (v_writelane_b32: lane `lane` of `old` replaced by the
+// wave-uniform `x`), declared by its intrinsic name so that the compiler, which
+// knows its wait-state rules, schedules it.
+__device__ int amdgcn_writelane(int x, int lane, int old) __asm("llvm.amdgcn.writelane.i32");
+
+// Lane j < N of (lo, hi) receives the wave's ballot of pred(j): the low and the
+// high 32 lanes' bits.
+template <int N, int J = 0, typename P>
+__device__ __forceinline__ void ballot_rows(P pred, uint32_t& lo, uint32_t& hi) {
+  if constexpr (J < N) {
+    const uint64_t m = __ballot(pred(J));
+    lo = (uint32_t)amdgcn_writelane((int)(uint32_t)m, J, (int)lo);
+    hi = (uint32_t)amdgcn_writelane((int)(uint32_t)(m >> 32), J, (int)hi);
+    ballot_rows<N, J + 1>(pred, lo, hi);
+  }
+}
+
+// Positions p0 .. p0 + c - 1 of one kept block.
+__device__ __forceinline__ void store_block(int32_t* dst, int32_t p0, int c) {
+  if (c == 4) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) dst[t] = p0 + t;
+  } else {
+    for (int t = 0; t < c; ++t) dst[t] = p0 + t;
+  }
 }
 
 template <int KPT>
@@ -597,16 +662,22 @@ select_wide_kernel(const float* __restrict__ scores, int64_t scores_ld, const in
                    const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos, int c, int k_blk,
                    int32_t* __restrict__ sel, int64_t sel_ld, int32_t* __restrict__ n_sel) {
   __shared__ WideSmem sm;
-  const int q = blockIdx.x, tid = threadIdx.x, lane = tid % kWave;
+  const int q = blockIdx.x, tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const float* row = scores + (int64_t)q * scores_ld;
   // The whole row is loaded up front and kept in registers for every pass; the
   // query's length arrives with it (indices below scores_ld are valid memory).
-  const int last = (int)min(scores_ld, (int64_t)KPT * kWideThreads) - 1;
+  float raw[KPT];
+  {
+    const int last = (int)min(scores_ld, (int64_t)KPT * kWideThreads) - 1;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) raw[j] = row[min(j * kWideThreads + tid, last)];
+  }
+  __builtin_amdgcn_sched_barrier(0);                 // every load in flight before the first is used
   uint32_t key[KPT];
 #pragma unroll
-  for (int j = 0; j < KPT; ++j) key[j] = key_clamped(row, j * kWideThreads + tid, last);
+  for (int j = 0; j < KPT; ++j) key[j] = score_key(raw[j]);
   const QueryRowInfo qr = query_blocks(seq_len, q_seq, q_pos, q, c);
-  for (int e = tid; e < kWideCopies * kWideStride; e += kWideThreads) sm.h1[e] = 0u;
+  for (int e = tid; e < kWideBins * kWideCopies / 4; e += kWideThreads) ((uint4*)sm.h1)[e] = uint4{0u, 0u, 0u, 0u};
   for (int e = tid; e < kWideBins; e += kWideThreads) sm.h2[e] = 0u;
   sm.keep[tid] = 0u;
   sm.tie[tid] = 0u;
@@ -621,94 +692,93 @@ select_wide_kernel(const float* __restrict__ scores, int64_t scores_ld, const in
   // padding keys back out of bin 0, and a prefix of 0 (the only one they can match)
   // never takes its bin whole, so they are never kept.
   const int n_pad = KPT * kWideThreads - nb;
-  uint32_t all = 0xffffffffu;
+  if (n_pad != 0) {
 #pragma unroll
-  for (int j = 0; j < KPT; ++j) {
-    const bool ok = j * kWideThreads + tid < nb;
-    all &= ok ? key[j] : 0xffffffffu;
-    key[j] = ok ? key[j] : 0u;
+    for (int j = 0; j < KPT; ++j) key[j] = j * kWideThreads + tid < nb ? key[j] : 0u;
   }
-  // When every key of the row has its top bit set (no negative scores: the usual
-  // case, as block scores are sums of rectified products), that bit tells nothing
-  // and the digits start one bit lower, over twice the bins the keys fall into.
-  const int top = __syncthreads_and((int)(all >> 31));
-  const int s1 = 21 - top, s2 = 10 - top;            // digits: [s1, s1+11), [s2, s1), [0, s2)
+  __syncthreads();
 
-  // ---- pass 1: the top digit, 8 privatised copies ----------------------------------
+  // ---- pass 1: the top 11 bits ------------------------------------------------------------
   {
-    uint32_t* mine = sm.h1 + (lane & (kWideCopies - 1)) * kWideStride;
+    uint32_t* mine = sm.h1 + (lane & (kWideCopies - 1));
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) atomicAdd(&mine[(key[j] >> s1) & 2047u], 1u);
+    for (int j = 0; j < KPT; ++j) atomicAdd(&mine[(key[j] >> 21) * kWideCopies], 1u);
   }
   __syncthreads();
   {
-    uint32_t cnt[2];
+    // thread t: bins 2t and 2t+1, the copies read from a lane-rotated start
+    uint32_t cnt[2] = {0u, 0u};
+    const uint32_t* h = sm.h1 + tid * 2 * kWideCopies;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      uint32_t n = 0;
-#pragma unroll
-      for (int cp = 0; cp < kWideCopies; ++cp) n += sm.h1[cp * kWideStride + tid * 2 + j];
-      cnt[j] = n;
+    for (int j = 0; j < kWideCopies; ++j) {
+      const int cp = (j + tid) & (kWideCopies - 1);
+      cnt[0] += h[cp];
+      cnt[1] += h[kWideCopies + cp];
     }
-    if (tid == 0) cnt[0] -= (uint32_t)n_pad;
-    wide_pick<2>(cnt, k_blk, sm);
+    wide_pick<2>(cnt, k_blk, n_pad, sm.scan[0], sm.pick);
   }
-  // prefix = key >> shift of the keys still in the running (the padding's 0 is below
-  // every such prefix when top is set)
-  uint32_t prefix = ((uint32_t)top << 11) | (uint32_t)sm.pick[0];
+  uint32_t prefix = (uint32_t)sm.pick[0];            // key >> shift of the keys still in the running
   int k_rem = k_blk - sm.pick[1];
-  int shift = s1;
+  int shift = 21;
   bool whole = sm.pick[2] == k_rem && prefix != 0u;
-  __syncthreads();                                   // pick[] is rewritten below
-  // ---- pass 2: next 11 bits among keys in the bin ---------------------------------
+  // ---- pass 2: next 11 bits among keys in the bin -----------------------------------------
   if (!whole) {
-    sm.h1[tid] = 0u;                                 // copy 0 serves pass 3
+    sm.h1[tid] = 0u;                                 // words 0..1023 serve pass 3
+    const uint32_t lo = prefix << 21;
 #pragma unroll
     for (int j = 0; j < KPT; ++j)
-      if ((key[j] >> s1) == prefix) atomicAdd(&sm.h2[(key[j] >> s2) & 2047u], 1u);
+      if (key[j] - lo < (1u << 21)) atomicAdd(&sm.h2[(key[j] >> 10) & (kWideBins - 1)], 1u);
     __syncthreads();
     uint32_t cnt[2] = {sm.h2[tid * 2], sm.h2[tid * 2 + 1]};
-    if (tid == 0 && prefix == 0u) cnt[0] -= (uint32_t)n_pad;
-    wide_pick<2>(cnt, k_rem, sm);
+    wide_pick<2>(cnt, k_rem, prefix == 0u ? n_pad : 0, sm.scan[1], sm.pick);
     prefix = (prefix << 11) | (uint32_t)sm.pick[0];
     k_rem -= sm.pick[1];
-    shift = s2;
+    shift = 10;
     whole = sm.pick[2] == k_rem && prefix != 0u;
-    __syncthreads();
-    // ---- pass 3: last 10 bits ------------------------------------------------------
+    // ---- pass 3: last 10 bits ------------------------------------------------------------
     if (!whole) {
+      const uint32_t lo3 = prefix << 10;
 #pragma unroll
       for (int j = 0; j < KPT; ++j)
-        if ((key[j] >> s2) == prefix) atomicAdd(&sm.h1[key[j] & ((1u << s2) - 1u)], 1u);
+        if (key[j] - lo3 < (1u << 10)) atomicAdd(&sm.h1[key[j] & 1023u], 1u);
       __syncthreads();
       uint32_t cnt1[1] = {sm.h1[tid]};
-      if (tid == 0 && prefix == 0u) cnt1[0] -= (uint32_t)n_pad;
-      wide_pick<1>(cnt1, k_rem, sm);
-      prefix = (prefix << s2) | (uint32_t)sm.pick[0];
+      wide_pick<1>(cnt1, k_rem, prefix == 0u ? n_pad : 0, sm.scan[0], sm.pick);
+      prefix = (prefix << 10) | (uint32_t)sm.pick[0];
       k_rem -= sm.pick[1];
       shift = 0;
       whole = sm.pick[2] == k_rem && prefix != 0u;
-      __syncthreads();
     }
   }
-  // ---- kept blocks -> bitmap -----------------------------------------------------------
-  // Above the prefix, or inside its bin when the bin is taken whole, always kept;
-  // otherwise the keys equal to the prefix go to the tie bitmap.  Padding keys are 0:
-  // never above a prefix, and equal only to a prefix of 0, which is never whole.
-#pragma unroll
-  for (int j = 0; j < KPT; ++j) {
-    const int idx = j * kWideThreads + tid;
-    const uint32_t hi = (uint32_t)((uint64_t)key[j] >> shift);
-    if (hi > prefix || (whole && hi == prefix)) atomicOr(&sm.keep[idx >> 5], 1u << (idx & 31));
-    else if (hi == prefix) atomicOr(&sm.tie[idx >> 5], 1u << (idx & 31));
+  // ---- kept blocks -> bitmaps -----------------------------------------------------------
+  // Kept for sure: key >> shift above the prefix, or equal to it when its bin is
+  // taken whole, i.e. key >= thr.  A search that did not end whole ran to the full
+  // width (shift 0): keys above T are kept, keys equal to T are ties.  Padding keys
+  // are 0: below every threshold of a prefix other than 0, which is never whole.
+  // Register j of the wave's lanes holds blocks j*1024 + 64*wave + [0, 64): bitmap
+  // words 32j + 2 wave + {0, 1}, collected in lane j.
+  {
+    uint32_t k_lo = 0u, k_hi = 0u, t_lo = 0u, t_hi = 0u;
+    if (whole || prefix != 0xffffffffu) {
+      const uint32_t thr = whole ? prefix << shift : prefix + 1u;
+      ballot_rows<KPT>([&](int j) { return key[j] >= thr; }, k_lo, k_hi);
+    }
+    if (!whole) ballot_rows<KPT>([&](int j) { return key[j] == prefix; }, t_lo, t_hi);
+    if (lane < KPT) {
+      *(uint2*)&sm.keep[lane * 32 + wave * 2] = uint2{k_lo, k_hi};
+      *(uint2*)&sm.tie[lane * 32 + wave * 2] = uint2{t_lo, t_hi};
+    }
   }
   __syncthreads();
-  uint32_t word = sm.keep[tid];
+  // ---- this wave's 64 words -> positions in index order ---------------------------------------
+  const int w = wave * kWave + lane;                 // bitmap word of this lane: blocks 32w .. 32w+31
+  uint32_t word = sm.keep[w];
+  int o = bits_before(sm.keep, wave, lane);
   if (!whole) {                                      // the first k_rem tied blocks in index order
-    uint32_t t = sm.tie[tid];
-    int n_tie;
-    const int before = block_exclusive_scan<kWideThreads>(__popc(t), sm.scan, &n_tie);
-    int take = k_rem - before;
+    uint32_t t = sm.tie[w];
+    const int t_before = bits_before(sm.tie, wave, lane);
+    o += min(k_rem, t_before);
+    int take = k_rem - t_before - (wave_inclusive_scan(__popc(t), lane) - __popc(t));
     while (t != 0u && take > 0) {
       const uint32_t low = t & (0u - t);
       word |= low;
@@ -716,14 +786,11 @@ select_wide_kernel(const float* __restrict__ scores, int64_t scores_ld, const in
       --take;
     }
   }
-  int ktot;
-  int o = block_exclusive_scan<kWideThreads>(__popc(word), sm.scan, &ktot);
+  o += wave_inclusive_scan(__popc(word), lane) - __popc(word);
   while (word != 0u && o < k_blk) {                  // o < k_blk always; the bound only guards memory
     const int b = __ffs(word) - 1;
     word &= word - 1u;
-    const int32_t p0 = (tid * 32 + b) * c;
-    int32_t* dst = out + (int64_t)o * c;
-    for (int t = 0; t < c; ++t) dst[t] = p0 + t;
+    store_block(out + (int64_t)o * c, (w * 32 + b) * c, c);
     ++o;
   }
   write_tail<kWideThreads>(out, sel_ld, nb, qr.n_vis, c, k_blk, n_sel + q);

@@ -285,3 +285,46 @@ def sparse_mask(n_rows: int, n_kv: int, n_kv_max: int, *, seed: int, case_id: in
         pos = np.sort(rng.choice(n_kv, size=cnt, replace=False))
         m[r, pos] = -(1.0 + (np.arange(cnt) + r) % 7) / 32.0
     return round_to_dtype(m, dtype)
+
+
+# ---------------------------------------------------------------------------
+# Score rows that stress a block selection directly (not produced by scoring).
+# ---------------------------------------------------------------------------
+
+SCORE_ROW_KINDS = ("normal", "small_ints", "all_equal", "signed_zeros", "binade_gap", "lognormal_dups")
+
+
+def score_row(kind: str, nb: int, k_blk: int, *, seed: int, case_id: int) -> np.ndarray:
+    """[nb] float32 scores of one query's blocks, of a shape a selection must handle.
+
+    normal          standard normal, so about half the scores are negative;
+    small_ints      integers -3..4: few distinct values, the cut falls inside a run of
+                    exact ties;
+    all_equal       every score 1.5;
+    signed_zeros    a few hundred positive scores, the rest +0.0 and -0.0 at random;
+    binade_gap      k_blk scores of 4.0 at random blocks over uniform draws in [1, 2);
+    lognormal_dups  positive lognormal draws, then the draws ranked k_blk - 40 ..
+                    k_blk + 40 all set to the one ranked k_blk (ties across the cut).
+    """
+    rng = np.random.default_rng([seed, case_id, 6, SCORE_ROW_KINDS.index(kind)])
+    if kind == "normal":
+        s = rng.standard_normal(nb)
+    elif kind == "small_ints":
+        s = rng.integers(-3, 5, size=nb).astype(np.float64)
+    elif kind == "all_equal":
+        s = np.full(nb, 1.5)
+    elif kind == "signed_zeros":
+        s = np.where(rng.random(nb) < 0.5, 0.0, -0.0)
+        hot = rng.choice(nb, size=min(nb, 300), replace=False)
+        s[hot] = rng.random(hot.size) + 0.5
+    elif kind == "binade_gap":
+        s = rng.random(nb) + 1.0
+        s[rng.choice(nb, size=min(nb, k_blk), replace=False)] = 4.0
+    elif kind == "lognormal_dups":
+        s = rng.lognormal(0.0, 0.5, size=nb)
+        order = np.argsort(-s, kind="stable")
+        lo, hi = max(0, k_blk - 41), min(nb, k_blk + 40)
+        s[order[lo:hi]] = s[order[min(k_blk - 1, nb - 1)]]
+    else:
+        raise ValueError(f"unknown score row kind {kind}")
+    return s.astype(np.float32)

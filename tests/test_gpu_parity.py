@@ -184,6 +184,34 @@ def test_select_streams_long_score_rows(gpu_lib):
     run_and_check(case, queries=[0, 1, 40, 79])
 
 
+@pytest.mark.parametrize("seq_len,top_k", [(131072, 2048), (16000, 256)])
+def test_select_on_adversarial_score_rows(gpu_lib, seq_len, top_k):
+    # the select kernel alone on score rows no scoring produces: negative scores,
+    # few distinct values, all equal, signed zeros, a whole binade at the cut, ties
+    # across the cut; full, ragged, exactly-dense, one-over-dense and empty rows
+    d = dims(h_q=16, d_kq=128, d_v=128, h_idx=1, d_idx=64, compress_ratio=4, top_k=top_k, dtype="bf16")
+    c, k_blk = d.compress_ratio, top_k // 4
+    kinds = datagen.SCORE_ROW_KINDS
+    q_pos = [seq_len - 1] * len(kinds) + [seq_len - 1 - 4093, k_blk * c - 1, k_blk * c + 3, -1]
+    case = datagen.make_case("select_rows", d, [seq_len], [0] * len(q_pos), q_pos, seed=0, case_id=245, std=1.0,
+                             v_separate=False)
+    layer = DeviceLayer(case)
+    rows, want = [], []
+    for i, p in enumerate(q_pos):
+        n_vis = oracle.visible_tokens(seq_len, p)
+        nb = n_vis // c
+        kind = kinds[i] if i < len(kinds) else kinds[i % 3]
+        s = datagen.score_row(kind, nb, k_blk, seed=0, case_id=246 + i)
+        rows.append(s)
+        want.append(oracle.select_positions(s, n_vis, c, top_k))
+    layer.select(scores=parity.upload_scores(layer, rows))
+    torch.cuda.synchronize()
+    got = layer.selections()
+    for i in range(len(q_pos)):
+        assert np.array_equal(got[i], want[i]), f"row {i} (q_pos {q_pos[i]}): selection differs"
+    say(f"[parity] select rows seq_len={seq_len} top_k={top_k}: ok")
+
+
 def test_max_list_capacity(gpu_lib):
     # the largest list the library accepts: top_k + c - 1 = 65536
     d = dims(h_q=16, d_kq=128, d_v=128, h_idx=32, d_idx=64, compress_ratio=1, top_k=65536, dtype="bf16")
