@@ -570,11 +570,11 @@ constexpr int kWideCopies = 16;                      // pass-1 copies: lanes l, 
 constexpr int kWideWords = kWideThreads * kWideMaxKpt / 32;   // bitmap words, 64 per wave
 
 struct alignas(16) WideSmem {
-  uint32_t h1[kWideBins * kWideCopies];              // pass 1 [bin][copy]; pass 3 uses words 0..1023
-  uint32_t h2[kWideBins];                            // pass 2
+  uint32_t h2[kWideBins];                            // pass 2 (first: its bins' addresses need no base)
+  uint32_t h1[kWideBins * kWideCopies];              // pass 1 [bin][copy]; pass 3: words 0..1023; the list
   uint32_t keep[kWideWords];                         // blocks at or above the threshold
   uint32_t tie[kWideWords];                          // blocks equal to T (full-width search)
-  int scan[2][kWideThreads / kWave];                 // per-wave sums, alternating between picks
+  int wsum[2][kWideThreads / kWave];                 // per-wave totals, alternating between picks
   int pick[4];
 };
 
@@ -588,30 +588,39 @@ __device__ __forceinline__ uint32_t score_key(float f) {
 // The bin holding the k-th largest of the counted keys, for a histogram held as PER
 // consecutive bins per thread (thread t: bins [t*PER, t*PER + PER)), with `pad` keys
 // taken back out of bin 0.  Writes bin, keys in higher bins and keys in the bin to
-// pick[0..2] and synchronises.  `scan` must not be in use by the previous pick.
+// pick[0..2] and synchronises.  `wsum` must not be in use by the previous pick.
+// Every wave posts its total; each then finds, from the 16 totals, the one wave whose
+// range holds the k-th key, and only that wave scans its lanes.
 template <int PER>
-__device__ __forceinline__ void wide_pick(uint32_t (&cnt)[PER], int k, int pad, int* scan, int* pick) {
+__device__ __forceinline__ void wide_pick(uint32_t (&cnt)[PER], int k, int pad, int* wsum, int* pick) {
+  constexpr int kWaves = kWideThreads / kWave;
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   if (tid == 0) cnt[0] -= (uint32_t)pad;
   int sum = 0;
 #pragma unroll
   for (int j = 0; j < PER; ++j) sum += (int)cnt[j];
   const int incl = wave_inclusive_scan(sum, lane);
-  if (lane == kWave - 1) scan[wave] = incl;
+  const int wave_total = __builtin_amdgcn_readlane(incl, kWave - 1);
+  if (lane == 0) wsum[wave] = wave_total;
   __syncthreads();
-  int after = 0;                                     // keys counted by later waves
+  // lanes 0..15: keys in the waves above wave `lane`, and whether the k-th is in it
+  const int v = lane < kWaves ? wsum[lane] : 0;
+  const int v_incl = wave_inclusive_scan(v, lane);
+  const int v_after = __builtin_amdgcn_readlane(v_incl, kWave - 1) - v_incl;
+  const uint64_t hit = __ballot(lane < kWaves && v_after < k && v_after + v >= k);
+  const int w_hit = (int)__builtin_ctzll(hit | (1ull << 63));   // exactly one wave when 0 < k <= keys
+  if (wave == w_hit) {
+    int above = __builtin_amdgcn_readlane(v_after, w_hit) + wave_total - incl;   // keys in bins >= (t+1)*PER
 #pragma unroll
-  for (int w = 0; w < kWideThreads / kWave; ++w) after += w > wave ? scan[w] : 0;
-  int above = after + __builtin_amdgcn_readlane(incl, kWave - 1) - incl;   // keys in bins >= (t+1)*PER
-#pragma unroll
-  for (int j = PER - 1; j >= 0; --j) {
-    const int gt = above, ge = above + (int)cnt[j];
-    if (gt < k && ge >= k) {
-      pick[0] = tid * PER + j;
-      pick[1] = gt;
-      pick[2] = (int)cnt[j];
+    for (int j = PER - 1; j >= 0; --j) {
+      const int gt = above, ge = above + (int)cnt[j];
+      if (gt < k && ge >= k) {
+        pick[0] = tid * PER + j;
+        pick[1] = gt;
+        pick[2] = (int)cnt[j];
+      }
+      above = ge;
     }
-    above = ge;
   }
   __syncthreads();
 }
@@ -672,15 +681,15 @@ select_wide_kernel(const float* __restrict__ scores, int64_t scores_ld, const in
 #pragma unroll
     for (int j = 0; j < KPT; ++j) raw[j] = row[min(j * kWideThreads + tid, last)];
   }
-  __builtin_amdgcn_sched_barrier(0);                 // every load in flight before the first is used
-  uint32_t key[KPT];
-#pragma unroll
-  for (int j = 0; j < KPT; ++j) key[j] = score_key(raw[j]);
   const QueryRowInfo qr = query_blocks(seq_len, q_seq, q_pos, q, c);
   for (int e = tid; e < kWideBins * kWideCopies / 4; e += kWideThreads) ((uint4*)sm.h1)[e] = uint4{0u, 0u, 0u, 0u};
   for (int e = tid; e < kWideBins; e += kWideThreads) sm.h2[e] = 0u;
   sm.keep[tid] = 0u;
   sm.tie[tid] = 0u;
+  __builtin_amdgcn_sched_barrier(0);                 // every load in flight before the first is used
+  uint32_t key[KPT];
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) key[j] = score_key(raw[j]);
   int32_t* out = sel + (int64_t)q * sel_ld;
   if (qr.nb <= k_blk) {
     write_dense<kWideThreads>(out, sel_ld, qr.n_vis, n_sel + q);
@@ -706,16 +715,19 @@ select_wide_kernel(const float* __restrict__ scores, int64_t scores_ld, const in
   }
   __syncthreads();
   {
-    // thread t: bins 2t and 2t+1, the copies read from a lane-rotated start
+    // thread t: bins 2t and 2t+1, 32 words read as 8 quads from a lane-rotated start,
+    // so that 8 consecutive lanes cover all 32 banks
     uint32_t cnt[2] = {0u, 0u};
-    const uint32_t* h = sm.h1 + tid * 2 * kWideCopies;
+    const uint4* h = (const uint4*)(sm.h1 + tid * 2 * kWideCopies);
 #pragma unroll
-    for (int j = 0; j < kWideCopies; ++j) {
-      const int cp = (j + tid) & (kWideCopies - 1);
-      cnt[0] += h[cp];
-      cnt[1] += h[kWideCopies + cp];
+    for (int i = 0; i < 8; ++i) {
+      const int quad = (i + tid) & 7;                // quads 0..3: bin 2t, 4..7: bin 2t+1
+      const uint4 v = h[quad];
+      const uint32_t s4 = v.x + v.y + v.z + v.w;
+      cnt[0] += quad < 4 ? s4 : 0u;
+      cnt[1] += quad < 4 ? 0u : s4;
     }
-    wide_pick<2>(cnt, k_blk, n_pad, sm.scan[0], sm.pick);
+    wide_pick<2>(cnt, k_blk, n_pad, sm.wsum[0], sm.pick);
   }
   uint32_t prefix = (uint32_t)sm.pick[0];            // key >> shift of the keys still in the running
   int k_rem = k_blk - sm.pick[1];
@@ -725,12 +737,14 @@ select_wide_kernel(const float* __restrict__ scores, int64_t scores_ld, const in
   if (!whole) {
     sm.h1[tid] = 0u;                                 // words 0..1023 serve pass 3
     const uint32_t lo = prefix << 21;
+    uint32_t one = 1u;
+    asm volatile("" : "+v"(one));                    // one register for every add, not one per key
 #pragma unroll
     for (int j = 0; j < KPT; ++j)
-      if (key[j] - lo < (1u << 21)) atomicAdd(&sm.h2[(key[j] >> 10) & (kWideBins - 1)], 1u);
+      if (key[j] - lo < (1u << 21)) atomicAdd(&sm.h2[(key[j] >> 10) & (kWideBins - 1)], one);
     __syncthreads();
     uint32_t cnt[2] = {sm.h2[tid * 2], sm.h2[tid * 2 + 1]};
-    wide_pick<2>(cnt, k_rem, prefix == 0u ? n_pad : 0, sm.scan[1], sm.pick);
+    wide_pick<2>(cnt, k_rem, prefix == 0u ? n_pad : 0, sm.wsum[1], sm.pick);
     prefix = (prefix << 11) | (uint32_t)sm.pick[0];
     k_rem -= sm.pick[1];
     shift = 10;
@@ -743,7 +757,7 @@ select_wide_kernel(const float* __restrict__ scores, int64_t scores_ld, const in
         if (key[j] - lo3 < (1u << 10)) atomicAdd(&sm.h1[key[j] & 1023u], 1u);
       __syncthreads();
       uint32_t cnt1[1] = {sm.h1[tid]};
-      wide_pick<1>(cnt1, k_rem, prefix == 0u ? n_pad : 0, sm.scan[0], sm.pick);
+      wide_pick<1>(cnt1, k_rem, prefix == 0u ? n_pad : 0, sm.wsum[0], sm.pick);
       prefix = (prefix << 10) | (uint32_t)sm.pick[0];
       k_rem -= sm.pick[1];
       shift = 0;
@@ -787,11 +801,35 @@ select_wide_kernel(const float* __restrict__ scores, int64_t scores_ld, const in
     }
   }
   o += wave_inclusive_scan(__popc(word), lane) - __popc(word);
-  while (word != 0u && o < k_blk) {                  // o < k_blk always; the bound only guards memory
-    const int b = __ffs(word) - 1;
-    word &= word - 1u;
-    store_block(out + (int64_t)o * c, (w * 32 + b) * c, c);
-    ++o;
+  const int body = k_blk * c;
+  if (body <= kWideBins * kWideCopies) {
+    // the list is assembled in LDS (pass 1's histogram is free) and written out
+    // coalesced, rather than as scattered stores of a few lanes each
+    int32_t* list = (int32_t*)sm.h1;
+    if (c == 4) {
+      while (word != 0u && o < k_blk) {              // o < k_blk always; the bound only guards memory
+        const int32_t p0 = (w * 32 + __ffs(word) - 1) * 4;
+        word &= word - 1u;
+        *(int4*)&list[o * 4] = int4{p0, p0 + 1, p0 + 2, p0 + 3};
+        ++o;
+      }
+    } else {
+      while (word != 0u && o < k_blk) {
+        const int32_t p0 = (w * 32 + __ffs(word) - 1) * c;
+        word &= word - 1u;
+        for (int t = 0; t < c; ++t) list[o * c + t] = p0 + t;
+        ++o;
+      }
+    }
+    __syncthreads();
+    for (int i = tid; i < body; i += kWideThreads) out[i] = list[i];
+  } else {
+    while (word != 0u && o < k_blk) {                // o < k_blk always; the bound only guards memory
+      const int b = __ffs(word) - 1;
+      word &= word - 1u;
+      store_block(out + (int64_t)o * c, (w * 32 + b) * c, c);
+      ++o;
+    }
   }
   write_tail<kWideThreads>(out, sel_ld, nb, qr.n_vis, c, k_blk, n_sel + q);
 }
