@@ -687,31 +687,36 @@ select_wide_kernel(const float* __restrict__ scores, int64_t scores_ld, const in
   sm.keep[tid] = 0u;
   sm.tie[tid] = 0u;
   __builtin_amdgcn_sched_barrier(0);                 // every load in flight before the first is used
-  uint32_t key[KPT];
-#pragma unroll
-  for (int j = 0; j < KPT; ++j) key[j] = score_key(raw[j]);
   int32_t* out = sel + (int64_t)q * sel_ld;
   if (qr.nb <= k_blk) {
     write_dense<kWideThreads>(out, sel_ld, qr.n_vis, n_sel + q);
     return;
   }
   const int nb = min(qr.nb, KPT * kWideThreads);     // the launch guarantees qr.nb fits; the bitmap relies on it
+  const int n_pad = KPT * kWideThreads - nb;
+  __syncthreads();                                   // the histograms are clear (the loads may still fly)
+
+  // ---- pass 1: the top 11 bits, each key counted as it arrives ---------------------------
   // Keys past the row's end become 0 -- below every key a score can have except
   // negative NaNs -- so the passes need no bounds checks: the picks take the n_pad
   // padding keys back out of bin 0, and a prefix of 0 (the only one they can match)
   // never takes its bin whole, so they are never kept.
-  const int n_pad = KPT * kWideThreads - nb;
-  if (n_pad != 0) {
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) key[j] = j * kWideThreads + tid < nb ? key[j] : 0u;
-  }
-  __syncthreads();
-
-  // ---- pass 1: the top 11 bits ------------------------------------------------------------
+  uint32_t key[KPT];
   {
     uint32_t* mine = sm.h1 + (lane & (kWideCopies - 1));
+    if (n_pad == 0) {
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) atomicAdd(&mine[(key[j] >> 21) * kWideCopies], 1u);
+      for (int j = 0; j < KPT; ++j) {
+        key[j] = score_key(raw[j]);
+        atomicAdd(&mine[(key[j] >> 21) * kWideCopies], 1u);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < KPT; ++j) {
+        key[j] = j * kWideThreads + tid < nb ? score_key(raw[j]) : 0u;
+        atomicAdd(&mine[(key[j] >> 21) * kWideCopies], 1u);
+      }
+    }
   }
   __syncthreads();
   {
