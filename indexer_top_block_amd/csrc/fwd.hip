@@ -381,8 +381,14 @@ fwd_mfma_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, 
 // per workgroup keeps LDS at 78 KiB, so two workgroups share a CU and one's gathers
 // overlap the other's compute.  There are no register buffers and no landing
 // stores; the compute is that of the kernel above.
-template <typename T, int DKQ>
-__global__ void __launch_bounds__(256, 2)
+//
+// QLDS (launches of at most one workgroup per CU, e.g. one decode token's splits):
+// every wave needs the whole query block as its MFMA B operand, and four register
+// copies of it cost a CU more load time than the tile's rows.  The block is then
+// brought into LDS once, with the rows, and each wave reads its operands from there;
+// the extra 19 KiB of LDS leave one workgroup per CU.
+template <typename T, int DKQ, bool QLDS>
+__global__ void __launch_bounds__(256, QLDS ? 1 : 2)
 fwd_lds_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, int64_t k_hs,
                const int64_t* __restrict__ seq_row0, const int32_t* __restrict__ seq_len,
                const int32_t* __restrict__ q_seq, const int32_t* __restrict__ sel, int64_t sel_ld,
@@ -406,6 +412,12 @@ fwd_lds_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, i
   __shared__ __attribute__((aligned(16))) T kmain0[RT * MP];
   __shared__ __attribute__((aligned(16))) T krem0[RT * REMP * 8];
   __shared__ __attribute__((aligned(16))) float st[16 * SP];   // scaled scores, [head][row]
+  // Query block in LDS (QLDS): 16-byte chunk p holds chunk p % QP of head p / QP; one
+  // pad chunk per head spreads the heads over the banks.
+  constexpr int QCH = DKQ / 8;
+  constexpr int QP = QCH + 1;
+  constexpr int QINST = (16 * QP + kWave - 1) / kWave;   // wave instructions for 16 heads
+  __shared__ __attribute__((aligned(16))) T qs[QLDS ? QINST * kWave * 8 : 8];
 
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
@@ -437,7 +449,17 @@ fwd_lds_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, i
 
   const T* qbase = q + ((int64_t)i * h_q + (int64_t)g * G) * DKQ;
   V8 qf[KST];
-  {
+  if constexpr (QLDS) {
+    // issued with the list reads; read into registers after the first tile's barrier.
+    // Chunks past the G heads and the pad chunks repeat valid data.
+    for (int u = wave; u < QINST; u += 256 / kWave) {
+      const int p = u * kWave + lane;
+      const int h = p / QP < G ? p / QP : 0;
+      const int cc = p % QP < QCH ? p % QP : QCH - 1;
+      __builtin_amdgcn_global_load_lds((const void*)(qbase + h * DKQ + cc * 8), (lds_void*)&qs[u * kWave * 8], 16, 0,
+                                       0);
+    }
+  } else {
     const T* qh = qbase + (col < G ? col : 0) * DKQ + grp * 8;
 #pragma unroll
     for (int st_ = 0; st_ < KST; ++st_) qf[st_] = *reinterpret_cast<const V8*>(qh + st_ * 32);
@@ -571,6 +593,17 @@ fwd_lds_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, i
     for (int t = 0; t < n_tiles; ++t) {
       __builtin_amdgcn_s_waitcnt(0);                 // this wave's gathers of tile t
       __syncthreads();                               // everyone's
+      if constexpr (QLDS) {
+        if (t == 0) {                                // the query block landed with the first tile
+          const V8* qrow = reinterpret_cast<const V8*>(qs) + (col < G ? col : 0) * QP + grp;
+#pragma unroll
+          for (int st_ = 0; st_ < KST; ++st_) qf[st_] = qrow[st_ * 4];
+          if (col >= G) {
+#pragma unroll
+            for (int st_ = 0; st_ < KST; ++st_) qf[st_] = V8{};
+          }
+        }
+      }
       const int raw_new = list_at(t + 3);
       const int64_t ko1 = row_off(raw1, t + 1, &v1);
       const float b1 = bias_at(t + 1);
@@ -582,6 +615,9 @@ fwd_lds_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, i
       raw1 = raw2;
       raw2 = raw_new;
     }
+  }
+  if constexpr (QLDS) {
+    if (n_tiles == 0) __builtin_amdgcn_s_waitcnt(0);   // the query block's loads land before the wave ends
   }
 
   if (col < G) {
@@ -741,15 +777,33 @@ static void launch_mfma_t(const sa_dims& d, const CacheArgs& c, const void* q, c
                      sel_bias, q_pos, window, plan.list_max, d.h_q, d.h_kv, scale_log2, plan.n_split, plan.rows_per_split, out, ws_o, ws_ml);
 }
 
+// Compute units of the current device (cached per device).
+static int device_cus() {
+  static int cus[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess) cus[dev] = n;
+  }
+  return cus[dev];
+}
+
 template <typename T, int DKQ>
 static void launch_lds_t(const sa_dims& d, const CacheArgs& c, const void* q, const int32_t* q_seq,
                          const int32_t* sel, int64_t sel_ld, const int32_t* n_sel, const float* sel_bias, const int32_t* q_pos, int window, int n_q,
                           float scale_log2,
                          float* out, float* ws_o, float* ws_ml, const FwdPlan& plan, hipStream_t stream) {
   dim3 grid(plan.n_split, n_q * d.h_kv);
-  hipLaunchKernelGGL((fwd_lds_kernel<T, DKQ>), grid, dim3(256), 0, stream, (const T*)q, (const T*)c.k, c.k_ld,
-                     c.k_hs, c.seq_row0, c.seq_len, q_seq, sel, sel_ld, n_sel, sel_bias, q_pos, window, plan.list_max, d.h_q, d.h_kv, scale_log2,
-                     plan.n_split, plan.rows_per_split, out, ws_o, ws_ml);
+  // at most one workgroup per CU: the query block goes through LDS
+  const bool qlds = (long long)plan.n_split * n_q * d.h_kv <= device_cus();
+#define SA_LDS_LAUNCH(QL)                                                                                        \
+  hipLaunchKernelGGL((fwd_lds_kernel<T, DKQ, QL>), grid, dim3(256), 0, stream, (const T*)q, (const T*)c.k, c.k_ld,   \
+                     c.k_hs, c.seq_row0, c.seq_len, q_seq, sel, sel_ld, n_sel, sel_bias, q_pos, window, plan.list_max,   \
+                     d.h_q, d.h_kv, scale_log2, plan.n_split, plan.rows_per_split, out, ws_o, ws_ml)
+  if (qlds) SA_LDS_LAUNCH(true);
+  else SA_LDS_LAUNCH(false);
+#undef SA_LDS_LAUNCH
 }
 
 template <typename T>
