@@ -777,8 +777,8 @@ static void launch_mfma_t(const sa_dims& d, const CacheArgs& c, const void* q, c
                      sel_bias, q_pos, window, plan.list_max, d.h_q, d.h_kv, scale_log2, plan.n_split, plan.rows_per_split, out, ws_o, ws_ml);
 }
 
-// Compute units of the current device (cached per device).
-static int device_cus() {
+// Compute units of the current device (cached per device; 0 if unknown).
+int device_cus() {
   static int cus[64] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;

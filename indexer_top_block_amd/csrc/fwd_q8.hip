@@ -56,7 +56,9 @@ __device__ __forceinline__ uint64_t shfl64(uint64_t x, int src) {
 // (one takes the first half of the q8_0 blocks, the other the second, and the
 // softmax sums the two partial tiles) and each wave owns 64 output dims, so a tile's
 // conversion work -- the bulk of its VALU time -- is spread over twice the waves.
-template <typename T, int DKQ, int NW>
+// QLDS: the query block is brought into LDS once and the waves read their operands
+// from there, as in the bf16 kernel (launches of at most one workgroup per CU).
+template <typename T, int DKQ, int NW, bool QLDS>
 __global__ void __launch_bounds__(64 * NW, 8 / NW)
 fwd_q8_lds_kernel(const T* __restrict__ q, const int8_t* __restrict__ kq, int64_t k_ld, int64_t k_hs,
                   const f16* __restrict__ ks, int64_t ks_ld, int64_t ks_hs, const int64_t* __restrict__ seq_row0,
@@ -88,6 +90,12 @@ fwd_q8_lds_kernel(const T* __restrict__ q, const int8_t* __restrict__ kq, int64_
   __shared__ __attribute__((aligned(16))) int8_t kt[RT * PITCH];
   __shared__ __attribute__((aligned(16))) uint32_t sct[RT * SCW];
   __shared__ __attribute__((aligned(16))) float st[KSPLIT * 16 * SP];   // scaled partial scores, [part][head][row]
+  // Query block in LDS (QLDS): 16-byte chunk p holds chunk p % QP of head p / QP; one
+  // pad chunk per head spreads the heads over the banks.
+  constexpr int QCH = DKQ / 8;
+  constexpr int QP = QCH + 1;
+  constexpr int QINST = (16 * QP + kWave - 1) / kWave;   // wave instructions for 16 heads
+  __shared__ __attribute__((aligned(16))) T qs[QLDS ? QINST * kWave * 8 : 8];
 
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
@@ -116,7 +124,17 @@ fwd_q8_lds_kernel(const T* __restrict__ q, const int8_t* __restrict__ kq, int64_
   const int dvb = wave * DVW;                     // its output dims
   const T* qbase = q + ((int64_t)i * h_q + (int64_t)g * G) * DKQ;
   V8 qf[KB];
-  {
+  if constexpr (QLDS) {
+    // issued with the list reads; read into registers after the first tile's barrier.
+    // Chunks past the G heads and the pad chunks repeat valid data.
+    for (int u = wave; u < QINST; u += NW) {
+      const int p = u * kWave + lane;
+      const int h = p / QP < G ? p / QP : 0;
+      const int cc = p % QP < QCH ? p % QP : QCH - 1;
+      __builtin_amdgcn_global_load_lds((const void*)(qbase + h * DKQ + cc * 8), (lds_void*)&qs[u * kWave * 8], 16, 0,
+                                       0);
+    }
+  } else {
     const T* qh = qbase + (col < G ? col : 0) * DKQ + grp * 8 + kb0 * 32;
 #pragma unroll
     for (int b = 0; b < KB; ++b) qf[b] = b < nkb ? *reinterpret_cast<const V8*>(qh + b * 32) : V8{};
@@ -281,6 +299,13 @@ fwd_q8_lds_kernel(const T* __restrict__ q, const int8_t* __restrict__ kq, int64_
     for (int t = 0; t < n_tiles; ++t) {
       __builtin_amdgcn_s_waitcnt(0);              // this wave's gathers of tile t
       __syncthreads();                            // everyone's
+      if constexpr (QLDS) {
+        if (t == 0) {                             // the query block landed with the first tile
+          const V8* qrow = reinterpret_cast<const V8*>(qs) + (col < G ? col : 0) * QP + grp + kb0 * 4;
+#pragma unroll
+          for (int b = 0; b < KB; ++b) qf[b] = b < nkb && col < G ? qrow[b * 4] : V8{};
+        }
+      }
       const int raw_new = list_at(t + 3);
       const uint64_t k1 = row_src(raw1, t + 1, &v1, &s1);
       compute(v0);
@@ -290,6 +315,9 @@ fwd_q8_lds_kernel(const T* __restrict__ q, const int8_t* __restrict__ kq, int64_
       raw1 = raw2;
       raw2 = raw_new;
     }
+  }
+  if constexpr (QLDS) {
+    if (n_tiles == 0) __builtin_amdgcn_s_waitcnt(0);   // the query block's loads land before the wave ends
   }
 
   if (col < G) {
@@ -338,10 +366,16 @@ static void launch_q8_lds_t(const sa_dims& d, const CacheArgs& c, const Q8Args& 
                             float scale_log2, float* out, float* ws_o, float* ws_ml, const FwdPlan& plan,
                             hipStream_t stream) {
   dim3 grid(plan.n_split, n_q * d.h_kv);
-  hipLaunchKernelGGL((fwd_q8_lds_kernel<T, DKQ, kQ8Waves>), grid, dim3(64 * kQ8Waves), 0, stream, (const T*)q,
-                     (const int8_t*)kv.k, kv.k_ld, kv.k_hs, (const f16*)kv.ks, kv.ks_ld, kv.ks_hs, c.seq_row0,
-                     c.seq_len, q_seq, sel, sel_ld, n_sel, plan.list_max, d.h_q, d.h_kv, scale_log2, plan.n_split,
-                     plan.rows_per_split, out, ws_o, ws_ml);
+  // at most one workgroup per CU: the query block goes through LDS
+  const bool qlds = (long long)plan.n_split * n_q * d.h_kv <= device_cus();
+#define SA_Q8_LDS_LAUNCH(QL)                                                                                         \
+  hipLaunchKernelGGL((fwd_q8_lds_kernel<T, DKQ, kQ8Waves, QL>), grid, dim3(64 * kQ8Waves), 0, stream, (const T*)q,   \
+                     (const int8_t*)kv.k, kv.k_ld, kv.k_hs, (const f16*)kv.ks, kv.ks_ld, kv.ks_hs, c.seq_row0,      \
+                     c.seq_len, q_seq, sel, sel_ld, n_sel, plan.list_max, d.h_q, d.h_kv, scale_log2, plan.n_split,  \
+                     plan.rows_per_split, out, ws_o, ws_ml)
+  if (qlds) SA_Q8_LDS_LAUNCH(true);
+  else SA_Q8_LDS_LAUNCH(false);
+#undef SA_Q8_LDS_LAUNCH
 }
 
 template <typename T>

@@ -86,6 +86,8 @@ hipError_t launch_fwd_q8(const sa_dims& d, const CacheArgs& c, const Q8Args& kv,
                          void* ws, const FwdPlan& plan, hipStream_t stream);
 hipError_t launch_quantize_q8_0(const void* x, int x_dtype, int64_t n_rows, int n_cols, int64_t x_ld, int8_t* codes,
                                 int64_t codes_ld, void* scales, int64_t scales_ld, hipStream_t stream);
+// Compute units of the current device (cached per device; 0 if unknown).
+int device_cus();
 // Merges the split partials (ws_o, ws_ml) into out; nothing when unsplit.
 hipError_t launch_combine(const sa_dims& d, int n_q, float* out, const float* ws_o, const float* ws_ml,
                           const FwdPlan& plan, hipStream_t stream);
