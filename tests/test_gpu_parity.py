@@ -379,6 +379,46 @@ def test_mask_form_edges(gpu_lib):
         assert layer.n_sel.cpu().numpy()[0] == 1000 and not layer.out[2].abs().max().item()
 
 
+def test_mask_to_indices_long_rows(gpu_lib):
+    # f16 rows longer than one group of chunks with a ragged end, aligned and unaligned
+    # pitches, lists staged in LDS and lists too long for it, dense rows cut to the
+    # list, empty rows, and finite entries only at the ends
+    n_kv = 200003
+    rng = np.random.default_rng(320)
+    n_q = 6
+    mask = np.full((n_q, n_kv), -np.inf, dtype=np.float32)
+    idx = rng.choice(n_kv, 4000, replace=False)
+    mask[0, idx] = -(1 + idx % 7) / 32.0                                # ~2%, more than a 2051 list holds
+    mask[2, rng.random(n_kv) < 0.5] = 0.5                              # dense: cut to the list
+    mask[3, [0, n_kv - 1]] = -0.25                                     # the two ends only
+    idx = rng.choice(n_kv, 600, replace=False)
+    mask[4, idx] = 0.125
+    mask[4, idx[:5]] = np.inf
+    mask[4, idx[5:9]] = np.nan
+    mask[5, 131072 - 3:131072 + 3] = -1.0                              # across the group boundary
+    for pitch in (n_kv, n_kv + 5):                                     # 16-byte rows (f16) or not
+        host = np.full((n_q, pitch), -np.inf, dtype=np.float32)
+        host[:, :n_kv] = mask
+        dev = torch.from_numpy(host).to(torch.float16).cuda()
+        for sel_ld in (2051, 9000):
+            sel = torch.full((n_q, sel_ld), 7, dtype=torch.int32, device="cuda")
+            n_sel = torch.zeros((n_q,), dtype=torch.int32, device="cuda")
+            bias = torch.full((n_q, sel_ld), 7.0, dtype=torch.float32, device="cuda")
+            sa.sparse_attn_mask_to_indices(dev, "f16", pitch, n_q, n_kv, sel, sel_ld, n_sel, bias)
+            torch.cuda.synchronize()
+            s_, n_, b_ = sel.cpu().numpy(), n_sel.cpu().numpy(), bias.cpu().numpy()
+            for qi in range(n_q):
+                pos = oracle.mask_positions(mask[qi])
+                m = min(len(pos), sel_ld)
+                assert n_[qi] == len(pos), f"pitch {pitch} list {sel_ld} row {qi}: count {n_[qi]} != {len(pos)}"
+                assert np.array_equal(s_[qi, :m], pos[:m]) and (s_[qi, m:] == -1).all(), \
+                    f"pitch {pitch} list {sel_ld} row {qi}: list differs"
+                want = mask[qi, pos[:m]].astype(np.float16).astype(np.float32)
+                assert np.array_equal(b_[qi, :m], want) and (b_[qi, m:] == 0).all(), \
+                    f"pitch {pitch} list {sel_ld} row {qi}: values differ"
+    say("[parity] mask_to_indices long f16 rows: ok")
+
+
 # ------------------------------------------------------ dense window + selection
 
 def run_window(case, windows, queries=None):
