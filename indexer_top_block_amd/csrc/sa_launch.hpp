@@ -46,7 +46,6 @@ bool pool_score_fused(const sa_dims& d, const CacheArgs& c, const void* qidx, in
 constexpr int kStateQueries = 64;          // query tokens the chunked selection keeps state for
 struct WsState {
   uint32_t ghist[kStateQueries][4096];     // per-query histogram of the top 12 key bits
-  uint32_t hist_done[kStateQueries];       // chunks of the histogram pass that have arrived
   uint32_t sel_done[kStateQueries];        // chunks of the selection pass that have arrived
 };
 static_assert(sizeof(WsState) <= SA_WS_STATE_BYTES, "state region too small");

@@ -31,16 +31,18 @@
 // chunks of 2048 blocks, one workgroup each, so the whole GPU takes part; two kernels.
 //   hist    each chunk histograms the top 12 bits of its keys in LDS and adds the
 //           non-empty bins to the query's histogram in the workspace (device-scope
-//           atomics); the last chunk to arrive finds the bin b holding the K_blk-th
-//           largest key and the number of keys above it, records both and clears
-//           the histogram for the next call;
-//   select  each chunk writes its keys in b or above, in index order, to its own
+//           atomics);
+//   select  each chunk finds, from that (complete) histogram, the bin b holding the
+//           K_blk-th largest key and the number of keys above it -- every chunk
+//           alike, so no workgroup waits on another for it -- and writes its keys in
+//           b or above, in index order, to its own
 //           segment as (key << 32 | ~index) -- unique 64-bit values whose order is
 //           exactly (score desc, index asc), so ties need no special case; the last
 //           chunk to arrive gathers the segments, radix-selects the cut among the
 //           values inside b (8-bit digits below the 12 shared bits, stopping once
 //           the chosen bin holds one value) and writes every value at or above the
-//           cut as positions in index order, then the tail, the padding and n_sel.
+//           cut as positions in index order, then the tail, the padding and n_sel,
+//           and returns the histogram to zero for the next call.
 // If the values in b and above overflow what the last workgroup holds (massive exact
 // ties), it runs the 4-pass algorithm above over the whole row instead.
 #include "sa_common.hpp"
@@ -258,18 +260,18 @@ struct ChunkScratch {
   static __host__ size_t query_bytes(int g) { return head_bytes(g) + (size_t)g * kChunk * 8; }
 };
 
-// Bin holding the k-th largest key of a histogram split as 16 bins per thread
-// (thread t holds bins [t*16, t*16+16)), and the number of keys in higher bins,
-// to all threads of the 256-thread workgroup.
-__device__ __forceinline__ void find_top_bin(const uint32_t (&cnt)[16], int k, int* lds_scan, int* out_bin,
+// Bin holding the k-th largest key of a histogram split as PER bins per thread
+// (thread t holds bins [t*PER, t*PER+PER)), and the number of keys in higher bins,
+// to all threads of the BLOCK-thread workgroup.
+template <int BLOCK, int PER>
+__device__ __forceinline__ void find_top_bin(const uint32_t (&cnt)[PER], int k, int* lds_scan, int* out_bin,
                                              int* out_above) {
-  constexpr int PER = 16;
   const int tid = threadIdx.x;
   int sum = 0;
 #pragma unroll
   for (int j = 0; j < PER; ++j) sum += (int)cnt[j];
   int total;
-  const int below_incl = block_exclusive_scan<256>(sum, lds_scan, &total) + sum;
+  const int below_incl = block_exclusive_scan<BLOCK>(sum, lds_scan, &total) + sum;
   int above = total - below_incl;                    // keys in bins >= (t+1)*16
 #pragma unroll
   for (int j = PER - 1; j >= 0; --j) {
@@ -315,18 +317,13 @@ __device__ __forceinline__ bool arrive_last(uint32_t* counter, int n, int* lds_f
 }
 
 // Pass 1 (one workgroup per chunk): the chunk's histogram of the top 12 key bits is
-// added to the query's histogram; the last chunk to arrive finds the bin holding the
-// K_blk-th largest key, records it with the number still to take inside it, and
-// clears the histogram for the next call.
+// added to the query's histogram.
 __global__ void __launch_bounds__(kHistThreads)
 chunk_hist_kernel(const float* __restrict__ scores, int64_t scores_ld, const int32_t* __restrict__ seq_len,
                   const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos, int c, int k_blk,
                   WsState* __restrict__ st, ChunkScratch sc) {
   constexpr int kStride = kBins1 + 1;
-  constexpr int PER = kBins1 / kHistThreads;         // 16 bins per thread in the last workgroup
   __shared__ uint32_t h[kHistCopies * kStride];
-  __shared__ int scan[kHistThreads / kWave + 1];
-  __shared__ int sh_last, sh_bin, sh_above;
   const int q = blockIdx.y, tid = threadIdx.x;
   const int base = blockIdx.x * kChunk;
   const float* row = scores + (int64_t)q * scores_ld;
@@ -341,7 +338,6 @@ chunk_hist_kernel(const float* __restrict__ scores, int64_t scores_ld, const int
   for (int e = tid; e < kHistCopies * kStride; e += kHistThreads) h[e] = 0u;
   const QueryRowInfo qr = query_blocks(seq_len, q_seq, q_pos, q, c);
   if (qr.nb <= k_blk || base >= qr.nb) return;      // uniform over the workgroup
-  const int n_chunks = (qr.nb + kChunk - 1) / kChunk;
   __syncthreads();
   uint32_t* mine = h + (tid & (kHistCopies - 1)) * kStride;
 #pragma unroll
@@ -354,18 +350,6 @@ chunk_hist_kernel(const float* __restrict__ scores, int64_t scores_ld, const int
 #pragma unroll
     for (int cp = 0; cp < kHistCopies; ++cp) n += h[cp * kStride + b];
     if (n) atomicAdd(&g[b], n);
-  }
-  if (!arrive_last(&st->hist_done[q], n_chunks, &sh_last)) return;
-  uint32_t hc[PER];
-#pragma unroll
-  for (int j = 0; j < PER; ++j) hc[j] = coherent_load(&g[tid * PER + j]);
-  find_top_bin(hc, k_blk, scan, &sh_bin, &sh_above);
-#pragma unroll
-  for (int j = 0; j < PER; ++j) g[tid * PER + j] = 0u;
-  if (tid == 0) {
-    uint32_t* ctrl = sc.ctrl(q);
-    ctrl[0] = (uint32_t)sh_bin;
-    ctrl[1] = (uint32_t)(k_blk - sh_above);
   }
 }
 
@@ -405,9 +389,11 @@ chunk_select_kernel(const float* __restrict__ scores, int64_t scores_ld, const i
     idx[j] = base + tid * kSelKpt + j;               // contiguous: index order across threads
     key[j] = key_clamped(row, idx[j], (int)scores_ld - 1);
   }
-  const uint32_t* ctrl = sc.ctrl(q);
-  const uint32_t bin = ctrl[0];
-  int k_rem = (int)ctrl[1];
+  uint32_t* ghist = st->ghist[q];
+  constexpr int PER1 = kBins1 / kSelThreads;         // histogram bins per thread
+  uint32_t hc[PER1];
+#pragma unroll
+  for (int j = 0; j < PER1; ++j) hc[j] = coherent_load(&ghist[tid * PER1 + j]);
   const QueryRowInfo qr = query_blocks(seq_len, q_seq, q_pos, q, c);
   int32_t* out = sel + (int64_t)q * sel_ld;
   if (qr.nb <= k_blk) {                              // every block fits: dense
@@ -416,6 +402,10 @@ chunk_select_kernel(const float* __restrict__ scores, int64_t scores_ld, const i
   }
   if (base >= qr.nb) return;
   const int n_chunks = (qr.nb + kChunk - 1) / kChunk;
+  // the bin b holding the K_blk-th largest key, and how many to take inside it
+  find_top_bin<kSelThreads, PER1>(hc, k_blk, sm.f.scan, &sm.f.pick[0], &sm.f.pick[1]);
+  const uint32_t bin = (uint32_t)sm.f.pick[0];
+  int k_rem = k_blk - sm.f.pick[1];
   // this chunk's entries, in index order
   bool keep[kSelKpt];
   int n = 0;
@@ -432,6 +422,7 @@ chunk_select_kernel(const float* __restrict__ scores, int64_t scores_ld, const i
     if (keep[j]) seg[slot++] = ((uint64_t)key[j] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)idx[j]);
   if (tid == 0) sc.n_ent(q)[blockIdx.x] = (uint32_t)tot;
   if (!arrive_last(&st->sel_done[q], n_chunks, &sm.f.last)) return;
+  for (int b = tid; b < kBins1; b += kSelThreads) ghist[b] = 0u;   // every chunk has read it
 
   // ---- the last chunk: gather, cut, write ---------------------------------------
   constexpr int PER = kMaxChunks / kSelThreads;      // 2 chunk counts per thread
