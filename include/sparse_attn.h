@@ -113,7 +113,7 @@ int sparse_attn_check_dims(const sa_dims* dims);
  * size serves both calls.  Returns 0 on bad arguments or when no workspace is needed.
  * Host only, no HIP call.
  * Contract: zero-fill the buffer once before its first use (e.g. hipMemset when it is
- * allocated).  Its first SA_WS_STATE_BYTES bytes hold histograms and arrival counters
+ * allocated).  Its first SA_WS_STATE_BYTES bytes hold histograms
  * that every call returns to zero, so later calls need no re-initialisation; the rest
  * is scratch that each call overwrites.  Calls that share a workspace must not run
  * concurrently (use one workspace per stream).                                     */

@@ -41,12 +41,11 @@ bool pool_score_fused(const sa_dims& d, const CacheArgs& c, const void* qidx, in
 
 // Workspace layout shared by sparse_attn_select and sparse_attn_fwd:
 //   [0, SA_WS_STATE_BYTES)   state -- zero before the first call, left zero by every call
-//                            (histograms and arrival counters of the chunked selection);
+//                            (the chunked selection's histograms);
 //   [SA_WS_STATE_BYTES, ...) scratch -- overwritten by each call.
 constexpr int kStateQueries = 64;          // query tokens the chunked selection keeps state for
 struct WsState {
   uint32_t ghist[kStateQueries][4096];     // per-query histogram of the top 12 key bits
-  uint32_t sel_done[kStateQueries];        // chunks of the selection pass that have arrived
 };
 static_assert(sizeof(WsState) <= SA_WS_STATE_BYTES, "state region too small");
 

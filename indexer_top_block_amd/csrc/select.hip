@@ -28,22 +28,22 @@
 // rows stream chunk by chunk.
 //
 // Longer rows, few query tokens (long-context decode), chunked: the row is cut into
-// chunks of 2048 blocks, one workgroup each, so the whole GPU takes part; two kernels.
+// chunks of 2048 blocks, one workgroup each, so the whole GPU takes part; three
+// launches, whose boundaries order them (no workgroup ever waits on another):
 //   hist    each chunk histograms the top 12 bits of its keys in LDS and adds the
 //           non-empty bins to the query's histogram in the workspace (device-scope
 //           atomics);
 //   select  each chunk finds, from that (complete) histogram, the bin b holding the
 //           K_blk-th largest key and the number of keys above it -- every chunk
-//           alike, so no workgroup waits on another for it -- and writes its keys in
-//           b or above, in index order, to its own
-//           segment as (key << 32 | ~index) -- unique 64-bit values whose order is
-//           exactly (score desc, index asc), so ties need no special case; the last
-//           chunk to arrive gathers the segments, radix-selects the cut among the
-//           values inside b (8-bit digits below the 12 shared bits, stopping once
-//           the chosen bin holds one value) and writes every value at or above the
-//           cut as positions in index order, then the tail, the padding and n_sel,
-//           and returns the histogram to zero for the next call.
-// If the values in b and above overflow what the last workgroup holds (massive exact
+//           alike -- and writes its keys in b or above, in index order, to its own
+//           segment as (key << 32 | ~index): unique 64-bit values whose order is
+//           exactly (score desc, index asc), so ties need no special case;
+//   finish  one workgroup per query gathers the segments, radix-selects the cut
+//           among the values inside b (8-bit digits below the 12 shared bits,
+//           stopping once the chosen bin holds one value), writes every value at or
+//           above the cut as positions in index order, then the tail, the padding
+//           and n_sel, and returns the histogram to zero for the next call.
+// If the values in b and above overflow what that workgroup holds (massive exact
 // ties), it runs the 4-pass algorithm above over the whole row instead.
 #include "sa_common.hpp"
 #include "sa_launch.hpp"
@@ -297,25 +297,6 @@ __device__ __forceinline__ QueryRowInfo query_blocks(const int32_t* seq_len, con
   return QueryRowInfo{n_vis / c, n_vis};
 }
 
-// True in every thread of the workgroup that arrives last at `counter` out of `n`
-// (the counter is returned to zero by that workgroup).  Releases this workgroup's
-// writes before arriving and acquires the others' in the last one.
-__device__ __forceinline__ bool arrive_last(uint32_t* counter, int n, int* lds_flag) {
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    __threadfence();
-    const uint32_t prev = atomicAdd(counter, 1u);
-    *lds_flag = (prev == (uint32_t)(n - 1));
-  }
-  __syncthreads();
-  const bool last = *lds_flag != 0;
-  if (last) {
-    __threadfence();
-    if (threadIdx.x == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  return last;
-}
-
 // Pass 1 (one workgroup per chunk): the chunk's histogram of the top 12 key bits is
 // added to the query's histogram.
 __global__ void __launch_bounds__(kHistThreads)
@@ -363,23 +344,19 @@ struct SelSmem {
   uint64_t cut;
 };
 
-// Pass 2 (one workgroup per chunk): the chunk keeps, in index order, every block
-// whose key lies in the recorded bin or above as (key << 32 | ~index) -- unique
-// values ordered exactly as (score desc, index asc).  The last chunk to arrive
-// gathers all entries, radix-selects the cut among those inside the bin (8-bit
-// digits below the shared 12 bits, stopping once the chosen bin holds one value),
-// and writes the list: every entry at or above the cut in index order, then the
-// tail and the padding.
+// Pass 2 (one workgroup per chunk): the chunk finds the bin holding the K_blk-th
+// largest key from the query's histogram and keeps, in index order, every block whose
+// key lies in that bin or above as (key << 32 | ~index) -- unique values ordered
+// exactly as (score desc, index asc).  Chunk 0 records the bin and the number still
+// to take inside it for pass 3; the dense case is written here.
 __global__ void __launch_bounds__(kSelThreads)
 chunk_select_kernel(const float* __restrict__ scores, int64_t scores_ld, const int32_t* __restrict__ seq_len,
                     const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos, int c, int k_blk,
                     int32_t* __restrict__ sel, int64_t sel_ld, int32_t* __restrict__ n_sel, WsState* __restrict__ st,
                     ChunkScratch sc) {
-  __shared__ union {
-    SelSmem f;
-    WgSmem w;
-  } sm;
-  const int q = blockIdx.y, tid = threadIdx.x, lane = tid % kWave;
+  __shared__ int scan[kSelThreads / kWave + 1];
+  __shared__ int pick[2];
+  const int q = blockIdx.y, tid = threadIdx.x;
   const int base = blockIdx.x * kChunk;
   const float* row = scores + (int64_t)q * scores_ld;
   uint32_t key[kSelKpt];
@@ -401,11 +378,10 @@ chunk_select_kernel(const float* __restrict__ scores, int64_t scores_ld, const i
     return;
   }
   if (base >= qr.nb) return;
-  const int n_chunks = (qr.nb + kChunk - 1) / kChunk;
   // the bin b holding the K_blk-th largest key, and how many to take inside it
-  find_top_bin<kSelThreads, PER1>(hc, k_blk, sm.f.scan, &sm.f.pick[0], &sm.f.pick[1]);
-  const uint32_t bin = (uint32_t)sm.f.pick[0];
-  int k_rem = k_blk - sm.f.pick[1];
+  find_top_bin<kSelThreads, PER1>(hc, k_blk, scan, &pick[0], &pick[1]);
+  const uint32_t bin = (uint32_t)pick[0];
+  int k_rem = k_blk - pick[1];
   // this chunk's entries, in index order
   bool keep[kSelKpt];
   int n = 0;
@@ -415,16 +391,43 @@ chunk_select_kernel(const float* __restrict__ scores, int64_t scores_ld, const i
     n += keep[j] ? 1 : 0;
   }
   int tot;
-  int slot = block_exclusive_scan<kSelThreads>(n, sm.f.scan, &tot);
+  int slot = block_exclusive_scan<kSelThreads>(n, scan, &tot);
   uint64_t* seg = sc.ent(q, blockIdx.x);
 #pragma unroll
   for (int j = 0; j < kSelKpt; ++j)
     if (keep[j]) seg[slot++] = ((uint64_t)key[j] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)idx[j]);
-  if (tid == 0) sc.n_ent(q)[blockIdx.x] = (uint32_t)tot;
-  if (!arrive_last(&st->sel_done[q], n_chunks, &sm.f.last)) return;
-  for (int b = tid; b < kBins1; b += kSelThreads) ghist[b] = 0u;   // every chunk has read it
+  if (tid == 0) {
+    sc.n_ent(q)[blockIdx.x] = (uint32_t)tot;
+    if (blockIdx.x == 0) {
+      sc.ctrl(q)[0] = bin;
+      sc.ctrl(q)[1] = (uint32_t)k_rem;
+    }
+  }
+}
 
-  // ---- the last chunk: gather, cut, write ---------------------------------------
+// Pass 3 (one workgroup per query, after every chunk's entries are written): gather
+// the entries, cut inside the bin, write the list, return the histogram to zero.
+__global__ void __launch_bounds__(kSelThreads)
+chunk_finish_kernel(const float* __restrict__ scores, int64_t scores_ld, const int32_t* __restrict__ seq_len,
+                    const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos, int c, int k_blk,
+                    int32_t* __restrict__ sel, int64_t sel_ld, int32_t* __restrict__ n_sel, WsState* __restrict__ st,
+                    ChunkScratch sc) {
+  __shared__ union {
+    SelSmem f;
+    WgSmem w;
+  } sm;
+  const int q = blockIdx.x, tid = threadIdx.x, lane = tid % kWave;
+  const float* row = scores + (int64_t)q * scores_ld;
+  const QueryRowInfo qr = query_blocks(seq_len, q_seq, q_pos, q, c);
+  if (qr.nb <= k_blk) return;                        // dense: written by the selection pass
+  int32_t* out = sel + (int64_t)q * sel_ld;
+  const int n_chunks = (qr.nb + kChunk - 1) / kChunk;
+  uint32_t* ghist = st->ghist[q];
+  for (int b = tid; b < kBins1; b += kSelThreads) ghist[b] = 0u;   // every chunk has read it
+  const uint32_t bin = sc.ctrl(q)[0];
+  int k_rem = (int)sc.ctrl(q)[1];
+
+  // ---- gather, cut, write ----------------------------------------------------------
   constexpr int PER = kMaxChunks / kSelThreads;      // 2 chunk counts per thread
   const int gcap = n_chunks < kMaxChunks ? n_chunks : kMaxChunks;
   uint32_t ne[PER];
@@ -432,7 +435,7 @@ chunk_select_kernel(const float* __restrict__ scores, int64_t scores_ld, const i
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
     const int w = tid * PER + j;
-    ne[j] = w < gcap ? coherent_load(&sc.n_ent(q)[w]) : 0u;
+    ne[j] = w < gcap ? sc.n_ent(q)[w] : 0u;
     loc += (int)ne[j];
   }
   int n_ent;
@@ -872,6 +875,8 @@ hipError_t launch_select(const sa_dims& d, const CacheArgs& c, const float* scor
                        q_pos, cr, k_blk, st, sc);
     hipLaunchKernelGGL(chunk_select_kernel, grid, dim3(kSelThreads), 0, stream, scores, scores_ld, c.seq_len, q_seq,
                        q_pos, cr, k_blk, sel, sel_ld, n_sel, st, sc);
+    hipLaunchKernelGGL(chunk_finish_kernel, dim3(n_q), dim3(kSelThreads), 0, stream, scores, scores_ld, c.seq_len,
+                       q_seq, q_pos, cr, k_blk, sel, sel_ld, n_sel, st, sc);
     return hipGetLastError();
   }
   if (max_blocks <= kWideMax) {                      // rows that fit one workgroup's registers
