@@ -334,13 +334,14 @@ chunk_hist_kernel(const float* __restrict__ scores, int64_t scores_ld, const int
   }
 }
 
+constexpr int kFinBins = 2048;                      // 11-bit digits of the cut inside the bin
 struct SelSmem {
   uint64_t ent[kEntCap];                             // 128 KiB
-  uint32_t hist[8 * kCopyStride];
+  uint32_t h[2][kFinBins];                           // alternating digit histograms
   uint32_t cpre[kMaxChunks + 1];                     // exclusive prefix of entries per chunk
   int scan[kSelThreads / kWave + 1];
-  int pick[3];
-  int last;
+  int wsum[2][kSelThreads / kWave];                  // per-wave totals of the picks
+  int pick[4];
   uint64_t cut;
 };
 
@@ -403,133 +404,6 @@ chunk_select_kernel(const float* __restrict__ scores, int64_t scores_ld, const i
       sc.ctrl(q)[1] = (uint32_t)k_rem;
     }
   }
-}
-
-// Pass 3 (one workgroup per query, after every chunk's entries are written): gather
-// the entries, cut inside the bin, write the list, return the histogram to zero.
-__global__ void __launch_bounds__(kSelThreads)
-chunk_finish_kernel(const float* __restrict__ scores, int64_t scores_ld, const int32_t* __restrict__ seq_len,
-                    const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos, int c, int k_blk,
-                    int32_t* __restrict__ sel, int64_t sel_ld, int32_t* __restrict__ n_sel, WsState* __restrict__ st,
-                    ChunkScratch sc) {
-  __shared__ union {
-    SelSmem f;
-    WgSmem w;
-  } sm;
-  const int q = blockIdx.x, tid = threadIdx.x, lane = tid % kWave;
-  const float* row = scores + (int64_t)q * scores_ld;
-  const QueryRowInfo qr = query_blocks(seq_len, q_seq, q_pos, q, c);
-  if (qr.nb <= k_blk) return;                        // dense: written by the selection pass
-  int32_t* out = sel + (int64_t)q * sel_ld;
-  const int n_chunks = (qr.nb + kChunk - 1) / kChunk;
-  uint32_t* ghist = st->ghist[q];
-  for (int b = tid; b < kBins1; b += kSelThreads) ghist[b] = 0u;   // every chunk has read it
-  const uint32_t bin = sc.ctrl(q)[0];
-  int k_rem = (int)sc.ctrl(q)[1];
-
-  // ---- gather, cut, write ----------------------------------------------------------
-  constexpr int PER = kMaxChunks / kSelThreads;      // 2 chunk counts per thread
-  const int gcap = n_chunks < kMaxChunks ? n_chunks : kMaxChunks;
-  uint32_t ne[PER];
-  int loc = 0;
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const int w = tid * PER + j;
-    ne[j] = w < gcap ? sc.n_ent(q)[w] : 0u;
-    loc += (int)ne[j];
-  }
-  int n_ent;
-  int cp = block_exclusive_scan<kSelThreads>(loc, sm.f.scan, &n_ent);
-  if (n_ent > kEntCap || n_chunks > kMaxChunks) {   // massive exact ties: per-query select over the row
-    select_one_query<kSelThreads, 8>(row, qr.nb, qr.n_vis, c, k_blk, out, sel_ld, n_sel + q, sm.w);
-    return;
-  }
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    sm.f.cpre[tid * PER + j] = (uint32_t)cp;
-    cp += (int)ne[j];
-  }
-  __syncthreads();
-  for (int e = tid; e < n_ent; e += kSelThreads) {
-    int lo = 0, hi = n_chunks - 1;                   // largest w with cpre[w] <= e
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if ((int)sm.f.cpre[mid] <= e) lo = mid;
-      else hi = mid - 1;
-    }
-    sm.f.ent[e] = sc.ent(q, lo)[e - (int)sm.f.cpre[lo]];
-  }
-  __syncthreads();
-  // k_rem-th largest value among the entries inside the bin (top 12 bits == bin)
-  uint64_t prefix = bin;
-  for (int shift = 64 - kTopBits; shift > 0;) {
-    const int width = shift >= 8 ? 8 : shift;
-    shift -= width;
-    const uint32_t dmask = (1u << width) - 1u;
-    for (int e = tid; e < 8 * kCopyStride; e += kSelThreads) sm.f.hist[e] = 0u;
-    __syncthreads();
-    uint32_t* mine = sm.f.hist + (lane & 7) * kCopyStride;
-    for (int e = tid; e < n_ent; e += kSelThreads) {
-      const uint64_t v = sm.f.ent[e];
-      if ((v >> (shift + width)) == prefix) atomicAdd(&mine[(uint32_t)(v >> shift) & dmask], 1u);
-    }
-    __syncthreads();
-    if (tid < kBins) {                               // 4 whole waves
-      uint32_t cnt = 0;
-#pragma unroll
-      for (int cpy = 0; cpy < 8; ++cpy) cnt += sm.f.hist[cpy * kCopyStride + tid];
-      sm.f.hist[tid] = cnt;                          // copy 0 now holds the totals
-    }
-    __syncthreads();
-    int ge_in_wave = 0;
-    if (tid < kBins) {
-      ge_in_wave = wave_inclusive_scan((int)sm.f.hist[kBins - 1 - tid], lane);
-      if (lane == kWave - 1) sm.f.scan[tid / kWave] = ge_in_wave;
-    }
-    __syncthreads();
-    if (tid < kBins) {
-      const int v = kBins - 1 - tid;
-      int b = 0;
-      for (int w = 0; w < tid / kWave; ++w) b += sm.f.scan[w];
-      const int ge = b + ge_in_wave, cnt = (int)sm.f.hist[v], gt = ge - cnt;
-      if (gt < k_rem && ge >= k_rem) {
-        sm.f.pick[0] = v;
-        sm.f.pick[1] = k_rem - gt;
-        sm.f.pick[2] = cnt;
-      }
-    }
-    __syncthreads();
-    prefix = (prefix << width) | (uint64_t)sm.f.pick[0];
-    k_rem = sm.f.pick[1];
-    const int cnt = sm.f.pick[2];
-    __syncthreads();
-    if (cnt == 1 || shift == 0) {                    // the cut is the single value left in the bin
-      for (int e = tid; e < n_ent; e += kSelThreads) {
-        const uint64_t v = sm.f.ent[e];
-        if ((v >> shift) == prefix) sm.f.cut = v;
-      }
-      __syncthreads();
-      break;
-    }
-  }
-  const uint64_t cut = sm.f.cut;
-  // kept entries (value >= cut) in index order -> positions
-  const int per = (n_ent + kSelThreads - 1) / kSelThreads;
-  const int e0 = tid * per, e1 = min(n_ent, e0 + per);
-  int nk = 0;
-  for (int e = e0; e < e1; ++e) nk += sm.f.ent[e] >= cut ? 1 : 0;
-  int ktot;
-  int o = block_exclusive_scan<kSelThreads>(nk, sm.f.scan, &ktot);
-  for (int e = e0; e < e1; ++e) {
-    const uint64_t v = sm.f.ent[e];
-    if (v >= cut && o < k_blk) {                     // o < k_blk always; the bound only guards memory
-      const int32_t p0 = (int32_t)(0xFFFFFFFFu - (uint32_t)v) * c;
-      int32_t* dst = out + (int64_t)o * c;
-      for (int t = 0; t < c; ++t) dst[t] = p0 + t;
-      ++o;
-    }
-  }
-  write_tail<kSelThreads>(out, sel_ld, qr.nb, qr.n_vis, c, k_blk, n_sel + q);
 }
 
 // ------------------------------------------------------ one wide workgroup per row
@@ -831,6 +705,154 @@ select_wide_kernel(const float* __restrict__ scores, int64_t scores_ld, const in
     }
   }
   write_tail<kWideThreads>(out, sel_ld, nb, qr.n_vis, c, k_blk, n_sel + q);
+}
+
+// ------------------------------------------------------------ chunked: finish
+
+// Pass 3 (one workgroup per query, after every chunk's entries are written): gather
+// the entries, cut inside the bin, write the list, return the histogram to zero.
+__global__ void __launch_bounds__(kSelThreads)
+chunk_finish_kernel(const float* __restrict__ scores, int64_t scores_ld, const int32_t* __restrict__ seq_len,
+                    const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos, int c, int k_blk,
+                    int32_t* __restrict__ sel, int64_t sel_ld, int32_t* __restrict__ n_sel, WsState* __restrict__ st,
+                    ChunkScratch sc) {
+  __shared__ union {
+    SelSmem f;
+    WgSmem w;
+  } sm;
+  const int q = blockIdx.x, tid = threadIdx.x;
+  const float* row = scores + (int64_t)q * scores_ld;
+  // Scratch of up to 256 chunks: every chunk's count and its first entries are read
+  // at once, before the query's length (and so its chunk count) is known -- one round
+  // trip instead of three.  Thread t serves chunk t / tpc, entries t % tpc + tpc*i.
+  constexpr int kSpecB = 4;
+  const bool spec = sc.g <= kSelThreads / 4;
+  int tpc = 1;                                       // a power of two, <= kChunk / kSpecB
+  while (tpc * 2 * sc.g <= kSelThreads && tpc * 2 * kSpecB <= kChunk) tpc *= 2;
+  const int cw = tid / tpc, cr = tid % tpc;
+  uint32_t ne_w = 0u;
+  uint64_t sv[kSpecB];
+  if (spec && cw < sc.g) {
+    ne_w = sc.n_ent(q)[cw];
+    const uint64_t* seg = sc.ent(q, cw);
+#pragma unroll
+    for (int i = 0; i < kSpecB; ++i) sv[i] = seg[cr + tpc * i];   // < kChunk: inside the segment
+  }
+  const uint32_t bin = sc.ctrl(q)[0];
+  int k_rem = (int)sc.ctrl(q)[1];
+  const QueryRowInfo qr = query_blocks(seq_len, q_seq, q_pos, q, c);
+  if (qr.nb <= k_blk) return;                        // dense: written by the selection pass
+  int32_t* out = sel + (int64_t)q * sel_ld;
+  const int n_chunks = (qr.nb + kChunk - 1) / kChunk;
+  uint32_t* ghist = st->ghist[q];
+  for (int b = tid; b < kBins1; b += kSelThreads) ghist[b] = 0u;   // every chunk has read it
+
+  // ---- gather, cut, write ----------------------------------------------------------
+  int n_ent;
+  if (spec) {
+    if (cw >= n_chunks) ne_w = 0u;
+    // exclusive prefix over the chunks: only each chunk's first thread contributes
+    const int cp = block_exclusive_scan<kSelThreads>(cr == 0 ? (int)ne_w : 0, sm.f.scan, &n_ent);
+    if (n_ent > kEntCap) {                           // massive exact ties: per-query select over the row
+      select_one_query<kSelThreads, 8>(row, qr.nb, qr.n_vis, c, k_blk, out, sel_ld, n_sel + q, sm.w);
+      return;
+    }
+    if (cr == 0 && cw < n_chunks) sm.f.cpre[cw] = (uint32_t)cp;
+    __syncthreads();
+    if (cw < n_chunks && ne_w > 0u) {
+      const int base_e = (int)sm.f.cpre[cw];
+#pragma unroll
+      for (int i = 0; i < kSpecB; ++i)
+        if (cr + tpc * i < (int)ne_w) sm.f.ent[base_e + cr + tpc * i] = sv[i];
+      const uint64_t* seg = sc.ent(q, cw);
+      for (int k = cr + tpc * kSpecB; k < (int)ne_w; k += tpc) sm.f.ent[base_e + k] = seg[k];
+    }
+  } else {
+    constexpr int PER = kMaxChunks / kSelThreads;    // 2 chunk counts per thread
+    const int gcap = n_chunks < kMaxChunks ? n_chunks : kMaxChunks;
+    uint32_t ne[PER];
+    int loc = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int w = tid * PER + j;
+      ne[j] = w < gcap ? sc.n_ent(q)[w] : 0u;
+      loc += (int)ne[j];
+    }
+    int cp = block_exclusive_scan<kSelThreads>(loc, sm.f.scan, &n_ent);
+    if (n_ent > kEntCap || n_chunks > kMaxChunks) {   // massive exact ties: per-query select over the row
+      select_one_query<kSelThreads, 8>(row, qr.nb, qr.n_vis, c, k_blk, out, sel_ld, n_sel + q, sm.w);
+      return;
+    }
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      sm.f.cpre[tid * PER + j] = (uint32_t)cp;
+      cp += (int)ne[j];
+    }
+    __syncthreads();
+    for (int e = tid; e < n_ent; e += kSelThreads) {
+      int lo = 0, hi = n_chunks - 1;                 // largest w with cpre[w] <= e
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if ((int)sm.f.cpre[mid] <= e) lo = mid;
+        else hi = mid - 1;
+      }
+      sm.f.ent[e] = sc.ent(q, lo)[e - (int)sm.f.cpre[lo]];
+    }
+  }
+  __syncthreads();
+  // k_rem-th largest value among the entries inside the bin (top 12 bits == bin):
+  // 11-bit digits below them, each bin found with the hierarchical pick; two
+  // histograms, each cleared while the other counts; stop once the chosen bin holds
+  // one value (values are unique).
+  for (int b = tid; b < kFinBins; b += kSelThreads) {
+    sm.f.h[0][b] = 0u;
+    sm.f.h[1][b] = 0u;
+  }
+  __syncthreads();
+  uint64_t prefix = bin;
+  for (int shift = 64 - kTopBits, pass = 0; shift > 0; ++pass) {
+    const int width = shift >= 11 ? 11 : shift;
+    shift -= width;
+    const uint32_t dmask = (1u << width) - 1u;
+    uint32_t* h = sm.f.h[pass & 1];
+    for (int e = tid; e < n_ent; e += kSelThreads) {
+      const uint64_t v = sm.f.ent[e];
+      if ((v >> (shift + width)) == prefix) atomicAdd(&h[(uint32_t)(v >> shift) & dmask], 1u);
+    }
+    if (pass > 0)                                    // the previous pass's (read before its pick), for the next
+      for (int b = tid; b < kFinBins; b += kSelThreads) sm.f.h[(pass + 1) & 1][b] = 0u;
+    __syncthreads();
+    uint32_t cnt2[2] = {h[2 * tid], h[2 * tid + 1]};
+    wide_pick<2>(cnt2, k_rem, 0, sm.f.wsum[pass & 1], sm.f.pick);
+    prefix = (prefix << width) | (uint64_t)sm.f.pick[0];
+    k_rem -= sm.f.pick[1];
+    if (sm.f.pick[2] == 1 || shift == 0) {           // the cut is the single value left in the bin
+      for (int e = tid; e < n_ent; e += kSelThreads) {
+        const uint64_t v = sm.f.ent[e];
+        if ((v >> shift) == prefix) sm.f.cut = v;
+      }
+      __syncthreads();
+      break;
+    }
+  }
+  const uint64_t cut = sm.f.cut;
+  // kept entries (value >= cut) in index order -> positions
+  const int per = (n_ent + kSelThreads - 1) / kSelThreads;
+  const int e0 = tid * per, e1 = min(n_ent, e0 + per);
+  int nk = 0;
+  for (int e = e0; e < e1; ++e) nk += sm.f.ent[e] >= cut ? 1 : 0;
+  int ktot;
+  int o = block_exclusive_scan<kSelThreads>(nk, sm.f.scan, &ktot);
+  for (int e = e0; e < e1; ++e) {
+    const uint64_t v = sm.f.ent[e];
+    if (v >= cut && o < k_blk) {                     // o < k_blk always; the bound only guards memory
+      const int32_t p0 = (int32_t)(0xFFFFFFFFu - (uint32_t)v) * c;
+      int32_t* dst = out + (int64_t)o * c;
+      for (int t = 0; t < c; ++t) dst[t] = p0 + t;
+      ++o;
+    }
+  }
+  write_tail<kSelThreads>(out, sel_ld, qr.nb, qr.n_vis, c, k_blk, n_sel + q);
 }
 
 // ---------------------------------------------------------------------------- host

@@ -212,6 +212,31 @@ def test_select_on_adversarial_score_rows(gpu_lib, seq_len, top_k):
     say(f"[parity] select rows seq_len={seq_len} top_k={top_k}: ok")
 
 
+def test_select_chunked_many_chunks(gpu_lib):
+    # token-level rows of 600001 blocks: more chunks (293) than the finishing
+    # workgroup reads speculatively, so it takes the counted gather; ties across the
+    # cut and a ragged shorter row
+    d = dims(h_q=16, d_kq=128, d_v=128, h_idx=1, d_idx=64, compress_ratio=1, top_k=4096, dtype="bf16")
+    L = 600001
+    kinds = ("normal", "small_ints", "lognormal_dups")
+    q_pos = [L - 1] * len(kinds) + [L - 1 - 70001]
+    case = datagen.make_case("select_many_chunks", d, [L], [0] * len(q_pos), q_pos, seed=0, case_id=247, std=1.0,
+                             v_separate=False)
+    layer = DeviceLayer(case)
+    rows, want = [], []
+    for i, p in enumerate(q_pos):
+        n_vis = oracle.visible_tokens(L, p)
+        s_ = datagen.score_row(kinds[i % len(kinds)], n_vis, d.top_k, seed=0, case_id=248 + i)
+        rows.append(s_)
+        want.append(oracle.select_positions(s_, n_vis, 1, d.top_k))
+    layer.select(scores=parity.upload_scores(layer, rows))
+    torch.cuda.synchronize()
+    got = layer.selections()
+    for i in range(len(q_pos)):
+        assert np.array_equal(got[i], want[i]), f"row {i}: selection differs"
+    say("[parity] select rows of 600001 blocks: ok")
+
+
 def test_max_list_capacity(gpu_lib):
     # the largest list the library accepts: top_k + c - 1 = 65536
     d = dims(h_q=16, d_kq=128, d_v=128, h_idx=32, d_idx=64, compress_ratio=1, top_k=65536, dtype="bf16")
