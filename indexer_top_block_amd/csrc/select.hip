@@ -238,7 +238,7 @@ constexpr int kSelKpt = kChunk / kSelThreads;        // 2
 constexpr int kTopBits = 12;
 constexpr int kBins1 = 1 << kTopBits;                // 4096 bins of the top 12 bits
 constexpr int kHistCopies = 4;
-constexpr int kEntCap = 16384;                       // entries the last workgroup holds in LDS
+constexpr int kEntCap = 16384;                       // entries the finishing workgroup holds in LDS
 constexpr int kMaxChunks = 2048;                     // chunks per query it tallies
 
 struct QueryRowInfo {
