@@ -184,7 +184,7 @@ def test_select_streams_long_score_rows(gpu_lib):
     run_and_check(case, queries=[0, 1, 40, 79])
 
 
-@pytest.mark.parametrize("seq_len,top_k", [(131072, 2048), (16000, 256)])
+@pytest.mark.parametrize("seq_len,top_k", [(131072, 2048), (60000, 1024), (30000, 512), (16000, 256)])
 def test_select_on_adversarial_score_rows(gpu_lib, seq_len, top_k):
     # the select kernel alone on score rows no scoring produces: negative scores,
     # few distinct values, all equal, signed zeros, a whole binade at the cut, ties
