@@ -434,14 +434,21 @@ chunk_select_kernel(const float* __restrict__ scores, int64_t scores_ld, const i
 constexpr int kWideThreads = 1024;
 constexpr int kWideMaxKpt = 32;
 constexpr int kWideBins = 2048;
-constexpr int kWideCopies = 16;                      // pass-1 copies: lanes l, l+16, l+32, l+48 share one
-constexpr int kWideWords = kWideThreads * kWideMaxKpt / 32;   // bitmap words, 64 per wave
+// Pass-1 histogram copies and bitmap words by row size: rows of up to 16384 keys take
+// 8 copies and their own bitmap size, so that the workgroup's LDS (< 80 KiB) and
+// registers leave room for a second workgroup on the CU (prefill: many rows).
+template <int KPT>
+struct WideCfg {
+  static constexpr int copies = KPT >= 32 ? 16 : 8;  // lanes l, l+copies, ... share a copy
+  static constexpr int words = KPT * 32;             // bitmap words (32 blocks each)
+};
 
+template <int KPT>
 struct alignas(16) WideSmem {
   uint32_t h2[kWideBins];                            // pass 2 (first: its bins' addresses need no base)
-  uint32_t h1[kWideBins * kWideCopies];              // pass 1 [bin][copy]; pass 3: words 0..1023; the list
-  uint32_t keep[kWideWords];                         // blocks at or above the threshold
-  uint32_t tie[kWideWords];                          // blocks equal to T (full-width search)
+  uint32_t h1[kWideBins * WideCfg<KPT>::copies];    // pass 1 [bin][copy]; pass 3: words 0..1023; the list
+  uint32_t keep[WideCfg<KPT>::words];                // blocks at or above the threshold
+  uint32_t tie[WideCfg<KPT>::words];                 // blocks equal to T (full-width search)
   int wsum[2][kWideThreads / kWave];                 // per-wave totals, alternating between picks
   int pick[4];
 };
@@ -493,10 +500,11 @@ __device__ __forceinline__ void wide_pick(uint32_t (&cnt)[PER], int k, int pad, 
   __syncthreads();
 }
 
-// Set bits in the bitmap words before word 64 * wave (lane l reads words [16 l, 16 l + 16)).
-__device__ __forceinline__ int bits_before(const uint32_t* bm, int wave, int lane) {
+// Set bits in the bitmap words before word 64 * wave (lane l reads words [16 l, 16 l + 16));
+// the bitmap holds `words` words.
+__device__ __forceinline__ int bits_before(const uint32_t* bm, int words, int wave, int lane) {
   int n = 0;
-  if (lane < 4 * wave) {
+  if (lane < 4 * wave && lane * 16 < words) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint4 v = *(const uint4*)&bm[lane * 16 + i * 4];
@@ -538,7 +546,8 @@ __global__ void __launch_bounds__(kWideThreads)
 select_wide_kernel(const float* __restrict__ scores, int64_t scores_ld, const int32_t* __restrict__ seq_len,
                    const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos, int c, int k_blk,
                    int32_t* __restrict__ sel, int64_t sel_ld, int32_t* __restrict__ n_sel) {
-  __shared__ WideSmem sm;
+  constexpr int COPIES = WideCfg<KPT>::copies, WORDS = WideCfg<KPT>::words;
+  __shared__ WideSmem<KPT> sm;
   const int q = blockIdx.x, tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const float* row = scores + (int64_t)q * scores_ld;
   // The whole row is loaded up front and kept in registers for every pass; the
@@ -550,10 +559,8 @@ select_wide_kernel(const float* __restrict__ scores, int64_t scores_ld, const in
     for (int j = 0; j < KPT; ++j) raw[j] = row[min(j * kWideThreads + tid, last)];
   }
   const QueryRowInfo qr = query_blocks(seq_len, q_seq, q_pos, q, c);
-  for (int e = tid; e < kWideBins * kWideCopies / 4; e += kWideThreads) ((uint4*)sm.h1)[e] = uint4{0u, 0u, 0u, 0u};
+  for (int e = tid; e < kWideBins * COPIES / 4; e += kWideThreads) ((uint4*)sm.h1)[e] = uint4{0u, 0u, 0u, 0u};
   for (int e = tid; e < kWideBins; e += kWideThreads) sm.h2[e] = 0u;
-  sm.keep[tid] = 0u;
-  sm.tie[tid] = 0u;
   __builtin_amdgcn_sched_barrier(0);                 // every load in flight before the first is used
   int32_t* out = sel + (int64_t)q * sel_ld;
   if (qr.nb <= k_blk) {
@@ -571,34 +578,35 @@ select_wide_kernel(const float* __restrict__ scores, int64_t scores_ld, const in
   // never takes its bin whole, so they are never kept.
   uint32_t key[KPT];
   {
-    uint32_t* mine = sm.h1 + (lane & (kWideCopies - 1));
+    uint32_t* mine = sm.h1 + (lane & (COPIES - 1));
     if (n_pad == 0) {
 #pragma unroll
       for (int j = 0; j < KPT; ++j) {
         key[j] = score_key(raw[j]);
-        atomicAdd(&mine[(key[j] >> 21) * kWideCopies], 1u);
+        atomicAdd(&mine[(key[j] >> 21) * COPIES], 1u);
       }
     } else {
 #pragma unroll
       for (int j = 0; j < KPT; ++j) {
         key[j] = j * kWideThreads + tid < nb ? score_key(raw[j]) : 0u;
-        atomicAdd(&mine[(key[j] >> 21) * kWideCopies], 1u);
+        atomicAdd(&mine[(key[j] >> 21) * COPIES], 1u);
       }
     }
   }
   __syncthreads();
   {
-    // thread t: bins 2t and 2t+1, 32 words read as 8 quads from a lane-rotated start,
-    // so that 8 consecutive lanes cover all 32 banks
+    // thread t: bins 2t and 2t+1, their copies read as quads from a lane-rotated start,
+    // so that consecutive lanes spread over the banks
+    constexpr int NQD = 2 * COPIES / 4;              // quads; the first half: bin 2t
     uint32_t cnt[2] = {0u, 0u};
-    const uint4* h = (const uint4*)(sm.h1 + tid * 2 * kWideCopies);
+    const uint4* h = (const uint4*)(sm.h1 + tid * 2 * COPIES);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int quad = (i + tid) & 7;                // quads 0..3: bin 2t, 4..7: bin 2t+1
+    for (int i = 0; i < NQD; ++i) {
+      const int quad = (i + tid) & (NQD - 1);
       const uint4 v = h[quad];
       const uint32_t s4 = v.x + v.y + v.z + v.w;
-      cnt[0] += quad < 4 ? s4 : 0u;
-      cnt[1] += quad < 4 ? 0u : s4;
+      cnt[0] += quad < NQD / 2 ? s4 : 0u;
+      cnt[1] += quad < NQD / 2 ? 0u : s4;
     }
     wide_pick<2>(cnt, k_blk, n_pad, sm.wsum[0], sm.pick);
   }
@@ -659,11 +667,11 @@ select_wide_kernel(const float* __restrict__ scores, int64_t scores_ld, const in
   __syncthreads();
   // ---- this wave's 64 words -> positions in index order ---------------------------------------
   const int w = wave * kWave + lane;                 // bitmap word of this lane: blocks 32w .. 32w+31
-  uint32_t word = sm.keep[w];
-  int o = bits_before(sm.keep, wave, lane);
+  uint32_t word = w < WORDS ? sm.keep[w] : 0u;
+  int o = bits_before(sm.keep, WORDS, wave, lane);
   if (!whole) {                                      // the first k_rem tied blocks in index order
-    uint32_t t = sm.tie[w];
-    const int t_before = bits_before(sm.tie, wave, lane);
+    uint32_t t = w < WORDS ? sm.tie[w] : 0u;
+    const int t_before = bits_before(sm.tie, WORDS, wave, lane);
     o += min(k_rem, t_before);
     int take = k_rem - t_before - (wave_inclusive_scan(__popc(t), lane) - __popc(t));
     while (t != 0u && take > 0) {
@@ -675,7 +683,7 @@ select_wide_kernel(const float* __restrict__ scores, int64_t scores_ld, const in
   }
   o += wave_inclusive_scan(__popc(word), lane) - __popc(word);
   const int body = k_blk * c;
-  if (body <= kWideBins * kWideCopies) {
+  if (body <= kWideBins * COPIES) {
     // the list is assembled in LDS (pass 1's histogram is free) and written out
     // coalesced, rather than as scattered stores of a few lanes each
     int32_t* list = (int32_t*)sm.h1;
