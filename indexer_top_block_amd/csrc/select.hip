@@ -751,7 +751,7 @@ chunk_finish_kernel(const float* __restrict__ scores, int64_t scores_ld, const i
   const QueryRowInfo qr = query_blocks(seq_len, q_seq, q_pos, q, c);
   if (qr.nb <= k_blk) return;                        // dense: written by the selection pass
   int32_t* out = sel + (int64_t)q * sel_ld;
-  const int n_chunks = (qr.nb + kChunk - 1) / kChunk;
+  const int n_chunks = min((qr.nb + kChunk - 1) / kChunk, sc.g);   // (a length beyond max_len is clamped)
   uint32_t* ghist = st->ghist[q];
   for (int b = tid; b < kBins1; b += kSelThreads) ghist[b] = 0u;   // every chunk has read it
 
