@@ -648,7 +648,7 @@ fwd_lds_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, i
 // MAXS splits every partial value and statistic is loaded into registers before any
 // is used (indices clamped, not guarded), so the combine costs one round trip;
 // beyond that the splits stream in chunks.
-constexpr int kCombineThreads = 128;
+constexpr int kCombineThreads = 64;
 
 template <int MAXS>
 __global__ void __launch_bounds__(kCombineThreads)
