@@ -184,6 +184,17 @@ def test_select_streams_long_score_rows(gpu_lib):
     run_and_check(case, queries=[0, 1, 40, 79])
 
 
+def test_score_long_rows_several_queries(gpu_lib):
+    # long rows (several thousand scoring workgroups, several rounds of them per CU)
+    # with several queries, two sequences and ragged tails, for two indexer shapes
+    for j, (h_idx, d_idx, dt) in enumerate(((64, 128, "bf16"), (128, 64, "f16"))):
+        d = dims(h_q=8, d_kq=128, d_v=128, h_idx=h_idx, d_idx=d_idx, compress_ratio=1, top_k=2048, dtype=dt)
+        case = datagen.make_case(f"score_long_{j}", d, [70001, 52003], [0, 0, 0, 1, 1, 1],
+                                 [70000, 69000, 33333, 52002, 40961, 5], seed=0, case_id=250 + j,
+                                 std="inv_sqrt_dim", v_separate=True)
+        run_and_check(case, components=False)
+
+
 @pytest.mark.parametrize("seq_len,top_k", [(131072, 2048), (60000, 1024), (30000, 512), (16000, 256)])
 def test_select_on_adversarial_score_rows(gpu_lib, seq_len, top_k):
     # the select kernel alone on score rows no scoring produces: negative scores,
@@ -765,3 +776,22 @@ def test_pool_score_full_size_decode(gpu_lib):
     assert torch.equal(n0, n1) and torch.equal(kp0.view(torch.int16), kp1.view(torch.int16))
     assert torch.equal(s0.view(torch.int32), s1.view(torch.int32))
     say("[parity] pool+score fused at 128K and the 70-token fallback: bit for bit")
+
+
+def test_pool_score_long_rows(gpu_lib):
+    # pooling inside the scoring launch on long rows: the token-level decode step as
+    # the benchmark launches it, and a fresh cache of long rows (every block new,
+    # pooled by the scoring waves in rounds), both bit for bit equal to pool then score
+    say(f"[parity] generating workload 6: {datagen.WORKLOADS[6]}")
+    case = datagen.make_workload(6)
+    nb = int(case.seq_len[0]) // case.dims.compress_ratio
+    (kp0, n0, s0), (kp1, n1, s1) = _pool_then_score(case, nb - 1, 1)
+    assert torch.equal(n0, n1) and torch.equal(kp0.view(torch.int16), kp1.view(torch.int16))
+    assert torch.equal(s0.view(torch.int32), s1.view(torch.int32))
+    d = dims(h_q=8, d_kq=128, d_v=128, compress_ratio=1, top_k=2048)
+    fresh = datagen.make_case("ps_long", d, [70001, 52003], [0, 0, 1], [70000, 12345, 52002], seed=0, case_id=604,
+                              std="inv_sqrt_dim", v_separate=True)
+    (kp0, n0, s0), (kp1, n1, s1) = _pool_then_score(fresh, None, 2 ** 30)
+    assert torch.equal(n0, n1) and torch.equal(kp0.view(torch.int16), kp1.view(torch.int16))
+    assert torch.equal(s0.view(torch.int32), s1.view(torch.int32))
+    say("[parity] pool+score fused on long rows: bit for bit")
