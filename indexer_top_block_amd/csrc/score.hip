@@ -342,8 +342,9 @@ score_gemm_kernel(const T* __restrict__ qidx, const T* __restrict__ kpool, int64
       if (b0 >= nb) break;                           // uniform per wave
       const int key = nt * 32 + n;
       const T* krow = buf + key * D;
-      // one B step at a time, shared by the M tiles (a register budget of 128 lets two
-      // workgroups share a CU)
+      // one B step at a time, shared by the M tiles (the compiler keeps several steps'
+      // reads in flight: ~170 registers for 64 heads of 128 dims, so one workgroup per
+      // CU; a 128-register build, two workgroups per CU, spills and is no faster)
       f32x16 acc[MT];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x16{};
