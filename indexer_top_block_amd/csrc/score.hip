@@ -37,6 +37,12 @@ __device__ __forceinline__ f32x16 mfma32x32x16<f16>(const f16x8& a, const f16x8&
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
+// max(x, 0) as one integer max on the bit pattern: every float with the sign bit set
+// (negatives and -0) reads as a negative integer and becomes +0; the rest keep their
+// value.  fmaxf takes a second instruction per element (it quiets a possible
+// signalling NaN first) and gives the same result for every non-NaN x.
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 constexpr int kScoreWaves = 4;        // waves per workgroup
 constexpr int kScoreTile = 32;        // blocks per wave tile (MFMA N)
 
@@ -215,7 +221,7 @@ score_mfma_kernel(const T* __restrict__ qidx, const T* __restrict__ kpool, int64
 #pragma unroll
     for (int st = 0; st < KS; ++st) acc = mfma32x32x16<T>(*reinterpret_cast<const V8*>(qa + st * 8), kb[st], acc);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sum += fmaxf(acc[r], 0.f);
+    for (int r = 0; r < 16; ++r) sum += relu(acc[r]);
   }
   sum += __shfl_xor(sum, 32);
   if (hf == 0 && valid) scores[(int64_t)i * scores_ld + b] = sum + 0.0f;  // +0.0 turns -0.0 into +0.0
@@ -296,7 +302,7 @@ score_gemm_kernel(const T* __restrict__ qidx, const T* __restrict__ kpool, int64
 #pragma unroll
       for (int st = 0; st < KS; ++st) acc = mfma32x32x16<T>(qa[mt][st], kb[st], acc);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sum += fmaxf(acc[r], 0.f);
+      for (int r = 0; r < 16; ++r) sum += relu(acc[r]);
     }
     sum += __shfl_xor(sum, 32);
     if (hf == 0 && b < nb) srow[b] = sum + 0.0f;     // +0.0 turns -0.0 into +0.0
@@ -358,7 +364,7 @@ score_gemm_kernel(const T* __restrict__ qidx, const T* __restrict__ kpool, int64
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sum += fmaxf(acc[mt][r], 0.f);
+        for (int r = 0; r < 16; ++r) sum += relu(acc[mt][r]);
       sum += __shfl_xor(sum, 32);
       const int b = b0 + n;
       if (hf == 0 && b < nb) srow[b] = sum + 0.0f;   // +0.0 turns -0.0 into +0.0
