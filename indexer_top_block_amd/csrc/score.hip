@@ -342,32 +342,54 @@ score_gemm_kernel(const T* __restrict__ qidx, const T* __restrict__ kpool, int64
                                        (lds_void*)(buf + k0 * D), 16, 0, 0);
     }
   };
+  // the products of one 32-block step of a tile: acc[mt] = heads mt*32.. x blocks
+  // (B read once per step from LDS and shared by the M tiles)
+  auto products = [&](const T* buf, int nt, f32x16 (&acc)[MT]) {
+    const int key = nt * 32 + n;
+    const T* krow = buf + key * D;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x16{};
+#pragma unroll
+    for (int st = 0; st < KS; ++st) {
+      const V8 kb = *reinterpret_cast<const V8*>(krow + (((hf * (CH / 2) + st) ^ (key & (CH - 1))) * 8));
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma32x32x16<T>(qa[mt][st], kb, acc[mt]);
+    }
+  };
+  // ReLU and head sum of one step: lane (n, hf) holds 16 heads of block n per M tile,
+  // the partner lane n ^ 32 the other 16
+  auto reduce = [&](const f32x16 (&acc)[MT]) {
+    float sum = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sum += relu(acc[mt][r]);
+    return sum + __shfl_xor(sum, 32);
+  };
+  // A tile's four steps, software-pipelined over two accumulator sets: step nt+1's
+  // products are issued before step nt's epilogue, so the matrix pipe works while
+  // the epilogue runs; the scores are stored after the last step (the last tile's
+  // steps past nb multiply clamped keys and store nothing).  (~180 registers for 64
+  // heads of 128 dims, so one workgroup per CU; a 128-register build, two
+  // workgroups per CU, spills and is no faster.)
   auto multiply = [&](int t, const T* buf) {
-    for (int nt = 0; nt < kGemmBN / 32; ++nt) {
-      const int b0 = t * kGemmBN + nt * 32;
-      if (b0 >= nb) break;                           // uniform per wave
-      const int key = nt * 32 + n;
-      const T* krow = buf + key * D;
-      // one B step at a time, shared by the M tiles (the compiler keeps several steps'
-      // reads in flight: ~170 registers for 64 heads of 128 dims, so one workgroup per
-      // CU; a 128-register build, two workgroups per CU, spills and is no faster)
-      f32x16 acc[MT];
+    if (t * kGemmBN >= nb) return;                   // uniform per wave
+    constexpr int NT = kGemmBN / 32;
+    static_assert(NT % 2 == 0, "steps pair up over the two accumulator sets");
+    float sums[NT];
+    f32x16 acc0[MT], acc1[MT];
+    products(buf, 0, acc0);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x16{};
+    for (int nt = 0; nt < NT; nt += 2) {
+      products(buf, nt + 1, acc1);
+      sums[nt] = reduce(acc0);
+      if (nt + 2 < NT) products(buf, nt + 2, acc0);
+      sums[nt + 1] = reduce(acc1);
+    }
 #pragma unroll
-      for (int st = 0; st < KS; ++st) {
-        const V8 kb = *reinterpret_cast<const V8*>(krow + (((hf * (CH / 2) + st) ^ (key & (CH - 1))) * 8));
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma32x32x16<T>(qa[mt][st], kb, acc[mt]);
-      }
-      float sum = 0.f;
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sum += relu(acc[mt][r]);
-      sum += __shfl_xor(sum, 32);
-      const int b = b0 + n;
-      if (hf == 0 && b < nb) srow[b] = sum + 0.0f;   // +0.0 turns -0.0 into +0.0
+    for (int nt = 0; nt < NT; ++nt) {
+      const int b = t * kGemmBN + nt * 32 + n;
+      if (hf == 0 && b < nb) srow[b] = sums[nt] + 0.0f;   // +0.0 turns -0.0 into +0.0
     }
   };
   issue(t_begin, ks0);
