@@ -369,7 +369,7 @@ score_gemm_kernel(const T* __restrict__ qidx, const T* __restrict__ kpool, int64
   // A tile's four steps, software-pipelined over two accumulator sets: step nt+1's
   // products are issued before step nt's epilogue, so the matrix pipe works while
   // the epilogue runs; the scores are stored after the last step (the last tile's
-  // steps past nb multiply clamped keys and store nothing).  (~180 registers for 64
+  // steps past nb multiply clamped keys and store nothing).  (~220 registers for 64
   // heads of 128 dims, so one workgroup per CU; a 128-register build, two
   // workgroups per CU, spills and is no faster.)
   auto multiply = [&](int t, const T* buf) {
