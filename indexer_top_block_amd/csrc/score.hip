@@ -366,30 +366,45 @@ score_gemm_kernel(const T* __restrict__ qidx, const T* __restrict__ kpool, int64
       for (int r = 0; r < 16; ++r) sum += relu(acc[mt][r]);
     return sum + __shfl_xor(sum, 32);
   };
-  // A tile's four steps, software-pipelined over two accumulator sets: step nt+1's
-  // products are issued before step nt's epilogue, so the matrix pipe works while
-  // the epilogue runs; the scores are stored after the last step (the last tile's
-  // steps past nb multiply clamped keys and store nothing).  (~220 registers for 64
-  // heads of 128 dims, so one workgroup per CU; a 128-register build, two
-  // workgroups per CU, spills and is no faster.)
+  // A tile's four steps.  Pipelined (PIPE): over two accumulator sets, step nt+1's
+  // products issued before step nt's epilogue, so the matrix pipe works while the
+  // epilogue runs, the scores stored after the last step (a store per step is a
+  // branch the scheduler does not cross; the last tile's steps past nb multiply
+  // clamped keys and store nothing).  That takes ~60 more registers, so it is used
+  // where the held heads take 64-96 registers and the kernel runs one workgroup per
+  // CU either way (64 heads of 128 dims: ~220 registers against ~170; a 128-register
+  // build, two workgroups per CU, spills and is no faster); smaller shapes keep two
+  // or more workgroups per CU with one step at a time, and 128 heads of 128 dims
+  // would spill.
+  constexpr bool PIPE = MT * D >= 256 && MT * D <= 384;
   auto multiply = [&](int t, const T* buf) {
     if (t * kGemmBN >= nb) return;                   // uniform per wave
     constexpr int NT = kGemmBN / 32;
-    static_assert(NT % 2 == 0, "steps pair up over the two accumulator sets");
-    float sums[NT];
-    f32x16 acc0[MT], acc1[MT];
-    products(buf, 0, acc0);
+    if constexpr (PIPE) {
+      float sums[NT];
+      f32x16 acc0[MT], acc1[MT];
+      products(buf, 0, acc0);
 #pragma unroll
-    for (int nt = 0; nt < NT; nt += 2) {
-      products(buf, nt + 1, acc1);
-      sums[nt] = reduce(acc0);
-      if (nt + 2 < NT) products(buf, nt + 2, acc0);
-      sums[nt + 1] = reduce(acc1);
-    }
+      for (int nt = 0; nt < NT; nt += 2) {
+        products(buf, nt + 1, acc1);
+        sums[nt] = reduce(acc0);
+        if (nt + 2 < NT) products(buf, nt + 2, acc0);
+        sums[nt + 1] = reduce(acc1);
+      }
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int b = t * kGemmBN + nt * 32 + n;
-      if (hf == 0 && b < nb) srow[b] = sums[nt] + 0.0f;   // +0.0 turns -0.0 into +0.0
+      for (int nt = 0; nt < NT; ++nt) {
+        const int b = t * kGemmBN + nt * 32 + n;
+        if (hf == 0 && b < nb) srow[b] = sums[nt] + 0.0f;   // +0.0 turns -0.0 into +0.0
+      }
+    } else {
+      for (int nt = 0; nt < NT; ++nt) {
+        const int b = t * kGemmBN + nt * 32 + n;
+        if (b - n >= nb) break;                      // uniform per wave
+        f32x16 acc[MT];
+        products(buf, nt, acc);
+        const float sum = reduce(acc);
+        if (hf == 0 && b < nb) srow[b] = sum + 0.0f;   // +0.0 turns -0.0 into +0.0
+      }
     }
   };
   issue(t_begin, ks0);

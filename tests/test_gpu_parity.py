@@ -195,6 +195,25 @@ def test_score_long_rows_several_queries(gpu_lib):
         run_and_check(case, components=False)
 
 
+@pytest.mark.parametrize("h_idx,d_idx,dt,case_id", [(96, 64, "f16", 620), (32, 256, "bf16", 621),
+                                                    (128, 64, "bf16", 622), (128, 128, "f16", 623),
+                                                    (32, 64, "f16", 624)])
+def test_score_gemm_shapes(gpu_lib, h_idx, d_idx, dt, case_id):
+    # 72 query tokens: the many-query scoring kernel, for indexer shapes that take its
+    # pipelined steps (96x64 is not one of them; 32x256, 128x64 are) and its one-step
+    # form (128x128, 32x64); three ragged sequences, so that some groups of 8 tokens
+    # share a sequence (LDS tiles) and one straddles two (direct reads), and tokens at
+    # different depths in one group (per-token visible blocks)
+    d = dims(h_q=8, d_kq=128, d_v=128, h_idx=h_idx, d_idx=d_idx, compress_ratio=4, top_k=256, dtype=dt)
+    lens = [3001, 1777, 2500]
+    q_seq = [0] * 30 + [1] * 20 + [2] * 22
+    q_pos = ([3000 - 97 * j for j in range(30)] + [1776 - 61 * j for j in range(20)]
+             + [2499 - 113 * j for j in range(22)])
+    case = datagen.make_case(f"score_gemm_{h_idx}x{d_idx}_{dt}", d, lens, q_seq, q_pos, seed=0,
+                             case_id=case_id, std="inv_sqrt_dim", v_separate=True)
+    run_and_check(case, queries=[0, 7, 8, 23, 24, 29, 30, 31, 49, 50, 55, 56, 71], components=False)
+
+
 @pytest.mark.parametrize("seq_len,top_k", [(131072, 2048), (60000, 1024), (30000, 512), (16000, 256)])
 def test_select_on_adversarial_score_rows(gpu_lib, seq_len, top_k):
     # the select kernel alone on score rows no scoring produces: negative scores,
