@@ -411,7 +411,7 @@ chunk_select_kernel(const float* __restrict__ scores, int64_t scores_ld, const i
 // Decode rows of up to 32768 blocks: one 1024-thread workgroup holds the whole row in
 // registers and needs no workspace.  Thread t owns blocks j*1024 + t (j < KPT), so
 // every load is coalesced.  The K_blk-th largest key T is found by radix select
-// over the registers, most significant digit first (11, 11, then 10 bits), each
+// over the registers, most significant digit first (10, 11, then 11 bits), each
 // pass histogramming the keys that match the digits fixed so far; a pass whose
 // chosen bin is taken whole (its count equals the number still to take) ends the
 // search early, and the remaining digits do not matter.
@@ -420,10 +420,11 @@ chunk_select_kernel(const float* __restrict__ scores, int64_t scores_ld, const i
 // per key in each pass (about 0.2 us per instruction per key at 32768 keys), and the
 // passes are written for few of them:
 //   - keys are formed with two integer operations after an add that folds -0 into +0;
-//   - the first pass, which counts every key, adds into 16 copies of its histogram
+//   - the first pass, which counts every key, adds into 32 copies of its histogram
 //     laid out [bin][copy] (the address is the digit shifted onto the lane's copy, no
 //     other arithmetic), so keys sharing a digit -- scores crowd into a few binades --
-//     hit different copies;
+//     hit different copies; a 10-bit first digit keeps 32 copies within the LDS that
+//     16 copies of an 11-bit digit took, and halves the lanes sharing each copy;
 //   - later passes test membership in the running bin with one subtract and compare;
 //   - kept blocks (key at or above a threshold) and, when the search ran to the full
 //     32 bits, the keys equal to T go to bitmaps of the row with one compare and one
@@ -433,20 +434,21 @@ chunk_select_kernel(const float* __restrict__ scores, int64_t scores_ld, const i
 //     index order are taken.
 constexpr int kWideThreads = 1024;
 constexpr int kWideMaxKpt = 32;
-constexpr int kWideBins = 2048;
+constexpr int kWideBins = 2048;                      // passes 2 and 3 (11-bit digits)
+constexpr int kP1Bins = 1024;                        // pass 1 (10-bit digit)
 // Pass-1 histogram copies and bitmap words by row size: rows of up to 16384 keys take
-// 8 copies and their own bitmap size, so that the workgroup's LDS (< 80 KiB) and
+// 16 copies and their own bitmap size, so that the workgroup's LDS (< 80 KiB) and
 // registers leave room for a second workgroup on the CU (prefill: many rows).
 template <int KPT>
 struct WideCfg {
-  static constexpr int copies = KPT >= 32 ? 16 : 8;  // lanes l, l+copies, ... share a copy
+  static constexpr int copies = KPT >= 32 ? 32 : 16;  // lanes l, l+copies, ... share a copy
   static constexpr int words = KPT * 32;             // bitmap words (32 blocks each)
 };
 
 template <int KPT>
 struct alignas(16) WideSmem {
   uint32_t h2[kWideBins];                            // pass 2 (first: its bins' addresses need no base)
-  uint32_t h1[kWideBins * WideCfg<KPT>::copies];    // pass 1 [bin][copy]; pass 3: words 0..1023; the list
+  uint32_t h1[kP1Bins * WideCfg<KPT>::copies];      // pass 1 [bin][copy]; pass 3: words 0..2047; the list
   uint32_t keep[WideCfg<KPT>::words];                // blocks at or above the threshold
   uint32_t tie[WideCfg<KPT>::words];                 // blocks equal to T (full-width search)
   int wsum[2][kWideThreads / kWave];                 // per-wave totals, alternating between picks
@@ -559,7 +561,7 @@ select_wide_kernel(const float* __restrict__ scores, int64_t scores_ld, const in
     for (int j = 0; j < KPT; ++j) raw[j] = row[min(j * kWideThreads + tid, last)];
   }
   const QueryRowInfo qr = query_blocks(seq_len, q_seq, q_pos, q, c);
-  for (int e = tid; e < kWideBins * COPIES / 4; e += kWideThreads) ((uint4*)sm.h1)[e] = uint4{0u, 0u, 0u, 0u};
+  for (int e = tid; e < kP1Bins * COPIES / 4; e += kWideThreads) ((uint4*)sm.h1)[e] = uint4{0u, 0u, 0u, 0u};
   for (int e = tid; e < kWideBins; e += kWideThreads) sm.h2[e] = 0u;
   __builtin_amdgcn_sched_barrier(0);                 // every load in flight before the first is used
   int32_t* out = sel + (int64_t)q * sel_ld;
@@ -571,7 +573,7 @@ select_wide_kernel(const float* __restrict__ scores, int64_t scores_ld, const in
   const int n_pad = KPT * kWideThreads - nb;
   __syncthreads();                                   // the histograms are clear (the loads may still fly)
 
-  // ---- pass 1: the top 11 bits, each key counted as it arrives ---------------------------
+  // ---- pass 1: the top 10 bits, each key counted as it arrives ---------------------------
   // Keys past the row's end become 0 -- below every key a score can have except
   // negative NaNs -- so the passes need no bounds checks: the picks take the n_pad
   // padding keys back out of bin 0, and a prefix of 0 (the only one they can match)
@@ -583,63 +585,60 @@ select_wide_kernel(const float* __restrict__ scores, int64_t scores_ld, const in
 #pragma unroll
       for (int j = 0; j < KPT; ++j) {
         key[j] = score_key(raw[j]);
-        atomicAdd(&mine[(key[j] >> 21) * COPIES], 1u);
+        atomicAdd(&mine[(key[j] >> 22) * COPIES], 1u);
       }
     } else {
 #pragma unroll
       for (int j = 0; j < KPT; ++j) {
         key[j] = j * kWideThreads + tid < nb ? score_key(raw[j]) : 0u;
-        atomicAdd(&mine[(key[j] >> 21) * COPIES], 1u);
+        atomicAdd(&mine[(key[j] >> 22) * COPIES], 1u);
       }
     }
   }
   __syncthreads();
   {
-    // thread t: bins 2t and 2t+1, their copies read as quads from a lane-rotated start,
-    // so that consecutive lanes spread over the banks
-    constexpr int NQD = 2 * COPIES / 4;              // quads; the first half: bin 2t
-    uint32_t cnt[2] = {0u, 0u};
-    const uint4* h = (const uint4*)(sm.h1 + tid * 2 * COPIES);
+    // thread t: bin t, its copies read as quads from a lane-rotated start, so that
+    // consecutive lanes spread over the banks
+    constexpr int NQD = COPIES / 4;
+    uint32_t cnt[1] = {0u};
+    const uint4* h = (const uint4*)(sm.h1 + tid * COPIES);
 #pragma unroll
     for (int i = 0; i < NQD; ++i) {
-      const int quad = (i + tid) & (NQD - 1);
-      const uint4 v = h[quad];
-      const uint32_t s4 = v.x + v.y + v.z + v.w;
-      cnt[0] += quad < NQD / 2 ? s4 : 0u;
-      cnt[1] += quad < NQD / 2 ? 0u : s4;
+      const uint4 v = h[(i + tid) & (NQD - 1)];
+      cnt[0] += v.x + v.y + v.z + v.w;
     }
-    wide_pick<2>(cnt, k_blk, n_pad, sm.wsum[0], sm.pick);
+    wide_pick<1>(cnt, k_blk, n_pad, sm.wsum[0], sm.pick);
   }
   uint32_t prefix = (uint32_t)sm.pick[0];            // key >> shift of the keys still in the running
   int k_rem = k_blk - sm.pick[1];
-  int shift = 21;
+  int shift = 22;
   bool whole = sm.pick[2] == k_rem && prefix != 0u;
   // ---- pass 2: next 11 bits among keys in the bin -----------------------------------------
   if (!whole) {
-    sm.h1[tid] = 0u;                                 // words 0..1023 serve pass 3
-    const uint32_t lo = prefix << 21;
+    ((uint2*)sm.h1)[tid] = uint2{0u, 0u};             // words 0..2047 serve pass 3
+    const uint32_t lo = prefix << 22;
     uint32_t one = 1u;
     asm volatile("" : "+v"(one));                    // one register for every add, not one per key
 #pragma unroll
     for (int j = 0; j < KPT; ++j)
-      if (key[j] - lo < (1u << 21)) atomicAdd(&sm.h2[(key[j] >> 10) & (kWideBins - 1)], one);
+      if (key[j] - lo < (1u << 22)) atomicAdd(&sm.h2[(key[j] >> 11) & (kWideBins - 1)], one);
     __syncthreads();
     uint32_t cnt[2] = {sm.h2[tid * 2], sm.h2[tid * 2 + 1]};
     wide_pick<2>(cnt, k_rem, prefix == 0u ? n_pad : 0, sm.wsum[1], sm.pick);
     prefix = (prefix << 11) | (uint32_t)sm.pick[0];
     k_rem -= sm.pick[1];
-    shift = 10;
+    shift = 11;
     whole = sm.pick[2] == k_rem && prefix != 0u;
-    // ---- pass 3: last 10 bits ------------------------------------------------------------
+    // ---- pass 3: last 11 bits ------------------------------------------------------------
     if (!whole) {
-      const uint32_t lo3 = prefix << 10;
+      const uint32_t lo3 = prefix << 11;
 #pragma unroll
       for (int j = 0; j < KPT; ++j)
-        if (key[j] - lo3 < (1u << 10)) atomicAdd(&sm.h1[key[j] & 1023u], 1u);
+        if (key[j] - lo3 < (1u << 11)) atomicAdd(&sm.h1[key[j] & 2047u], 1u);
       __syncthreads();
-      uint32_t cnt1[1] = {sm.h1[tid]};
-      wide_pick<1>(cnt1, k_rem, prefix == 0u ? n_pad : 0, sm.wsum[0], sm.pick);
-      prefix = (prefix << 10) | (uint32_t)sm.pick[0];
+      uint32_t cnt3[2] = {sm.h1[tid * 2], sm.h1[tid * 2 + 1]};
+      wide_pick<2>(cnt3, k_rem, prefix == 0u ? n_pad : 0, sm.wsum[0], sm.pick);
+      prefix = (prefix << 11) | (uint32_t)sm.pick[0];
       k_rem -= sm.pick[1];
       shift = 0;
       whole = sm.pick[2] == k_rem && prefix != 0u;
@@ -683,7 +682,7 @@ select_wide_kernel(const float* __restrict__ scores, int64_t scores_ld, const in
   }
   o += wave_inclusive_scan(__popc(word), lane) - __popc(word);
   const int body = k_blk * c;
-  if (body <= kWideBins * COPIES) {
+  if (body <= kP1Bins * COPIES) {
     // the list is assembled in LDS (pass 1's histogram is free) and written out
     // coalesced, rather than as scattered stores of a few lanes each
     int32_t* list = (int32_t*)sm.h1;
