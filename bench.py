@@ -5,14 +5,24 @@
 A step is one pass of the whole path -- pool the newest block, score every block,
 select, attend -- for one decode token of a DeepSeek-V4-shaped layer at 128K context
 (16 query heads on one 576-wide latent KV head with V = its first 512 dims; indexer of
-64 heads x 128, compress_ratio 4, top_k 2048; bf16 caches).  Steps cycle through
-`--layers` independent copies of the layer's caches (like a model's layers), so that
-every step reads its ~10.7 MB from HBM rather than from the 256 MB last-level cache.
-The timed steps are replayed as one HIP graph (the same kernel launches, without the
-host-side launch overhead of the Python binding).
+64 heads x 128, compress_ratio 4, top_k 2048; bf16 caches).  The timed steps are
+replayed as one HIP graph (the same kernel launches, without the host-side launch
+overhead of the Python binding).
+
+Cold (the headline): `--layers` independent copies of the layer's caches are resident
+(like a model's layers) and step k runs on copy k mod layers.  Between the untimed
+and the timed replay a 1 GiB buffer is read, four times the 256 MB last-level cache,
+so every step of the timed replay reads a copy that nothing has touched since; with
+more steps than copies, a copy comes back only after all the others (more than twice
+the cache) have streamed through.  This holds for any --steps.  Warm: every step on
+the same copy, right after an untimed replay, so its ~10.7 MB stay cached.
 
 Prints one JSON line.  `value` is algorithmic HBM bytes per step (pooled indexer keys
-of the visible blocks + gathered K rows) divided by the step time, in GB/s.
+of the visible blocks + gathered K rows) divided by the cold step time, in GB/s.
+Further sections: the prefill chunk (TFLOP/s against the dense bf16 MFMA peak, the
+vendor figure and one measured with a plain MFMA loop), the 1M-context decode, the
+batched 32-sequence decode, the token-level decode, the mask form, the dense window,
+the q8_0 cache, and the CPU oracle's rate on the same decode step.
 """
 from __future__ import annotations
 
@@ -186,8 +196,23 @@ def traffic_from_counters(path: str):
         return None
 
 
-def time_graph(fn_per_step, n_steps: int, warmup: int) -> float:
-    """Capture n_steps calls of fn_per_step(k) in one graph; return ms per step of a replay."""
+class Flusher:
+    """Reads a buffer of `mib` MiB (a reduction kernel): evicts the L2s and the
+    last-level cache without leaving dirty lines to be written back later."""
+
+    def __init__(self, mib: int):
+        self.mib = mib
+        self.buf = torch.ones(mib * (1 << 20) // 4, dtype=torch.float32, device="cuda") if mib > 0 else None
+
+    def __call__(self) -> None:
+        if self.buf is not None:
+            torch.sum(self.buf)
+
+
+def time_graph(fn_per_step, n_steps: int, warmup: int, flush: "Flusher | None" = None) -> float:
+    """Capture n_steps calls of fn_per_step(k) in one graph; return ms per step of a
+    replay.  One untimed replay comes first; with `flush`, the cache-evicting read
+    runs between it and the timed replay (outside the timed region)."""
     for k in range(max(warmup, 1)):
         fn_per_step(k)
     torch.cuda.synchronize()
@@ -197,12 +222,15 @@ def time_graph(fn_per_step, n_steps: int, warmup: int) -> float:
             fn_per_step(k)
     torch.cuda.synchronize()
     g.replay()                       # one untimed replay
+    if flush is not None:
+        flush()
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
     g.replay()
     end.record()
     torch.cuda.synchronize()
+    del g
     return start.elapsed_time(end) / n_steps
 
 
@@ -217,6 +245,86 @@ def time_eager(fn_per_step, n_steps: int, warmup: int) -> float:
     end.record()
     torch.cuda.synchronize()
     return start.elapsed_time(end) / n_steps
+
+
+def gbs(nbytes: float, ms: float) -> float:
+    return nbytes / (ms * 1e-3) / 1e9
+
+
+def decode_section(lay: "RotatingLayers", ab: dict, steps: int, warmup: int, flush: Flusher,
+                   kernels=("pool_score", "select", "fwd"), warm: bool = True) -> dict:
+    """Cold step time over the rotated copies (flush before the timed replay), each
+    entry point alone under the same protocol, and (optionally) the warm step time."""
+    R = lay.n
+    ms = time_graph(lambda k: lay.step(k % R), steps, warmup, flush)
+    rec = {"us_per_step": round(ms * 1e3, 3), "value": round(gbs(ab["total"], ms), 2), "unit": "GB/s",
+           "frac_of_hbm_peak": round(gbs(ab["total"], ms) / HBM_PEAK_GBS, 4), "bytes_per_step": ab,
+           "timed_region": {"steps": steps, "distinct_layer_copies": min(steps, R),
+                            "distinct_bytes": min(steps, R) * ab["total"],
+                            "read_before_it_bytes": flush.mib << 20}}
+    per = {}
+    for name in kernels:
+        fn = getattr(lay, name)
+        per[name] = round(time_graph(lambda k, fn=fn: fn(k % R), steps, warmup, flush) * 1e3, 3)
+    rec["kernel_avg_us"] = per
+    if warm:
+        wms = time_graph(lambda k: lay.step(0), steps, warmup)
+        rec["warm"] = {"us_per_step": round(wms * 1e3, 3), "value": round(gbs(ab["total"], wms), 2),
+                       "unit": "GB/s", "protocol": "every step on the same layer copy, after an untimed replay"}
+    return rec
+
+
+def roofline_block(ab: dict, sec: dict, score_kernel: str, traffic=None) -> dict:
+    """Roofline of the scoring launch (the step's dominant byte stream), with the whole
+    step's and the attention call's fractions beside it."""
+    us = sec["kernel_avg_us"]["pool_score"]
+    achieved = gbs(ab["pooled"], us * 1e-3)
+    r = {"bound": "hbm", "kernel": score_kernel, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+         "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+         "bytes_per_launch": ab["pooled"], "avg_launch_us": us,
+         "step_share": round(us / sec["us_per_step"], 3),
+         "step": {"achieved": sec["value"], "frac": sec["frac_of_hbm_peak"], "bytes": ab["total"],
+                  "us": sec["us_per_step"]}}
+    if "fwd" in sec["kernel_avg_us"]:
+        fus = sec["kernel_avg_us"]["fwd"]
+        fa = gbs(ab["gathered"], fus * 1e-3)
+        r["attention"] = {"kernels": "attention + split combine (sparse_attn_fwd)", "bytes_per_call": ab["gathered"],
+                          "avg_call_us": fus, "achieved": round(fa, 1), "frac": round(fa / HBM_PEAK_GBS, 4)}
+    return r
+
+
+# ------------------------------------------------------------ MFMA peak (probe)
+
+def measured_mfma_peak() -> dict:
+    """The dense bf16 rate of a plain loop of v_mfma_f32_32x32x16_bf16 chains
+    (libsa_probe.so), beside the vendor's figure."""
+    import ctypes
+
+    path = os.path.join(ROOT, "indexer_top_block_amd", "libsa_probe.so")
+    lib = ctypes.CDLL(path)
+    lib.sa_probe_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.sa_probe_mfma_bf16.restype = ctypes.c_int
+    lib.sa_probe_mfma_bf16_flop.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.sa_probe_mfma_bf16_flop.restype = ctypes.c_double
+    n_wg, iters = 2048, 4096
+    ab = (torch.randn(128 * 8, device="cuda") * 0.01).to(torch.bfloat16)
+    out = torch.empty(n_wg * 256, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    for _ in range(2):
+        assert lib.sa_probe_mfma_bf16(n_wg, iters, ab.data_ptr(), out.data_ptr(), stream) == 0
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 5
+    start.record()
+    for _ in range(reps):
+        lib.sa_probe_mfma_bf16(n_wg, iters, ab.data_ptr(), out.data_ptr(), stream)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / reps
+    tf = lib.sa_probe_mfma_bf16_flop(n_wg, iters) / (ms * 1e-3) / 1e12
+    return {"vendor_tflops": MFMA_BF16_PEAK_TFLOPS, "measured_tflops": round(tf, 1),
+            "measured_with": f"{n_wg} workgroups x 4 waves x {iters} rounds of 8 independent "
+                             "v_mfma_f32_32x32x16_bf16, no memory traffic"}
 
 
 # -------------------------------------------------------------------- CPU oracle
@@ -266,49 +374,65 @@ def cpu_baseline(case: datagen.Case, seconds: float, bytes_per_step: int) -> dic
 
 # ------------------------------------------------------------------------ prefill
 
-def prefill_report(steps: int) -> dict:
-    """Workload 4: 2048 query tokens at depth 32768 -- TFLOP/s of the score and the
-    attention stages and of the whole path, against the dense bf16 MFMA peak."""
+def prefill_report(steps: int, mfma_peak: dict) -> dict:
+    """Workload 4: 2048 query tokens at depth 32768 -- the chunk's pooling (its 512
+    new blocks), scoring, selection and attention; TFLOP/s of the score and the
+    attention stages and of the whole chunk, against the dense bf16 MFMA peak (the
+    vendor figure and the measured one)."""
     from indexer_top_block_amd.device import DeviceLayer
 
     case = datagen.make_workload(4)
     lay = DeviceLayer(case)
-    lay.pool()
-    torch.cuda.synchronize()
     d = case.dims
     c = d.compress_ratio
+    depth = int(case.q_pos[0])
+    # the cache before the chunk holds depth / c pooled blocks; every step pools the
+    # chunk's own blocks again from there
+    n_before = torch.full_like(lay.n_pooled, depth // c)
+    n_after = torch.zeros_like(lay.n_pooled)
+    lay.pool()
+    torch.cuda.synchronize()
     nb = np.array([min(int(case.seq_len[0]), int(p) + 1) // c for p in case.q_pos], dtype=np.int64)
     idx_flop = 2.0 * d.h_idx * d.d_idx * float(nb.sum())
     lay.score(); lay.select(); torch.cuda.synchronize()
     n_sel = lay.n_sel.cpu().numpy().astype(np.int64)
     att_flop = 2.0 * d.h_q * float(n_sel.sum()) * (d.d_kq + d.d_v)
+    pool = lambda k: lay.pool(n_in=n_before, n_out=n_after)
+    t_pool = time_eager(pool, steps, 2)
     t_score = time_eager(lambda k: lay.score(), steps, 2)
     t_select = time_eager(lambda k: lay.select(), steps, 2)
     t_fwd = time_eager(lambda k: lay.fwd(), steps, 2)
-    t_all = time_eager(lambda k: (lay.score(), lay.select(), lay.fwd()), steps, 2)
+    t_all = time_eager(lambda k: (pool(k), lay.score(), lay.select(), lay.fwd()), steps, 2)
     tf = lambda flop, ms: flop / (ms * 1e-3) / 1e12
+    total = tf(idx_flop + att_flop, t_all)
     return {
         "workload": datagen.WORKLOADS[4],
         "ms_per_step": round(t_all, 4),
-        "tflops": round(tf(idx_flop + att_flop, t_all), 2),
-        "frac_of_mfma_peak": round(tf(idx_flop + att_flop, t_all) / MFMA_BF16_PEAK_TFLOPS, 4),
+        "tflops": round(total, 2),
+        "frac_of_mfma_peak": round(total / MFMA_BF16_PEAK_TFLOPS, 4),
+        "frac_of_measured_mfma_peak": round(total / mfma_peak["measured_tflops"], 4),
         "gflop": {"indexer": round(idx_flop / 1e9, 2), "attention": round(att_flop / 1e9, 2)},
-        "stage_ms": {"score": round(t_score, 4), "select": round(t_select, 4), "fwd": round(t_fwd, 4)},
+        "stage_ms": {"pool": round(t_pool, 4), "score": round(t_score, 4), "select": round(t_select, 4),
+                     "fwd": round(t_fwd, 4)},
         "stage_tflops": {"score": round(tf(idx_flop, t_score), 2), "fwd": round(tf(att_flop, t_fwd), 2)},
+        "stage_frac_of_mfma_peak": {"score": round(tf(idx_flop, t_score) / MFMA_BF16_PEAK_TFLOPS, 4),
+                                    "fwd": round(tf(att_flop, t_fwd) / MFMA_BF16_PEAK_TFLOPS, 4)},
+        "timing": "eager launches, steps back to back; the chunk's pooling re-pools its 512 blocks each step",
     }
 
 
 # ------------------------------------------------------------------ mask form
 
-def mask_form_report(lay: "RotatingLayers", steps: int, warmup: int) -> dict:
+def mask_form_report(lay: "RotatingLayers", steps: int, warmup: int, flush: Flusher) -> dict:
     """The additive-mask form on the 128K decode layer: one f16 mask row of 131072
-    columns whose finite entries are the step's 2051 selected positions (values -k/32)
-    -> index list -> attention with the mask values as bias, per step."""
+    columns whose finite entries are the step's selected positions (values -k/32)
+    -> index list -> attention with the mask values as bias, per step (cold)."""
     R = lay.n
     lay.step(0)
     torch.cuda.synchronize()
     n_kv = lay.max_len
-    pos = lay.sel[0, : int(lay.n_sel[0].item())].cpu().numpy()
+    n_fin = int(lay.n_sel[0].item())
+    pos = lay.sel[0, :n_fin].cpu().numpy()
     mask = np.full((1, n_kv), -np.inf, dtype=np.float32)
     mask[0, pos] = -(1.0 + np.arange(len(pos)) % 7) / 32.0
     dev_mask = torch.from_numpy(mask).to(torch.float16).cuda()
@@ -321,10 +445,10 @@ def mask_form_report(lay: "RotatingLayers", steps: int, warmup: int) -> dict:
         sa.sparse_attn_fwd_bias(lay.dims, lay.caches[k % R], lay.q, lay.q_seq, lay.sel, lay.sel_ld, lay.n_sel,
                                 sel_bias, 1, lay.case.scale, lay.out, lay.ws, lay.ws_bytes)
 
-    both = time_graph(lambda k: (m2i(k), fwd_b(k)), steps, warmup)
-    t_m2i = time_graph(m2i, steps, warmup)
-    t_fwd = time_graph(fwd_b, steps, warmup)
-    return {"workload": "one 131072-column f16 mask row over the 128K decode layer, 2051 finite entries",
+    both = time_graph(lambda k: (m2i(k), fwd_b(k)), steps, warmup, flush)
+    t_m2i = time_graph(m2i, steps, warmup, flush)
+    t_fwd = time_graph(fwd_b, steps, warmup, flush)
+    return {"workload": f"one 131072-column f16 mask row over the 128K decode layer, {n_fin} finite entries",
             "us_per_step": round(both * 1e3, 3),
             "kernel_avg_us": {"mask_to_indices": round(t_m2i * 1e3, 3), "fwd_bias": round(t_fwd * 1e3, 3)},
             "mask_bytes": n_kv * 2}
@@ -332,7 +456,7 @@ def mask_form_report(lay: "RotatingLayers", steps: int, warmup: int) -> dict:
 
 # ------------------------------------------------------------------ dense window
 
-def window_report(lay: "RotatingLayers", steps: int, warmup: int, window: int = 128) -> dict:
+def window_report(lay: "RotatingLayers", steps: int, warmup: int, flush: Flusher, window: int = 128) -> dict:
     """The decode step with the attention taken over the selected rows together with
     the `window` most recent positions (dense window + selection, merged in one pass;
     the window size is not fixed by the method's description, 128 is an example)."""
@@ -353,15 +477,15 @@ def window_report(lay: "RotatingLayers", steps: int, warmup: int, window: int = 
         select_w(k)
         fwd_w(k)
 
-    ms = time_graph(step_w, steps, warmup)
-    t_fwd = time_graph(fwd_w, steps, warmup)
+    ms = time_graph(step_w, steps, warmup, flush)
+    t_fwd = time_graph(fwd_w, steps, warmup, flush)
     return {"workload": f"the 128K decode step with a dense window of the {window} most recent positions",
             "window": window, "us_per_step": round(ms * 1e3, 3), "kernel_avg_us": {"fwd_window": round(t_fwd * 1e3, 3)}}
 
 
 # ------------------------------------------------------------------ q8_0 cache
 
-def q8_report(lay: "RotatingLayers", steps: int, warmup: int) -> dict:
+def q8_report(lay: "RotatingLayers", steps: int, warmup: int, flush: Flusher) -> dict:
     """The 128K decode step over q8_0 copies of the layer's K/V cache (quantized once on
     the GPU from the bf16 copies): pool, score, select, attention over the q8_0 rows."""
     d = lay.case.dims
@@ -392,35 +516,37 @@ def q8_report(lay: "RotatingLayers", steps: int, warmup: int) -> dict:
         sa.sparse_attn_quantize_q8_0(new_row, d.dtype, 1, d.d_kq, d.d_kq, codes[k % R, rows - 1:rows], d.d_kq,
                                      scales[k % R, rows - 1:rows], nb)
 
-    ms = time_graph(step_q, steps, warmup)
-    t_fwd = time_graph(fwd_q, steps, warmup)
-    t_w = time_graph(write_row, steps, warmup)
+    ms = time_graph(step_q, steps, warmup, flush)
+    t_fwd = time_graph(fwd_q, steps, warmup, flush)
+    t_w = time_graph(write_row, steps, warmup, flush)
     ab = algorithmic_bytes(lay.case, kv="q8_0")
     del kvs, codes, scales
     torch.cuda.empty_cache()
     return {"workload": "the 128K decode step over a q8_0 K/V cache (V = K[:512])", "us_per_step": round(ms * 1e3, 3),
-            "value": round(ab["total"] / (ms * 1e-3) / 1e9, 2), "unit": "GB/s", "bytes_per_step": ab,
+            "value": round(gbs(ab["total"], ms), 2), "unit": "GB/s", "bytes_per_step": ab,
             "kernel_avg_us": {"fwd_q8_0": round(t_fwd * 1e3, 3), "quantize_one_row": round(t_w * 1e3, 3)}}
 
 
-# ------------------------------------------------------------------ token-level
+# ------------------------------------------------- other decode workloads
 
-def token_level_report(steps: int, warmup: int, layers: int) -> dict:
-    """Workload 6: the decode step of workload 2 with token-level selection
-    (compress_ratio 1: 131072 candidates per query, so selection runs on the whole GPU)."""
-    case = datagen.make_workload(6)
+def workload_decode_report(cfg: int, steps: int, warmup: int, layers: int, flush: Flusher) -> dict:
+    """A whole decode step of workload `cfg` (the token-level, the 1M-context or the
+    batched 32-sequence decode) under the cold protocol, its entry points alone, and
+    the roofline of its scoring launch and its attention."""
+    log(f"[bench] generating workload {cfg}")
+    case = datagen.make_workload(cfg)
     ab = algorithmic_bytes(case)
     lay = RotatingLayers(case, layers)
     lay.fill_pools()
     torch.cuda.synchronize()
-    ms = time_graph(lambda k: lay.step(k % layers), steps, warmup)
-    kernels = {name: round(time_graph(lambda k, fn=getattr(lay, name): fn(k % layers), steps, warmup) * 1e3, 3)
-               for name in ("pool_score", "pool", "score", "select", "fwd")}
+    log(f"[bench] workload {cfg}: {layers} copies resident; timing")
+    sec = decode_section(lay, ab, steps, warmup, flush, kernels=("pool_score", "select", "fwd"), warm=True)
+    sec["workload"] = datagen.WORKLOADS[cfg]
+    sec["layers_rotated"] = layers
+    sec["roofline"] = roofline_block(ab, sec, "score_mfma_kernel (pooling variant)")
     del lay
     torch.cuda.empty_cache()
-    return {"workload": datagen.WORKLOADS[6], "layers_rotated": layers, "us_per_step": round(ms * 1e3, 3),
-            "value": round(ab["total"] / (ms * 1e-3) / 1e9, 2), "unit": "GB/s", "bytes_per_step": ab,
-            "kernel_avg_us": kernels}
+    return sec
 
 
 # --------------------------------------------------------------------------- main
@@ -428,16 +554,22 @@ def token_level_report(steps: int, warmup: int, layers: int) -> dict:
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=256)
-    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--layers", type=int, default=64, help="copies of the layer's caches the steps cycle through")
+    ap.add_argument("--flush-mib", type=int, default=1024, help="MiB read between the untimed and the timed replay")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-token-level", action="store_true")
+    ap.add_argument("--no-long", action="store_true", help="skip the 1M-context decode")
+    ap.add_argument("--no-batched", action="store_true", help="skip the batched 32-sequence decode")
+    ap.add_argument("--no-forms", action="store_true", help="skip the mask, window and q8_0 sections")
     ap.add_argument("--eager", action="store_true", help="launch every step from the host (no graph)")
-    ap.add_argument("--only", choices=["pool_score", "pool", "score", "select", "fwd"], default=None,
-                    help="run just this kernel for --steps launches (for counter collection)")
+    ap.add_argument("--workload", type=int, choices=[2, 3, 5, 6], default=2,
+                    help="decode workload of --only")
+    ap.add_argument("--only", choices=["pool_score", "pool", "score", "select", "fwd", "step"], default=None,
+                    help="run just this call for --steps launches over the rotated copies (counter collection)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--traffic-file", default=os.path.join(ROOT, "profiles", "score_mfma_kernel_decode128k_traffic.txt"),
@@ -456,14 +588,6 @@ def main() -> int:
     torch.cuda.set_device(0)
     sa.load()
 
-    log("[bench] generating workload 2")
-    case = datagen.make_workload(2)
-    ab = algorithmic_bytes(case)
-    lay = RotatingLayers(case, args.layers)
-    lay.fill_pools()
-    torch.cuda.synchronize()
-    log(f"[bench] {args.layers} layer copies resident; algorithmic bytes/step {ab}")
-
     if args.copy_probe_mb:
         n = args.copy_probe_mb * 1024 * 1024 // 4
         src = torch.randn(n, device="cuda")
@@ -474,64 +598,84 @@ def main() -> int:
         log(f"[bench] copy probe: {args.copy_probe_mb} MiB read + written by one elementwise kernel")
         del src, dst
 
-    R = args.layers
     if args.only:
+        cfg = args.workload
+        layers = args.layers if cfg in (2, 6) else {5: 8, 3: 4}[cfg]
+        log(f"[bench] --only {args.only}: generating workload {cfg}")
+        case = datagen.make_workload(cfg)
+        lay = RotatingLayers(case, layers)
+        lay.fill_pools()
+        torch.cuda.synchronize()
         fn = getattr(lay, args.only)
-        ms = time_eager(lambda k: fn(k % R), args.steps, args.warmup)
-        print(json.dumps({"only": args.only, "launches": args.steps, "ms_per_launch": ms}))
+        ms = time_eager(lambda k: fn(k % layers), args.steps, args.warmup)
+        print(json.dumps({"only": args.only, "workload": cfg, "launches": args.steps, "ms_per_launch": ms}))
         return 0
 
-    # whole steps
-    run = time_eager if args.eager else time_graph
-    log("[bench] timing steps")
-    ms = run(lambda k: lay.step(k % R), args.steps, args.warmup)
-    # each kernel alone, back to back over the same rotation (average launch duration)
-    kernels = {}
-    for name in ("pool_score", "pool", "score", "select", "fwd"):
-        fn = getattr(lay, name)
-        kernels[name] = run(lambda k, fn=fn: fn(k % R), args.steps, args.warmup) * 1e3
-    log(f"[bench] step {ms * 1e3:.2f} us; per-call us {kernels}")
-    value = ab["total"] / (ms * 1e-3) / 1e9
+    flush = Flusher(args.flush_mib)
+    log("[bench] generating workload 2")
+    case = datagen.make_workload(2)
+    ab = algorithmic_bytes(case)
+    lay = RotatingLayers(case, args.layers)
+    lay.fill_pools()
+    torch.cuda.synchronize()
+    R = args.layers
+    log(f"[bench] {R} layer copies resident; algorithmic bytes/step {ab}")
 
+    log("[bench] timing the 128K decode step (cold and warm)")
+    if args.eager:
+        ms = time_eager(lambda k: lay.step(k % R), args.steps, args.warmup)
+        sec = {"us_per_step": round(ms * 1e3, 3), "value": round(gbs(ab["total"], ms), 2),
+               "frac_of_hbm_peak": round(gbs(ab["total"], ms) / HBM_PEAK_GBS, 4),
+               "kernel_avg_us": {n: round(time_eager(lambda k, fn=getattr(lay, n): fn(k % R), args.steps,
+                                                     args.warmup) * 1e3, 3)
+                                 for n in ("pool_score", "pool", "score", "select", "fwd")}}
+    else:
+        sec = decode_section(lay, ab, args.steps, args.warmup, flush,
+                             kernels=("pool_score", "pool", "score", "select", "fwd"))
+    ms = sec["us_per_step"] * 1e-3
+    log(f"[bench] step {sec['us_per_step']:.2f} us (cold); per-call us {sec['kernel_avg_us']}; "
+        f"warm {sec.get('warm', {}).get('us_per_step')}")
     # The roofline is taken on the scoring kernel as the step launches it (with the
     # newest block pooled inside): sparse_attn_pool_score is one kernel launch, and it
     # streams the pooled indexer keys -- most of the step's algorithmic bytes.
-    # (sparse_attn_fwd is two launches, attention + combine.)
-    dom = "pool_score"
-    bytes_per_launch = ab["pooled"]
-    achieved = bytes_per_launch / (kernels[dom] * 1e-6) / 1e9
-    roofline = {"bound": "hbm", "kernel": "score_mfma_kernel (pooling variant)", "achieved": round(achieved, 1),
-                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": traffic_from_counters(args.traffic_file), "bytes_per_launch": bytes_per_launch,
-                "avg_launch_us": round(kernels[dom], 3),
-                "step_share": round(kernels[dom] * 1e-3 / ms, 3)}
+    roofline = roofline_block(ab, sec, "score_mfma_kernel (pooling variant)", traffic_from_counters(args.traffic_file))
 
     rec = {
-        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms, 6), "us_per_step": round(ms * 1e3, 3),
+        "metric": METRIC, "value": sec["value"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 6), "us_per_step": sec["us_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "dsv4_decode_128k_bf16: 1 decode token, ctx 131072, 16 q heads on 1 latent KV "
                                "head (DKQ 576 / DV 512, V = K[:512]), indexer 64x128, compress_ratio 4, "
                                "top_k 2048",
-                   "layers_rotated": R, "graph": not args.eager,
-                   "bytes_per_step": ab},
-        "kernel_avg_us": {k: round(v, 3) for k, v in kernels.items()},
+                   "layers_rotated": R, "graph": not args.eager, "bytes_per_step": ab},
+        "protocol": ("cold: step k on layer copy k mod layers; a 1 GiB read between the untimed and the timed "
+                     "replay; the timed replay is exactly `steps` steps"),
+        "timed_region": sec.get("timed_region"),
+        "warm": sec.get("warm"),
+        "kernel_avg_us": sec["kernel_avg_us"],
         "roofline": roofline,
     }
+    if not args.no_forms:
+        log("[bench] mask form")
+        rec["mask_form"] = mask_form_report(lay, args.steps, args.warmup, flush)
+        log("[bench] dense window + selection")
+        rec["window"] = window_report(lay, args.steps, args.warmup, flush)
+        log("[bench] q8_0 cache")
+        rec["q8_0"] = q8_report(lay, args.steps, args.warmup, flush)
+    del lay
+    torch.cuda.empty_cache()
+    log("[bench] MFMA peak probe")
+    peak = measured_mfma_peak()
+    rec["mfma_bf16_peak"] = peak
     if not args.no_prefill:
         log("[bench] prefill workload")
-        rec["prefill"] = prefill_report(max(5, min(args.steps, 20)))
-    log("[bench] mask form")
-    rec["mask_form"] = mask_form_report(lay, args.steps, args.warmup)
-    log("[bench] dense window + selection")
-    rec["window"] = window_report(lay, args.steps, args.warmup)
-    log("[bench] q8_0 cache")
-    rec["q8_0"] = q8_report(lay, args.steps, args.warmup)
+        rec["prefill"] = prefill_report(max(5, min(args.steps, 20)), peak)
     if not args.no_token_level:
-        del lay
-        torch.cuda.empty_cache()
-        log("[bench] token-level decode workload")
-        rec["token_level"] = token_level_report(args.steps, args.warmup, min(args.layers, 32))
+        rec["token_level"] = workload_decode_report(6, args.steps, args.warmup, min(args.layers, 32), flush)
+    if not args.no_long:
+        rec["long_decode_1m"] = workload_decode_report(5, args.steps, args.warmup, 8, flush)
+    if not args.no_batched:
+        rec["batched_decode"] = workload_decode_report(3, args.steps, args.warmup, 4, flush)
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline")
         rec["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds, ab["total"])

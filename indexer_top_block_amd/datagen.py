@@ -143,10 +143,12 @@ def _round_up(x: int, m: int) -> int:
 
 def make_case(name: str, dims: Dims, seq_lens, q_seq, q_pos, *, seed: int, case_id: int,
               std: str | float = 1.0, v_separate: bool = True, scale: Optional[float] = None,
-              plant_fraction: float = 0.0, plant_sigmas: float = 3.0) -> Case:
+              plant_fraction: float = 0.0, plant_sigmas: float = 3.0, q_std: Optional[float] = None) -> Case:
     """Draw a case with the given shapes.
 
     ``std`` is a number, or ``"inv_sqrt_dim"`` for N(0,1)/sqrt(last dim) per tensor.
+    ``q_std`` (optional) replaces it for the attention queries alone, so that a test
+    can widen the spread of the attention logits while K and V keep theirs.
     ``plant_fraction`` > 0 adds ``plant_sigmas`` standard deviations of the raw
     indexer keys to every element of every token of that fraction of the blocks of
     sequence 0 (blocks drawn without replacement).
@@ -177,7 +179,8 @@ def make_case(name: str, dims: Dims, seq_lens, q_seq, q_pos, *, seed: int, case_
             v[r] = _normal((seed, case_id, 1001 + 4 * s), (L, dims.h_kv, dims.d_v), sd(dims.d_v), dims.dtype)
         kidx[r] = _normal((seed, case_id, 1002 + 4 * s), (L, dims.d_idx), sd(dims.d_idx), dims.dtype)
     n_q = len(q_seq)
-    q = _normal((seed, case_id, 1), (n_q, dims.h_q, dims.d_kq), sd(dims.d_kq), dims.dtype)
+    q = _normal((seed, case_id, 1), (n_q, dims.h_q, dims.d_kq), sd(dims.d_kq) if q_std is None else float(q_std),
+                dims.dtype)
     qidx = _normal((seed, case_id, 2), (n_q, dims.h_idx, dims.d_idx), sd(dims.d_idx), dims.dtype)
 
     planted = None
@@ -230,36 +233,38 @@ def workload_dims(cfg: int) -> Dims:
     raise ValueError(f"unknown workload {cfg}")
 
 
-def make_workload(cfg: int, seed: int = 0, ctx: Optional[int] = None) -> Case:
+def make_workload(cfg: int, seed: int = 0, ctx: Optional[int] = None, q_std: Optional[float] = None) -> Case:
     """Build workload ``cfg`` (1..6).  ``ctx`` overrides the cached length of the
-    single-sequence decode workloads (used for reduced-size test variants)."""
+    single-sequence decode workloads (used for reduced-size test variants); ``q_std``
+    overrides the attention queries' standard deviation (see make_case)."""
     dims = workload_dims(cfg)
     if cfg == 1:
         L = ctx or 1024
         return make_case("tiny_decode_f32", dims, [L], [0], [L], seed=seed, case_id=cfg, std=1.0,
-                         v_separate=True, scale=1.0 / math.sqrt(128))
+                         v_separate=True, scale=1.0 / math.sqrt(128), q_std=q_std)
     if cfg == 2:
         L = ctx or 131072
         return make_case("dsv4_decode_128k_bf16", dims, [L], [0], [L], seed=seed, case_id=cfg,
-                         std="inv_sqrt_dim", v_separate=False, scale=1.0 / math.sqrt(576))
+                         std="inv_sqrt_dim", v_separate=False, scale=1.0 / math.sqrt(576), q_std=q_std)
     if cfg == 3:
         lens = np.random.default_rng([seed, cfg, 3]).integers(4096, 65536, size=32, endpoint=True)
         return make_case("batched_decode_f16", dims, lens, list(range(32)), [int(x) for x in lens], seed=seed,
-                         case_id=cfg, std=0.5, v_separate=True, scale=1.0 / math.sqrt(512))
+                         case_id=cfg, std=0.5, v_separate=True, scale=1.0 / math.sqrt(512), q_std=q_std)
     if cfg == 4:
         depth = ctx or 32768
         n_q = 2048
         L = depth + n_q
         return make_case("prefill_chunk_bf16", dims, [L], [0] * n_q, list(range(depth, depth + n_q)), seed=seed,
-                         case_id=cfg, std="inv_sqrt_dim", v_separate=False, scale=1.0 / math.sqrt(576))
+                         case_id=cfg, std="inv_sqrt_dim", v_separate=False, scale=1.0 / math.sqrt(576), q_std=q_std)
     if cfg == 5:
         L = ctx or 1048576
         return make_case("long_decode_1m_bf16", dims, [L], [0], [L], seed=seed, case_id=cfg, std="inv_sqrt_dim",
-                         v_separate=False, scale=1.0 / math.sqrt(576), plant_fraction=0.01, plant_sigmas=3.0)
+                         v_separate=False, scale=1.0 / math.sqrt(576), plant_fraction=0.01, plant_sigmas=3.0,
+                         q_std=q_std)
     if cfg == 6:
         L = ctx or 131072
         return make_case("token_level_decode_128k_bf16", dims, [L], [0], [L], seed=seed, case_id=cfg,
-                         std="inv_sqrt_dim", v_separate=False, scale=1.0 / math.sqrt(576))
+                         std="inv_sqrt_dim", v_separate=False, scale=1.0 / math.sqrt(576), q_std=q_std)
     raise ValueError(f"unknown workload {cfg}")
 
 
