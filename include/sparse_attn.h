@@ -59,7 +59,8 @@ enum {
   SA_ERR_DIMS = -2,      /* dimensions unsupported or inconsistent (see sparse_attn_check_dims) */
   SA_ERR_ARG = -3,       /* another argument out of range (count, leading dimension, size) */
   SA_ERR_WORKSPACE = -4, /* workspace NULL or smaller than sparse_attn_workspace_bytes     */
-  SA_ERR_HIP = -5        /* a kernel launch failed                                        */
+  SA_ERR_HIP = -5,       /* a kernel launch failed                                        */
+  SA_ERR_SCRATCH = -6    /* sparse_attn_fwd_noalloc: the call needs more than the static scratch */
 };
 
 /* Shape of one attention layer and its indexer. */
@@ -190,6 +191,28 @@ int sparse_attn_select(const sa_dims* dims, const sa_cache* cache, const float* 
 int sparse_attn_fwd(const sa_dims* dims, const sa_cache* cache, const void* q,
                     const int32_t* q_seq, const int32_t* sel, int64_t sel_ld, const int32_t* n_sel,
                     int32_t n_q, float scale, float* out, void* ws, size_t ws_bytes, void* stream);
+
+/* Bytes of the library's static scratch (per GPU), used by sparse_attn_fwd_noalloc. */
+#define SA_STATIC_SCRATCH_BYTES ((size_t)16777216)
+
+/* sparse_attn_fwd without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments (less ws / ws_bytes), same kernels and the same
+ * results as sparse_attn_fwd.  The split-KV partials go to a static device array of
+ * SA_STATIC_SCRATCH_BYTES that the library holds on each GPU it runs on until the
+ * process ends; its device address is looked up on the first call on each device.
+ * The call allocates nothing (no hipMalloc / hipFree, no allocating library call).
+ * The scratch needed is sparse_attn_workspace_bytes(dims, n_q, max_len) minus
+ * SA_WS_STATE_BYTES (0 when unsplit); a call needing more than SA_STATIC_SCRATCH_BYTES
+ * returns SA_ERR_SCRATCH before any HIP call (e.g. one decode token of 16 heads
+ * 576/512 with top_k 2048 needs 1.09 MB and up to 30 such tokens fit; 32 sequences
+ * of 8 heads 512/512 need 8.4 MB).  Every call on a GPU
+ * shares that GPU's array: calls that overlap on one GPU (on any streams) race, so
+ * issue them in one stream order.  Nothing in the array needs to start at zero.
+ * Errors: those of sparse_attn_fwd (no SA_ERR_WORKSPACE), SA_ERR_SCRATCH.           */
+int sparse_attn_fwd_noalloc(const sa_dims* dims, const sa_cache* cache, const void* q,
+                            const int32_t* q_seq, const int32_t* sel, int64_t sel_ld, const int32_t* n_sel,
+                            int32_t n_q, float scale, float* out, void* stream);
 
 /* The additive-mask form of the attention (pages: PR #27970, the sparse mode of the
  * flash-attention op: the finite entries of each query's mask row are its K/V set

@@ -145,10 +145,11 @@ int sparse_attn_select(const sa_dims* dims, const sa_cache* cache, const float* 
                                       n_sel, ws, (hipStream_t)stream));
 }
 
+// use_static: the split partials go to the library's static scratch, ws is unused.
 static int fwd_common(const sa_dims* dims, const sa_cache* cache, const void* q, const int32_t* q_seq,
                       const int32_t* sel, int64_t sel_ld, const int32_t* n_sel, const float* sel_bias,
                       const int32_t* q_pos, int32_t window, int32_t n_q, float scale, float* out, void* ws,
-                      size_t ws_bytes, void* stream) {
+                      size_t ws_bytes, void* stream, bool use_static = false) {
   int rc = check_dims(dims);
   if (rc) return rc;
   if ((rc = check_cache_common(dims, cache))) return rc;
@@ -165,12 +166,18 @@ static int fwd_common(const sa_dims* dims, const sa_cache* cache, const void* q,
   if (!(scale == scale)) return SA_ERR_ARG;  // NaN
   if (window < 0 || window > (1 << 24)) return SA_ERR_ARG;
   if (window > 0 && !q_pos) return SA_ERR_NULL;
-  const size_t ws_avail = (ws && ws_bytes > SA_WS_STATE_BYTES) ? ws_bytes - SA_WS_STATE_BYTES : 0;
+  const size_t ws_avail = use_static ? SA_STATIC_SCRATCH_BYTES
+                                     : ((ws && ws_bytes > SA_WS_STATE_BYTES) ? ws_bytes - SA_WS_STATE_BYTES : 0);
   const sa::FwdPlan plan = sa::plan_fwd_window(*dims, n_q, window, ws_avail);
   void* scratch = nullptr;
   if (plan.ws_bytes > 0) {
-    if (!ws || ws_bytes < SA_WS_STATE_BYTES + plan.ws_bytes) return SA_ERR_WORKSPACE;
-    scratch = (char*)ws + SA_WS_STATE_BYTES;
+    if (use_static) {
+      if (plan.ws_bytes > SA_STATIC_SCRATCH_BYTES) return SA_ERR_SCRATCH;
+      if (sa::static_scratch(&scratch) != hipSuccess) return SA_ERR_HIP;
+    } else {
+      if (!ws || ws_bytes < SA_WS_STATE_BYTES + plan.ws_bytes) return SA_ERR_WORKSPACE;
+      scratch = (char*)ws + SA_WS_STATE_BYTES;
+    }
   }
   (void)hipGetLastError();
   return hip_status(sa::launch_fwd(*dims, to_args(cache), q, q_seq, sel, sel_ld, n_sel, sel_bias, q_pos, window,
@@ -182,6 +189,13 @@ int sparse_attn_fwd(const sa_dims* dims, const sa_cache* cache, const void* q, c
                     void* ws, size_t ws_bytes, void* stream) {
   return fwd_common(dims, cache, q, q_seq, sel, sel_ld, n_sel, nullptr, nullptr, 0, n_q, scale, out, ws, ws_bytes,
                     stream);
+}
+
+int sparse_attn_fwd_noalloc(const sa_dims* dims, const sa_cache* cache, const void* q, const int32_t* q_seq,
+                            const int32_t* sel, int64_t sel_ld, const int32_t* n_sel, int32_t n_q, float scale,
+                            float* out, void* stream) {
+  return fwd_common(dims, cache, q, q_seq, sel, sel_ld, n_sel, nullptr, nullptr, 0, n_q, scale, out, nullptr, 0,
+                    stream, /*use_static=*/true);
 }
 
 int sparse_attn_fwd_window(const sa_dims* dims, const sa_cache* cache, const void* q, const int32_t* q_seq,
@@ -280,6 +294,7 @@ const char* sparse_attn_strerror(int code) {
     case SA_ERR_ARG: return "argument out of range";
     case SA_ERR_WORKSPACE: return "workspace missing or too small";
     case SA_ERR_HIP: return "HIP kernel launch failed";
+    case SA_ERR_SCRATCH: return "the call needs more than the library's static scratch (SA_STATIC_SCRATCH_BYTES)";
     default: return "unknown error code";
   }
 }

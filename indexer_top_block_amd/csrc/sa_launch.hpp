@@ -100,6 +100,10 @@ hipError_t launch_fwd(const sa_dims& d, const CacheArgs& c, const void* q, const
                       const int32_t* q_pos, int window, int n_q, float scale, float* out, void* ws,
                       const FwdPlan& plan, hipStream_t stream);
 
+// Device address of this device's copy of the static scratch array
+// (SA_STATIC_SCRATCH_BYTES), looked up on first use per device (fwd_static.hip).
+hipError_t static_scratch(void** ptr);
+
 // Total workspace bytes for n_q query tokens (state + the larger scratch), 0 if none.
 size_t workspace_bytes(const sa_dims& d, int n_q, int max_len);
 size_t workspace_bytes_window(const sa_dims& d, int n_q, int max_len, int window);

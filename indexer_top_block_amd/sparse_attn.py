@@ -19,11 +19,12 @@ SA_F32, SA_F16, SA_BF16 = 0, 1, 2
 DTYPE_CODE = {"f32": SA_F32, "f16": SA_F16, "bf16": SA_BF16}
 TORCH_DTYPE = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 
-SA_OK, SA_ERR_NULL, SA_ERR_DIMS, SA_ERR_ARG, SA_ERR_WORKSPACE, SA_ERR_HIP = 0, -1, -2, -3, -4, -5
+SA_OK, SA_ERR_NULL, SA_ERR_DIMS, SA_ERR_ARG, SA_ERR_WORKSPACE, SA_ERR_HIP, SA_ERR_SCRATCH = 0, -1, -2, -3, -4, -5, -6
 
 # Leading bytes of a workspace that hold state between calls (zero-filled once by the
 # caller, kept at zero by the library); SA_WS_STATE_BYTES in the header.
 WS_STATE_BYTES = 1056768
+STATIC_SCRATCH_BYTES = 16777216   # SA_STATIC_SCRATCH_BYTES
 
 EXPORTS = (
     "sparse_attn_check_dims",
@@ -33,6 +34,7 @@ EXPORTS = (
     "sparse_attn_pool_score",
     "sparse_attn_select",
     "sparse_attn_fwd",
+    "sparse_attn_fwd_noalloc",
     "sparse_attn_mask_to_indices",
     "sparse_attn_fwd_bias",
     "sparse_attn_workspace_bytes_window",
@@ -101,6 +103,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.sparse_attn_select.restype = ctypes.c_int
     lib.sparse_attn_fwd.argtypes = [dp, cp, P, P, P, I64, P, I32, ctypes.c_float, P, P, SZ, P]
     lib.sparse_attn_fwd.restype = ctypes.c_int
+    lib.sparse_attn_fwd_noalloc.argtypes = [dp, cp, P, P, P, I64, P, I32, ctypes.c_float, P, P]
+    lib.sparse_attn_fwd_noalloc.restype = ctypes.c_int
     lib.sparse_attn_mask_to_indices.argtypes = [P, I32, I64, I32, I32, P, I64, P, P, P]
     lib.sparse_attn_mask_to_indices.restype = ctypes.c_int
     lib.sparse_attn_fwd_bias.argtypes = [dp, cp, P, P, P, I64, P, P, I32, ctypes.c_float, P, P, SZ, P]
@@ -221,6 +225,14 @@ def sparse_attn_fwd(dims: SaDims, cache: Cache, q, q_seq, sel, sel_ld: int, n_se
                                                      _ptr(q_seq), _ptr(sel), int(sel_ld), _ptr(n_sel), int(n_q),
                                                      float(scale), _ptr(out), _ptr(ws), int(ws_bytes),
                                                      _stream(stream)))
+
+
+def sparse_attn_fwd_noalloc(dims: SaDims, cache: Cache, q, q_seq, sel, sel_ld: int, n_sel, n_q: int, scale: float,
+                            out, stream=None) -> None:
+    _check("sparse_attn_fwd_noalloc",
+           load().sparse_attn_fwd_noalloc(ctypes.byref(dims), ctypes.byref(cache.struct), _ptr(q), _ptr(q_seq),
+                                          _ptr(sel), int(sel_ld), _ptr(n_sel), int(n_q), float(scale), _ptr(out),
+                                          _stream(stream)))
 
 
 def sparse_attn_mask_to_indices(mask, mask_dtype, mask_ld: int, n_q: int, n_kv: int, sel, sel_ld: int, n_sel,

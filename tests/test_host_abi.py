@@ -35,7 +35,7 @@ def test_library_exports_every_declared_function():
 
 def test_version_and_strerror():
     assert "gfx950" in sa.sparse_attn_version()
-    for code in (0, -1, -2, -3, -4, -5, 7):
+    for code in (0, -1, -2, -3, -4, -5, -6, 7):
         assert isinstance(sa.sparse_attn_strerror(code), str) and sa.sparse_attn_strerror(code)
 
 
@@ -247,3 +247,25 @@ def test_pool_score_rejects_bad_arguments():
     assert _call(f, d, c, FAKE, FAKE, 1, FAKE, FAKE, FAKE, 1, FAKE, 1000, None) == sa.SA_ERR_ARG   # scores_ld
     bad = _cache(kidx_ld=64)
     assert _call(f, d, ctypes.byref(bad), FAKE, FAKE, 1, FAKE, FAKE, FAKE, 1, FAKE, 32768, None) == sa.SA_ERR_ARG
+
+
+def test_noalloc_fwd_rejects_bad_arguments_and_oversize():
+    # sparse_attn_fwd_noalloc: the checks of sparse_attn_fwd, and a call whose split
+    # partials exceed the static scratch is refused before any HIP call
+    hdr = open(HEADER).read()
+    assert f"#define SA_STATIC_SCRATCH_BYTES ((size_t){sa.STATIC_SCRATCH_BYTES})" in hdr
+    d = ctypes.byref(_dims())
+    c = ctypes.byref(_cache())
+    f = ctypes.c_float(0.04)
+    fn = "sparse_attn_fwd_noalloc"
+    assert _call(fn, d, c, None, FAKE, FAKE, 2051, FAKE, 1, f, FAKE, None) == sa.SA_ERR_NULL
+    assert _call(fn, d, c, FAKE, FAKE, FAKE, 2051, FAKE, 1, ctypes.c_float(float("nan")), FAKE, None) == sa.SA_ERR_ARG
+    assert _call(fn, d, c, FAKE, FAKE, FAKE, 0, FAKE, 1, f, FAKE, None) == sa.SA_ERR_ARG
+    assert _call(fn, d, c, FAKE, FAKE, FAKE, 2051, FAKE, 0, f, FAKE, None) == sa.SA_OK   # nothing to do
+    # scratch needed = the workspace's scratch part: 31 tokens of the 576/512 shape (17
+    # splits each: 31 x 16 x 17 x 514 x 4 B = 17.3 MB) exceed 16 MiB; 30 tokens fit
+    need31 = sa.sparse_attn_workspace_bytes(_dims(), 31, 4096) - sa.WS_STATE_BYTES
+    need30 = sa.sparse_attn_workspace_bytes(_dims(), 30, 4096) - sa.WS_STATE_BYTES
+    assert need30 <= sa.STATIC_SCRATCH_BYTES < need31
+    assert _call(fn, d, c, FAKE, FAKE, FAKE, 2051, FAKE, 31, f, FAKE, None) == sa.SA_ERR_SCRATCH
+    assert "static scratch" in sa.sparse_attn_strerror(sa.SA_ERR_SCRATCH)
