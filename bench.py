@@ -372,6 +372,56 @@ def cpu_baseline(case: datagen.Case, seconds: float, bytes_per_step: int) -> dic
             "ms_per_step": round(per * 1e3, 3)}
 
 
+def measured_hbm_read() -> dict:
+    """The read bandwidth a plain streaming kernel and a gather of random 1 KiB rows
+    get from HBM on this chip (libsa_probe.so), beside the 8 TB/s peak: the ceilings
+    the byte-bound kernels are compared with.  Each figure is the best of 5 cold runs
+    (a 1 GiB read between them), timed with events around one eager launch."""
+    import ctypes
+
+    lib = ctypes.CDLL(os.path.join(ROOT, "indexer_top_block_amd", "libsa_probe.so"))
+    P, I64 = ctypes.c_void_p, ctypes.c_int64
+    lib.sa_probe_stream_read.argtypes = [P, I64, ctypes.c_int, P, P]
+    lib.sa_probe_stream_read.restype = ctypes.c_int
+    lib.sa_probe_gather_read.argtypes = [P, P, I64, ctypes.c_int, P, P]
+    lib.sa_probe_gather_read.restype = ctypes.c_int
+    stream = torch.cuda.current_stream().cuda_stream
+    src_bytes = 2 << 30
+    src = torch.ones(src_bytes // 4, dtype=torch.int32, device="cuda")
+    out = torch.empty(8192 * 256, dtype=torch.int32, device="cuda")
+    flush = Flusher(1024)
+
+    def best(fn, nbytes):
+        fn()
+        torch.cuda.synchronize()
+        ms = []
+        for _ in range(5):
+            flush()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ms.append(a.elapsed_time(b))
+        return round(nbytes / (min(ms) * 1e-3) / 1e9, 1)
+
+    res = {"peak_gbs": HBM_PEAK_GBS}
+    for mib in (64, 2048):
+        nb = mib << 20
+        res[f"stream_{mib}MiB_gbs"] = best(lambda nb=nb: lib.sa_probe_stream_read(src.data_ptr(), nb, 8192,
+                                                                                  out.data_ptr(), stream), nb)
+    rows = torch.from_numpy(np.random.default_rng(0).integers(0, src_bytes // 1024, 131072).astype(np.int32)).cuda()
+    res["gather_1KiB_rows_128MiB_gbs"] = best(lambda: lib.sa_probe_gather_read(src.data_ptr(), rows.data_ptr(), 131072,
+                                                                               1024, out.data_ptr(), stream),
+                                              131072 * 1024)
+    res["measured_with"] = ("a grid-stride kernel of 16-byte loads (8192 workgroups of 256 threads); one wave per "
+                            "random 1 KiB row, 1024 workgroups")
+    del src, out, flush
+    torch.cuda.empty_cache()
+    return res
+
+
 # ------------------------------------------------------------------------ prefill
 
 def prefill_report(steps: int, mfma_peak: dict) -> dict:
@@ -664,9 +714,10 @@ def main() -> int:
         rec["q8_0"] = q8_report(lay, args.steps, args.warmup, flush)
     del lay
     torch.cuda.empty_cache()
-    log("[bench] MFMA peak probe")
+    log("[bench] MFMA peak and HBM read probes")
     peak = measured_mfma_peak()
     rec["mfma_bf16_peak"] = peak
+    rec["hbm_read_measured"] = measured_hbm_read()
     if not args.no_prefill:
         log("[bench] prefill workload")
         rec["prefill"] = prefill_report(max(5, min(args.steps, 20)), peak)

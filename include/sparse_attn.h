@@ -192,8 +192,11 @@ int sparse_attn_fwd(const sa_dims* dims, const sa_cache* cache, const void* q,
                     const int32_t* q_seq, const int32_t* sel, int64_t sel_ld, const int32_t* n_sel,
                     int32_t n_q, float scale, float* out, void* ws, size_t ws_bytes, void* stream);
 
-/* Bytes of the library's static scratch (per GPU), used by sparse_attn_fwd_noalloc. */
-#define SA_STATIC_SCRATCH_BYTES ((size_t)16777216)
+/* Bytes of the library's static scratch (per GPU), used by sparse_attn_fwd_noalloc:
+ * the split partials of 512 workgroups of 16 query heads with d_v = 512 (the most the
+ * split plan makes), 512 * 16 * (512 + 2) * 4 bytes, so every call with
+ * h_q / h_kv <= 16 and d_v <= 512 fits.                                              */
+#define SA_STATIC_SCRATCH_BYTES ((size_t)16842752)
 
 /* sparse_attn_fwd without a workspace argument, for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops, harnesses that
@@ -204,9 +207,9 @@ int sparse_attn_fwd(const sa_dims* dims, const sa_cache* cache, const void* q,
  * The call allocates nothing (no hipMalloc / hipFree, no allocating library call).
  * The scratch needed is sparse_attn_workspace_bytes(dims, n_q, max_len) minus
  * SA_WS_STATE_BYTES (0 when unsplit); a call needing more than SA_STATIC_SCRATCH_BYTES
- * returns SA_ERR_SCRATCH before any HIP call (e.g. one decode token of 16 heads
- * 576/512 with top_k 2048 needs 1.09 MB and up to 30 such tokens fit; 32 sequences
- * of 8 heads 512/512 need 8.4 MB).  Every call on a GPU
+ * returns SA_ERR_SCRATCH before any HIP call; that cannot happen for d_v <= 512 (e.g.
+ * one decode token of 16 heads 576/512 with top_k 2048 needs 1.09 MB, 32 sequences
+ * of 8 heads 512/512 8.4 MB), but can for wider V heads.  Every call on a GPU
  * shares that GPU's array: calls that overlap on one GPU (on any streams) race, so
  * issue them in one stream order.  Nothing in the array needs to start at zero.
  * Errors: those of sparse_attn_fwd (no SA_ERR_WORKSPACE), SA_ERR_SCRATCH.           */

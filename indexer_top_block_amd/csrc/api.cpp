@@ -168,18 +168,26 @@ static int fwd_common(const sa_dims* dims, const sa_cache* cache, const void* q,
   if (window > 0 && !q_pos) return SA_ERR_NULL;
   const size_t ws_avail = use_static ? SA_STATIC_SCRATCH_BYTES
                                      : ((ws && ws_bytes > SA_WS_STATE_BYTES) ? ws_bytes - SA_WS_STATE_BYTES : 0);
-  const sa::FwdPlan plan = sa::plan_fwd_window(*dims, n_q, window, ws_avail);
-  void* scratch = nullptr;
-  if (plan.ws_bytes > 0) {
+  // The workspace is checked against the plan for the most workgroups any device
+  // takes (host only); the plan for this device never needs more.
+  const sa::FwdPlan bound = sa::plan_fwd_window(*dims, n_q, window, ws_avail, sa::kPlanSlots);
+  if (bound.ws_bytes > 0) {
     if (use_static) {
-      if (plan.ws_bytes > SA_STATIC_SCRATCH_BYTES) return SA_ERR_SCRATCH;
-      if (sa::static_scratch(&scratch) != hipSuccess) return SA_ERR_HIP;
-    } else {
-      if (!ws || ws_bytes < SA_WS_STATE_BYTES + plan.ws_bytes) return SA_ERR_WORKSPACE;
-      scratch = (char*)ws + SA_WS_STATE_BYTES;
+      if (bound.ws_bytes > SA_STATIC_SCRATCH_BYTES) return SA_ERR_SCRATCH;
+    } else if (!ws || ws_bytes < SA_WS_STATE_BYTES + bound.ws_bytes) {
+      return SA_ERR_WORKSPACE;
     }
   }
   (void)hipGetLastError();
+  const sa::FwdPlan plan = sa::plan_fwd_window(*dims, n_q, window, ws_avail, sa::fwd_slots(*dims, to_args(cache), q));
+  void* scratch = nullptr;
+  if (plan.ws_bytes > 0) {
+    if (use_static) {
+      if (sa::static_scratch(&scratch) != hipSuccess) return SA_ERR_HIP;
+    } else {
+      scratch = (char*)ws + SA_WS_STATE_BYTES;
+    }
+  }
   return hip_status(sa::launch_fwd(*dims, to_args(cache), q, q_seq, sel, sel_ld, n_sel, sel_bias, q_pos, window,
                                    n_q, scale, out, scratch, plan, (hipStream_t)stream));
 }

@@ -90,7 +90,8 @@ fwd_mfma_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, 
     wlen = min(window, n_vis);
     w0 = n_vis - wlen;
   }
-  const int r_end = min(cnt + wlen, r_begin + rows_per_split);
+  // the last split takes every remaining row (the tail rows when they have no split of their own)
+  const int r_end = split == n_split - 1 ? cnt + wlen : min(cnt + wlen, r_begin + rows_per_split);
   const int n_tiles = r_end > r_begin ? (r_end - r_begin + RT - 1) / RT : 0;
   const T* kg = k + (int64_t)g * k_hs;
   const T* vg = v + (int64_t)g * v_hs;
@@ -443,7 +444,8 @@ fwd_lds_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, i
     wlen = min(window, n_vis);
     w0 = n_vis - wlen;
   }
-  const int r_end = min(cnt + wlen, r_begin + rows_per_split);
+  // the last split takes every remaining row (the tail rows when they have no split of their own)
+  const int r_end = split == n_split - 1 ? cnt + wlen : min(cnt + wlen, r_begin + rows_per_split);
   const int n_tiles = r_end > r_begin ? (r_end - r_begin + RT - 1) / RT : 0;
   const T* kg = k + (int64_t)g * k_hs;
 
@@ -698,29 +700,35 @@ static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 static int fwd_cap(const sa_dims& d) { return d.top_k + d.compress_ratio - 1; }
 
-// Split plan for up to `rows` attended rows per query.
-static FwdPlan plan_rows(const sa_dims& d, int n_q, long long rows) {
+// Split plan for up to `rows` attended rows per query, for a kernel that `slots`
+// workgroups fill (compute units x workgroups resident per unit).  The rows of whole
+// blocks (all but the c - 1 rows a tail can add) go to splits of T 64-row tiles, T
+// the smallest count for which the splits of all queries fit in one round of `slots`
+// workgroups -- a second, partial round would leave most of the chip idle while it
+// runs.  The tail rows get a split of their own when one more split per query still
+// fits (so a list with a tail adds no tile to any split), else the last split takes
+// them; kernels give the last split every remaining row.
+static FwdPlan plan_rows(const sa_dims& d, int n_q, long long rows, long long slots) {
   FwdPlan p{};
   const long long units = (long long)n_q * d.h_kv;
-  // Aim at about 512 workgroups; never split below one 64-row tile.  (Decode is bound
-  // by what one CU can pull: a second tile per workgroup costs more than the smaller
-  // combine it buys.)
-  long long want = units > 0 ? (512 + units - 1) / units : 1;
-  const long long max_split = (rows + kMfmaTile - 1) / kMfmaTile;
-  if (want > max_split) want = max_split;
-  if (want < 1) want = 1;
-  long long rps = (rows + want - 1) / want;
-  rps = (rps + kMfmaTile - 1) / kMfmaTile * kMfmaTile;
-  if (rps < kMfmaTile) rps = kMfmaTile;
-  p.rows_per_split = (int)rps;
+  const long long tail = d.compress_ratio - 1;
+  const long long bulk = rows - tail > 1 ? rows - tail : 1;
+  const long long tiles = (bulk + kMfmaTile - 1) / kMfmaTile;
+  if (slots > kPlanSlots) slots = kPlanSlots;
+  if (slots < 1) slots = 1;
+  long long per = tiles;                      // tiles per split
+  if (units > 0 && units < slots && tiles > 1) per = (tiles * units + slots - 1) / slots;
+  if (per < 1) per = 1;
+  long long n = (tiles + per - 1) / per;
+  if (tail > 0 && rows > bulk && units * (n + 1) <= slots) ++n;
+  p.rows_per_split = (int)(per * kMfmaTile);
   p.list_max = fwd_cap(d);
-  p.n_split = (int)((rows + rps - 1) / rps);
-  if (p.n_split < 1) p.n_split = 1;
+  p.n_split = n > 1 ? (int)n : 1;
   p.ws_bytes = p.n_split > 1 ? (size_t)n_q * d.h_q * p.n_split * ((size_t)d.d_v + 2) * sizeof(float) : 0;
   return p;
 }
 
-FwdPlan plan_fwd(const sa_dims& d, int n_q) { return plan_rows(d, n_q, fwd_cap(d)); }
+FwdPlan plan_fwd(const sa_dims& d, int n_q) { return plan_rows(d, n_q, fwd_cap(d), kPlanSlots); }
 
 static long long window_rows(const sa_dims& d, int window) { return (long long)fwd_cap(d) + (window > 0 ? window : 0); }
 
@@ -728,11 +736,13 @@ static long long window_rows(const sa_dims& d, int window) { return (long long)f
 // `window`.  When the workspace holds the partials of the plan for all those rows
 // (workspace_bytes_window), that plan is used; otherwise the split count of the
 // plain plan is kept -- its workspace always suffices -- and each split takes more rows.
-FwdPlan plan_fwd_window(const sa_dims& d, int n_q, int window, size_t ws_avail) {
+// A plan for fewer slots than kPlanSlots never has more splits, so the workspace
+// sizes below (taken at kPlanSlots) cover it.
+FwdPlan plan_fwd_window(const sa_dims& d, int n_q, int window, size_t ws_avail, long long slots) {
   const long long total = window_rows(d, window);
-  FwdPlan full = plan_rows(d, n_q, total);
+  FwdPlan full = plan_rows(d, n_q, total, slots);
   if (full.ws_bytes <= ws_avail) return full;
-  FwdPlan p = plan_fwd(d, n_q);
+  FwdPlan p = plan_rows(d, n_q, fwd_cap(d), slots);
   long long rps = (total + p.n_split - 1) / p.n_split;
   rps = (rps + kMfmaTile - 1) / kMfmaTile * kMfmaTile;
   if (rps > p.rows_per_split) p.rows_per_split = (int)rps;
@@ -748,7 +758,7 @@ size_t workspace_bytes(const sa_dims& d, int n_q, int max_len) {
 
 size_t workspace_bytes_window(const sa_dims& d, int n_q, int max_len, int window) {
   const size_t base = workspace_bytes(d, n_q, max_len);
-  const size_t f = plan_rows(d, n_q, window_rows(d, window)).ws_bytes;
+  const size_t f = plan_rows(d, n_q, window_rows(d, window), kPlanSlots).ws_bytes;
   const size_t w = f > 0 ? SA_WS_STATE_BYTES + f : 0;
   return w > base ? w : base;
 }
@@ -764,6 +774,17 @@ bool fwd_uses_mfma(const sa_dims& d, const CacheArgs& c, const void* q) {
   if (c.k_ld % 8 || c.k_hs % 8 || !aligned16(c.k) || !aligned16(q)) return false;
   if (!alias && (c.v_ld % 8 || c.v_hs % 8 || !aligned16(c.v))) return false;
   return true;
+}
+
+// Workgroups the attention call's kernel fills the chip with: the register-path kernel
+// with a separate V of 512+ dims holds a K and a V tile in LDS (135 KiB), one
+// workgroup per compute unit; the other kernels fit two.
+long long fwd_slots(const sa_dims& d, const CacheArgs& c, const void* q) {
+  int cus = device_cus();
+  if (cus <= 0) cus = 256;
+  const bool alias = c.v == c.k && c.v_ld == c.k_ld && c.v_hs == c.k_hs;
+  const bool one_per_cu = fwd_uses_mfma(d, c, q) && !alias && d.d_kq >= 512;
+  return (long long)cus * (one_per_cu ? 1 : 2);
 }
 
 template <typename T, int DKQ, int DV, bool ALIAS>

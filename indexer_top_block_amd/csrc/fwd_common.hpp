@@ -139,7 +139,8 @@ fwd_valu_kernel(const T* __restrict__ q, const KV kv, const int64_t* __restrict_
     wlen = min(window, n_vis);
     w0 = n_vis - wlen;
   }
-  const int r_end = min(cnt + wlen, r_begin + rows_per_split);
+  // the last split takes every remaining row (the tail rows when they have no split of their own)
+  const int r_end = split == n_split - 1 ? cnt + wlen : min(cnt + wlen, r_begin + rows_per_split);
   const int32_t* list = sel + (int64_t)i * sel_ld;
   const float* blist = sel_bias ? sel_bias + (int64_t)i * sel_ld : nullptr;
   const T* qg = q + ((int64_t)i * h_q + (int64_t)g * G) * d_kq;

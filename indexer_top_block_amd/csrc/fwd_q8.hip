@@ -113,7 +113,8 @@ fwd_q8_lds_kernel(const T* __restrict__ q, const int8_t* __restrict__ kq, int64_
   const int L = sm.len;
   const int64_t row0 = sm.row0;
   const int cnt = max(0, (int)min((int64_t)n_sel[i], min(sel_ld, (int64_t)list_max)));
-  const int r_end = min(cnt, r_begin + rows_per_split);
+  // the last split takes every remaining row (the tail rows when they have no split of their own)
+  const int r_end = split == n_split - 1 ? cnt : min(cnt, r_begin + rows_per_split);
   const int n_tiles = r_end > r_begin ? (r_end - r_begin + RT - 1) / RT : 0;
   const int8_t* kqg = kq + (int64_t)g * k_hs;
   const f16* ksg = ks + (int64_t)g * ks_hs;

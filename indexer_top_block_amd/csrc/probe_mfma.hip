@@ -1,4 +1,4 @@
-// Measurement probe (not part of the sparse-attention library): the dense bf16
+// Measurement probes (not part of the sparse-attention library): the dense bf16
 // matrix-core rate of the chip, measured with a plain loop of independent
 // v_mfma_f32_32x32x16_bf16 chains and no memory traffic, to be reported beside the
 // vendor's peak figure.  Built as its own library, libsa_probe.so.
@@ -52,6 +52,81 @@ int sa_probe_mfma_bf16(int n_wg, int iters, const void* ab, float* out, void* st
 // FLOP one call performs.
 double sa_probe_mfma_bf16_flop(int n_wg, int iters) {
   return (double)n_wg * (kThreads / 64) * iters * kChains * (2.0 * 32 * 32 * 16);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------------
+// HBM read probes: the read bandwidth the chip delivers to a plain streaming kernel
+// and to a gather of random 1 KiB rows (the access pattern of the attention's row
+// gathers), reported beside the 8 TB/s peak.
+
+namespace {
+
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+
+// Every thread reads UNR 16-byte vectors per round, grid-stride, and keeps an xor.
+template <int UNR>
+__global__ void __launch_bounds__(256) stream_read_kernel(const u32x4v* __restrict__ src, int64_t n_vec,
+                                                          uint32_t* __restrict__ out) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  u32x4v acc = {0, 0, 0, 0};
+  for (; i + (UNR - 1) * stride < n_vec; i += UNR * stride) {
+    u32x4v v[UNR];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) v[u] = src[i + u * stride];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) acc ^= v[u];
+  }
+  for (; i < n_vec; i += stride) acc ^= src[i];
+  out[(int64_t)blockIdx.x * 256 + threadIdx.x] = acc.x ^ acc.y ^ acc.z ^ acc.w;
+}
+
+// Each wave reads whole 1 KiB rows (one 16-byte vector per lane) at row indices
+// rows[] (UNR rows in flight per wave), grid-stride over the index list.
+template <int UNR>
+__global__ void __launch_bounds__(256) gather_read_kernel(const u32x4v* __restrict__ src,
+                                                          const int32_t* __restrict__ rows, int64_t n_rows,
+                                                          uint32_t* __restrict__ out) {
+  const int lane = threadIdx.x % 64;
+  const int64_t waves = (int64_t)gridDim.x * 4;
+  int64_t w = (int64_t)blockIdx.x * 4 + threadIdx.x / 64;
+  u32x4v acc = {0, 0, 0, 0};
+  for (; w + (UNR - 1) * waves < n_rows; w += UNR * waves) {
+    u32x4v v[UNR];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) v[u] = src[(int64_t)rows[w + u * waves] * 64 + lane];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) acc ^= v[u];
+  }
+  for (; w < n_rows; w += waves) acc ^= src[(int64_t)rows[w] * 64 + lane];
+  out[(int64_t)blockIdx.x * 256 + threadIdx.x] = acc.x ^ acc.y ^ acc.z ^ acc.w;
+}
+
+}  // namespace
+
+extern "C" {
+
+// Streams `bytes` (a multiple of 16, 16-byte aligned) from src with n_wg workgroups
+// of 256 threads; out: device, n_wg * 256 uint32.  0, or -1 / -2 as above.
+int sa_probe_stream_read(const void* src, int64_t bytes, int n_wg, uint32_t* out, void* stream) {
+  if (!src || !out || bytes < 16 || bytes % 16 || n_wg < 1) return -1;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(stream_read_kernel<8>, dim3(n_wg), dim3(256), 0, (hipStream_t)stream, (const u32x4v*)src,
+                     bytes / 16, out);
+  return hipGetLastError() == hipSuccess ? 0 : -2;
+}
+
+// Gathers n_rows rows of 1 KiB from src (rows[j] < the number of rows src holds;
+// the caller guarantees it) with n_wg workgroups; out: device, n_wg * 256 uint32.
+int sa_probe_gather_read(const void* src, const int32_t* rows, int64_t n_rows, int n_wg, uint32_t* out,
+                         void* stream) {
+  if (!src || !rows || !out || n_rows < 1 || n_wg < 1) return -1;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(gather_read_kernel<8>, dim3(n_wg), dim3(256), 0, (hipStream_t)stream, (const u32x4v*)src,
+                     rows, n_rows, out);
+  return hipGetLastError() == hipSuccess ? 0 : -2;
 }
 
 }  // extern "C"

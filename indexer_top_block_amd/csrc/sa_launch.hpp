@@ -66,6 +66,7 @@ struct FwdPlan {
   size_t ws_bytes;                         // scratch bytes (partial results), 0 when unsplit
 };
 FwdPlan plan_fwd(const sa_dims& d, int n_q);
+constexpr long long kPlanSlots = 512;      // the most workgroups a split plan aims at
 // A q8_0 K/V cache: int8 code planes and float16 scale planes (one scale per 32
 // codes), strides in elements.
 struct Q8Args {
@@ -89,7 +90,9 @@ int device_cus();
 // Merges the split partials (ws_o, ws_ml) into out; nothing when unsplit.
 hipError_t launch_combine(const sa_dims& d, int n_q, float* out, const float* ws_o, const float* ws_ml,
                           const FwdPlan& plan, hipStream_t stream);
-FwdPlan plan_fwd_window(const sa_dims& d, int n_q, int window, size_t ws_avail);
+FwdPlan plan_fwd_window(const sa_dims& d, int n_q, int window, size_t ws_avail, long long slots);
+// Workgroups that fill the chip for the attention kernel this call takes.
+long long fwd_slots(const sa_dims& d, const CacheArgs& c, const void* q);
 
 // ws: the scratch part of the workspace.
 hipError_t launch_mask_to_indices(const void* mask, int mask_dtype, int64_t mask_ld, int n_q, int n_kv,

@@ -24,7 +24,7 @@ SA_OK, SA_ERR_NULL, SA_ERR_DIMS, SA_ERR_ARG, SA_ERR_WORKSPACE, SA_ERR_HIP, SA_ER
 # Leading bytes of a workspace that hold state between calls (zero-filled once by the
 # caller, kept at zero by the library); SA_WS_STATE_BYTES in the header.
 WS_STATE_BYTES = 1056768
-STATIC_SCRATCH_BYTES = 16777216   # SA_STATIC_SCRATCH_BYTES
+STATIC_SCRATCH_BYTES = 16842752   # SA_STATIC_SCRATCH_BYTES
 
 EXPORTS = (
     "sparse_attn_check_dims",

@@ -262,10 +262,15 @@ def test_noalloc_fwd_rejects_bad_arguments_and_oversize():
     assert _call(fn, d, c, FAKE, FAKE, FAKE, 2051, FAKE, 1, ctypes.c_float(float("nan")), FAKE, None) == sa.SA_ERR_ARG
     assert _call(fn, d, c, FAKE, FAKE, FAKE, 0, FAKE, 1, f, FAKE, None) == sa.SA_ERR_ARG
     assert _call(fn, d, c, FAKE, FAKE, FAKE, 2051, FAKE, 0, f, FAKE, None) == sa.SA_OK   # nothing to do
-    # scratch needed = the workspace's scratch part: 31 tokens of the 576/512 shape (17
-    # splits each: 31 x 16 x 17 x 514 x 4 B = 17.3 MB) exceed 16 MiB; 30 tokens fit
-    need31 = sa.sparse_attn_workspace_bytes(_dims(), 31, 4096) - sa.WS_STATE_BYTES
-    need30 = sa.sparse_attn_workspace_bytes(_dims(), 30, 4096) - sa.WS_STATE_BYTES
-    assert need30 <= sa.STATIC_SCRATCH_BYTES < need31
-    assert _call(fn, d, c, FAKE, FAKE, FAKE, 2051, FAKE, 31, f, FAKE, None) == sa.SA_ERR_SCRATCH
+    # scratch needed = the workspace's scratch part; every shape with d_v <= 512 fits,
+    # e.g. any number of decode tokens of 16 heads 576/512
+    for n_q in (1, 15, 16, 31, 32, 256, 511):
+        need = sa.sparse_attn_workspace_bytes(_dims(), n_q, 4096)
+        assert (need - sa.WS_STATE_BYTES if need else 0) <= sa.STATIC_SCRATCH_BYTES, n_q
+    # wider V heads can exceed it: 16 tokens of 16 heads 1024/1024 (32 splits each)
+    wide = _dims(d_kq=1024, d_v=1024)
+    need = sa.sparse_attn_workspace_bytes(wide, 16, 4096) - sa.WS_STATE_BYTES
+    assert need > sa.STATIC_SCRATCH_BYTES
+    wc = ctypes.byref(_cache(k_ld=1024, v_ld=1024))
+    assert _call(fn, ctypes.byref(wide), wc, FAKE, FAKE, FAKE, 2051, FAKE, 16, f, FAKE, None) == sa.SA_ERR_SCRATCH
     assert "static scratch" in sa.sparse_attn_strerror(sa.SA_ERR_SCRATCH)

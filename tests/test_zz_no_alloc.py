@@ -59,9 +59,12 @@ def test_noalloc_fwd_matches_fwd_on_two_calls(gpu_lib):
 
 
 def test_noalloc_fwd_refuses_oversize(gpu_lib):
-    # 31 decode tokens need more partials than the static scratch holds: refused, and
-    # the output is untouched
-    case = _case("noalloc_oversize", [5000], [0] * 31, [4999 - 100 * j for j in range(31)], 2048, 952)
+    # 16 decode tokens of 16 heads with 1024-wide K and V need more partials than the
+    # static scratch holds: refused before any launch, and the output is untouched
+    dims = datagen.Dims(h_q=16, h_kv=1, d_kq=1024, d_v=1024, h_idx=64, d_idx=128, compress_ratio=4, top_k=2048,
+                        dtype="bf16")
+    case = datagen.make_case("noalloc_oversize", dims, [3000], [0] * 16, [2999 - 100 * j for j in range(16)], seed=0,
+                             case_id=952, std="inv_sqrt_dim", v_separate=True)
     layer = DeviceLayer(case)
     layer.out.fill_(-3.0)
     with pytest.raises(sa.SparseAttnError) as e:
