@@ -422,6 +422,41 @@ def measured_hbm_read() -> dict:
     return res
 
 
+def measured_latency() -> dict:
+    """Floors of a chain of small kernels on this chip (libsa_probe.so), each a graph
+    of 32 back-to-back launches replayed cold: an empty kernel, and one thread per
+    workgroup following 1, 2 or 4 dependent loads through a 1 GiB table of random
+    indices (each load a cache miss)."""
+    import ctypes
+
+    lib = ctypes.CDLL(os.path.join(ROOT, "indexer_top_block_amd", "libsa_probe.so"))
+    P = ctypes.c_void_p
+    lib.sa_probe_empty.argtypes = [ctypes.c_int, P]
+    lib.sa_probe_empty.restype = ctypes.c_int
+    lib.sa_probe_chain.argtypes = [P, P, ctypes.c_int, ctypes.c_int, P, P]
+    lib.sa_probe_chain.restype = ctypes.c_int
+    n = 1 << 28                                   # 1 GiB of int32 indices
+    rng = np.random.default_rng(1)
+    nxt = torch.randint(0, n, (n,), dtype=torch.int32, device="cuda")
+    starts = [torch.from_numpy(rng.integers(0, n, 256).astype(np.int32)).cuda() for _ in range(32)]
+    out = torch.empty(256, dtype=torch.int32, device="cuda")
+    flush = Flusher(1024)
+
+    def per_launch_us(call):
+        return round(time_graph(lambda k: call(k), 32, 2, flush) * 1e3, 3)
+
+    res = {"empty_kernel_us": per_launch_us(lambda k: lib.sa_probe_empty(256, torch.cuda.current_stream().cuda_stream))}
+    for hops in (1, 2, 4):
+        res[f"dependent_loads_{hops}_us"] = per_launch_us(
+            lambda k, h=hops: lib.sa_probe_chain(nxt.data_ptr(), starts[k % 32].data_ptr(), h, 256, out.data_ptr(),
+                                                 torch.cuda.current_stream().cuda_stream))
+    res["measured_with"] = ("graph replays of 32 launches after a 1 GiB read; 256 workgroups; chains through a "
+                            "1 GiB table of random int32 indices")
+    del nxt, out, flush
+    torch.cuda.empty_cache()
+    return res
+
+
 # ------------------------------------------------------------------------ prefill
 
 def prefill_report(steps: int, mfma_peak: dict) -> dict:
@@ -718,6 +753,7 @@ def main() -> int:
     peak = measured_mfma_peak()
     rec["mfma_bf16_peak"] = peak
     rec["hbm_read_measured"] = measured_hbm_read()
+    rec["latency_measured"] = measured_latency()
     if not args.no_prefill:
         log("[bench] prefill workload")
         rec["prefill"] = prefill_report(max(5, min(args.steps, 20)), peak)

@@ -130,3 +130,46 @@ int sa_probe_gather_read(const void* src, const int32_t* rows, int64_t n_rows, i
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------------
+// Latency probes: what a graph node and a dependent memory round trip cost, the
+// floors of a chain of small kernels.
+
+namespace {
+
+__global__ void empty_kernel(uint32_t* __restrict__ out) {
+  if (threadIdx.x == 0 && blockIdx.x == 0 && out == nullptr) out[0] = 1u;   // never taken; keeps the argument
+}
+
+// One thread per workgroup follows `hops` dependent loads through next[] (each index
+// read decides the next address), starting at start[blockIdx.x].
+__global__ void chain_kernel(const int32_t* __restrict__ next, const int32_t* __restrict__ start, int hops,
+                             int32_t* __restrict__ out) {
+  if (threadIdx.x != 0) return;
+  int32_t i = start[blockIdx.x];
+  for (int h = 0; h < hops; ++h) i = __builtin_nontemporal_load(&next[i]);
+  out[blockIdx.x] = i;
+}
+
+}  // namespace
+
+extern "C" {
+
+// An empty kernel of n_wg workgroups of 64 threads.
+int sa_probe_empty(int n_wg, void* stream) {
+  if (n_wg < 1) return -1;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(empty_kernel, dim3(n_wg), dim3(64), 0, (hipStream_t)stream, (uint32_t*)nullptr);
+  return hipGetLastError() == hipSuccess ? 0 : -2;
+}
+
+// n_wg workgroups each follow `hops` dependent loads; next[] and start[] hold valid
+// indices into next[] (the caller guarantees it); out: device, n_wg int32.
+int sa_probe_chain(const int32_t* next, const int32_t* start, int hops, int n_wg, int32_t* out, void* stream) {
+  if (!next || !start || !out || hops < 0 || n_wg < 1) return -1;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(chain_kernel, dim3(n_wg), dim3(64), 0, (hipStream_t)stream, next, start, hops, out);
+  return hipGetLastError() == hipSuccess ? 0 : -2;
+}
+
+}  // extern "C"
