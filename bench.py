@@ -653,8 +653,10 @@ def main() -> int:
     ap.add_argument("--eager", action="store_true", help="launch every step from the host (no graph)")
     ap.add_argument("--workload", type=int, choices=[2, 3, 5, 6], default=2,
                     help="decode workload of --only")
-    ap.add_argument("--only", choices=["pool_score", "pool", "score", "select", "fwd", "step"], default=None,
-                    help="run just this call for --steps launches over the rotated copies (counter collection)")
+    ap.add_argument("--only", choices=["pool_score", "pool", "score", "select", "fwd", "step", "prefill_score",
+                                       "prefill_fwd"], default=None,
+                    help="run just this call for --steps launches over the rotated copies of --workload, or one "
+                         "stage of the prefill chunk (counter collection)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--traffic-file", default=os.path.join(ROOT, "profiles", "score_mfma_kernel_decode128k_traffic.txt"),
@@ -683,6 +685,17 @@ def main() -> int:
         log(f"[bench] copy probe: {args.copy_probe_mb} MiB read + written by one elementwise kernel")
         del src, dst
 
+    if args.only in ("prefill_score", "prefill_fwd"):
+        from indexer_top_block_amd.device import DeviceLayer
+
+        log(f"[bench] --only {args.only}: generating workload 4")
+        lay = DeviceLayer(datagen.make_workload(4))
+        lay.pool(); lay.score(); lay.select()
+        torch.cuda.synchronize()
+        fn = lay.score if args.only == "prefill_score" else lay.fwd
+        ms = time_eager(lambda k: fn(), args.steps, args.warmup)
+        print(json.dumps({"only": args.only, "workload": 4, "launches": args.steps, "ms_per_launch": ms}))
+        return 0
     if args.only:
         cfg = args.workload
         layers = args.layers if cfg in (2, 6) else {5: 8, 3: 4}[cfg]
@@ -690,6 +703,7 @@ def main() -> int:
         case = datagen.make_workload(cfg)
         lay = RotatingLayers(case, layers)
         lay.fill_pools()
+        lay.step(0)                              # a real selection for select / fwd (same on every copy)
         torch.cuda.synchronize()
         fn = getattr(lay, args.only)
         ms = time_eager(lambda k: fn(k % layers), args.steps, args.warmup)
