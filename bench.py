@@ -139,10 +139,18 @@ class RotatingLayers:
         sa.sparse_attn_pool_score(self.dims, self.caches[r], self.n_pooled_prev, self.n_pooled_out, 1, self.qidx,
                                   self.q_seq, self.q_pos, self.n_q, self.scores, self.scores_ld)
 
+    def select_fwd(self, r):
+        """select + fwd in one call (the selection inside the attention's launch where it fits)."""
+        sa.sparse_attn_select_fwd(self.dims, self.caches[r], self.scores, self.scores_ld, self.q_seq, self.q_pos,
+                                  self.q, self.n_q, self.case.scale, self.sel, self.sel_ld, self.n_sel, self.out,
+                                  self.ws, self.ws_bytes)
+
+    def select_fwd_is_fused(self) -> bool:
+        return sa.sparse_attn_select_fwd_is_fused(self.dims, self.caches[0], self.q, self.n_q)
+
     def step(self, r):
         self.pool_score(r)
-        self.select(r)
-        self.fwd(r)
+        self.select_fwd(r)
 
 
 def algorithmic_bytes(case: datagen.Case, kv: str = "cache") -> dict:
@@ -252,7 +260,7 @@ def gbs(nbytes: float, ms: float) -> float:
 
 
 def decode_section(lay: "RotatingLayers", ab: dict, steps: int, warmup: int, flush: Flusher,
-                   kernels=("pool_score", "select", "fwd"), warm: bool = True) -> dict:
+                   kernels=("pool_score", "select_fwd", "select", "fwd"), warm: bool = True) -> dict:
     """Cold step time over the rotated copies (flush before the timed replay), each
     entry point alone under the same protocol, and (optionally) the warm step time."""
     R = lay.n
@@ -267,6 +275,7 @@ def decode_section(lay: "RotatingLayers", ab: dict, steps: int, warmup: int, flu
         fn = getattr(lay, name)
         per[name] = round(time_graph(lambda k, fn=fn: fn(k % R), steps, warmup, flush) * 1e3, 3)
     rec["kernel_avg_us"] = per
+    rec["select_fwd_fused"] = lay.select_fwd_is_fused()
     if warm:
         wms = time_graph(lambda k: lay.step(0), steps, warmup)
         rec["warm"] = {"us_per_step": round(wms * 1e3, 3), "value": round(gbs(ab["total"], wms), 2),
@@ -290,6 +299,15 @@ def roofline_block(ab: dict, sec: dict, score_kernel: str, traffic=None) -> dict
         fa = gbs(ab["gathered"], fus * 1e-3)
         r["attention"] = {"kernels": "attention + split combine (sparse_attn_fwd)", "bytes_per_call": ab["gathered"],
                           "avg_call_us": fus, "achieved": round(fa, 1), "frac": round(fa / HBM_PEAK_GBS, 4)}
+    if "select_fwd" in sec["kernel_avg_us"]:
+        sus = sec["kernel_avg_us"]["select_fwd"]
+        sb = ab["gathered"]
+        fa = gbs(sb, sus * 1e-3)
+        r["select_attention"] = {
+            "kernels": ("selection + attention in one launch, then the split combine (sparse_attn_select_fwd)"
+                        if sec.get("select_fwd_fused") else "sparse_attn_select then sparse_attn_fwd "
+                                                            "(sparse_attn_select_fwd, unfused form)"),
+            "bytes_per_call": sb, "avg_call_us": sus, "achieved": round(fa, 1), "frac": round(fa / HBM_PEAK_GBS, 4)}
     return r
 
 
@@ -625,7 +643,7 @@ def workload_decode_report(cfg: int, steps: int, warmup: int, layers: int, flush
     lay.fill_pools()
     torch.cuda.synchronize()
     log(f"[bench] workload {cfg}: {layers} copies resident; timing")
-    sec = decode_section(lay, ab, steps, warmup, flush, kernels=("pool_score", "select", "fwd"), warm=True)
+    sec = decode_section(lay, ab, steps, warmup, flush, warm=True)
     sec["workload"] = datagen.WORKLOADS[cfg]
     sec["layers_rotated"] = layers
     sec["roofline"] = roofline_block(ab, sec, "score_mfma_kernel (pooling variant)")
@@ -653,8 +671,8 @@ def main() -> int:
     ap.add_argument("--eager", action="store_true", help="launch every step from the host (no graph)")
     ap.add_argument("--workload", type=int, choices=[2, 3, 5, 6], default=2,
                     help="decode workload of --only")
-    ap.add_argument("--only", choices=["pool_score", "pool", "score", "select", "fwd", "step", "prefill_score",
-                                       "prefill_fwd"], default=None,
+    ap.add_argument("--only", choices=["pool_score", "pool", "score", "select", "fwd", "select_fwd", "step",
+                                       "prefill_score", "prefill_fwd"], default=None,
                     help="run just this call for --steps launches over the rotated copies of --workload, or one "
                          "stage of the prefill chunk (counter collection)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
@@ -727,10 +745,10 @@ def main() -> int:
                "frac_of_hbm_peak": round(gbs(ab["total"], ms) / HBM_PEAK_GBS, 4),
                "kernel_avg_us": {n: round(time_eager(lambda k, fn=getattr(lay, n): fn(k % R), args.steps,
                                                      args.warmup) * 1e3, 3)
-                                 for n in ("pool_score", "pool", "score", "select", "fwd")}}
+                                 for n in ("pool_score", "pool", "score", "select", "fwd", "select_fwd")}}
     else:
         sec = decode_section(lay, ab, args.steps, args.warmup, flush,
-                             kernels=("pool_score", "pool", "score", "select", "fwd"))
+                             kernels=("pool_score", "pool", "score", "select_fwd", "select", "fwd"))
     ms = sec["us_per_step"] * 1e-3
     log(f"[bench] step {sec['us_per_step']:.2f} us (cold); per-call us {sec['kernel_avg_us']}; "
         f"warm {sec.get('warm', {}).get('us_per_step')}")

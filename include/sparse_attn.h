@@ -13,11 +13,13 @@
  * #27970 "CUDA + ggml: add sparse-fa for DSV4/GLM": gather through an ascending
  * int32 index list, many query heads per KV head, V optionally a view of K).
  *
- * Four calls, one per step, all asynchronous on the caller's HIP stream:
+ * Four calls, one per step, all asynchronous on the caller's HIP stream (and one that
+ * joins the last two):
  *   sparse_attn_pool   -- incremental block mean-pool of the raw indexer keys
  *   sparse_attn_score  -- indexer block scores per query token
  *   sparse_attn_select -- kept blocks + tail -> ascending position list per query
  *   sparse_attn_fwd    -- gather-fused attention over the position lists
+ *   sparse_attn_select_fwd -- the two above in one call (one launch where it fits)
  *
  * Conventions shared by every call
  *  - Ownership: the caller allocates every buffer; the library never allocates,
@@ -191,6 +193,30 @@ int sparse_attn_select(const sa_dims* dims, const sa_cache* cache, const float* 
 int sparse_attn_fwd(const sa_dims* dims, const sa_cache* cache, const void* q,
                     const int32_t* q_seq, const int32_t* sel, int64_t sel_ld, const int32_t* n_sel,
                     int32_t n_q, float scale, float* out, void* ws, size_t ws_bytes, void* stream);
+
+/* sparse_attn_select followed by sparse_attn_fwd (pages: the indexer's block selection
+ * of the QSA commit, then the sparse flash attention of PR #27970 over the list it
+ * writes), for the same n_q query tokens: writes sel, n_sel and out exactly as the two
+ * calls would, bit for bit.  When every (token, KV head, split) workgroup of the
+ * attention has a compute unit of its own -- few decode tokens, rows of at most 32768
+ * blocks, the MLA shapes with V inside K (d_v 512, d_kq 512 or 576, f16 / bf16), lists
+ * of at most 3072 entries -- the selection runs inside the attention's launch (each
+ * workgroup selects its token's list into LDS), saving a launch and the list's round
+ * trip through memory; otherwise the call makes the two calls.  Arguments are those of
+ * the two calls (scores/scores_ld/q_pos as in sparse_attn_select; q/scale/out as in
+ * sparse_attn_fwd); ws: sparse_attn_workspace_bytes(dims, n_q, cache->max_len) bytes,
+ * one buffer for both parts.
+ * Errors: those of sparse_attn_select and of sparse_attn_fwd.                        */
+int sparse_attn_select_fwd(const sa_dims* dims, const sa_cache* cache, const float* scores,
+                           int64_t scores_ld, const int32_t* q_seq, const int32_t* q_pos, const void* q,
+                           int32_t n_q, float scale, int32_t* sel, int64_t sel_ld, int32_t* n_sel,
+                           float* out, void* ws, size_t ws_bytes, void* stream);
+
+/* Which form sparse_attn_select_fwd takes for these arguments on the current device:
+ * 1 = the selection inside the attention's launch, 0 = the two calls; a negative
+ * SA_ERR_* on bad arguments (n_q < 1 is SA_ERR_ARG).  Host only: reads the device's
+ * compute-unit count, launches nothing.                                              */
+int sparse_attn_select_fwd_is_fused(const sa_dims* dims, const sa_cache* cache, const void* q, int32_t n_q);
 
 /* Bytes of the library's static scratch (per GPU), used by sparse_attn_fwd_noalloc:
  * the split partials of 512 workgroups of 16 query heads with d_v = 512 (the most the

@@ -19,8 +19,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsparse_attn.so")
-SOURCES = ["api.cpp", "pool.hip", "score.hip", "select.hip", "fwd.hip", "fwd_q8.hip", "fwd_static.hip", "mask.hip",
-           "quant.hip"]
+SOURCES = ["api.cpp", "pool.hip", "score.hip", "select.hip", "fwd.hip", "select_fwd.hip", "fwd_q8.hip", "fwd_static.hip",
+           "mask.hip", "quant.hip"]
 # the benchmark's measurement probe (a plain MFMA loop), a library of its own
 PROBE_LIB = os.path.join(PKG, "libsa_probe.so")
 PROBE_SOURCES = ["probe_mfma.hip"]

@@ -145,11 +145,13 @@ int sparse_attn_select(const sa_dims* dims, const sa_cache* cache, const float* 
                                       n_sel, ws, (hipStream_t)stream));
 }
 
-// use_static: the split partials go to the library's static scratch, ws is unused.
-static int fwd_common(const sa_dims* dims, const sa_cache* cache, const void* q, const int32_t* q_seq,
-                      const int32_t* sel, int64_t sel_ld, const int32_t* n_sel, const float* sel_bias,
-                      const int32_t* q_pos, int32_t window, int32_t n_q, float scale, float* out, void* ws,
-                      size_t ws_bytes, void* stream, bool use_static = false) {
+// Checks of the attention's arguments (those sel/n_sel/q_pos/window shared with the
+// select are the caller's), then its split plan for this device and the partials'
+// scratch.  use_static: the partials go to the library's static scratch, ws is unused.
+static int fwd_prepare(const sa_dims* dims, const sa_cache* cache, const void* q, const int32_t* q_seq,
+                       const int32_t* sel, int64_t sel_ld, const int32_t* n_sel, const int32_t* q_pos, int32_t window,
+                       int32_t n_q, float scale, float* out, void* ws, size_t ws_bytes, bool use_static,
+                       sa::FwdPlan* plan, void** scratch) {
   int rc = check_dims(dims);
   if (rc) return rc;
   if ((rc = check_cache_common(dims, cache))) return rc;
@@ -179,17 +181,67 @@ static int fwd_common(const sa_dims* dims, const sa_cache* cache, const void* q,
     }
   }
   (void)hipGetLastError();
-  const sa::FwdPlan plan = sa::plan_fwd_window(*dims, n_q, window, ws_avail, sa::fwd_slots(*dims, to_args(cache), q));
-  void* scratch = nullptr;
-  if (plan.ws_bytes > 0) {
+  *plan = sa::plan_fwd_window(*dims, n_q, window, ws_avail, sa::fwd_slots(*dims, to_args(cache), q));
+  *scratch = nullptr;
+  if (plan->ws_bytes > 0) {
     if (use_static) {
-      if (sa::static_scratch(&scratch) != hipSuccess) return SA_ERR_HIP;
+      if (sa::static_scratch(scratch) != hipSuccess) return SA_ERR_HIP;
     } else {
-      scratch = (char*)ws + SA_WS_STATE_BYTES;
+      *scratch = (char*)ws + SA_WS_STATE_BYTES;
     }
   }
+  return SA_OK;
+}
+
+static int fwd_common(const sa_dims* dims, const sa_cache* cache, const void* q, const int32_t* q_seq,
+                      const int32_t* sel, int64_t sel_ld, const int32_t* n_sel, const float* sel_bias,
+                      const int32_t* q_pos, int32_t window, int32_t n_q, float scale, float* out, void* ws,
+                      size_t ws_bytes, void* stream, bool use_static = false) {
+  sa::FwdPlan plan{};
+  void* scratch = nullptr;
+  const int rc = fwd_prepare(dims, cache, q, q_seq, sel, sel_ld, n_sel, q_pos, window, n_q, scale, out, ws, ws_bytes,
+                             use_static, &plan, &scratch);
+  if (rc != SA_OK || n_q == 0) return rc;
   return hip_status(sa::launch_fwd(*dims, to_args(cache), q, q_seq, sel, sel_ld, n_sel, sel_bias, q_pos, window,
                                    n_q, scale, out, scratch, plan, (hipStream_t)stream));
+}
+
+int sparse_attn_select_fwd(const sa_dims* dims, const sa_cache* cache, const float* scores, int64_t scores_ld,
+                           const int32_t* q_seq, const int32_t* q_pos, const void* q, int32_t n_q, float scale,
+                           int32_t* sel, int64_t sel_ld, int32_t* n_sel, float* out, void* ws, size_t ws_bytes,
+                           void* stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if ((rc = check_cache_common(dims, cache))) return rc;
+  if (n_q < 0) return SA_ERR_ARG;
+  if (n_q == 0) return SA_OK;
+  // the select's checks
+  if (!scores || !q_seq || !q_pos || !sel || !n_sel) return SA_ERR_NULL;
+  if (sel_ld < (int64_t)dims->top_k + dims->compress_ratio - 1) return SA_ERR_ARG;
+  if (scores_ld < (int64_t)(cache->max_len / dims->compress_ratio) || scores_ld < 0) return SA_ERR_ARG;
+  if (sa::select_scratch_bytes(*dims, n_q, cache->max_len) > 0) {
+    const size_t need = sa::workspace_bytes(*dims, n_q, cache->max_len);
+    if (!ws || ws_bytes < need) return SA_ERR_WORKSPACE;
+  }
+  // the attention's
+  sa::FwdPlan plan{};
+  void* scratch = nullptr;
+  rc = fwd_prepare(dims, cache, q, q_seq, sel, sel_ld, n_sel, q_pos, 0, n_q, scale, out, ws, ws_bytes, false, &plan,
+                   &scratch);
+  if (rc != SA_OK) return rc;
+  return hip_status(sa::launch_select_fwd(*dims, to_args(cache), scores, scores_ld, q_seq, q_pos, n_q, sel, sel_ld,
+                                          n_sel, q, scale, out, ws, scratch, plan, (hipStream_t)stream));
+}
+
+int sparse_attn_select_fwd_is_fused(const sa_dims* dims, const sa_cache* cache, const void* q, int32_t n_q) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if ((rc = check_cache_common(dims, cache))) return rc;
+  if (n_q < 1 || (int64_t)n_q * dims->h_kv > kMaxGridY) return SA_ERR_ARG;
+  if (!cache->k || !cache->v || !q) return SA_ERR_NULL;
+  const sa::CacheArgs a = to_args(cache);
+  const sa::FwdPlan plan = sa::plan_fwd_window(*dims, n_q, 0, SIZE_MAX, sa::fwd_slots(*dims, a, q));
+  return sa::select_fwd_fused(*dims, a, q, n_q, plan) ? 1 : 0;
 }
 
 int sparse_attn_fwd(const sa_dims* dims, const sa_cache* cache, const void* q, const int32_t* q_seq,

@@ -103,6 +103,15 @@ hipError_t launch_fwd(const sa_dims& d, const CacheArgs& c, const void* q, const
                       const int32_t* q_pos, int window, int n_q, float scale, float* out, void* ws,
                       const FwdPlan& plan, hipStream_t stream);
 
+// sparse_attn_select then sparse_attn_fwd (plain form) for the same query tokens, in
+// one launch plus the combine when select_fwd_fused says so (select_fwd.hip).  ws: the
+// whole workspace (the select's); scratch: its partials part (null when unsplit).
+bool select_fwd_fused(const sa_dims& d, const CacheArgs& c, const void* q, int n_q, const FwdPlan& plan);
+hipError_t launch_select_fwd(const sa_dims& d, const CacheArgs& c, const float* scores, int64_t scores_ld,
+                             const int32_t* q_seq, const int32_t* q_pos, int n_q, int32_t* sel, int64_t sel_ld,
+                             int32_t* n_sel, const void* q, float scale, float* out, void* ws, void* scratch,
+                             const FwdPlan& plan, hipStream_t stream);
+
 // Device address of this device's copy of the static scratch array
 // (SA_STATIC_SCRATCH_BYTES), looked up on first use per device (fwd_static.hip).
 hipError_t static_scratch(void** ptr);

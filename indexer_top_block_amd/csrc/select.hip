@@ -47,6 +47,7 @@
 // ties), it runs the 4-pass algorithm above over the whole row instead.
 #include "sa_common.hpp"
 #include "sa_launch.hpp"
+#include "select_wide.hpp"
 
 namespace sa {
 
@@ -65,23 +66,6 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 // Callers mask keys past the row's end themselves.
 __device__ __forceinline__ uint32_t key_clamped(const float* __restrict__ row, int idx, int last) {
   return order_key(row[idx < last ? idx : last]);
-}
-
-// Positions of the dense case (every block fits): 0 .. n_vis-1, then -1.
-template <int BLOCK>
-__device__ __forceinline__ void write_dense(int32_t* out, int64_t sel_ld, int n_vis, int32_t* n_sel_out) {
-  for (int64_t j = threadIdx.x; j < sel_ld; j += BLOCK) out[j] = j < n_vis ? (int32_t)j : -1;
-  if (threadIdx.x == 0) *n_sel_out = n_vis;
-}
-
-// Tail positions after the K_blk kept blocks, then -1, then the count.
-template <int BLOCK>
-__device__ __forceinline__ void write_tail(int32_t* out, int64_t sel_ld, int nb, int n_vis, int c, int k_blk,
-                                           int32_t* n_sel_out) {
-  const int body = k_blk * c, tail = n_vis - nb * c;
-  for (int j = threadIdx.x; j < tail; j += BLOCK) out[body + j] = nb * c + j;
-  for (int64_t j = body + tail + threadIdx.x; j < sel_ld; j += BLOCK) out[j] = -1;
-  if (threadIdx.x == 0) *n_sel_out = body + tail;
 }
 
 // ------------------------------------------------------- per-query workgroup select
@@ -241,10 +225,6 @@ constexpr int kHistCopies = 4;
 constexpr int kEntCap = 16384;                       // entries the finishing workgroup holds in LDS
 constexpr int kMaxChunks = 2048;                     // chunks per query it tallies
 
-struct QueryRowInfo {
-  int nb, n_vis;                                     // visible complete blocks, visible positions
-};
-
 // Scratch of one query: bin and remaining count from the histogram pass, the
 // number of entries each chunk kept, and each chunk's entries (index order).
 struct ChunkScratch {
@@ -287,14 +267,6 @@ __device__ __forceinline__ void find_top_bin(const uint32_t (&cnt)[PER], int k, 
 
 __device__ __forceinline__ uint32_t coherent_load(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Visible complete blocks of query q.
-__device__ __forceinline__ QueryRowInfo query_blocks(const int32_t* seq_len, const int32_t* q_seq,
-                                                     const int32_t* q_pos, int q, int c) {
-  const SeqMeta m = seq_meta(q_seq, seq_len, nullptr, nullptr, q);
-  const int n_vis = visible_tokens(m.len, q_pos[q]);
-  return QueryRowInfo{n_vis / c, n_vis};
 }
 
 // Pass 1 (one workgroup per chunk): the chunk's histogram of the top 12 key bits is
@@ -409,309 +381,43 @@ chunk_select_kernel(const float* __restrict__ scores, int64_t scores_ld, const i
 // ------------------------------------------------------ one wide workgroup per row
 
 // Decode rows of up to 32768 blocks: one 1024-thread workgroup holds the whole row in
-// registers and needs no workspace.  Thread t owns blocks j*1024 + t (j < KPT), so
-// every load is coalesced.  The K_blk-th largest key T is found by radix select
-// over the registers, most significant digit first (10, 11, then 11 bits), each
-// pass histogramming the keys that match the digits fixed so far; a pass whose
-// chosen bin is taken whole (its count equals the number still to take) ends the
-// search early, and the remaining digits do not matter.
-//
-// One compute unit runs the whole row, so the cost is the vector instructions spent
-// per key in each pass (about 0.2 us per instruction per key at 32768 keys), and the
-// passes are written for few of them:
-//   - keys are formed with two integer operations after an add that folds -0 into +0;
-//   - the first pass, which counts every key, adds into 32 copies of its histogram
-//     laid out [bin][copy] (the address is the digit shifted onto the lane's copy, no
-//     other arithmetic), so keys sharing a digit -- scores crowd into a few binades --
-//     hit different copies; a 10-bit first digit keeps 32 copies within the LDS that
-//     16 copies of an 11-bit digit took, and halves the lanes sharing each copy;
-//   - later passes test membership in the running bin with one subtract and compare;
-//   - kept blocks (key at or above a threshold) and, when the search ran to the full
-//     32 bits, the keys equal to T go to bitmaps of the row with one compare and one
-//     wave ballot per register (64 consecutive blocks); every wave then places its 64
-//     bitmap words itself, counting the bits of the words before its own, so the
-//     output needs no workgroup-wide prefix sum.  Only the first keys equal to T in
-//     index order are taken.
+// registers and needs no workspace (the radix select of select_wide.hpp).
 constexpr int kWideThreads = 1024;
 constexpr int kWideMaxKpt = 32;
-constexpr int kWideBins = 2048;                      // passes 2 and 3 (11-bit digits)
-constexpr int kP1Bins = 1024;                        // pass 1 (10-bit digit)
-// Pass-1 histogram copies and bitmap words by row size: rows of up to 16384 keys take
-// 16 copies and their own bitmap size, so that the workgroup's LDS (< 80 KiB) and
-// registers leave room for a second workgroup on the CU (prefill: many rows).
-template <int KPT>
-struct WideCfg {
-  static constexpr int copies = KPT >= 32 ? 32 : 16;  // lanes l, l+copies, ... share a copy
-  static constexpr int words = KPT * 32;             // bitmap words (32 blocks each)
-};
-
-template <int KPT>
-struct alignas(16) WideSmem {
-  uint32_t h2[kWideBins];                            // pass 2 (first: its bins' addresses need no base)
-  uint32_t h1[kP1Bins * WideCfg<KPT>::copies];      // pass 1 [bin][copy]; pass 3: words 0..2047; the list
-  uint32_t keep[WideCfg<KPT>::words];                // blocks at or above the threshold
-  uint32_t tie[WideCfg<KPT>::words];                 // blocks equal to T (full-width search)
-  int wsum[2][kWideThreads / kWave];                 // per-wave totals, alternating between picks
-  int pick[4];
-};
-
-// Order-preserving 32-bit key of a score: +0 and -0 give the same key, negative
-// scores map below positive ones.
-__device__ __forceinline__ uint32_t score_key(float f) {
-  const uint32_t u = __float_as_uint(f + 0.0f);      // -0 + +0 = +0
-  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
-}
-
-// The bin holding the k-th largest of the counted keys, for a histogram held as PER
-// consecutive bins per thread (thread t: bins [t*PER, t*PER + PER)), with `pad` keys
-// taken back out of bin 0.  Writes bin, keys in higher bins and keys in the bin to
-// pick[0..2] and synchronises.  `wsum` must not be in use by the previous pick.
-// Every wave posts its total; each then finds, from the 16 totals, the one wave whose
-// range holds the k-th key, and only that wave scans its lanes.
-template <int PER>
-__device__ __forceinline__ void wide_pick(uint32_t (&cnt)[PER], int k, int pad, int* wsum, int* pick) {
-  constexpr int kWaves = kWideThreads / kWave;
-  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-  if (tid == 0) cnt[0] -= (uint32_t)pad;
-  int sum = 0;
-#pragma unroll
-  for (int j = 0; j < PER; ++j) sum += (int)cnt[j];
-  const int incl = wave_inclusive_scan(sum, lane);
-  const int wave_total = __builtin_amdgcn_readlane(incl, kWave - 1);
-  if (lane == 0) wsum[wave] = wave_total;
-  __syncthreads();
-  // lanes 0..15: keys in the waves above wave `lane`, and whether the k-th is in it
-  const int v = lane < kWaves ? wsum[lane] : 0;
-  const int v_incl = wave_inclusive_scan(v, lane);
-  const int v_after = __builtin_amdgcn_readlane(v_incl, kWave - 1) - v_incl;
-  const uint64_t hit = __ballot(lane < kWaves && v_after < k && v_after + v >= k);
-  const int w_hit = (int)__builtin_ctzll(hit | (1ull << 63));   // exactly one wave when 0 < k <= keys
-  if (wave == w_hit) {
-    int above = __builtin_amdgcn_readlane(v_after, w_hit) + wave_total - incl;   // keys in bins >= (t+1)*PER
-#pragma unroll
-    for (int j = PER - 1; j >= 0; --j) {
-      const int gt = above, ge = above + (int)cnt[j];
-      if (gt < k && ge >= k) {
-        pick[0] = tid * PER + j;
-        pick[1] = gt;
-        pick[2] = (int)cnt[j];
-      }
-      above = ge;
-    }
-  }
-  __syncthreads();
-}
-
-// Set bits in the bitmap words before word 64 * wave (lane l reads words [16 l, 16 l + 16));
-// the bitmap holds `words` words.
-__device__ __forceinline__ int bits_before(const uint32_t* bm, int words, int wave, int lane) {
-  int n = 0;
-  if (lane < 4 * wave && lane * 16 < words) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint4 v = *(const uint4*)&bm[lane * 16 + i * 4];
-      n += __popc(v.x) + __popc(v.y) + __popc(v.z) + __popc(v.w);
-    }
-  }
-  return __builtin_amdgcn_readlane(wave_inclusive_scan(n, lane), kWave - 1);
-}
-
-// The compiler's lane write (v_writelane_b32: lane `lane` of `old` replaced by the
-// wave-uniform `x`), declared by its intrinsic name so that the compiler, which
-// knows its wait-state rules, schedules it.
-__device__ int amdgcn_writelane(int x, int lane, int old) __asm("llvm.amdgcn.writelane.i32");
-
-// Lane j < N of (lo, hi) receives the wave's ballot of pred(j): the low and the
-// high 32 lanes' bits.
-template <int N, int J = 0, typename P>
-__device__ __forceinline__ void ballot_rows(P pred, uint32_t& lo, uint32_t& hi) {
-  if constexpr (J < N) {
-    const uint64_t m = __ballot(pred(J));
-    lo = (uint32_t)amdgcn_writelane((int)(uint32_t)m, J, (int)lo);
-    hi = (uint32_t)amdgcn_writelane((int)(uint32_t)(m >> 32), J, (int)hi);
-    ballot_rows<N, J + 1>(pred, lo, hi);
-  }
-}
-
-// Positions p0 .. p0 + c - 1 of one kept block.
-__device__ __forceinline__ void store_block(int32_t* dst, int32_t p0, int c) {
-  if (c == 4) {
-#pragma unroll
-    for (int t = 0; t < 4; ++t) dst[t] = p0 + t;
-  } else {
-    for (int t = 0; t < c; ++t) dst[t] = p0 + t;
-  }
-}
 
 template <int KPT>
 __global__ void __launch_bounds__(kWideThreads)
 select_wide_kernel(const float* __restrict__ scores, int64_t scores_ld, const int32_t* __restrict__ seq_len,
                    const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos, int c, int k_blk,
                    int32_t* __restrict__ sel, int64_t sel_ld, int32_t* __restrict__ n_sel) {
-  constexpr int COPIES = WideCfg<KPT>::copies, WORDS = WideCfg<KPT>::words;
-  __shared__ WideSmem<KPT> sm;
-  const int q = blockIdx.x, tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  constexpr int NT = kWideThreads, COPIES = WideCfg<NT, KPT>::copies;
+  __shared__ WideSmem<NT, KPT> sm;
+  const int q = blockIdx.x, tid = threadIdx.x;
   const float* row = scores + (int64_t)q * scores_ld;
   // The whole row is loaded up front and kept in registers for every pass; the
   // query's length arrives with it (indices below scores_ld are valid memory).
   float raw[KPT];
   {
-    const int last = (int)min(scores_ld, (int64_t)KPT * kWideThreads) - 1;
+    const int last = (int)min(scores_ld, (int64_t)KPT * NT) - 1;
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) raw[j] = row[min(j * kWideThreads + tid, last)];
+    for (int j = 0; j < KPT; ++j) raw[j] = row[min(j * NT + tid, last)];
   }
   const QueryRowInfo qr = query_blocks(seq_len, q_seq, q_pos, q, c);
-  for (int e = tid; e < kP1Bins * COPIES / 4; e += kWideThreads) ((uint4*)sm.h1)[e] = uint4{0u, 0u, 0u, 0u};
-  for (int e = tid; e < kWideBins; e += kWideThreads) sm.h2[e] = 0u;
+  for (int e = tid; e < kP1Bins * COPIES / 4; e += NT) ((uint4*)sm.h1)[e] = uint4{0u, 0u, 0u, 0u};
+  for (int e = tid; e < kWideBins; e += NT) sm.h2[e] = 0u;
   __builtin_amdgcn_sched_barrier(0);                 // every load in flight before the first is used
   int32_t* out = sel + (int64_t)q * sel_ld;
   if (qr.nb <= k_blk) {
-    write_dense<kWideThreads>(out, sel_ld, qr.n_vis, n_sel + q);
+    write_dense<NT>(out, sel_ld, qr.n_vis, n_sel + q);
     return;
   }
-  const int nb = min(qr.nb, KPT * kWideThreads);     // the launch guarantees qr.nb fits; the bitmap relies on it
-  const int n_pad = KPT * kWideThreads - nb;
   __syncthreads();                                   // the histograms are clear (the loads may still fly)
-
-  // ---- pass 1: the top 10 bits, each key counted as it arrives ---------------------------
-  // Keys past the row's end become 0 -- below every key a score can have except
-  // negative NaNs -- so the passes need no bounds checks: the picks take the n_pad
-  // padding keys back out of bin 0, and a prefix of 0 (the only one they can match)
-  // never takes its bin whole, so they are never kept.
-  uint32_t key[KPT];
-  {
-    uint32_t* mine = sm.h1 + (lane & (COPIES - 1));
-    if (n_pad == 0) {
-#pragma unroll
-      for (int j = 0; j < KPT; ++j) {
-        key[j] = score_key(raw[j]);
-        atomicAdd(&mine[(key[j] >> 22) * COPIES], 1u);
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < KPT; ++j) {
-        key[j] = j * kWideThreads + tid < nb ? score_key(raw[j]) : 0u;
-        atomicAdd(&mine[(key[j] >> 22) * COPIES], 1u);
-      }
-    }
-  }
-  __syncthreads();
-  {
-    // thread t: bin t, its copies read as quads from a lane-rotated start, so that
-    // consecutive lanes spread over the banks
-    constexpr int NQD = COPIES / 4;
-    uint32_t cnt[1] = {0u};
-    const uint4* h = (const uint4*)(sm.h1 + tid * COPIES);
-#pragma unroll
-    for (int i = 0; i < NQD; ++i) {
-      const uint4 v = h[(i + tid) & (NQD - 1)];
-      cnt[0] += v.x + v.y + v.z + v.w;
-    }
-    wide_pick<1>(cnt, k_blk, n_pad, sm.wsum[0], sm.pick);
-  }
-  uint32_t prefix = (uint32_t)sm.pick[0];            // key >> shift of the keys still in the running
-  int k_rem = k_blk - sm.pick[1];
-  int shift = 22;
-  bool whole = sm.pick[2] == k_rem && prefix != 0u;
-  // ---- pass 2: next 11 bits among keys in the bin -----------------------------------------
-  if (!whole) {
-    ((uint2*)sm.h1)[tid] = uint2{0u, 0u};             // words 0..2047 serve pass 3
-    const uint32_t lo = prefix << 22;
-    uint32_t one = 1u;
-    asm volatile("" : "+v"(one));                    // one register for every add, not one per key
-#pragma unroll
-    for (int j = 0; j < KPT; ++j)
-      if (key[j] - lo < (1u << 22)) atomicAdd(&sm.h2[(key[j] >> 11) & (kWideBins - 1)], one);
-    __syncthreads();
-    uint32_t cnt[2] = {sm.h2[tid * 2], sm.h2[tid * 2 + 1]};
-    wide_pick<2>(cnt, k_rem, prefix == 0u ? n_pad : 0, sm.wsum[1], sm.pick);
-    prefix = (prefix << 11) | (uint32_t)sm.pick[0];
-    k_rem -= sm.pick[1];
-    shift = 11;
-    whole = sm.pick[2] == k_rem && prefix != 0u;
-    // ---- pass 3: last 11 bits ------------------------------------------------------------
-    if (!whole) {
-      const uint32_t lo3 = prefix << 11;
-#pragma unroll
-      for (int j = 0; j < KPT; ++j)
-        if (key[j] - lo3 < (1u << 11)) atomicAdd(&sm.h1[key[j] & 2047u], 1u);
-      __syncthreads();
-      uint32_t cnt3[2] = {sm.h1[tid * 2], sm.h1[tid * 2 + 1]};
-      wide_pick<2>(cnt3, k_rem, prefix == 0u ? n_pad : 0, sm.wsum[0], sm.pick);
-      prefix = (prefix << 11) | (uint32_t)sm.pick[0];
-      k_rem -= sm.pick[1];
-      shift = 0;
-      whole = sm.pick[2] == k_rem && prefix != 0u;
-    }
-  }
-  // ---- kept blocks -> bitmaps -----------------------------------------------------------
-  // Kept for sure: key >> shift above the prefix, or equal to it when its bin is
-  // taken whole, i.e. key >= thr.  A search that did not end whole ran to the full
-  // width (shift 0): keys above T are kept, keys equal to T are ties.  Padding keys
-  // are 0: below every threshold of a prefix other than 0, which is never whole.
-  // Register j of the wave's lanes holds blocks j*1024 + 64*wave + [0, 64): bitmap
-  // words 32j + 2 wave + {0, 1}, collected in lane j.
-  {
-    uint32_t k_lo = 0u, k_hi = 0u, t_lo = 0u, t_hi = 0u;
-    if (whole || prefix != 0xffffffffu) {
-      const uint32_t thr = whole ? prefix << shift : prefix + 1u;
-      ballot_rows<KPT>([&](int j) { return key[j] >= thr; }, k_lo, k_hi);
-    }
-    if (!whole) ballot_rows<KPT>([&](int j) { return key[j] == prefix; }, t_lo, t_hi);
-    if (lane < KPT) {
-      *(uint2*)&sm.keep[lane * 32 + wave * 2] = uint2{k_lo, k_hi};
-      *(uint2*)&sm.tie[lane * 32 + wave * 2] = uint2{t_lo, t_hi};
-    }
-  }
-  __syncthreads();
-  // ---- this wave's 64 words -> positions in index order ---------------------------------------
-  const int w = wave * kWave + lane;                 // bitmap word of this lane: blocks 32w .. 32w+31
-  uint32_t word = w < WORDS ? sm.keep[w] : 0u;
-  int o = bits_before(sm.keep, WORDS, wave, lane);
-  if (!whole) {                                      // the first k_rem tied blocks in index order
-    uint32_t t = w < WORDS ? sm.tie[w] : 0u;
-    const int t_before = bits_before(sm.tie, WORDS, wave, lane);
-    o += min(k_rem, t_before);
-    int take = k_rem - t_before - (wave_inclusive_scan(__popc(t), lane) - __popc(t));
-    while (t != 0u && take > 0) {
-      const uint32_t low = t & (0u - t);
-      word |= low;
-      t ^= low;
-      --take;
-    }
-  }
-  o += wave_inclusive_scan(__popc(word), lane) - __popc(word);
   const int body = k_blk * c;
-  if (body <= kP1Bins * COPIES) {
-    // the list is assembled in LDS (pass 1's histogram is free) and written out
-    // coalesced, rather than as scattered stores of a few lanes each
-    int32_t* list = (int32_t*)sm.h1;
-    if (c == 4) {
-      while (word != 0u && o < k_blk) {              // o < k_blk always; the bound only guards memory
-        const int32_t p0 = (w * 32 + __ffs(word) - 1) * 4;
-        word &= word - 1u;
-        *(int4*)&list[o * 4] = int4{p0, p0 + 1, p0 + 2, p0 + 3};
-        ++o;
-      }
-    } else {
-      while (word != 0u && o < k_blk) {
-        const int32_t p0 = (w * 32 + __ffs(word) - 1) * c;
-        word &= word - 1u;
-        for (int t = 0; t < c; ++t) list[o * c + t] = p0 + t;
-        ++o;
-      }
-    }
-    __syncthreads();
-    for (int i = tid; i < body; i += kWideThreads) out[i] = list[i];
-  } else {
-    while (word != 0u && o < k_blk) {                // o < k_blk always; the bound only guards memory
-      const int b = __ffs(word) - 1;
-      word &= word - 1u;
-      store_block(out + (int64_t)o * c, (w * 32 + b) * c, c);
-      ++o;
-    }
-  }
-  write_tail<kWideThreads>(out, sel_ld, nb, qr.n_vis, c, k_blk, n_sel + q);
+  int32_t* list = body <= kP1Bins * COPIES ? (int32_t*)sm.h1 : nullptr;   // pass 1's histogram is free by then
+  wide_select_rows<NT, KPT>(raw, 0, qr.nb, c, k_blk, sm, list, out);
+  if (list)
+    for (int i = tid; i < body; i += NT) out[i] = list[i];
+  write_tail<NT>(out, sel_ld, qr.nb, qr.n_vis, c, k_blk, n_sel + q);
 }
 
 // ------------------------------------------------------------ chunked: finish
@@ -830,7 +536,7 @@ chunk_finish_kernel(const float* __restrict__ scores, int64_t scores_ld, const i
       for (int b = tid; b < kFinBins; b += kSelThreads) sm.f.h[(pass + 1) & 1][b] = 0u;
     __syncthreads();
     uint32_t cnt2[2] = {h[2 * tid], h[2 * tid + 1]};
-    wide_pick<2>(cnt2, k_rem, 0, sm.f.wsum[pass & 1], sm.f.pick);
+    wide_pick<kSelThreads, 2>(cnt2, k_rem, 0, sm.f.wsum[pass & 1], sm.f.pick);
     prefix = (prefix << width) | (uint64_t)sm.f.pick[0];
     k_rem -= sm.f.pick[1];
     if (sm.f.pick[2] == 1 || shift == 0) {           // the cut is the single value left in the bin

@@ -1,0 +1,173 @@
+// Block selection and attention in one launch (sparse_attn_select_fwd).
+//
+// The decode chain is a row of dependent launches (score -> select -> attention ->
+// combine), each of which costs a launch and at least one memory round trip before
+// its work starts.  When every (query token, KV head, split) workgroup of the
+// attention has a compute unit to itself, the select can ride along: each
+// workgroup runs the one-workgroup radix select of its query's row (select_wide.hpp)
+// with 8 waves, keeps the list in LDS, and then attends over its own split's rows
+// with 4 of them (fwd_lds.hpp) -- every workgroup of a query computes the same list.
+// That removes the select's launch and the list's trip through memory; the split
+// partials are merged by the usual combine launch.
+//
+// Workgroup (split 0, KV head 0) of each query also writes the list, the padding and
+// the count, so the call leaves exactly what sparse_attn_select followed by
+// sparse_attn_fwd leaves, bit for bit (the same select, the same split plan, the same
+// attention arithmetic).  Calls that do not fit (more workgroups than compute units,
+// rows of more than 32768 blocks, shapes other than the MLA ones with V inside K,
+// lists longer than kFusedListMax) take those two calls instead.
+#include "fwd_lds.hpp"
+#include "select_wide.hpp"
+
+namespace sa {
+
+constexpr int kFusedThreads = 512;           // 8 waves select; waves 0..3 then attend
+constexpr int kFusedMaxKpt = 64;             // keys per thread: rows of up to 32768 blocks
+constexpr int kFusedListMax = 3072;          // list entries held in LDS (top_k + c - 1)
+
+// The list the workgroup selected, in LDS: cnt entries (kept blocks, then the tail),
+// read clamped so that every lane reads valid memory.
+struct LdsList {
+  const int32_t* lds;
+  int cnt;
+  SeqMeta sm;                                        // read at the start, while the select ran
+  __device__ __forceinline__ int at(int j) const { return cnt > 0 ? lds[min(j, cnt - 1)] : -1; }
+  __device__ __forceinline__ float bias(int) const { return 0.f; }
+  __device__ __forceinline__ bool has_bias() const { return false; }
+  __device__ __forceinline__ int count() const { return cnt; }
+  __device__ __forceinline__ SeqMeta meta(const int32_t*, const int32_t*, const int64_t*, int) const { return sm; }
+};
+
+// The select's LDS and the attention's LDS share the same bytes: the select is done
+// (and its list copied out of them) before the attention's first gather lands.
+template <typename T, int DKQ, int KPT>
+union FusedSmem {
+  WideSmem<kFusedThreads, KPT> sel;
+  FwdLdsSmem<T, DKQ, true> att;
+};
+
+template <typename T, int DKQ, int KPT>
+__global__ void __launch_bounds__(kFusedThreads, 1)
+select_fwd_kernel(const float* __restrict__ scores, int64_t scores_ld, const int32_t* __restrict__ seq_len,
+                  const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos, int c, int k_blk,
+                  int32_t* __restrict__ sel, int64_t sel_ld, int32_t* __restrict__ n_sel, const T* __restrict__ q,
+                  const T* __restrict__ k, int64_t k_ld, int64_t k_hs, const int64_t* __restrict__ seq_row0, int h_q,
+                  int h_kv, float scale_log2, int n_split, int rows_per_split, float* __restrict__ out,
+                  float* __restrict__ ws_o, float* __restrict__ ws_ml) {
+  constexpr int NT = kFusedThreads, COPIES = WideCfg<NT, KPT>::copies;
+  __shared__ FusedSmem<T, DKQ, KPT> sm;
+  __shared__ int32_t list[kFusedListMax];
+  const int i = blockIdx.y / h_kv, tid = threadIdx.x;
+  const bool writer = blockIdx.x == 0 && blockIdx.y % h_kv == 0;   // writes sel and n_sel of query i
+  const float* row = scores + (int64_t)i * scores_ld;
+  // The whole row, loaded up front (indices below scores_ld are valid memory).  All
+  // workgroups of a query read the same row at once; each starts at a different 2 KiB
+  // run of it, so that they do not queue on the same memory channels.
+  const int rot = (int)(2 * blockIdx.x + blockIdx.y) & (KPT - 1);
+  float raw[KPT];
+  {
+    const int last = (int)min(scores_ld, (int64_t)KPT * NT) - 1;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) raw[j] = row[min(wide_block<NT, KPT>(j, rot, tid), last)];
+  }
+  // the query's sequence (its cache rows too, for the attention) and visible blocks
+  const SeqMeta meta = seq_meta(q_seq, seq_len, seq_row0, nullptr, i);
+  const int n_vis = visible_tokens(meta.len, q_pos[i]);
+  const QueryRowInfo qr{n_vis / c, n_vis};
+  for (int e = tid; e < kP1Bins * COPIES / 4; e += NT) ((uint4*)sm.sel.h1)[e] = uint4{0u, 0u, 0u, 0u};
+  for (int e = tid; e < kWideBins; e += NT) sm.sel.h2[e] = 0u;
+  __builtin_amdgcn_sched_barrier(0);                 // every load in flight before the first is used
+  int32_t* gsel = sel + (int64_t)i * sel_ld;
+  int cnt;
+  if (qr.nb <= k_blk) {                              // dense: every visible position
+    cnt = qr.n_vis;
+    for (int j = tid; j < cnt; j += NT) list[j] = j;
+    if (writer) write_dense<NT>(gsel, sel_ld, qr.n_vis, n_sel + i);
+  } else {
+    __syncthreads();                                 // the histograms are clear
+    wide_select_rows<NT, KPT>(raw, rot, qr.nb, c, k_blk, sm.sel, list, nullptr);
+    const int body = k_blk * c, tail = qr.n_vis - qr.nb * c;
+    cnt = body + tail;
+    for (int j = tid; j < tail; j += NT) list[body + j] = qr.nb * c + j;
+    if (writer) {
+      for (int j = tid; j < body; j += NT) gsel[j] = list[j];
+      write_tail<NT>(gsel, sel_ld, qr.nb, qr.n_vis, c, k_blk, n_sel + i);
+    }
+  }
+  __syncthreads();                                   // the list is whole; the select's LDS is free
+  // Waves 4..7 are done (a barrier waits only for the waves still running).
+  if (__builtin_amdgcn_readfirstlane(tid / kWave) >= 4) return;
+  const LdsList ls{list, cnt, meta};
+  fwd_lds_body<T, DKQ, true>(sm.att, ls, q, k, k_ld, k_hs, seq_row0, seq_len, q_seq, q_pos, 0, h_q, h_kv,
+                             scale_log2, n_split, rows_per_split, out, ws_o, ws_ml);
+}
+
+// ---------------------------------------------------------------------------- host
+
+static bool alias_of(const CacheArgs& c) { return c.v == c.k && c.v_ld == c.k_ld && c.v_hs == c.k_hs; }
+
+bool select_fwd_fused(const sa_dims& d, const CacheArgs& c, const void* q, int n_q, const FwdPlan& plan) {
+  if (n_q < 1 || !fwd_uses_mfma(d, c, q) || !alias_of(c)) return false;
+  if (d.d_v != 512 || (d.d_kq != 576 && d.d_kq != 512)) return false;
+  if ((long long)d.top_k + d.compress_ratio - 1 > kFusedListMax) return false;
+  const long long max_blocks = (long long)c.max_len / d.compress_ratio;
+  if (max_blocks > (long long)kFusedThreads * kFusedMaxKpt) return false;
+  const int cus = device_cus();
+  return cus > 0 && (long long)plan.n_split * n_q * d.h_kv <= cus;   // one workgroup per compute unit
+}
+
+template <typename T, int DKQ, int KPT>
+static void launch_fused_t(const sa_dims& d, const CacheArgs& c, const float* scores, int64_t scores_ld,
+                           const int32_t* q_seq, const int32_t* q_pos, int n_q, int32_t* sel, int64_t sel_ld,
+                           int32_t* n_sel, const void* q, float scale_log2, float* out, float* ws_o, float* ws_ml,
+                           const FwdPlan& plan, hipStream_t stream) {
+  const dim3 grid(plan.n_split, n_q * d.h_kv);
+  hipLaunchKernelGGL((select_fwd_kernel<T, DKQ, KPT>), grid, dim3(kFusedThreads), 0, stream, scores, scores_ld,
+                     c.seq_len, q_seq, q_pos, d.compress_ratio, d.top_k / d.compress_ratio, sel, sel_ld, n_sel,
+                     (const T*)q, (const T*)c.k, c.k_ld, c.k_hs, c.seq_row0, d.h_q, d.h_kv, scale_log2, plan.n_split,
+                     plan.rows_per_split, out, ws_o, ws_ml);
+}
+
+template <typename T, int DKQ>
+static void dispatch_fused(const sa_dims& d, const CacheArgs& c, const float* scores, int64_t scores_ld,
+                           const int32_t* q_seq, const int32_t* q_pos, int n_q, int32_t* sel, int64_t sel_ld,
+                           int32_t* n_sel, const void* q, float scale_log2, float* out, float* ws_o, float* ws_ml,
+                           const FwdPlan& plan, hipStream_t stream) {
+  const long long max_blocks = (long long)c.max_len / d.compress_ratio;
+#define SA_FUSED(KPT_)                                                                                              \
+  launch_fused_t<T, DKQ, KPT_>(d, c, scores, scores_ld, q_seq, q_pos, n_q, sel, sel_ld, n_sel, q, scale_log2, out, \
+                               ws_o, ws_ml, plan, stream)
+  if (max_blocks <= (long long)kFusedThreads * 8) SA_FUSED(8);
+  else if (max_blocks <= (long long)kFusedThreads * 16) SA_FUSED(16);
+  else if (max_blocks <= (long long)kFusedThreads * 32) SA_FUSED(32);
+  else SA_FUSED(64);
+#undef SA_FUSED
+}
+
+hipError_t launch_select_fwd(const sa_dims& d, const CacheArgs& c, const float* scores, int64_t scores_ld,
+                             const int32_t* q_seq, const int32_t* q_pos, int n_q, int32_t* sel, int64_t sel_ld,
+                             int32_t* n_sel, const void* q, float scale, float* out, void* ws, void* scratch,
+                             const FwdPlan& plan, hipStream_t stream) {
+  if (n_q == 0) return hipSuccess;
+  if (!select_fwd_fused(d, c, q, n_q, plan)) {
+    hipError_t err = launch_select(d, c, scores, scores_ld, q_seq, q_pos, n_q, sel, sel_ld, n_sel, ws, stream);
+    if (err != hipSuccess) return err;
+    return launch_fwd(d, c, q, q_seq, sel, sel_ld, n_sel, nullptr, nullptr, 0, n_q, scale, out, scratch, plan,
+                      stream);
+  }
+  const float scale_log2 = scale * kLog2e;
+  float* ws_o = (float*)scratch;
+  float* ws_ml = plan.n_split > 1 ? ws_o + (size_t)n_q * d.h_q * plan.n_split * d.d_v : nullptr;
+  if (d.dtype == SA_BF16) {
+    if (d.d_kq == 576) dispatch_fused<bf16, 576>(d, c, scores, scores_ld, q_seq, q_pos, n_q, sel, sel_ld, n_sel, q, scale_log2, out, ws_o, ws_ml, plan, stream);
+    else dispatch_fused<bf16, 512>(d, c, scores, scores_ld, q_seq, q_pos, n_q, sel, sel_ld, n_sel, q, scale_log2, out, ws_o, ws_ml, plan, stream);
+  } else {
+    if (d.d_kq == 576) dispatch_fused<f16, 576>(d, c, scores, scores_ld, q_seq, q_pos, n_q, sel, sel_ld, n_sel, q, scale_log2, out, ws_o, ws_ml, plan, stream);
+    else dispatch_fused<f16, 512>(d, c, scores, scores_ld, q_seq, q_pos, n_q, sel, sel_ld, n_sel, q, scale_log2, out, ws_o, ws_ml, plan, stream);
+  }
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  return launch_combine(d, n_q, out, ws_o, ws_ml, plan, stream);
+}
+
+}  // namespace sa

@@ -85,6 +85,17 @@ class DeviceLayer:
         sa.sparse_attn_fwd(self.dims, self.cache, self.q, self.q_seq, sel, sel.shape[1], n_sel, self.n_q,
                            self.scale, self.out, self.ws, self.ws_bytes, stream)
 
+    def select_fwd(self, scores: Optional[torch.Tensor] = None, stream=None) -> None:
+        """select then fwd in one call (the selection inside the attention's launch
+        where it fits)."""
+        scores = self.scores if scores is None else scores
+        sa.sparse_attn_select_fwd(self.dims, self.cache, scores, scores.shape[1], self.q_seq, self.q_pos, self.q,
+                                  self.n_q, self.scale, self.sel, self.sel_ld, self.n_sel, self.out, self.ws,
+                                  self.ws_bytes, stream)
+
+    def select_fwd_is_fused(self) -> bool:
+        return sa.sparse_attn_select_fwd_is_fused(self.dims, self.cache, self.q, self.n_q)
+
     def fwd_window(self, window: int, sel: Optional[torch.Tensor] = None, n_sel: Optional[torch.Tensor] = None,
                    stream=None) -> None:
         sel = self.sel if sel is None else sel
@@ -123,11 +134,11 @@ class DeviceLayer:
                                 self.n_q, self.scale, self.out, self.ws, self.ws_bytes, stream)
 
     def step(self, stream=None) -> None:
-        """One pass of the whole path: pool what is new, score, select, attend."""
+        """One pass of the whole path: pool what is new, score, then select and attend
+        in one call (sparse_attn_select_fwd)."""
         self.pool(stream=stream)
         self.score(stream)
-        self.select(stream=stream)
-        self.fwd(stream=stream)
+        self.select_fwd(stream=stream)
 
     # ------------------------------------------------------------------ readback
     def selections(self) -> list[np.ndarray]:

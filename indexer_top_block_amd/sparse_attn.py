@@ -35,6 +35,8 @@ EXPORTS = (
     "sparse_attn_select",
     "sparse_attn_fwd",
     "sparse_attn_fwd_noalloc",
+    "sparse_attn_select_fwd",
+    "sparse_attn_select_fwd_is_fused",
     "sparse_attn_mask_to_indices",
     "sparse_attn_fwd_bias",
     "sparse_attn_workspace_bytes_window",
@@ -105,6 +107,10 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.sparse_attn_fwd.restype = ctypes.c_int
     lib.sparse_attn_fwd_noalloc.argtypes = [dp, cp, P, P, P, I64, P, I32, ctypes.c_float, P, P]
     lib.sparse_attn_fwd_noalloc.restype = ctypes.c_int
+    lib.sparse_attn_select_fwd.argtypes = [dp, cp, P, I64, P, P, P, I32, ctypes.c_float, P, I64, P, P, P, SZ, P]
+    lib.sparse_attn_select_fwd.restype = ctypes.c_int
+    lib.sparse_attn_select_fwd_is_fused.argtypes = [dp, cp, P, I32]
+    lib.sparse_attn_select_fwd_is_fused.restype = ctypes.c_int
     lib.sparse_attn_mask_to_indices.argtypes = [P, I32, I64, I32, I32, P, I64, P, P, P]
     lib.sparse_attn_mask_to_indices.restype = ctypes.c_int
     lib.sparse_attn_fwd_bias.argtypes = [dp, cp, P, P, P, I64, P, P, I32, ctypes.c_float, P, P, SZ, P]
@@ -233,6 +239,23 @@ def sparse_attn_fwd_noalloc(dims: SaDims, cache: Cache, q, q_seq, sel, sel_ld: i
            load().sparse_attn_fwd_noalloc(ctypes.byref(dims), ctypes.byref(cache.struct), _ptr(q), _ptr(q_seq),
                                           _ptr(sel), int(sel_ld), _ptr(n_sel), int(n_q), float(scale), _ptr(out),
                                           _stream(stream)))
+
+
+def sparse_attn_select_fwd(dims: SaDims, cache: Cache, scores, scores_ld: int, q_seq, q_pos, q, n_q: int,
+                           scale: float, sel, sel_ld: int, n_sel, out, ws=None, ws_bytes: int = 0,
+                           stream=None) -> None:
+    _check("sparse_attn_select_fwd",
+           load().sparse_attn_select_fwd(ctypes.byref(dims), ctypes.byref(cache.struct), _ptr(scores), int(scores_ld),
+                                         _ptr(q_seq), _ptr(q_pos), _ptr(q), int(n_q), float(scale), _ptr(sel),
+                                         int(sel_ld), _ptr(n_sel), _ptr(out), _ptr(ws), int(ws_bytes),
+                                         _stream(stream)))
+
+
+def sparse_attn_select_fwd_is_fused(dims: SaDims, cache: Cache, q, n_q: int) -> bool:
+    rc = load().sparse_attn_select_fwd_is_fused(ctypes.byref(dims), ctypes.byref(cache.struct), _ptr(q), int(n_q))
+    if rc < 0:
+        _check("sparse_attn_select_fwd_is_fused", rc)
+    return rc == 1
 
 
 def sparse_attn_mask_to_indices(mask, mask_dtype, mask_ld: int, n_q: int, n_kv: int, sel, sel_ld: int, n_sel,

@@ -274,3 +274,45 @@ def test_noalloc_fwd_rejects_bad_arguments_and_oversize():
     wc = ctypes.byref(_cache(k_ld=1024, v_ld=1024))
     assert _call(fn, ctypes.byref(wide), wc, FAKE, FAKE, FAKE, 2051, FAKE, 16, f, FAKE, None) == sa.SA_ERR_SCRATCH
     assert "static scratch" in sa.sparse_attn_strerror(sa.SA_ERR_SCRATCH)
+
+
+def test_select_fwd_rejects_bad_arguments():
+    # sparse_attn_select_fwd: the checks of sparse_attn_select and of sparse_attn_fwd,
+    # all before any HIP call
+    fn = "sparse_attn_select_fwd"
+    ws = sa.sparse_attn_workspace_bytes(_dims(), 1, 4096)
+    # dims, cache, scores, scores_ld, q_seq, q_pos, q, n_q, scale, sel, sel_ld, n_sel, out, ws, ws_bytes, stream
+    good = [ctypes.byref(_dims()), ctypes.byref(_cache()), FAKE, 1024, FAKE, FAKE, FAKE, 1, ctypes.c_float(0.04),
+            FAKE, 2051, FAKE, FAKE, FAKE, ws, None]
+
+    def call(**changes):
+        args = list(good)
+        for k, v in changes.items():
+            args[int(k[1:])] = v
+        return _call(fn, *args)
+
+    assert call(a0=None) == sa.SA_ERR_NULL
+    assert call(a0=ctypes.byref(_dims(top_k=2050))) == sa.SA_ERR_DIMS
+    assert call(a1=ctypes.byref(_cache(seq_len=None))) == sa.SA_ERR_NULL
+    assert call(a2=None) == sa.SA_ERR_NULL                            # scores
+    assert call(a3=1023) == sa.SA_ERR_ARG                             # scores_ld < max_len / c
+    assert call(a5=None) == sa.SA_ERR_NULL                            # q_pos
+    assert call(a6=None) == sa.SA_ERR_NULL                            # q
+    assert call(a7=-1) == sa.SA_ERR_ARG
+    assert call(a7=0) == sa.SA_OK                                     # nothing to do
+    assert call(a8=ctypes.c_float(float("nan"))) == sa.SA_ERR_ARG
+    assert call(a10=2050) == sa.SA_ERR_ARG                            # sel_ld < top_k + c - 1
+    assert call(a11=None) == sa.SA_ERR_NULL                           # n_sel
+    assert call(a12=None) == sa.SA_ERR_NULL                           # out
+    assert call(a13=None, a14=0) == sa.SA_ERR_WORKSPACE               # the split partials
+    assert call(a14=ws - 1) == sa.SA_ERR_WORKSPACE
+    # a 1M row needs the chunked selection's workspace
+    long_c = ctypes.byref(_cache(max_len=1048576))
+    need = sa.sparse_attn_workspace_bytes(_dims(), 1, 1048576)
+    assert call(a1=long_c, a3=262144, a14=ws) == sa.SA_ERR_WORKSPACE
+    assert call(a1=long_c, a3=262144, a14=need - 1) == sa.SA_ERR_WORKSPACE
+    # the form query
+    q = "sparse_attn_select_fwd_is_fused"
+    assert _call(q, ctypes.byref(_dims()), ctypes.byref(_cache()), FAKE, 0) == sa.SA_ERR_ARG
+    assert _call(q, ctypes.byref(_dims()), ctypes.byref(_cache()), None, 1) == sa.SA_ERR_NULL
+    assert _call(q, ctypes.byref(_dims(top_k=2050)), ctypes.byref(_cache()), FAKE, 1) == sa.SA_ERR_DIMS
