@@ -233,6 +233,9 @@ def quantize_q8_0(x) -> tuple[np.ndarray, np.ndarray]:
 
     ``x``: float values [..., n], n % 32 == 0.  Returns (codes int8 [..., n],
     scales float64 [..., n / 32] holding float16 values).
+
+    Pinned to that definition (a hand-worked block, invariants); agreement with ggml's
+    own quantizer is parity unpinned: the pages hold no q8_0 value to compare with.
     """
     x = np.asarray(x, dtype=np.float32)
     n = x.shape[-1]
