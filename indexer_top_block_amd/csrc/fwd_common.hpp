@@ -38,31 +38,19 @@ __device__ __forceinline__ f32x4 mfma16x16x32<f16>(const f16x8& a, const f16x8& 
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-// 16x16x16 product with four 16-bit A and B elements per lane.
-template <typename T> struct pv_mfma;
-template <> struct pv_mfma<bf16> {
-  static __device__ __forceinline__ f32x4 run_v(const i16x4& a, const bf16 (&b)[4], const f32x4& c) {
-    bf16x4 bv = {b[0], b[1], b[2], b[3]};
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, __builtin_bit_cast(i16x4, bv), c, 0, 0, 0);
-  }
-  static __device__ __forceinline__ f32x4 run(const bf16 (&a)[4], const bf16 (&b)[4], const f32x4& c) {
-    bf16x4 av = {a[0], a[1], a[2], a[3]};
-    bf16x4 bv = {b[0], b[1], b[2], b[3]};
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, av), __builtin_bit_cast(i16x4, bv),
-                                                     c, 0, 0, 0);
-  }
-};
-template <> struct pv_mfma<f16> {
-  static __device__ __forceinline__ f32x4 run_v(const i16x4& a, const f16 (&b)[4], const f32x4& c) {
-    f16x4 bv = {b[0], b[1], b[2], b[3]};
-    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a), bv, c, 0, 0, 0);
-  }
-  static __device__ __forceinline__ f32x4 run(const f16 (&a)[4], const f16 (&b)[4], const f32x4& c) {
-    f16x4 av = {a[0], a[1], a[2], a[3]};
-    f16x4 bv = {b[0], b[1], b[2], b[3]};
-    return __builtin_amdgcn_mfma_f32_16x16x16f16(av, bv, c, 0, 0, 0);
-  }
-};
+// P^T V^T as one 16x16x32 product (the full-rate bf16 / f16 shape) over two 16-row
+// chunks of a tile: A = two transposing reads of V (4 rows each; lane i of a 16-lane
+// group: dim i), B = the matching two 4-row pieces of P.  The rows a lane group
+// contributes as its 8 k-values need not be contiguous, only the same in A and B.
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+template <typename T>
+__device__ __forceinline__ f32x4 pv_mfma32(const i16x4& a_lo, const i16x4& a_hi, const T (&b_lo)[4],
+                                           const T (&b_hi)[4], const f32x4& c) {
+  typedef typename vec8<T>::type V8;
+  const i16x8 a = __builtin_shufflevector(a_lo, a_hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  const V8 b = {b_lo[0], b_lo[1], b_lo[2], b_lo[3], b_hi[0], b_hi[1], b_hi[2], b_hi[3]};
+  return mfma16x16x32<T>(__builtin_bit_cast(V8, a), b, c);
+}
 
 // ---------------------------------------------------------------------------- MFMA
 

@@ -244,15 +244,20 @@ __device__ __forceinline__ void fwd_lds_body(FwdLdsSmem<T, DKQ, QLDS>& lds, cons
     }
     // V^T operand by transposing LDS reads: in each 16-lane group, lane r reads 4
     // dims at row 4*grp + r/4, dims 4*(r%4) .. +4 of the 16-dim tile, and lane i then
-    // holds dim i of rows 4*grp .. 4*grp+3 -- the A-operand layout.
+    // holds dim i of rows 4*grp .. 4*grp+3 -- the A-operand layout.  Two such reads,
+    // rows 32*kk2 + 4*grp + [0, 4) and 16 rows further, make a lane group's 8 k-values
+    // of one 16x16x32 product, with P's pieces pb[2*kk2] and pb[2*kk2 + 1].
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const T* vrow = &kmain[(16 * kk + 4 * grp + (col >> 2)) * MP + dvb + 4 * (col & 3)];
+    for (int kk2 = 0; kk2 < 2; ++kk2) {
+      const T* vrow0 = &kmain[(32 * kk2 + 4 * grp + (col >> 2)) * MP + dvb + 4 * (col & 3)];
+      const T* vrow1 = vrow0 + 16 * MP;
 #pragma unroll
       for (int nt = 0; nt < NTW; ++nt) {
-        const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4*)(vrow + nt * 16));
-        o[nt] = pv_mfma<T>::run_v(a, pb[kk], o[nt]);
+        const i16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(vrow0 + nt * 16));
+        const i16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(vrow1 + nt * 16));
+        o[nt] = pv_mfma32<T>(a0, a1, pb[2 * kk2], pb[2 * kk2 + 1], o[nt]);
       }
     }
   };
