@@ -397,11 +397,7 @@ select_wide_kernel(const float* __restrict__ scores, int64_t scores_ld, const in
   // The whole row is loaded up front and kept in registers for every pass; the
   // query's length arrives with it (indices below scores_ld are valid memory).
   float raw[KPT];
-  {
-    const int last = (int)min(scores_ld, (int64_t)KPT * NT) - 1;
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) raw[j] = row[min(j * NT + tid, last)];
-  }
+  wide_load_row<NT, KPT>(row, scores_ld, raw);
   const QueryRowInfo qr = query_blocks(seq_len, q_seq, q_pos, q, c);
   for (int e = tid; e < kP1Bins * COPIES / 4; e += NT) ((uint4*)sm.h1)[e] = uint4{0u, 0u, 0u, 0u};
   for (int e = tid; e < kWideBins; e += NT) sm.h2[e] = 0u;
@@ -414,7 +410,7 @@ select_wide_kernel(const float* __restrict__ scores, int64_t scores_ld, const in
   __syncthreads();                                   // the histograms are clear (the loads may still fly)
   const int body = k_blk * c;
   int32_t* list = body <= kP1Bins * COPIES ? (int32_t*)sm.h1 : nullptr;   // pass 1's histogram is free by then
-  wide_select_rows<NT, KPT>(raw, 0, qr.nb, c, k_blk, sm, list, out);
+  wide_select_rows<NT, KPT>(raw, qr.nb, c, k_blk, sm, list, out);
   if (list)
     for (int i = tid; i < body; i += NT) out[i] = list[i];
   write_tail<NT>(out, sel_ld, qr.nb, qr.n_vis, c, k_blk, n_sel + q);

@@ -60,16 +60,9 @@ select_fwd_kernel(const float* __restrict__ scores, int64_t scores_ld, const int
   const int i = blockIdx.y / h_kv, tid = threadIdx.x;
   const bool writer = blockIdx.x == 0 && blockIdx.y % h_kv == 0;   // writes sel and n_sel of query i
   const float* row = scores + (int64_t)i * scores_ld;
-  // The whole row, loaded up front (indices below scores_ld are valid memory).  All
-  // workgroups of a query read the same row at once; each starts at a different 2 KiB
-  // run of it, so that they do not queue on the same memory channels.
-  const int rot = (int)(2 * blockIdx.x + blockIdx.y) & (KPT - 1);
+  // the whole row, loaded up front (indices below scores_ld are valid memory)
   float raw[KPT];
-  {
-    const int last = (int)min(scores_ld, (int64_t)KPT * NT) - 1;
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) raw[j] = row[min(wide_block<NT, KPT>(j, rot, tid), last)];
-  }
+  wide_load_row<NT, KPT>(row, scores_ld, raw);
   // the query's sequence (its cache rows too, for the attention) and visible blocks
   const SeqMeta meta = seq_meta(q_seq, seq_len, seq_row0, nullptr, i);
   const int n_vis = visible_tokens(meta.len, q_pos[i]);
@@ -85,7 +78,7 @@ select_fwd_kernel(const float* __restrict__ scores, int64_t scores_ld, const int
     if (writer) write_dense<NT>(gsel, sel_ld, qr.n_vis, n_sel + i);
   } else {
     __syncthreads();                                 // the histograms are clear
-    wide_select_rows<NT, KPT>(raw, rot, qr.nb, c, k_blk, sm.sel, list, nullptr);
+    wide_select_rows<NT, KPT>(raw, qr.nb, c, k_blk, sm.sel, list, nullptr);
     const int body = k_blk * c, tail = qr.n_vis - qr.nb * c;
     cnt = body + tail;
     for (int j = tid; j < tail; j += NT) list[body + j] = qr.nb * c + j;

@@ -191,23 +191,28 @@ __device__ __forceinline__ int popcount(uint64_t x) { return __popcll(x); }
 __device__ __forceinline__ int lowest_bit(uint32_t x) { return __ffs(x) - 1; }
 __device__ __forceinline__ int lowest_bit(uint64_t x) { return __ffsll((unsigned long long)x) - 1; }
 
-// Block held in register j of thread t: register j holds the 2 KiB run of the row
-// (j + rot) mod KPT, so that workgroups reading one row together can start at
-// different places of it.
+// The row's scores into registers, thread t register j holding block j*NT + t, all
+// loads issued before the first is used; each index is clamped to the row's last
+// readable entry rather than the load guarded (callers mask the entries past the
+// row's blocks themselves).  (Buffer loads with a scalar offset per register, which
+// spend no vector instruction on addresses, measured 0.3-0.4 us later to the first
+// pass at 32768 keys.)
 template <int NT, int KPT>
-__device__ __forceinline__ int wide_block(int j, int rot, int tid) {
-  return ((j + rot) & (KPT - 1)) * NT + tid;
+__device__ __forceinline__ void wide_load_row(const float* __restrict__ row, int64_t ld, float (&raw)[KPT]) {
+  const int tid = threadIdx.x;
+  const int last = (int)min(ld, (int64_t)KPT * NT) - 1;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) raw[j] = row[min(j * NT + tid, last)];
 }
 
 // The K_blk kept blocks of a row of nb > k_blk complete blocks whose scores the
-// threads hold in raw[] (thread t, register j: block wide_block(j, rot, t); entries
-// past nb are ignored), as k_blk*c ascending positions: into the LDS array `list`
-// when it is given, else straight to `out` (global).  The histograms h1 and h2 must
-// be zero on entry.  Ends with the list complete and visible to the whole workgroup.
+// threads hold in raw[] (thread t, register j: block j*NT + t; entries past nb are
+// ignored), as k_blk*c ascending positions: into the LDS array `list` when it is
+// given, else straight to `out` (global).  The histograms h1 and h2 must be zero on
+// entry.  Ends with the list complete and visible to the whole workgroup.
 template <int NT, int KPT>
-__device__ __forceinline__ void wide_select_rows(const float (&raw)[KPT], int rot, int nb_vis, int c, int k_blk,
+__device__ __forceinline__ void wide_select_rows(const float (&raw)[KPT], int nb_vis, int c, int k_blk,
                                                  WideSmem<NT, KPT>& sm, int32_t* list, int32_t* out) {
-  static_assert((KPT & (KPT - 1)) == 0, "KPT is a power of two");
   constexpr int COPIES = WideCfg<NT, KPT>::copies, WORDS = WideCfg<NT, KPT>::words;
   constexpr int WPL = WideCfg<NT, KPT>::wpl;
   constexpr int PER1 = kP1Bins / NT, PER2 = kWideBins / NT;
@@ -232,7 +237,7 @@ __device__ __forceinline__ void wide_select_rows(const float (&raw)[KPT], int ro
     } else {
 #pragma unroll
       for (int j = 0; j < KPT; ++j) {
-        key[j] = wide_block<NT, KPT>(j, rot, tid) < nb ? score_key(raw[j]) : 0u;
+        key[j] = j * NT + tid < nb ? score_key(raw[j]) : 0u;
         atomicAdd(&mine[(key[j] >> 22) * COPIES], 1u);
       }
     }
@@ -302,8 +307,8 @@ __device__ __forceinline__ void wide_select_rows(const float (&raw)[KPT], int ro
   // taken whole, i.e. key >= thr.  A search that did not end whole ran to the full
   // width (shift 0): keys above T are kept, keys equal to T are ties.  Padding keys
   // are 0: below every threshold of a prefix other than 0, which is never whole.
-  // Register j of the wave's lanes holds blocks r*NT + 64*wave + [0, 64), r = (j + rot)
-  // mod KPT: bitmap words r*NT/32 + 2 wave + {0, 1}, collected in lane j.
+  // Register j of the wave's lanes holds blocks j*NT + 64*wave + [0, 64): bitmap
+  // words j*NT/32 + 2 wave + {0, 1}, collected in lane j.
   {
     uint32_t k_lo = 0u, k_hi = 0u, t_lo = 0u, t_hi = 0u;
     if (whole || prefix != 0xffffffffu) {
@@ -312,9 +317,8 @@ __device__ __forceinline__ void wide_select_rows(const float (&raw)[KPT], int ro
     }
     if (!whole) ballot_rows<KPT>([&](int j) { return key[j] == prefix; }, t_lo, t_hi);
     if (lane < KPT) {
-      const int r = (lane + rot) & (KPT - 1);
-      *(uint2*)&sm.keep[r * (NT / 32) + wave * 2] = uint2{k_lo, k_hi};
-      *(uint2*)&sm.tie[r * (NT / 32) + wave * 2] = uint2{t_lo, t_hi};
+      *(uint2*)&sm.keep[lane * (NT / 32) + wave * 2] = uint2{k_lo, k_hi};
+      *(uint2*)&sm.tie[lane * (NT / 32) + wave * 2] = uint2{t_lo, t_hi};
     }
   }
   __syncthreads();
