@@ -67,7 +67,7 @@ struct GlobalList {
   }
 };
 
-template <typename T, int DKQ, bool QLDS, typename ListSrc>
+template <typename T, int DKQ, bool QLDS, typename ListSrc, bool QSTREAM = false>
 __device__ __forceinline__ void fwd_lds_body(FwdLdsSmem<T, DKQ, QLDS>& lds, const ListSrc& ls,
                                              const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld,
                                              int64_t k_hs, const int64_t* __restrict__ seq_row0,
@@ -76,6 +76,7 @@ __device__ __forceinline__ void fwd_lds_body(FwdLdsSmem<T, DKQ, QLDS>& lds, cons
                                              float scale_log2, int n_split, int rows_per_split,
                                              float* __restrict__ out, float* __restrict__ ws_o,
                                              float* __restrict__ ws_ml) {
+  static_assert(QLDS || !QSTREAM, "the query streams from LDS only when it is there");
   typedef FwdLdsSmem<T, DKQ, QLDS> S;
   typedef typename vec8<T>::type V8;
   typedef __attribute__((address_space(3))) void lds_void;
@@ -199,8 +200,15 @@ __device__ __forceinline__ void fwd_lds_body(FwdLdsSmem<T, DKQ, QLDS>& lds, cons
           const int c = (st_ - 16) * 4 + grp;           // chunk past 512 dims
           a = *reinterpret_cast<const V8*>(&krem[(r * REMP + (c ^ (r & 7))) * 8]);
         }
-        if (st_ & 1) s1 = mfma16x16x32<T>(a, qf[st_], s1);
-        else s0 = mfma16x16x32<T>(a, qf[st_], s0);
+        V8 qv;
+        if constexpr (QSTREAM) {                        // the query operand read per step
+          qv = reinterpret_cast<const V8*>(qs)[(col < G ? col : 0) * QP + grp + st_ * 4];
+          if (col >= G) qv = V8{};
+        } else {
+          qv = qf[st_];
+        }
+        if (st_ & 1) s1 = mfma16x16x32<T>(a, qv, s1);
+        else s0 = mfma16x16x32<T>(a, qv, s0);
       }
       const f32x4 sacc = s0 + s1;
       f32x4 x;
@@ -273,7 +281,7 @@ __device__ __forceinline__ void fwd_lds_body(FwdLdsSmem<T, DKQ, QLDS>& lds, cons
     for (int t = 0; t < n_tiles; ++t) {
       __builtin_amdgcn_s_waitcnt(0);                 // this wave's gathers of tile t
       __syncthreads();                               // everyone's
-      if constexpr (QLDS) {
+      if constexpr (QLDS && !QSTREAM) {
         if (t == 0) {                                // the query block landed with the first tile
           const V8* qrow = reinterpret_cast<const V8*>(qs) + (col < G ? col : 0) * QP + grp;
 #pragma unroll

@@ -21,8 +21,8 @@
 
 namespace sa {
 
-constexpr int kFusedThreads = 512;           // 8 waves select; waves 0..3 then attend
-constexpr int kFusedMaxKpt = 64;             // keys per thread: rows of up to 32768 blocks
+constexpr int kFusedThreads = 1024;          // 16 waves select; waves 0..3 then attend
+constexpr int kFusedMaxKpt = 32;             // keys per thread: rows of up to 32768 blocks
 constexpr int kFusedListMax = 3072;          // list entries held in LDS (top_k + c - 1)
 
 // The list the workgroup selected, in LDS: cnt entries (kept blocks, then the tail),
@@ -91,8 +91,8 @@ select_fwd_kernel(const float* __restrict__ scores, int64_t scores_ld, const int
   // Waves 4..7 are done (a barrier waits only for the waves still running).
   if (__builtin_amdgcn_readfirstlane(tid / kWave) >= 4) return;
   const LdsList ls{list, cnt, meta};
-  fwd_lds_body<T, DKQ, true>(sm.att, ls, q, k, k_ld, k_hs, seq_row0, seq_len, q_seq, q_pos, 0, h_q, h_kv,
-                             scale_log2, n_split, rows_per_split, out, ws_o, ws_ml);
+  fwd_lds_body<T, DKQ, true, LdsList, true>(sm.att, ls, q, k, k_ld, k_hs, seq_row0, seq_len, q_seq, q_pos, 0, h_q,
+                                            h_kv, scale_log2, n_split, rows_per_split, out, ws_o, ws_ml);
 }
 
 // ---------------------------------------------------------------------------- host
@@ -130,10 +130,10 @@ static void dispatch_fused(const sa_dims& d, const CacheArgs& c, const float* sc
 #define SA_FUSED(KPT_)                                                                                              \
   launch_fused_t<T, DKQ, KPT_>(d, c, scores, scores_ld, q_seq, q_pos, n_q, sel, sel_ld, n_sel, q, scale_log2, out, \
                                ws_o, ws_ml, plan, stream)
-  if (max_blocks <= (long long)kFusedThreads * 8) SA_FUSED(8);
+  if (max_blocks <= (long long)kFusedThreads * 4) SA_FUSED(4);
+  else if (max_blocks <= (long long)kFusedThreads * 8) SA_FUSED(8);
   else if (max_blocks <= (long long)kFusedThreads * 16) SA_FUSED(16);
-  else if (max_blocks <= (long long)kFusedThreads * 32) SA_FUSED(32);
-  else SA_FUSED(64);
+  else SA_FUSED(32);
 #undef SA_FUSED
 }
 
