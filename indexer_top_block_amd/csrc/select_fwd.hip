@@ -5,10 +5,12 @@
 // its work starts.  When every (query token, KV head, split) workgroup of the
 // attention has a compute unit to itself, the select can ride along: each
 // workgroup runs the one-workgroup radix select of its query's row (select_wide.hpp)
-// with 8 waves, keeps the list in LDS, and then attends over its own split's rows
+// with 16 waves, keeps the list in LDS, and then attends over its own split's rows
 // with 4 of them (fwd_lds.hpp) -- every workgroup of a query computes the same list.
 // That removes the select's launch and the list's trip through memory; the split
-// partials are merged by the usual combine launch.
+// partials are merged by the usual combine launch.  A 1024-thread workgroup leaves
+// 128 registers per lane, so the attention reads its query operand from LDS at every
+// Q.K^T step instead of holding it in registers.
 //
 // Workgroup (split 0, KV head 0) of each query also writes the list, the padding and
 // the count, so the call leaves exactly what sparse_attn_select followed by
@@ -88,7 +90,7 @@ select_fwd_kernel(const float* __restrict__ scores, int64_t scores_ld, const int
     }
   }
   __syncthreads();                                   // the list is whole; the select's LDS is free
-  // Waves 4..7 are done (a barrier waits only for the waves still running).
+  // Waves 4..15 are done (a barrier waits only for the waves still running).
   if (__builtin_amdgcn_readfirstlane(tid / kWave) >= 4) return;
   const LdsList ls{list, cnt, meta};
   fwd_lds_body<T, DKQ, true, LdsList, true>(sm.att, ls, q, k, k_ld, k_hs, seq_row0, seq_len, q_seq, q_pos, 0, h_q,
