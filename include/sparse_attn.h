@@ -111,9 +111,11 @@ int sparse_attn_check_dims(const sa_dims* dims);
 /* Bytes at the start of a workspace that hold state between calls. */
 #define SA_WS_STATE_BYTES ((size_t)1056768)
 
-/* Bytes of device workspace that sparse_attn_select and sparse_attn_fwd need for n_q
- * query tokens over caches whose sa_cache.max_len is max_len; one buffer of this
- * size serves both calls.  Returns 0 on bad arguments or when no workspace is needed.
+/* Bytes of device workspace that sparse_attn_select, sparse_attn_fwd and
+ * sparse_attn_select_fwd need for n_q query tokens over caches whose sa_cache.max_len
+ * is max_len; one buffer of this size serves every call (after the state, room for
+ * the chunked selection's candidates and the attention's split partials side by
+ * side).  Returns 0 on bad arguments or when no workspace is needed.
  * Host only, no HIP call.
  * Contract: zero-fill the buffer once before its first use (e.g. hipMemset when it is
  * allocated).  Its first SA_WS_STATE_BYTES bytes hold histograms
@@ -198,10 +200,12 @@ int sparse_attn_fwd(const sa_dims* dims, const sa_cache* cache, const void* q,
  * of the QSA commit, then the sparse flash attention of PR #27970 over the list it
  * writes), for the same n_q query tokens: writes sel, n_sel and out exactly as the two
  * calls would, bit for bit.  When every (token, KV head, split) workgroup of the
- * attention has a compute unit of its own -- few decode tokens, rows of at most 32768
- * blocks, the MLA shapes with V inside K (d_v 512, d_kq 512 or 576, f16 / bf16), lists
- * of at most 3072 entries -- the selection runs inside the attention's launch (each
- * workgroup selects its token's list into LDS), saving a launch and the list's round
+ * attention has a compute unit of its own -- few decode tokens, the MLA shapes with V
+ * inside K (d_v 512, d_kq 512 or 576, f16 / bf16), lists of at most 3072 entries --
+ * the selection runs inside the attention's launch (each workgroup selects its token's
+ * list into LDS): all of it for rows of at most 32768 blocks, the finishing pass of
+ * the chunked selection for longer rows of at most 256 chunks of 2048 blocks (its
+ * histogram and candidate launches run first), saving a launch and the list's round
  * trip through memory; otherwise the call makes the two calls.  Arguments are those of
  * the two calls (scores/scores_ld/q_pos as in sparse_attn_select; q/scale/out as in
  * sparse_attn_fwd); ws: sparse_attn_workspace_bytes(dims, n_q, cache->max_len) bytes,
@@ -212,10 +216,11 @@ int sparse_attn_select_fwd(const sa_dims* dims, const sa_cache* cache, const flo
                            int32_t n_q, float scale, int32_t* sel, int64_t sel_ld, int32_t* n_sel,
                            float* out, void* ws, size_t ws_bytes, void* stream);
 
-/* Which form sparse_attn_select_fwd takes for these arguments on the current device:
- * 1 = the selection inside the attention's launch, 0 = the two calls; a negative
- * SA_ERR_* on bad arguments (n_q < 1 is SA_ERR_ARG).  Host only: reads the device's
- * compute-unit count, launches nothing.                                              */
+/* Which form sparse_attn_select_fwd takes for these arguments on the current device,
+ * with a workspace of sparse_attn_workspace_bytes: 1 = the selection (or its finishing
+ * pass) inside the attention's launch, 0 = the two calls; a negative SA_ERR_* on bad
+ * arguments (n_q < 1 is SA_ERR_ARG).  Host only: reads the device's compute-unit
+ * count, launches nothing.                                                           */
 int sparse_attn_select_fwd_is_fused(const sa_dims* dims, const sa_cache* cache, const void* q, int32_t n_q);
 
 /* Bytes of the library's static scratch (per GPU), used by sparse_attn_fwd_noalloc:
@@ -231,8 +236,9 @@ int sparse_attn_select_fwd_is_fused(const sa_dims* dims, const sa_cache* cache, 
  * SA_STATIC_SCRATCH_BYTES that the library holds on each GPU it runs on until the
  * process ends; its device address is looked up on the first call on each device.
  * The call allocates nothing (no hipMalloc / hipFree, no allocating library call).
- * The scratch needed is sparse_attn_workspace_bytes(dims, n_q, max_len) minus
- * SA_WS_STATE_BYTES (0 when unsplit); a call needing more than SA_STATIC_SCRATCH_BYTES
+ * The scratch needed is that of the split partials (0 when unsplit; at most
+ * sparse_attn_workspace_bytes(dims, n_q, max_len) minus SA_WS_STATE_BYTES, which also
+ * counts the selection's scratch); a call needing more than SA_STATIC_SCRATCH_BYTES
  * returns SA_ERR_SCRATCH before any HIP call; that cannot happen for d_v <= 512 (e.g.
  * one decode token of 16 heads 576/512 with top_k 2048 needs 1.09 MB, 32 sequences
  * of 8 heads 512/512 8.4 MB), but can for wider V heads.  Every call on a GPU

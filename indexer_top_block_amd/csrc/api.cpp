@@ -230,7 +230,8 @@ int sparse_attn_select_fwd(const sa_dims* dims, const sa_cache* cache, const flo
                    &scratch);
   if (rc != SA_OK) return rc;
   return hip_status(sa::launch_select_fwd(*dims, to_args(cache), scores, scores_ld, q_seq, q_pos, n_q, sel, sel_ld,
-                                          n_sel, q, scale, out, ws, scratch, plan, (hipStream_t)stream));
+                                          n_sel, q, scale, out, ws, ws ? ws_bytes : 0, scratch, plan,
+                                          (hipStream_t)stream));
 }
 
 int sparse_attn_select_fwd_is_fused(const sa_dims* dims, const sa_cache* cache, const void* q, int32_t n_q) {
@@ -241,7 +242,8 @@ int sparse_attn_select_fwd_is_fused(const sa_dims* dims, const sa_cache* cache, 
   if (!cache->k || !cache->v || !q) return SA_ERR_NULL;
   const sa::CacheArgs a = to_args(cache);
   const sa::FwdPlan plan = sa::plan_fwd_window(*dims, n_q, 0, SIZE_MAX, sa::fwd_slots(*dims, a, q));
-  return sa::select_fwd_fused(*dims, a, q, n_q, plan) ? 1 : 0;
+  // with a workspace of sparse_attn_workspace_bytes
+  return sa::select_fwd_fused(*dims, a, q, n_q, plan, sa::workspace_bytes(*dims, n_q, cache->max_len)) ? 1 : 0;
 }
 
 int sparse_attn_fwd(const sa_dims* dims, const sa_cache* cache, const void* q, const int32_t* q_seq,

@@ -507,7 +507,7 @@ size_t workspace_bytes(const sa_dims& d, int n_q, int max_len) {
   const size_t f = plan_fwd(d, n_q).ws_bytes;
   const size_t s = select_scratch_bytes(d, n_q, max_len);
   if (f == 0 && s == 0) return 0;
-  return SA_WS_STATE_BYTES + (f > s ? f : s);
+  return SA_WS_STATE_BYTES + s + f;                  // both at once: the fused finish + attention reads one, writes the other
 }
 
 size_t workspace_bytes_window(const sa_dims& d, int n_q, int max_len, int window) {

@@ -56,6 +56,14 @@ size_t select_scratch_bytes(const sa_dims& d, int n_q, int max_len);
 hipError_t launch_select(const sa_dims& d, const CacheArgs& c, const float* scores, int64_t scores_ld,
                          const int32_t* q_seq, const int32_t* q_pos, int n_q, int32_t* sel, int64_t sel_ld,
                          int32_t* n_sel, void* ws, hipStream_t stream);
+// Whether the selection takes the chunked passes, and over how many chunks.
+bool select_chunked(const sa_dims& d, int n_q, int max_len);
+int select_chunk_count(const sa_dims& d, int max_len);
+// The chunked selection's first two launches (histogram, candidates); the finishing
+// pass is the caller's.  ws: the whole workspace.
+hipError_t launch_chunk_passes(const sa_dims& d, const CacheArgs& c, const float* scores, int64_t scores_ld,
+                               const int32_t* q_seq, const int32_t* q_pos, int n_q, int32_t* sel, int64_t sel_ld,
+                               int32_t* n_sel, void* ws, hipStream_t stream);
 
 // Split-KV partition of the attention for n_q query tokens: rows of each query's
 // list handled per split (a multiple of 32) and the number of splits.
@@ -103,20 +111,23 @@ hipError_t launch_fwd(const sa_dims& d, const CacheArgs& c, const void* q, const
                       const int32_t* q_pos, int window, int n_q, float scale, float* out, void* ws,
                       const FwdPlan& plan, hipStream_t stream);
 
-// sparse_attn_select then sparse_attn_fwd (plain form) for the same query tokens, in
-// one launch plus the combine when select_fwd_fused says so (select_fwd.hip).  ws: the
-// whole workspace (the select's); scratch: its partials part (null when unsplit).
-bool select_fwd_fused(const sa_dims& d, const CacheArgs& c, const void* q, int n_q, const FwdPlan& plan);
+// sparse_attn_select then sparse_attn_fwd (plain form) for the same query tokens, with
+// the selection (or its finishing pass) inside the attention's launch when
+// select_fwd_fused says so (select_fwd.hip).  ws / ws_bytes: the whole workspace (the
+// select's); scratch: its partials part for the two calls (null when unsplit).
+bool select_fwd_fused(const sa_dims& d, const CacheArgs& c, const void* q, int n_q, const FwdPlan& plan,
+                      size_t ws_bytes);
 hipError_t launch_select_fwd(const sa_dims& d, const CacheArgs& c, const float* scores, int64_t scores_ld,
                              const int32_t* q_seq, const int32_t* q_pos, int n_q, int32_t* sel, int64_t sel_ld,
-                             int32_t* n_sel, const void* q, float scale, float* out, void* ws, void* scratch,
-                             const FwdPlan& plan, hipStream_t stream);
+                             int32_t* n_sel, const void* q, float scale, float* out, void* ws, size_t ws_bytes,
+                             void* scratch, const FwdPlan& plan, hipStream_t stream);
 
 // Device address of this device's copy of the static scratch array
 // (SA_STATIC_SCRATCH_BYTES), looked up on first use per device (fwd_static.hip).
 hipError_t static_scratch(void** ptr);
 
-// Total workspace bytes for n_q query tokens (state + the larger scratch), 0 if none.
+// Total workspace bytes for n_q query tokens (state, then the chunked selection's
+// scratch and the attention's partials side by side), 0 if none.
 size_t workspace_bytes(const sa_dims& d, int n_q, int max_len);
 size_t workspace_bytes_window(const sa_dims& d, int n_q, int max_len, int window);
 

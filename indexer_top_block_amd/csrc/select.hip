@@ -39,161 +39,17 @@
 //           segment as (key << 32 | ~index): unique 64-bit values whose order is
 //           exactly (score desc, index asc), so ties need no special case;
 //   finish  one workgroup per query gathers the segments, radix-selects the cut
-//           among the values inside b (8-bit digits below the 12 shared bits,
+//           among the values inside b (11-bit digits below the 12 shared bits,
 //           stopping once the chosen bin holds one value), writes every value at or
 //           above the cut as positions in index order, then the tail, the padding
 //           and n_sel, and returns the histogram to zero for the next call.
 // If the values in b and above overflow what that workgroup holds (massive exact
 // ties), it runs the 4-pass algorithm above over the whole row instead.
-#include "sa_common.hpp"
-#include "sa_launch.hpp"
-#include "select_wide.hpp"
+#include "select_chunk.hpp"
 
 namespace sa {
 
-constexpr int kCopies = 32;
-constexpr int kBins = 256;
-constexpr int kCopyStride = kBins + 1;
-
-__device__ __forceinline__ uint32_t order_key(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u << 1) == 0u) u = 0u;                       // -0.0 -> +0.0
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-// Key of row[min(idx, last)]: the index is clamped rather than the load guarded, so
-// consecutive loads issue back to back instead of each waiting behind a branch.
-// Callers mask keys past the row's end themselves.
-__device__ __forceinline__ uint32_t key_clamped(const float* __restrict__ row, int idx, int last) {
-  return order_key(row[idx < last ? idx : last]);
-}
-
 // ------------------------------------------------------- per-query workgroup select
-
-struct WgSmem {
-  int hist[kCopies * kCopyStride];
-  int total[kBins];
-  int scan_scratch[1024 / kWave + 1];
-  int pick[2];
-};
-
-// One workgroup selects for one query whose scores are row[0 .. nb).  Requires nb > k_blk.
-template <int BLOCK, int KPT>
-__device__ void select_one_query(const float* __restrict__ row, int nb, int n_vis, int c, int k_blk,
-                                 int32_t* __restrict__ out, int64_t sel_ld, int32_t* n_sel_out, WgSmem& sm) {
-  constexpr int CH = BLOCK * KPT;                    // blocks per chunk
-  const int tid = threadIdx.x;
-  const int lane = tid % kWave;
-  const int n_chunks = (nb + CH - 1) / CH;
-  const bool resident = (n_chunks == 1);
-  uint32_t key[KPT];
-  auto load_chunk = [&](int ch) {
-    const int base = ch * CH + tid * KPT;
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) key[j] = key_clamped(row, base + j, nb - 1);
-  };
-  if (resident) load_chunk(0);
-
-  // ---- exact K_blk-th largest key by 4 radix passes -------------------------------
-  uint32_t prefix = 0;
-  int k_rem = k_blk;
-  int* my_hist = sm.hist + (lane & (kCopies - 1)) * kCopyStride;
-#pragma unroll 1
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    for (int e = tid; e < kCopies * kCopyStride; e += BLOCK) sm.hist[e] = 0;
-    __syncthreads();
-#pragma unroll 1
-    for (int ch = 0; ch < n_chunks; ++ch) {
-      if (!resident) load_chunk(ch);
-      const int base = ch * CH + tid * KPT;
-#pragma unroll
-      for (int j = 0; j < KPT; ++j) {
-        const uint32_t k = key[j];
-        const bool match = (base + j < nb) && (uint32_t)((uint64_t)k >> (shift + 8)) == prefix;
-        if (match) atomicAdd(&my_hist[(k >> shift) & 0xFFu], 1);
-      }
-    }
-    __syncthreads();
-    for (int v = tid; v < kBins; v += BLOCK) {
-      int sum = 0;
-#pragma unroll 8
-      for (int cp = 0; cp < kCopies; ++cp) sum += sm.hist[cp * kCopyStride + v];
-      sm.total[v] = sum;
-    }
-    __syncthreads();
-    // Suffix sums over the 256 bins, highest bin first: thread t < 256 takes bin
-    // 255 - t; a wave-level inclusive scan gives the keys in bins >= v within the
-    // wave's span and the per-wave totals are added after a barrier.  The thread
-    // whose bin holds the k_rem-th largest matching key publishes it.
-    int ge_in_wave = 0;
-    if (tid < kBins) {                               // whole waves 0..3
-      ge_in_wave = wave_inclusive_scan(sm.total[kBins - 1 - tid], lane);
-      if (lane == kWave - 1) sm.scan_scratch[tid / kWave] = ge_in_wave;
-    }
-    __syncthreads();
-    if (tid < kBins) {
-      const int v = kBins - 1 - tid;
-      int base = 0;
-      for (int w = 0; w < tid / kWave; ++w) base += sm.scan_scratch[w];
-      const int ge = base + ge_in_wave;              // matching keys in bins >= v
-      const int gt = ge - sm.total[v];               // matching keys in bins > v
-      if (gt < k_rem && ge >= k_rem) {
-        sm.pick[0] = v;
-        sm.pick[1] = k_rem - gt;
-      }
-    }
-    __syncthreads();
-    prefix = (prefix << 8) | (uint32_t)sm.pick[0];
-    k_rem = sm.pick[1];
-    __syncthreads();
-  }
-  const uint32_t T = prefix;                         // the K_blk-th largest key
-  const int r_eq = k_rem;                            // keys equal to T that are kept
-
-  // ---- compaction in block-index order --------------------------------------------
-  int eq_base = 0, out_base = 0;
-#pragma unroll 1
-  for (int ch = 0; ch < n_chunks; ++ch) {
-    if (!resident) load_chunk(ch);
-    const int base = ch * CH + tid * KPT;
-    int n_eq = 0;
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) n_eq += (base + j < nb && key[j] == T) ? 1 : 0;
-    int eq_tot;
-    const int eq_before = eq_base + block_exclusive_scan<BLOCK>(n_eq, sm.scan_scratch, &eq_tot);
-    int n_take = 0, e = eq_before;
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      const bool ok = base + j < nb;
-      const bool gt = ok && key[j] > T;
-      const bool eq = ok && key[j] == T;
-      const bool take = gt || (eq && e < r_eq);
-      e += eq ? 1 : 0;
-      n_take += take ? 1 : 0;
-    }
-    int take_tot;
-    int o = out_base + block_exclusive_scan<BLOCK>(n_take, sm.scan_scratch, &take_tot);
-    e = eq_before;
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      const bool ok = base + j < nb;
-      const bool gt = ok && key[j] > T;
-      const bool eq = ok && key[j] == T;
-      const bool take = gt || (eq && e < r_eq);
-      e += eq ? 1 : 0;
-      if (take && o < k_blk) {                       // o < k_blk always; the bound only guards memory
-        const int32_t p0 = (int32_t)(base + j) * c;
-        int32_t* dst = out + (int64_t)o * c;
-        for (int t = 0; t < c; ++t) dst[t] = p0 + t;
-        ++o;
-      }
-    }
-    eq_base += eq_tot;
-    out_base += take_tot;
-  }
-  write_tail<BLOCK>(out, sel_ld, nb, n_vis, c, k_blk, n_sel_out);
-}
 
 template <int BLOCK, int KPT>
 __global__ void __launch_bounds__(BLOCK)
@@ -209,36 +65,11 @@ select_kernel(const float* __restrict__ scores, int64_t scores_ld, const int32_t
     write_dense<BLOCK>(out, sel_ld, n_vis, n_sel + i);
     return;
   }
-  select_one_query<BLOCK, KPT>(scores + (int64_t)i * scores_ld, nb, n_vis, c, k_blk, out, sel_ld, n_sel + i, sm);
+  select_one_query<BLOCK, KPT>(scores + (int64_t)i * scores_ld, nb, c, k_blk, out, sm);
+  write_tail<BLOCK>(out, sel_ld, nb, n_vis, c, k_blk, n_sel + i);
 }
 
 // ------------------------------------------------------------------ chunked select
-
-constexpr int kChunk = 2048;                         // blocks per chunk workgroup
-constexpr int kHistThreads = 256;
-constexpr int kHistKpt = kChunk / kHistThreads;      // 8
-constexpr int kSelThreads = 1024;
-constexpr int kSelKpt = kChunk / kSelThreads;        // 2
-constexpr int kTopBits = 12;
-constexpr int kBins1 = 1 << kTopBits;                // 4096 bins of the top 12 bits
-constexpr int kHistCopies = 4;
-constexpr int kEntCap = 16384;                       // entries the finishing workgroup holds in LDS
-constexpr int kMaxChunks = 2048;                     // chunks per query it tallies
-
-// Scratch of one query: bin and remaining count from the histogram pass, the
-// number of entries each chunk kept, and each chunk's entries (index order).
-struct ChunkScratch {
-  char* base;
-  size_t q_stride;
-  int g;
-  static __device__ __host__ size_t head_bytes(int g) { return ((size_t)(16 + g) * 4 + 255) / 256 * 256; }
-  __device__ uint32_t* ctrl(int q) const { return (uint32_t*)(base + q * q_stride); }
-  __device__ uint32_t* n_ent(int q) const { return ctrl(q) + 16; }
-  __device__ uint64_t* ent(int q, int w) const {
-    return (uint64_t*)(base + q * q_stride + head_bytes(g)) + (size_t)w * kChunk;
-  }
-  static __host__ size_t query_bytes(int g) { return head_bytes(g) + (size_t)g * kChunk * 8; }
-};
 
 // Bin holding the k-th largest key of a histogram split as PER bins per thread
 // (thread t holds bins [t*PER, t*PER+PER)), and the number of keys in higher bins,
@@ -305,17 +136,6 @@ chunk_hist_kernel(const float* __restrict__ scores, int64_t scores_ld, const int
     if (n) atomicAdd(&g[b], n);
   }
 }
-
-constexpr int kFinBins = 2048;                      // 11-bit digits of the cut inside the bin
-struct SelSmem {
-  uint64_t ent[kEntCap];                             // 128 KiB
-  uint32_t h[2][kFinBins];                           // alternating digit histograms
-  uint32_t cpre[kMaxChunks + 1];                     // exclusive prefix of entries per chunk
-  int scan[kSelThreads / kWave + 1];
-  int wsum[2][kSelThreads / kWave];                  // per-wave totals of the picks
-  int pick[4];
-  uint64_t cut;
-};
 
 // Pass 2 (one workgroup per chunk): the chunk finds the bin holding the K_blk-th
 // largest key from the query's histogram and keeps, in index order, every block whose
@@ -426,141 +246,21 @@ chunk_finish_kernel(const float* __restrict__ scores, int64_t scores_ld, const i
                     int32_t* __restrict__ sel, int64_t sel_ld, int32_t* __restrict__ n_sel, WsState* __restrict__ st,
                     ChunkScratch sc) {
   __shared__ union {
-    SelSmem f;
+    FinSmem<kEntCap, kMaxChunks> f;
     WgSmem w;
   } sm;
-  const int q = blockIdx.x, tid = threadIdx.x;
-  const float* row = scores + (int64_t)q * scores_ld;
-  // Scratch of up to 256 chunks: every chunk's count and its first entries are read
-  // at once, before the query's length (and so its chunk count) is known -- one round
-  // trip instead of three.  Thread t serves chunk t / tpc, entries t % tpc + tpc*i.
-  constexpr int kSpecB = 4;
-  const bool spec = sc.g <= kSelThreads / 4;
-  int tpc = 1;                                       // a power of two, <= kChunk / kSpecB
-  while (tpc * 2 * sc.g <= kSelThreads && tpc * 2 * kSpecB <= kChunk) tpc *= 2;
-  const int cw = tid / tpc, cr = tid % tpc;
-  uint32_t ne_w = 0u;
-  uint64_t sv[kSpecB];
-  if (spec && cw < sc.g) {
-    ne_w = sc.n_ent(q)[cw];
-    const uint64_t* seg = sc.ent(q, cw);
-#pragma unroll
-    for (int i = 0; i < kSpecB; ++i) sv[i] = seg[cr + tpc * i];   // < kChunk: inside the segment
-  }
+  const int q = blockIdx.x;
+  ChunkSpec sp;
+  sp.issue(sc, q);
   const uint32_t bin = sc.ctrl(q)[0];
-  int k_rem = (int)sc.ctrl(q)[1];
+  const int k_rem = (int)sc.ctrl(q)[1];
   const QueryRowInfo qr = query_blocks(seq_len, q_seq, q_pos, q, c);
   if (qr.nb <= k_blk) return;                        // dense: written by the selection pass
-  int32_t* out = sel + (int64_t)q * sel_ld;
-  const int n_chunks = min((qr.nb + kChunk - 1) / kChunk, sc.g);   // (a length beyond max_len is clamped)
   uint32_t* ghist = st->ghist[q];
-  for (int b = tid; b < kBins1; b += kSelThreads) ghist[b] = 0u;   // every chunk has read it
-
-  // ---- gather, cut, write ----------------------------------------------------------
-  int n_ent;
-  if (spec) {
-    if (cw >= n_chunks) ne_w = 0u;
-    // exclusive prefix over the chunks: only each chunk's first thread contributes
-    const int cp = block_exclusive_scan<kSelThreads>(cr == 0 ? (int)ne_w : 0, sm.f.scan, &n_ent);
-    if (n_ent > kEntCap) {                           // massive exact ties: per-query select over the row
-      select_one_query<kSelThreads, 8>(row, qr.nb, qr.n_vis, c, k_blk, out, sel_ld, n_sel + q, sm.w);
-      return;
-    }
-    if (cr == 0 && cw < n_chunks) sm.f.cpre[cw] = (uint32_t)cp;
-    __syncthreads();
-    if (cw < n_chunks && ne_w > 0u) {
-      const int base_e = (int)sm.f.cpre[cw];
-#pragma unroll
-      for (int i = 0; i < kSpecB; ++i)
-        if (cr + tpc * i < (int)ne_w) sm.f.ent[base_e + cr + tpc * i] = sv[i];
-      const uint64_t* seg = sc.ent(q, cw);
-      for (int k = cr + tpc * kSpecB; k < (int)ne_w; k += tpc) sm.f.ent[base_e + k] = seg[k];
-    }
-  } else {
-    constexpr int PER = kMaxChunks / kSelThreads;    // 2 chunk counts per thread
-    const int gcap = n_chunks < kMaxChunks ? n_chunks : kMaxChunks;
-    uint32_t ne[PER];
-    int loc = 0;
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int w = tid * PER + j;
-      ne[j] = w < gcap ? sc.n_ent(q)[w] : 0u;
-      loc += (int)ne[j];
-    }
-    int cp = block_exclusive_scan<kSelThreads>(loc, sm.f.scan, &n_ent);
-    if (n_ent > kEntCap || n_chunks > kMaxChunks) {   // massive exact ties: per-query select over the row
-      select_one_query<kSelThreads, 8>(row, qr.nb, qr.n_vis, c, k_blk, out, sel_ld, n_sel + q, sm.w);
-      return;
-    }
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      sm.f.cpre[tid * PER + j] = (uint32_t)cp;
-      cp += (int)ne[j];
-    }
-    __syncthreads();
-    for (int e = tid; e < n_ent; e += kSelThreads) {
-      int lo = 0, hi = n_chunks - 1;                 // largest w with cpre[w] <= e
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if ((int)sm.f.cpre[mid] <= e) lo = mid;
-        else hi = mid - 1;
-      }
-      sm.f.ent[e] = sc.ent(q, lo)[e - (int)sm.f.cpre[lo]];
-    }
-  }
-  __syncthreads();
-  // k_rem-th largest value among the entries inside the bin (top 12 bits == bin):
-  // 11-bit digits below them, each bin found with the hierarchical pick; two
-  // histograms, each cleared while the other counts; stop once the chosen bin holds
-  // one value (values are unique).
-  for (int b = tid; b < kFinBins; b += kSelThreads) {
-    sm.f.h[0][b] = 0u;
-    sm.f.h[1][b] = 0u;
-  }
-  __syncthreads();
-  uint64_t prefix = bin;
-  for (int shift = 64 - kTopBits, pass = 0; shift > 0; ++pass) {
-    const int width = shift >= 11 ? 11 : shift;
-    shift -= width;
-    const uint32_t dmask = (1u << width) - 1u;
-    uint32_t* h = sm.f.h[pass & 1];
-    for (int e = tid; e < n_ent; e += kSelThreads) {
-      const uint64_t v = sm.f.ent[e];
-      if ((v >> (shift + width)) == prefix) atomicAdd(&h[(uint32_t)(v >> shift) & dmask], 1u);
-    }
-    if (pass > 0)                                    // the previous pass's (read before its pick), for the next
-      for (int b = tid; b < kFinBins; b += kSelThreads) sm.f.h[(pass + 1) & 1][b] = 0u;
-    __syncthreads();
-    uint32_t cnt2[2] = {h[2 * tid], h[2 * tid + 1]};
-    wide_pick<kSelThreads, 2>(cnt2, k_rem, 0, sm.f.wsum[pass & 1], sm.f.pick);
-    prefix = (prefix << width) | (uint64_t)sm.f.pick[0];
-    k_rem -= sm.f.pick[1];
-    if (sm.f.pick[2] == 1 || shift == 0) {           // the cut is the single value left in the bin
-      for (int e = tid; e < n_ent; e += kSelThreads) {
-        const uint64_t v = sm.f.ent[e];
-        if ((v >> shift) == prefix) sm.f.cut = v;
-      }
-      __syncthreads();
-      break;
-    }
-  }
-  const uint64_t cut = sm.f.cut;
-  // kept entries (value >= cut) in index order -> positions
-  const int per = (n_ent + kSelThreads - 1) / kSelThreads;
-  const int e0 = tid * per, e1 = min(n_ent, e0 + per);
-  int nk = 0;
-  for (int e = e0; e < e1; ++e) nk += sm.f.ent[e] >= cut ? 1 : 0;
-  int ktot;
-  int o = block_exclusive_scan<kSelThreads>(nk, sm.f.scan, &ktot);
-  for (int e = e0; e < e1; ++e) {
-    const uint64_t v = sm.f.ent[e];
-    if (v >= cut && o < k_blk) {                     // o < k_blk always; the bound only guards memory
-      const int32_t p0 = (int32_t)(0xFFFFFFFFu - (uint32_t)v) * c;
-      int32_t* dst = out + (int64_t)o * c;
-      for (int t = 0; t < c; ++t) dst[t] = p0 + t;
-      ++o;
-    }
-  }
+  for (int b = threadIdx.x; b < kBins1; b += kSelThreads) ghist[b] = 0u;   // every chunk has read it
+  int32_t* out = sel + (int64_t)q * sel_ld;
+  chunk_cut<kEntCap, kMaxChunks>(sp, sc, q, scores + (int64_t)q * scores_ld, qr, c, k_blk, bin, k_rem, sm.f, sm.w,
+                                 out);
   write_tail<kSelThreads>(out, sel_ld, qr.nb, qr.n_vis, c, k_blk, n_sel + q);
 }
 
@@ -568,19 +268,38 @@ chunk_finish_kernel(const float* __restrict__ scores, int64_t scores_ld, const i
 
 constexpr long long kWideMax = (long long)kWideThreads * kWideMaxKpt;   // blocks one wide workgroup holds
 
-static bool use_chunked(const sa_dims& d, int n_q, int max_len) {
+bool select_chunked(const sa_dims& d, int n_q, int max_len) {
   const long long max_blocks = (long long)max_len / d.compress_ratio;
   return n_q <= kStateQueries && max_blocks > kWideMax && max_blocks > d.top_k / d.compress_ratio;
 }
 
-static int chunks_for(const sa_dims& d, int max_len) {
+int select_chunk_count(const sa_dims& d, int max_len) {
   const long long max_blocks = (long long)max_len / d.compress_ratio;
   return (int)((max_blocks + kChunk - 1) / kChunk);
 }
 
 size_t select_scratch_bytes(const sa_dims& d, int n_q, int max_len) {
-  if (!use_chunked(d, n_q, max_len)) return 0;
-  return (size_t)n_q * ChunkScratch::query_bytes(chunks_for(d, max_len));
+  if (!select_chunked(d, n_q, max_len)) return 0;
+  return (size_t)n_q * ChunkScratch::query_bytes(select_chunk_count(d, max_len));
+}
+
+ChunkScratch chunk_scratch(const sa_dims& d, const CacheArgs& c, void* ws) {
+  const int g = select_chunk_count(d, c.max_len);
+  return ChunkScratch{(char*)ws + SA_WS_STATE_BYTES, ChunkScratch::query_bytes(g), g};
+}
+
+hipError_t launch_chunk_passes(const sa_dims& d, const CacheArgs& c, const float* scores, int64_t scores_ld,
+                               const int32_t* q_seq, const int32_t* q_pos, int n_q, int32_t* sel, int64_t sel_ld,
+                               int32_t* n_sel, void* ws, hipStream_t stream) {
+  const int cr = d.compress_ratio, k_blk = d.top_k / d.compress_ratio;
+  WsState* st = (WsState*)ws;
+  const ChunkScratch sc = chunk_scratch(d, c, ws);
+  const dim3 grid(sc.g, n_q);
+  hipLaunchKernelGGL(chunk_hist_kernel, grid, dim3(kHistThreads), 0, stream, scores, scores_ld, c.seq_len, q_seq,
+                     q_pos, cr, k_blk, st, sc);
+  hipLaunchKernelGGL(chunk_select_kernel, grid, dim3(kSelThreads), 0, stream, scores, scores_ld, c.seq_len, q_seq,
+                     q_pos, cr, k_blk, sel, sel_ld, n_sel, st, sc);
+  return hipGetLastError();
 }
 
 template <int BLOCK, int KPT>
@@ -597,17 +316,12 @@ hipError_t launch_select(const sa_dims& d, const CacheArgs& c, const float* scor
   if (n_q == 0) return hipSuccess;
   const int cr = d.compress_ratio, k_blk = d.top_k / d.compress_ratio;
   const long long max_blocks = (long long)c.max_len / cr;
-  if (use_chunked(d, n_q, c.max_len)) {
-    const int g = chunks_for(d, c.max_len);
-    WsState* st = (WsState*)ws;
-    ChunkScratch sc{(char*)ws + SA_WS_STATE_BYTES, ChunkScratch::query_bytes(g), g};
-    dim3 grid(g, n_q);
-    hipLaunchKernelGGL(chunk_hist_kernel, grid, dim3(kHistThreads), 0, stream, scores, scores_ld, c.seq_len, q_seq,
-                       q_pos, cr, k_blk, st, sc);
-    hipLaunchKernelGGL(chunk_select_kernel, grid, dim3(kSelThreads), 0, stream, scores, scores_ld, c.seq_len, q_seq,
-                       q_pos, cr, k_blk, sel, sel_ld, n_sel, st, sc);
+  if (select_chunked(d, n_q, c.max_len)) {
+    const hipError_t err = launch_chunk_passes(d, c, scores, scores_ld, q_seq, q_pos, n_q, sel, sel_ld, n_sel, ws,
+                                               stream);
+    if (err != hipSuccess) return err;
     hipLaunchKernelGGL(chunk_finish_kernel, dim3(n_q), dim3(kSelThreads), 0, stream, scores, scores_ld, c.seq_len,
-                       q_seq, q_pos, cr, k_blk, sel, sel_ld, n_sel, st, sc);
+                       q_seq, q_pos, cr, k_blk, sel, sel_ld, n_sel, (WsState*)ws, chunk_scratch(d, c, ws));
     return hipGetLastError();
   }
   if (max_blocks <= kWideMax) {                      // rows that fit one workgroup's registers

@@ -4,21 +4,31 @@
 // combine), each of which costs a launch and at least one memory round trip before
 // its work starts.  When every (query token, KV head, split) workgroup of the
 // attention has a compute unit to itself, the select can ride along: each
-// workgroup runs the one-workgroup radix select of its query's row (select_wide.hpp)
-// with 16 waves, keeps the list in LDS, and then attends over its own split's rows
-// with 4 of them (fwd_lds.hpp) -- every workgroup of a query computes the same list.
-// That removes the select's launch and the list's trip through memory; the split
-// partials are merged by the usual combine launch.  A 1024-thread workgroup leaves
-// 128 registers per lane, so the attention reads its query operand from LDS at every
-// Q.K^T step instead of holding it in registers.
+// workgroup runs its query's selection with 16 waves, keeps the list in LDS, and then
+// attends over its own split's rows with 4 of them (fwd_lds.hpp) -- every workgroup
+// of a query computes the same list.  That removes the select's launch (or, for rows
+// too long for one workgroup, the chunked selection's finishing launch) and the list's
+// trip through memory; the split partials are merged by the usual combine launch.  A
+// 1024-thread workgroup leaves 128 registers per lane, so the attention reads its
+// query operand from LDS at every Q.K^T step instead of holding it in registers.
+//
+// Two forms:
+//   rows of up to 32768 blocks: the one-workgroup radix select over the row in
+//     registers (select_wide.hpp);
+//   longer rows of few query tokens: the chunked selection's histogram and candidate
+//     launches run first, and the finishing pass (select_chunk.hpp) runs in every
+//     attention workgroup; the attention's partials go after the candidates in the
+//     workspace.
 //
 // Workgroup (split 0, KV head 0) of each query also writes the list, the padding and
-// the count, so the call leaves exactly what sparse_attn_select followed by
-// sparse_attn_fwd leaves, bit for bit (the same select, the same split plan, the same
-// attention arithmetic).  Calls that do not fit (more workgroups than compute units,
-// rows of more than 32768 blocks, shapes other than the MLA ones with V inside K,
-// lists longer than kFusedListMax) take those two calls instead.
+// the count (and returns the chunked selection's histogram to zero), so the call
+// leaves exactly what sparse_attn_select followed by sparse_attn_fwd leaves, bit for
+// bit (the same select, the same split plan, the same attention arithmetic).  Calls
+// that do not fit (more workgroups than compute units, shapes other than the MLA ones
+// with V inside K, lists longer than kFusedListMax, more chunks than the finishing
+// pass reads at once) take those two calls instead.
 #include "fwd_lds.hpp"
+#include "select_chunk.hpp"
 #include "select_wide.hpp"
 
 namespace sa {
@@ -26,6 +36,8 @@ namespace sa {
 constexpr int kFusedThreads = 1024;          // 16 waves select; waves 0..3 then attend
 constexpr int kFusedMaxKpt = 32;             // keys per thread: rows of up to 32768 blocks
 constexpr int kFusedListMax = 3072;          // list entries held in LDS (top_k + c - 1)
+constexpr int kFusedMaxChunks = kSelThreads / 4;   // chunks whose counts the finishing pass reads at once
+static_assert(kSelThreads == kFusedThreads, "the finishing pass runs on the fused workgroup");
 
 // The list the workgroup selected, in LDS: cnt entries (kept blocks, then the tail),
 // read clamped so that every lane reads valid memory.
@@ -97,18 +109,89 @@ select_fwd_kernel(const float* __restrict__ scores, int64_t scores_ld, const int
                                             h_kv, scale_log2, n_split, rows_per_split, out, ws_o, ws_ml);
 }
 
+template <typename T, int DKQ>
+union FinishFusedSmem {
+  FinSmem<kEntCap, kFusedMaxChunks> fin;
+  WgSmem one;                                        // the per-query select (massive exact ties)
+  FwdLdsSmem<T, DKQ, true> att;
+};
+
+// Rows longer than one workgroup holds: the chunked selection's histogram and
+// candidate launches have run; each attention workgroup runs the finishing pass into
+// LDS, then attends.
+template <typename T, int DKQ>
+__global__ void __launch_bounds__(kFusedThreads, 1)
+finish_fwd_kernel(const float* __restrict__ scores, int64_t scores_ld, const int32_t* __restrict__ seq_len,
+                  const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos, int c, int k_blk,
+                  int32_t* __restrict__ sel, int64_t sel_ld, int32_t* __restrict__ n_sel, WsState* __restrict__ st,
+                  ChunkScratch sc, const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, int64_t k_hs,
+                  const int64_t* __restrict__ seq_row0, int h_q, int h_kv, float scale_log2, int n_split,
+                  int rows_per_split, float* __restrict__ out, float* __restrict__ ws_o, float* __restrict__ ws_ml) {
+  constexpr int NT = kFusedThreads;
+  __shared__ FinishFusedSmem<T, DKQ> sm;
+  __shared__ int32_t list[kFusedListMax];
+  const int i = blockIdx.y / h_kv, tid = threadIdx.x;
+  const bool writer = blockIdx.x == 0 && blockIdx.y % h_kv == 0;   // writes sel and n_sel of query i
+  ChunkSpec sp;
+  sp.issue(sc, i);                                   // the candidates' first round trip, with the metadata's
+  const uint32_t bin = sc.ctrl(i)[0];
+  const int k_rem = (int)sc.ctrl(i)[1];
+  const SeqMeta meta = seq_meta(q_seq, seq_len, seq_row0, nullptr, i);
+  const int n_vis = visible_tokens(meta.len, q_pos[i]);
+  const QueryRowInfo qr{n_vis / c, n_vis};
+  int cnt;
+  if (qr.nb <= k_blk) {                              // dense: the candidate launch wrote sel and n_sel
+    cnt = qr.n_vis;
+    for (int j = tid; j < cnt; j += NT) list[j] = j;
+  } else {
+    if (writer)                                      // every chunk has read it
+      for (int b = tid; b < kBins1; b += NT) st->ghist[i][b] = 0u;
+    chunk_cut<kEntCap, kFusedMaxChunks>(sp, sc, i, scores + (int64_t)i * scores_ld, qr, c, k_blk, bin, k_rem, sm.fin,
+                                        sm.one, list);
+    const int body = k_blk * c, tail = qr.n_vis - qr.nb * c;
+    cnt = body + tail;
+    for (int j = tid; j < tail; j += NT) list[body + j] = qr.nb * c + j;
+    __syncthreads();                                 // the list is whole
+    if (writer) {
+      int32_t* gsel = sel + (int64_t)i * sel_ld;
+      for (int j = tid; j < body; j += NT) gsel[j] = list[j];
+      write_tail<NT>(gsel, sel_ld, qr.nb, qr.n_vis, c, k_blk, n_sel + i);
+    }
+  }
+  __syncthreads();                                   // the list is whole; the selection's LDS is free
+  if (__builtin_amdgcn_readfirstlane(tid / kWave) >= 4) return;   // waves 4..15 are done
+  const LdsList ls{list, cnt, meta};
+  fwd_lds_body<T, DKQ, true, LdsList, true>(sm.att, ls, q, k, k_ld, k_hs, seq_row0, seq_len, q_seq, q_pos, 0, h_q,
+                                            h_kv, scale_log2, n_split, rows_per_split, out, ws_o, ws_ml);
+}
+
 // ---------------------------------------------------------------------------- host
 
 static bool alias_of(const CacheArgs& c) { return c.v == c.k && c.v_ld == c.k_ld && c.v_hs == c.k_hs; }
 
-bool select_fwd_fused(const sa_dims& d, const CacheArgs& c, const void* q, int n_q, const FwdPlan& plan) {
-  if (n_q < 1 || !fwd_uses_mfma(d, c, q) || !alias_of(c)) return false;
-  if (d.d_v != 512 || (d.d_kq != 576 && d.d_kq != 512)) return false;
-  if ((long long)d.top_k + d.compress_ratio - 1 > kFusedListMax) return false;
-  const long long max_blocks = (long long)c.max_len / d.compress_ratio;
-  if (max_blocks > (long long)kFusedThreads * kFusedMaxKpt) return false;
+enum class FusedForm { kTwoCalls, kWide, kChunked };
+
+static FusedForm fused_form(const sa_dims& d, const CacheArgs& c, const void* q, int n_q, const FwdPlan& plan,
+                            size_t ws_bytes) {
+  if (n_q < 1 || !fwd_uses_mfma(d, c, q) || !alias_of(c)) return FusedForm::kTwoCalls;
+  if (d.d_v != 512 || (d.d_kq != 576 && d.d_kq != 512)) return FusedForm::kTwoCalls;
+  if ((long long)d.top_k + d.compress_ratio - 1 > kFusedListMax) return FusedForm::kTwoCalls;
   const int cus = device_cus();
-  return cus > 0 && (long long)plan.n_split * n_q * d.h_kv <= cus;   // one workgroup per compute unit
+  if (cus <= 0 || (long long)plan.n_split * n_q * d.h_kv > cus) return FusedForm::kTwoCalls;   // one per CU
+  const long long max_blocks = (long long)c.max_len / d.compress_ratio;
+  if (max_blocks <= (long long)kFusedThreads * kFusedMaxKpt) return FusedForm::kWide;
+  if (!select_chunked(d, n_q, c.max_len) || select_chunk_count(d, c.max_len) > kFusedMaxChunks)
+    return FusedForm::kTwoCalls;
+  // the partials go after the candidates, which the launch is still reading (the
+  // workspace the calls require has room for both)
+  if (SA_WS_STATE_BYTES + select_scratch_bytes(d, n_q, c.max_len) + plan.ws_bytes > ws_bytes)
+    return FusedForm::kTwoCalls;
+  return FusedForm::kChunked;
+}
+
+bool select_fwd_fused(const sa_dims& d, const CacheArgs& c, const void* q, int n_q, const FwdPlan& plan,
+                      size_t ws_bytes) {
+  return fused_form(d, c, q, n_q, plan, ws_bytes) != FusedForm::kTwoCalls;
 }
 
 template <typename T, int DKQ, int KPT>
@@ -139,12 +222,25 @@ static void dispatch_fused(const sa_dims& d, const CacheArgs& c, const float* sc
 #undef SA_FUSED
 }
 
+template <typename T, int DKQ>
+static void launch_finish_fwd_t(const sa_dims& d, const CacheArgs& c, const float* scores, int64_t scores_ld,
+                                const int32_t* q_seq, const int32_t* q_pos, int n_q, int32_t* sel, int64_t sel_ld,
+                                int32_t* n_sel, void* ws, const void* q, float scale_log2, float* out, float* ws_o,
+                                float* ws_ml, const FwdPlan& plan, hipStream_t stream) {
+  const dim3 grid(plan.n_split, n_q * d.h_kv);
+  hipLaunchKernelGGL((finish_fwd_kernel<T, DKQ>), grid, dim3(kFusedThreads), 0, stream, scores, scores_ld, c.seq_len,
+                     q_seq, q_pos, d.compress_ratio, d.top_k / d.compress_ratio, sel, sel_ld, n_sel, (WsState*)ws,
+                     chunk_scratch(d, c, ws), (const T*)q, (const T*)c.k, c.k_ld, c.k_hs, c.seq_row0, d.h_q, d.h_kv,
+                     scale_log2, plan.n_split, plan.rows_per_split, out, ws_o, ws_ml);
+}
+
 hipError_t launch_select_fwd(const sa_dims& d, const CacheArgs& c, const float* scores, int64_t scores_ld,
                              const int32_t* q_seq, const int32_t* q_pos, int n_q, int32_t* sel, int64_t sel_ld,
-                             int32_t* n_sel, const void* q, float scale, float* out, void* ws, void* scratch,
-                             const FwdPlan& plan, hipStream_t stream) {
+                             int32_t* n_sel, const void* q, float scale, float* out, void* ws, size_t ws_bytes,
+                             void* scratch, const FwdPlan& plan, hipStream_t stream) {
   if (n_q == 0) return hipSuccess;
-  if (!select_fwd_fused(d, c, q, n_q, plan)) {
+  const FusedForm form = fused_form(d, c, q, n_q, plan, ws_bytes);
+  if (form == FusedForm::kTwoCalls) {
     hipError_t err = launch_select(d, c, scores, scores_ld, q_seq, q_pos, n_q, sel, sel_ld, n_sel, ws, stream);
     if (err != hipSuccess) return err;
     return launch_fwd(d, c, q, q_seq, sel, sel_ld, n_sel, nullptr, nullptr, 0, n_q, scale, out, scratch, plan,
@@ -152,8 +248,25 @@ hipError_t launch_select_fwd(const sa_dims& d, const CacheArgs& c, const float* 
   }
   const float scale_log2 = scale * kLog2e;
   float* ws_o = (float*)scratch;
+  if (form == FusedForm::kChunked) {
+    hipError_t err = launch_chunk_passes(d, c, scores, scores_ld, q_seq, q_pos, n_q, sel, sel_ld, n_sel, ws, stream);
+    if (err != hipSuccess) return err;
+    ws_o = (float*)((char*)ws + SA_WS_STATE_BYTES + select_scratch_bytes(d, n_q, c.max_len));
+  }
   float* ws_ml = plan.n_split > 1 ? ws_o + (size_t)n_q * d.h_q * plan.n_split * d.d_v : nullptr;
-  if (d.dtype == SA_BF16) {
+  if (form == FusedForm::kChunked) {
+#define SA_FIN(T_, DKQ_)                                                                                      \
+  launch_finish_fwd_t<T_, DKQ_>(d, c, scores, scores_ld, q_seq, q_pos, n_q, sel, sel_ld, n_sel, ws, q, scale_log2, \
+                                out, ws_o, ws_ml, plan, stream)
+    if (d.dtype == SA_BF16) {
+      if (d.d_kq == 576) SA_FIN(bf16, 576);
+      else SA_FIN(bf16, 512);
+    } else {
+      if (d.d_kq == 576) SA_FIN(f16, 576);
+      else SA_FIN(f16, 512);
+    }
+#undef SA_FIN
+  } else if (d.dtype == SA_BF16) {
     if (d.d_kq == 576) dispatch_fused<bf16, 576>(d, c, scores, scores_ld, q_seq, q_pos, n_q, sel, sel_ld, n_sel, q, scale_log2, out, ws_o, ws_ml, plan, stream);
     else dispatch_fused<bf16, 512>(d, c, scores, scores_ld, q_seq, q_pos, n_q, sel, sel_ld, n_sel, q, scale_log2, out, ws_o, ws_ml, plan, stream);
   } else {

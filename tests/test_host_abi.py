@@ -80,8 +80,9 @@ def test_workspace_bytes():
     assert sa.sparse_attn_workspace_bytes(d, 2048, 34816) == 0
     # 128K rows: one workgroup holds a row of 32768 blocks, so selection adds nothing
     assert sa.sparse_attn_workspace_bytes(d, 1, 131072) == sa.WS_STATE_BYTES + partials_1
-    # 1M rows: 128 chunks of 2048 8-byte entries outgrow the partials
-    assert sa.sparse_attn_workspace_bytes(d, 1, 1048576) >= sa.WS_STATE_BYTES + 128 * 2048 * 8
+    # 1M rows: the chunked selection's 128 chunks of 2048 8-byte entries (after a
+    # 768-byte head of counts), then the partials, side by side
+    assert sa.sparse_attn_workspace_bytes(d, 1, 1048576) == sa.WS_STATE_BYTES + 768 + 128 * 2048 * 8 + partials_1
     assert sa.sparse_attn_workspace_bytes(_dims(top_k=2050), 1, 4096) == 0
     assert sa.sparse_attn_workspace_bytes(d, 1, -1) == 0
 
