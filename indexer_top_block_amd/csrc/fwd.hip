@@ -224,8 +224,7 @@ fwd_mfma_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, 
     for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
       for (int j = 0; j < 4; ++j) mx = fmaxf(mx, xs[kk][j]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = max_xor32(max_xor16(mx));
     const float m_new = fmaxf(m, mx);
     const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m - m_new);
     T pb[4][4];
@@ -238,8 +237,7 @@ fwd_mfma_kernel(const T* __restrict__ q, const T* __restrict__ k, int64_t k_ld, 
         psum += p;
         pb[kk][j] = (T)p;
       }
-    psum += __shfl_xor(psum, 16);
-    psum += __shfl_xor(psum, 32);
+    psum = sum_xor32(sum_xor16(psum));
     lsum = lsum * alpha + psum;
     m = m_new;
     // O^T[dv][head] = alpha * O^T + V^T[dv][row] P^T[row][head] for this wave's dims.

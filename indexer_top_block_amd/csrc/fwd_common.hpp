@@ -61,6 +61,27 @@ constexpr int kMfmaTile = 64;        // rows per workgroup tile: S for 16 per wa
 // clobber keeps the compiler from moving memory operations across it.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// A lane's value and that of the lane 16 (32) apart, by the permlane swaps: each lane
+// of a pair receives both values in lane order, so max and sum come out the same in
+// both lanes (and equal to those of a shuffle: the operations commute).  VALU
+// operations, where a shuffle is an LDS round trip on the softmax's critical path.
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Lane `src` (wave-uniform) of a 64-bit per-lane value.
 __device__ __forceinline__ int64_t readlane64(int64_t x, int src) {
   const int lo = __builtin_amdgcn_readlane((int)(uint32_t)x, src);

@@ -210,6 +210,18 @@ __device__ __forceinline__ void fwd_lds_body(FwdLdsSmem<T, DKQ, QLDS>& lds, cons
         if (st_ & 1) s1 = mfma16x16x32<T>(a, qv, s1);
         else s0 = mfma16x16x32<T>(a, qv, s0);
       }
+      if constexpr (!QSTREAM) {
+        // four A reads ahead of the products (the compiler's own order keeps one or
+        // two, and each product then waits on an LDS round trip)
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);           // 4 LDS reads
+#pragma unroll
+        for (int i = 0; i < KST - 4; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);         // 1 MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);         // 1 LDS read
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
       const f32x4 sacc = s0 + s1;
       f32x4 x;
 #pragma unroll
@@ -228,8 +240,7 @@ __device__ __forceinline__ void fwd_lds_body(FwdLdsSmem<T, DKQ, QLDS>& lds, cons
     for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
       for (int j = 0; j < 4; ++j) mx = fmaxf(mx, xs[kk][j]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = max_xor32(max_xor16(mx));
     const float m_new = fmaxf(m, mx);
     const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m - m_new);
     T pb[4][4];
@@ -242,8 +253,7 @@ __device__ __forceinline__ void fwd_lds_body(FwdLdsSmem<T, DKQ, QLDS>& lds, cons
         psum += p;
         pb[kk][j] = (T)p;
       }
-    psum += __shfl_xor(psum, 16);
-    psum += __shfl_xor(psum, 32);
+    psum = sum_xor32(sum_xor16(psum));
     lsum = lsum * alpha + psum;
     m = m_new;
     if (__ballot(alpha != 1.f) != 0ull) {            // the running max moved (else nothing to rescale)

@@ -239,8 +239,7 @@ fwd_q8_lds_kernel(const T* __restrict__ q, const int8_t* __restrict__ kq, int64_
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
       for (int j = 0; j < 8; ++j) mx = fmaxf(mx, xs[kk][j]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = max_xor32(max_xor16(mx));
     const float m_new = fmaxf(m, mx);
     const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m - m_new);
     float p[2][8];
@@ -252,8 +251,7 @@ fwd_q8_lds_kernel(const T* __restrict__ q, const int8_t* __restrict__ kq, int64_
         p[kk][j] = (xs[kk][j] == -INFINITY) ? 0.f : fast_exp2(xs[kk][j] - m_new);
         psum += p[kk][j];
       }
-    psum += __shfl_xor(psum, 16);
-    psum += __shfl_xor(psum, 32);
+    psum = sum_xor32(sum_xor16(psum));
     lsum = lsum * alpha + psum;
     m = m_new;
 #pragma unroll
