@@ -852,3 +852,34 @@ def test_pool_score_long_rows(gpu_lib):
     assert torch.equal(n0, n1) and torch.equal(kp0.view(torch.int16), kp1.view(torch.int16))
     assert torch.equal(s0.view(torch.int32), s1.view(torch.int32))
     say("[parity] pool+score fused on long rows: bit for bit")
+
+
+def test_combine_forms_agree(gpu_lib):
+    # 64 decode tokens of 8 query heads give plans of at most 8 splits, merged two
+    # outputs per thread; an output pointer off 8-byte alignment takes the one-output
+    # merge instead.  Both do the same arithmetic per output, so they agree bit for
+    # bit, and both match the oracle.
+    d = datagen.Dims(h_q=8, h_kv=1, d_kq=512, d_v=512, h_idx=32, d_idx=128, compress_ratio=4, top_k=1024,
+                     dtype="f16")
+    q_pos = [5999 - 61 * j for j in range(64)]
+    case = datagen.make_case("combine_forms", d, [6000], [0] * len(q_pos), q_pos, seed=0, case_id=250, std=1.0,
+                             v_separate=True)
+    layer = DeviceLayer(case)
+    layer.pool()
+    layer.score()
+    layer.select()
+    layer.fwd()
+    torch.cuda.synchronize()
+    aligned = layer.out.clone()
+    buf = torch.full((layer.out.numel() + 1,), float("nan"), dtype=torch.float32, device=layer.device)
+    shifted = buf[1:].view(layer.out.shape)
+    assert shifted.data_ptr() % 8 == 4
+    sa.sparse_attn_fwd(layer.dims, layer.cache, layer.q, layer.q_seq, layer.sel, layer.sel_ld, layer.n_sel, layer.n_q,
+                       layer.scale, shifted, layer.ws, layer.ws_bytes)
+    torch.cuda.synchronize()
+    assert torch.equal(aligned.view(torch.int32), shifted.contiguous().view(torch.int32)), "combine forms differ"
+    sel = layer.selections()
+    out = aligned.cpu().numpy()
+    for qi in (0, 31, 63):
+        check_attn(out[qi], case, qi, sel[qi], f"combine_forms q{qi}")
+    say(f"[parity] combine forms agree bit for bit; oracle bound-ratio={parity.take_worst_ratio():.3g}")
