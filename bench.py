@@ -148,9 +148,29 @@ class RotatingLayers:
     def select_fwd_is_fused(self) -> bool:
         return sa.sparse_attn_select_fwd_is_fused(self.dims, self.caches[0], self.q, self.n_q)
 
-    def step(self, r):
+    def pool_score_select_fwd(self, r):
+        """pool + score, then select + fwd, in one call (the selection from the scoring
+        launch's candidate list where it applies)."""
+        sa.sparse_attn_pool_score_select_fwd(self.dims, self.caches[r], self.n_pooled_prev, self.n_pooled_out, 1,
+                                             self.qidx, self.q_seq, self.q_pos, self.n_q, self.scores,
+                                             self.scores_ld, self.q, self.case.scale, self.sel, self.sel_ld,
+                                             self.n_sel, self.out, self.ws, self.ws_bytes)
+
+    def uses_list(self) -> bool:
+        return sa.sparse_attn_pool_score_select_fwd_uses_list(self.dims, self.caches[0], self.n_pooled_prev,
+                                                              self.n_pooled_out, self.qidx, self.q, self.n_q)
+
+    def list_decided(self) -> list:
+        """Per token, 1 where the last call's candidate list decided the selection."""
+        tail = self.ws[self.ws_bytes - 4 * self.n_q: self.ws_bytes].view(torch.int32)
+        return [int(x) for x in tail.cpu()]
+
+    def two_calls(self, r):
         self.pool_score(r)
         self.select_fwd(r)
+
+    def step(self, r):
+        self.pool_score_select_fwd(r)
 
 
 def algorithmic_bytes(case: datagen.Case, kv: str = "cache") -> dict:

@@ -114,8 +114,9 @@ int sparse_attn_check_dims(const sa_dims* dims);
 /* Bytes of device workspace that sparse_attn_select, sparse_attn_fwd and
  * sparse_attn_select_fwd need for n_q query tokens over caches whose sa_cache.max_len
  * is max_len; one buffer of this size serves every call (after the state, room for
- * the chunked selection's candidates and the attention's split partials side by
- * side).  Returns 0 on bad arguments or when no workspace is needed.
+ * the chunked selection's candidates, the attention's split partials and, for fewer
+ * than 64 tokens over rows of at most 32768 blocks, the candidate list of
+ * sparse_attn_pool_score_select_fwd, side by side).  Returns 0 on bad arguments or when no workspace is needed.
  * Host only, no HIP call.
  * Contract: zero-fill the buffer once before its first use (e.g. hipMemset when it is
  * allocated).  Its first SA_WS_STATE_BYTES bytes hold histograms
@@ -223,6 +224,36 @@ int sparse_attn_select_fwd(const sa_dims* dims, const sa_cache* cache, const flo
  * count, launches nothing.                                                           */
 int sparse_attn_select_fwd_is_fused(const sa_dims* dims, const sa_cache* cache, const void* q, int32_t n_q);
 
+/* The decode step's first links: sparse_attn_pool_score followed by
+ * sparse_attn_select_fwd (pages: the indexer's pooled keys and block scores, the
+ * top-k block selection, then the sparse attention over the list), with the
+ * arguments of the two calls (ws: sparse_attn_workspace_bytes(dims, n_q,
+ * cache->max_len) bytes) and their results bit for bit (kpool, n_pooled_out, scores,
+ * sel, n_sel, out).  Where the pooled scoring launch and the selection inside the
+ * attention's launch both apply to rows of at most 32768 blocks (see
+ * sparse_attn_pool_score_select_fwd_uses_list), the scoring launch also writes, for
+ * every 32 consecutive blocks of each token's row, the 8 best (ties to the lower
+ * block) into the workspace's last part, and each attention workgroup selects from
+ * that list (a quarter of the keys) instead of the row: the list's cut is the row's
+ * cut exactly when every block it leaves out scores below that cut, which each group's
+ * 8th best bounds; where it does not, the workgroup selects over the row as
+ * sparse_attn_select_fwd does.  The list part ends with one int32 per token: 1 when
+ * the list decided its selection, 0 when the row did (or the token was dense).
+ * Errors: those of sparse_attn_pool_score and sparse_attn_select_fwd; n_q == 0 makes
+ * the pooling alone.                                                                 */
+int sparse_attn_pool_score_select_fwd(const sa_dims* dims, const sa_cache* cache, const int32_t* n_pooled_in,
+                                      int32_t* n_pooled_out, int32_t max_new_blocks, const void* qidx,
+                                      const int32_t* q_seq, const int32_t* q_pos, int32_t n_q, float* scores,
+                                      int64_t scores_ld, const void* q, float scale, int32_t* sel, int64_t sel_ld,
+                                      int32_t* n_sel, float* out, void* ws, size_t ws_bytes, void* stream);
+
+/* 1 when sparse_attn_pool_score_select_fwd with these arguments and a workspace of
+ * sparse_attn_workspace_bytes writes the candidate list and selects from it, 0 when it
+ * makes the two calls unchanged; a negative SA_ERR_* on bad arguments.  Host only.   */
+int sparse_attn_pool_score_select_fwd_uses_list(const sa_dims* dims, const sa_cache* cache,
+                                                const int32_t* n_pooled_in, const int32_t* n_pooled_out,
+                                                const void* qidx, const void* q, int32_t n_q);
+
 /* Bytes of the library's static scratch (per GPU), used by sparse_attn_fwd_noalloc:
  * the split partials of 512 workgroups of 16 query heads with d_v = 512 (the most the
  * split plan makes), 512 * 16 * (512 + 2) * 4 bytes, so every call with
@@ -238,7 +269,7 @@ int sparse_attn_select_fwd_is_fused(const sa_dims* dims, const sa_cache* cache, 
  * The call allocates nothing (no hipMalloc / hipFree, no allocating library call).
  * The scratch needed is that of the split partials (0 when unsplit; at most
  * sparse_attn_workspace_bytes(dims, n_q, max_len) minus SA_WS_STATE_BYTES, which also
- * counts the selection's scratch); a call needing more than SA_STATIC_SCRATCH_BYTES
+ * counts the selection's scratch and the candidate list); a call needing more than SA_STATIC_SCRATCH_BYTES
  * returns SA_ERR_SCRATCH before any HIP call; that cannot happen for d_v <= 512 (e.g.
  * one decode token of 16 heads 576/512 with top_k 2048 needs 1.09 MB, 32 sequences
  * of 8 heads 512/512 8.4 MB), but can for wider V heads.  Every call on a GPU

@@ -234,6 +234,58 @@ int sparse_attn_select_fwd(const sa_dims* dims, const sa_cache* cache, const flo
                                           (hipStream_t)stream));
 }
 
+int sparse_attn_pool_score_select_fwd(const sa_dims* dims, const sa_cache* cache, const int32_t* n_pooled_in,
+                                      int32_t* n_pooled_out, int32_t max_new_blocks, const void* qidx,
+                                      const int32_t* q_seq, const int32_t* q_pos, int32_t n_q, float* scores,
+                                      int64_t scores_ld, const void* q, float scale, int32_t* sel, int64_t sel_ld,
+                                      int32_t* n_sel, float* out, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if ((rc = check_cache_common(dims, cache))) return rc;
+  if (n_q < 0 || n_q > kMaxGridY) return SA_ERR_ARG;
+  if (n_q == 0)                                      // nothing to score or select: the pooling alone
+    return sparse_attn_pool(dims, cache, n_pooled_in, n_pooled_out, max_new_blocks, stream);
+  // the pooling's and the scoring's checks
+  if (!cache->seq_blk0 || !cache->kidx || !cache->kpool || !n_pooled_in || !n_pooled_out) return SA_ERR_NULL;
+  if (max_new_blocks < 0 || cache->kidx_ld < dims->d_idx || cache->kpool_ld < dims->d_idx) return SA_ERR_ARG;
+  if (cache->n_seq > kMaxGridY) return SA_ERR_ARG;
+  if (!qidx || !q_seq || !q_pos || !scores) return SA_ERR_NULL;
+  if (scores_ld < (int64_t)(cache->max_len / dims->compress_ratio) || scores_ld < 0) return SA_ERR_ARG;
+  // the select's
+  if (!sel || !n_sel) return SA_ERR_NULL;
+  if (sel_ld < (int64_t)dims->top_k + dims->compress_ratio - 1) return SA_ERR_ARG;
+  if (sa::select_scratch_bytes(*dims, n_q, cache->max_len) > 0) {
+    const size_t need = sa::workspace_bytes(*dims, n_q, cache->max_len);
+    if (!ws || ws_bytes < need) return SA_ERR_WORKSPACE;
+  }
+  // the attention's
+  sa::FwdPlan plan{};
+  void* scratch = nullptr;
+  rc = fwd_prepare(dims, cache, q, q_seq, sel, sel_ld, n_sel, q_pos, 0, n_q, scale, out, ws, ws_bytes, false, &plan,
+                   &scratch);
+  if (rc != SA_OK) return rc;
+  return hip_status(sa::launch_pool_score_select_fwd(*dims, to_args(cache), n_pooled_in, n_pooled_out,
+                                                     max_new_blocks, qidx, q_seq, q_pos, n_q, scores, scores_ld, q,
+                                                     scale, sel, sel_ld, n_sel, out, ws, ws ? ws_bytes : 0, scratch,
+                                                     plan, (hipStream_t)stream));
+}
+
+int sparse_attn_pool_score_select_fwd_uses_list(const sa_dims* dims, const sa_cache* cache,
+                                                const int32_t* n_pooled_in, const int32_t* n_pooled_out,
+                                                const void* qidx, const void* q, int32_t n_q) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if ((rc = check_cache_common(dims, cache))) return rc;
+  if (n_q < 1 || (int64_t)n_q * dims->h_kv > kMaxGridY) return SA_ERR_ARG;
+  if (!cache->k || !cache->v || !q || !qidx || !n_pooled_in || !n_pooled_out) return SA_ERR_NULL;
+  const sa::CacheArgs a = to_args(cache);
+  const sa::FwdPlan plan = sa::plan_fwd_window(*dims, n_q, 0, SIZE_MAX, sa::fwd_slots(*dims, a, q));
+  return sa::step_uses_cand(*dims, a, qidx, q, n_q, n_pooled_in, n_pooled_out, plan,
+                            sa::workspace_bytes(*dims, n_q, cache->max_len))
+             ? 1
+             : 0;
+}
+
 int sparse_attn_select_fwd_is_fused(const sa_dims* dims, const sa_cache* cache, const void* q, int32_t n_q) {
   int rc = check_dims(dims);
   if (rc) return rc;

@@ -543,8 +543,12 @@ FwdPlan plan_fwd_window(const sa_dims& d, int n_q, int window, size_t ws_avail, 
 size_t workspace_bytes(const sa_dims& d, int n_q, int max_len) {
   const size_t f = plan_fwd(d, n_q).ws_bytes;
   const size_t s = select_scratch_bytes(d, n_q, max_len);
-  if (f == 0 && s == 0) return 0;
-  return SA_WS_STATE_BYTES + s + f;                  // both at once: the fused finish + attention reads one, writes the other
+  const size_t l = cand_bytes(d, n_q, max_len);
+  if (f == 0 && s == 0 && l == 0) return 0;
+  // side by side: a fused launch reads one while it writes another; the candidate
+  // list (read in 16-byte pieces) starts on a 256-byte boundary
+  if (l == 0) return SA_WS_STATE_BYTES + s + f;
+  return (SA_WS_STATE_BYTES + s + f + 255) / 256 * 256 + l;
 }
 
 size_t workspace_bytes_window(const sa_dims& d, int n_q, int max_len, int window) {

@@ -33,9 +33,12 @@ hipError_t launch_score(const sa_dims& d, const CacheArgs& c, const void* qidx, 
                         const int32_t* q_pos, int n_q, float* scores, int64_t scores_ld, hipStream_t stream);
 // sparse_attn_pool then sparse_attn_score, in one launch when the decode scoring
 // kernel applies (else the two launches).
+// cand (optional): the candidate list of the fused select (kCandKeep best blocks of
+// every kCandTile, select_wide.hpp), cand_ld words per query token; only the pooling
+// scoring launch writes it (pool_score_fused), else the call fails.
 hipError_t launch_pool_score(const sa_dims& d, const CacheArgs& c, const int32_t* n_in, int32_t* n_out, int max_new,
                              const void* qidx, const int32_t* q_seq, const int32_t* q_pos, int n_q, float* scores,
-                             int64_t scores_ld, hipStream_t stream);
+                             int64_t scores_ld, hipStream_t stream, uint32_t* cand = nullptr, int64_t cand_ld = 0);
 bool pool_score_fused(const sa_dims& d, const CacheArgs& c, const void* qidx, int n_q, const int32_t* n_in,
                       const int32_t* n_out);
 
@@ -117,17 +120,40 @@ hipError_t launch_fwd(const sa_dims& d, const CacheArgs& c, const void* q, const
 // select's); scratch: its partials part for the two calls (null when unsplit).
 bool select_fwd_fused(const sa_dims& d, const CacheArgs& c, const void* q, int n_q, const FwdPlan& plan,
                       size_t ws_bytes);
+// cand (optional): the scoring launch's candidate list (cand_ld words per query token,
+// then a word per query token that the launch sets to 1 when the list decided that
+// token's selection, else 0); only for the one-workgroup form, else the call fails.
 hipError_t launch_select_fwd(const sa_dims& d, const CacheArgs& c, const float* scores, int64_t scores_ld,
                              const int32_t* q_seq, const int32_t* q_pos, int n_q, int32_t* sel, int64_t sel_ld,
                              int32_t* n_sel, const void* q, float scale, float* out, void* ws, size_t ws_bytes,
-                             void* scratch, const FwdPlan& plan, hipStream_t stream);
+                             void* scratch, const FwdPlan& plan, hipStream_t stream, const uint32_t* cand = nullptr,
+                             int64_t cand_ld = 0);
+
+// The candidate list's words per query token (0: rows these shapes never select
+// from one; select_fwd.hip) and its bytes for n_q tokens with the decided flags (0
+// when the list is never used: rows of more than 32768 blocks, or more query tokens
+// than the pooling scoring launch takes); it is the workspace's last part.
+int64_t cand_words(const sa_dims& d, int max_len);
+size_t cand_bytes(const sa_dims& d, int n_q, int max_len);
+
+// sparse_attn_pool_score then sparse_attn_select_fwd; where the pooling scoring launch
+// and the one-workgroup fused select both apply and ws holds workspace_bytes, the
+// scoring launch also writes the candidate list and the select starts from it.
+hipError_t launch_pool_score_select_fwd(const sa_dims& d, const CacheArgs& c, const int32_t* n_in, int32_t* n_out,
+                                        int max_new, const void* qidx, const int32_t* q_seq, const int32_t* q_pos,
+                                        int n_q, float* scores, int64_t scores_ld, const void* q, float scale,
+                                        int32_t* sel, int64_t sel_ld, int32_t* n_sel, float* out, void* ws,
+                                        size_t ws_bytes, void* scratch, const FwdPlan& plan, hipStream_t stream);
+// Whether launch_pool_score_select_fwd starts the select from the candidate list.
+bool step_uses_cand(const sa_dims& d, const CacheArgs& c, const void* qidx, const void* q, int n_q,
+                    const int32_t* n_in, const int32_t* n_out, const FwdPlan& plan, size_t ws_bytes);
 
 // Device address of this device's copy of the static scratch array
 // (SA_STATIC_SCRATCH_BYTES), looked up on first use per device (fwd_static.hip).
 hipError_t static_scratch(void** ptr);
 
 // Total workspace bytes for n_q query tokens (state, then the chunked selection's
-// scratch and the attention's partials side by side), 0 if none.
+// scratch, the attention's partials and the candidate list side by side), 0 if none.
 size_t workspace_bytes(const sa_dims& d, int n_q, int max_len);
 size_t workspace_bytes_window(const sa_dims& d, int n_q, int max_len, int window);
 

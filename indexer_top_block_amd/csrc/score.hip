@@ -20,6 +20,7 @@
 // the heads.
 #include "sa_common.hpp"
 #include "sa_launch.hpp"
+#include "select_wide.hpp"
 
 namespace sa {
 
@@ -45,6 +46,7 @@ __device__ __forceinline__ float relu(float x) { return __int_as_float(max(__flo
 
 constexpr int kScoreWaves = 4;        // waves per workgroup
 constexpr int kScoreTile = 32;        // blocks per wave tile (MFMA N)
+static_assert(kScoreTile == kCandTile, "one candidate tile per wave");
 
 // grid = (ceil(max_blocks / (4 * 32)), n_q); wave w of workgroup x scores blocks
 // [(x*4 + w) * 32, +32) of query blockIdx.y (with pooling, the grid is one-dimensional
@@ -67,6 +69,11 @@ struct PoolArgs {
   int max_new;
   int pool_wgs, n_seq;                // pooling workgroups per sequence; sequences
   int gx;                             // scoring workgroups per query
+  // Optional (null: none): the candidate list of the selection (kCandKeep best blocks
+  // of each wave's kCandTile), `cand_ld` words per query token, tile w at kCandWords w.
+  // A wave past the row's blocks writes nothing.
+  uint32_t* cand;
+  int64_t cand_ld;
 };
 
 template <typename T, int MT, int D, bool POOL>
@@ -225,6 +232,28 @@ score_mfma_kernel(const T* __restrict__ qidx, const T* __restrict__ kpool, int64
   }
   sum += __shfl_xor(sum, 32);
   if (hf == 0 && valid) scores[(int64_t)i * scores_ld + b] = sum + 0.0f;  // +0.0 turns -0.0 into +0.0
+  if constexpr (POOL) {
+    if (pa.cand != nullptr && b_base / kCandTile < pa.cand_ld / kCandWords) {   // the tile's best blocks
+      // lanes 0..31 hold the tile's blocks (lanes 32..63 the same sums)
+      const uint64_t lo = 0xFFFFFFFFull;
+      const uint32_t key = valid ? score_key(sum + 0.0f) : 0u;   // the selection's key of the stored score
+      uint32_t v = 0u;                               // the tile's kCandKeep-th largest key, bit by bit
+      for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t tv = v | (1u << bit);
+        if (__popcll(__ballot(key >= tv) & lo) >= kCandKeep) v = tv;
+      }
+      const uint64_t below_me = (1ull << lane) - 1ull;
+      const int n_above = __popcll(__ballot(key > v) & lo);
+      const int eq_rank = __popcll(__ballot(key == v) & lo & below_me);
+      const bool take = hf == 0 && (key > v || (key == v && eq_rank < kCandKeep - n_above));
+      const int slot = __popcll(__ballot(take) & below_me);
+      uint32_t* cw = pa.cand + (int64_t)i * pa.cand_ld + (int64_t)(b_base / kCandTile) * kCandWords;
+      if (take) {                                    // exactly kCandKeep lanes (blocks past the row: key 0)
+        cw[slot] = key;
+        cw[kCandKeep + slot] = (uint32_t)b;
+      }
+    }
+  }
 }
 
 // ------------------------------------------------------------- MFMA, many queries
@@ -513,7 +542,8 @@ static void launch_mfma(const sa_dims& d, const CacheArgs& c, const void* qidx, 
 template <typename T, int MT, int D>
 static void launch_pool_score_t(const sa_dims& d, const CacheArgs& c, const int32_t* n_in, int32_t* n_out,
                                 int max_new, const void* qidx, const int32_t* q_seq, const int32_t* q_pos, int n_q,
-                                float* scores, int64_t scores_ld, hipStream_t stream) {
+                                float* scores, int64_t scores_ld, uint32_t* cand, int64_t cand_ld,
+                                hipStream_t stream) {
   const long long max_blocks = (long long)c.max_len / d.compress_ratio;
   const long long per_wg = kScoreWaves * kScoreTile;
   const long long gx = (max_blocks + per_wg - 1) / per_wg;
@@ -522,7 +552,7 @@ static void launch_pool_score_t(const sa_dims& d, const CacheArgs& c, const int3
   pool_wgs = pool_wgs < 1 ? 1 : (pool_wgs > 2048 ? 2048 : pool_wgs);
   const dim3 grid((unsigned)(pool_wgs * c.n_seq + gx * n_q));
   const PoolArgs<T> pa{(const T*)c.kidx, c.kidx_ld, (T*)c.kpool, c.seq_row0, n_in, n_out, max_new,
-                       (int)pool_wgs, c.n_seq, (int)gx};
+                       (int)pool_wgs, c.n_seq, (int)gx, cand, cand_ld};
   hipLaunchKernelGGL((score_mfma_kernel<T, MT, D, true>), grid, dim3(256), 0, stream, (const T*)qidx,
                      (const T*)c.kpool, c.kpool_ld, c.seq_blk0, c.seq_len, q_seq, q_pos, d.compress_ratio, scores,
                      scores_ld, pa);
@@ -572,11 +602,12 @@ bool pool_score_fused(const sa_dims& d, const CacheArgs& c, const void* qidx, in
 template <typename T>
 static void dispatch_pool_score(const sa_dims& d, const CacheArgs& c, const int32_t* n_in, int32_t* n_out,
                                 int max_new, const void* qidx, const int32_t* q_seq, const int32_t* q_pos, int n_q,
-                                float* scores, int64_t scores_ld, hipStream_t stream) {
+                                float* scores, int64_t scores_ld, uint32_t* cand, int64_t cand_ld,
+                                hipStream_t stream) {
 #define SA_PS_CASE(MT_, D_)                                                                                        \
   if (d.h_idx / 32 == MT_ && d.d_idx == D_) {                                                                      \
-    launch_pool_score_t<T, MT_, D_>(d, c, n_in, n_out, max_new, qidx, q_seq, q_pos, n_q, scores, scores_ld,       \
-                                    stream);                                                                       \
+    launch_pool_score_t<T, MT_, D_>(d, c, n_in, n_out, max_new, qidx, q_seq, q_pos, n_q, scores, scores_ld, cand, \
+                                    cand_ld, stream);                                                              \
     return;                                                                                                        \
   }
   SA_PS_CASE(1, 64) SA_PS_CASE(1, 128) SA_PS_CASE(1, 256)
@@ -588,14 +619,19 @@ static void dispatch_pool_score(const sa_dims& d, const CacheArgs& c, const int3
 
 hipError_t launch_pool_score(const sa_dims& d, const CacheArgs& c, const int32_t* n_in, int32_t* n_out, int max_new,
                              const void* qidx, const int32_t* q_seq, const int32_t* q_pos, int n_q, float* scores,
-                             int64_t scores_ld, hipStream_t stream) {
+                             int64_t scores_ld, hipStream_t stream, uint32_t* cand, int64_t cand_ld) {
   if (!pool_score_fused(d, c, qidx, n_q, n_in, n_out)) {
+    if (cand) return hipErrorInvalidValue;           // candidates come only from the pooling scoring launch
     hipError_t err = launch_pool(d, c, n_in, n_out, max_new, stream);
     if (err != hipSuccess) return err;
     return launch_score(d, c, qidx, q_seq, q_pos, n_q, scores, scores_ld, stream);
   }
-  if (d.dtype == SA_BF16) dispatch_pool_score<bf16>(d, c, n_in, n_out, max_new, qidx, q_seq, q_pos, n_q, scores, scores_ld, stream);
-  else dispatch_pool_score<f16>(d, c, n_in, n_out, max_new, qidx, q_seq, q_pos, n_q, scores, scores_ld, stream);
+  if (d.dtype == SA_BF16)
+    dispatch_pool_score<bf16>(d, c, n_in, n_out, max_new, qidx, q_seq, q_pos, n_q, scores, scores_ld, cand, cand_ld,
+                              stream);
+  else
+    dispatch_pool_score<f16>(d, c, n_in, n_out, max_new, qidx, q_seq, q_pos, n_q, scores, scores_ld, cand, cand_ld,
+                             stream);
   return hipGetLastError();
 }
 

@@ -37,6 +37,7 @@ constexpr int kFusedThreads = 1024;          // 16 waves select; waves 0..3 then
 constexpr int kFusedMaxKpt = 32;             // keys per thread: rows of up to 32768 blocks
 constexpr int kFusedListMax = 3072;          // list entries held in LDS (top_k + c - 1)
 constexpr int kFusedMaxChunks = kSelThreads / 4;   // chunks whose counts the finishing pass reads at once
+constexpr int kCandMaxQueries = 63;         // query tokens of the pooling scoring launch
 static_assert(kSelThreads == kFusedThreads, "the finishing pass runs on the fused workgroup");
 
 // The list the workgroup selected, in LDS: cnt entries (kept blocks, then the tail),
@@ -60,23 +61,90 @@ union FusedSmem {
   FwdLdsSmem<T, DKQ, true> att;
 };
 
-template <typename T, int DKQ, int KPT>
+// The select from the scoring launch's candidate list: thread t holds tile t's
+// kCandKeep keys and block indices (keys 0 past the row), counts them into the pass-1
+// histogram and runs the passes over them; the keep and tie words of tile t come from
+// its own candidates.  The result is the row's select exactly when every block left
+// out of the list falls below the cut: below the cut's bin when the bin is taken
+// whole, below the cut key T otherwise (a block equal to T, left out, could be a tie
+// the row's select takes).  Each tile's smallest listed key bounds those it left out,
+// so the workgroup checks that bound and returns false when it is not below the cut
+// (the caller then selects over the row).  Requires nb > k_blk and at least k_blk
+// listed blocks; the histograms are clear on entry and dirty on return.
+template <int NT, int KPT>
+__device__ __forceinline__ bool cand_select(const uint4 (&cv)[4], int nb, int c, int k_blk, WideSmem<NT, KPT>& sm,
+                                            int32_t* list) {
+  constexpr int COPIES = WideCfg<NT, KPT>::copies, WORDS = WideCfg<NT, KPT>::words;
+  static_assert(kCandKeep == 8 && WORDS <= NT, "one tile's list per thread");
+  const int tid = threadIdx.x, lane = tid % kWave;
+  nb = min(nb, KPT * NT);                            // the launch guarantees nb fits; the bitmap relies on it
+  const bool in_row = tid * kCandTile < nb;
+  const uint32_t key[kCandKeep] = {in_row ? cv[0].x : 0u, in_row ? cv[0].y : 0u, in_row ? cv[0].z : 0u,
+                                   in_row ? cv[0].w : 0u, in_row ? cv[1].x : 0u, in_row ? cv[1].y : 0u,
+                                   in_row ? cv[1].z : 0u, in_row ? cv[1].w : 0u};
+  const uint32_t idx[kCandKeep] = {cv[2].x, cv[2].y, cv[2].z, cv[2].w, cv[3].x, cv[3].y, cv[3].z, cv[3].w};
+  // blocks listed: kCandKeep per whole tile, all of a last tile shorter than that
+  const int n_listed = nb / kCandTile * kCandKeep + min(kCandKeep, nb % kCandTile);
+  {
+    uint32_t* mine = sm.h1 + (lane & (COPIES - 1));
+#pragma unroll
+    for (int j = 0; j < kCandKeep; ++j) atomicAdd(&mine[(key[j] >> 22) * COPIES], 1u);
+  }
+  const WideCut cut = wide_cut<NT, KPT, kCandKeep>(key, k_blk, NT * kCandKeep - n_listed, sm);
+  const uint32_t bound = cut.whole ? cut.prefix << cut.shift : cut.prefix;
+  uint32_t least = key[0];
+#pragma unroll
+  for (int j = 1; j < kCandKeep; ++j) least = min(least, key[j]);
+  if (__syncthreads_or(least >= bound)) return false;
+  // keep: key >= thr (thr > 0: bound > 0 here, since every key is >= 0); tie: key == T
+  const uint32_t thr = cut.whole ? bound : bound + 1u;
+  const bool full = !cut.whole && bound == 0xffffffffu;   // nothing above T
+  uint32_t kw = 0u, tw = 0u;
+#pragma unroll
+  for (int j = 0; j < kCandKeep; ++j) {
+    const uint32_t bit = 1u << (idx[j] % kCandTile);
+    if (!full && key[j] >= thr) kw |= bit;
+    if (!cut.whole && key[j] == bound) tw |= bit;
+  }
+  if (tid < WORDS) {
+    sm.keep[tid] = kw;
+    sm.tie[tid] = tw;
+  }
+  __syncthreads();
+  wide_list<NT, KPT>(sm, cut.whole, cut.k_rem, c, k_blk, list, nullptr);
+  return true;
+}
+
+// CAND: the select starts from the scoring launch's candidate list (cand, cand_ld
+// words per query token) and takes the row only when the list cannot decide it;
+// decided[i] records which (1: the list).  Otherwise cand and decided are unused.
+template <typename T, int DKQ, int KPT, bool CAND>
 __global__ void __launch_bounds__(kFusedThreads, 1)
 select_fwd_kernel(const float* __restrict__ scores, int64_t scores_ld, const int32_t* __restrict__ seq_len,
                   const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos, int c, int k_blk,
                   int32_t* __restrict__ sel, int64_t sel_ld, int32_t* __restrict__ n_sel, const T* __restrict__ q,
                   const T* __restrict__ k, int64_t k_ld, int64_t k_hs, const int64_t* __restrict__ seq_row0, int h_q,
                   int h_kv, float scale_log2, int n_split, int rows_per_split, float* __restrict__ out,
-                  float* __restrict__ ws_o, float* __restrict__ ws_ml) {
+                  float* __restrict__ ws_o, float* __restrict__ ws_ml, const uint32_t* __restrict__ cand,
+                  int64_t cand_ld, uint32_t* __restrict__ decided) {
   constexpr int NT = kFusedThreads, COPIES = WideCfg<NT, KPT>::copies;
   __shared__ FusedSmem<T, DKQ, KPT> sm;
   __shared__ int32_t list[kFusedListMax];
   const int i = blockIdx.y / h_kv, tid = threadIdx.x;
   const bool writer = blockIdx.x == 0 && blockIdx.y % h_kv == 0;   // writes sel and n_sel of query i
   const float* row = scores + (int64_t)i * scores_ld;
-  // the whole row, loaded up front (indices below scores_ld are valid memory)
+  // the whole row, loaded up front (indices below scores_ld are valid memory); with
+  // the candidate list, this thread's tile of it instead (clamped to the last tile)
   float raw[KPT];
-  wide_load_row<NT, KPT>(row, scores_ld, raw);
+  uint4 cv[4];
+  if constexpr (CAND) {
+    const int tile = min(tid, (int)(cand_ld / kCandWords) - 1);
+    const uint4* src = (const uint4*)(cand + (int64_t)i * cand_ld + (int64_t)tile * kCandWords);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) cv[j] = src[j];
+  } else {
+    wide_load_row<NT, KPT>(row, scores_ld, raw);
+  }
   // the query's sequence (its cache rows too, for the attention) and visible blocks
   const SeqMeta meta = seq_meta(q_seq, seq_len, seq_row0, nullptr, i);
   const int n_vis = visible_tokens(meta.len, q_pos[i]);
@@ -90,9 +158,23 @@ select_fwd_kernel(const float* __restrict__ scores, int64_t scores_ld, const int
     cnt = qr.n_vis;
     for (int j = tid; j < cnt; j += NT) list[j] = j;
     if (writer) write_dense<NT>(gsel, sel_ld, qr.n_vis, n_sel + i);
+    if (CAND && writer && tid == 0) decided[i] = 0u;
   } else {
     __syncthreads();                                 // the histograms are clear
-    wide_select_rows<NT, KPT>(raw, qr.nb, c, k_blk, sm.sel, list, nullptr);
+    bool done = false;
+    if constexpr (CAND) {
+      // the list must hold well over k_blk blocks for its cut to be likely exact
+      if (qr.nb / kCandTile * kCandKeep >= 2 * k_blk) done = cand_select<NT, KPT>(cv, qr.nb, c, k_blk, sm.sel, list);
+      if (!done) {                                   // the row's select: fresh histograms, the row's keys
+        __syncthreads();
+        for (int e = tid; e < kP1Bins * COPIES / 4; e += NT) ((uint4*)sm.sel.h1)[e] = uint4{0u, 0u, 0u, 0u};
+        for (int e = tid; e < kWideBins; e += NT) sm.sel.h2[e] = 0u;
+        wide_load_row<NT, KPT>(row, scores_ld, raw);
+        __syncthreads();
+      }
+    }
+    if (!done) wide_select_rows<NT, KPT>(raw, qr.nb, c, k_blk, sm.sel, list, nullptr);
+    if (CAND && writer && tid == 0) decided[i] = done ? 1u : 0u;
     const int body = k_blk * c, tail = qr.n_vis - qr.nb * c;
     cnt = body + tail;
     for (int j = tid; j < tail; j += NT) list[body + j] = qr.nb * c + j;
@@ -194,31 +276,54 @@ bool select_fwd_fused(const sa_dims& d, const CacheArgs& c, const void* q, int n
   return fused_form(d, c, q, n_q, plan, ws_bytes) != FusedForm::kTwoCalls;
 }
 
-template <typename T, int DKQ, int KPT>
+int64_t cand_words(const sa_dims& d, int max_len) {
+  const long long max_blocks = (long long)max_len / d.compress_ratio;
+  if (max_blocks <= d.top_k / d.compress_ratio || max_blocks > (long long)kFusedThreads * kFusedMaxKpt) return 0;
+  return (max_blocks + kCandTile - 1) / kCandTile * kCandWords;
+}
+
+// The tiles of n_q tokens, then one decided flag per token; cand_words is a multiple
+// of kCandWords, so n_q * cand_words + n_q words end on the part's last word.
+size_t cand_bytes(const sa_dims& d, int n_q, int max_len) {
+  if (n_q < 1 || n_q > kCandMaxQueries) return 0;
+  const size_t words = (size_t)n_q * cand_words(d, max_len);
+  return words == 0 ? 0 : (words + n_q) * 4;
+}
+
+template <typename T, int DKQ, int KPT, bool CAND>
 static void launch_fused_t(const sa_dims& d, const CacheArgs& c, const float* scores, int64_t scores_ld,
                            const int32_t* q_seq, const int32_t* q_pos, int n_q, int32_t* sel, int64_t sel_ld,
                            int32_t* n_sel, const void* q, float scale_log2, float* out, float* ws_o, float* ws_ml,
-                           const FwdPlan& plan, hipStream_t stream) {
+                           const uint32_t* cand, int64_t cand_ld, const FwdPlan& plan, hipStream_t stream) {
   const dim3 grid(plan.n_split, n_q * d.h_kv);
-  hipLaunchKernelGGL((select_fwd_kernel<T, DKQ, KPT>), grid, dim3(kFusedThreads), 0, stream, scores, scores_ld,
-                     c.seq_len, q_seq, q_pos, d.compress_ratio, d.top_k / d.compress_ratio, sel, sel_ld, n_sel,
-                     (const T*)q, (const T*)c.k, c.k_ld, c.k_hs, c.seq_row0, d.h_q, d.h_kv, scale_log2, plan.n_split,
-                     plan.rows_per_split, out, ws_o, ws_ml);
+  // the decided flags: the n_q words that end the workspace's candidate part
+  uint32_t* decided = cand ? (uint32_t*)(cand + (int64_t)n_q * cand_ld) : nullptr;
+  hipLaunchKernelGGL((select_fwd_kernel<T, DKQ, KPT, CAND>), grid, dim3(kFusedThreads), 0, stream, scores,
+                     scores_ld, c.seq_len, q_seq, q_pos, d.compress_ratio, d.top_k / d.compress_ratio, sel, sel_ld,
+                     n_sel, (const T*)q, (const T*)c.k, c.k_ld, c.k_hs, c.seq_row0, d.h_q, d.h_kv, scale_log2,
+                     plan.n_split, plan.rows_per_split, out, ws_o, ws_ml, cand, cand_ld, decided);
 }
 
 template <typename T, int DKQ>
 static void dispatch_fused(const sa_dims& d, const CacheArgs& c, const float* scores, int64_t scores_ld,
                            const int32_t* q_seq, const int32_t* q_pos, int n_q, int32_t* sel, int64_t sel_ld,
                            int32_t* n_sel, const void* q, float scale_log2, float* out, float* ws_o, float* ws_ml,
-                           const FwdPlan& plan, hipStream_t stream) {
+                           const uint32_t* cand, int64_t cand_ld, const FwdPlan& plan, hipStream_t stream) {
   const long long max_blocks = (long long)c.max_len / d.compress_ratio;
-#define SA_FUSED(KPT_)                                                                                              \
-  launch_fused_t<T, DKQ, KPT_>(d, c, scores, scores_ld, q_seq, q_pos, n_q, sel, sel_ld, n_sel, q, scale_log2, out, \
-                               ws_o, ws_ml, plan, stream)
-  if (max_blocks <= (long long)kFusedThreads * 4) SA_FUSED(4);
-  else if (max_blocks <= (long long)kFusedThreads * 8) SA_FUSED(8);
-  else if (max_blocks <= (long long)kFusedThreads * 16) SA_FUSED(16);
-  else SA_FUSED(32);
+#define SA_FUSED(KPT_, CAND_)                                                                                   \
+  launch_fused_t<T, DKQ, KPT_, CAND_>(d, c, scores, scores_ld, q_seq, q_pos, n_q, sel, sel_ld, n_sel, q,        \
+                                      scale_log2, out, ws_o, ws_ml, cand, cand_ld, plan, stream)
+  if (cand) {
+    if (max_blocks <= (long long)kFusedThreads * 4) SA_FUSED(4, true);
+    else if (max_blocks <= (long long)kFusedThreads * 8) SA_FUSED(8, true);
+    else if (max_blocks <= (long long)kFusedThreads * 16) SA_FUSED(16, true);
+    else SA_FUSED(32, true);
+  } else {
+    if (max_blocks <= (long long)kFusedThreads * 4) SA_FUSED(4, false);
+    else if (max_blocks <= (long long)kFusedThreads * 8) SA_FUSED(8, false);
+    else if (max_blocks <= (long long)kFusedThreads * 16) SA_FUSED(16, false);
+    else SA_FUSED(32, false);
+  }
 #undef SA_FUSED
 }
 
@@ -237,9 +342,12 @@ static void launch_finish_fwd_t(const sa_dims& d, const CacheArgs& c, const floa
 hipError_t launch_select_fwd(const sa_dims& d, const CacheArgs& c, const float* scores, int64_t scores_ld,
                              const int32_t* q_seq, const int32_t* q_pos, int n_q, int32_t* sel, int64_t sel_ld,
                              int32_t* n_sel, const void* q, float scale, float* out, void* ws, size_t ws_bytes,
-                             void* scratch, const FwdPlan& plan, hipStream_t stream) {
+                             void* scratch, const FwdPlan& plan, hipStream_t stream, const uint32_t* cand,
+                             int64_t cand_ld) {
   if (n_q == 0) return hipSuccess;
   const FusedForm form = fused_form(d, c, q, n_q, plan, ws_bytes);
+  if (cand && (form != FusedForm::kWide || cand_ld < cand_words(d, c.max_len)))
+    return hipErrorInvalidValue;                     // the candidate list serves the one-workgroup select only
   if (form == FusedForm::kTwoCalls) {
     hipError_t err = launch_select(d, c, scores, scores_ld, q_seq, q_pos, n_q, sel, sel_ld, n_sel, ws, stream);
     if (err != hipSuccess) return err;
@@ -267,15 +375,41 @@ hipError_t launch_select_fwd(const sa_dims& d, const CacheArgs& c, const float* 
     }
 #undef SA_FIN
   } else if (d.dtype == SA_BF16) {
-    if (d.d_kq == 576) dispatch_fused<bf16, 576>(d, c, scores, scores_ld, q_seq, q_pos, n_q, sel, sel_ld, n_sel, q, scale_log2, out, ws_o, ws_ml, plan, stream);
-    else dispatch_fused<bf16, 512>(d, c, scores, scores_ld, q_seq, q_pos, n_q, sel, sel_ld, n_sel, q, scale_log2, out, ws_o, ws_ml, plan, stream);
+    if (d.d_kq == 576) dispatch_fused<bf16, 576>(d, c, scores, scores_ld, q_seq, q_pos, n_q, sel, sel_ld, n_sel, q, scale_log2, out, ws_o, ws_ml, cand, cand_ld, plan, stream);
+    else dispatch_fused<bf16, 512>(d, c, scores, scores_ld, q_seq, q_pos, n_q, sel, sel_ld, n_sel, q, scale_log2, out, ws_o, ws_ml, cand, cand_ld, plan, stream);
   } else {
-    if (d.d_kq == 576) dispatch_fused<f16, 576>(d, c, scores, scores_ld, q_seq, q_pos, n_q, sel, sel_ld, n_sel, q, scale_log2, out, ws_o, ws_ml, plan, stream);
-    else dispatch_fused<f16, 512>(d, c, scores, scores_ld, q_seq, q_pos, n_q, sel, sel_ld, n_sel, q, scale_log2, out, ws_o, ws_ml, plan, stream);
+    if (d.d_kq == 576) dispatch_fused<f16, 576>(d, c, scores, scores_ld, q_seq, q_pos, n_q, sel, sel_ld, n_sel, q, scale_log2, out, ws_o, ws_ml, cand, cand_ld, plan, stream);
+    else dispatch_fused<f16, 512>(d, c, scores, scores_ld, q_seq, q_pos, n_q, sel, sel_ld, n_sel, q, scale_log2, out, ws_o, ws_ml, cand, cand_ld, plan, stream);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   return launch_combine(d, n_q, out, ws_o, ws_ml, plan, stream);
+}
+
+bool step_uses_cand(const sa_dims& d, const CacheArgs& c, const void* qidx, const void* q, int n_q,
+                    const int32_t* n_in, const int32_t* n_out, const FwdPlan& plan, size_t ws_bytes) {
+  return cand_bytes(d, n_q, c.max_len) > 0 && ws_bytes >= workspace_bytes(d, n_q, c.max_len) &&
+         pool_score_fused(d, c, qidx, n_q, n_in, n_out) && fused_form(d, c, q, n_q, plan, ws_bytes) == FusedForm::kWide;
+}
+
+hipError_t launch_pool_score_select_fwd(const sa_dims& d, const CacheArgs& c, const int32_t* n_in, int32_t* n_out,
+                                        int max_new, const void* qidx, const int32_t* q_seq, const int32_t* q_pos,
+                                        int n_q, float* scores, int64_t scores_ld, const void* q, float scale,
+                                        int32_t* sel, int64_t sel_ld, int32_t* n_sel, float* out, void* ws,
+                                        size_t ws_bytes, void* scratch, const FwdPlan& plan, hipStream_t stream) {
+  uint32_t* cand = nullptr;
+  int64_t cand_ld = 0;
+  if (ws && step_uses_cand(d, c, qidx, q, n_q, n_in, n_out, plan, ws_bytes)) {
+    // the workspace's last part (after the partials, which the select's launch writes)
+    const size_t need = workspace_bytes(d, n_q, c.max_len);
+    cand = (uint32_t*)((char*)ws + need - cand_bytes(d, n_q, c.max_len));
+    cand_ld = cand_words(d, c.max_len);
+  }
+  hipError_t err = launch_pool_score(d, c, n_in, n_out, max_new, qidx, q_seq, q_pos, n_q, scores, scores_ld, stream,
+                                     cand, cand_ld);
+  if (err != hipSuccess) return err;
+  return launch_select_fwd(d, c, scores, scores_ld, q_seq, q_pos, n_q, sel, sel_ld, n_sel, q, scale, out, ws,
+                           ws_bytes, scratch, plan, stream, cand, cand_ld);
 }
 
 }  // namespace sa

@@ -97,6 +97,13 @@ struct alignas(16) WideSmem {
   int pick[4];
 };
 
+// The scoring launch's candidate list (optional): for each tile of kCandTile
+// consecutive blocks of a query's row, the kCandKeep largest keys (ties to the lower
+// block; key 0 in the slots of a tile with fewer blocks) and then their block
+// indices, kCandWords words per tile.  Every block outside a tile's list scores at
+// most the smallest key in it.
+constexpr int kCandTile = 32, kCandKeep = 8, kCandWords = 2 * kCandKeep;
+
 // Order-preserving 32-bit key of a score: +0 and -0 give the same key, negative
 // scores map below positive ones.
 __device__ __forceinline__ uint32_t score_key(float f) {
@@ -205,43 +212,24 @@ __device__ __forceinline__ void wide_load_row(const float* __restrict__ row, int
   for (int j = 0; j < KPT; ++j) raw[j] = row[min(j * NT + tid, last)];
 }
 
-// The K_blk kept blocks of a row of nb > k_blk complete blocks whose scores the
-// threads hold in raw[] (thread t, register j: block j*NT + t; entries past nb are
-// ignored), as k_blk*c ascending positions: into the LDS array `list` when it is
-// given, else straight to `out` (global).  The histograms h1 and h2 must be zero on
-// entry.  Ends with the list complete and visible to the whole workgroup.
-template <int NT, int KPT>
-__device__ __forceinline__ void wide_select_rows(const float (&raw)[KPT], int nb_vis, int c, int k_blk,
-                                                 WideSmem<NT, KPT>& sm, int32_t* list, int32_t* out) {
-  constexpr int COPIES = WideCfg<NT, KPT>::copies, WORDS = WideCfg<NT, KPT>::words;
-  constexpr int WPL = WideCfg<NT, KPT>::wpl;
+// The cut of a radix select after its first pass has counted every key (keys in
+// registers, KC per thread; each key's top 10 bits added into the pass-1 histogram
+// h1 laid out [bin][copy]): the first pick, then the 11-bit passes 2 and 3 among
+// the keys still in the running, stopping once a pass's bin is taken whole.  Returns
+// the prefix of the k_blk-th largest key at `shift` (the kept keys are those >=
+// prefix << shift when whole; else shift is 0, prefix is that key T, and k_rem keys
+// equal to T are kept besides those above it).  n_pad keys of 0 are padding.
+struct WideCut {
+  uint32_t prefix;
+  int shift;
+  bool whole;
+  int k_rem;
+};
+template <int NT, int KPT, int KC>
+__device__ __forceinline__ WideCut wide_cut(const uint32_t (&key)[KC], int k_blk, int n_pad, WideSmem<NT, KPT>& sm) {
+  constexpr int COPIES = WideCfg<NT, KPT>::copies;
   constexpr int PER1 = kP1Bins / NT, PER2 = kWideBins / NT;
-  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-  const int nb = min(nb_vis, KPT * NT);              // the launch guarantees nb_vis fits; the bitmap relies on it
-  const int n_pad = KPT * NT - nb;
-
-  // ---- pass 1: the top 10 bits, each key counted as it arrives ---------------------------
-  // Keys past the row's end become 0 -- below every key a score can have except
-  // negative NaNs -- so the passes need no bounds checks: the picks take the n_pad
-  // padding keys back out of bin 0, and a prefix of 0 (the only one they can match)
-  // never takes its bin whole, so they are never kept.
-  uint32_t key[KPT];
-  {
-    uint32_t* mine = sm.h1 + (lane & (COPIES - 1));
-    if (n_pad == 0) {
-#pragma unroll
-      for (int j = 0; j < KPT; ++j) {
-        key[j] = score_key(raw[j]);
-        atomicAdd(&mine[(key[j] >> 22) * COPIES], 1u);
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < KPT; ++j) {
-        key[j] = j * NT + tid < nb ? score_key(raw[j]) : 0u;
-        atomicAdd(&mine[(key[j] >> 22) * COPIES], 1u);
-      }
-    }
-  }
+  const int tid = threadIdx.x;
   __syncthreads();
   {
     // thread t: bins t*PER1 ..; each bin's copies read as quads from a lane-rotated
@@ -274,7 +262,7 @@ __device__ __forceinline__ void wide_select_rows(const float (&raw)[KPT], int nb
     uint32_t one = 1u;
     asm volatile("" : "+v"(one));                    // one register for every add, not one per key
 #pragma unroll
-    for (int j = 0; j < KPT; ++j)
+    for (int j = 0; j < KC; ++j)
       if (key[j] - lo < (1u << 22)) atomicAdd(&sm.h2[(key[j] >> 11) & (kWideBins - 1)], one);
     __syncthreads();
     uint32_t cnt[PER2];
@@ -289,7 +277,7 @@ __device__ __forceinline__ void wide_select_rows(const float (&raw)[KPT], int nb
     if (!whole) {
       const uint32_t lo3 = prefix << 11;
 #pragma unroll
-      for (int j = 0; j < KPT; ++j)
+      for (int j = 0; j < KC; ++j)
         if (key[j] - lo3 < (1u << 11)) atomicAdd(&sm.h1[key[j] & 2047u], 1u);
       __syncthreads();
       uint32_t cnt3[PER2];
@@ -302,26 +290,19 @@ __device__ __forceinline__ void wide_select_rows(const float (&raw)[KPT], int nb
       whole = sm.pick[2] == k_rem && prefix != 0u;
     }
   }
-  // ---- kept blocks -> bitmaps -----------------------------------------------------------
-  // Kept for sure: key >> shift above the prefix, or equal to it when its bin is
-  // taken whole, i.e. key >= thr.  A search that did not end whole ran to the full
-  // width (shift 0): keys above T are kept, keys equal to T are ties.  Padding keys
-  // are 0: below every threshold of a prefix other than 0, which is never whole.
-  // Register j of the wave's lanes holds blocks j*NT + 64*wave + [0, 64): bitmap
-  // words j*NT/32 + 2 wave + {0, 1}, collected in lane j.
-  {
-    uint32_t k_lo = 0u, k_hi = 0u, t_lo = 0u, t_hi = 0u;
-    if (whole || prefix != 0xffffffffu) {
-      const uint32_t thr = whole ? prefix << shift : prefix + 1u;
-      ballot_rows<KPT>([&](int j) { return key[j] >= thr; }, k_lo, k_hi);
-    }
-    if (!whole) ballot_rows<KPT>([&](int j) { return key[j] == prefix; }, t_lo, t_hi);
-    if (lane < KPT) {
-      *(uint2*)&sm.keep[lane * (NT / 32) + wave * 2] = uint2{k_lo, k_hi};
-      *(uint2*)&sm.tie[lane * (NT / 32) + wave * 2] = uint2{t_lo, t_hi};
-    }
-  }
-  __syncthreads();
+  return WideCut{prefix, shift, whole, k_rem};
+}
+
+// The kept blocks' positions, k_blk * c ascending entries, from the workgroup's keep
+// and tie bitmaps (bit b of word b / 32: block b): every block in keep, then, when the
+// cut fell inside one key value (!whole), the first k_rem blocks of tie in index
+// order.  Into the LDS array `list` when it is given (complete and visible to the
+// whole workgroup on return), else straight to `out` (global).
+template <int NT, int KPT>
+__device__ __forceinline__ void wide_list(const WideSmem<NT, KPT>& sm, bool whole, int k_rem, int c, int k_blk,
+                                          int32_t* list, int32_t* out) {
+  constexpr int WORDS = WideCfg<NT, KPT>::words, WPL = WideCfg<NT, KPT>::wpl;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   // ---- this wave's words -> positions in index order ------------------------------------------
   // Lane word w (WPL bitmap words, 32*WPL blocks) of this lane: w = 64 * wave + lane.
   typedef typename std::conditional<WPL == 2, uint64_t, uint32_t>::type Word;
@@ -369,6 +350,68 @@ __device__ __forceinline__ void wide_select_rows(const float (&raw)[KPT], int nb
       ++o;
     }
   }
+}
+
+// The K_blk kept blocks of a row of nb > k_blk complete blocks whose scores the
+// threads hold in raw[] (thread t, register j: block j*NT + t; entries past nb are
+// ignored), as k_blk*c ascending positions: into the LDS array `list` when it is
+// given, else straight to `out` (global).  The histograms h1 and h2 must be zero on
+// entry.  Ends with the list complete and visible to the whole workgroup.
+template <int NT, int KPT>
+__device__ __forceinline__ void wide_select_rows(const float (&raw)[KPT], int nb_vis, int c, int k_blk,
+                                                 WideSmem<NT, KPT>& sm, int32_t* list, int32_t* out) {
+  constexpr int COPIES = WideCfg<NT, KPT>::copies;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int nb = min(nb_vis, KPT * NT);              // the launch guarantees nb_vis fits; the bitmap relies on it
+  const int n_pad = KPT * NT - nb;
+
+  // ---- pass 1: the top 10 bits, each key counted as it arrives ---------------------------
+  // Keys past the row's end become 0 -- below every key a score can have except
+  // negative NaNs -- so the passes need no bounds checks: the picks take the n_pad
+  // padding keys back out of bin 0, and a prefix of 0 (the only one they can match)
+  // never takes its bin whole, so they are never kept.
+  uint32_t key[KPT];
+  {
+    uint32_t* mine = sm.h1 + (lane & (COPIES - 1));
+    if (n_pad == 0) {
+#pragma unroll
+      for (int j = 0; j < KPT; ++j) {
+        key[j] = score_key(raw[j]);
+        atomicAdd(&mine[(key[j] >> 22) * COPIES], 1u);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < KPT; ++j) {
+        key[j] = j * NT + tid < nb ? score_key(raw[j]) : 0u;
+        atomicAdd(&mine[(key[j] >> 22) * COPIES], 1u);
+      }
+    }
+  }
+  const WideCut cut = wide_cut<NT, KPT, KPT>(key, k_blk, n_pad, sm);
+  const uint32_t prefix = cut.prefix;
+  const int shift = cut.shift, k_rem = cut.k_rem;
+  const bool whole = cut.whole;
+  // ---- kept blocks -> bitmaps -----------------------------------------------------------
+  // Kept for sure: key >> shift above the prefix, or equal to it when its bin is
+  // taken whole, i.e. key >= thr.  A search that did not end whole ran to the full
+  // width (shift 0): keys above T are kept, keys equal to T are ties.  Padding keys
+  // are 0: below every threshold of a prefix other than 0, which is never whole.
+  // Register j of the wave's lanes holds blocks j*NT + 64*wave + [0, 64): bitmap
+  // words j*NT/32 + 2 wave + {0, 1}, collected in lane j.
+  {
+    uint32_t k_lo = 0u, k_hi = 0u, t_lo = 0u, t_hi = 0u;
+    if (whole || prefix != 0xffffffffu) {
+      const uint32_t thr = whole ? prefix << shift : prefix + 1u;
+      ballot_rows<KPT>([&](int j) { return key[j] >= thr; }, k_lo, k_hi);
+    }
+    if (!whole) ballot_rows<KPT>([&](int j) { return key[j] == prefix; }, t_lo, t_hi);
+    if (lane < KPT) {
+      *(uint2*)&sm.keep[lane * (NT / 32) + wave * 2] = uint2{k_lo, k_hi};
+      *(uint2*)&sm.tie[lane * (NT / 32) + wave * 2] = uint2{t_lo, t_hi};
+    }
+  }
+  __syncthreads();
+  wide_list<NT, KPT>(sm, whole, k_rem, c, k_blk, list, out);
 }
 
 }  // namespace sa

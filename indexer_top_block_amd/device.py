@@ -96,6 +96,36 @@ class DeviceLayer:
     def select_fwd_is_fused(self) -> bool:
         return sa.sparse_attn_select_fwd_is_fused(self.dims, self.cache, self.q, self.n_q)
 
+    def pool_score_select_fwd(self, max_new_blocks: int = 2 ** 31 - 1, n_in=None, n_out=None, stream=None) -> None:
+        """pool + score, then select and attend (sparse_attn_pool_score_select_fwd): the
+        selection from the scoring launch's candidate list where it applies."""
+        n_in, n_out = self._counts(n_in, n_out)
+        sa.sparse_attn_pool_score_select_fwd(self.dims, self.cache, n_in, n_out, max_new_blocks, self.qidx,
+                                             self.q_seq, self.q_pos, self.n_q, self.scores, self.scores_ld, self.q,
+                                             self.scale, self.sel, self.sel_ld, self.n_sel, self.out, self.ws,
+                                             self.ws_bytes, stream)
+
+    def pool_score_select_fwd_uses_list(self, n_in=None, n_out=None) -> bool:
+        n_in, n_out = self._counts(n_in, n_out)
+        return sa.sparse_attn_pool_score_select_fwd_uses_list(self.dims, self.cache, n_in, n_out, self.qidx, self.q,
+                                                              self.n_q)
+
+    def _counts(self, n_in, n_out):
+        """Pooled-count arrays in and out: distinct by default (the pooling scoring
+        launch needs them apart); the output becomes the layer's count."""
+        if n_in is None:
+            n_in = self.n_pooled
+        if n_out is None:
+            if not hasattr(self, "n_pooled_next"):
+                self.n_pooled_next = torch.zeros_like(self.n_pooled)
+            n_out = self.n_pooled_next
+        return n_in, n_out
+
+    def list_decided(self) -> np.ndarray:
+        """The n_q int32 that end the workspace: 1 where sparse_attn_pool_score_select_fwd's
+        candidate list decided the token's selection, 0 where the row did."""
+        return self.ws[self.ws_bytes - 4 * self.n_q: self.ws_bytes].view(torch.int32).cpu().numpy()
+
     def fwd_window(self, window: int, sel: Optional[torch.Tensor] = None, n_sel: Optional[torch.Tensor] = None,
                    stream=None) -> None:
         sel = self.sel if sel is None else sel

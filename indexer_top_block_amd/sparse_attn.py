@@ -37,6 +37,8 @@ EXPORTS = (
     "sparse_attn_fwd_noalloc",
     "sparse_attn_select_fwd",
     "sparse_attn_select_fwd_is_fused",
+    "sparse_attn_pool_score_select_fwd",
+    "sparse_attn_pool_score_select_fwd_uses_list",
     "sparse_attn_mask_to_indices",
     "sparse_attn_fwd_bias",
     "sparse_attn_workspace_bytes_window",
@@ -111,6 +113,11 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.sparse_attn_select_fwd.restype = ctypes.c_int
     lib.sparse_attn_select_fwd_is_fused.argtypes = [dp, cp, P, I32]
     lib.sparse_attn_select_fwd_is_fused.restype = ctypes.c_int
+    lib.sparse_attn_pool_score_select_fwd.argtypes = [dp, cp, P, P, I32, P, P, P, I32, P, I64, P, ctypes.c_float,
+                                                      P, I64, P, P, P, SZ, P]
+    lib.sparse_attn_pool_score_select_fwd.restype = ctypes.c_int
+    lib.sparse_attn_pool_score_select_fwd_uses_list.argtypes = [dp, cp, P, P, P, P, I32]
+    lib.sparse_attn_pool_score_select_fwd_uses_list.restype = ctypes.c_int
     lib.sparse_attn_mask_to_indices.argtypes = [P, I32, I64, I32, I32, P, I64, P, P, P]
     lib.sparse_attn_mask_to_indices.restype = ctypes.c_int
     lib.sparse_attn_fwd_bias.argtypes = [dp, cp, P, P, P, I64, P, P, I32, ctypes.c_float, P, P, SZ, P]
@@ -255,6 +262,27 @@ def sparse_attn_select_fwd_is_fused(dims: SaDims, cache: Cache, q, n_q: int) -> 
     rc = load().sparse_attn_select_fwd_is_fused(ctypes.byref(dims), ctypes.byref(cache.struct), _ptr(q), int(n_q))
     if rc < 0:
         _check("sparse_attn_select_fwd_is_fused", rc)
+    return rc == 1
+
+
+def sparse_attn_pool_score_select_fwd(dims: SaDims, cache: Cache, n_pooled_in, n_pooled_out, max_new_blocks: int,
+                                      qidx, q_seq, q_pos, n_q: int, scores, scores_ld: int, q, scale: float, sel,
+                                      sel_ld: int, n_sel, out, ws=None, ws_bytes: int = 0, stream=None) -> None:
+    _check("sparse_attn_pool_score_select_fwd",
+           load().sparse_attn_pool_score_select_fwd(ctypes.byref(dims), ctypes.byref(cache.struct), _ptr(n_pooled_in),
+                                                    _ptr(n_pooled_out), int(max_new_blocks), _ptr(qidx), _ptr(q_seq),
+                                                    _ptr(q_pos), int(n_q), _ptr(scores), int(scores_ld), _ptr(q),
+                                                    float(scale), _ptr(sel), int(sel_ld), _ptr(n_sel), _ptr(out),
+                                                    _ptr(ws), int(ws_bytes), _stream(stream)))
+
+
+def sparse_attn_pool_score_select_fwd_uses_list(dims: SaDims, cache: Cache, n_pooled_in, n_pooled_out, qidx, q,
+                                                n_q: int) -> bool:
+    rc = load().sparse_attn_pool_score_select_fwd_uses_list(ctypes.byref(dims), ctypes.byref(cache.struct),
+                                                            _ptr(n_pooled_in), _ptr(n_pooled_out), _ptr(qidx),
+                                                            _ptr(q), int(n_q))
+    if rc < 0:
+        _check("sparse_attn_pool_score_select_fwd_uses_list", rc)
     return rc == 1
 
 

@@ -14,6 +14,7 @@ HEADER = os.path.join(ROOT, "include", "sparse_attn.h")
 
 # Any non-zero value: validation never dereferences device pointers on the host.
 FAKE = 0x10000
+FAKE2 = 0x20000               # a second distinct non-null address
 
 
 def _declared_functions():
@@ -74,12 +75,21 @@ def test_workspace_bytes():
     hdr = open(HEADER).read()
     assert f"#define SA_WS_STATE_BYTES ((size_t){sa.WS_STATE_BYTES})" in hdr
     partials_1 = 33 * 16 * (512 + 2) * 4            # one decode token: 33 splits of (o, m, l) for 16 heads
-    # short rows: state region + split-KV partials
-    assert sa.sparse_attn_workspace_bytes(d, 1, 4096) == sa.WS_STATE_BYTES + partials_1
+    # the candidate list of the pool + score + select call, after the partials on a
+    # 256-byte boundary: 16 words per 32 blocks of each token's row, then one flag per token
+    def after(n):
+        return (n + 255) // 256 * 256
+
+    # short rows: state region + split-KV partials (+ the list: rows of at most
+    # k_blk = 512 blocks are always dense and have none)
+    assert sa.sparse_attn_workspace_bytes(d, 1, 2048) == sa.WS_STATE_BYTES + partials_1
+    assert sa.sparse_attn_workspace_bytes(d, 1, 4096) == after(sa.WS_STATE_BYTES + partials_1) + (32 * 16 + 1) * 4
     # a prefill chunk: unsplit attention and one selection workgroup per query token
+    # (no list for 64 tokens or more)
     assert sa.sparse_attn_workspace_bytes(d, 2048, 34816) == 0
     # 128K rows: one workgroup holds a row of 32768 blocks, so selection adds nothing
-    assert sa.sparse_attn_workspace_bytes(d, 1, 131072) == sa.WS_STATE_BYTES + partials_1
+    # but the list: 1024 groups
+    assert sa.sparse_attn_workspace_bytes(d, 1, 131072) == after(sa.WS_STATE_BYTES + partials_1) + (1024 * 16 + 1) * 4
     # 1M rows: the chunked selection's 128 chunks of 2048 8-byte entries (after a
     # 768-byte head of counts), then the partials, side by side
     assert sa.sparse_attn_workspace_bytes(d, 1, 1048576) == sa.WS_STATE_BYTES + 768 + 128 * 2048 * 8 + partials_1
@@ -135,7 +145,9 @@ def test_entry_points_reject_bad_arguments_before_any_launch():
     ws = sa.sparse_attn_workspace_bytes(_dims(), 1, 4096)
     args = [d, c, FAKE, FAKE, FAKE, 2051, FAKE, 1, ctypes.c_float(0.04), FAKE]
     assert _call("sparse_attn_fwd", *args, None, 0, None) == sa.SA_ERR_WORKSPACE
-    assert _call("sparse_attn_fwd", *args, FAKE, ws - 1, None) == sa.SA_ERR_WORKSPACE
+    need_fwd = sa.WS_STATE_BYTES + 33 * 16 * (512 + 2) * 4      # the attention's part: state + partials
+    assert ws > need_fwd                                          # (the rest: the candidate list)
+    assert _call("sparse_attn_fwd", *args, FAKE, need_fwd - 1, None) == sa.SA_ERR_WORKSPACE
     assert _call("sparse_attn_fwd", d, c, None, FAKE, FAKE, 2051, FAKE, 1, ctypes.c_float(0.04), FAKE, FAKE, ws,
                  None) == sa.SA_ERR_NULL
     assert _call("sparse_attn_fwd", d, c, FAKE, FAKE, FAKE, 2051, FAKE, 1, ctypes.c_float(float("nan")), FAKE, FAKE,
@@ -263,14 +275,15 @@ def test_noalloc_fwd_rejects_bad_arguments_and_oversize():
     assert _call(fn, d, c, FAKE, FAKE, FAKE, 2051, FAKE, 1, ctypes.c_float(float("nan")), FAKE, None) == sa.SA_ERR_ARG
     assert _call(fn, d, c, FAKE, FAKE, FAKE, 0, FAKE, 1, f, FAKE, None) == sa.SA_ERR_ARG
     assert _call(fn, d, c, FAKE, FAKE, FAKE, 2051, FAKE, 0, f, FAKE, None) == sa.SA_OK   # nothing to do
-    # scratch needed = the workspace's scratch part; every shape with d_v <= 512 fits,
-    # e.g. any number of decode tokens of 16 heads 576/512
+    # scratch needed = the workspace's partials part (rows of 2048 tokens, 512 blocks:
+    # always dense, so the workspace holds no selection scratch and no candidate list);
+    # every shape with d_v <= 512 fits, e.g. any number of decode tokens of 16 heads 576/512
     for n_q in (1, 15, 16, 31, 32, 256, 511):
-        need = sa.sparse_attn_workspace_bytes(_dims(), n_q, 4096)
+        need = sa.sparse_attn_workspace_bytes(_dims(), n_q, 2048)
         assert (need - sa.WS_STATE_BYTES if need else 0) <= sa.STATIC_SCRATCH_BYTES, n_q
     # wider V heads can exceed it: 16 tokens of 16 heads 1024/1024 (32 splits each)
     wide = _dims(d_kq=1024, d_v=1024)
-    need = sa.sparse_attn_workspace_bytes(wide, 16, 4096) - sa.WS_STATE_BYTES
+    need = sa.sparse_attn_workspace_bytes(wide, 16, 2048) - sa.WS_STATE_BYTES
     assert need > sa.STATIC_SCRATCH_BYTES
     wc = ctypes.byref(_cache(k_ld=1024, v_ld=1024))
     assert _call(fn, ctypes.byref(wide), wc, FAKE, FAKE, FAKE, 2051, FAKE, 16, f, FAKE, None) == sa.SA_ERR_SCRATCH
@@ -306,7 +319,7 @@ def test_select_fwd_rejects_bad_arguments():
     assert call(a11=None) == sa.SA_ERR_NULL                           # n_sel
     assert call(a12=None) == sa.SA_ERR_NULL                           # out
     assert call(a13=None, a14=0) == sa.SA_ERR_WORKSPACE               # the split partials
-    assert call(a14=ws - 1) == sa.SA_ERR_WORKSPACE
+    assert call(a14=sa.WS_STATE_BYTES + 33 * 16 * (512 + 2) * 4 - 1) == sa.SA_ERR_WORKSPACE
     # a 1M row needs the chunked selection's workspace
     long_c = ctypes.byref(_cache(max_len=1048576))
     need = sa.sparse_attn_workspace_bytes(_dims(), 1, 1048576)
@@ -317,3 +330,51 @@ def test_select_fwd_rejects_bad_arguments():
     assert _call(q, ctypes.byref(_dims()), ctypes.byref(_cache()), FAKE, 0) == sa.SA_ERR_ARG
     assert _call(q, ctypes.byref(_dims()), ctypes.byref(_cache()), None, 1) == sa.SA_ERR_NULL
     assert _call(q, ctypes.byref(_dims(top_k=2050)), ctypes.byref(_cache()), FAKE, 1) == sa.SA_ERR_DIMS
+
+
+def test_pool_score_select_fwd_rejects_bad_arguments():
+    # sparse_attn_pool_score_select_fwd: the checks of sparse_attn_pool_score and of
+    # sparse_attn_select_fwd, all before any HIP call
+    fn = "sparse_attn_pool_score_select_fwd"
+    ws = sa.sparse_attn_workspace_bytes(_dims(), 1, 4096)
+    # dims, cache, n_in, n_out, max_new, qidx, q_seq, q_pos, n_q, scores, scores_ld, q, scale, sel, sel_ld,
+    # n_sel, out, ws, ws_bytes, stream
+    good = [ctypes.byref(_dims()), ctypes.byref(_cache()), FAKE, FAKE2, 1, FAKE, FAKE, FAKE, 1, FAKE, 1024, FAKE,
+            ctypes.c_float(0.04), FAKE, 2051, FAKE, FAKE, FAKE, ws, None]
+
+    def call(**changes):
+        args = list(good)
+        for k, v in changes.items():
+            args[int(k[1:])] = v
+        return _call(fn, *args)
+
+    assert call(a0=None) == sa.SA_ERR_NULL
+    assert call(a0=ctypes.byref(_dims(top_k=2050))) == sa.SA_ERR_DIMS
+    assert call(a1=ctypes.byref(_cache(seq_len=None))) == sa.SA_ERR_NULL
+    assert call(a1=ctypes.byref(_cache(kidx_ld=64))) == sa.SA_ERR_ARG
+    assert call(a2=None) == sa.SA_ERR_NULL                            # n_pooled_in
+    assert call(a3=None) == sa.SA_ERR_NULL                            # n_pooled_out
+    assert call(a4=-1) == sa.SA_ERR_ARG                               # max_new_blocks
+    assert call(a5=None) == sa.SA_ERR_NULL                            # qidx
+    assert call(a7=None) == sa.SA_ERR_NULL                            # q_pos
+    assert call(a8=-1) == sa.SA_ERR_ARG
+    assert call(a9=None) == sa.SA_ERR_NULL                            # scores
+    assert call(a10=1023) == sa.SA_ERR_ARG                            # scores_ld < max_len / c
+    assert call(a11=None) == sa.SA_ERR_NULL                           # q
+    assert call(a12=ctypes.c_float(float("nan"))) == sa.SA_ERR_ARG
+    assert call(a13=None) == sa.SA_ERR_NULL                           # sel
+    assert call(a14=2050) == sa.SA_ERR_ARG                            # sel_ld < top_k + c - 1
+    assert call(a15=None) == sa.SA_ERR_NULL                           # n_sel
+    assert call(a16=None) == sa.SA_ERR_NULL                           # out
+    assert call(a17=None, a18=0) == sa.SA_ERR_WORKSPACE               # the split partials
+    assert call(a18=sa.WS_STATE_BYTES + 33 * 16 * (512 + 2) * 4 - 1) == sa.SA_ERR_WORKSPACE
+    long_c = ctypes.byref(_cache(max_len=1048576))
+    need = sa.sparse_attn_workspace_bytes(_dims(), 1, 1048576)
+    assert call(a1=long_c, a10=262144, a18=need - 1) == sa.SA_ERR_WORKSPACE
+    # the form query
+    q = "sparse_attn_pool_score_select_fwd_uses_list"
+    cc = ctypes.byref(_cache())
+    assert _call(q, ctypes.byref(_dims()), cc, FAKE, FAKE2, FAKE, FAKE, 0) == sa.SA_ERR_ARG
+    assert _call(q, ctypes.byref(_dims()), cc, None, FAKE2, FAKE, FAKE, 1) == sa.SA_ERR_NULL
+    assert _call(q, ctypes.byref(_dims()), cc, FAKE, FAKE2, None, FAKE, 1) == sa.SA_ERR_NULL
+    assert _call(q, ctypes.byref(_dims(top_k=2050)), cc, FAKE, FAKE2, FAKE, FAKE, 1) == sa.SA_ERR_DIMS
