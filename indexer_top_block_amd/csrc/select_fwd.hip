@@ -63,21 +63,23 @@ union FusedSmem {
 
 // The select from the scoring launch's candidate list: thread t holds tile t's
 // kCandKeep keys and block indices (keys 0 past the row), counts them into the pass-1
-// histogram and runs the passes over them; the keep and tie words of tile t come from
-// its own candidates.  The result is the row's select exactly when every block left
-// out of the list falls below the cut: below the cut's bin when the bin is taken
-// whole, below the cut key T otherwise (a block equal to T, left out, could be a tie
-// the row's select takes).  Each tile's smallest listed key bounds those it left out,
-// so the workgroup checks that bound and returns false when it is not below the cut
-// (the caller then selects over the row).  Requires nb > k_blk and at least k_blk
-// listed blocks; the histograms are clear on entry and dirty on return.
+// histogram and runs the passes over them.  The result is the row's select exactly
+// when every block left out of the list falls below the cut: below the cut's bin when
+// the bin is taken whole, below the cut key T otherwise (a block equal to T, left
+// out, could be a tie the row's select takes).  Each tile's smallest listed key
+// bounds those it left out, so the largest of those bounds is compared with the cut
+// (false: the caller selects over the row).  The kept blocks of tile t are then
+// t's own candidates: each thread places them in the list from the counts of the
+// tiles before it (kept blocks, and the first k_rem tied blocks in index order).
+// Requires nb > k_blk and at least k_blk listed blocks; the histograms are clear on
+// entry and dirty on return.
 template <int NT, int KPT>
 __device__ __forceinline__ bool cand_select(const uint4 (&cv)[4], int nb, int c, int k_blk, WideSmem<NT, KPT>& sm,
                                             int32_t* list) {
-  constexpr int COPIES = WideCfg<NT, KPT>::copies, WORDS = WideCfg<NT, KPT>::words;
-  static_assert(kCandKeep == 8 && WORDS <= NT, "one tile's list per thread");
-  const int tid = threadIdx.x, lane = tid % kWave;
-  nb = min(nb, KPT * NT);                            // the launch guarantees nb fits; the bitmap relies on it
+  constexpr int COPIES = WideCfg<NT, KPT>::copies, WAVES = NT / kWave;
+  static_assert(kCandKeep == 8 && WideCfg<NT, KPT>::words >= WAVES && kWideBins >= 2 * WAVES, "LDS reuse");
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  nb = min(nb, KPT * NT);                            // the launch guarantees nb fits; the list relies on it
   const bool in_row = tid * kCandTile < nb;
   const uint32_t key[kCandKeep] = {in_row ? cv[0].x : 0u, in_row ? cv[0].y : 0u, in_row ? cv[0].z : 0u,
                                    in_row ? cv[0].w : 0u, in_row ? cv[1].x : 0u, in_row ? cv[1].y : 0u,
@@ -90,13 +92,20 @@ __device__ __forceinline__ bool cand_select(const uint4 (&cv)[4], int nb, int c,
 #pragma unroll
     for (int j = 0; j < kCandKeep; ++j) atomicAdd(&mine[(key[j] >> 22) * COPIES], 1u);
   }
-  const WideCut cut = wide_cut<NT, KPT, kCandKeep>(key, k_blk, NT * kCandKeep - n_listed, sm);
-  const uint32_t bound = cut.whole ? cut.prefix << cut.shift : cut.prefix;
+  // the bound on the keys left out: per wave into keep[wave] (free until the list),
+  // ordered before its reads by the picks' barriers
   uint32_t least = key[0];
 #pragma unroll
   for (int j = 1; j < kCandKeep; ++j) least = min(least, key[j]);
-  if (__syncthreads_or(least >= bound)) return false;
-  // keep: key >= thr (thr > 0: bound > 0 here, since every key is >= 0); tie: key == T
+  least = wave_max_u32(least);
+  if (lane == 0) sm.keep[wave] = least;
+  const WideCut cut = wide_cut<NT, KPT, kCandKeep>(key, k_blk, NT * kCandKeep - n_listed, sm);
+  const uint32_t bound = cut.whole ? cut.prefix << cut.shift : cut.prefix;
+  uint32_t left_out = 0u;
+#pragma unroll
+  for (int w = 0; w < WAVES; ++w) left_out = max(left_out, sm.keep[w]);
+  if (left_out >= bound) return false;               // (bound 0: never taken)
+  // keep: key >= thr (thr > 0: bound > 0 here); tie: key == T (the cut inside a key)
   const uint32_t thr = cut.whole ? bound : bound + 1u;
   const bool full = !cut.whole && bound == 0xffffffffu;   // nothing above T
   uint32_t kw = 0u, tw = 0u;
@@ -106,12 +115,42 @@ __device__ __forceinline__ bool cand_select(const uint4 (&cv)[4], int nb, int c,
     if (!full && key[j] >= thr) kw |= bit;
     if (!cut.whole && key[j] == bound) tw |= bit;
   }
-  if (tid < WORDS) {
-    sm.keep[tid] = kw;
-    sm.tie[tid] = tw;
+  // counts of the tiles before this one: wave scans, then the wave totals (in h2,
+  // free since the last pick)
+  const int kc = __popc(kw), tc = __popc(tw);
+  const int k_incl = wave_inclusive_scan(kc, lane), t_incl = wave_inclusive_scan(tc, lane);
+  if (lane == kWave - 1) {
+    sm.h2[wave] = (uint32_t)k_incl;
+    sm.h2[WAVES + wave] = (uint32_t)t_incl;
+  }
+  lds_barrier();
+  const int wk = lane < WAVES ? (int)sm.h2[lane] : 0, wt = lane < WAVES ? (int)sm.h2[WAVES + lane] : 0;
+  const int wk_incl = wave_inclusive_scan(wk, lane), wt_incl = wave_inclusive_scan(wt, lane);
+  const int k_before = (wave > 0 ? __builtin_amdgcn_readlane(wk_incl, wave - 1) : 0) + k_incl - kc;
+  const int t_before = (wave > 0 ? __builtin_amdgcn_readlane(wt_incl, wave - 1) : 0) + t_incl - tc;
+  int o = k_before + min(cut.k_rem, t_before);
+  uint32_t word = kw;
+  for (int take = min(tc, cut.k_rem - t_before); take > 0; --take) {   // the first tied blocks still wanted
+    word |= tw & (0u - tw);
+    tw &= tw - 1u;
+  }
+  const int32_t b0 = tid * kCandTile;
+  if (c == 4) {
+    while (word != 0u && o < k_blk) {                // o < k_blk always; the bound only guards memory
+      const int32_t p0 = (b0 + __ffs(word) - 1) * 4;
+      word &= word - 1u;
+      *(int4*)&list[o * 4] = int4{p0, p0 + 1, p0 + 2, p0 + 3};
+      ++o;
+    }
+  } else {
+    while (word != 0u && o < k_blk) {
+      const int32_t p0 = (b0 + __ffs(word) - 1) * c;
+      word &= word - 1u;
+      for (int t = 0; t < c; ++t) list[o * c + t] = p0 + t;
+      ++o;
+    }
   }
   __syncthreads();
-  wide_list<NT, KPT>(sm, cut.whole, cut.k_rem, c, k_blk, list, nullptr);
   return true;
 }
 

@@ -104,6 +104,24 @@ struct alignas(16) WideSmem {
 // most the smallest key in it.
 constexpr int kCandTile = 32, kCandKeep = 8, kCandWords = 2 * kCandKeep;
 
+// Maximum / minimum over the wave by DPP and permlane exchanges, the same value in
+// every lane (lane ^ 1, lane ^ 2, the mirror in 8, lane ^ 8, then the 16- and 32-lane
+// swaps: each step combines two halves that already hold their own extremes).
+template <bool MAX>
+__device__ __forceinline__ uint32_t wave_extreme_u32(uint32_t x) {
+  auto f = [](uint32_t a, uint32_t b) { return MAX ? max(a, b) : min(a, b); };
+  x = f(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xf, 0xf, false));   // lane ^ 1
+  x = f(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xf, 0xf, false));   // lane ^ 2
+  x = f(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x141, 0xf, 0xf, false));  // 7 - lane in 8
+  x = f(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x128, 0xf, 0xf, false));  // lane ^ 8 in 16
+  const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  x = f(a[0], a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return f(b[0], b[1]);
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) { return wave_extreme_u32<true>(x); }
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) { return wave_extreme_u32<false>(x); }
+
 // Order-preserving 32-bit key of a score: +0 and -0 give the same key, negative
 // scores map below positive ones.
 __device__ __forceinline__ uint32_t score_key(float f) {
