@@ -5,9 +5,11 @@
 A step is one pass of the whole path -- pool the newest block, score every block,
 select, attend -- for one decode token of a DeepSeek-V4-shaped layer at 128K context
 (16 query heads on one 576-wide latent KV head with V = its first 512 dims; indexer of
-64 heads x 128, compress_ratio 4, top_k 2048; bf16 caches).  The timed steps are
-replayed as one HIP graph (the same kernel launches, without the host-side launch
-overhead of the Python binding).
+64 heads x 128, compress_ratio 4, top_k 2048; bf16 caches), made by one call,
+sparse_attn_pool_score_select_fwd: the pooling scoring launch (which also writes each
+32-block group's 8 best blocks), the selection from that list inside the attention's
+launch, and the split combine.  The timed steps are replayed as one HIP graph (the
+same kernel launches, without the host-side launch overhead of the Python binding).
 
 Cold (the headline): `--layers` independent copies of the layer's caches are resident
 (like a model's layers) and step k runs on copy k mod layers.  Between the untimed
@@ -280,11 +282,14 @@ def gbs(nbytes: float, ms: float) -> float:
 
 
 def decode_section(lay: "RotatingLayers", ab: dict, steps: int, warmup: int, flush: Flusher,
-                   kernels=("pool_score", "select_fwd", "select", "fwd"), warm: bool = True) -> dict:
+                   kernels=("pool_score", "select_fwd", "two_calls", "select", "fwd"), warm: bool = True) -> dict:
     """Cold step time over the rotated copies (flush before the timed replay), each
-    entry point alone under the same protocol, and (optionally) the warm step time."""
+    entry point alone under the same protocol (two_calls: sparse_attn_pool_score then
+    sparse_attn_select_fwd, the step without the candidate list), and (optionally)
+    the warm step time."""
     R = lay.n
     ms = time_graph(lambda k: lay.step(k % R), steps, warmup, flush)
+    decided = lay.list_decided() if lay.uses_list() else None
     rec = {"us_per_step": round(ms * 1e3, 3), "value": round(gbs(ab["total"], ms), 2), "unit": "GB/s",
            "frac_of_hbm_peak": round(gbs(ab["total"], ms) / HBM_PEAK_GBS, 4), "bytes_per_step": ab,
            "timed_region": {"steps": steps, "distinct_layer_copies": min(steps, R),
@@ -296,11 +301,20 @@ def decode_section(lay: "RotatingLayers", ab: dict, steps: int, warmup: int, flu
         per[name] = round(time_graph(lambda k, fn=fn: fn(k % R), steps, warmup, flush) * 1e3, 3)
     rec["kernel_avg_us"] = per
     rec["select_fwd_fused"] = lay.select_fwd_is_fused()
+    # the step's form: the selection from the scoring launch's candidate list, and for
+    # how many tokens of the last timed step the list decided it (else their rows did)
+    rec["select_from_list"] = decided is not None
+    if decided is not None:
+        rec["tokens_decided_by_list"] = f"{sum(decided)} of {len(decided)}"
     if warm:
         wms = time_graph(lambda k: lay.step(0), steps, warmup)
         rec["warm"] = {"us_per_step": round(wms * 1e3, 3), "value": round(gbs(ab["total"], wms), 2),
                        "unit": "GB/s", "protocol": "every step on the same layer copy, after an untimed replay"}
     return rec
+
+
+SCORE_KERNEL = ("score_mfma_kernel (pooling variant) as sparse_attn_pool_score launches it; in the step's "
+                "sparse_attn_pool_score_select_fwd the same launch also writes the candidate list")
 
 
 def roofline_block(ab: dict, sec: dict, score_kernel: str, traffic=None) -> dict:
@@ -666,7 +680,7 @@ def workload_decode_report(cfg: int, steps: int, warmup: int, layers: int, flush
     sec = decode_section(lay, ab, steps, warmup, flush, warm=True)
     sec["workload"] = datagen.WORKLOADS[cfg]
     sec["layers_rotated"] = layers
-    sec["roofline"] = roofline_block(ab, sec, "score_mfma_kernel (pooling variant)")
+    sec["roofline"] = roofline_block(ab, sec, SCORE_KERNEL)
     del lay
     torch.cuda.empty_cache()
     return sec
@@ -692,7 +706,7 @@ def main() -> int:
     ap.add_argument("--workload", type=int, choices=[2, 3, 5, 6], default=2,
                     help="decode workload of --only")
     ap.add_argument("--only", choices=["pool_score", "pool", "score", "select", "fwd", "select_fwd", "step",
-                                       "prefill_score", "prefill_fwd"], default=None,
+                                       "two_calls", "prefill_score", "prefill_fwd"], default=None,
                     help="run just this call for --steps launches over the rotated copies of --workload, or one "
                          "stage of the prefill chunk (counter collection)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
@@ -765,17 +779,20 @@ def main() -> int:
                "frac_of_hbm_peak": round(gbs(ab["total"], ms) / HBM_PEAK_GBS, 4),
                "kernel_avg_us": {n: round(time_eager(lambda k, fn=getattr(lay, n): fn(k % R), args.steps,
                                                      args.warmup) * 1e3, 3)
-                                 for n in ("pool_score", "pool", "score", "select", "fwd", "select_fwd")}}
+                                 for n in ("pool_score", "pool", "score", "select", "fwd", "select_fwd",
+                                           "two_calls")}}
     else:
         sec = decode_section(lay, ab, args.steps, args.warmup, flush,
-                             kernels=("pool_score", "pool", "score", "select_fwd", "select", "fwd"))
+                             kernels=("pool_score", "pool", "score", "select_fwd", "two_calls", "select", "fwd"))
     ms = sec["us_per_step"] * 1e-3
     log(f"[bench] step {sec['us_per_step']:.2f} us (cold); per-call us {sec['kernel_avg_us']}; "
         f"warm {sec.get('warm', {}).get('us_per_step')}")
-    # The roofline is taken on the scoring kernel as the step launches it (with the
-    # newest block pooled inside): sparse_attn_pool_score is one kernel launch, and it
-    # streams the pooled indexer keys -- most of the step's algorithmic bytes.
-    roofline = roofline_block(ab, sec, "score_mfma_kernel (pooling variant)", traffic_from_counters(args.traffic_file))
+    # The roofline is taken on the scoring kernel with the newest block pooled inside,
+    # timed as sparse_attn_pool_score launches it (one kernel launch streaming the
+    # pooled indexer keys -- most of the step's algorithmic bytes).  Inside the step
+    # (sparse_attn_pool_score_select_fwd) the same kernel also writes the candidate
+    # list, which the per-call figure of the step's own launches includes.
+    roofline = roofline_block(ab, sec, SCORE_KERNEL, traffic_from_counters(args.traffic_file))
 
     rec = {
         "metric": METRIC, "value": sec["value"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,

@@ -164,11 +164,13 @@ class DeviceLayer:
                                 self.n_q, self.scale, self.out, self.ws, self.ws_bytes, stream)
 
     def step(self, stream=None) -> None:
-        """One pass of the whole path: pool what is new, score, then select and attend
-        in one call (sparse_attn_select_fwd)."""
-        self.pool(stream=stream)
-        self.score(stream)
-        self.select_fwd(stream=stream)
+        """One pass of the whole path in one call (sparse_attn_pool_score_select_fwd):
+        pool what is new, score, select, attend.  The pooled counts go from n_pooled to
+        a second array, and the two are swapped (the pooling scoring launch needs them
+        apart)."""
+        n_in, n_out = self._counts(None, None)
+        self.pool_score_select_fwd(n_in=n_in, n_out=n_out, stream=stream)
+        self.n_pooled, self.n_pooled_next = n_out, n_in
 
     # ------------------------------------------------------------------ readback
     def selections(self) -> list[np.ndarray]:
