@@ -807,6 +807,8 @@ def main() -> int:
         "timed_region": sec.get("timed_region"),
         "warm": sec.get("warm"),
         "kernel_avg_us": sec["kernel_avg_us"],
+        "select_from_list": sec.get("select_from_list"),
+        "tokens_decided_by_list": sec.get("tokens_decided_by_list"),
         "roofline": roofline,
     }
     if not args.no_forms:
