@@ -199,11 +199,11 @@ def algorithmic_bytes(case: datagen.Case, kv: str = "cache") -> dict:
 # ----------------------------------------------------------------------- timing
 
 def score_source_digest() -> str:
-    """sha256 over the score kernel's source and the device header it includes (the
+    """sha256 over the score kernel's source and the device headers it includes (the
     launch header holds host declarations only)."""
     import hashlib
     h = hashlib.sha256()
-    for f in ("score.hip", "sa_common.hpp"):
+    for f in ("score.hip", "sa_common.hpp", "select_wide.hpp"):
         h.update(open(os.path.join(ROOT, "indexer_top_block_amd", "csrc", f), "rb").read())
     return h.hexdigest()
 
