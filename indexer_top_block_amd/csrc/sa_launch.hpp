@@ -33,12 +33,13 @@ hipError_t launch_score(const sa_dims& d, const CacheArgs& c, const void* qidx, 
                         const int32_t* q_pos, int n_q, float* scores, int64_t scores_ld, hipStream_t stream);
 // sparse_attn_pool then sparse_attn_score, in one launch when the decode scoring
 // kernel applies (else the two launches).
-// cand (optional): the candidate list of the fused select (kCandKeep best blocks of
-// every kCandTile, select_wide.hpp), cand_ld words per query token; only the pooling
-// scoring launch writes it (pool_score_fused), else the call fails.
+// cand (optional): the candidate list of the fused select (the cand_keep <= kCandKeep
+// best blocks of every kCandTile, select_wide.hpp), cand_ld words per query token;
+// only the pooling scoring launch writes it (pool_score_fused), else the call fails.
 hipError_t launch_pool_score(const sa_dims& d, const CacheArgs& c, const int32_t* n_in, int32_t* n_out, int max_new,
                              const void* qidx, const int32_t* q_seq, const int32_t* q_pos, int n_q, float* scores,
-                             int64_t scores_ld, hipStream_t stream, uint32_t* cand = nullptr, int64_t cand_ld = 0);
+                             int64_t scores_ld, hipStream_t stream, uint32_t* cand = nullptr, int64_t cand_ld = 0,
+                             int cand_keep = 0, int cand_tpt = 0);
 bool pool_score_fused(const sa_dims& d, const CacheArgs& c, const void* qidx, int n_q, const int32_t* n_in,
                       const int32_t* n_out);
 
@@ -129,16 +130,21 @@ hipError_t launch_select_fwd(const sa_dims& d, const CacheArgs& c, const float* 
                              void* scratch, const FwdPlan& plan, hipStream_t stream, const uint32_t* cand = nullptr,
                              int64_t cand_ld = 0);
 
-// The candidate list's words per query token (0: rows these shapes never select
-// from one; select_fwd.hip) and its bytes for n_q tokens with the decided flags (0
-// when the list is never used: rows of more than 32768 blocks, or more query tokens
-// than the pooling scoring launch takes); it is the workspace's last part.
+// The candidate list (select_fwd.hip): the best blocks it keeps per 32-block tile (8,
+// or 4 for rows of 131073-262144 blocks; 0: no list), the tiles each select thread
+// reads (1 for rows of up to 32768 blocks, else 32 / keep), its words per query token, and
+// its bytes for n_q tokens with the decided flags (0 when the list is never used: rows
+// that are always dense or longer than 262144 blocks, or more query tokens than the
+// pooling scoring launch takes); it is the workspace's last part.
+int cand_keep(const sa_dims& d, int max_len);
+int cand_tpt(const sa_dims& d, int max_len);
 int64_t cand_words(const sa_dims& d, int max_len);
 size_t cand_bytes(const sa_dims& d, int n_q, int max_len);
 
 // sparse_attn_pool_score then sparse_attn_select_fwd; where the pooling scoring launch
-// and the one-workgroup fused select both apply and ws holds workspace_bytes, the
-// scoring launch also writes the candidate list and the select starts from it.
+// and a fused select both apply and ws holds workspace_bytes, the scoring launch also
+// writes the candidate list and the select starts from it (rows of up to 32768 blocks
+// in select_fwd_kernel, longer ones in list_fwd_kernel).
 hipError_t launch_pool_score_select_fwd(const sa_dims& d, const CacheArgs& c, const int32_t* n_in, int32_t* n_out,
                                         int max_new, const void* qidx, const int32_t* q_seq, const int32_t* q_pos,
                                         int n_q, float* scores, int64_t scores_ld, const void* q, float scale,

@@ -69,11 +69,14 @@ struct PoolArgs {
   int max_new;
   int pool_wgs, n_seq;                // pooling workgroups per sequence; sequences
   int gx;                             // scoring workgroups per query
-  // Optional (null: none): the candidate list of the selection (kCandKeep best blocks
-  // of each wave's kCandTile), `cand_ld` words per query token, tile w at kCandWords w.
-  // A wave past the row's blocks writes nothing.
+  // Optional (null: none): the candidate list of the selection, `cand_ld` words per
+  // query token: for each wave's kCandTile blocks (tile g) its cand_keep best keys,
+  // then their block indices, a record of cand_keep / 2 16-byte pieces laid out for
+  // the select's loads (cand_offset in select_wide.hpp: the workgroup's thread t reads
+  // its pieces q at q * kCandThreads + t).  A wave past the row's blocks writes nothing.
   uint32_t* cand;
   int64_t cand_ld;
+  int cand_keep, cand_tpt;
 };
 
 template <typename T, int MT, int D, bool POOL>
@@ -233,24 +236,26 @@ score_mfma_kernel(const T* __restrict__ qidx, const T* __restrict__ kpool, int64
   sum += __shfl_xor(sum, 32);
   if (hf == 0 && valid) scores[(int64_t)i * scores_ld + b] = sum + 0.0f;  // +0.0 turns -0.0 into +0.0
   if constexpr (POOL) {
-    if (pa.cand != nullptr && b_base / kCandTile < pa.cand_ld / kCandWords) {   // the tile's best blocks
+    if (pa.cand != nullptr && b_base / kCandTile < kCandThreads * pa.cand_tpt) {   // the tile's best blocks
       // lanes 0..31 hold the tile's blocks (lanes 32..63 the same sums)
       const uint64_t lo = 0xFFFFFFFFull;
       const uint32_t key = valid ? score_key(sum + 0.0f) : 0u;   // the selection's key of the stored score
-      uint32_t v = 0u;                               // the tile's kCandKeep-th largest key, bit by bit
+      const int keep = pa.cand_keep;
+      uint32_t v = 0u;                               // the tile's keep-th largest key, bit by bit
       for (int bit = 31; bit >= 0; --bit) {
         const uint32_t tv = v | (1u << bit);
-        if (__popcll(__ballot(key >= tv) & lo) >= kCandKeep) v = tv;
+        if (__popcll(__ballot(key >= tv) & lo) >= keep) v = tv;
       }
       const uint64_t below_me = (1ull << lane) - 1ull;
       const int n_above = __popcll(__ballot(key > v) & lo);
       const int eq_rank = __popcll(__ballot(key == v) & lo & below_me);
-      const bool take = hf == 0 && (key > v || (key == v && eq_rank < kCandKeep - n_above));
+      const bool take = hf == 0 && (key > v || (key == v && eq_rank < keep - n_above));
       const int slot = __popcll(__ballot(take) & below_me);
-      uint32_t* cw = pa.cand + (int64_t)i * pa.cand_ld + (int64_t)(b_base / kCandTile) * kCandWords;
-      if (take) {                                    // exactly kCandKeep lanes (blocks past the row: key 0)
-        cw[slot] = key;
-        cw[kCandKeep + slot] = (uint32_t)b;
+      uint32_t* cw = pa.cand + (int64_t)i * pa.cand_ld;
+      const int g = b_base / kCandTile;
+      if (take) {                                    // exactly keep lanes (blocks past the row: key 0)
+        cw[cand_offset(g, slot, keep, pa.cand_tpt)] = key;
+        cw[cand_offset(g, keep + slot, keep, pa.cand_tpt)] = (uint32_t)b;
       }
     }
   }
@@ -543,7 +548,7 @@ template <typename T, int MT, int D>
 static void launch_pool_score_t(const sa_dims& d, const CacheArgs& c, const int32_t* n_in, int32_t* n_out,
                                 int max_new, const void* qidx, const int32_t* q_seq, const int32_t* q_pos, int n_q,
                                 float* scores, int64_t scores_ld, uint32_t* cand, int64_t cand_ld,
-                                hipStream_t stream) {
+                                int cand_keep, int cand_tpt, hipStream_t stream) {
   const long long max_blocks = (long long)c.max_len / d.compress_ratio;
   const long long per_wg = kScoreWaves * kScoreTile;
   const long long gx = (max_blocks + per_wg - 1) / per_wg;
@@ -552,7 +557,7 @@ static void launch_pool_score_t(const sa_dims& d, const CacheArgs& c, const int3
   pool_wgs = pool_wgs < 1 ? 1 : (pool_wgs > 2048 ? 2048 : pool_wgs);
   const dim3 grid((unsigned)(pool_wgs * c.n_seq + gx * n_q));
   const PoolArgs<T> pa{(const T*)c.kidx, c.kidx_ld, (T*)c.kpool, c.seq_row0, n_in, n_out, max_new,
-                       (int)pool_wgs, c.n_seq, (int)gx, cand, cand_ld};
+                       (int)pool_wgs, c.n_seq, (int)gx, cand, cand_ld, cand_keep, cand_tpt};
   hipLaunchKernelGGL((score_mfma_kernel<T, MT, D, true>), grid, dim3(256), 0, stream, (const T*)qidx,
                      (const T*)c.kpool, c.kpool_ld, c.seq_blk0, c.seq_len, q_seq, q_pos, d.compress_ratio, scores,
                      scores_ld, pa);
@@ -603,11 +608,11 @@ template <typename T>
 static void dispatch_pool_score(const sa_dims& d, const CacheArgs& c, const int32_t* n_in, int32_t* n_out,
                                 int max_new, const void* qidx, const int32_t* q_seq, const int32_t* q_pos, int n_q,
                                 float* scores, int64_t scores_ld, uint32_t* cand, int64_t cand_ld,
-                                hipStream_t stream) {
+                                int cand_keep, int cand_tpt, hipStream_t stream) {
 #define SA_PS_CASE(MT_, D_)                                                                                        \
   if (d.h_idx / 32 == MT_ && d.d_idx == D_) {                                                                      \
     launch_pool_score_t<T, MT_, D_>(d, c, n_in, n_out, max_new, qidx, q_seq, q_pos, n_q, scores, scores_ld, cand, \
-                                    cand_ld, stream);                                                              \
+                                    cand_ld, cand_keep, cand_tpt, stream);                                         \
     return;                                                                                                        \
   }
   SA_PS_CASE(1, 64) SA_PS_CASE(1, 128) SA_PS_CASE(1, 256)
@@ -619,7 +624,11 @@ static void dispatch_pool_score(const sa_dims& d, const CacheArgs& c, const int3
 
 hipError_t launch_pool_score(const sa_dims& d, const CacheArgs& c, const int32_t* n_in, int32_t* n_out, int max_new,
                              const void* qidx, const int32_t* q_seq, const int32_t* q_pos, int n_q, float* scores,
-                             int64_t scores_ld, hipStream_t stream, uint32_t* cand, int64_t cand_ld) {
+                             int64_t scores_ld, hipStream_t stream, uint32_t* cand, int64_t cand_ld, int cand_keep,
+                             int cand_tpt) {
+  if (cand && (cand_keep % 4 != 0 || cand_keep > kCandKeep || cand_tpt < 1 ||
+               cand_ld < (int64_t)kCandThreads * cand_tpt * 2 * cand_keep))
+    return hipErrorInvalidValue;
   if (!pool_score_fused(d, c, qidx, n_q, n_in, n_out)) {
     if (cand) return hipErrorInvalidValue;           // candidates come only from the pooling scoring launch
     hipError_t err = launch_pool(d, c, n_in, n_out, max_new, stream);
@@ -628,10 +637,10 @@ hipError_t launch_pool_score(const sa_dims& d, const CacheArgs& c, const int32_t
   }
   if (d.dtype == SA_BF16)
     dispatch_pool_score<bf16>(d, c, n_in, n_out, max_new, qidx, q_seq, q_pos, n_q, scores, scores_ld, cand, cand_ld,
-                              stream);
+                              cand_keep, cand_tpt, stream);
   else
     dispatch_pool_score<f16>(d, c, n_in, n_out, max_new, qidx, q_seq, q_pos, n_q, scores, scores_ld, cand, cand_ld,
-                             stream);
+                             cand_keep, cand_tpt, stream);
   return hipGetLastError();
 }
 

@@ -27,6 +27,8 @@
 // that do not fit (more workgroups than compute units, shapes other than the MLA ones
 // with V inside K, lists longer than kFusedListMax, more chunks than the finishing
 // pass reads at once) take those two calls instead.
+#include <cmath>
+
 #include "fwd_lds.hpp"
 #include "select_chunk.hpp"
 #include "select_wide.hpp"
@@ -39,6 +41,7 @@ constexpr int kFusedListMax = 3072;          // list entries held in LDS (top_k 
 constexpr int kFusedMaxChunks = kSelThreads / 4;   // chunks whose counts the finishing pass reads at once
 constexpr int kCandMaxQueries = 63;         // query tokens of the pooling scoring launch
 static_assert(kSelThreads == kFusedThreads, "the finishing pass runs on the fused workgroup");
+static_assert(kCandThreads == kFusedThreads, "the list is laid out for the fused workgroup's loads");
 
 // The list the workgroup selected, in LDS: cnt entries (kept blocks, then the tail),
 // read clamped so that every lane reads valid memory.
@@ -61,63 +64,82 @@ union FusedSmem {
   FwdLdsSmem<T, DKQ, true> att;
 };
 
-// The select from the scoring launch's candidate list: thread t holds tile t's
-// kCandKeep keys and block indices (keys 0 past the row), counts them into the pass-1
-// histogram and runs the passes over them.  The result is the row's select exactly
-// when every block left out of the list falls below the cut: below the cut's bin when
-// the bin is taken whole, below the cut key T otherwise (a block equal to T, left
-// out, could be a tie the row's select takes).  Each tile's smallest listed key
-// bounds those it left out, so the largest of those bounds is compared with the cut
-// (false: the caller selects over the row).  The kept blocks of tile t are then
-// t's own candidates: each thread places them in the list from the counts of the
-// tiles before it (kept blocks, and the first k_rem tied blocks in index order).
-// Requires nb > k_blk and at least k_blk listed blocks; the histograms are clear on
-// entry and dirty on return.
-template <int NT, int KPT>
-__device__ __forceinline__ bool cand_select(const uint4 (&cv)[4], int nb, int c, int k_blk, WideSmem<NT, KPT>& sm,
-                                            int32_t* list) {
-  constexpr int COPIES = WideCfg<NT, KPT>::copies, WAVES = NT / kWave;
-  static_assert(kCandKeep == 8 && WideCfg<NT, KPT>::words >= WAVES && kWideBins >= 2 * WAVES, "LDS reuse");
+// The select from the scoring launch's candidate list: thread t holds tiles
+// [TPT t, TPT t + TPT), each tile's KEEP largest keys and their block indices (keys 0
+// past the row), counts the keys into the pass-1 histogram and runs the passes over
+// them.  The result is the row's select exactly when every block left out of the list
+// falls below the cut: below the cut's bin when the bin is taken whole, below the cut
+// key T otherwise (a block equal to T, left out, could be a tie the row's select
+// takes).  Each tile's smallest listed key bounds those it left out, so the largest
+// of those bounds is compared with the cut (false: the caller selects over the row).
+// The kept blocks of a tile are then its own candidates: each thread places its
+// tiles' kept blocks in the list from the counts of the tiles before it (kept blocks,
+// and the first k_rem tied blocks in index order).  Requires nb > k_blk and at least
+// k_blk listed blocks; the histograms are clear on entry and dirty on return.
+template <int NT, int KPT, int KEEP, int TPT>
+__device__ __forceinline__ bool cand_select(uint4 (&cv)[KEEP * TPT / 2], int nb, int c, int k_blk,
+                                            WideSmem<NT, KPT>& sm, int32_t* list) {
+  constexpr int COPIES = WideCfg<NT, KPT>::copies, WAVES = NT / kWave, KC = KEEP * TPT;
+  static_assert(KEEP % 4 == 0 && WideCfg<NT, KPT>::words >= WAVES && kWideBins >= 2 * WAVES,
+                "tile records in 16-byte pieces; LDS words reused for the wave totals");
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-  nb = min(nb, KPT * NT);                            // the launch guarantees nb fits; the list relies on it
-  const bool in_row = tid * kCandTile < nb;
-  const uint32_t key[kCandKeep] = {in_row ? cv[0].x : 0u, in_row ? cv[0].y : 0u, in_row ? cv[0].z : 0u,
-                                   in_row ? cv[0].w : 0u, in_row ? cv[1].x : 0u, in_row ? cv[1].y : 0u,
-                                   in_row ? cv[1].z : 0u, in_row ? cv[1].w : 0u};
-  const uint32_t idx[kCandKeep] = {cv[2].x, cv[2].y, cv[2].z, cv[2].w, cv[3].x, cv[3].y, cv[3].z, cv[3].w};
-  // blocks listed: kCandKeep per whole tile, all of a last tile shorter than that
-  const int n_listed = nb / kCandTile * kCandKeep + min(kCandKeep, nb % kCandTile);
+  nb = min(nb, NT * TPT * kCandTile);                // the launch guarantees nb fits; the list relies on it
+  // tile j: KEEP keys, then KEEP block indices; the keys of tiles past the row become
+  // 0 in place (no second copy of 32 keys in registers)
+  uint32_t* w = reinterpret_cast<uint32_t*>(cv);
+#pragma unroll
+  for (int j = 0; j < TPT; ++j) {
+    const bool in_row = (tid * TPT + j) * kCandTile < nb;
+#pragma unroll
+    for (int e = 0; e < KEEP; ++e) w[j * 2 * KEEP + e] = in_row ? w[j * 2 * KEEP + e] : 0u;
+  }
+  auto key = [&](int j) -> uint32_t { return w[(j / KEEP) * 2 * KEEP + j % KEEP]; };
+  // blocks listed: KEEP per whole tile, all of a last tile shorter than that
+  const int n_listed = nb / kCandTile * KEEP + min(KEEP, nb % kCandTile);
   {
     uint32_t* mine = sm.h1 + (lane & (COPIES - 1));
 #pragma unroll
-    for (int j = 0; j < kCandKeep; ++j) atomicAdd(&mine[(key[j] >> 22) * COPIES], 1u);
+    for (int j = 0; j < KC; ++j) atomicAdd(&mine[(key(j) >> 22) * COPIES], 1u);
   }
-  // the bound on the keys left out: per wave into keep[wave] (free until the list),
-  // ordered before its reads by the picks' barriers
-  uint32_t least = key[0];
+  // the bound on the keys left out (each tile's smallest listed key, the largest of
+  // them): per wave into keep[wave] (free until the list), ordered before its reads by
+  // the picks' barriers
+  uint32_t bound_out = 0u;
 #pragma unroll
-  for (int j = 1; j < kCandKeep; ++j) least = min(least, key[j]);
-  least = wave_max_u32(least);
-  if (lane == 0) sm.keep[wave] = least;
-  const WideCut cut = wide_cut<NT, KPT, kCandKeep>(key, k_blk, NT * kCandKeep - n_listed, sm);
+  for (int j = 0; j < TPT; ++j) {
+    uint32_t least = key(j * KEEP);
+#pragma unroll
+    for (int e = 1; e < KEEP; ++e) least = min(least, key(j * KEEP + e));
+    bound_out = max(bound_out, least);
+  }
+  bound_out = wave_max_u32(bound_out);
+  if (lane == 0) sm.keep[wave] = bound_out;
+  const WideCut cut = wide_cut<NT, KPT, KC>(key, k_blk, NT * KC - n_listed, sm);
   const uint32_t bound = cut.whole ? cut.prefix << cut.shift : cut.prefix;
   uint32_t left_out = 0u;
 #pragma unroll
-  for (int w = 0; w < WAVES; ++w) left_out = max(left_out, sm.keep[w]);
+  for (int v = 0; v < WAVES; ++v) left_out = max(left_out, sm.keep[v]);
   if (left_out >= bound) return false;               // (bound 0: never taken)
   // keep: key >= thr (thr > 0: bound > 0 here); tie: key == T (the cut inside a key)
   const uint32_t thr = cut.whole ? bound : bound + 1u;
   const bool full = !cut.whole && bound == 0xffffffffu;   // nothing above T
-  uint32_t kw = 0u, tw = 0u;
+  uint32_t kw[TPT], tw[TPT];
+  int kc = 0, tc = 0;
 #pragma unroll
-  for (int j = 0; j < kCandKeep; ++j) {
-    const uint32_t bit = 1u << (idx[j] % kCandTile);
-    if (!full && key[j] >= thr) kw |= bit;
-    if (!cut.whole && key[j] == bound) tw |= bit;
+  for (int j = 0; j < TPT; ++j) {
+    kw[j] = 0u;
+    tw[j] = 0u;
+#pragma unroll
+    for (int e = 0; e < KEEP; ++e) {
+      const uint32_t k = key(j * KEEP + e), bit = 1u << (w[j * 2 * KEEP + KEEP + e] % kCandTile);
+      kw[j] |= (!full && k >= thr) ? bit : 0u;
+      if (!cut.whole) tw[j] |= k == bound ? bit : 0u;
+    }
+    kc += __popc(kw[j]);
+    tc += __popc(tw[j]);
   }
-  // counts of the tiles before this one: wave scans, then the wave totals (in h2,
+  // counts of the tiles before this thread's: wave scans, then the wave totals (in h2,
   // free since the last pick)
-  const int kc = __popc(kw), tc = __popc(tw);
   const int k_incl = wave_inclusive_scan(kc, lane), t_incl = wave_inclusive_scan(tc, lane);
   if (lane == kWave - 1) {
     sm.h2[wave] = (uint32_t)k_incl;
@@ -129,25 +151,29 @@ __device__ __forceinline__ bool cand_select(const uint4 (&cv)[4], int nb, int c,
   const int k_before = (wave > 0 ? __builtin_amdgcn_readlane(wk_incl, wave - 1) : 0) + k_incl - kc;
   const int t_before = (wave > 0 ? __builtin_amdgcn_readlane(wt_incl, wave - 1) : 0) + t_incl - tc;
   int o = k_before + min(cut.k_rem, t_before);
-  uint32_t word = kw;
-  for (int take = min(tc, cut.k_rem - t_before); take > 0; --take) {   // the first tied blocks still wanted
-    word |= tw & (0u - tw);
-    tw &= tw - 1u;
-  }
-  const int32_t b0 = tid * kCandTile;
-  if (c == 4) {
-    while (word != 0u && o < k_blk) {                // o < k_blk always; the bound only guards memory
-      const int32_t p0 = (b0 + __ffs(word) - 1) * 4;
-      word &= word - 1u;
-      *(int4*)&list[o * 4] = int4{p0, p0 + 1, p0 + 2, p0 + 3};
-      ++o;
+  int want = cut.k_rem - t_before;                   // tied blocks still wanted at this thread's first tile
+#pragma unroll
+  for (int j = 0; j < TPT; ++j) {
+    uint32_t word = kw[j], t = tw[j];
+    for (; want > 0 && t != 0u; --want) {            // the first tied blocks still wanted, in index order
+      word |= t & (0u - t);
+      t &= t - 1u;
     }
-  } else {
-    while (word != 0u && o < k_blk) {
-      const int32_t p0 = (b0 + __ffs(word) - 1) * c;
-      word &= word - 1u;
-      for (int t = 0; t < c; ++t) list[o * c + t] = p0 + t;
-      ++o;
+    const int32_t b0 = (tid * TPT + j) * kCandTile;
+    if (c == 4) {
+      while (word != 0u && o < k_blk) {              // o < k_blk always; the bound only guards memory
+        const int32_t p0 = (b0 + __ffs(word) - 1) * 4;
+        word &= word - 1u;
+        *(int4*)&list[o * 4] = int4{p0, p0 + 1, p0 + 2, p0 + 3};
+        ++o;
+      }
+    } else {
+      while (word != 0u && o < k_blk) {
+        const int32_t p0 = (b0 + __ffs(word) - 1) * c;
+        word &= word - 1u;
+        for (int u = 0; u < c; ++u) list[o * c + u] = p0 + u;
+        ++o;
+      }
     }
   }
   __syncthreads();
@@ -155,8 +181,9 @@ __device__ __forceinline__ bool cand_select(const uint4 (&cv)[4], int nb, int c,
 }
 
 // CAND: the select starts from the scoring launch's candidate list (cand, cand_ld
-// words per query token) and takes the row only when the list cannot decide it;
-// decided[i] records which (1: the list).  Otherwise cand and decided are unused.
+// words per query token) for rows of at least cand_min_groups whole groups, and takes
+// the row when the list cannot decide it; decided[i] records which (1: the list).
+// Otherwise cand, cand_min_groups and decided are unused.
 template <typename T, int DKQ, int KPT, bool CAND>
 __global__ void __launch_bounds__(kFusedThreads, 1)
 select_fwd_kernel(const float* __restrict__ scores, int64_t scores_ld, const int32_t* __restrict__ seq_len,
@@ -165,7 +192,7 @@ select_fwd_kernel(const float* __restrict__ scores, int64_t scores_ld, const int
                   const T* __restrict__ k, int64_t k_ld, int64_t k_hs, const int64_t* __restrict__ seq_row0, int h_q,
                   int h_kv, float scale_log2, int n_split, int rows_per_split, float* __restrict__ out,
                   float* __restrict__ ws_o, float* __restrict__ ws_ml, const uint32_t* __restrict__ cand,
-                  int64_t cand_ld, uint32_t* __restrict__ decided) {
+                  int64_t cand_ld, int cand_min_groups, uint32_t* __restrict__ decided) {
   constexpr int NT = kFusedThreads, COPIES = WideCfg<NT, KPT>::copies;
   __shared__ FusedSmem<T, DKQ, KPT> sm;
   __shared__ int32_t list[kFusedListMax];
@@ -176,11 +203,10 @@ select_fwd_kernel(const float* __restrict__ scores, int64_t scores_ld, const int
   // the candidate list, this thread's tile of it instead (clamped to the last tile)
   float raw[KPT];
   uint4 cv[4];
-  if constexpr (CAND) {
-    const int tile = min(tid, (int)(cand_ld / kCandWords) - 1);
-    const uint4* src = (const uint4*)(cand + (int64_t)i * cand_ld + (int64_t)tile * kCandWords);
+  if constexpr (CAND) {                              // coalesced: piece q of thread t at q * kCandThreads + t
+    const uint4* src = (const uint4*)(cand + (int64_t)i * cand_ld) + tid;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) cv[j] = src[j];
+    for (int q = 0; q < 4; ++q) cv[q] = src[q * kCandThreads];
   } else {
     wide_load_row<NT, KPT>(row, scores_ld, raw);
   }
@@ -202,8 +228,9 @@ select_fwd_kernel(const float* __restrict__ scores, int64_t scores_ld, const int
     __syncthreads();                                 // the histograms are clear
     bool done = false;
     if constexpr (CAND) {
-      // the list must hold well over k_blk blocks for its cut to be likely exact
-      if (qr.nb / kCandTile * kCandKeep >= 2 * k_blk) done = cand_select<NT, KPT>(cv, qr.nb, c, k_blk, sm.sel, list);
+      // only rows of enough groups for the list to be likely to decide (cand_min_groups)
+      if (qr.nb / kCandTile >= cand_min_groups)
+        done = cand_select<NT, KPT, kCandKeep, 1>(cv, qr.nb, c, k_blk, sm.sel, list);
       if (!done) {                                   // the row's select: fresh histograms, the row's keys
         __syncthreads();
         for (int e = tid; e < kP1Bins * COPIES / 4; e += NT) ((uint4*)sm.sel.h1)[e] = uint4{0u, 0u, 0u, 0u};
@@ -225,6 +252,77 @@ select_fwd_kernel(const float* __restrict__ scores, int64_t scores_ld, const int
   __syncthreads();                                   // the list is whole; the select's LDS is free
   // Waves 4..15 are done (a barrier waits only for the waves still running).
   if (__builtin_amdgcn_readfirstlane(tid / kWave) >= 4) return;
+  const LdsList ls{list, cnt, meta};
+  fwd_lds_body<T, DKQ, true, LdsList, true>(sm.att, ls, q, k, k_ld, k_hs, seq_row0, seq_len, q_seq, q_pos, 0, h_q,
+                                            h_kv, scale_log2, n_split, rows_per_split, out, ws_o, ws_ml);
+}
+
+// Rows longer than one workgroup's registers hold (more than 32768 blocks), from the
+// scoring launch's list of the KEEP best of every 32 blocks (KEEP 8: rows of up to
+// 131072 blocks; 4: up to 262144), 32 listed keys per thread; where the list cannot
+// decide, the per-query select over the row (select_chunk.hpp) runs instead.
+template <typename T, int DKQ>
+union ListLongSmem {
+  WideSmem<kFusedThreads, kFusedMaxKpt> sel;
+  WgSmem one;                                        // the per-query select over the row
+  FwdLdsSmem<T, DKQ, true> att;
+};
+
+template <typename T, int DKQ, int KEEP>
+__global__ void __launch_bounds__(kFusedThreads, 1)
+list_fwd_kernel(const float* __restrict__ scores, int64_t scores_ld, const int32_t* __restrict__ seq_len,
+                const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos, int c, int k_blk,
+                int32_t* __restrict__ sel, int64_t sel_ld, int32_t* __restrict__ n_sel, const T* __restrict__ q,
+                const T* __restrict__ k, int64_t k_ld, int64_t k_hs, const int64_t* __restrict__ seq_row0, int h_q,
+                int h_kv, float scale_log2, int n_split, int rows_per_split, float* __restrict__ out,
+                float* __restrict__ ws_o, float* __restrict__ ws_ml, const uint32_t* __restrict__ cand,
+                int64_t cand_ld, int cand_min_groups, uint32_t* __restrict__ decided) {
+  constexpr int NT = kFusedThreads, KPT = kFusedMaxKpt, COPIES = WideCfg<NT, KPT>::copies;
+  constexpr int TPT = KPT / KEEP;                    // tiles per thread (32 listed keys)
+  __shared__ ListLongSmem<T, DKQ> sm;
+  __shared__ int32_t list[kFusedListMax];
+  const int i = blockIdx.y / h_kv, tid = threadIdx.x;
+  const bool writer = blockIdx.x == 0 && blockIdx.y % h_kv == 0;   // writes sel and n_sel of query i
+  // this thread's tiles of the list, coalesced: piece q of thread t at q * kCandThreads + t
+  uint4 cv[KEEP * TPT / 2];
+  {
+    const uint4* src = (const uint4*)(cand + (int64_t)i * cand_ld) + tid;
+#pragma unroll
+    for (int q = 0; q < KEEP * TPT / 2; ++q) cv[q] = src[q * kCandThreads];
+  }
+  const SeqMeta meta = seq_meta(q_seq, seq_len, seq_row0, nullptr, i);
+  const int n_vis = visible_tokens(meta.len, q_pos[i]);
+  const QueryRowInfo qr{n_vis / c, n_vis};
+  for (int e = tid; e < kP1Bins * COPIES / 4; e += NT) ((uint4*)sm.sel.h1)[e] = uint4{0u, 0u, 0u, 0u};
+  for (int e = tid; e < kWideBins; e += NT) sm.sel.h2[e] = 0u;
+  int32_t* gsel = sel + (int64_t)i * sel_ld;
+  int cnt;
+  if (qr.nb <= k_blk) {                              // dense: every visible position
+    cnt = qr.n_vis;
+    for (int j = tid; j < cnt; j += NT) list[j] = j;
+    if (writer) write_dense<NT>(gsel, sel_ld, qr.n_vis, n_sel + i);
+    if (writer && tid == 0) decided[i] = 0u;
+  } else {
+    __syncthreads();                                 // the histograms are clear
+    bool done = false;
+    if (qr.nb / kCandTile >= cand_min_groups)
+      done = cand_select<NT, KPT, KEEP, TPT>(cv, qr.nb, c, k_blk, sm.sel, list);
+    if (!done) {                                     // the row's select, streamed (rare)
+      __syncthreads();
+      select_one_query<NT, 8>(scores + (int64_t)i * scores_ld, qr.nb, c, k_blk, list, sm.one);
+      __syncthreads();
+    }
+    if (writer && tid == 0) decided[i] = done ? 1u : 0u;
+    const int body = k_blk * c, tail = qr.n_vis - qr.nb * c;
+    cnt = body + tail;
+    for (int j = tid; j < tail; j += NT) list[body + j] = qr.nb * c + j;
+    if (writer) {
+      for (int j = tid; j < body; j += NT) gsel[j] = list[j];
+      write_tail<NT>(gsel, sel_ld, qr.nb, qr.n_vis, c, k_blk, n_sel + i);
+    }
+  }
+  __syncthreads();                                   // the list is whole; the select's LDS is free
+  if (__builtin_amdgcn_readfirstlane(tid / kWave) >= 4) return;   // waves 4..15 are done
   const LdsList ls{list, cnt, meta};
   fwd_lds_body<T, DKQ, true, LdsList, true>(sm.att, ls, q, k, k_ld, k_hs, seq_row0, seq_len, q_seq, q_pos, 0, h_q,
                                             h_kv, scale_log2, n_split, rows_per_split, out, ws_o, ws_ml);
@@ -292,13 +390,19 @@ static bool alias_of(const CacheArgs& c) { return c.v == c.k && c.v_ld == c.k_ld
 
 enum class FusedForm { kTwoCalls, kWide, kChunked };
 
+// What every form with the selection inside the attention's launch needs: the MLA
+// shapes with V inside K, a list that fits LDS, one workgroup per compute unit.
+static bool fused_base(const sa_dims& d, const CacheArgs& c, const void* q, int n_q, const FwdPlan& plan) {
+  if (n_q < 1 || !fwd_uses_mfma(d, c, q) || !alias_of(c)) return false;
+  if (d.d_v != 512 || (d.d_kq != 576 && d.d_kq != 512)) return false;
+  if ((long long)d.top_k + d.compress_ratio - 1 > kFusedListMax) return false;
+  const int cus = device_cus();
+  return cus > 0 && (long long)plan.n_split * n_q * d.h_kv <= cus;   // one per CU
+}
+
 static FusedForm fused_form(const sa_dims& d, const CacheArgs& c, const void* q, int n_q, const FwdPlan& plan,
                             size_t ws_bytes) {
-  if (n_q < 1 || !fwd_uses_mfma(d, c, q) || !alias_of(c)) return FusedForm::kTwoCalls;
-  if (d.d_v != 512 || (d.d_kq != 576 && d.d_kq != 512)) return FusedForm::kTwoCalls;
-  if ((long long)d.top_k + d.compress_ratio - 1 > kFusedListMax) return FusedForm::kTwoCalls;
-  const int cus = device_cus();
-  if (cus <= 0 || (long long)plan.n_split * n_q * d.h_kv > cus) return FusedForm::kTwoCalls;   // one per CU
+  if (!fused_base(d, c, q, n_q, plan)) return FusedForm::kTwoCalls;
   const long long max_blocks = (long long)c.max_len / d.compress_ratio;
   if (max_blocks <= (long long)kFusedThreads * kFusedMaxKpt) return FusedForm::kWide;
   if (!select_chunked(d, n_q, c.max_len) || select_chunk_count(d, c.max_len) > kFusedMaxChunks)
@@ -315,14 +419,61 @@ bool select_fwd_fused(const sa_dims& d, const CacheArgs& c, const void* q, int n
   return fused_form(d, c, q, n_q, plan, ws_bytes) != FusedForm::kTwoCalls;
 }
 
-int64_t cand_words(const sa_dims& d, int max_len) {
-  const long long max_blocks = (long long)max_len / d.compress_ratio;
-  if (max_blocks <= d.top_k / d.compress_ratio || max_blocks > (long long)kFusedThreads * kFusedMaxKpt) return 0;
-  return (max_blocks + kCandTile - 1) / kCandTile * kCandWords;
+// P(X >= k) for X ~ Poisson(lam).
+static double poisson_tail(double lam, int k) {
+  double term = std::exp(-lam), below = 0.0;
+  for (int j = 0; j < k; ++j) {
+    below += term;
+    term *= lam / (j + 1);
+  }
+  return below >= 1.0 ? 0.0 : 1.0 - below;
 }
 
-// The tiles of n_q tokens, then one decided flag per token; cand_words is a multiple
-// of kCandWords, so n_q * cand_words + n_q words end on the part's last word.
+// The candidate list's best blocks per 32-block tile for rows of max_len tokens: the
+// larger of 8 and 4 for which the list holds at most 32768 keys (one workgroup's) and
+// a row of independent scores would rarely hold more than that many kept blocks in
+// some tile (fewer than 1 row in 10 falls back to its row select: the list's attempt
+// costs about twice what it saves); 0: no list (also for rows that are always dense).
+int cand_keep(const sa_dims& d, int max_len) {
+  const long long max_blocks = (long long)max_len / d.compress_ratio, k_blk = d.top_k / d.compress_ratio;
+  if (max_blocks <= k_blk) return 0;
+  const long long tiles = (max_blocks + kCandTile - 1) / kCandTile;
+  const long long cap = (long long)kFusedThreads * kFusedMaxKpt;   // listed keys one workgroup holds
+  for (int keep = kCandKeep; keep >= kCandKeep / 2; keep /= 2)
+    if (tiles * keep <= cap && (double)tiles * poisson_tail((double)k_blk / tiles, keep + 1) < 0.1) return keep;
+  return 0;
+}
+
+// The fewest whole groups a token's row must have for the list to be tried: with
+// fewer, a row of independent scores would fall back once in 10 or more (the same
+// rule as cand_keep's, for the token's own row), and the list would hold less than
+// twice the cut.  The fallback rate falls as the groups grow past k_blk / keep.
+static int cand_min_groups(const sa_dims& d, int keep) {
+  const long long k_blk = d.top_k / d.compress_ratio, cap = (long long)kFusedThreads * kFusedMaxKpt / keep;
+  auto ok = [&](long long g) { return (double)g * poisson_tail((double)k_blk / g, keep + 1) < 0.1; };
+  long long lo = std::max(1LL, (2 * k_blk + keep - 1) / keep), hi = cap;
+  if (lo > hi || !ok(hi)) return (int)(cap + 1);
+  while (lo < hi) {
+    const long long mid = (lo + hi) / 2;
+    if (ok(mid)) hi = mid;
+    else lo = mid + 1;
+  }
+  return (int)lo;
+}
+
+int cand_tpt(const sa_dims& d, int max_len) {
+  const int keep = cand_keep(d, max_len);
+  if (keep == 0) return 0;
+  return (long long)max_len / d.compress_ratio <= (long long)kFusedThreads * kFusedMaxKpt ? 1 : kFusedMaxKpt / keep;
+}
+
+// Room for kCandThreads * tpt tiles: every reader's load is in bounds.
+int64_t cand_words(const sa_dims& d, int max_len) {
+  return (int64_t)kCandThreads * cand_tpt(d, max_len) * 2 * cand_keep(d, max_len);
+}
+
+// The tiles of n_q tokens, then one decided flag per token (n_q * cand_words + n_q
+// words).
 size_t cand_bytes(const sa_dims& d, int n_q, int max_len) {
   if (n_q < 1 || n_q > kCandMaxQueries) return 0;
   const size_t words = (size_t)n_q * cand_words(d, max_len);
@@ -340,7 +491,8 @@ static void launch_fused_t(const sa_dims& d, const CacheArgs& c, const float* sc
   hipLaunchKernelGGL((select_fwd_kernel<T, DKQ, KPT, CAND>), grid, dim3(kFusedThreads), 0, stream, scores,
                      scores_ld, c.seq_len, q_seq, q_pos, d.compress_ratio, d.top_k / d.compress_ratio, sel, sel_ld,
                      n_sel, (const T*)q, (const T*)c.k, c.k_ld, c.k_hs, c.seq_row0, d.h_q, d.h_kv, scale_log2,
-                     plan.n_split, plan.rows_per_split, out, ws_o, ws_ml, cand, cand_ld, decided);
+                     plan.n_split, plan.rows_per_split, out, ws_o, ws_ml, cand, cand_ld,
+                     cand ? cand_min_groups(d, kCandKeep) : 0, decided);
 }
 
 template <typename T, int DKQ>
@@ -425,10 +577,42 @@ hipError_t launch_select_fwd(const sa_dims& d, const CacheArgs& c, const float* 
   return launch_combine(d, n_q, out, ws_o, ws_ml, plan, stream);
 }
 
+enum class StepForm { kNoList, kListWide, kListLong };
+
+// The form of pool + score + select + attention: with the candidate list where the
+// pooling scoring launch and a fused select both apply and the workspace has the list's
+// room; rows of up to 32768 blocks in the one-workgroup kernel, longer ones in
+// list_fwd_kernel.
+static StepForm step_form(const sa_dims& d, const CacheArgs& c, const void* qidx, const void* q, int n_q,
+                          const int32_t* n_in, const int32_t* n_out, const FwdPlan& plan, size_t ws_bytes) {
+  if (cand_bytes(d, n_q, c.max_len) == 0 || ws_bytes < workspace_bytes(d, n_q, c.max_len)) return StepForm::kNoList;
+  if (!pool_score_fused(d, c, qidx, n_q, n_in, n_out) || !fused_base(d, c, q, n_q, plan)) return StepForm::kNoList;
+  const long long max_blocks = (long long)c.max_len / d.compress_ratio;
+  return max_blocks <= (long long)kFusedThreads * kFusedMaxKpt ? StepForm::kListWide : StepForm::kListLong;
+}
+
 bool step_uses_cand(const sa_dims& d, const CacheArgs& c, const void* qidx, const void* q, int n_q,
                     const int32_t* n_in, const int32_t* n_out, const FwdPlan& plan, size_t ws_bytes) {
-  return cand_bytes(d, n_q, c.max_len) > 0 && ws_bytes >= workspace_bytes(d, n_q, c.max_len) &&
-         pool_score_fused(d, c, qidx, n_q, n_in, n_out) && fused_form(d, c, q, n_q, plan, ws_bytes) == FusedForm::kWide;
+  return step_form(d, c, qidx, q, n_q, n_in, n_out, plan, ws_bytes) != StepForm::kNoList;
+}
+
+template <typename T, int DKQ>
+static void launch_list_long_t(const sa_dims& d, const CacheArgs& c, const float* scores, int64_t scores_ld,
+                               const int32_t* q_seq, const int32_t* q_pos, int n_q, int32_t* sel, int64_t sel_ld,
+                               int32_t* n_sel, const void* q, float scale_log2, float* out, float* ws_o, float* ws_ml,
+                               const uint32_t* cand, int64_t cand_ld, int keep, const FwdPlan& plan,
+                               hipStream_t stream) {
+  const dim3 grid(plan.n_split, n_q * d.h_kv);
+  uint32_t* decided = (uint32_t*)(cand + (int64_t)n_q * cand_ld);
+#define SA_LIST_LONG(KEEP_)                                                                                          \
+  hipLaunchKernelGGL((list_fwd_kernel<T, DKQ, KEEP_>), grid, dim3(kFusedThreads), 0, stream, scores, scores_ld,      \
+                     c.seq_len, q_seq, q_pos, d.compress_ratio, d.top_k / d.compress_ratio, sel, sel_ld, n_sel,     \
+                     (const T*)q, (const T*)c.k, c.k_ld, c.k_hs, c.seq_row0, d.h_q, d.h_kv, scale_log2,            \
+                     plan.n_split, plan.rows_per_split, out, ws_o, ws_ml, cand, cand_ld, min_groups, decided)
+  const int min_groups = cand_min_groups(d, keep);
+  if (keep == kCandKeep) SA_LIST_LONG(kCandKeep);
+  else SA_LIST_LONG(kCandKeep / 2);
+#undef SA_LIST_LONG
 }
 
 hipError_t launch_pool_score_select_fwd(const sa_dims& d, const CacheArgs& c, const int32_t* n_in, int32_t* n_out,
@@ -436,19 +620,41 @@ hipError_t launch_pool_score_select_fwd(const sa_dims& d, const CacheArgs& c, co
                                         int n_q, float* scores, int64_t scores_ld, const void* q, float scale,
                                         int32_t* sel, int64_t sel_ld, int32_t* n_sel, float* out, void* ws,
                                         size_t ws_bytes, void* scratch, const FwdPlan& plan, hipStream_t stream) {
-  uint32_t* cand = nullptr;
-  int64_t cand_ld = 0;
-  if (ws && step_uses_cand(d, c, qidx, q, n_q, n_in, n_out, plan, ws_bytes)) {
-    // the workspace's last part (after the partials, which the select's launch writes)
-    const size_t need = workspace_bytes(d, n_q, c.max_len);
-    cand = (uint32_t*)((char*)ws + need - cand_bytes(d, n_q, c.max_len));
-    cand_ld = cand_words(d, c.max_len);
+  const StepForm form = ws ? step_form(d, c, qidx, q, n_q, n_in, n_out, plan, ws_bytes) : StepForm::kNoList;
+  if (form == StepForm::kNoList) {
+    hipError_t err = launch_pool_score(d, c, n_in, n_out, max_new, qidx, q_seq, q_pos, n_q, scores, scores_ld, stream);
+    if (err != hipSuccess) return err;
+    return launch_select_fwd(d, c, scores, scores_ld, q_seq, q_pos, n_q, sel, sel_ld, n_sel, q, scale, out, ws,
+                             ws_bytes, scratch, plan, stream);
   }
+  // the list: the workspace's last part (after the partials, which the select's launch writes)
+  const size_t need = workspace_bytes(d, n_q, c.max_len);
+  uint32_t* cand = (uint32_t*)((char*)ws + need - cand_bytes(d, n_q, c.max_len));
+  const int64_t cand_ld = cand_words(d, c.max_len);
+  const int keep = cand_keep(d, c.max_len);
   hipError_t err = launch_pool_score(d, c, n_in, n_out, max_new, qidx, q_seq, q_pos, n_q, scores, scores_ld, stream,
-                                     cand, cand_ld);
+                                     cand, cand_ld, keep, cand_tpt(d, c.max_len));
   if (err != hipSuccess) return err;
-  return launch_select_fwd(d, c, scores, scores_ld, q_seq, q_pos, n_q, sel, sel_ld, n_sel, q, scale, out, ws,
-                           ws_bytes, scratch, plan, stream, cand, cand_ld);
+  if (form == StepForm::kListWide)
+    return launch_select_fwd(d, c, scores, scores_ld, q_seq, q_pos, n_q, sel, sel_ld, n_sel, q, scale, out, ws,
+                             ws_bytes, scratch, plan, stream, cand, cand_ld);
+  const float scale_log2 = scale * kLog2e;
+  float* ws_o = (float*)scratch;
+  float* ws_ml = plan.n_split > 1 ? ws_o + (size_t)n_q * d.h_q * plan.n_split * d.d_v : nullptr;
+#define SA_LL(T_, DKQ_)                                                                                         \
+  launch_list_long_t<T_, DKQ_>(d, c, scores, scores_ld, q_seq, q_pos, n_q, sel, sel_ld, n_sel, q, scale_log2, out, \
+                               ws_o, ws_ml, cand, cand_ld, keep, plan, stream)
+  if (d.dtype == SA_BF16) {
+    if (d.d_kq == 576) SA_LL(bf16, 576);
+    else SA_LL(bf16, 512);
+  } else {
+    if (d.d_kq == 576) SA_LL(f16, 576);
+    else SA_LL(f16, 512);
+  }
+#undef SA_LL
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  return launch_combine(d, n_q, out, ws_o, ws_ml, plan, stream);
 }
 
 }  // namespace sa

@@ -98,11 +98,22 @@ struct alignas(16) WideSmem {
 };
 
 // The scoring launch's candidate list (optional): for each tile of kCandTile
-// consecutive blocks of a query's row, the kCandKeep largest keys (ties to the lower
-// block; key 0 in the slots of a tile with fewer blocks) and then their block
-// indices, kCandWords words per tile.  Every block outside a tile's list scores at
-// most the smallest key in it.
-constexpr int kCandTile = 32, kCandKeep = 8, kCandWords = 2 * kCandKeep;
+// consecutive blocks of a query's row, its keep (kCandKeep or kCandKeep / 2) largest
+// keys (ties to the lower block; key 0 in the slots of a tile with fewer blocks) and
+// then their block indices.  Every block outside a tile's list scores at most the
+// smallest key in it.
+constexpr int kCandTile = 32, kCandKeep = 8;
+constexpr int kCandThreads = 1024;                   // threads of the workgroup that reads the list
+
+// Word offset in a token's list of word r (keys 0..keep-1, then the indices) of tile
+// g's record, for a reader whose thread t holds tiles [tpt t, tpt t + tpt): thread
+// t's 16-byte piece q (piece r / 4 of tile tpt t + j, whose record is keep / 2 pieces,
+// is q = j keep / 2 + r / 4) sits at q * kCandThreads + t, so that each of the
+// reader's loads is one contiguous run across its lanes.
+__host__ __device__ __forceinline__ int64_t cand_offset(int g, int r, int keep, int tpt) {
+  const int t = g / tpt, q = (g % tpt) * (keep / 2) + r / 4;
+  return ((int64_t)q * kCandThreads + t) * 4 + r % 4;
+}
 
 // Maximum / minimum over the wave by DPP and permlane exchanges, the same value in
 // every lane (lane ^ 1, lane ^ 2, the mirror in 8, lane ^ 8, then the 16- and 32-lane
@@ -231,8 +242,8 @@ __device__ __forceinline__ void wide_load_row(const float* __restrict__ row, int
 }
 
 // The cut of a radix select after its first pass has counted every key (keys in
-// registers, KC per thread; each key's top 10 bits added into the pass-1 histogram
-// h1 laid out [bin][copy]): the first pick, then the 11-bit passes 2 and 3 among
+// registers, KC per thread, key(j) the j-th; each key's top 10 bits added into the
+// pass-1 histogram h1 laid out [bin][copy]): the first pick, then the 11-bit passes 2 and 3 among
 // the keys still in the running, stopping once a pass's bin is taken whole.  Returns
 // the prefix of the k_blk-th largest key at `shift` (the kept keys are those >=
 // prefix << shift when whole; else shift is 0, prefix is that key T, and k_rem keys
@@ -243,8 +254,8 @@ struct WideCut {
   bool whole;
   int k_rem;
 };
-template <int NT, int KPT, int KC>
-__device__ __forceinline__ WideCut wide_cut(const uint32_t (&key)[KC], int k_blk, int n_pad, WideSmem<NT, KPT>& sm) {
+template <int NT, int KPT, int KC, typename KeyOf>
+__device__ __forceinline__ WideCut wide_cut(const KeyOf& key, int k_blk, int n_pad, WideSmem<NT, KPT>& sm) {
   constexpr int COPIES = WideCfg<NT, KPT>::copies;
   constexpr int PER1 = kP1Bins / NT, PER2 = kWideBins / NT;
   const int tid = threadIdx.x;
@@ -281,7 +292,7 @@ __device__ __forceinline__ WideCut wide_cut(const uint32_t (&key)[KC], int k_blk
     asm volatile("" : "+v"(one));                    // one register for every add, not one per key
 #pragma unroll
     for (int j = 0; j < KC; ++j)
-      if (key[j] - lo < (1u << 22)) atomicAdd(&sm.h2[(key[j] >> 11) & (kWideBins - 1)], one);
+      if (key(j) - lo < (1u << 22)) atomicAdd(&sm.h2[(key(j) >> 11) & (kWideBins - 1)], one);
     __syncthreads();
     uint32_t cnt[PER2];
 #pragma unroll
@@ -296,7 +307,7 @@ __device__ __forceinline__ WideCut wide_cut(const uint32_t (&key)[KC], int k_blk
       const uint32_t lo3 = prefix << 11;
 #pragma unroll
       for (int j = 0; j < KC; ++j)
-        if (key[j] - lo3 < (1u << 11)) atomicAdd(&sm.h1[key[j] & 2047u], 1u);
+        if (key(j) - lo3 < (1u << 11)) atomicAdd(&sm.h1[key(j) & 2047u], 1u);
       __syncthreads();
       uint32_t cnt3[PER2];
 #pragma unroll
@@ -405,7 +416,7 @@ __device__ __forceinline__ void wide_select_rows(const float (&raw)[KPT], int nb
       }
     }
   }
-  const WideCut cut = wide_cut<NT, KPT, KPT>(key, k_blk, n_pad, sm);
+  const WideCut cut = wide_cut<NT, KPT, KPT>([&](int j) { return key[j]; }, k_blk, n_pad, sm);
   const uint32_t prefix = cut.prefix;
   const int shift = cut.shift, k_rem = cut.k_rem;
   const bool whole = cut.whole;

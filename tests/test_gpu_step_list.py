@@ -20,7 +20,36 @@ from indexer_top_block_amd.device import DeviceLayer
 
 pytestmark = pytest.mark.gpu
 
-GROUP, KEEP = 32, 8           # blocks per group of the list, and the best of each it keeps
+GROUP = 32                    # blocks per group of the list
+LIST_CAP = 32768              # listed keys one workgroup holds
+READERS = 1024                # threads of the workgroup that reads the list
+
+
+def record_word(g: int, r: int, keep: int, tpt: int) -> int:
+    """Where word r of group g's record lies in a token's list: the reading thread t
+    holds groups [tpt t, tpt t + tpt), and its 16-byte piece q (group j of its own,
+    word r: q = j keep / 2 + r / 4) sits at q * READERS + t."""
+    t, q = g // tpt, (g % tpt) * (keep // 2) + r // 4
+    return (q * READERS + t) * 4 + r % 4
+
+
+def poisson_tail(lam: float, k: int) -> float:
+    """P(X >= k) for X ~ Poisson(lam)."""
+    return float(1.0 - sum(math.exp(-lam) * lam ** j / math.factorial(j) for j in range(k)))
+
+
+def keep_of(max_blocks: int, k_blk: int) -> int:
+    """The best blocks the list keeps per group: the larger of 8 and 4 for which the
+    list holds at most 32768 keys and a row of independent scores would fall back to
+    its row select less than once in 10 (some group holding more kept blocks than
+    that); else none (and none for rows that are always dense)."""
+    groups = -(-max_blocks // GROUP)
+    if max_blocks <= k_blk:
+        return 0
+    for keep in (8, 4):
+        if groups * keep <= LIST_CAP and groups * poisson_tail(k_blk / groups, keep + 1) < 0.1:
+            return keep
+    return 0
 
 
 def say(msg):
@@ -44,14 +73,15 @@ def order_keys(scores: np.ndarray) -> np.ndarray:
     return np.where(u >> 31 == 1, ~u, u | np.uint32(0x80000000)).astype(np.uint32)
 
 
-def expected_lists(keys: np.ndarray, nb: int):
-    """[groups, 16] per group g with 32 g < nb: its 8 best blocks by (key descending,
-    index ascending), listed by index (blocks past nb count as key 0)."""
+def expected_lists(keys: np.ndarray, nb: int, keep: int):
+    """Per group g with 32 g < nb: its `keep` best blocks by (key descending, index
+    ascending), their keys then their indices, listed by index (blocks past nb count
+    as key 0)."""
     out = {}
     for g in range((nb + GROUP - 1) // GROUP):
         b = np.arange(g * GROUP, g * GROUP + GROUP)
         k = np.where(b < nb, keys[np.minimum(b, nb - 1)], 0).astype(np.int64)
-        best = np.lexsort((b, -k))[:KEEP]
+        best = np.lexsort((b, -k))[:keep]
         take = np.sort(best)
         out[g] = np.concatenate([k[take], b[take]]).astype(np.uint32)
     return out
@@ -75,15 +105,26 @@ def radix_bound(listed: np.ndarray, k: int) -> int:
     return prefix
 
 
-def expected_decided(keys: np.ndarray, nb: int, k_blk: int) -> int:
-    if nb <= k_blk or nb // GROUP * KEEP < 2 * k_blk:
+def min_groups(k_blk: int, keep: int) -> int:
+    """The fewest whole groups a token's row needs for the list to be tried: the
+    smallest g >= 2 k_blk / keep with g P(Poisson(k_blk / g) > keep) < 0.1 (the same
+    rule as keep_of's, for the token's own row)."""
+    cap = LIST_CAP // keep
+    g = max(1, -(-2 * k_blk // keep))
+    while g <= cap and g * poisson_tail(k_blk / g, keep + 1) >= 0.1:
+        g += 1
+    return g
+
+
+def expected_decided(keys: np.ndarray, nb: int, k_blk: int, keep: int) -> int:
+    if nb <= k_blk or nb // GROUP < min_groups(k_blk, keep):
         return 0
-    lists = expected_lists(keys, nb)
-    listed = np.concatenate([v[:KEEP] for v in lists.values()])
-    n_listed = nb // GROUP * KEEP + min(KEEP, nb % GROUP)
+    lists = expected_lists(keys, nb, keep)
+    listed = np.concatenate([v[:keep] for v in lists.values()])
+    n_listed = nb // GROUP * keep + min(keep, nb % GROUP)
     listed = np.sort(listed)[::-1][:n_listed]
     bound = radix_bound(listed, k_blk)
-    return int(all(int(v[:KEEP].min()) < bound for v in lists.values()))
+    return int(all(int(v[:keep].min()) < bound for v in lists.values()))
 
 
 def _run(layer, fused_step: bool):
@@ -120,7 +161,9 @@ def _check(case, expect_list, expect_decided=None, oracle_queries=()):
         assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"{case.name}: {name} differs"
     if expect_list:
         ws = layer.ws.cpu().numpy()
-        words = -(-(layer.max_len // c) // GROUP) * 16
+        keep = keep_of(layer.max_len // c, k_blk)
+        tpt = 1 if layer.max_len // c <= LIST_CAP else 32 // keep      # groups per reading thread
+        words = READERS * tpt * 2 * keep
         end = layer.ws_bytes
         flags = ws[end - 4 * case.n_q: end].view(np.int32)
         lists = ws[end - 4 * case.n_q * (words + 1): end - 4 * case.n_q].view(np.uint32).reshape(case.n_q, words)
@@ -130,10 +173,11 @@ def _check(case, expect_list, expect_decided=None, oracle_queries=()):
             n_vis = oracle.visible_tokens(int(case.seq_len[case.q_seq[i]]), int(case.q_pos[i]))
             nb = n_vis // c
             keys = order_keys(scores[i, :nb])
-            want = expected_decided(keys, nb, k_blk)
-            if nb > k_blk and nb // GROUP * KEEP >= 2 * k_blk:
-                for g, v in expected_lists(keys, nb).items():
-                    assert np.array_equal(lists[i, 16 * g: 16 * g + 16], v), f"{case.name} q{i} group {g}"
+            want = expected_decided(keys, nb, k_blk, keep)
+            if nb > k_blk and nb // GROUP >= min_groups(k_blk, keep):
+                for g, v in expected_lists(keys, nb, keep).items():
+                    rec = lists[i, [record_word(g, r, keep, tpt) for r in range(2 * keep)]]
+                    assert np.array_equal(rec, v), f"{case.name} q{i} group {g}"
             assert int(flags[i]) == want, f"{case.name} q{i}: decided {flags[i]}, expected {want}"
             got_decided.append(int(flags[i]))
         if expect_decided is not None:
@@ -160,11 +204,12 @@ def test_step_list_decode_128k(gpu_lib):
 
 def test_step_list_mixed_tokens(gpu_lib):
     # six tokens of one 40000-token sequence (10000 blocks: a last group of 16 blocks):
-    # long rows the list decides (one with a 2-position tail), a row whose list would
-    # hold fewer than twice the cut (its row select), the dense case at the threshold,
-    # one visible position and none
+    # long rows the list decides (one with a 2-position tail), a row of too few groups
+    # for the list to be tried (2000 blocks: its row select), the dense case at the
+    # threshold, one visible position and none
     d = _dims()
-    q_pos = [39999, 30001, 8000, 2050, 0, -1]
+    assert min_groups(512, 8) == 237
+    q_pos = [39999, 35001, 8000, 2050, 0, -1]
     case = _case("step_list_mixed", d, [40000], [0] * len(q_pos), q_pos, 980)
     _check(case, expect_list=True, expect_decided=[1, 1, 0, 0, 0, 0], oracle_queries=[0, 1, 2, 3])
 
@@ -207,11 +252,37 @@ def test_step_list_falls_back_to_the_row(gpu_lib):
     _check(case, expect_list=True, expect_decided=[1], oracle_queries=[0])
 
 
-def test_step_list_not_used(gpu_lib):
-    # rows longer than 32768 blocks (the chunked selection) and eight tokens of 33
-    # splits (more workgroups than compute units): the two calls, unchanged
+def test_step_list_long_rows(gpu_lib):
+    # rows longer than one workgroup's registers (list_fwd_kernel): token level over
+    # 40 000 positions (1250 groups, 8 listed each: 10 000 keys) with whole, ragged and
+    # dense-at-the-threshold rows; and a crowded group in a 40 000-position row, where
+    # the per-query select over the row runs inside the launch (4 listed per group:
+    # the 1M decode below)
     d = _dims(compress_ratio=1)
-    _check(_case("step_list_chunked_row", d, [40000], [0], [39999], 986), expect_list=False, oracle_queries=[0])
+    assert keep_of(40000, 2048) == 8 and keep_of(262144, 512) == 4
+    q_pos = [39999, 31234, 2047]              # 1250 groups; 976 (fewer than the 1178 the list needs); dense
+    _check(_case("step_list_token_level_long", d, [40000], [0] * 3, q_pos, 990), expect_list=True,
+           expect_decided=[1, 0, 0], oracle_queries=[0, 1, 2])
+    case = _case("step_list_long_crowded", d, [40000], [0], [39999], 992)
+    tok = slice(int(case.row0[0]) + 64, int(case.row0[0]) + 96)
+    case.kidx[tok] = case.kidx[tok] * np.float32(8.0)
+    _check(case, expect_list=True, expect_decided=[0], oracle_queries=[0])
+
+
+def test_step_list_decode_1m(gpu_lib):
+    # the 1M-context decode workload (262 144 blocks, 1% planted): 8192 groups, 4 listed each
+    case = datagen.make_workload(5, q_std=2.0 * math.sqrt(576))
+    _check(case, expect_list=True, expect_decided=[1], oracle_queries=[0])
+
+
+def test_step_list_not_used(gpu_lib):
+    # token level over 140 000 positions (4375 groups: 8 listed each would exceed 32768
+    # keys, and with 4 a row of independent scores would fall back about every other
+    # time), a row of 5000 blocks for a cut of 512 (too few groups for the list), and
+    # eight tokens of 33 splits (more workgroups than compute units): the two calls
+    d = _dims(compress_ratio=1)
+    assert keep_of(140032, 2048) == 0 and keep_of(5000, 512) == 0
+    _check(_case("step_list_chunked_row", d, [140000], [0], [139999], 986), expect_list=False)
     d = _dims()
     q_pos = [19999 - 997 * j for j in range(8)]
     _check(_case("step_list_eight_tokens", d, [20000], [0] * 8, q_pos, 987), expect_list=False,

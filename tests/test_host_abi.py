@@ -76,14 +76,17 @@ def test_workspace_bytes():
     assert f"#define SA_WS_STATE_BYTES ((size_t){sa.WS_STATE_BYTES})" in hdr
     partials_1 = 33 * 16 * (512 + 2) * 4            # one decode token: 33 splits of (o, m, l) for 16 heads
     # the candidate list of the pool + score + select call, after the partials on a
-    # 256-byte boundary: 16 words per 32 blocks of each token's row, then one flag per token
+    # 256-byte boundary: room for 1024 records of 16 words (rows of up to 32768 blocks) or
+    # 8192 of 8 (4 listed per group, longer rows) per token, then one flag per token
     def after(n):
         return (n + 255) // 256 * 256
 
-    # short rows: state region + split-KV partials (+ the list: rows of at most
-    # k_blk = 512 blocks are always dense and have none)
+    # short rows: state region + split-KV partials (no list: rows of at most k_blk = 512
+    # blocks are always dense, and 32 groups of 1024 blocks are too few for a cut of 512)
     assert sa.sparse_attn_workspace_bytes(d, 1, 2048) == sa.WS_STATE_BYTES + partials_1
-    assert sa.sparse_attn_workspace_bytes(d, 1, 4096) == after(sa.WS_STATE_BYTES + partials_1) + (32 * 16 + 1) * 4
+    assert sa.sparse_attn_workspace_bytes(d, 1, 4096) == sa.WS_STATE_BYTES + partials_1
+    # 40 000 tokens (10 000 blocks: 8 listed per group, room for 1024 groups of 16 words)
+    assert sa.sparse_attn_workspace_bytes(d, 1, 40000) == after(sa.WS_STATE_BYTES + partials_1) + (1024 * 16 + 1) * 4
     # a prefill chunk: unsplit attention and one selection workgroup per query token
     # (no list for 64 tokens or more)
     assert sa.sparse_attn_workspace_bytes(d, 2048, 34816) == 0
@@ -91,8 +94,9 @@ def test_workspace_bytes():
     # but the list: 1024 groups
     assert sa.sparse_attn_workspace_bytes(d, 1, 131072) == after(sa.WS_STATE_BYTES + partials_1) + (1024 * 16 + 1) * 4
     # 1M rows: the chunked selection's 128 chunks of 2048 8-byte entries (after a
-    # 768-byte head of counts), then the partials, side by side
-    assert sa.sparse_attn_workspace_bytes(d, 1, 1048576) == sa.WS_STATE_BYTES + 768 + 128 * 2048 * 8 + partials_1
+    # 768-byte head of counts), the partials, then the list (8192 groups of 4 listed, 8 words each)
+    assert sa.sparse_attn_workspace_bytes(d, 1, 1048576) == (after(sa.WS_STATE_BYTES + 768 + 128 * 2048 * 8 + partials_1)
+                                                             + (8192 * 8 + 1) * 4)
     assert sa.sparse_attn_workspace_bytes(_dims(top_k=2050), 1, 4096) == 0
     assert sa.sparse_attn_workspace_bytes(d, 1, -1) == 0
 
@@ -145,9 +149,8 @@ def test_entry_points_reject_bad_arguments_before_any_launch():
     ws = sa.sparse_attn_workspace_bytes(_dims(), 1, 4096)
     args = [d, c, FAKE, FAKE, FAKE, 2051, FAKE, 1, ctypes.c_float(0.04), FAKE]
     assert _call("sparse_attn_fwd", *args, None, 0, None) == sa.SA_ERR_WORKSPACE
-    need_fwd = sa.WS_STATE_BYTES + 33 * 16 * (512 + 2) * 4      # the attention's part: state + partials
-    assert ws > need_fwd                                          # (the rest: the candidate list)
-    assert _call("sparse_attn_fwd", *args, FAKE, need_fwd - 1, None) == sa.SA_ERR_WORKSPACE
+    assert ws == sa.WS_STATE_BYTES + 33 * 16 * (512 + 2) * 4      # state + partials (no list at 4096 tokens)
+    assert _call("sparse_attn_fwd", *args, FAKE, ws - 1, None) == sa.SA_ERR_WORKSPACE
     assert _call("sparse_attn_fwd", d, c, None, FAKE, FAKE, 2051, FAKE, 1, ctypes.c_float(0.04), FAKE, FAKE, ws,
                  None) == sa.SA_ERR_NULL
     assert _call("sparse_attn_fwd", d, c, FAKE, FAKE, FAKE, 2051, FAKE, 1, ctypes.c_float(float("nan")), FAKE, FAKE,
