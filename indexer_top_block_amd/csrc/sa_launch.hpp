@@ -134,8 +134,9 @@ hipError_t launch_select_fwd(const sa_dims& d, const CacheArgs& c, const float* 
 // or 4 for rows of 131073-262144 blocks; 0: no list), the tiles each select thread
 // reads (1 for rows of up to 32768 blocks, else 32 / keep), its words per query token, and
 // its bytes for n_q tokens with the decided flags (0 when the list is never used: rows
-// that are always dense or longer than 262144 blocks, or more query tokens than the
-// pooling scoring launch takes); it is the workspace's last part.
+// that are always dense or longer than 262144 blocks, more query tokens than the
+// pooling scoring launch takes, or more than 8192 tiles in all); it is the workspace's
+// last part.
 int cand_keep(const sa_dims& d, int max_len);
 int cand_tpt(const sa_dims& d, int max_len);
 int64_t cand_words(const sa_dims& d, int max_len);

@@ -40,6 +40,7 @@ constexpr int kFusedMaxKpt = 32;             // keys per thread: rows of up to 3
 constexpr int kFusedListMax = 3072;          // list entries held in LDS (top_k + c - 1)
 constexpr int kFusedMaxChunks = kSelThreads / 4;   // chunks whose counts the finishing pass reads at once
 constexpr int kCandMaxQueries = 63;         // query tokens of the pooling scoring launch
+constexpr long long kCandMaxTiles = 8192;   // listed tiles of all tokens of a call
 static_assert(kSelThreads == kFusedThreads, "the finishing pass runs on the fused workgroup");
 static_assert(kCandThreads == kFusedThreads, "the list is laid out for the fused workgroup's loads");
 
@@ -476,6 +477,11 @@ int64_t cand_words(const sa_dims& d, int max_len) {
 // words).
 size_t cand_bytes(const sa_dims& d, int n_q, int max_len) {
   if (n_q < 1 || n_q > kCandMaxQueries) return 0;
+  // Each scoring wave's tile search costs ~0.3-0.45 us per round of workgroups on the
+  // chip; past 8192 tiles in all (the 1M decode token) the rounds cost more than the
+  // selection saves (32 batched tokens of 16384 blocks: 67.4 us against 63.0)
+  const long long tiles = ((long long)max_len / d.compress_ratio + kCandTile - 1) / kCandTile;
+  if ((long long)n_q * tiles > kCandMaxTiles) return 0;
   const size_t words = (size_t)n_q * cand_words(d, max_len);
   return words == 0 ? 0 : (words + n_q) * 4;
 }
@@ -582,12 +588,14 @@ enum class StepForm { kNoList, kListWide, kListLong };
 // The form of pool + score + select + attention: with the candidate list where the
 // pooling scoring launch and a fused select both apply and the workspace has the list's
 // room; rows of up to 32768 blocks in the one-workgroup kernel, longer ones in
-// list_fwd_kernel.
+// list_fwd_kernel.  (Where the attention runs as a launch of its own, a selection from
+// the list in a launch of its own measured no faster than the row's.)
 static StepForm step_form(const sa_dims& d, const CacheArgs& c, const void* qidx, const void* q, int n_q,
                           const int32_t* n_in, const int32_t* n_out, const FwdPlan& plan, size_t ws_bytes) {
   if (cand_bytes(d, n_q, c.max_len) == 0 || ws_bytes < workspace_bytes(d, n_q, c.max_len)) return StepForm::kNoList;
-  if (!pool_score_fused(d, c, qidx, n_q, n_in, n_out) || !fused_base(d, c, q, n_q, plan)) return StepForm::kNoList;
+  if (!pool_score_fused(d, c, qidx, n_q, n_in, n_out)) return StepForm::kNoList;
   const long long max_blocks = (long long)c.max_len / d.compress_ratio;
+  if (!fused_base(d, c, q, n_q, plan)) return StepForm::kNoList;
   return max_blocks <= (long long)kFusedThreads * kFusedMaxKpt ? StepForm::kListWide : StepForm::kListLong;
 }
 

@@ -278,8 +278,9 @@ def test_step_list_decode_1m(gpu_lib):
 def test_step_list_not_used(gpu_lib):
     # token level over 140 000 positions (4375 groups: 8 listed each would exceed 32768
     # keys, and with 4 a row of independent scores would fall back about every other
-    # time), a row of 5000 blocks for a cut of 512 (too few groups for the list), and
-    # eight tokens of 33 splits (more workgroups than compute units): the two calls
+    # time), a row of 5000 blocks for a cut of 512 (too few groups for the list), eight
+    # tokens of 33 splits (more workgroups than compute units), and the batched decode
+    # workload (a separate V: no fused form; 16 384 tiles in all): the two calls
     d = _dims(compress_ratio=1)
     assert keep_of(140032, 2048) == 0 and keep_of(5000, 512) == 0
     _check(_case("step_list_chunked_row", d, [140000], [0], [139999], 986), expect_list=False)
@@ -287,3 +288,4 @@ def test_step_list_not_used(gpu_lib):
     q_pos = [19999 - 997 * j for j in range(8)]
     _check(_case("step_list_eight_tokens", d, [20000], [0] * 8, q_pos, 987), expect_list=False,
            oracle_queries=[0, 7])
+    _check(datagen.make_workload(3), expect_list=False, oracle_queries=[0, 31])
