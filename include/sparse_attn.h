@@ -229,16 +229,18 @@ int sparse_attn_select_fwd_is_fused(const sa_dims* dims, const sa_cache* cache, 
  * top-k block selection, then the sparse attention over the list), with the
  * arguments of the two calls (ws: sparse_attn_workspace_bytes(dims, n_q,
  * cache->max_len) bytes) and their results bit for bit (kpool, n_pooled_out, scores,
- * sel, n_sel, out).  Where the pooled scoring launch and the selection inside the
- * attention's launch both apply to rows of at most 32768 blocks (see
- * sparse_attn_pool_score_select_fwd_uses_list), the scoring launch also writes, for
- * every 32 consecutive blocks of each token's row, the 8 best (ties to the lower
- * block) into the workspace's last part, and each attention workgroup selects from
- * that list (a quarter of the keys) instead of the row: the list's cut is the row's
- * cut exactly when every block it leaves out scores below that cut, which each group's
- * 8th best bounds; where it does not, the workgroup selects over the row as
- * sparse_attn_select_fwd does.  The list part ends with one int32 per token: 1 when
- * the list decided its selection, 0 when the row did (or the token was dense).
+ * sel, n_sel, out).  Where the pooled scoring launch and a selection inside the
+ * attention's launch both apply (see sparse_attn_pool_score_select_fwd_uses_list:
+ * fewer than 64 tokens of the MLA shapes, at most 8192 groups of 32 blocks in all,
+ * rows of at most 262144 blocks), the scoring launch also writes, for every 32
+ * consecutive blocks of each token's row, the 8 best (4 for rows of more than 131072
+ * blocks; ties to the lower block) into the workspace's last part, and each attention
+ * workgroup selects from that list instead of the row: the list's cut is the row's cut
+ * exactly when every block it leaves out scores below that cut, which each group's
+ * last listed key bounds; where it does not (or the token's row is too short for the
+ * list to be likely to decide), the workgroup selects over the row.  The list part ends
+ * with one int32 per token: 1 when the list decided its selection, 0 when the row did
+ * (or the token was dense).
  * Errors: those of sparse_attn_pool_score and sparse_attn_select_fwd; n_q == 0 makes
  * the pooling alone.                                                                 */
 int sparse_attn_pool_score_select_fwd(const sa_dims* dims, const sa_cache* cache, const int32_t* n_pooled_in,
