@@ -27,6 +27,13 @@
 // that do not fit (more workgroups than compute units, shapes other than the MLA ones
 // with V inside K, lists longer than kFusedListMax, more chunks than the finishing
 // pass reads at once) take those two calls instead.
+//
+// With the scoring launch's candidate list (sparse_attn_pool_score_select_fwd: the
+// best 8 -- or 4 -- of every 32 blocks), the select starts from the list instead of
+// the row: select_fwd_kernel's list form for rows of up to 32768 blocks, and
+// list_fwd_kernel for rows of up to 262144, where it replaces the chunked selection.
+// The list's cut is the row's exactly when no block it leaves out reaches the cut
+// (cand_select); otherwise the workgroup selects over the row, with the same result.
 #include <cmath>
 
 #include "fwd_lds.hpp"
