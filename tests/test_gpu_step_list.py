@@ -269,6 +269,21 @@ def test_step_list_long_rows(gpu_lib):
     _check(case, expect_list=True, expect_decided=[0], oracle_queries=[0])
 
 
+def test_step_list_other_block_sizes(gpu_lib):
+    # blocks of 8 and of 2 tokens (the list's positions written c at a time, not as
+    # four-wide stores): c = 8 over 120 000 positions (15 000 blocks, with a 7-position
+    # tail on the second token); c = 2 over 60 000 (one workgroup's registers) and over
+    # 100 000 positions (50 000 blocks: list_fwd_kernel)
+    d = _dims(compress_ratio=8, top_k=1024)
+    _check(_case("step_list_c8", d, [120000], [0, 0], [119999, 90006], 994), expect_list=True,
+           expect_decided=[1, 1], oracle_queries=[0, 1])
+    d = _dims(compress_ratio=2)
+    _check(_case("step_list_c2_wide", d, [60000], [0], [59999], 995), expect_list=True, expect_decided=[1],
+           oracle_queries=[0])
+    _check(_case("step_list_c2_long", d, [100000], [0, 0], [99999, 70000], 996), expect_list=True,
+           expect_decided=[1, 1], oracle_queries=[0, 1])
+
+
 def test_step_list_decode_1m(gpu_lib):
     # the 1M-context decode workload (262 144 blocks, 1% planted): 8192 groups, 4 listed each
     case = datagen.make_workload(5, q_std=2.0 * math.sqrt(576))
