@@ -237,10 +237,12 @@ int sparse_attn_select_fwd_is_fused(const sa_dims* dims, const sa_cache* cache, 
  * blocks; ties to the lower block) into the workspace's last part, and each attention
  * workgroup selects from that list instead of the row: the list's cut is the row's cut
  * exactly when every block it leaves out scores below that cut, which each group's
- * last listed key bounds; where it does not (or the token's row is too short for the
- * list to be likely to decide), the workgroup selects over the row.  The list part ends
- * with one int32 per token: 1 when the list decided its selection, 0 when the row did
- * (or the token was dense).
+ * last listed key bounds; where it does not, the groups whose listed keys reach the cut
+ * are read whole from the row and the cut taken again, and where that does not decide
+ * either (or the token's row is too short for the list to be likely to decide), the
+ * workgroup selects over the row.  The list part ends with one int32 per token: 1 when
+ * the list (with any groups read whole) decided its selection, 0 when the row did (or
+ * the token was dense).
  * Errors: those of sparse_attn_pool_score and sparse_attn_select_fwd; n_q == 0 makes
  * the pooling alone.                                                                 */
 int sparse_attn_pool_score_select_fwd(const sa_dims* dims, const sa_cache* cache, const int32_t* n_pooled_in,

@@ -72,6 +72,55 @@ union FusedSmem {
   FwdLdsSmem<T, DKQ, true> att;
 };
 
+// The kept blocks' positions into the LDS list from each thread's tile words (bit b of
+// kw[j] / tw[j]: block b of the thread's tile j kept / tied) and their counts: every
+// kept block and the first k_rem tied blocks in index order, placed from the counts of
+// the threads before (wave scans, then the wave totals in h2, which the picks no
+// longer use).  Ends with the list complete and visible to the workgroup.
+template <int NT, int KPT, int TPT>
+__device__ __forceinline__ void place_words(const uint32_t (&kw)[TPT], const uint32_t (&tw)[TPT], int kc, int tc,
+                                            int k_rem, int c, int k_blk, WideSmem<NT, KPT>& sm, int32_t* list) {
+  constexpr int WAVES = NT / kWave;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int k_incl = wave_inclusive_scan(kc, lane), t_incl = wave_inclusive_scan(tc, lane);
+  if (lane == kWave - 1) {
+    sm.h2[wave] = (uint32_t)k_incl;
+    sm.h2[WAVES + wave] = (uint32_t)t_incl;
+  }
+  lds_barrier();
+  const int wk = lane < WAVES ? (int)sm.h2[lane] : 0, wt = lane < WAVES ? (int)sm.h2[WAVES + lane] : 0;
+  const int wk_incl = wave_inclusive_scan(wk, lane), wt_incl = wave_inclusive_scan(wt, lane);
+  const int k_before = (wave > 0 ? __builtin_amdgcn_readlane(wk_incl, wave - 1) : 0) + k_incl - kc;
+  const int t_before = (wave > 0 ? __builtin_amdgcn_readlane(wt_incl, wave - 1) : 0) + t_incl - tc;
+  int o = k_before + min(k_rem, t_before);
+  int want = k_rem - t_before;                       // tied blocks still wanted at this thread's first tile
+#pragma unroll
+  for (int j = 0; j < TPT; ++j) {
+    uint32_t word = kw[j], t = tw[j];
+    for (; want > 0 && t != 0u; --want) {            // the first tied blocks still wanted, in index order
+      word |= t & (0u - t);
+      t &= t - 1u;
+    }
+    const int32_t b0 = (tid * TPT + j) * kCandTile;
+    if (c == 4) {
+      while (word != 0u && o < k_blk) {              // o < k_blk always; the bound only guards memory
+        const int32_t p0 = (b0 + __ffs(word) - 1) * 4;
+        word &= word - 1u;
+        *(int4*)&list[o * 4] = int4{p0, p0 + 1, p0 + 2, p0 + 3};
+        ++o;
+      }
+    } else {
+      while (word != 0u && o < k_blk) {
+        const int32_t p0 = (b0 + __ffs(word) - 1) * c;
+        word &= word - 1u;
+        for (int u = 0; u < c; ++u) list[o * c + u] = p0 + u;
+        ++o;
+      }
+    }
+  }
+  __syncthreads();
+}
+
 // The select from the scoring launch's candidate list: thread t holds tiles
 // [TPT t, TPT t + TPT), each tile's KEEP largest keys and their block indices (keys 0
 // past the row), counts the keys into the pass-1 histogram and runs the passes over
@@ -83,10 +132,12 @@ union FusedSmem {
 // The kept blocks of a tile are then its own candidates: each thread places its
 // tiles' kept blocks in the list from the counts of the tiles before it (kept blocks,
 // and the first k_rem tied blocks in index order).  Requires nb > k_blk and at least
-// k_blk listed blocks; the histograms are clear on entry and dirty on return.
+// k_blk listed blocks; the histograms are clear on entry and dirty on return.  On
+// failure failed_bound is the cut the list reached (the keys of cv are then those the
+// cut counted: 0 past the row).
 template <int NT, int KPT, int KEEP, int TPT>
 __device__ __forceinline__ bool cand_select(uint4 (&cv)[KEEP * TPT / 2], int nb, int c, int k_blk,
-                                            WideSmem<NT, KPT>& sm, int32_t* list) {
+                                            WideSmem<NT, KPT>& sm, int32_t* list, uint32_t& failed_bound) {
   constexpr int COPIES = WideCfg<NT, KPT>::copies, WAVES = NT / kWave, KC = KEEP * TPT;
   static_assert(KEEP % 4 == 0 && WideCfg<NT, KPT>::words >= WAVES && kWideBins >= 2 * WAVES,
                 "tile records in 16-byte pieces; LDS words reused for the wave totals");
@@ -127,7 +178,10 @@ __device__ __forceinline__ bool cand_select(uint4 (&cv)[KEEP * TPT / 2], int nb,
   uint32_t left_out = 0u;
 #pragma unroll
   for (int v = 0; v < WAVES; ++v) left_out = max(left_out, sm.keep[v]);
-  if (left_out >= bound) return false;               // (bound 0: never taken)
+  if (left_out >= bound) {                           // (bound 0: never taken)
+    failed_bound = bound;
+    return false;
+  }
   // keep: key >= thr (thr > 0: bound > 0 here); tie: key == T (the cut inside a key)
   const uint32_t thr = cut.whole ? bound : bound + 1u;
   const bool full = !cut.whole && bound == 0xffffffffu;   // nothing above T
@@ -146,45 +200,98 @@ __device__ __forceinline__ bool cand_select(uint4 (&cv)[KEEP * TPT / 2], int nb,
     kc += __popc(kw[j]);
     tc += __popc(tw[j]);
   }
-  // counts of the tiles before this thread's: wave scans, then the wave totals (in h2,
-  // free since the last pick)
-  const int k_incl = wave_inclusive_scan(kc, lane), t_incl = wave_inclusive_scan(tc, lane);
-  if (lane == kWave - 1) {
-    sm.h2[wave] = (uint32_t)k_incl;
-    sm.h2[WAVES + wave] = (uint32_t)t_incl;
-  }
-  lds_barrier();
-  const int wk = lane < WAVES ? (int)sm.h2[lane] : 0, wt = lane < WAVES ? (int)sm.h2[WAVES + lane] : 0;
-  const int wk_incl = wave_inclusive_scan(wk, lane), wt_incl = wave_inclusive_scan(wt, lane);
-  const int k_before = (wave > 0 ? __builtin_amdgcn_readlane(wk_incl, wave - 1) : 0) + k_incl - kc;
-  const int t_before = (wave > 0 ? __builtin_amdgcn_readlane(wt_incl, wave - 1) : 0) + t_incl - tc;
-  int o = k_before + min(cut.k_rem, t_before);
-  int want = cut.k_rem - t_before;                   // tied blocks still wanted at this thread's first tile
+  place_words<NT, KPT, TPT>(kw, tw, kc, tc, cut.k_rem, c, k_blk, sm, list);
+  return true;
+}
+
+// The list could not decide: some tiles' smallest listed key reached the cut bound0,
+// so a block such a tile left out might be kept.  Those tiles (at most 32) are read
+// whole from the row, one block per thread of 32 consecutive threads each, in place of
+// their listed keys, and the cut is taken again over them and the other tiles' listed
+// keys (9 keys per thread at most): adding keys only raises it, so the other tiles'
+// left-out blocks stay below it -- unless the new cut's whole bin starts at or below one
+// of their smallest listed keys, which is checked again (false: the caller selects over
+// the row).  The kept and tied blocks then go to the keep and tie bitmaps and the list
+// is made from them in index order (wide_list).  For the one-tile-per-thread list (rows
+// of up to 32768 blocks); cv as cand_select left it.
+template <int NT, int KPT>
+__device__ __forceinline__ bool cand_complete(const uint4 (&cv)[kCandKeep / 2], const float* __restrict__ row, int nb,
+                                              int c, int k_blk, uint32_t bound0, WideSmem<NT, KPT>& sm,
+                                              int32_t* list) {
+  constexpr int COPIES = WideCfg<NT, KPT>::copies, WAVES = NT / kWave, MAX_OVER = NT / kCandTile;
+  static_assert(WideCfg<NT, KPT>::words >= 2 * WAVES + MAX_OVER, "LDS words reused for counts and tile numbers");
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  nb = min(nb, KPT * NT);                            // the launch guarantees nb fits; the bitmaps rely on it
+  const uint32_t* w = reinterpret_cast<const uint32_t*>(cv);
+  uint32_t least = w[0];
 #pragma unroll
-  for (int j = 0; j < TPT; ++j) {
-    uint32_t word = kw[j], t = tw[j];
-    for (; want > 0 && t != 0u; --want) {            // the first tied blocks still wanted, in index order
-      word |= t & (0u - t);
-      t &= t - 1u;
-    }
-    const int32_t b0 = (tid * TPT + j) * kCandTile;
-    if (c == 4) {
-      while (word != 0u && o < k_blk) {              // o < k_blk always; the bound only guards memory
-        const int32_t p0 = (b0 + __ffs(word) - 1) * 4;
-        word &= word - 1u;
-        *(int4*)&list[o * 4] = int4{p0, p0 + 1, p0 + 2, p0 + 3};
-        ++o;
-      }
-    } else {
-      while (word != 0u && o < k_blk) {
-        const int32_t p0 = (b0 + __ffs(word) - 1) * c;
-        word &= word - 1u;
-        for (int u = 0; u < c; ++u) list[o * c + u] = p0 + u;
-        ++o;
-      }
-    }
+  for (int e = 1; e < kCandKeep; ++e) least = min(least, w[e]);
+  const bool over = tid * kCandTile < nb && least >= bound0;   // this thread's tile is read whole
+  // the tiles read whole, numbered in tile order: per-wave counts, then their offsets
+  const uint64_t ob = __ballot(over);
+  __syncthreads();                                   // the first cut's LDS reads are done
+  if (lane == 0) sm.tie[wave] = (uint32_t)__popcll(ob);
+  __syncthreads();
+  int n_over = 0, before = 0;
+#pragma unroll
+  for (int v = 0; v < WAVES; ++v) {
+    const int n = (int)sm.tie[v];
+    before += v < wave ? n : 0;
+    n_over += n;
+  }
+  if (n_over > MAX_OVER) return false;               // (uniform) too many: the row's select
+  if (over) sm.tie[2 * WAVES + before + __popcll(ob & ((1ull << lane) - 1ull))] = (uint32_t)tid;
+  for (int e = tid; e < kP1Bins * COPIES / 4; e += NT) ((uint4*)sm.h1)[e] = uint4{0u, 0u, 0u, 0u};
+  for (int e = tid; e < kWideBins; e += NT) sm.h2[e] = 0u;
+  const uint32_t bound_out = wave_max_u32(over ? 0u : least);        // completed tiles leave nothing out
+  if (lane == 0) sm.keep[wave] = bound_out;
+  __syncthreads();
+  // keys: this tile's listed 8 (none when it is read whole), and block tid % 32 of the
+  // (tid / 32)-th tile read whole
+  uint32_t key[kCandKeep + 1];
+#pragma unroll
+  for (int e = 0; e < kCandKeep; ++e) key[e] = over ? 0u : w[e];
+  const int xo = tid / kCandTile;
+  const int xtile = xo < n_over ? (int)sm.tie[2 * WAVES + xo] : -1;
+  const int xb = xtile * kCandTile + tid % kCandTile;
+  key[kCandKeep] = (xtile >= 0 && xb < nb) ? score_key(row[xtile >= 0 ? min(xb, nb - 1) : 0]) : 0u;
+  int zeros = 0;                                     // padding: key 0 (no score has it)
+#pragma unroll
+  for (int e = 0; e <= kCandKeep; ++e) zeros += key[e] == 0u ? 1 : 0;
+  {
+    uint32_t* mine = sm.h1 + (lane & (COPIES - 1));
+#pragma unroll
+    for (int e = 0; e <= kCandKeep; ++e) atomicAdd(&mine[(key[e] >> 22) * COPIES], 1u);
+  }
+  const int z_incl = wave_inclusive_scan(zeros, lane);
+  if (lane == kWave - 1) sm.tie[WAVES + wave] = (uint32_t)z_incl;
+  __syncthreads();
+  int n_pad = 0;
+#pragma unroll
+  for (int v = 0; v < WAVES; ++v) n_pad += (int)sm.tie[WAVES + v];
+  const WideCut cut = wide_cut<NT, KPT, kCandKeep + 1>([&](int e) { return key[e]; }, k_blk, n_pad, sm);
+  const uint32_t bound = cut.whole ? cut.prefix << cut.shift : cut.prefix;
+  uint32_t left_out = 0u;
+#pragma unroll
+  for (int v = 0; v < WAVES; ++v) left_out = max(left_out, sm.keep[v]);
+  if (left_out >= bound) return false;
+  // kept and tied blocks into the bitmaps (bit b % 32 of word b / 32)
+  const uint32_t thr = cut.whole ? bound : bound + 1u;
+  const bool full = !cut.whole && bound == 0xffffffffu;
+  __syncthreads();                                   // every wave has read keep[]
+  for (int e = tid; e < WideCfg<NT, KPT>::words; e += NT) {
+    sm.keep[e] = 0u;
+    sm.tie[e] = 0u;
   }
   __syncthreads();
+#pragma unroll
+  for (int e = 0; e <= kCandKeep; ++e) {
+    const int b = e < kCandKeep ? tid * kCandTile + (int)(w[kCandKeep + e] % kCandTile) : xb;
+    if (key[e] != 0u && !full && key[e] >= thr) atomicOr(&sm.keep[b / kCandTile], 1u << (b % kCandTile));
+    if (key[e] != 0u && !cut.whole && key[e] == bound) atomicOr(&sm.tie[b / kCandTile], 1u << (b % kCandTile));
+  }
+  __syncthreads();
+  wide_list<NT, KPT>(sm, cut.whole, cut.k_rem, c, k_blk, list, nullptr);
   return true;
 }
 
@@ -237,8 +344,11 @@ select_fwd_kernel(const float* __restrict__ scores, int64_t scores_ld, const int
     bool done = false;
     if constexpr (CAND) {
       // only rows of enough groups for the list to be likely to decide (cand_min_groups)
+      uint32_t failed = 0u;
       if (qr.nb / kCandTile >= cand_min_groups)
-        done = cand_select<NT, KPT, kCandKeep, 1>(cv, qr.nb, c, k_blk, sm.sel, list);
+        done = cand_select<NT, KPT, kCandKeep, 1>(cv, qr.nb, c, k_blk, sm.sel, list, failed);
+      // a few tiles held more of the kept blocks than they list: read them whole
+      if (!done && failed != 0u) done = cand_complete<NT, KPT>(cv, row, qr.nb, c, k_blk, failed, sm.sel, list);
       if (!done) {                                   // the row's select: fresh histograms, the row's keys
         __syncthreads();
         for (int e = tid; e < kP1Bins * COPIES / 4; e += NT) ((uint4*)sm.sel.h1)[e] = uint4{0u, 0u, 0u, 0u};
@@ -313,8 +423,9 @@ list_fwd_kernel(const float* __restrict__ scores, int64_t scores_ld, const int32
   } else {
     __syncthreads();                                 // the histograms are clear
     bool done = false;
+    uint32_t failed = 0u;
     if (qr.nb / kCandTile >= cand_min_groups)
-      done = cand_select<NT, KPT, KEEP, TPT>(cv, qr.nb, c, k_blk, sm.sel, list);
+      done = cand_select<NT, KPT, KEEP, TPT>(cv, qr.nb, c, k_blk, sm.sel, list, failed);
     if (!done) {                                     // the row's select, streamed (rare)
       __syncthreads();
       select_one_query<NT, 8>(scores + (int64_t)i * scores_ld, qr.nb, c, k_blk, list, sm.one);

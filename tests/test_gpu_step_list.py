@@ -116,15 +116,34 @@ def min_groups(k_blk: int, keep: int) -> int:
     return g
 
 
-def expected_decided(keys: np.ndarray, nb: int, k_blk: int, keep: int) -> int:
+def expected_decided(keys: np.ndarray, nb: int, k_blk: int, keep: int, complete: bool) -> int:
+    """1 where the list decides the selection: its cut bound above every group's smallest
+    listed key; else, with `complete` (rows of one workgroup's registers), the groups
+    whose smallest listed key reached the bound are read whole and the cut is taken
+    again over them and the other groups' listed keys, which decides when the new
+    bound is above the other groups' smallest listed keys."""
     if nb <= k_blk or nb // GROUP < min_groups(k_blk, keep):
         return 0
     lists = expected_lists(keys, nb, keep)
+    least = {g: int(v[:keep].min()) for g, v in lists.items()}
     listed = np.concatenate([v[:keep] for v in lists.values()])
-    n_listed = nb // GROUP * keep + min(keep, nb % GROUP)
-    listed = np.sort(listed)[::-1][:n_listed]
+    listed = listed[listed != 0]
     bound = radix_bound(listed, k_blk)
-    return int(all(int(v[:keep].min()) < bound for v in lists.values()))
+    if all(x < bound for x in least.values()):
+        return 1
+    if not complete:
+        return 0
+    over = {g for g, x in least.items() if x >= bound}
+    parts = []
+    for g, v in lists.items():
+        if g in over:
+            parts.append(keys[g * GROUP: min(nb, g * GROUP + GROUP)].astype(np.int64))
+        else:
+            parts.append(v[:keep].astype(np.int64))
+    merged = np.concatenate(parts)
+    merged = merged[merged != 0]
+    bound2 = radix_bound(merged, k_blk)
+    return int(all(x < bound2 for g, x in least.items() if g not in over))
 
 
 def _run(layer, fused_step: bool):
@@ -173,7 +192,7 @@ def _check(case, expect_list, expect_decided=None, oracle_queries=()):
             n_vis = oracle.visible_tokens(int(case.seq_len[case.q_seq[i]]), int(case.q_pos[i]))
             nb = n_vis // c
             keys = order_keys(scores[i, :nb])
-            want = expected_decided(keys, nb, k_blk, keep)
+            want = expected_decided(keys, nb, k_blk, keep, complete=tpt == 1)
             if nb > k_blk and nb // GROUP >= min_groups(k_blk, keep):
                 for g, v in expected_lists(keys, nb, keep).items():
                     rec = lists[i, [record_word(g, r, keep, tpt) for r in range(2 * keep)]]
@@ -228,16 +247,22 @@ def test_step_list_shapes(gpu_lib):
            oracle_queries=[0])
 
 
-def test_step_list_falls_back_to_the_row(gpu_lib):
-    # one group of 32 blocks scaled up eight times (exact in bf16): all 32 are among the
-    # best, so the group's 8th best is above the cut and the row decides; then 600
-    # copies of one block scaled up four times, at most 3 per group: the cut falls
-    # inside their common score (ties go to the lower blocks) and the list decides it
+def test_step_list_completes_crowded_groups(gpu_lib):
+    # groups of 32 blocks scaled up eight times (exact in bf16): all 32 are among the
+    # best, so each such group's 8th best is above the list's cut; those groups are read
+    # whole from the row and the cut taken again (one group; the last three groups, the
+    # most recent positions); then 600 copies of one block scaled up four times, at most
+    # 3 per group: the cut falls inside their common score (ties go to the lower blocks)
+    # and the list decides it
     d = _dims()
     case = _case("step_list_crowded_group", d, [131072], [0], [131071], 984)
     tok = slice(int(case.row0[0]) + 64 * 4, int(case.row0[0]) + 96 * 4)
     case.kidx[tok] = case.kidx[tok] * np.float32(8.0)
-    _check(case, expect_list=True, expect_decided=[0], oracle_queries=[0])
+    _check(case, expect_list=True, expect_decided=[1], oracle_queries=[0])
+    case = _case("step_list_recent_groups", d, [131072], [0], [131071], 989)
+    tok = slice(int(case.row0[0]) + (32768 - 96) * 4, int(case.row0[0]) + 32768 * 4)
+    case.kidx[tok] = case.kidx[tok] * np.float32(8.0)
+    _check(case, expect_list=True, expect_decided=[1], oracle_queries=[0])
 
     case = _case("step_list_tied_copies", d, [131072], [0], [131071], 985)
     rng = np.random.default_rng([985, 1])
