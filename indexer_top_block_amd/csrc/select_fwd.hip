@@ -295,6 +295,152 @@ __device__ __forceinline__ bool cand_complete(const uint4 (&cv)[kCandKeep / 2], 
   return true;
 }
 
+// cand_complete for the lists of rows longer than one workgroup's registers hold
+// (TPT tiles per thread): the crowded tiles (at most 32 * XPT) are read whole, XPT
+// blocks per thread, and the cut taken again over them and the other tiles' listed
+// keys, with the same check.  A crowded tile's kept and tied blocks are collected
+// into LDS words by the threads that read its blocks, and the tile's own thread
+// places them with its other tiles' in index order (place_words).  src: this
+// thread's first list piece, as the launch loaded it; the list is read again here
+// rather than held in registers through the common path.
+template <int NT, int KPT, int KEEP, int TPT, int XPT>
+__device__ __forceinline__ bool cand_complete_tiles(const uint4* __restrict__ src, const float* __restrict__ row,
+                                                    int nb, int c, int k_blk, uint32_t bound0, WideSmem<NT, KPT>& sm,
+                                                    int32_t* list) {
+  constexpr int COPIES = WideCfg<NT, KPT>::copies, WAVES = NT / kWave, KC = KEEP * TPT;
+  constexpr int MAX_OVER = NT * XPT / kCandTile;
+  // keep[] words: [0, WAVES) bounds, [WAVES, 2 WAVES) crowded tiles per wave, then the
+  // crowded tiles' numbers, their kept words and their tied words; tie[]: zero counts
+  constexpr int OT = 2 * WAVES, OK = OT + MAX_OVER, OTW = OK + MAX_OVER;
+  static_assert(WideCfg<NT, KPT>::words >= OTW + MAX_OVER, "LDS words for the crowded tiles");
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  nb = min(nb, NT * TPT * kCandTile);
+  // the addresses are formed anew (an empty asm hides src's origin), so the common
+  // path keeps none of its own load addresses live for this one
+  asm volatile("" : "+v"(src));
+  uint4 cv[KEEP * TPT / 2];
+#pragma unroll
+  for (int q = 0; q < KEEP * TPT / 2; ++q) cv[q] = src[q * kCandThreads];
+  uint32_t* w = reinterpret_cast<uint32_t*>(cv);     // tile j: KEEP keys, then KEEP block indices
+#pragma unroll
+  for (int j = 0; j < TPT; ++j)                      // tiles past the row list nothing
+#pragma unroll
+    for (int e = 0; e < KEEP; ++e) w[j * 2 * KEEP + e] = (tid * TPT + j) * kCandTile < nb ? w[j * 2 * KEEP + e] : 0u;
+  auto tile_least = [&](int j) {
+    uint32_t x = w[j * 2 * KEEP];
+#pragma unroll
+    for (int e = 1; e < KEEP; ++e) x = min(x, w[j * 2 * KEEP + e]);
+    return x;
+  };
+  uint32_t ov = 0u;                                  // bit j: this thread's tile j is read whole
+  uint32_t bmax = 0u;                                // the largest smallest-key of the others
+#pragma unroll
+  for (int j = 0; j < TPT; ++j) {
+    const uint32_t x = tile_least(j);
+    const bool o = (tid * TPT + j) * kCandTile < nb && x >= bound0;
+    ov |= o ? 1u << j : 0u;
+    bmax = max(bmax, o ? 0u : x);
+  }
+  const int n_mine = __popc(ov);
+  const int incl = wave_inclusive_scan(n_mine, lane);
+  bmax = wave_max_u32(bmax);
+  __syncthreads();                                   // the first cut's LDS reads are done
+  if (lane == kWave - 1) sm.keep[WAVES + wave] = (uint32_t)incl;
+  if (lane == 0) sm.keep[wave] = bmax;
+  __syncthreads();
+  int n_over = 0, first = incl - n_mine;             // this thread's first crowded tile's rank
+#pragma unroll
+  for (int v = 0; v < WAVES; ++v) {
+    const int n = (int)sm.keep[WAVES + v];
+    first += v < wave ? n : 0;
+    n_over += n;
+  }
+  if (n_over > MAX_OVER) return false;               // (uniform) too many: the row's select
+  {
+    int r = first;
+#pragma unroll
+    for (int j = 0; j < TPT; ++j)
+      if (ov & (1u << j)) sm.keep[OT + r++] = (uint32_t)(tid * TPT + j);
+  }
+  for (int e = tid; e < kP1Bins * COPIES / 4; e += NT) ((uint4*)sm.h1)[e] = uint4{0u, 0u, 0u, 0u};
+  for (int e = tid; e < kWideBins; e += NT) sm.h2[e] = 0u;
+  for (int e = tid; e < 2 * MAX_OVER; e += NT) sm.keep[OK + e] = 0u;
+  // the crowded tiles' listed keys leave the count (their blocks come whole below)
+#pragma unroll
+  for (int j = 0; j < TPT; ++j)
+#pragma unroll
+    for (int e = 0; e < KEEP; ++e) w[j * 2 * KEEP + e] = (ov & (1u << j)) ? 0u : w[j * 2 * KEEP + e];
+  __syncthreads();
+  // extra keys: slot x * NT + tid is block slot % 32 of the (slot / 32)-th crowded tile
+  uint32_t xkey[XPT];
+  int xtile[XPT];
+#pragma unroll
+  for (int x = 0; x < XPT; ++x) {
+    const int slot = x * NT + tid, k = slot / kCandTile;
+    xtile[x] = k < n_over ? (int)sm.keep[OT + k] : -1;
+    const int b = xtile[x] * kCandTile + slot % kCandTile;
+    const bool ok = xtile[x] >= 0 && b < nb;
+    const uint32_t rk = score_key(row[ok ? b : 0]);
+    xkey[x] = ok ? rk : 0u;
+  }
+  auto key = [&](int j) -> uint32_t { return j < KC ? w[(j / KEEP) * 2 * KEEP + j % KEEP] : xkey[j - KC]; };
+  int zeros = 0;                                     // padding: key 0 (no score has it)
+#pragma unroll
+  for (int j = 0; j < KC + XPT; ++j) zeros += key(j) == 0u ? 1 : 0;
+  {
+    uint32_t* mine = sm.h1 + (lane & (COPIES - 1));
+#pragma unroll
+    for (int j = 0; j < KC + XPT; ++j) atomicAdd(&mine[(key(j) >> 22) * COPIES], 1u);
+  }
+  const int z_incl = wave_inclusive_scan(zeros, lane);
+  if (lane == kWave - 1) sm.tie[wave] = (uint32_t)z_incl;
+  __syncthreads();
+  int n_pad = 0;
+#pragma unroll
+  for (int v = 0; v < WAVES; ++v) n_pad += (int)sm.tie[v];
+  const WideCut cut = wide_cut<NT, KPT, KC + XPT>(key, k_blk, n_pad, sm);
+  const uint32_t bound = cut.whole ? cut.prefix << cut.shift : cut.prefix;
+  uint32_t left_out = 0u;
+#pragma unroll
+  for (int v = 0; v < WAVES; ++v) left_out = max(left_out, sm.keep[v]);
+  if (left_out >= bound) return false;
+  const uint32_t thr = cut.whole ? bound : bound + 1u;
+  const bool full = !cut.whole && bound == 0xffffffffu;
+  // the crowded tiles' kept and tied blocks, collected by the threads that read them
+#pragma unroll
+  for (int x = 0; x < XPT; ++x) {
+    if (xkey[x] == 0u) continue;
+    const int slot = x * NT + tid, k = slot / kCandTile;
+    const uint32_t bit = 1u << (slot % kCandTile);
+    if (!full && xkey[x] >= thr) atomicOr(&sm.keep[OK + k], bit);
+    if (!cut.whole && xkey[x] == bound) atomicOr(&sm.keep[OTW + k], bit);
+  }
+  __syncthreads();
+  uint32_t kw[TPT], tw[TPT];
+  int kc = 0, tc = 0, r = first;
+#pragma unroll
+  for (int j = 0; j < TPT; ++j) {
+    kw[j] = 0u;
+    tw[j] = 0u;
+    if (ov & (1u << j)) {
+      kw[j] = sm.keep[OK + r];
+      tw[j] = sm.keep[OTW + r];
+      ++r;
+    } else {
+#pragma unroll
+      for (int e = 0; e < KEEP; ++e) {
+        const uint32_t k = w[j * 2 * KEEP + e], bit = 1u << (w[j * 2 * KEEP + KEEP + e] % kCandTile);
+        kw[j] |= (!full && k >= thr) ? bit : 0u;
+        if (!cut.whole) tw[j] |= k == bound ? bit : 0u;
+      }
+    }
+    kc += __popc(kw[j]);
+    tc += __popc(tw[j]);
+  }
+  place_words<NT, KPT, TPT>(kw, tw, kc, tc, cut.k_rem, c, k_blk, sm, list);
+  return true;
+}
+
 // CAND: the select starts from the scoring launch's candidate list (cand, cand_ld
 // words per query token) for rows of at least cand_min_groups whole groups, and takes
 // the row when the list cannot decide it; decided[i] records which (1: the list).
@@ -403,11 +549,9 @@ list_fwd_kernel(const float* __restrict__ scores, int64_t scores_ld, const int32
   const bool writer = blockIdx.x == 0 && blockIdx.y % h_kv == 0;   // writes sel and n_sel of query i
   // this thread's tiles of the list, coalesced: piece q of thread t at q * kCandThreads + t
   uint4 cv[KEEP * TPT / 2];
-  {
-    const uint4* src = (const uint4*)(cand + (int64_t)i * cand_ld) + tid;
+  const uint4* cand_src = (const uint4*)(cand + (int64_t)i * cand_ld) + tid;
 #pragma unroll
-    for (int q = 0; q < KEEP * TPT / 2; ++q) cv[q] = src[q * kCandThreads];
-  }
+  for (int q = 0; q < KEEP * TPT / 2; ++q) cv[q] = cand_src[q * kCandThreads];
   const SeqMeta meta = seq_meta(q_seq, seq_len, seq_row0, nullptr, i);
   const int n_vis = visible_tokens(meta.len, q_pos[i]);
   const QueryRowInfo qr{n_vis / c, n_vis};
@@ -426,6 +570,10 @@ list_fwd_kernel(const float* __restrict__ scores, int64_t scores_ld, const int32
     uint32_t failed = 0u;
     if (qr.nb / kCandTile >= cand_min_groups)
       done = cand_select<NT, KPT, KEEP, TPT>(cv, qr.nb, c, k_blk, sm.sel, list, failed);
+    // a few tiles held more of the kept blocks than they list: read them whole
+    if (!done && failed != 0u)
+      done = cand_complete_tiles<NT, KPT, KEEP, TPT, 2>(cand_src, scores + (int64_t)i * scores_ld, qr.nb, c, k_blk, failed,
+                                                        sm.sel, list);
     if (!done) {                                     // the row's select, streamed (rare)
       __syncthreads();
       select_one_query<NT, 8>(scores + (int64_t)i * scores_ld, qr.nb, c, k_blk, list, sm.one);

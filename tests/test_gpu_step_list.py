@@ -116,12 +116,12 @@ def min_groups(k_blk: int, keep: int) -> int:
     return g
 
 
-def expected_decided(keys: np.ndarray, nb: int, k_blk: int, keep: int, complete: bool) -> int:
+def expected_decided(keys: np.ndarray, nb: int, k_blk: int, keep: int, max_over: int) -> int:
     """1 where the list decides the selection: its cut bound above every group's smallest
-    listed key; else, with `complete` (rows of one workgroup's registers), the groups
-    whose smallest listed key reached the bound are read whole and the cut is taken
-    again over them and the other groups' listed keys, which decides when the new
-    bound is above the other groups' smallest listed keys."""
+    listed key; else the groups whose smallest listed key reached the bound (at most
+    max_over of them) are read whole and the cut is taken again over them and the other
+    groups' listed keys, which decides when the new bound is above the other groups'
+    smallest listed keys."""
     if nb <= k_blk or nb // GROUP < min_groups(k_blk, keep):
         return 0
     lists = expected_lists(keys, nb, keep)
@@ -131,9 +131,9 @@ def expected_decided(keys: np.ndarray, nb: int, k_blk: int, keep: int, complete:
     bound = radix_bound(listed, k_blk)
     if all(x < bound for x in least.values()):
         return 1
-    if not complete:
-        return 0
     over = {g for g, x in least.items() if x >= bound}
+    if len(over) > max_over:
+        return 0
     parts = []
     for g, v in lists.items():
         if g in over:
@@ -192,7 +192,7 @@ def _check(case, expect_list, expect_decided=None, oracle_queries=()):
             n_vis = oracle.visible_tokens(int(case.seq_len[case.q_seq[i]]), int(case.q_pos[i]))
             nb = n_vis // c
             keys = order_keys(scores[i, :nb])
-            want = expected_decided(keys, nb, k_blk, keep, complete=tpt == 1)
+            want = expected_decided(keys, nb, k_blk, keep, max_over=32 if tpt == 1 else 64)
             if nb > k_blk and nb // GROUP >= min_groups(k_blk, keep):
                 for g, v in expected_lists(keys, nb, keep).items():
                     rec = lists[i, [record_word(g, r, keep, tpt) for r in range(2 * keep)]]
@@ -280,9 +280,8 @@ def test_step_list_completes_crowded_groups(gpu_lib):
 def test_step_list_long_rows(gpu_lib):
     # rows longer than one workgroup's registers (list_fwd_kernel): token level over
     # 40 000 positions (1250 groups, 8 listed each: 10 000 keys) with whole, ragged and
-    # dense-at-the-threshold rows; and a crowded group in a 40 000-position row, where
-    # the per-query select over the row runs inside the launch (4 listed per group:
-    # the 1M decode below)
+    # dense-at-the-threshold rows; and a crowded group in a 40 000-position row, read
+    # whole from the row (4 listed per group: the 1M decode below)
     d = _dims(compress_ratio=1)
     assert keep_of(40000, 2048) == 8 and keep_of(262144, 512) == 4
     q_pos = [39999, 31234, 2047]              # 1250 groups; 976 (fewer than the 1178 the list needs); dense
@@ -290,6 +289,12 @@ def test_step_list_long_rows(gpu_lib):
            expect_decided=[1, 0, 0], oracle_queries=[0, 1, 2])
     case = _case("step_list_long_crowded", d, [40000], [0], [39999], 992)
     tok = slice(int(case.row0[0]) + 64, int(case.row0[0]) + 96)
+    case.kidx[tok] = case.kidx[tok] * np.float32(8.0)
+    _check(case, expect_list=True, expect_decided=[1], oracle_queries=[0])
+    # 70 crowded groups (2240 blocks scaled up, more than the 2048 kept): more than the
+    # 64 the launch reads whole, so the streamed per-query select over the row runs
+    case = _case("step_list_long_very_crowded", d, [40000], [0], [39999], 997)
+    tok = slice(int(case.row0[0]) + 3200, int(case.row0[0]) + 3200 + 70 * 32)
     case.kidx[tok] = case.kidx[tok] * np.float32(8.0)
     _check(case, expect_list=True, expect_decided=[0], oracle_queries=[0])
 
