@@ -76,10 +76,14 @@ union FusedSmem {
 // kw[j] / tw[j]: block b of the thread's tile j kept / tied) and their counts: every
 // kept block and the first k_rem tied blocks in index order, placed from the counts of
 // the threads before (wave scans, then the wave totals in h2, which the picks no
-// longer use).  Ends with the list complete and visible to the workgroup.
+// longer use).  Ends with the list complete and visible to the workgroup -- except
+// for the tiles of skip (bit j: tile j): for each of those, in tile order, the first
+// list entry its blocks take and the tied blocks it still takes at most go to at[0],
+// at[1], then at += 2, and the caller places its blocks.
 template <int NT, int KPT, int TPT>
 __device__ __forceinline__ void place_words(const uint32_t (&kw)[TPT], const uint32_t (&tw)[TPT], int kc, int tc,
-                                            int k_rem, int c, int k_blk, WideSmem<NT, KPT>& sm, int32_t* list) {
+                                            int k_rem, int c, int k_blk, WideSmem<NT, KPT>& sm, int32_t* list,
+                                            uint32_t skip = 0u, uint32_t* at = nullptr) {
   constexpr int WAVES = NT / kWave;
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int k_incl = wave_inclusive_scan(kc, lane), t_incl = wave_inclusive_scan(tc, lane);
@@ -97,6 +101,15 @@ __device__ __forceinline__ void place_words(const uint32_t (&kw)[TPT], const uin
 #pragma unroll
   for (int j = 0; j < TPT; ++j) {
     uint32_t word = kw[j], t = tw[j];
+    if (skip & (1u << j)) {
+      const int take = min(max(want, 0), __popc(t));
+      at[0] = (uint32_t)o;
+      at[1] = (uint32_t)max(want, 0);
+      at += 2;
+      o += __popc(word) + take;
+      want -= take;
+      continue;
+    }
     for (; want > 0 && t != 0u; --want) {            // the first tied blocks still wanted, in index order
       word |= t & (0u - t);
       t &= t - 1u;
@@ -299,44 +312,44 @@ __device__ __forceinline__ bool cand_complete(const uint4 (&cv)[kCandKeep / 2], 
 // (TPT tiles per thread): the crowded tiles (at most 32 * XPT) are read whole, XPT
 // blocks per thread, and the cut taken again over them and the other tiles' listed
 // keys, with the same check.  A crowded tile's kept and tied blocks are collected
-// into LDS words by the threads that read its blocks, and the tile's own thread
-// places them with its other tiles' in index order (place_words).  src: this
-// thread's first list piece, as the launch loaded it; the list is read again here
-// rather than held in registers through the common path.
+// into LDS words by the threads that read its blocks; its own thread counts them in
+// index order with its other tiles (place_words) and leaves their first list entry,
+// from which the threads that read them place them.  src: this thread's first list
+// piece, as the launch loaded it; the list is read again here (the keys first, the
+// block indices after the cut) rather than held in registers through the common path.
 template <int NT, int KPT, int KEEP, int TPT, int XPT>
 __device__ __forceinline__ bool cand_complete_tiles(const uint4* __restrict__ src, const float* __restrict__ row,
                                                     int nb, int c, int k_blk, uint32_t bound0, WideSmem<NT, KPT>& sm,
                                                     int32_t* list) {
-  constexpr int COPIES = WideCfg<NT, KPT>::copies, WAVES = NT / kWave, KC = KEEP * TPT;
+  constexpr int COPIES = WideCfg<NT, KPT>::copies, WAVES = NT / kWave, KC = KEEP * TPT, KP = KEEP / 4;
   constexpr int MAX_OVER = NT * XPT / kCandTile;
   // keep[] words: [0, WAVES) bounds, [WAVES, 2 WAVES) crowded tiles per wave, then the
-  // crowded tiles' numbers, their kept words and their tied words; tie[]: zero counts
-  constexpr int OT = 2 * WAVES, OK = OT + MAX_OVER, OTW = OK + MAX_OVER;
-  static_assert(WideCfg<NT, KPT>::words >= OTW + MAX_OVER, "LDS words for the crowded tiles");
+  // crowded tiles' numbers, their kept words, their tied words and their (first list
+  // entry, tied blocks wanted) pairs; tie[]: zero counts
+  constexpr int OT = 2 * WAVES, OK = OT + MAX_OVER, OTW = OK + MAX_OVER, OP = OTW + MAX_OVER;
+  static_assert(WideCfg<NT, KPT>::words >= OP + 2 * MAX_OVER, "LDS words for the crowded tiles");
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   nb = min(nb, NT * TPT * kCandTile);
   // the addresses are formed anew (an empty asm hides src's origin), so the common
   // path keeps none of its own load addresses live for this one
   asm volatile("" : "+v"(src));
-  uint4 cv[KEEP * TPT / 2];
+  uint4 kv[TPT * KP];                                // tile j's keys: pieces j * 2 KP .. + KP of the record
 #pragma unroll
-  for (int q = 0; q < KEEP * TPT / 2; ++q) cv[q] = src[q * kCandThreads];
-  uint32_t* w = reinterpret_cast<uint32_t*>(cv);     // tile j: KEEP keys, then KEEP block indices
+  for (int j = 0; j < TPT; ++j)
+#pragma unroll
+    for (int p = 0; p < KP; ++p) kv[j * KP + p] = src[(j * 2 * KP + p) * kCandThreads];
+  uint32_t* w = reinterpret_cast<uint32_t*>(kv);     // key e of tile j: w[j * KEEP + e]
 #pragma unroll
   for (int j = 0; j < TPT; ++j)                      // tiles past the row list nothing
 #pragma unroll
-    for (int e = 0; e < KEEP; ++e) w[j * 2 * KEEP + e] = (tid * TPT + j) * kCandTile < nb ? w[j * 2 * KEEP + e] : 0u;
-  auto tile_least = [&](int j) {
-    uint32_t x = w[j * 2 * KEEP];
-#pragma unroll
-    for (int e = 1; e < KEEP; ++e) x = min(x, w[j * 2 * KEEP + e]);
-    return x;
-  };
+    for (int e = 0; e < KEEP; ++e) w[j * KEEP + e] = (tid * TPT + j) * kCandTile < nb ? w[j * KEEP + e] : 0u;
   uint32_t ov = 0u;                                  // bit j: this thread's tile j is read whole
   uint32_t bmax = 0u;                                // the largest smallest-key of the others
 #pragma unroll
   for (int j = 0; j < TPT; ++j) {
-    const uint32_t x = tile_least(j);
+    uint32_t x = w[j * KEEP];
+#pragma unroll
+    for (int e = 1; e < KEEP; ++e) x = min(x, w[j * KEEP + e]);
     const bool o = (tid * TPT + j) * kCandTile < nb && x >= bound0;
     ov |= o ? 1u << j : 0u;
     bmax = max(bmax, o ? 0u : x);
@@ -369,21 +382,20 @@ __device__ __forceinline__ bool cand_complete_tiles(const uint4* __restrict__ sr
 #pragma unroll
   for (int j = 0; j < TPT; ++j)
 #pragma unroll
-    for (int e = 0; e < KEEP; ++e) w[j * 2 * KEEP + e] = (ov & (1u << j)) ? 0u : w[j * 2 * KEEP + e];
+    for (int e = 0; e < KEEP; ++e) w[j * KEEP + e] = (ov & (1u << j)) ? 0u : w[j * KEEP + e];
   __syncthreads();
   // extra keys: slot x * NT + tid is block slot % 32 of the (slot / 32)-th crowded tile
   uint32_t xkey[XPT];
-  int xtile[XPT];
 #pragma unroll
   for (int x = 0; x < XPT; ++x) {
     const int slot = x * NT + tid, k = slot / kCandTile;
-    xtile[x] = k < n_over ? (int)sm.keep[OT + k] : -1;
-    const int b = xtile[x] * kCandTile + slot % kCandTile;
-    const bool ok = xtile[x] >= 0 && b < nb;
+    const int xtile = k < n_over ? (int)sm.keep[OT + k] : -1;
+    const int b = xtile * kCandTile + slot % kCandTile;
+    const bool ok = xtile >= 0 && b < nb;
     const uint32_t rk = score_key(row[ok ? b : 0]);
     xkey[x] = ok ? rk : 0u;
   }
-  auto key = [&](int j) -> uint32_t { return j < KC ? w[(j / KEEP) * 2 * KEEP + j % KEEP] : xkey[j - KC]; };
+  auto key = [&](int j) -> uint32_t { return j < KC ? w[j] : xkey[j - KC]; };
   int zeros = 0;                                     // padding: key 0 (no score has it)
 #pragma unroll
   for (int j = 0; j < KC + XPT; ++j) zeros += key(j) == 0u ? 1 : 0;
@@ -406,6 +418,13 @@ __device__ __forceinline__ bool cand_complete_tiles(const uint4* __restrict__ sr
   if (left_out >= bound) return false;
   const uint32_t thr = cut.whole ? bound : bound + 1u;
   const bool full = !cut.whole && bound == 0xffffffffu;
+  // the other tiles' block indices (their keys' order)
+  uint4 iv[TPT * KP];
+#pragma unroll
+  for (int j = 0; j < TPT; ++j)
+#pragma unroll
+    for (int p = 0; p < KP; ++p) iv[j * KP + p] = src[(j * 2 * KP + KP + p) * kCandThreads];
+  const uint32_t* wi = reinterpret_cast<const uint32_t*>(iv);
   // the crowded tiles' kept and tied blocks, collected by the threads that read them
 #pragma unroll
   for (int x = 0; x < XPT; ++x) {
@@ -429,7 +448,7 @@ __device__ __forceinline__ bool cand_complete_tiles(const uint4* __restrict__ sr
     } else {
 #pragma unroll
       for (int e = 0; e < KEEP; ++e) {
-        const uint32_t k = w[j * 2 * KEEP + e], bit = 1u << (w[j * 2 * KEEP + KEEP + e] % kCandTile);
+        const uint32_t k = w[j * KEEP + e], bit = 1u << (wi[j * KEEP + e] % kCandTile);
         kw[j] |= (!full && k >= thr) ? bit : 0u;
         if (!cut.whole) tw[j] |= k == bound ? bit : 0u;
       }
@@ -437,7 +456,23 @@ __device__ __forceinline__ bool cand_complete_tiles(const uint4* __restrict__ sr
     kc += __popc(kw[j]);
     tc += __popc(tw[j]);
   }
-  place_words<NT, KPT, TPT>(kw, tw, kc, tc, cut.k_rem, c, k_blk, sm, list);
+  place_words<NT, KPT, TPT>(kw, tw, kc, tc, cut.k_rem, c, k_blk, sm, list, ov, &sm.keep[OP + 2 * first]);
+  // the crowded tiles' blocks, each placed by the thread that read it: after the kept
+  // and taken tied blocks before it in its tile
+#pragma unroll
+  for (int x = 0; x < XPT; ++x) {
+    const int slot = x * NT + tid, k = slot / kCandTile;
+    if (xkey[x] == 0u) continue;
+    const uint32_t below = (1u << (slot % kCandTile)) - 1u, bit = below + 1u;
+    const uint32_t kwt = sm.keep[OK + k], twt = sm.keep[OTW + k];
+    const int want = (int)sm.keep[OP + 2 * k + 1], tb = __popc(twt & below);
+    const int o = (int)sm.keep[OP + 2 * k] + __popc(kwt & below) + min(want, tb);
+    if (((kwt & bit) != 0u || ((twt & bit) != 0u && tb < want)) && o < k_blk) {
+      const int32_t p0 = ((int)sm.keep[OT + k] * kCandTile + slot % kCandTile) * c;
+      for (int u = 0; u < c; ++u) list[o * c + u] = p0 + u;
+    }
+  }
+  __syncthreads();
   return true;
 }
 

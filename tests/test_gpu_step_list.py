@@ -291,6 +291,18 @@ def test_step_list_long_rows(gpu_lib):
     tok = slice(int(case.row0[0]) + 64, int(case.row0[0]) + 96)
     case.kidx[tok] = case.kidx[tok] * np.float32(8.0)
     _check(case, expect_list=True, expect_decided=[1], oracle_queries=[0])
+    # ties at the cut inside crowded groups: 60 whole groups of copies of one key (scaled
+    # up eight times) and up to 600 more copies, at most 3 per group, in lower groups:
+    # some 2500 copies for the 2048 kept, the lower ones first; the 60 groups are read
+    # whole and their kept and tied blocks placed by the threads that read them
+    case = _case("step_list_long_tied_crowded", d, [40000], [0], [39999], 998)
+    rng = np.random.default_rng([998, 1])
+    r0 = int(case.row0[0])
+    groups = rng.choice(600, size=200, replace=False)
+    sparse = np.unique((groups[:, None] * GROUP + rng.choice(GROUP, size=(200, 3), replace=True)).reshape(-1))
+    blocks = np.concatenate([sparse, np.arange(700 * GROUP, 760 * GROUP)])
+    case.kidx[r0 + blocks] = case.kidx[r0 + 7] * np.float32(8.0)
+    _check(case, expect_list=True, expect_decided=[1], oracle_queries=[0])
     # 70 crowded groups (2240 blocks scaled up, more than the 2048 kept): more than the
     # 64 the launch reads whole, so the streamed per-query select over the row runs
     case = _case("step_list_long_very_crowded", d, [40000], [0], [39999], 997)
