@@ -238,7 +238,8 @@ int sparse_attn_select_fwd_is_fused(const sa_dims* dims, const sa_cache* cache, 
  * workgroup selects from that list instead of the row: the list's cut is the row's cut
  * exactly when every block it leaves out scores below that cut, which each group's
  * last listed key bounds; where it does not, the groups whose listed keys reach the cut
- * are read whole from the row and the cut taken again, and where that does not decide
+ * (at most 32; 64 for rows of more than 32768 blocks) are read whole from the row and
+ * the cut taken again, and where that does not decide
  * either (or the token's row is too short for the list to be likely to decide), the
  * workgroup selects over the row.  The list part ends with one int32 per token: 1 when
  * the list (with any groups read whole) decided its selection, 0 when the row did (or
