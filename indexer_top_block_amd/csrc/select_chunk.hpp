@@ -151,7 +151,11 @@ __device__ void select_one_query(const float* __restrict__ row, int nb, int c, i
       if (take && o < k_blk) {                       // o < k_blk always; the bound only guards memory
         const int32_t p0 = (int32_t)(base + j) * c;
         int32_t* dst = out + (int64_t)o * c;
-        for (int t = 0; t < c; ++t) dst[t] = p0 + t;
+        if (c == 1) {
+          dst[0] = p0;
+        } else {
+          for (int t = 0; t < c; ++t) dst[t] = p0 + t;
+        }
         ++o;
       }
     }
@@ -350,7 +354,11 @@ __device__ __forceinline__ void chunk_cut(ChunkSpec& sp, const ChunkScratch& sc,
     if (v >= cut && o < k_blk) {                     // o < k_blk always; the bound only guards memory
       const int32_t p0 = (int32_t)(0xFFFFFFFFu - (uint32_t)v) * c;
       int32_t* d = dst + (int64_t)o * c;
-      for (int t = 0; t < c; ++t) d[t] = p0 + t;
+      if (c == 1) {
+        d[0] = p0;
+      } else {
+        for (int t = 0; t < c; ++t) d[t] = p0 + t;
+      }
       ++o;
     }
   }

@@ -122,6 +122,11 @@ __device__ __forceinline__ void place_words(const uint32_t (&kw)[TPT], const uin
         *(int4*)&list[o * 4] = int4{p0, p0 + 1, p0 + 2, p0 + 3};
         ++o;
       }
+    } else if (c == 1) {
+      while (word != 0u && o < k_blk) {
+        list[o++] = b0 + __ffs(word) - 1;
+        word &= word - 1u;
+      }
     } else {
       while (word != 0u && o < k_blk) {
         const int32_t p0 = (b0 + __ffs(word) - 1) * c;

@@ -217,6 +217,8 @@ __device__ __forceinline__ void store_block(int32_t* dst, int32_t p0, int c) {
   if (c == 4) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) dst[t] = p0 + t;
+  } else if (c == 1) {
+    dst[0] = p0;
   } else {
     for (int t = 0; t < c; ++t) dst[t] = p0 + t;
   }
@@ -361,6 +363,11 @@ __device__ __forceinline__ void wide_list(const WideSmem<NT, KPT>& sm, bool whol
         word &= word - Word(1);
         *(int4*)&list[o * 4] = int4{p0, p0 + 1, p0 + 2, p0 + 3};
         ++o;
+      }
+    } else if (c == 1) {
+      while (word != Word(0) && o < k_blk) {
+        list[o++] = w * BPW + lowest_bit(word);
+        word &= word - Word(1);
       }
     } else {
       while (word != Word(0) && o < k_blk) {
