@@ -237,20 +237,38 @@ score_mfma_kernel(const T* __restrict__ qidx, const T* __restrict__ kpool, int64
   if (hf == 0 && valid) scores[(int64_t)i * scores_ld + b] = sum + 0.0f;  // +0.0 turns -0.0 into +0.0
   if constexpr (POOL) {
     if (pa.cand != nullptr && b_base / kCandTile < kCandThreads * pa.cand_tpt) {   // the tile's best blocks
-      // lanes 0..31 hold the tile's blocks (lanes 32..63 the same sums)
-      const uint64_t lo = 0xFFFFFFFFull;
+      // lanes n and n + 32 both hold block n's sum; the keep best of the tile's 32, ties
+      // to the lower block, as a mask of lanes 0..31 (uniform)
       const uint32_t key = valid ? score_key(sum + 0.0f) : 0u;   // the selection's key of the stored score
       const int keep = pa.cand_keep;
-      uint32_t v = 0u;                               // the tile's keep-th largest key, bit by bit
-      for (int bit = 31; bit >= 0; --bit) {
-        const uint32_t tv = v | (1u << bit);
-        if (__popcll(__ballot(key >= tv) & lo) >= keep) v = tv;
+      uint32_t taken = 0u;
+      if (keep <= 4) {
+        // the largest key not yet taken, keep times (the lowest lane holding it), each
+        // over the 32 lanes of a half: fewer dependent steps than the bit search below
+        // for 4, more for 8
+        for (int r = 0; r < keep; ++r) {
+          const bool alive = ((taken >> n) & 1u) == 0u;
+          const uint32_t x = alive ? key : 0u;
+          const uint32_t m = wave_extreme_u32<true, true>(x);
+          const uint32_t hit = (uint32_t)__ballot(alive && x == m);
+          taken |= hit & (0u - hit);
+        }
+      } else {
+        // the keep-th largest key v, bit by bit; then the keys above v and the first of
+        // those equal to it
+        const uint64_t lo = 0xFFFFFFFFull;
+        uint32_t v = 0u;
+        for (int bit = 31; bit >= 0; --bit) {
+          const uint32_t tv = v | (1u << bit);
+          if (__popcll(__ballot(key >= tv) & lo) >= keep) v = tv;
+        }
+        const uint64_t below_me = (1ull << lane) - 1ull;
+        const int n_above = __popcll(__ballot(key > v) & lo);
+        const int eq_rank = __popcll(__ballot(key == v) & lo & below_me);
+        taken = (uint32_t)__ballot(key > v || (key == v && eq_rank < keep - n_above));
       }
-      const uint64_t below_me = (1ull << lane) - 1ull;
-      const int n_above = __popcll(__ballot(key > v) & lo);
-      const int eq_rank = __popcll(__ballot(key == v) & lo & below_me);
-      const bool take = hf == 0 && (key > v || (key == v && eq_rank < keep - n_above));
-      const int slot = __popcll(__ballot(take) & below_me);
+      const bool take = hf == 0 && ((taken >> n) & 1u) != 0u;
+      const int slot = __popc(taken & ((1u << n) - 1u));
       uint32_t* cw = pa.cand + (int64_t)i * pa.cand_ld;
       const int g = b_base / kCandTile;
       if (take) {                                    // exactly keep lanes (blocks past the row: key 0)

@@ -117,8 +117,9 @@ __host__ __device__ __forceinline__ int64_t cand_offset(int g, int r, int keep, 
 
 // Maximum / minimum over the wave by DPP and permlane exchanges, the same value in
 // every lane (lane ^ 1, lane ^ 2, the mirror in 8, lane ^ 8, then the 16- and 32-lane
-// swaps: each step combines two halves that already hold their own extremes).
-template <bool MAX>
+// swaps: each step combines two halves that already hold their own extremes).  HALF:
+// over each 32-lane half only (the 32-lane swap left out).
+template <bool MAX, bool HALF = false>
 __device__ __forceinline__ uint32_t wave_extreme_u32(uint32_t x) {
   auto f = [](uint32_t a, uint32_t b) { return MAX ? max(a, b) : min(a, b); };
   x = f(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xf, 0xf, false));   // lane ^ 1
@@ -127,6 +128,7 @@ __device__ __forceinline__ uint32_t wave_extreme_u32(uint32_t x) {
   x = f(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x128, 0xf, 0xf, false));  // lane ^ 8 in 16
   const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
   x = f(a[0], a[1]);
+  if constexpr (HALF) return x;
   const auto b = __builtin_amdgcn_permlane32_swap(x, x, false, false);
   return f(b[0], b[1]);
 }
