@@ -330,6 +330,12 @@ def test_step_list_decode_1m(gpu_lib):
     # the 1M-context decode workload (262 144 blocks, 1% planted): 8192 groups, 4 listed each
     case = datagen.make_workload(5, q_std=2.0 * math.sqrt(576))
     _check(case, expect_list=True, expect_decided=[1], oracle_queries=[0])
+    # the same row with its three most recent groups (384 positions) scaled up eight
+    # times: 96 kept blocks in groups that list 4 each, read whole from the row
+    case = datagen.make_workload(5, q_std=2.0 * math.sqrt(576))
+    end = int(case.row0[0]) + int(case.seq_len[0]) // (4 * GROUP) * (4 * GROUP)
+    case.kidx[end - 3 * 4 * GROUP: end] = case.kidx[end - 3 * 4 * GROUP: end] * np.float32(8.0)
+    _check(case, expect_list=True, expect_decided=[1], oracle_queries=[0])
 
 
 def test_step_list_not_used(gpu_lib):
