@@ -255,12 +255,15 @@ score_mfma_kernel(const T* __restrict__ qidx, const T* __restrict__ kpool, int64
         }
       } else {
         // the keep-th largest key v, bit by bit; then the keys above v and the first of
-        // those equal to it
+        // those equal to it.  The search stops once exactly keep keys reach v: those are
+        // the keep best (the first bit where the keep-th and the next largest differ)
         const uint64_t lo = 0xFFFFFFFFull;
         uint32_t v = 0u;
         for (int bit = 31; bit >= 0; --bit) {
           const uint32_t tv = v | (1u << bit);
-          if (__popcll(__ballot(key >= tv) & lo) >= keep) v = tv;
+          const int n_ge = __popcll(__ballot(key >= tv) & lo);
+          if (n_ge >= keep) v = tv;
+          if (n_ge == keep) break;
         }
         const uint64_t below_me = (1ull << lane) - 1ull;
         const int n_above = __popcll(__ballot(key > v) & lo);
